@@ -1,0 +1,272 @@
+"""Deterministic generators for the five solve workloads and their scaled-down twins.
+
+The workloads follow the benchmark matrices described on the torch-sla page
+("torch-sla: Differentiable Sparse Linear Algebra with Adjoint Solvers and
+Sparse Tensor Parallelism for PyTorch"): the 2D five-point Poisson problem with
+homogeneous Dirichlet boundary of its Figure 2 study (64x64 interior grid), and
+large single-GPU / per-GPU shares of the same stencil (Table 3 / Table 4 text).
+The pages leave scaling, boundary treatment and coefficients open; the readings
+used here are:
+
+* stencils are unscaled: an off-diagonal entry is minus the coefficient of the
+  face between the two cells, the diagonal is the sum of all faces of the cell,
+  boundary faces included (homogeneous Dirichlet), no 1/h^2 factor;
+* variable coefficients live on faces, one value per face, drawn log-uniformly;
+* the unstructured workload is an OR-symmetrised 16-nearest-neighbour graph of
+  uniform points with Gaussian edge weights exp(-d^2/h^2), h the expected
+  16-NN radius (3*16/(4*pi*n))^(1/3), plus 0.01 on the diagonal.
+
+Entries are emitted in row-major order, columns ascending inside a row, with no
+duplicates. Right-hand sides are standard normal from numpy's PCG64.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+
+def normal_vector(seed: int, shape) -> np.ndarray:
+    """Standard-normal float64 array from ``numpy.random.default_rng(seed)``."""
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _log_uniform(rng: np.random.Generator, lo_exp: float, hi_exp: float, shape) -> np.ndarray:
+    return 10.0 ** rng.uniform(lo_exp, hi_exp, shape)
+
+
+# --------------------------------------------------------------------------- 2D unit Poisson
+
+def poisson2d_coo(N: int, index_dtype=np.int32):
+    """Unit five-point Laplacian on an N x N interior grid (diag 4, neighbours -1).
+
+    Node (y, x) has index y*N + x. Returns (rows, cols, vals) sorted by (row, col).
+    """
+    n = N * N
+    idx = np.arange(n, dtype=np.int64)
+    y, x = np.divmod(idx, N)
+    cand = np.stack([idx - N, idx - 1, idx, idx + 1, idx + N], axis=1)
+    valid = np.stack([y > 0, x > 0, np.ones(n, bool), x < N - 1, y < N - 1], axis=1)
+    vals = np.broadcast_to(np.array([-1.0, -1.0, 4.0, -1.0, -1.0]), cand.shape)
+    rows = np.broadcast_to(idx[:, None], cand.shape)[valid].astype(index_dtype)
+    cols = cand[valid].astype(index_dtype)
+    return rows, cols, np.ascontiguousarray(vals[valid], dtype=np.float64)
+
+
+def poisson2d_csr(N: int, rowptr_dtype=np.int64, col_dtype=np.int32, chunk: int = 1 << 22):
+    """Same matrix as :func:`poisson2d_coo`, emitted directly as CSR arrays.
+
+    Used for grids too large to hold a COO row array comfortably. Row lengths
+    follow in closed form from the grid position; the arrays are filled in row
+    chunks to bound host memory.
+    """
+    n = N * N
+    nnz = 5 * n - 4 * N
+    row_ptr = np.empty(n + 1, dtype=rowptr_dtype)
+    row_ptr[0] = 0
+    cols = np.empty(nnz, dtype=col_dtype)
+    vals = np.empty(nnz, dtype=np.float64)
+    stencil = np.array([-1.0, -1.0, 4.0, -1.0, -1.0])
+    for a in range(0, n, chunk):
+        b = min(n, a + chunk)
+        ii = np.arange(a, b, dtype=np.int64)
+        y, x = np.divmod(ii, N)
+        valid = np.stack([y > 0, x > 0, np.ones(b - a, bool), x < N - 1, y < N - 1], axis=1)
+        cnt = valid.sum(axis=1)
+        start = int(row_ptr[a])
+        row_ptr[a + 1:b + 1] = start + np.cumsum(cnt)
+        end = int(row_ptr[b])
+        cand = np.stack([ii - N, ii - 1, ii, ii + 1, ii + N], axis=1)
+        cols[start:end] = cand[valid]
+        vals[start:end] = np.broadcast_to(stencil, cand.shape)[valid]
+    assert int(row_ptr[n]) == nnz
+    return row_ptr, cols, vals
+
+
+# --------------------------------------------------------------------------- variable coefficients
+
+def diffusion2d_coo(N: int, cx: np.ndarray, cy: np.ndarray, index_dtype=np.int32):
+    """Five-point variable-coefficient diffusion on an N x N grid.
+
+    cx[..., y, x] (shape [..., N, N+1]) is the face to the left of node (y, x);
+    cy[..., y, x] (shape [..., N+1, N]) is the face below node (y, x). Leading
+    axes are value sets sharing one pattern. Values are computed in float64.
+    Returns rows, cols (shared) and vals of shape [..., nnz].
+    """
+    n = N * N
+    lead = cx.shape[:-2]
+    idx = np.arange(n, dtype=np.int64)
+    y, x = np.divmod(idx, N)
+    cxl = cx[..., :, :N].reshape(lead + (n,))       # face left of the node
+    cxr = cx[..., :, 1:].reshape(lead + (n,))       # face right of the node
+    cyd = cy[..., :N, :].reshape(lead + (n,))       # face below
+    cyu = cy[..., 1:, :].reshape(lead + (n,))       # face above
+    diag = ((cxl + cxr) + cyd) + cyu
+    cand = np.stack([idx - N, idx - 1, idx, idx + 1, idx + N], axis=1)
+    valid = np.stack([y > 0, x > 0, np.ones(n, bool), x < N - 1, y < N - 1], axis=1)
+    v = np.stack([-cyd, -cxl, diag, -cxr, -cyu], axis=-1)        # [..., n, 5]
+    rows = np.broadcast_to(idx[:, None], cand.shape)[valid].astype(index_dtype)
+    cols = cand[valid].astype(index_dtype)
+    vals = v[..., valid]
+    return rows, cols, np.ascontiguousarray(vals)
+
+
+def diffusion3d_coo(N: int, cx: np.ndarray, cy: np.ndarray, cz: np.ndarray, index_dtype=np.int32):
+    """Seven-point variable-coefficient diffusion on an N^3 grid, index z*N*N + y*N + x.
+
+    cx has shape (N, N, N+1) [z][y][x] (face at the low-x side of node x),
+    cy (N, N+1, N), cz (N+1, N, N). Boundary faces add to the diagonal only.
+    """
+    n = N * N * N
+    idx = np.arange(n, dtype=np.int64)
+    z, rem = np.divmod(idx, N * N)
+    y, x = np.divmod(rem, N)
+    cxl = cx[:, :, :N].reshape(n)
+    cxr = cx[:, :, 1:].reshape(n)
+    cyd = cy[:, :N, :].reshape(n)
+    cyu = cy[:, 1:, :].reshape(n)
+    czd = cz[:N, :, :].reshape(n)
+    czu = cz[1:, :, :].reshape(n)
+    diag = ((((cxl + cxr) + cyd) + cyu) + czd) + czu
+    NN = N * N
+    cand = np.stack([idx - NN, idx - N, idx - 1, idx, idx + 1, idx + N, idx + NN], axis=1)
+    valid = np.stack([z > 0, y > 0, x > 0, np.ones(n, bool), x < N - 1, y < N - 1, z < N - 1], axis=1)
+    v = np.stack([-czd, -cyd, -cxl, diag, -cxr, -cyu, -czu], axis=1)
+    rows = np.broadcast_to(idx[:, None], cand.shape)[valid].astype(index_dtype)
+    cols = cand[valid].astype(index_dtype)
+    return rows, cols, np.ascontiguousarray(v[valid])
+
+
+# --------------------------------------------------------------------------- kNN graph Laplacian
+
+def knn_laplacian_coo(points: np.ndarray, k: int, h: float, shift: float, index_dtype=np.int32):
+    """Graph Laplacian D - W + shift*I of the OR-symmetrised k-NN graph of ``points``.
+
+    w_ij = exp(-d_ij^2 / h^2) with d_ij^2 summed over coordinates in float64.
+    The diagonal is the row's weight sum accumulated in ascending column order,
+    plus ``shift``.
+    """
+    from scipy.spatial import cKDTree
+
+    n = points.shape[0]
+    tree = cKDTree(points)
+    _, nbr = tree.query(points, k=k + 1, workers=-1)
+    src = np.repeat(np.arange(n, dtype=np.int64), k)
+    dst = nbr[:, 1:].astype(np.int64).ravel()              # drop self (first neighbour)
+    keys = np.concatenate([src * n + dst, dst * n + src])
+    keys = np.unique(keys)                                   # sorted, OR-symmetrised edge set
+    r = keys // n
+    c = keys - r * n
+    d2 = np.zeros(keys.shape[0], dtype=np.float64)
+    for dim in range(points.shape[1]):
+        d2 += (points[r, dim] - points[c, dim]) ** 2
+    w = np.exp(-d2 / (h * h))
+    diag = np.bincount(r, weights=w, minlength=n) + shift
+    all_keys = np.concatenate([keys, np.arange(n, dtype=np.int64) * (n + 1)])
+    all_vals = np.concatenate([-w, diag])
+    order = np.argsort(all_keys, kind="stable")
+    all_keys = all_keys[order]
+    rows = (all_keys // n).astype(index_dtype)
+    cols = (all_keys % n).astype(index_dtype)
+    return rows, cols, np.ascontiguousarray(all_vals[order])
+
+
+# --------------------------------------------------------------------------- workload registry
+
+@dataclass
+class Workload:
+    name: str
+    description: str
+    n: int
+    batch: int
+    dtype: str                    # "f64" or "f32" (storage type of values and vectors)
+    fmt: str                      # "coo" or "csr"
+    rows: Optional[np.ndarray]    # COO row indices (fmt == "coo")
+    row_ptr: Optional[np.ndarray]  # CSR row pointer (fmt == "csr")
+    cols: np.ndarray
+    vals: np.ndarray              # [nnz] or [batch, nnz]
+    b: np.ndarray                 # [n] or [batch, n]
+    g: Optional[np.ndarray]       # upstream gradient for the adjoint, same shape as b
+    tol: float
+    maxit: int
+    adjoint: bool
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def nnz(self) -> int:
+        return int(self.cols.shape[0])
+
+
+# name -> (seed base, default size)
+WORKLOADS = {
+    "poisson2d_64": (1000, 64),
+    "diffusion3d_128": (2000, 128),
+    "batched_diffusion2d_512x32": (3000, 512),
+    "knn_laplacian_2m": (4000, 2_000_000),
+    "poisson2d_11548": (5000, 11548),
+}
+
+
+def make_workload(name: str, size: Optional[int] = None, batch: Optional[int] = None) -> Workload:
+    """Build workload ``name``; ``size`` shrinks the grid edge (or point count) for tests.
+
+    Seeds: with base s, b is drawn from default_rng(s+1), the adjoint's upstream
+    gradient from default_rng(s+2), coefficients from default_rng(s+3) and point
+    coordinates from default_rng(s+4).
+    """
+    if name not in WORKLOADS:
+        raise KeyError(f"unknown workload {name!r}; choose from {sorted(WORKLOADS)}")
+    s, default = WORKLOADS[name]
+    N = default if size is None else int(size)
+
+    if name == "poisson2d_64":
+        rows, cols, vals = poisson2d_coo(N)
+        n = N * N
+        return Workload(name, f"2D 5-point Poisson {N}x{N}, Dirichlet, fp64", n, 1, "f64", "coo",
+                        rows, None, cols, vals, normal_vector(s + 1, n), normal_vector(s + 2, n),
+                        1e-10, 20000, True, {"grid": N})
+
+    if name == "diffusion3d_128":
+        rng = np.random.default_rng(s + 3)
+        cx = _log_uniform(rng, -1, 1, (N, N, N + 1))
+        cy = _log_uniform(rng, -1, 1, (N, N + 1, N))
+        cz = _log_uniform(rng, -1, 1, (N + 1, N, N))
+        rows, cols, vals = diffusion3d_coo(N, cx, cy, cz)
+        n = N ** 3
+        return Workload(name, f"3D 7-point variable-coefficient diffusion {N}^3, fp64", n, 1, "f64",
+                        "coo", rows, None, cols, vals, normal_vector(s + 1, n),
+                        normal_vector(s + 2, n), 1e-10, 20000, True, {"grid": N})
+
+    if name == "batched_diffusion2d_512x32":
+        B = 32 if batch is None else int(batch)
+        rng = np.random.default_rng(s + 3)
+        cx = np.empty((B, N, N + 1))
+        cy = np.empty((B, N + 1, N))
+        for k in range(B):
+            cx[k] = _log_uniform(rng, -2, 2, (N, N + 1))
+            cy[k] = _log_uniform(rng, -2, 2, (N + 1, N))
+        rows, cols, vals = diffusion2d_coo(N, cx, cy)
+        n = N * N
+        return Workload(name, f"batched 2D 5-point diffusion {N}x{N}, {B} value sets, fp32", n, B,
+                        "f32", "coo", rows, None, cols, vals.astype(np.float32),
+                        normal_vector(s + 1, (B, n)).astype(np.float32),
+                        normal_vector(s + 2, (B, n)).astype(np.float32), 1e-6, 20000, True,
+                        {"grid": N})
+
+    if name == "knn_laplacian_2m":
+        n = N
+        pts = np.random.default_rng(s + 4).random((n, 3))
+        h = (3.0 * 16.0 / (4.0 * math.pi * n)) ** (1.0 / 3.0)
+        rows, cols, vals = knn_laplacian_coo(pts, 16, h, 1e-2)
+        return Workload(name, f"16-NN Gaussian graph Laplacian + 0.01 I, {n} points, fp64", n, 1,
+                        "f64", "coo", rows, None, cols, vals, normal_vector(s + 1, n),
+                        normal_vector(s + 2, n), 1e-8, 20000, True, {"h": h})
+
+    # poisson2d_11548: CSR input, int64 row pointer, fixed iteration budget
+    row_ptr, cols, vals = poisson2d_csr(N)
+    n = N * N
+    return Workload(name, f"2D 5-point Poisson {N}x{N}, fp64, int64 row_ptr", n, 1, "f64", "csr",
+                    None, row_ptr, cols, vals, normal_vector(s + 1, n), None, 0.0, 500, False,
+                    {"grid": N})
