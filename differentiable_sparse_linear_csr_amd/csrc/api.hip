@@ -1,0 +1,342 @@
+// extern "C" entry points declared in include/sla.h: argument checks, handle
+// lifetime, error reporting. Every call runs its work in this library's
+// kernels on the caller's stream.
+#include <cstring>
+#include <new>
+
+#include "common.h"
+
+namespace sla {
+
+namespace {
+thread_local std::string g_last_error;
+
+int64_t spmv_grid_count(const Handle &h);
+}  // namespace
+
+int64_t spmv_grid(const Handle &h);
+
+[[noreturn]] void fail(sla_status st, const std::string &msg) { throw Error{st, msg}; }
+
+void *dalloc(Handle &h, size_t bytes) {
+    void *p = nullptr;
+    if (bytes == 0) bytes = 1;
+    const hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        fail(SLA_ERR_OOM, "hipMalloc of " + std::to_string(bytes) + " bytes failed: " +
+                              hipGetErrorString(e));
+    }
+    h.allocs.push_back(p);
+    h.bytes += (int64_t)bytes;
+    return p;
+}
+
+void dfree_all(Handle &h) {
+    for (void *p : h.allocs) (void)hipFree(p);
+    h.allocs.clear();
+    h.bytes = 0;
+}
+
+namespace {
+
+int64_t spmv_grid_count(const Handle &h) { return spmv_grid(h); }
+
+template <typename F>
+sla_status guard(F &&f) {
+    try {
+        f();
+        g_last_error.clear();
+        return SLA_OK;
+    } catch (const Error &e) {
+        g_last_error = e.msg;
+        return e.st;
+    } catch (const std::bad_alloc &) {
+        g_last_error = "host allocation failed";
+        return SLA_ERR_OOM;
+    } catch (...) {
+        g_last_error = "unexpected internal error";
+        return SLA_ERR_HIP;
+    }
+}
+
+void destroy(Handle *h) {
+    if (!h) return;
+    (void)hipSetDevice(h->device);
+    if (h->graph) (void)hipGraphExecDestroy(h->graph);
+    for (auto &rec : h->pending) {
+        (void)hipEventDestroy(rec.a);
+        (void)hipEventDestroy(rec.b);
+    }
+    for (hipEvent_t e : h->ev)
+        if (e) (void)hipEventDestroy(e);
+    if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
+    if (h->h_running) (void)hipHostFree(h->h_running);
+    if (h->h_state) (void)hipHostFree(h->h_state);
+    if (h->h_ctl) (void)hipHostFree(h->h_ctl);
+    dfree_all(*h);
+    delete h;
+}
+
+void alloc_workspace(Handle &h, hipStream_t s) {
+    const size_t vec = (size_t)h.n * h.B * h.vbytes;
+    h.dinv = dalloc(h, vec);
+    h.x = dalloc(h, vec);
+    h.r = dalloc(h, vec);
+    h.p = dalloc(h, vec);
+    h.q = dalloc(h, vec);
+    int64_t plen = spmv_grid_count(h) * h.B;
+    const int64_t vec_part = (int64_t)kMaxGrid * 2 * h.B;
+    if (vec_part > plen) plen = vec_part;
+    h.part_len = plen;
+    h.part = (double *)dalloc(h, (size_t)plen * sizeof(double));
+    h.st = (SysState *)dalloc(h, sizeof(SysState) * h.B);
+    h.ctl = (Ctl *)dalloc(h, sizeof(Ctl));
+    SLA_HIP(hipMemsetAsync(h.ctl, 0, sizeof(Ctl), s));
+    SLA_HIP(hipMemsetAsync(h.st, 0, sizeof(SysState) * h.B, s));
+    if (hipHostMalloc((void **)&h.h_running, sizeof(int32_t), hipHostMallocMapped) != hipSuccess)
+        fail(SLA_ERR_OOM, "pinned host allocation failed");
+    *h.h_running = 0;
+    SLA_HIP(hipHostGetDevicePointer((void **)&h.d_running, h.h_running, 0));
+    if (hipHostMalloc((void **)&h.h_state, sizeof(SysState) * h.B, hipHostMallocDefault) !=
+        hipSuccess)
+        fail(SLA_ERR_OOM, "pinned host allocation failed");
+    if (hipHostMalloc((void **)&h.h_ctl, sizeof(Ctl), hipHostMallocDefault) != hipSuccess)
+        fail(SLA_ERR_OOM, "pinned host allocation failed");
+    std::memset(h.h_ctl, 0, sizeof(Ctl));
+    SLA_HIP(hipEventCreateWithFlags(&h.ev[0], hipEventDisableTiming));
+    SLA_HIP(hipEventCreateWithFlags(&h.ev[1], hipEventDisableTiming));
+    SLA_HIP(hipStreamCreateWithFlags(&h.cap_stream, hipStreamNonBlocking));
+}
+
+Handle *checked(sla_csr h) {
+    if (!h) fail(SLA_ERR_INVALID_ARG, "null handle");
+    Handle *hh = reinterpret_cast<Handle *>(h);
+    SLA_HIP(hipSetDevice(hh->device));
+    return hh;
+}
+
+}  // namespace
+}  // namespace sla
+
+using namespace sla;
+
+extern "C" {
+
+sla_status sla_csr_create(sla_csr *out, sla_format fmt, int64_t n, int64_t nnz_in, int32_t batch,
+                          sla_itype row_itype, const void *rows_or_row_ptr, sla_itype col_itype,
+                          const void *cols, sla_dtype vtype, const void *values, uint32_t flags,
+                          void *stream) {
+    Handle *h = nullptr;
+    const sla_status st = guard([&] {
+        if (!out) fail(SLA_ERR_INVALID_ARG, "out is null");
+        *out = nullptr;
+        if (fmt != SLA_INPUT_COO && fmt != SLA_INPUT_CSR) fail(SLA_ERR_INVALID_ARG, "bad format");
+        if (n < 1 || n >= (int64_t(1) << 31)) fail(SLA_ERR_INVALID_ARG, "n must be in [1, 2^31)");
+        if (nnz_in < 0 || nnz_in >= (int64_t(1) << 62)) fail(SLA_ERR_INVALID_ARG, "bad nnz");
+        if (batch < 1 || batch > kMaxBatch) fail(SLA_ERR_INVALID_ARG, "batch must be in [1, 256]");
+        if ((row_itype != SLA_I32 && row_itype != SLA_I64) ||
+            (col_itype != SLA_I32 && col_itype != SLA_I64))
+            fail(SLA_ERR_INVALID_ARG, "bad index type");
+        if (vtype != SLA_F32 && vtype != SLA_F64) fail(SLA_ERR_INVALID_ARG, "bad value type");
+        if (flags & ~(uint32_t)SLA_FLAG_CHECK_SYMMETRIC) fail(SLA_ERR_INVALID_ARG, "unknown flag");
+        if (fmt == SLA_INPUT_CSR && !rows_or_row_ptr) fail(SLA_ERR_INVALID_ARG, "row_ptr is null");
+        if (nnz_in > 0 && (!rows_or_row_ptr || !cols || !values))
+            fail(SLA_ERR_INVALID_ARG, "null index or value pointer");
+        if (fmt == SLA_INPUT_CSR && row_itype == SLA_I32 && nnz_in >= (int64_t(1) << 31))
+            fail(SLA_ERR_INVALID_ARG, "int32 row_ptr cannot address nnz >= 2^31");
+        hipStream_t s = (hipStream_t)stream;
+        h = new Handle();
+        SLA_HIP(hipGetDevice(&h->device));
+        h->n = n;
+        h->nnz_in = nnz_in;
+        h->B = batch;
+        h->vt = vtype;
+        h->vbytes = vtype == SLA_F64 ? 8 : 4;
+        h->flags = flags;
+        if (fmt == SLA_INPUT_COO)
+            build_from_coo(*h, row_itype, rows_or_row_ptr, col_itype, cols, values, s);
+        else
+            build_from_csr(*h, row_itype, rows_or_row_ptr, col_itype, cols, values, s);
+        build_tiles(*h, s);
+        alloc_workspace(*h, s);
+        compute_dinv(*h, s);
+        if ((flags & SLA_FLAG_CHECK_SYMMETRIC) && !check_symmetric(*h, s))
+            fail(SLA_ERR_NOT_SYMMETRIC, "matrix is not symmetric (bitwise)");
+        SLA_HIP(hipStreamSynchronize(s));
+        *out = reinterpret_cast<sla_csr>(h);
+    });
+    if (st != SLA_OK && h) destroy(h);
+    return st;
+}
+
+sla_status sla_csr_set_values(sla_csr hd, const void *values, void *stream) {
+    return guard([&] {
+        Handle *h = checked(hd);
+        if (h->nnz_in > 0 && !values) fail(SLA_ERR_INVALID_ARG, "values is null");
+        hipStream_t s = (hipStream_t)stream;
+        load_values(*h, values, s);
+        compute_dinv(*h, s);
+        if ((h->flags & SLA_FLAG_CHECK_SYMMETRIC) && !check_symmetric(*h, s))
+            fail(SLA_ERR_NOT_SYMMETRIC, "matrix is not symmetric (bitwise)");
+    });
+}
+
+sla_status sla_csr_get(sla_csr hd, int64_t *n, int64_t *nnz, int64_t *nnz_in, int32_t *batch,
+                       int32_t *vtype, int32_t *row_itype, const void **row_ptr,
+                       const void **col_idx, const int64_t **slot) {
+    return guard([&] {
+        if (!hd) fail(SLA_ERR_INVALID_ARG, "null handle");
+        const Handle *h = reinterpret_cast<const Handle *>(hd);
+        if (n) *n = h->n;
+        if (nnz) *nnz = h->nnz;
+        if (nnz_in) *nnz_in = h->nnz_in;
+        if (batch) *batch = h->B;
+        if (vtype) *vtype = h->vt;
+        if (row_itype) *row_itype = h->rp64 ? SLA_I64 : SLA_I32;
+        if (row_ptr) *row_ptr = h->row_ptr;
+        if (col_idx) *col_idx = h->col;
+        if (slot) *slot = h->slot;
+    });
+}
+
+sla_status sla_csr_get_pattern(sla_csr hd, void *row_ptr_out, void *col_idx_out,
+                               int64_t *slot_out, void *stream) {
+    return guard([&] {
+        Handle *h = checked(hd);
+        hipStream_t s = (hipStream_t)stream;
+        if (row_ptr_out)
+            SLA_HIP(hipMemcpyAsync(row_ptr_out, h->row_ptr, (size_t)(h->n + 1) * (h->rp64 ? 8 : 4),
+                                   hipMemcpyDeviceToDevice, s));
+        if (col_idx_out && h->nnz > 0)
+            SLA_HIP(hipMemcpyAsync(col_idx_out, h->col, (size_t)h->nnz * 4, hipMemcpyDeviceToDevice,
+                                   s));
+        if (slot_out && h->nnz_in > 0) {
+            if (h->slot)
+                SLA_HIP(hipMemcpyAsync(slot_out, h->slot, (size_t)h->nnz_in * 8,
+                                       hipMemcpyDeviceToDevice, s));
+            else
+                iota_i64(slot_out, h->nnz_in, s);
+        }
+    });
+}
+
+sla_status sla_csr_get_values(sla_csr hd, void *values_out, void *stream) {
+    return guard([&] {
+        Handle *h = checked(hd);
+        if (!values_out) fail(SLA_ERR_INVALID_ARG, "values_out is null");
+        values_to_batch_major(*h, values_out, (hipStream_t)stream);
+    });
+}
+
+sla_status sla_csr_gather_to_input(sla_csr hd, const void *csr_order, void *input_order,
+                                   void *stream) {
+    return guard([&] {
+        Handle *h = checked(hd);
+        if (!csr_order || !input_order) fail(SLA_ERR_INVALID_ARG, "null pointer");
+        gather_to_input(*h, csr_order, input_order, (hipStream_t)stream);
+    });
+}
+
+sla_status sla_csr_set_option(sla_csr hd, int32_t key, int64_t value) {
+    return guard([&] {
+        Handle *h = checked(hd);
+        switch (key) {
+            case SLA_OPT_CHECK_INTERVAL:
+                if (value < 1 || value > 4096) fail(SLA_ERR_INVALID_ARG, "check interval in [1, 4096]");
+                h->check_k = (int)value;
+                break;
+            case SLA_OPT_USE_GRAPH:
+                h->use_graph = value != 0;
+                break;
+            case SLA_OPT_PROFILE:
+                h->profile = value != 0;
+                break;
+            default:
+                fail(SLA_ERR_INVALID_ARG, "unknown option");
+        }
+    });
+}
+
+sla_status sla_spmv(sla_csr hd, const void *x, void *y, void *stream) {
+    return guard([&] {
+        Handle *h = checked(hd);
+        if (!x || !y) fail(SLA_ERR_INVALID_ARG, "null vector");
+        if (x == y) fail(SLA_ERR_INVALID_ARG, "x and y must not alias");
+        spmv(*h, x, y, (hipStream_t)stream);
+    });
+}
+
+sla_status sla_pcg_solve(sla_csr hd, const void *b, void *x, double tol, int32_t maxit,
+                         sla_info *info, void *stream) {
+    return guard([&] {
+        Handle *h = checked(hd);
+        if (!b || !x || !info) fail(SLA_ERR_INVALID_ARG, "null pointer");
+        if (!(tol >= 0.0) || maxit < 0) fail(SLA_ERR_INVALID_ARG, "need tol >= 0 and maxit >= 0");
+        if (!h->diag_ok)
+            fail(SLA_ERR_BAD_DIAGONAL,
+                 "Jacobi preconditioning needs every diagonal entry present, positive and finite");
+        pcg(*h, b, x, tol, maxit, info, (hipStream_t)stream, false);
+    });
+}
+
+sla_status sla_adjoint_backward(sla_csr hd, const void *x, const void *grad_x, void *grad_b,
+                                void *grad_vals_out, double tol, int32_t maxit, sla_info *info,
+                                void *stream) {
+    return guard([&] {
+        Handle *h = checked(hd);
+        if (!x || !grad_x || !info) fail(SLA_ERR_INVALID_ARG, "null pointer");
+        if (!(tol >= 0.0) || maxit < 0) fail(SLA_ERR_INVALID_ARG, "need tol >= 0 and maxit >= 0");
+        if (!h->diag_ok)
+            fail(SLA_ERR_BAD_DIAGONAL,
+                 "Jacobi preconditioning needs every diagonal entry present, positive and finite");
+        hipStream_t s = (hipStream_t)stream;
+        pcg(*h, grad_x, nullptr, tol, maxit, info, s, true);  // lambda stays in the workspace
+        if (grad_b) {
+            if (h->B == 1)
+                SLA_HIP(hipMemcpyAsync(grad_b, h->x, (size_t)h->n * h->vbytes,
+                                       hipMemcpyDeviceToDevice, s));
+            else
+                transpose(h->x, grad_b, h->n, h->B, h->vbytes, s);
+        }
+        if (grad_vals_out) grad_vals(*h, h->x, x, grad_vals_out, s);
+        SLA_HIP(hipStreamSynchronize(s));
+        if (h->profile) flush_profile(*h);
+    });
+}
+
+sla_status sla_profile_get(sla_csr hd, int32_t kind, int64_t *launches, double *total_ms) {
+    return guard([&] {
+        if (!hd) fail(SLA_ERR_INVALID_ARG, "null handle");
+        if (kind < 0 || kind >= SLA_KERNEL_COUNT) fail(SLA_ERR_INVALID_ARG, "bad kernel kind");
+        const Handle *h = reinterpret_cast<const Handle *>(hd);
+        if (launches) *launches = h->prof_launches[kind];
+        if (total_ms) *total_ms = h->prof_ms[kind];
+    });
+}
+
+sla_status sla_profile_reset(sla_csr hd) {
+    return guard([&] {
+        if (!hd) fail(SLA_ERR_INVALID_ARG, "null handle");
+        Handle *h = reinterpret_cast<Handle *>(hd);
+        for (int k = 0; k < SLA_KERNEL_COUNT; ++k) {
+            h->prof_launches[k] = 0;
+            h->prof_ms[k] = 0.0;
+        }
+    });
+}
+
+sla_status sla_csr_memory(sla_csr hd, int64_t *bytes) {
+    return guard([&] {
+        if (!hd || !bytes) fail(SLA_ERR_INVALID_ARG, "null pointer");
+        *bytes = reinterpret_cast<const Handle *>(hd)->bytes;
+    });
+}
+
+void sla_csr_destroy(sla_csr hd) { destroy(reinterpret_cast<Handle *>(hd)); }
+
+const char *sla_last_error(void) { return g_last_error.c_str(); }
+
+const char *sla_version(void) { return "sla 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,560 @@
+// CSR assembly on the device: COO validation, stable (row, col) ordering,
+// in-order duplicate merge, row pointers, slot map; CSR validation and
+// adoption; SpMV tiles; Jacobi reciprocal; bitwise symmetry check.
+//
+// The storage a SparseTensor needs (one matrix, or a batch of value sets on
+// one pattern: torch-sla, tensor-types passage of its API section) is built
+// here. Duplicate entries are summed left to right in input order, in the
+// value type, so the result is bit-identical for any launch configuration.
+#include <type_traits>
+
+#include "common.h"
+
+namespace sla {
+
+namespace {
+
+enum : int { kBadIndex = 1, kUnsorted = 2, kBadCsr = 4 };
+
+template <typename I>
+__device__ __forceinline__ int64_t ld_idx(const I *p, int64_t k) {
+    return (int64_t)p[k];
+}
+
+template <typename RI, typename CI>
+__global__ __launch_bounds__(kBlock) void k_coo_check(const RI *__restrict__ rows,
+                                                      const CI *__restrict__ cols, int64_t m,
+                                                      int64_t n, int *__restrict__ flags) {
+    int f = 0;
+    for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < m;
+         e += (int64_t)gridDim.x * kBlock) {
+        const int64_t r = ld_idx(rows, e), c = ld_idx(cols, e);
+        if (r < 0 || r >= n || c < 0 || c >= n) f |= kBadIndex;
+        if (e + 1 < m) {
+            const int64_t r2 = ld_idx(rows, e + 1), c2 = ld_idx(cols, e + 1);
+            if (!(r < r2 || (r == r2 && c < c2))) f |= kUnsorted;
+        }
+    }
+    if (f) atomicOr(flags, f);
+}
+
+// row_ptr of a row-sorted index list: row_ptr[r] = first position with row >= r
+template <typename RI, typename RP>
+__global__ __launch_bounds__(kBlock) void k_rowptr_sorted(const RI *__restrict__ rows, int64_t m,
+                                                          int64_t n, RP *__restrict__ row_ptr) {
+    for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e <= m;
+         e += (int64_t)gridDim.x * kBlock) {
+        const int64_t prev = e == 0 ? -1 : ld_idx(rows, e - 1);
+        const int64_t cur = e == m ? n : ld_idx(rows, e);
+        for (int64_t r = prev + 1; r <= cur; ++r) row_ptr[r] = (RP)e;
+    }
+}
+
+template <typename S, typename D>
+__global__ __launch_bounds__(kBlock) void k_convert(const S *__restrict__ in, int64_t m,
+                                                    D *__restrict__ out) {
+    for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < m;
+         e += (int64_t)gridDim.x * kBlock)
+        out[e] = (D)in[e];
+}
+
+template <typename RI, typename CI>
+__global__ __launch_bounds__(kBlock) void k_make_keys(const RI *__restrict__ rows,
+                                                      const CI *__restrict__ cols, int64_t m,
+                                                      int64_t n, uint64_t *__restrict__ keys,
+                                                      int64_t *__restrict__ idx) {
+    for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < m;
+         e += (int64_t)gridDim.x * kBlock) {
+        keys[e] = (uint64_t)ld_idx(rows, e) * (uint64_t)n + (uint64_t)ld_idx(cols, e);
+        idx[e] = e;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_heads(const uint64_t *__restrict__ keys, int64_t m,
+                                                  int64_t *__restrict__ head) {
+    for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < m;
+         t += (int64_t)gridDim.x * kBlock)
+        head[t] = (t == 0 || keys[t] != keys[t - 1]) ? 1 : 0;
+}
+
+__global__ __launch_bounds__(kBlock) void k_unique(const uint64_t *__restrict__ keys,
+                                                   const int64_t *__restrict__ perm,
+                                                   const int64_t *__restrict__ excl,
+                                                   const int64_t *__restrict__ head, int64_t m,
+                                                   int64_t n, int32_t *__restrict__ col,
+                                                   int64_t *__restrict__ urow,
+                                                   int64_t *__restrict__ run,
+                                                   int64_t *__restrict__ slot) {
+    for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < m;
+         t += (int64_t)gridDim.x * kBlock) {
+        const int64_t u = excl[t] + head[t] - 1;
+        if (head[t]) {
+            const uint64_t k = keys[t];
+            run[u] = t;
+            urow[u] = (int64_t)(k / (uint64_t)n);
+            col[u] = (int32_t)(k % (uint64_t)n);
+        }
+        slot[perm[t]] = u;
+    }
+}
+
+// CSR entry u (of value set b) = v[run[u]] + v[run[u]+1] + ... in sorted
+// order, which is input order within one position (stable sort).
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_merge(const T *__restrict__ vin,
+                                                  const int64_t *__restrict__ perm,
+                                                  const int64_t *__restrict__ run, int64_t nnz,
+                                                  int64_t nnz_in, int B, T *__restrict__ out) {
+    const int64_t total = nnz * B;
+    for (int64_t f = (int64_t)blockIdx.x * kBlock + threadIdx.x; f < total;
+         f += (int64_t)gridDim.x * kBlock) {
+        const int64_t u = f / B;
+        const int b = (int)(f - u * B);
+        const T *vb = vin + (int64_t)b * nnz_in;
+        const int64_t t0 = run[u], t1 = run[u + 1];
+        T acc = vb[perm[t0]];
+        for (int64_t t = t0 + 1; t < t1; ++t) acc = acc + vb[perm[t]];
+        out[f] = acc;
+    }
+}
+
+template <typename RI, typename CI>
+__global__ __launch_bounds__(kBlock) void k_csr_check(const RI *__restrict__ row_ptr,
+                                                      const CI *__restrict__ cols, int64_t n,
+                                                      int64_t nnz, int *__restrict__ flags) {
+    int f = 0;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * kBlock) {
+        const int64_t a = ld_idx(row_ptr, i), b = ld_idx(row_ptr, i + 1);
+        if (i == 0 && a != 0) f |= kBadCsr;
+        if (i == n - 1 && b != nnz) f |= kBadCsr;
+        if (a < 0 || b > nnz || b < a) {
+            f |= kBadCsr;
+            continue;  // never index outside [0, nnz)
+        }
+        int64_t prevc = -1;
+        for (int64_t k = a; k < b; ++k) {
+            const int64_t c = ld_idx(cols, k);
+            if (c < 0 || c >= n) f |= kBadIndex;
+            if (c <= prevc) f |= kBadCsr;
+            prevc = c;
+        }
+    }
+    if (f) atomicOr(flags, f);
+}
+
+template <typename RP>
+__global__ __launch_bounds__(kBlock) void k_tile_flags(const RP *__restrict__ row_ptr, int64_t n,
+                                                       int64_t *__restrict__ flag) {
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * kBlock) {
+        const int64_t a = row_ptr[i], b = row_ptr[i + 1];
+        const bool long_i = (b - a) > kLongRow;
+        int64_t f = 1;
+        if (i > 0) {
+            const int64_t pa = row_ptr[i - 1];
+            const bool long_prev = (a - pa) > kLongRow;
+            const int64_t u_prev = pa + (i - 1), u_cur = a + i;
+            f = (long_i || long_prev || (u_prev / kTileUnits) != (u_cur / kTileUnits)) ? 1 : 0;
+        }
+        flag[i] = f;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_tile_fill(const int64_t *__restrict__ flag,
+                                                      const int64_t *__restrict__ excl, int64_t n,
+                                                      int32_t *__restrict__ tile_start) {
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * kBlock)
+        if (flag[i]) tile_start[excl[i]] = (int32_t)i;
+}
+
+// dinv[i][b] = 1 / A_ii (IEEE division; fp32 storage: formed in fp64, rounded
+// once). Missing, non-positive or non-finite diagonals are counted.
+template <typename T, typename RP>
+__global__ __launch_bounds__(kBlock) void k_dinv(const RP *__restrict__ row_ptr,
+                                                 const int32_t *__restrict__ col,
+                                                 const T *__restrict__ vals, int64_t n, int B,
+                                                 T *__restrict__ dinv, int *__restrict__ bad) {
+    int nbad = 0;
+    const int64_t total = n * B;
+    for (int64_t f = (int64_t)blockIdx.x * kBlock + threadIdx.x; f < total;
+         f += (int64_t)gridDim.x * kBlock) {
+        const int64_t i = f / B;
+        const int b = (int)(f - i * B);
+        int64_t lo = row_ptr[i], hi = row_ptr[i + 1];
+        while (lo < hi) {  // first column >= i
+            const int64_t mid = (lo + hi) >> 1;
+            if (col[mid] < i) lo = mid + 1;
+            else hi = mid;
+        }
+        const bool found = lo < (int64_t)row_ptr[i + 1] && col[lo] == i;
+        const double d = found ? (double)vals[lo * B + b] : 0.0;
+        if (!found || !(d > 0.0) || !isfinite(d)) {
+            ++nbad;
+            dinv[f] = (T)0;
+        } else {
+            dinv[f] = (T)(1.0 / d);
+        }
+    }
+    if (nbad) atomicAdd(bad, nbad);
+}
+
+template <typename T>
+struct Bits;
+template <>
+struct Bits<float> {
+    using U = uint32_t;
+};
+template <>
+struct Bits<double> {
+    using U = uint64_t;
+};
+
+template <typename T, typename RP>
+__global__ __launch_bounds__(kBlock) void k_symmetric(const RP *__restrict__ row_ptr,
+                                                      const int32_t *__restrict__ col,
+                                                      const T *__restrict__ vals, int64_t n, int B,
+                                                      int *__restrict__ flag) {
+    using U = typename Bits<T>::U;
+    const U *bits = reinterpret_cast<const U *>(vals);
+    int bad = 0;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * kBlock) {
+        for (int64_t k = row_ptr[i]; k < (int64_t)row_ptr[i + 1]; ++k) {
+            const int64_t j = col[k];
+            int64_t lo = row_ptr[j], hi = row_ptr[j + 1];
+            while (lo < hi) {
+                const int64_t mid = (lo + hi) >> 1;
+                if (col[mid] < i) lo = mid + 1;
+                else hi = mid;
+            }
+            if (!(lo < (int64_t)row_ptr[j + 1] && col[lo] == i)) {
+                bad = 1;
+                continue;
+            }
+            for (int b = 0; b < B; ++b)
+                if (bits[k * B + b] != bits[lo * B + b]) bad = 1;
+        }
+    }
+    if (bad) atomicOr(flag, 1);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_gather(const T *__restrict__ in,
+                                                   const int64_t *__restrict__ slot, int64_t nnz,
+                                                   int64_t nnz_in, int B, T *__restrict__ out) {
+    const int64_t total = nnz_in * B;
+    for (int64_t f = (int64_t)blockIdx.x * kBlock + threadIdx.x; f < total;
+         f += (int64_t)gridDim.x * kBlock) {
+        const int64_t b = f / nnz_in;
+        const int64_t e = f - b * nnz_in;
+        out[f] = in[b * nnz + slot[e]];
+    }
+}
+
+inline unsigned grid_for(int64_t work) {
+    int64_t g = (work + kBlock - 1) / kBlock;
+    if (g < 1) g = 1;
+    if (g > 65536) g = 65536;
+    return (unsigned)g;
+}
+
+template <typename F>
+void dispatch_idx(sla_itype it, F &&f) {
+    if (it == SLA_I32) f((const int32_t *)nullptr);
+    else f((const int64_t *)nullptr);
+}
+
+int read_flag(int *dflag, hipStream_t s) {
+    int h = 0;
+    SLA_HIP(hipMemcpyAsync(&h, dflag, sizeof(int), hipMemcpyDeviceToHost, s));
+    SLA_HIP(hipStreamSynchronize(s));
+    return h;
+}
+
+int64_t read_i64(const int64_t *d, hipStream_t s) {
+    int64_t h = 0;
+    SLA_HIP(hipMemcpyAsync(&h, d, sizeof(int64_t), hipMemcpyDeviceToHost, s));
+    SLA_HIP(hipStreamSynchronize(s));
+    return h;
+}
+
+struct Scratch {
+    hipStream_t s;
+    std::vector<void *> ptrs;
+    explicit Scratch(hipStream_t s_) : s(s_) {}
+    template <typename T>
+    T *get(int64_t count) {
+        void *p = nullptr;
+        SLA_HIP(hipMallocAsync(&p, (size_t)(count > 0 ? count : 1) * sizeof(T), s));
+        ptrs.push_back(p);
+        return (T *)p;
+    }
+    ~Scratch() {
+        for (void *p : ptrs) (void)hipFreeAsync(p, s);
+    }
+};
+
+}  // namespace
+
+// ------------------------------------------------------------------ COO input
+
+void build_from_coo(Handle &h, sla_itype rit, const void *rows, sla_itype cit, const void *cols,
+                    const void *values, hipStream_t s) {
+    const int64_t m = h.nnz_in, n = h.n;
+    Scratch sc(s);
+    int *dflag = sc.get<int>(1);
+    SLA_HIP(hipMemsetAsync(dflag, 0, sizeof(int), s));
+    if (m > 0) {
+        auto launch = [&](auto rtag, auto ctag) {
+            using RI = std::remove_const_t<std::remove_pointer_t<decltype(rtag)>>;
+            using CI = std::remove_const_t<std::remove_pointer_t<decltype(ctag)>>;
+            hipLaunchKernelGGL((k_coo_check<RI, CI>), dim3(grid_for(m)), dim3(kBlock), 0, s,
+                               (const RI *)rows, (const CI *)cols, m, n, dflag);
+        };
+        dispatch_idx(rit, [&](auto r) { dispatch_idx(cit, [&](auto c) { launch(r, c); }); });
+        SLA_HIP(hipGetLastError());
+    }
+    const int flags = read_flag(dflag, s);
+    if (flags & kBadIndex) fail(SLA_ERR_INDEX_RANGE, "a COO row or column index is outside [0, n)");
+
+    if (!(flags & kUnsorted)) {
+        // sorted, duplicate-free input: the permutation and the slot map are the identity
+        h.nnz = m;
+        h.rp64 = m >= (int64_t(1) << 31);
+        h.row_ptr = dalloc(h, (size_t)(n + 1) * (h.rp64 ? 8 : 4));
+        h.col = (int32_t *)dalloc(h, (size_t)(m > 0 ? m : 1) * 4);
+        auto launch = [&](auto rtag) {
+            using RI = std::remove_const_t<std::remove_pointer_t<decltype(rtag)>>;
+            if (h.rp64)
+                hipLaunchKernelGGL((k_rowptr_sorted<RI, int64_t>), dim3(grid_for(m + 1)),
+                                   dim3(kBlock), 0, s, (const RI *)rows, m, n,
+                                   (int64_t *)h.row_ptr);
+            else
+                hipLaunchKernelGGL((k_rowptr_sorted<RI, int32_t>), dim3(grid_for(m + 1)),
+                                   dim3(kBlock), 0, s, (const RI *)rows, m, n,
+                                   (int32_t *)h.row_ptr);
+        };
+        dispatch_idx(rit, launch);
+        SLA_HIP(hipGetLastError());
+        if (m > 0) {
+            if (cit == SLA_I32)
+                SLA_HIP(hipMemcpyAsync(h.col, cols, (size_t)m * 4, hipMemcpyDeviceToDevice, s));
+            else
+                hipLaunchKernelGGL((k_convert<int64_t, int32_t>), dim3(grid_for(m)), dim3(kBlock),
+                                   0, s, (const int64_t *)cols, m, h.col);
+            SLA_HIP(hipGetLastError());
+        }
+    } else {
+        // general input: stable radix sort of (row*n + col, input index)
+        uint64_t *keys = sc.get<uint64_t>(m);
+        h.perm = (int64_t *)dalloc(h, (size_t)m * 8);
+        auto launch = [&](auto rtag, auto ctag) {
+            using RI = std::remove_const_t<std::remove_pointer_t<decltype(rtag)>>;
+            using CI = std::remove_const_t<std::remove_pointer_t<decltype(ctag)>>;
+            hipLaunchKernelGGL((k_make_keys<RI, CI>), dim3(grid_for(m)), dim3(kBlock), 0, s,
+                               (const RI *)rows, (const CI *)cols, m, n, keys, h.perm);
+        };
+        dispatch_idx(rit, [&](auto r) { dispatch_idx(cit, [&](auto c) { launch(r, c); }); });
+        SLA_HIP(hipGetLastError());
+        int bits = 0;
+        while ((int64_t(1) << bits) < n) ++bits;
+        radix_sort_pairs(keys, h.perm, m, 2 * bits, s);
+
+        int64_t *head = sc.get<int64_t>(m);
+        int64_t *excl = sc.get<int64_t>(m);
+        hipLaunchKernelGGL(k_heads, dim3(grid_for(m)), dim3(kBlock), 0, s, (const uint64_t *)keys,
+                           m, head);
+        SLA_HIP(hipGetLastError());
+        exclusive_scan_i64(head, excl, m, s);
+        const int64_t nnz_u = read_i64(excl + (m - 1), s) + read_i64(head + (m - 1), s);
+        h.nnz = nnz_u;
+        h.rp64 = nnz_u >= (int64_t(1) << 31);
+        h.col = (int32_t *)dalloc(h, (size_t)nnz_u * 4);
+        h.run = (int64_t *)dalloc(h, (size_t)(nnz_u + 1) * 8);
+        h.slot = (int64_t *)dalloc(h, (size_t)m * 8);
+        int64_t *urow = sc.get<int64_t>(nnz_u);
+        hipLaunchKernelGGL(k_unique, dim3(grid_for(m)), dim3(kBlock), 0, s, (const uint64_t *)keys,
+                           (const int64_t *)h.perm, (const int64_t *)excl, (const int64_t *)head,
+                           m, n, h.col, urow, h.run, h.slot);
+        SLA_HIP(hipGetLastError());
+        SLA_HIP(hipMemcpyAsync(h.run + nnz_u, &m, 8, hipMemcpyHostToDevice, s));
+        h.row_ptr = dalloc(h, (size_t)(n + 1) * (h.rp64 ? 8 : 4));
+        if (h.rp64)
+            hipLaunchKernelGGL((k_rowptr_sorted<int64_t, int64_t>), dim3(grid_for(nnz_u + 1)),
+                               dim3(kBlock), 0, s, (const int64_t *)urow, nnz_u, n,
+                               (int64_t *)h.row_ptr);
+        else
+            hipLaunchKernelGGL((k_rowptr_sorted<int64_t, int32_t>), dim3(grid_for(nnz_u + 1)),
+                               dim3(kBlock), 0, s, (const int64_t *)urow, nnz_u, n,
+                               (int32_t *)h.row_ptr);
+        SLA_HIP(hipGetLastError());
+        SLA_HIP(hipStreamSynchronize(s));  // host value m above must outlive the copy
+    }
+    h.vals = dalloc(h, (size_t)(h.nnz > 0 ? h.nnz : 1) * h.B * h.vbytes);
+    load_values(h, values, s);
+}
+
+// ------------------------------------------------------------------ CSR input
+
+void build_from_csr(Handle &h, sla_itype rit, const void *row_ptr, sla_itype cit, const void *cols,
+                    const void *values, hipStream_t s) {
+    const int64_t n = h.n, nnz = h.nnz_in;
+    Scratch sc(s);
+    int *dflag = sc.get<int>(1);
+    SLA_HIP(hipMemsetAsync(dflag, 0, sizeof(int), s));
+    auto launch = [&](auto rtag, auto ctag) {
+        using RI = std::remove_const_t<std::remove_pointer_t<decltype(rtag)>>;
+        using CI = std::remove_const_t<std::remove_pointer_t<decltype(ctag)>>;
+        hipLaunchKernelGGL((k_csr_check<RI, CI>), dim3(grid_for(n)), dim3(kBlock), 0, s,
+                           (const RI *)row_ptr, (const CI *)cols, n, nnz, dflag);
+    };
+    dispatch_idx(rit, [&](auto r) { dispatch_idx(cit, [&](auto c) { launch(r, c); }); });
+    SLA_HIP(hipGetLastError());
+    const int flags = read_flag(dflag, s);
+    if (flags & kBadCsr)
+        fail(SLA_ERR_INVALID_CSR,
+             "CSR input: row_ptr must run 0..nnz without decreasing and columns must be strictly "
+             "increasing inside each row");
+    if (flags & kBadIndex) fail(SLA_ERR_INDEX_RANGE, "a CSR column index is outside [0, n)");
+
+    h.nnz = nnz;
+    h.rp64 = (rit == SLA_I64);  // CSR input keeps its row-pointer width
+    const size_t rp_bytes = (size_t)(n + 1) * (h.rp64 ? 8 : 4);
+    h.row_ptr = dalloc(h, rp_bytes);
+    SLA_HIP(hipMemcpyAsync(h.row_ptr, row_ptr, rp_bytes, hipMemcpyDeviceToDevice, s));
+    h.col = (int32_t *)dalloc(h, (size_t)(nnz > 0 ? nnz : 1) * 4);
+    if (nnz > 0) {
+        if (cit == SLA_I32)
+            SLA_HIP(hipMemcpyAsync(h.col, cols, (size_t)nnz * 4, hipMemcpyDeviceToDevice, s));
+        else
+            hipLaunchKernelGGL((k_convert<int64_t, int32_t>), dim3(grid_for(nnz)), dim3(kBlock), 0,
+                               s, (const int64_t *)cols, nnz, h.col);
+        SLA_HIP(hipGetLastError());
+    }
+    h.vals = dalloc(h, (size_t)(nnz > 0 ? nnz : 1) * h.B * h.vbytes);
+    load_values(h, values, s);
+}
+
+// values [B][nnz_in] (input order) -> internal [nnz][B]
+void load_values(Handle &h, const void *values, hipStream_t s) {
+    if (h.nnz_in == 0) return;
+    if (!h.perm) {
+        if (h.B == 1)
+            SLA_HIP(hipMemcpyAsync(h.vals, values, (size_t)h.nnz * h.vbytes,
+                                   hipMemcpyDeviceToDevice, s));
+        else
+            transpose(values, h.vals, h.B, h.nnz, h.vbytes, s);
+        return;
+    }
+    const unsigned g = grid_for(h.nnz * h.B);
+    if (h.vt == SLA_F64)
+        hipLaunchKernelGGL(k_merge<double>, dim3(g), dim3(kBlock), 0, s, (const double *)values,
+                           (const int64_t *)h.perm, (const int64_t *)h.run, h.nnz, h.nnz_in, h.B,
+                           (double *)h.vals);
+    else
+        hipLaunchKernelGGL(k_merge<float>, dim3(g), dim3(kBlock), 0, s, (const float *)values,
+                           (const int64_t *)h.perm, (const int64_t *)h.run, h.nnz, h.nnz_in, h.B,
+                           (float *)h.vals);
+    SLA_HIP(hipGetLastError());
+}
+
+// ------------------------------------------------------------------ tiles
+
+void build_tiles(Handle &h, hipStream_t s) {
+    const int64_t n = h.n;
+    Scratch sc(s);
+    int64_t *flag = sc.get<int64_t>(n);
+    int64_t *excl = sc.get<int64_t>(n);
+    if (h.rp64)
+        hipLaunchKernelGGL(k_tile_flags<int64_t>, dim3(grid_for(n)), dim3(kBlock), 0, s,
+                           (const int64_t *)h.row_ptr, n, flag);
+    else
+        hipLaunchKernelGGL(k_tile_flags<int32_t>, dim3(grid_for(n)), dim3(kBlock), 0, s,
+                           (const int32_t *)h.row_ptr, n, flag);
+    SLA_HIP(hipGetLastError());
+    exclusive_scan_i64(flag, excl, n, s);
+    const int64_t nt = read_i64(excl + (n - 1), s) + read_i64(flag + (n - 1), s);
+    h.ntiles = nt;
+    h.tile_start = (int32_t *)dalloc(h, (size_t)(nt + 1) * 4);
+    hipLaunchKernelGGL(k_tile_fill, dim3(grid_for(n)), dim3(kBlock), 0, s, (const int64_t *)flag,
+                       (const int64_t *)excl, n, h.tile_start);
+    SLA_HIP(hipGetLastError());
+    const int32_t nn = (int32_t)n;
+    SLA_HIP(hipMemcpyAsync(h.tile_start + nt, &nn, 4, hipMemcpyHostToDevice, s));
+    SLA_HIP(hipStreamSynchronize(s));
+}
+
+// ------------------------------------------------------------------ Jacobi
+
+void compute_dinv(Handle &h, hipStream_t s) {
+    Scratch sc(s);
+    int *bad = sc.get<int>(1);
+    SLA_HIP(hipMemsetAsync(bad, 0, sizeof(int), s));
+    const unsigned g = grid_for(h.n * h.B);
+    auto go = [&](auto ttag, auto rtag) {
+        using T = decltype(ttag);
+        using RP = decltype(rtag);
+        hipLaunchKernelGGL((k_dinv<T, RP>), dim3(g), dim3(kBlock), 0, s, (const RP *)h.row_ptr,
+                           (const int32_t *)h.col, (const T *)h.vals, h.n, h.B, (T *)h.dinv, bad);
+    };
+    if (h.vt == SLA_F64) {
+        if (h.rp64) go(double(), int64_t());
+        else go(double(), int32_t());
+    } else {
+        if (h.rp64) go(float(), int64_t());
+        else go(float(), int32_t());
+    }
+    SLA_HIP(hipGetLastError());
+    h.diag_ok = read_flag(bad, s) == 0;
+}
+
+bool check_symmetric(Handle &h, hipStream_t s) {
+    Scratch sc(s);
+    int *flag = sc.get<int>(1);
+    SLA_HIP(hipMemsetAsync(flag, 0, sizeof(int), s));
+    const unsigned g = grid_for(h.n);
+    auto go = [&](auto ttag, auto rtag) {
+        using T = decltype(ttag);
+        using RP = decltype(rtag);
+        hipLaunchKernelGGL((k_symmetric<T, RP>), dim3(g), dim3(kBlock), 0, s,
+                           (const RP *)h.row_ptr, (const int32_t *)h.col, (const T *)h.vals, h.n,
+                           h.B, flag);
+    };
+    if (h.vt == SLA_F64) {
+        if (h.rp64) go(double(), int64_t());
+        else go(double(), int32_t());
+    } else {
+        if (h.rp64) go(float(), int64_t());
+        else go(float(), int32_t());
+    }
+    SLA_HIP(hipGetLastError());
+    return read_flag(flag, s) == 0;
+}
+
+void gather_to_input(Handle &h, const void *in, void *out, hipStream_t s) {
+    if (h.nnz_in == 0) return;
+    if (!h.slot) {
+        SLA_HIP(hipMemcpyAsync(out, in, (size_t)h.nnz * h.B * h.vbytes, hipMemcpyDeviceToDevice, s));
+        return;
+    }
+    const unsigned g = grid_for(h.nnz_in * h.B);
+    if (h.vt == SLA_F64)
+        hipLaunchKernelGGL(k_gather<double>, dim3(g), dim3(kBlock), 0, s, (const double *)in,
+                           (const int64_t *)h.slot, h.nnz, h.nnz_in, h.B, (double *)out);
+    else
+        hipLaunchKernelGGL(k_gather<float>, dim3(g), dim3(kBlock), 0, s, (const float *)in,
+                           (const int64_t *)h.slot, h.nnz, h.nnz_in, h.B, (float *)out);
+    SLA_HIP(hipGetLastError());
+}
+
+void values_to_batch_major(Handle &h, void *out, hipStream_t s) {
+    if (h.nnz == 0) return;
+    if (h.B == 1)
+        SLA_HIP(hipMemcpyAsync(out, h.vals, (size_t)h.nnz * h.vbytes, hipMemcpyDeviceToDevice, s));
+    else
+        transpose(h.vals, out, h.nnz, h.B, h.vbytes, s);
+}
+
+}  // namespace sla

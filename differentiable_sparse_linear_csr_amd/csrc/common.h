@@ -1,0 +1,270 @@
+// Internal declarations of the MI355X sparse solve library (gfx950 / CDNA4).
+//
+// Device layout
+//  - CSR: row_ptr (int32 or int64, [n+1]), col (int32, [nnz]), values
+//    entry-major [nnz][B] so that the B value sets of one entry share a cache
+//    line (B = 1: plain [nnz]).
+//  - Solve vectors x, r, p, q and the Jacobi reciprocal dinv are row-major
+//    [n][B] (interleaved): the B systems of one row are contiguous, so the
+//    column gather of a batched SpMV reads one line for all systems.
+//  - Device scalars per system (SysState) and a control block (Ctl) hold
+//    everything the iteration needs; the host only polls a mapped copy of the
+//    number of running systems.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "sla.h"
+
+namespace sla {
+
+constexpr int kBlock = 256;                        // threads per workgroup (4 wave64)
+constexpr int kWaves = kBlock / 64;
+constexpr int kTileUnits = 2048;                   // rows + entries per SpMV tile window
+constexpr int kLongRow = 512;                      // longer rows get a workgroup each
+constexpr int kTileCap = kTileUnits + kLongRow;    // max entries of a short tile
+constexpr int kMaxGrid = 2048;                     // grid cap of grid-stride vector kernels
+constexpr int kMaxBatch = 256;
+
+// per-system status codes on the device: running, or an sla_outcome
+constexpr int32_t kRunning = -1;
+
+struct SysState {
+    double bb;      // ||b||^2
+    double rho;     // r.z of the current residual
+    double alpha;   // step of the current iteration
+    double beta;    // direction update factor
+    double rr;      // ||r||^2 of the last updated residual
+    int32_t iter;   // completed iterations
+    int32_t status; // kRunning or sla_outcome
+};
+
+struct Ctl {
+    double tol;
+    int32_t maxit;
+    int32_t n_running;
+    uint32_t counter[4]; // last-block arrival counters (one per kernel kind)
+};
+
+enum CounterSlot { kCntSpmv = 0, kCntUpdate = 1, kCntInit = 2 };
+
+struct Error {
+    sla_status st;
+    std::string msg;
+};
+
+[[noreturn]] void fail(sla_status st, const std::string &msg);
+
+#define SLA_HIP(expr)                                                                     \
+    do {                                                                                  \
+        hipError_t e_ = (expr);                                                           \
+        if (e_ != hipSuccess) {                                                           \
+            if (e_ == hipErrorOutOfMemory)                                                \
+                ::sla::fail(SLA_ERR_OOM, std::string(#expr) + ": out of device memory");  \
+            ::sla::fail(SLA_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_));  \
+        }                                                                                 \
+    } while (0)
+
+// ------------------------------------------------------------------ handle
+
+struct ProfileRec {
+    int kind;
+    hipEvent_t a, b;
+};
+
+struct Handle {
+    int64_t n = 0, nnz = 0, nnz_in = 0;
+    int32_t B = 1;
+    sla_dtype vt = SLA_F64;
+    int vbytes = 8;
+    bool rp64 = false;       // row_ptr element type
+    uint32_t flags = 0;
+
+    void *row_ptr = nullptr;
+    int32_t *col = nullptr;
+    void *vals = nullptr;    // [nnz][B]
+    int64_t *slot = nullptr; // input entry -> CSR position (null: identity)
+    int64_t *perm = nullptr; // sorted position -> input entry (null: identity)
+    int64_t *run = nullptr;  // [nnz+1] first sorted position of each CSR entry
+    int32_t *tile_start = nullptr;
+    int64_t ntiles = 0;
+    void *dinv = nullptr;    // [n][B]
+    bool diag_ok = false;
+
+    // solve workspace
+    void *x = nullptr, *r = nullptr, *p = nullptr, *q = nullptr; // [n][B]
+    double *part = nullptr;
+    int64_t part_len = 0;
+    SysState *st = nullptr;
+    Ctl *ctl = nullptr;
+    int32_t *h_running = nullptr; // pinned, mapped
+    int32_t *d_running = nullptr; // device alias of h_running
+    SysState *h_state = nullptr;  // pinned
+    Ctl *h_ctl = nullptr;         // pinned staging for the control block
+
+    // iteration driver
+    int check_k = 16;
+    bool use_graph = true;
+    bool profile = false;
+    hipStream_t cap_stream = nullptr;
+    hipGraphExec_t graph = nullptr;
+    int graph_k = 0;
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    int device = 0;
+
+    std::vector<ProfileRec> pending;
+    int64_t prof_launches[SLA_KERNEL_COUNT] = {};
+    double prof_ms[SLA_KERNEL_COUNT] = {};
+
+    int64_t bytes = 0;
+    std::vector<void *> allocs;
+};
+
+// allocation helpers (tracked per handle)
+void *dalloc(Handle &h, size_t bytes);
+void dfree_all(Handle &h);
+
+// ------------------------------------------------------------------ assembly
+void build_from_coo(Handle &h, sla_itype rit, const void *rows, sla_itype cit, const void *cols,
+                    const void *values, hipStream_t s);
+void build_from_csr(Handle &h, sla_itype rit, const void *row_ptr, sla_itype cit, const void *cols,
+                    const void *values, hipStream_t s);
+void load_values(Handle &h, const void *values, hipStream_t s);
+void build_tiles(Handle &h, hipStream_t s);
+void compute_dinv(Handle &h, hipStream_t s);       // sets h.diag_ok (synchronizes)
+bool check_symmetric(Handle &h, hipStream_t s);    // synchronizes
+void gather_to_input(Handle &h, const void *in, void *out, hipStream_t s);
+void values_to_batch_major(Handle &h, void *out, hipStream_t s);
+
+// ------------------------------------------------------------------ utilities
+void exclusive_scan_i64(const int64_t *in, int64_t *out, int64_t m, hipStream_t s);
+void radix_sort_pairs(uint64_t *keys, int64_t *vals, int64_t m, int key_bits, hipStream_t s);
+void transpose(const void *in, void *out, int64_t rows, int64_t cols, int vbytes, hipStream_t s);
+void iota_i64(int64_t *out, int64_t m, hipStream_t s);
+
+// ------------------------------------------------------------------ SpMV / solve
+void spmv(Handle &h, const void *x, void *y, hipStream_t s);
+void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit, sla_info *info,
+         hipStream_t s, bool keep_internal_solution);
+void grad_vals(Handle &h, const void *lam_internal, const void *x_user, void *grad, hipStream_t s);
+void flush_profile(Handle &h);
+
+// ------------------------------------------------------------------ device helpers
+
+__device__ __forceinline__ double wave_sum(double v) {
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Deterministic sum over the 256 threads of a block (fixed shuffle tree inside
+// each wave, then the 4 wave sums in order). Result valid in every thread.
+__device__ __forceinline__ double block_sum(double v, double *lds4) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) lds4[w] = v;
+    __syncthreads();
+    double s = ((lds4[0] + lds4[1]) + lds4[2]) + lds4[3];
+    __syncthreads();
+    return s;
+}
+
+// Rows of a batched layout handled by one block pass: lanes t < J*B, system
+// b = t % B, row offset t / B. J = kBlock / B.
+struct Lanes {
+    int B, J, b, jr;
+    bool on;
+    __device__ Lanes(int B_) : B(B_) {
+        J = kBlock / B;
+        const int t = threadIdx.x;
+        on = t < J * B;
+        b = on ? t % B : 0;
+        jr = on ? t / B : 0;
+    }
+};
+
+// Per-system block reduction of one value per lane (lanes with the same b are
+// summed in a fixed order). Writes out[b] for b < B from threads t < B.
+// tmp must hold kBlock doubles. Ends with a barrier.
+__device__ __forceinline__ void block_sum_per_system(double v, const Lanes &L, double *tmp,
+                                                      double *out) {
+    const int t = threadIdx.x;
+    if ((L.B & (L.B - 1)) == 0 && L.B <= 64) {
+        // power-of-two B: xor offsets >= B keep the system index
+        for (int off = 32; off >= L.B; off >>= 1) v += __shfl_xor(v, off, 64);
+        const int w = t >> 6;
+        if ((t & 63) < L.B) tmp[w * 64 + (t & 63)] = v;
+        __syncthreads();
+        if (t < L.B) {
+            const int nw = (L.J * L.B + 63) / 64;
+            double s = 0.0;
+            for (int k = 0; k < nw; ++k) s += tmp[k * 64 + t];
+            out[t] = s;
+        }
+    } else {
+        tmp[t] = L.on ? v : 0.0;
+        __syncthreads();
+        if (t < L.B) {
+            double s = 0.0;
+            for (int j = 0; j < L.J; ++j) s += tmp[j * L.B + t];
+            out[t] = s;
+        }
+    }
+    __syncthreads();
+}
+
+// Grid-wide combination of per-block partials part[blk][C]. Every block calls
+// it after thread 0 stored the block's C values. Returns true in the block
+// that arrived last; tot[0..C) (shared) then holds the column sums taken in
+// block order (deterministic). The arrival counter is reset for the next launch.
+__device__ __forceinline__ bool last_block_sums(double *part, uint32_t *counter, int64_t nblk,
+                                                int C, double *tmp, double *tot) {
+    __shared__ int s_last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();
+        const uint32_t prev = atomicAdd(counter, 1u);
+        s_last = (prev == (uint32_t)(nblk - 1));
+    }
+    __syncthreads();
+    if (!s_last) return false;
+    __threadfence();
+    const int t = threadIdx.x;
+    const int Cc = C < kBlock ? C : kBlock;
+    const int J = kBlock / Cc;
+    for (int cb = 0; cb < C; cb += Cc) {
+        const int c = cb + t % Cc;
+        const int j0 = t / Cc;
+        double s = 0.0;
+        if (c < C && j0 < J) {
+            const volatile double *vp = part;
+            for (int64_t j = j0; j < nblk; j += J) s += vp[j * C + c];
+        }
+        tmp[t] = s;
+        __syncthreads();
+        if (t < Cc && cb + t < C) {
+            double a = 0.0;
+            for (int k = 0; k < J; ++k) a += tmp[k * Cc + t];
+            tot[cb + t] = a;
+        }
+        __syncthreads();
+    }
+    if (t == 0) *counter = 0u;
+    return true;
+}
+
+__device__ __forceinline__ void publish_running(Ctl *ctl, int32_t *h_running, int32_t v) {
+    ctl->n_running = v;
+    __hip_atomic_store(h_running, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __threadfence_system();
+}
+
+template <typename T>
+__device__ __forceinline__ T from_double(double v) {
+    return static_cast<T>(v);
+}
+
+}  // namespace sla

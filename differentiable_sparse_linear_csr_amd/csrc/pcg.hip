@@ -1,0 +1,401 @@
+// Jacobi-preconditioned CG on the device, its adjoint value gradient, and the
+// host driver that replays blocks of iterations as hipGraphs.
+//
+// torch-sla's pytorch-native backend runs CG with Jacobi preconditioning with
+// every tensor on the device (backend list; distributed-CG paragraph: one
+// SpMV and the two inner products <r,r>, <p,Ap> per iteration; Table 3 and
+// Table 4 text). Backward solves A^T lambda = dL/dx and forms -lambda_i x_j
+// on the stored entries (adjoint paragraph of the distributed section). The
+// recurrence itself is not printed there; this is textbook PCG from x0 = 0:
+//   r = b, z = D^-1 r, p = z, rho = r.z
+//   q = A p, alpha = rho / p.q, x += alpha p, r -= alpha q,
+//   converged when ||r|| <= tol ||b||, else rho' = r.z', beta = rho'/rho,
+//   p = z' + beta p.
+// One iteration is three kernels: the fused SpMV (q and the p.q partials,
+// alpha), the fused update (x, r, and the r.z / r.r partials, the test, beta)
+// and the direction update. Each system's status lives on the device; kernels
+// leave finished systems untouched, so the host can poll every k iterations
+// without changing the iterate or the count.
+#include "common.h"
+
+namespace sla {
+
+void launch_spmv_dot(Handle &h, hipStream_t s);
+void launch_spmv_plain(Handle &h, const void *x, void *y, hipStream_t s);
+
+namespace {
+
+int64_t vec_grid(int64_t n, int B) {
+    const int J = kBlock / B;
+    int64_t g = (n + J - 1) / J;
+    if (g > kMaxGrid) g = kMaxGrid;
+    if (g < 1) g = 1;
+    return g;
+}
+
+// r = b, x = 0, p = z = dinv r; partials of b.b and r.z; last block sets up
+// the per-system scalars and status.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_init(int64_t n, int B, const T *__restrict__ b_in,
+                                                 T *__restrict__ x, T *__restrict__ r,
+                                                 T *__restrict__ p, const T *__restrict__ dinv,
+                                                 double *__restrict__ part, Ctl *__restrict__ ctl,
+                                                 SysState *__restrict__ st,
+                                                 int32_t *__restrict__ h_running) {
+    __shared__ double tmp[kBlock];
+    __shared__ double blk[kMaxBatch];
+    __shared__ double tot[2 * kMaxBatch];
+    const Lanes L(B);
+    double sbb = 0.0, srz = 0.0;
+    if (L.on) {
+        for (int64_t i = (int64_t)blockIdx.x * L.J + L.jr; i < n; i += (int64_t)gridDim.x * L.J) {
+            const int64_t f = i * B + L.b;
+            const T bv = b_in[f];
+            const double z = (double)dinv[f] * (double)bv;
+            x[f] = (T)0;
+            r[f] = bv;
+            p[f] = (T)z;
+            sbb += (double)bv * (double)bv;
+            srz += (double)bv * z;
+        }
+    }
+    block_sum_per_system(sbb, L, tmp, blk);
+    if (threadIdx.x < B) part[(int64_t)blockIdx.x * 2 * B + threadIdx.x] = blk[threadIdx.x];
+    __syncthreads();
+    block_sum_per_system(srz, L, tmp, blk);
+    if (threadIdx.x < B) part[(int64_t)blockIdx.x * 2 * B + B + threadIdx.x] = blk[threadIdx.x];
+    if (last_block_sums(part, &ctl->counter[kCntInit], gridDim.x, 2 * B, tmp, tot)) {
+        if (threadIdx.x == 0) {
+            int running = 0;
+            for (int b = 0; b < B; ++b) {
+                SysState s;
+                s.bb = tot[b];
+                s.rho = tot[B + b];
+                s.alpha = 0.0;
+                s.beta = 0.0;
+                s.rr = s.bb;
+                s.iter = 0;
+                if (s.bb == 0.0) s.status = SLA_CONVERGED;
+                else if (ctl->maxit <= 0) s.status = SLA_MAXIT;
+                else s.status = kRunning;
+                running += s.status == kRunning;
+                st[b] = s;
+            }
+            publish_running(ctl, h_running, running);
+        }
+    }
+}
+
+// x += alpha p, r -= alpha q; partials of r.z and r.r with z = dinv r; the
+// last block applies the stopping test, the iteration budget and beta.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_update(int64_t n, int B, T *__restrict__ x,
+                                                   T *__restrict__ r, const T *__restrict__ p,
+                                                   const T *__restrict__ q,
+                                                   const T *__restrict__ dinv,
+                                                   double *__restrict__ part,
+                                                   Ctl *__restrict__ ctl,
+                                                   SysState *__restrict__ st,
+                                                   int32_t *__restrict__ h_running) {
+    __shared__ double tmp[kBlock];
+    __shared__ double blk[kMaxBatch];
+    __shared__ double tot[2 * kMaxBatch];
+    if (ctl->n_running == 0) return;
+    const Lanes L(B);
+    const bool active = L.on && st[L.b].status == kRunning;
+    const double alpha = L.on ? st[L.b].alpha : 0.0;
+    double srz = 0.0, srr = 0.0;
+    if (active) {
+        for (int64_t i = (int64_t)blockIdx.x * L.J + L.jr; i < n; i += (int64_t)gridDim.x * L.J) {
+            const int64_t f = i * B + L.b;
+            const T xn = (T)((double)x[f] + alpha * (double)p[f]);
+            const T rn = (T)((double)r[f] - alpha * (double)q[f]);
+            x[f] = xn;
+            r[f] = rn;
+            const double z = (double)dinv[f] * (double)rn;
+            srz += (double)rn * z;
+            srr += (double)rn * (double)rn;
+        }
+    }
+    block_sum_per_system(srz, L, tmp, blk);
+    if (threadIdx.x < B) part[(int64_t)blockIdx.x * 2 * B + threadIdx.x] = blk[threadIdx.x];
+    __syncthreads();
+    block_sum_per_system(srr, L, tmp, blk);
+    if (threadIdx.x < B) part[(int64_t)blockIdx.x * 2 * B + B + threadIdx.x] = blk[threadIdx.x];
+    if (last_block_sums(part, &ctl->counter[kCntUpdate], gridDim.x, 2 * B, tmp, tot)) {
+        if (threadIdx.x == 0) {
+            int running = 0;
+            const double tol = ctl->tol;
+            for (int b = 0; b < B; ++b) {
+                SysState &s = st[b];
+                if (s.status != kRunning) continue;
+                const double rz = tot[b], rr = tot[B + b];
+                s.rr = rr;
+                s.iter += 1;
+                if (sqrt(rr) <= tol * sqrt(s.bb)) {
+                    s.status = SLA_CONVERGED;
+                } else if (s.iter >= ctl->maxit) {
+                    s.status = SLA_MAXIT;
+                } else {
+                    s.beta = rz / s.rho;
+                    s.rho = rz;
+                    ++running;
+                }
+            }
+            publish_running(ctl, h_running, running);
+        }
+    }
+}
+
+// p = dinv r + beta p for systems still running
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_direction(int64_t n, int B, const T *__restrict__ r,
+                                                      T *__restrict__ p, const T *__restrict__ dinv,
+                                                      const Ctl *__restrict__ ctl,
+                                                      const SysState *__restrict__ st) {
+    if (ctl->n_running == 0) return;
+    const Lanes L(B);
+    if (!L.on || st[L.b].status != kRunning) return;
+    const double beta = st[L.b].beta;
+    for (int64_t i = (int64_t)blockIdx.x * L.J + L.jr; i < n; i += (int64_t)gridDim.x * L.J) {
+        const int64_t f = i * B + L.b;
+        p[f] = (T)((double)dinv[f] * (double)r[f] + beta * (double)p[f]);
+    }
+}
+
+// grad[b][k] = -lam[row(k)][b] * x[col(k)][b], tile by tile (rows of the
+// tile's entries are recovered through LDS).
+template <typename T, typename RP>
+__global__ __launch_bounds__(kBlock) void k_grad_tile(const int32_t *__restrict__ tile_start,
+                                                      const RP *__restrict__ row_ptr,
+                                                      const int32_t *__restrict__ col, int64_t nnz,
+                                                      int B, const T *__restrict__ lam,
+                                                      const T *__restrict__ x,
+                                                      T *__restrict__ grad) {
+    __shared__ int32_t rowid[kTileCap];
+    const int tid = threadIdx.x;
+    const int64_t t = blockIdx.x;
+    const int32_t rs = tile_start[t], re = tile_start[t + 1];
+    const int64_t k0 = row_ptr[rs], k1 = row_ptr[re];
+    const int64_t nk = k1 - k0;
+    const bool long_tile = (re - rs == 1 && nk > kLongRow);
+    if (!long_tile) {
+        for (int32_t i = rs + tid; i < re; i += kBlock)
+            for (int64_t k = row_ptr[i]; k < (int64_t)row_ptr[i + 1]; ++k) rowid[k - k0] = i;
+        __syncthreads();
+    }
+    for (int b = 0; b < B; ++b) {
+        for (int64_t kk = tid; kk < nk; kk += kBlock) {
+            const int64_t i = long_tile ? rs : rowid[kk];
+            const int64_t k = k0 + kk;
+            const double g = -((double)lam[i * B + b] * (double)x[(int64_t)col[k] * B + b]);
+            grad[(int64_t)b * nnz + k] = (T)g;
+        }
+    }
+}
+
+struct Launcher {
+    Handle &h;
+    hipStream_t s;
+    bool prof;
+    void begin(int kind, hipEvent_t *a) {
+        (void)kind;
+        if (prof) {
+            SLA_HIP(hipEventCreate(a));
+            SLA_HIP(hipEventRecord(*a, s));
+        }
+    }
+    void end(int kind, hipEvent_t a) {
+        if (prof) {
+            hipEvent_t b;
+            SLA_HIP(hipEventCreate(&b));
+            SLA_HIP(hipEventRecord(b, s));
+            h.pending.push_back({kind, a, b});
+        }
+    }
+};
+
+template <typename T>
+void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
+    const int64_t g = vec_grid(h.n, h.B);
+    hipEvent_t a = nullptr;
+    if (lp) lp->begin(SLA_KERNEL_SPMV_DOT, &a);
+    launch_spmv_dot(h, s);
+    if (lp) lp->end(SLA_KERNEL_SPMV_DOT, a);
+    if (lp) lp->begin(SLA_KERNEL_UPDATE, &a);
+    hipLaunchKernelGGL(k_update<T>, dim3((unsigned)g), dim3(kBlock), 0, s, h.n, h.B, (T *)h.x,
+                       (T *)h.r, (const T *)h.p, (const T *)h.q, (const T *)h.dinv, h.part, h.ctl,
+                       h.st, h.d_running);
+    SLA_HIP(hipGetLastError());
+    if (lp) lp->end(SLA_KERNEL_UPDATE, a);
+    if (lp) lp->begin(SLA_KERNEL_DIRECTION, &a);
+    hipLaunchKernelGGL(k_direction<T>, dim3((unsigned)g), dim3(kBlock), 0, s, h.n, h.B,
+                       (const T *)h.r, (T *)h.p, (const T *)h.dinv, (const Ctl *)h.ctl,
+                       (const SysState *)h.st);
+    SLA_HIP(hipGetLastError());
+    if (lp) lp->end(SLA_KERNEL_DIRECTION, a);
+}
+
+void iter_kernels(Handle &h, hipStream_t s, Launcher *lp) {
+    if (h.vt == SLA_F64) iter_kernels_t<double>(h, s, lp);
+    else iter_kernels_t<float>(h, s, lp);
+}
+
+void ensure_graph(Handle &h) {
+    if (h.graph && h.graph_k == h.check_k) return;
+    if (h.graph) {
+        SLA_HIP(hipGraphExecDestroy(h.graph));
+        h.graph = nullptr;
+    }
+    hipGraph_t g = nullptr;
+    SLA_HIP(hipStreamBeginCapture(h.cap_stream, hipStreamCaptureModeThreadLocal));
+    try {
+        for (int k = 0; k < h.check_k; ++k) iter_kernels(h, h.cap_stream, nullptr);
+    } catch (...) {
+        hipGraph_t junk = nullptr;
+        (void)hipStreamEndCapture(h.cap_stream, &junk);
+        if (junk) (void)hipGraphDestroy(junk);
+        throw;
+    }
+    SLA_HIP(hipStreamEndCapture(h.cap_stream, &g));
+    hipGraphExec_t ex = nullptr;
+    const hipError_t e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    SLA_HIP(e);
+    h.graph = ex;
+    h.graph_k = h.check_k;
+}
+
+template <typename T>
+void init_t(Handle &h, const void *b_int, hipStream_t s, Launcher *lp) {
+    const int64_t g = vec_grid(h.n, h.B);
+    hipEvent_t a = nullptr;
+    if (lp) lp->begin(SLA_KERNEL_INIT, &a);
+    hipLaunchKernelGGL(k_init<T>, dim3((unsigned)g), dim3(kBlock), 0, s, h.n, h.B, (const T *)b_int,
+                       (T *)h.x, (T *)h.r, (T *)h.p, (const T *)h.dinv, h.part, h.ctl, h.st,
+                       h.d_running);
+    SLA_HIP(hipGetLastError());
+    if (lp) lp->end(SLA_KERNEL_INIT, a);
+}
+
+}  // namespace
+
+void flush_profile(Handle &h) {
+    for (auto &rec : h.pending) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, rec.a, rec.b) == hipSuccess) {
+            h.prof_launches[rec.kind] += 1;
+            h.prof_ms[rec.kind] += ms;
+        }
+        (void)hipEventDestroy(rec.a);
+        (void)hipEventDestroy(rec.b);
+    }
+    h.pending.clear();
+}
+
+void spmv(Handle &h, const void *x, void *y, hipStream_t s) {
+    Launcher L{h, s, h.profile};
+    hipEvent_t a = nullptr;
+    if (h.B == 1) {
+        L.begin(SLA_KERNEL_SPMV, &a);
+        launch_spmv_plain(h, x, y, s);
+        L.end(SLA_KERNEL_SPMV, a);
+    } else {
+        transpose(x, h.p, h.B, h.n, h.vbytes, s);
+        L.begin(SLA_KERNEL_SPMV, &a);
+        launch_spmv_plain(h, h.p, h.q, s);
+        L.end(SLA_KERNEL_SPMV, a);
+        transpose(h.q, y, h.n, h.B, h.vbytes, s);
+    }
+    if (h.profile) {
+        SLA_HIP(hipStreamSynchronize(s));
+        flush_profile(h);
+    }
+}
+
+// Solve A x = b for every system. b_user / x_user are [B][n]. With
+// keep_internal_solution the iterate stays in h.x (internal layout) and
+// x_user may be null.
+void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit, sla_info *info,
+         hipStream_t s, bool keep_internal_solution) {
+    Launcher L{h, s, h.profile};
+    Launcher *lp = h.profile ? &L : nullptr;
+    // control block: tolerance and budget (the counters stay zero between launches)
+    h.h_ctl->tol = tol;
+    h.h_ctl->maxit = maxit;
+    h.h_ctl->n_running = 0;
+    SLA_HIP(hipMemcpyAsync(h.ctl, h.h_ctl, offsetof(Ctl, counter), hipMemcpyHostToDevice, s));
+    const void *b_int = b_user;
+    if (h.B > 1) {
+        transpose(b_user, h.q, h.B, h.n, h.vbytes, s);  // q is free until the first SpMV
+        b_int = h.q;
+    }
+    if (h.vt == SLA_F64) init_t<double>(h, b_int, s, lp);
+    else init_t<float>(h, b_int, s, lp);
+
+    const bool graph = h.use_graph && !h.profile;
+    if (graph) ensure_graph(h);
+    const int64_t k = h.check_k;
+    const int64_t max_chunks = maxit <= 0 ? 0 : (maxit + k - 1) / k;
+    for (int64_t ch = 0; ch < max_chunks; ++ch) {
+        if (graph) {
+            SLA_HIP(hipGraphLaunch(h.graph, s));
+        } else {
+            for (int64_t j = 0; j < k; ++j) iter_kernels(h, s, lp);
+        }
+        SLA_HIP(hipEventRecord(h.ev[ch & 1], s));
+        // poll the block before this one while this one runs (the GPU never idles)
+        if (ch >= 1) {
+            SLA_HIP(hipEventSynchronize(h.ev[(ch - 1) & 1]));
+            if (__atomic_load_n(h.h_running, __ATOMIC_ACQUIRE) == 0) break;
+        }
+    }
+    if (!keep_internal_solution) {
+        if (h.B == 1)
+            SLA_HIP(hipMemcpyAsync(x_user, h.x, (size_t)h.n * h.vbytes, hipMemcpyDeviceToDevice, s));
+        else
+            transpose(h.x, x_user, h.n, h.B, h.vbytes, s);
+    }
+    SLA_HIP(hipMemcpyAsync(h.h_state, h.st, sizeof(SysState) * h.B, hipMemcpyDeviceToHost, s));
+    SLA_HIP(hipStreamSynchronize(s));
+    if (h.profile) flush_profile(h);
+    for (int b = 0; b < h.B; ++b) {
+        const SysState &st = h.h_state[b];
+        info[b].iterations = st.iter;
+        info[b].status = st.status == kRunning ? SLA_MAXIT : st.status;
+        info[b].rel_residual = st.bb == 0.0 ? 0.0 : sqrt(st.rr / st.bb);
+    }
+}
+
+// grad [B][nnz] (CSR order) from lambda (internal layout, h.x) and the
+// forward solution x_user [B][n].
+void grad_vals(Handle &h, const void *lam_internal, const void *x_user, void *grad, hipStream_t s) {
+    if (h.nnz == 0) return;
+    Launcher L{h, s, h.profile};
+    const void *x_int = x_user;
+    if (h.B > 1) {
+        transpose(x_user, h.p, h.B, h.n, h.vbytes, s);
+        x_int = h.p;
+    }
+    hipEvent_t a = nullptr;
+    L.begin(SLA_KERNEL_GRAD, &a);
+    auto go = [&](auto ttag, auto rtag) {
+        using T = decltype(ttag);
+        using RP = decltype(rtag);
+        hipLaunchKernelGGL((k_grad_tile<T, RP>), dim3((unsigned)h.ntiles), dim3(kBlock), 0, s,
+                           (const int32_t *)h.tile_start, (const RP *)h.row_ptr,
+                           (const int32_t *)h.col, h.nnz, h.B, (const T *)lam_internal,
+                           (const T *)x_int, (T *)grad);
+    };
+    if (h.vt == SLA_F64) {
+        if (h.rp64) go(double(), int64_t());
+        else go(double(), int32_t());
+    } else {
+        if (h.rp64) go(float(), int64_t());
+        else go(float(), int32_t());
+    }
+    SLA_HIP(hipGetLastError());
+    L.end(SLA_KERNEL_GRAD, a);
+}
+
+}  // namespace sla

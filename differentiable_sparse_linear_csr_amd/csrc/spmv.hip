@@ -1,0 +1,196 @@
+// Sparse matrix-vector products for gfx950 (the .matvec of SparseTensor and
+// the q = A p step of CG; torch-sla API section and backend list).
+//
+// Single matrix (B = 1): row-binned CSR. Rows are grouped into tiles of about
+// kTileUnits (rows + entries). A short-row tile streams its entries with
+// coalesced loads, forms val * x[col] in fp64 and parks the products in LDS;
+// the rows are then summed from LDS by groups of G lanes, G picked from the
+// tile's row count (one lane per row for stencil-like rows, up to a whole
+// wave for a few medium rows). A row longer than kLongRow is a tile of its own
+// and gets a full workgroup.
+//
+// Batch sharing one pattern (B > 1): values [nnz][B] and vectors [n][B]; lane
+// (row, b) walks its row, and the B lanes of a row read one index and B
+// consecutive values, so col_idx / row_ptr are read once for all systems.
+//
+// The fused variants also form per-block partials of p.q for the CG step
+// size; the last block to finish reduces them in block order (deterministic)
+// and writes alpha = rho / p.q per system, or flags a breakdown.
+#include "common.h"
+
+namespace sla {
+
+namespace {
+
+__device__ __forceinline__ int group_size(int nrows) {
+    int g = 1;
+    while (g < 64 && g * 2 * nrows <= kBlock) g *= 2;
+    return g;
+}
+
+// Last-block epilogue of the fused SpMV: sigma = p.q per system.
+__device__ __forceinline__ void finish_alpha(double *tot, int B, Ctl *ctl, SysState *st,
+                                             int32_t *h_running) {
+    if (threadIdx.x == 0) {
+        int running = 0;
+        for (int b = 0; b < B; ++b) {
+            SysState &s = st[b];
+            if (s.status != kRunning) continue;
+            const double sigma = tot[b];
+            if (!(sigma > 0.0) || !isfinite(sigma)) {
+                s.status = SLA_BREAKDOWN;
+                s.iter += 1;
+            } else {
+                s.alpha = s.rho / sigma;
+                ++running;
+            }
+        }
+        publish_running(ctl, h_running, running);
+    }
+}
+
+template <typename T, typename RP, bool FUSED>
+__global__ __launch_bounds__(kBlock) void k_spmv_tile(
+    const int32_t *__restrict__ tile_start, const RP *__restrict__ row_ptr,
+    const int32_t *__restrict__ col, const T *__restrict__ val, const T *__restrict__ x,
+    T *__restrict__ y, int64_t ntiles, double *__restrict__ part, Ctl *__restrict__ ctl,
+    SysState *__restrict__ st, int32_t *__restrict__ h_running) {
+    __shared__ double prod[kTileCap];
+    __shared__ double lds4[kWaves];
+    __shared__ double tmp[kBlock];
+    __shared__ double tot[1];
+    if (FUSED && st[0].status != kRunning) return;
+
+    const int tid = threadIdx.x;
+    const int64_t t = blockIdx.x;
+    const int32_t rs = tile_start[t], re = tile_start[t + 1];
+    const int64_t k0 = row_ptr[rs], k1 = row_ptr[re];
+    double dot = 0.0;
+
+    if (re - rs == 1 && k1 - k0 > kLongRow) {
+        double s = 0.0;
+        for (int64_t k = k0 + tid; k < k1; k += kBlock) s += (double)val[k] * (double)x[col[k]];
+        s = block_sum(s, lds4);
+        if (tid == 0) {
+            const T q = (T)s;
+            y[rs] = q;
+            if (FUSED) dot = (double)x[rs] * (double)q;
+        }
+    } else {
+        const int nk = (int)(k1 - k0);
+        for (int j = tid; j < nk; j += kBlock)
+            prod[j] = (double)val[k0 + j] * (double)x[col[k0 + j]];
+        __syncthreads();
+        const int nrows = re - rs;
+        const int G = group_size(nrows);
+        const int lg = tid & (G - 1);
+        const int grp = tid / G;
+        const int ngrp = kBlock / G;
+        for (int i = rs + grp; i < re; i += ngrp) {
+            const int a = (int)(row_ptr[i] - k0), b = (int)(row_ptr[i + 1] - k0);
+            double s = 0.0;
+            for (int j = a + lg; j < b; j += G) s += prod[j];
+            for (int off = G >> 1; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+            if (lg == 0) {
+                const T q = (T)s;
+                y[i] = q;
+                if (FUSED) dot += (double)x[i] * (double)q;
+            }
+        }
+    }
+    if (FUSED) {
+        dot = block_sum(dot, lds4);
+        if (tid == 0) part[t] = dot;
+        if (last_block_sums(part, &ctl->counter[kCntSpmv], ntiles, 1, tmp, tot))
+            finish_alpha(tot, 1, ctl, st, h_running);
+    }
+}
+
+template <typename T, typename RP, bool FUSED>
+__global__ __launch_bounds__(kBlock) void k_spmv_batched(
+    int64_t n, int B, int rows_per_lane, const RP *__restrict__ row_ptr,
+    const int32_t *__restrict__ col, const T *__restrict__ val, const T *__restrict__ x,
+    T *__restrict__ y, double *__restrict__ part, Ctl *__restrict__ ctl,
+    SysState *__restrict__ st, int32_t *__restrict__ h_running) {
+    __shared__ double tmp[kBlock];
+    __shared__ double tot[kMaxBatch];
+    __shared__ double blk[kMaxBatch];
+    if (FUSED && ctl->n_running == 0) return;
+    const Lanes L(B);
+    const bool active = L.on && (!FUSED || st[L.b].status == kRunning);
+    double dot = 0.0;
+    const int64_t row0 = (int64_t)blockIdx.x * L.J * rows_per_lane;
+    if (active) {
+        for (int j = 0; j < rows_per_lane; ++j) {
+            const int64_t i = row0 + (int64_t)j * L.J + L.jr;
+            if (i >= n) break;
+            const int64_t ka = row_ptr[i], kb = row_ptr[i + 1];
+            double s = 0.0;
+            for (int64_t k = ka; k < kb; ++k)
+                s += (double)val[k * B + L.b] * (double)x[(int64_t)col[k] * B + L.b];
+            const T q = (T)s;
+            y[i * B + L.b] = q;
+            if (FUSED) dot += (double)x[i * B + L.b] * (double)q;
+        }
+    }
+    if (FUSED) {
+        block_sum_per_system(dot, L, tmp, blk);
+        if (threadIdx.x < B) part[(int64_t)blockIdx.x * B + threadIdx.x] = blk[threadIdx.x];
+        if (last_block_sums(part, &ctl->counter[kCntSpmv], gridDim.x, B, tmp, tot))
+            finish_alpha(tot, B, ctl, st, h_running);
+    }
+}
+
+template <typename T, typename RP, bool FUSED>
+void launch_spmv_t(Handle &h, const void *x, void *y, hipStream_t s) {
+    if (h.B == 1) {
+        hipLaunchKernelGGL((k_spmv_tile<T, RP, FUSED>), dim3((unsigned)h.ntiles), dim3(kBlock), 0,
+                           s, (const int32_t *)h.tile_start, (const RP *)h.row_ptr,
+                           (const int32_t *)h.col, (const T *)h.vals, (const T *)x, (T *)y,
+                           h.ntiles, h.part, h.ctl, h.st, h.d_running);
+    } else {
+        const int J = kBlock / h.B;
+        int rpl = 1;
+        while ((h.n + (int64_t)J * rpl - 1) / ((int64_t)J * rpl) > kMaxGrid && rpl < 1024) rpl *= 2;
+        const int64_t grid = (h.n + (int64_t)J * rpl - 1) / ((int64_t)J * rpl);
+        hipLaunchKernelGGL((k_spmv_batched<T, RP, FUSED>), dim3((unsigned)grid), dim3(kBlock), 0,
+                           s, h.n, h.B, rpl, (const RP *)h.row_ptr, (const int32_t *)h.col,
+                           (const T *)h.vals, (const T *)x, (T *)y, h.part, h.ctl, h.st,
+                           h.d_running);
+    }
+    SLA_HIP(hipGetLastError());
+}
+
+}  // namespace
+
+int64_t spmv_grid(const Handle &h) {
+    if (h.B == 1) return h.ntiles;
+    const int J = kBlock / h.B;
+    int rpl = 1;
+    while ((h.n + (int64_t)J * rpl - 1) / ((int64_t)J * rpl) > kMaxGrid && rpl < 1024) rpl *= 2;
+    return (h.n + (int64_t)J * rpl - 1) / ((int64_t)J * rpl);
+}
+
+// q = A p on the solve workspace, fused with the p.q partials and alpha.
+void launch_spmv_dot(Handle &h, hipStream_t s) {
+    if (h.vt == SLA_F64) {
+        if (h.rp64) launch_spmv_t<double, int64_t, true>(h, h.p, h.q, s);
+        else launch_spmv_t<double, int32_t, true>(h, h.p, h.q, s);
+    } else {
+        if (h.rp64) launch_spmv_t<float, int64_t, true>(h, h.p, h.q, s);
+        else launch_spmv_t<float, int32_t, true>(h, h.p, h.q, s);
+    }
+}
+
+// plain y = A x, both in internal layout ([n][B])
+void launch_spmv_plain(Handle &h, const void *x, void *y, hipStream_t s) {
+    if (h.vt == SLA_F64) {
+        if (h.rp64) launch_spmv_t<double, int64_t, false>(h, x, y, s);
+        else launch_spmv_t<double, int32_t, false>(h, x, y, s);
+    } else {
+        if (h.rp64) launch_spmv_t<float, int64_t, false>(h, x, y, s);
+        else launch_spmv_t<float, int32_t, false>(h, x, y, s);
+    }
+}
+
+}  // namespace sla

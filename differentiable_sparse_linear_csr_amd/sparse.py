@@ -1,0 +1,279 @@
+"""Python face of the library: a CSR matrix handle (one matrix or a batch of
+value sets sharing one pattern) with .matvec and a differentiable .solve.
+
+Mirrors torch-sla's SparseTensor (tensor-types passage of its API section) and
+its autograd wrapping (forward runs the solver and keeps (A, x); backward runs
+the adjoint solve; autograd-wrapping paragraph). PyTorch supplies device
+memory and the current stream; every step runs in libsla.so.
+"""
+from __future__ import annotations
+
+import ctypes
+import warnings
+from typing import List, Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import Info, check
+
+_VT = {torch.float32: _lib.SLA_F32, torch.float64: _lib.SLA_F64}
+_IT = {torch.int32: _lib.SLA_I32, torch.int64: _lib.SLA_I64}
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[ctypes.c_void_p]:
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_cuda(t: torch.Tensor, what: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+class SolveInfo:
+    """Per-system outcome of a solve."""
+
+    def __init__(self, infos: List[Info]):
+        self.iterations = [int(i.iterations) for i in infos]
+        self.status = [int(i.status) for i in infos]
+        self.rel_residual = [float(i.rel_residual) for i in infos]
+
+    def __repr__(self) -> str:
+        names = {0: "converged", 1: "maxit", 2: "breakdown"}
+        return (f"SolveInfo(iterations={self.iterations}, "
+                f"status={[names.get(s, s) for s in self.status]}, "
+                f"rel_residual={self.rel_residual})")
+
+
+class SparseCSR:
+    """A CSR matrix (or a batch of value sets on one pattern) on the GPU.
+
+    Build with :meth:`from_coo` or :meth:`from_csr`. ``values`` is [nnz] for
+    one matrix or [batch, nnz] for a batch; vectors are [n] or [batch, n].
+    """
+
+    def __init__(self, handle: ctypes.c_void_p, device: torch.device, dtype: torch.dtype):
+        self._h = handle
+        self.device = device
+        self.dtype = dtype
+        L = _lib.load()
+        n, nnz, nnz_in = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        batch, vt, rit = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        rp, ci, sl = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
+        check(L.sla_csr_get(self._h, ctypes.byref(n), ctypes.byref(nnz), ctypes.byref(nnz_in),
+                            ctypes.byref(batch), ctypes.byref(vt), ctypes.byref(rit),
+                            ctypes.byref(rp), ctypes.byref(ci), ctypes.byref(sl)))
+        self.n, self.nnz, self.nnz_in, self.batch = n.value, nnz.value, nnz_in.value, batch.value
+        self.row_index_dtype = torch.int64 if rit.value == _lib.SLA_I64 else torch.int32
+        self._values_ref: Optional[torch.Tensor] = None
+        self.last_info: Optional[SolveInfo] = None
+        self.last_adjoint_info: Optional[SolveInfo] = None
+
+    # ------------------------------------------------------------------ construction
+    @classmethod
+    def _create(cls, fmt, n, nnz_in, batch, a, b, values, check_symmetric):
+        L = _lib.load()
+        dev = values.device
+        h = ctypes.c_void_p()
+        flags = _lib.SLA_FLAG_CHECK_SYMMETRIC if check_symmetric else 0
+        with torch.cuda.device(dev):
+            check(L.sla_csr_create(ctypes.byref(h), fmt, n, nnz_in, batch, _IT[a.dtype], _ptr(a),
+                                   _IT[b.dtype], _ptr(b), _VT[values.dtype], _ptr(values), flags,
+                                   _stream(dev)))
+        obj = cls(h, dev, values.dtype)
+        obj._values_ref = values
+        return obj
+
+    @classmethod
+    def from_coo(cls, row: torch.Tensor, col: torch.Tensor, values: torch.Tensor, n: int,
+                 check_symmetric: bool = False) -> "SparseCSR":
+        """COO triples; duplicates are summed in input order (stable (row, col) order)."""
+        for t, w in ((row, "row"), (col, "col"), (values, "values")):
+            _need_cuda(t, w)
+        if values.dtype not in _VT or row.dtype not in _IT or col.dtype not in _IT:
+            raise TypeError("values must be float32/float64 and indices int32/int64")
+        nnz_in = row.shape[0]
+        batch = 1 if values.dim() == 1 else values.shape[0]
+        if col.shape[0] != nnz_in or values.shape[-1] != nnz_in:
+            raise ValueError("row, col and values disagree on the number of entries")
+        return cls._create(_lib.SLA_INPUT_COO, int(n), nnz_in, batch, row, col, values,
+                           check_symmetric)
+
+    @classmethod
+    def from_csr(cls, row_ptr: torch.Tensor, col: torch.Tensor, values: torch.Tensor,
+                 check_symmetric: bool = False) -> "SparseCSR":
+        """CSR arrays (columns strictly increasing inside each row), adopted as is."""
+        for t, w in ((row_ptr, "row_ptr"), (col, "col"), (values, "values")):
+            _need_cuda(t, w)
+        if values.dtype not in _VT or row_ptr.dtype not in _IT or col.dtype not in _IT:
+            raise TypeError("values must be float32/float64 and indices int32/int64")
+        n = row_ptr.shape[0] - 1
+        batch = 1 if values.dim() == 1 else values.shape[0]
+        return cls._create(_lib.SLA_INPUT_CSR, n, col.shape[0], batch, row_ptr, col, values,
+                           check_symmetric)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            try:
+                _lib.load().sla_csr_destroy(h)
+            except Exception:
+                pass
+            self._h = None
+
+    # ------------------------------------------------------------------ accessors
+    def _vec_shape(self) -> Tuple[int, ...]:
+        return (self.n,) if self.batch == 1 else (self.batch, self.n)
+
+    def _check_vec(self, v: torch.Tensor, what: str) -> None:
+        _need_cuda(v, what)
+        if v.dtype != self.dtype:
+            raise TypeError(f"{what} must have dtype {self.dtype}")
+        if tuple(v.shape) != self._vec_shape():
+            raise ValueError(f"{what} must have shape {self._vec_shape()}, got {tuple(v.shape)}")
+
+    def set_values(self, values: torch.Tensor) -> None:
+        _need_cuda(values, "values")
+        exp = (self.nnz_in,) if self.batch == 1 else (self.batch, self.nnz_in)
+        if values.dtype != self.dtype or tuple(values.shape) != exp:
+            raise ValueError(f"values must be {self.dtype} of shape {exp}")
+        check(_lib.load().sla_csr_set_values(self._h, _ptr(values), _stream(self.device)))
+        self._values_ref = values
+
+    def csr(self) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+        """Copies of (row_ptr, col_idx, values[batch?, nnz]) in CSR order."""
+        L = _lib.load()
+        row_ptr = torch.empty(self.n + 1, dtype=self.row_index_dtype, device=self.device)
+        col = torch.empty(max(self.nnz, 1), dtype=torch.int32, device=self.device)
+        vals = torch.empty((self.batch, max(self.nnz, 1)), dtype=self.dtype, device=self.device)
+        s = _stream(self.device)
+        check(L.sla_csr_get_pattern(self._h, _ptr(row_ptr), _ptr(col), None, s))
+        check(L.sla_csr_get_values(self._h, _ptr(vals), s))
+        col, vals = col[:self.nnz], vals[:, :self.nnz]
+        return row_ptr, col, (vals[0] if self.batch == 1 else vals)
+
+    def slot(self) -> torch.Tensor:
+        """input entry -> CSR position (int64 [nnz_in])."""
+        out = torch.empty(max(self.nnz_in, 1), dtype=torch.int64, device=self.device)
+        check(_lib.load().sla_csr_get_pattern(self._h, None, None, _ptr(out),
+                                              _stream(self.device)))
+        return out[:self.nnz_in]
+
+    def set_option(self, key: int, value: int) -> None:
+        check(_lib.load().sla_csr_set_option(self._h, key, int(value)))
+
+    def memory_bytes(self) -> int:
+        b = ctypes.c_int64()
+        check(_lib.load().sla_csr_memory(self._h, ctypes.byref(b)))
+        return b.value
+
+    def profile(self) -> dict:
+        L = _lib.load()
+        out = {}
+        for name, k in _lib.KERNELS.items():
+            n, ms = ctypes.c_int64(), ctypes.c_double()
+            check(L.sla_profile_get(self._h, k, ctypes.byref(n), ctypes.byref(ms)))
+            out[name] = (n.value, ms.value)
+        return out
+
+    def profile_reset(self) -> None:
+        check(_lib.load().sla_profile_reset(self._h))
+
+    # ------------------------------------------------------------------ operations
+    def matvec(self, x: torch.Tensor) -> torch.Tensor:
+        """y = A x (no autograd)."""
+        self._check_vec(x, "x")
+        y = torch.empty_like(x)
+        check(_lib.load().sla_spmv(self._h, _ptr(x), _ptr(y), _stream(self.device)))
+        return y
+
+    def solve_raw(self, b: torch.Tensor, tol: float = 1e-10, maxit: int = 10000,
+                  out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, SolveInfo]:
+        """x = A^{-1} b by Jacobi-PCG (no autograd). Returns (x, info)."""
+        self._check_vec(b, "b")
+        x = torch.empty_like(b) if out is None else out
+        infos = (Info * self.batch)()
+        check(_lib.load().sla_pcg_solve(self._h, _ptr(b), _ptr(x), float(tol), int(maxit), infos,
+                                        _stream(self.device)))
+        info = SolveInfo(list(infos))
+        self.last_info = info
+        return x, info
+
+    def adjoint_raw(self, x: torch.Tensor, grad_x: torch.Tensor, tol: float = 1e-10,
+                    maxit: int = 10000, want_b: bool = True, want_vals: bool = True):
+        """(grad_b [like x] or None, grad_vals [batch?, nnz] in CSR order or None, info)."""
+        self._check_vec(x, "x")
+        self._check_vec(grad_x, "grad_x")
+        gb = torch.empty_like(x) if want_b else None
+        gv = None
+        if want_vals:
+            shape = (self.nnz,) if self.batch == 1 else (self.batch, self.nnz)
+            gv = torch.empty(shape, dtype=self.dtype, device=self.device)
+        infos = (Info * self.batch)()
+        check(_lib.load().sla_adjoint_backward(self._h, _ptr(x), _ptr(grad_x), _ptr(gb), _ptr(gv),
+                                               float(tol), int(maxit), infos,
+                                               _stream(self.device)))
+        info = SolveInfo(list(infos))
+        self.last_adjoint_info = info
+        return gb, gv, info
+
+    def gather_to_input(self, csr_order: torch.Tensor) -> torch.Tensor:
+        """[batch?, nnz] CSR order -> [batch?, nnz_in] input order (via the slot map)."""
+        shape = (self.nnz_in,) if self.batch == 1 else (self.batch, self.nnz_in)
+        out = torch.empty(shape, dtype=self.dtype, device=self.device)
+        check(_lib.load().sla_csr_gather_to_input(self._h, _ptr(csr_order), _ptr(out),
+                                                  _stream(self.device)))
+        return out
+
+    def solve(self, b: torch.Tensor, values: Optional[torch.Tensor] = None, tol: float = 1e-10,
+              maxit: int = 10000, adjoint_tol: Optional[float] = None) -> torch.Tensor:
+        """Differentiable x = A^{-1} b: gradients flow to ``b`` and to ``values``
+        (the input-order value tensor this handle was built or last set with,
+        or the one passed here, which is loaded into the handle)."""
+        vals = self._values_ref if values is None else values
+        return _SolveFn.apply(self, vals, b, float(tol), int(maxit),
+                              float(tol if adjoint_tol is None else adjoint_tol))
+
+
+def _report(info: SolveInfo, what: str) -> None:
+    if any(s == _lib.SLA_BREAKDOWN for s in info.status):
+        raise FloatingPointError(f"{what}: PCG breakdown (p.Ap <= 0: matrix not SPD?) {info}")
+    if any(s == _lib.SLA_MAXIT for s in info.status):
+        warnings.warn(f"{what}: iteration budget reached before the tolerance {info}",
+                      RuntimeWarning, stacklevel=3)
+
+
+class _SolveFn(torch.autograd.Function):
+    """One autograd node per solve (independent of the iteration count)."""
+
+    @staticmethod
+    def forward(ctx, A: SparseCSR, values: torch.Tensor, b: torch.Tensor, tol: float, maxit: int,
+                adjoint_tol: float):
+        if values is not None and values is not A._values_ref:
+            A.set_values(values.detach())
+        x, info = A.solve_raw(b.detach(), tol, maxit)
+        _report(info, "solve")
+        ctx.A = A
+        ctx.tol, ctx.maxit = adjoint_tol, maxit
+        ctx.save_for_backward(x)
+        return x
+
+    @staticmethod
+    def backward(ctx, grad_x: torch.Tensor):
+        (x,) = ctx.saved_tensors
+        A: SparseCSR = ctx.A
+        want_vals = ctx.needs_input_grad[1]
+        want_b = ctx.needs_input_grad[2]
+        if not (want_vals or want_b):
+            return None, None, None, None, None, None
+        gb, gv, info = A.adjoint_raw(x, grad_x.contiguous(), ctx.tol, ctx.maxit, want_b=True,
+                                     want_vals=want_vals)
+        _report(info, "adjoint solve")
+        g_vals = A.gather_to_input(gv) if want_vals else None
+        return None, g_vals, (gb if want_b else None), None, None, None

@@ -1,0 +1,201 @@
+/*
+ * sla.h — C ABI of the MI355X sparse solve library: CSR assembly, SpMV,
+ * Jacobi-preconditioned CG and its adjoint backward, for one matrix or a
+ * batch of matrices sharing one sparsity pattern.
+ *
+ * What the calls compute follows torch-sla ("Differentiable Sparse Linear
+ * Algebra with Adjoint Solvers and Sparse Tensor Parallelism for PyTorch",
+ * arXiv 2601.13994):
+ *  - a SparseTensor holds one matrix or a batch sharing one pattern, and
+ *    exposes .matvec and .solve (tensor-types passage of its API section);
+ *  - the pytorch-native backend solves SPD systems by CG with Jacobi
+ *    preconditioning, all tensors staying on the device (backend list; the
+ *    distributed-CG paragraph; Table 3 and Table 4 text);
+ *  - the solve is wrapped as one autograd node whose backward solves
+ *    A^T lambda = dL/dx and forms the matrix gradient -lambda_i x_j on the
+ *    stored entries (autograd-wrapping paragraph; adjoint paragraph of the
+ *    distributed section, result of its Section 3.2; Figure 2 discussion).
+ *
+ * Conventions shared by every call
+ *  - Pointers are DEVICE pointers unless marked (host). Device arrays are
+ *    contiguous. Batched vectors are batch-major: [batch][n]; batched values
+ *    are [batch][nnz].
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
+ *    is ordered on it. Calls on one handle must not overlap (the handle owns
+ *    one solve workspace).
+ *  - Ownership: the library copies what it keeps; the caller keeps ownership
+ *    of every argument pointer, and nothing is retained after a call returns.
+ *    A handle owns its device memory, allocated at create; solves allocate
+ *    nothing on the device.
+ *  - Errors: every call returns an sla_status and never aborts or throws;
+ *    sla_last_error() gives a message for the calling thread's last failure.
+ *    Solver outcomes are reported per system in sla_info, not as errors.
+ *  - Limits: 1 <= n < 2^31, 1 <= batch <= 256, nnz < 2^62.
+ */
+#ifndef SLA_H
+#define SLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sla_csr_s *sla_csr; /* opaque handle */
+
+typedef enum {
+    SLA_OK = 0,
+    SLA_ERR_INVALID_ARG = 1,   /* null pointer, bad enum, size out of range */
+    SLA_ERR_INDEX_RANGE = 2,   /* a row or column index outside [0, n) */
+    SLA_ERR_INVALID_CSR = 3,   /* CSR input: row_ptr not 0..nnz non-decreasing, or columns
+                                  not strictly increasing inside a row */
+    SLA_ERR_NOT_SYMMETRIC = 4, /* SLA_FLAG_CHECK_SYMMETRIC given and A != A^T bit for bit */
+    SLA_ERR_BAD_DIAGONAL = 5,  /* solve on a matrix with a missing, non-positive or
+                                  non-finite diagonal entry (Jacobi needs d_i > 0) */
+    SLA_ERR_OOM = 6,           /* device or pinned-host allocation failed */
+    SLA_ERR_HIP = 7            /* a HIP runtime call failed */
+} sla_status;
+
+typedef enum { SLA_F32 = 0, SLA_F64 = 1 } sla_dtype;
+typedef enum { SLA_I32 = 0, SLA_I64 = 1 } sla_itype;
+typedef enum { SLA_INPUT_COO = 0, SLA_INPUT_CSR = 1 } sla_format;
+
+enum { SLA_FLAG_CHECK_SYMMETRIC = 1u };
+
+/* per-system outcome of a solve */
+typedef enum { SLA_CONVERGED = 0, SLA_MAXIT = 1, SLA_BREAKDOWN = 2 } sla_outcome;
+
+typedef struct {
+    int32_t iterations;   /* iterations performed (the one that met the test counts) */
+    int32_t status;       /* sla_outcome */
+    double rel_residual;  /* ||r_k||_2 / ||b||_2 of the recursively updated residual;
+                             0 when b = 0 */
+} sla_info;
+
+/* options for sla_csr_set_option */
+enum {
+    SLA_OPT_CHECK_INTERVAL = 1, /* iterations per host poll of the convergence flag (>= 1,
+                                   default 16); results do not depend on it */
+    SLA_OPT_USE_GRAPH = 2,      /* 1 (default): replay the polled iteration block as a
+                                   hipGraph; 0: launch kernels one by one */
+    SLA_OPT_PROFILE = 3         /* 1: time every kernel launch of later calls with hipEvents
+                                   (implies eager launches); 0 (default): off */
+};
+
+/* kernel kinds reported by sla_profile_get */
+enum {
+    SLA_KERNEL_SPMV_DOT = 0,  /* q = A p fused with the per-block p.q partials and alpha */
+    SLA_KERNEL_UPDATE = 1,    /* x += alpha p, r -= alpha q, r.z and r.r partials, beta, test */
+    SLA_KERNEL_DIRECTION = 2, /* p = z + beta p */
+    SLA_KERNEL_INIT = 3,      /* r = b, x = 0, p = z, b.b and r.z */
+    SLA_KERNEL_SPMV = 4,      /* plain y = A x */
+    SLA_KERNEL_GRAD = 5,      /* grad_vals[k] = -lambda[row k] x[col k] */
+    SLA_KERNEL_COUNT = 6
+};
+
+/*
+ * Build a handle from COO triples or CSR arrays (SparseTensor construction).
+ *  fmt = SLA_INPUT_COO: rows_or_row_ptr and cols are [nnz_in] index arrays of
+ *    itypes row_itype / col_itype. Entries are ordered by (row, col) with a
+ *    stable sort, and entries at one position are summed left to right in
+ *    input order, in the value type. The resulting CSR is bit-identical for
+ *    any thread/launch configuration.
+ *  fmt = SLA_INPUT_CSR: rows_or_row_ptr is row_ptr [n+1] (row_itype), cols is
+ *    [nnz_in] with columns strictly increasing inside each row; it is
+ *    validated and adopted as is.
+ *  values: [batch][nnz_in] of vtype, in input order.
+ *  flags: SLA_FLAG_CHECK_SYMMETRIC rejects matrices that are not bitwise
+ *    symmetric (for every value set).
+ * Synchronizes `stream` before returning (validation results are read back).
+ * On failure *out is set to NULL.
+ */
+sla_status sla_csr_create(sla_csr *out, sla_format fmt, int64_t n, int64_t nnz_in, int32_t batch,
+                          sla_itype row_itype, const void *rows_or_row_ptr,
+                          sla_itype col_itype, const void *cols,
+                          sla_dtype vtype, const void *values, uint32_t flags, void *stream);
+
+/* Replace the values (same pattern, same input order and count as at create):
+ * values [batch][nnz_in] of the handle's vtype. Duplicate positions are merged
+ * exactly as at create. Synchronizes `stream`. */
+sla_status sla_csr_set_values(sla_csr h, const void *values, void *stream);
+
+/* Shapes and the handle's index arrays (host outputs; any may be NULL).
+ * row_ptr has itype *row_itype (SLA_I32 when nnz < 2^31 for COO input, else
+ * the input's), col_idx is int32 [nnz]. slot (int64 [nnz_in]) maps input entry
+ * e to the CSR position it was merged into; it is NULL when that map is the
+ * identity (sorted, duplicate-free input). The pointers stay valid until
+ * destroy and must not be written. */
+sla_status sla_csr_get(sla_csr h, int64_t *n, int64_t *nnz, int64_t *nnz_in, int32_t *batch,
+                       int32_t *vtype, int32_t *row_itype, const void **row_ptr,
+                       const void **col_idx, const int64_t **slot);
+
+/* Copy the pattern into caller buffers (any may be NULL): row_ptr_out [n+1]
+ * of the handle's row itype, col_idx_out int32 [nnz], slot_out int64 [nnz_in]
+ * (written as 0..nnz_in-1 when the map is the identity). Asynchronous. */
+sla_status sla_csr_get_pattern(sla_csr h, void *row_ptr_out, void *col_idx_out, int64_t *slot_out,
+                               void *stream);
+
+/* Copy the CSR values out as [batch][nnz] (CSR order) of the handle's vtype. */
+sla_status sla_csr_get_values(sla_csr h, void *values_out, void *stream);
+
+/* Gather a CSR-ordered array [batch][nnz] to input order [batch][nnz_in]:
+ * out[b][e] = in[b][slot[e]] (duplicates each receive their merged entry's value). */
+sla_status sla_csr_gather_to_input(sla_csr h, const void *csr_order, void *input_order,
+                                   void *stream);
+
+sla_status sla_csr_set_option(sla_csr h, int32_t key, int64_t value);
+
+/* Sparse matrix-vector product y = A x for every batch member (.matvec).
+ * x, y: [batch][n] of the handle's vtype; must not alias. fp32 handles form
+ * products and sums in fp64 and round once. Asynchronous. */
+sla_status sla_spmv(sla_csr h, const void *x, void *y, void *stream);
+
+/*
+ * Jacobi-preconditioned CG from x0 = 0 for every batch member (.solve):
+ *   r = b, z = D^-1 r, p = z; per iteration q = A p, alpha = r.z / p.q,
+ *   x += alpha p, r -= alpha q, stop when ||r|| <= tol ||b||, else
+ *   beta = r'.z' / r.z, p = z' + beta p.
+ * Each system stops on its own test; p.q <= 0 or non-finite ends it with
+ * SLA_BREAKDOWN (A not SPD). b, x: [batch][n]; info: host [batch].
+ * maxit >= 0, tol >= 0 (tol = 0 runs exactly maxit iterations).
+ * Returns SLA_ERR_BAD_DIAGONAL if some d_i is missing, <= 0 or not finite.
+ * fp32 handles store vectors in fp32 and compute in fp64.
+ * Blocks the host until the solve has finished (info is filled).
+ */
+sla_status sla_pcg_solve(sla_csr h, const void *b, void *x, double tol, int32_t maxit,
+                         sla_info *info, void *stream);
+
+/*
+ * Adjoint backward of x = A^{-1} b for upstream grad_x = dL/dx: solves
+ * A lambda = grad_x with the same PCG (A symmetric, so A^T = A), then
+ *   grad_b = lambda                                  ([batch][n], or NULL)
+ *   grad_vals[b][k] = -lambda[b][row(k)] * x[b][col(k)] ([batch][nnz] in CSR
+ *                                                        order, or NULL)
+ * x is the forward solution [batch][n]. info (host [batch]) reports the
+ * adjoint solve. Blocks the host until done.
+ */
+sla_status sla_adjoint_backward(sla_csr h, const void *x, const void *grad_x, void *grad_b,
+                                void *grad_vals, double tol, int32_t maxit, sla_info *info,
+                                void *stream);
+
+/* Accumulated kernel timings of calls made while SLA_OPT_PROFILE was on
+ * (host outputs): number of launches and total milliseconds per kind. */
+sla_status sla_profile_get(sla_csr h, int32_t kind, int64_t *launches, double *total_ms);
+sla_status sla_profile_reset(sla_csr h);
+
+/* Device bytes owned by the handle (matrix, index maps, solve workspace). */
+sla_status sla_csr_memory(sla_csr h, int64_t *bytes);
+
+void sla_csr_destroy(sla_csr h);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char *sla_last_error(void);
+
+/* Library version string. */
+const char *sla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLA_H */

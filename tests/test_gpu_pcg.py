@@ -1,0 +1,198 @@
+"""GPU Jacobi-PCG and adjoint versus the oracle at sizes the oracle finishes in
+seconds (several tiles and ragged tails): iterations within +-2, fp64
+solution within 1e-8 relative (fp32 storage: 1e-4), outcomes, exactness of
+the k-interval host poll, determinism, and the autograd path."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from differentiable_sparse_linear_csr_amd import _lib, SlaError
+from workloads import adversarial, make_workload, poisson2d_coo
+
+from gpu_util import coo_handle, csr_handle, dev, host, rel
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ("poisson2d_64", None, None),
+    ("diffusion3d_128", 24, None),
+    ("knn_laplacian_2m", 20000, None),
+    ("batched_diffusion2d_512x32", 48, 6),
+]
+
+
+def oracle_solve(w):
+    ref = oracle.coo_to_csr(w.n, w.rows, w.cols, w.vals)
+    x, it, rl, oc = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], w.b, w.tol, w.maxit)
+    return ref, x, np.atleast_1d(it), np.atleast_1d(rl), np.atleast_1d(oc)
+
+
+@pytest.mark.parametrize("name,size,batch", CASES)
+def test_solve_matches_oracle(name, size, batch):
+    w = make_workload(name, size=size, batch=batch)
+    print(f"pcg {name} n={w.n} nnz={w.nnz} batch={w.batch}", flush=True)
+    ref, xo, ito, rlo, oco = oracle_solve(w)
+    A = coo_handle(w.n, w.rows, w.cols, w.vals)
+    x, info = A.solve_raw(dev(w.b), w.tol, w.maxit)
+    xg = np.atleast_2d(host(x))
+    xo = np.atleast_2d(xo)
+    xtol = 1e-8 if w.dtype == "f64" else 1e-4
+    for s in range(w.batch):
+        assert info.status[s] == oco[s] == oracle.CONVERGED
+        assert abs(info.iterations[s] - ito[s]) <= 2, (s, info.iterations[s], ito[s])
+        assert rel(xg[s], xo[s]) <= xtol, (s, rel(xg[s], xo[s]))
+        assert info.rel_residual[s] <= w.tol
+        if info.iterations[s] == ito[s]:
+            assert abs(info.rel_residual[s] - rlo[s]) <= 1e-3 * rlo[s]
+
+
+@pytest.mark.parametrize("name,size,batch", CASES)
+def test_adjoint_matches_oracle(name, size, batch):
+    w = make_workload(name, size=size, batch=batch)
+    ref, xo, *_ = oracle_solve(w)
+    lam_o, gv_o, it_o, rl_o, oc_o = oracle.adjoint(ref["row_ptr"], ref["col"], ref["vals"], xo, w.g,
+                                                   w.tol, w.maxit)
+    A = coo_handle(w.n, w.rows, w.cols, w.vals)
+    x, _ = A.solve_raw(dev(w.b), w.tol, w.maxit)
+    gb, gv, info = A.adjoint_raw(x, dev(w.g), w.tol, w.maxit)
+    tol = 1e-8 if w.dtype == "f64" else 1e-3
+    gb, gv = np.atleast_2d(host(gb)), np.atleast_2d(host(gv))
+    lam_o, gv_o = np.atleast_2d(lam_o), np.atleast_2d(gv_o)
+    it_o = np.atleast_1d(it_o)
+    for s in range(w.batch):
+        assert abs(info.iterations[s] - it_o[s]) <= 2
+        assert rel(gb[s], lam_o[s]) <= tol
+        assert rel(gv[s], gv_o[s]) <= tol
+
+
+def test_check_interval_and_graph_do_not_change_results():
+    w = make_workload("diffusion3d_128", size=20)
+    A = coo_handle(w.n, w.rows, w.cols, w.vals)
+    b = dev(w.b)
+    outs = []
+    for k, graph in [(1, 1), (7, 1), (16, 1), (64, 1), (16, 0)]:
+        A.set_option(_lib.SLA_OPT_CHECK_INTERVAL, k)
+        A.set_option(_lib.SLA_OPT_USE_GRAPH, graph)
+        x, info = A.solve_raw(b, w.tol, w.maxit)
+        outs.append((host(x).tobytes(), info.iterations[0], info.rel_residual[0]))
+    assert all(o == outs[0] for o in outs)
+
+
+def test_batched_slices_equal_single_solves():
+    w = make_workload("batched_diffusion2d_512x32", size=32, batch=4)
+    A = coo_handle(w.n, w.rows, w.cols, w.vals)
+    X, info = A.solve_raw(dev(w.b), w.tol, w.maxit)
+    for s in range(4):
+        As = coo_handle(w.n, w.rows, w.cols, np.ascontiguousarray(w.vals[s]))
+        xs, inf_s = As.solve_raw(dev(w.b[s]), w.tol, w.maxit)
+        assert inf_s.iterations[0] == info.iterations[s]
+        assert rel(host(xs), host(X[s])) <= 1e-5
+
+
+def test_outcomes():
+    r, c, v = poisson2d_coo(30)
+    A = coo_handle(900, r, c, v)
+    b = np.random.default_rng(0).standard_normal(900)
+    x, info = A.solve_raw(dev(np.zeros(900)), 1e-10, 100)
+    assert info.iterations[0] == 0 and info.status[0] == _lib.SLA_CONVERGED
+    assert not host(x).any() and info.rel_residual[0] == 0.0
+    x, info = A.solve_raw(dev(b), 1e-10, 0)
+    assert info.iterations[0] == 0 and info.status[0] == _lib.SLA_MAXIT and not host(x).any()
+    ref = oracle.coo_to_csr(900, r, c, v)
+    for maxit in (1, 3, 17):
+        x, info = A.solve_raw(dev(b), 1e-14, maxit)
+        xo, ito, rlo, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, 1e-14, maxit)
+        assert info.iterations[0] == ito == maxit and info.status[0] == _lib.SLA_MAXIT
+        assert rel(host(x), xo) <= 1e-12
+        assert abs(info.rel_residual[0] - rlo) <= 1e-12 * rlo
+    x, info = A.solve_raw(dev(b), 0.0, 50)
+    assert info.iterations[0] == 50 and info.status[0] == _lib.SLA_MAXIT
+    # indefinite -> breakdown at the first step, x untouched
+    A2 = coo_handle(2, np.array([0, 0, 1, 1]), np.array([0, 1, 0, 1]), np.array([1.0, 2, 2, 1]))
+    x, info = A2.solve_raw(dev(np.array([1.0, -1.0])), 1e-10, 10)
+    assert info.status[0] == _lib.SLA_BREAKDOWN and info.iterations[0] == 1 and not host(x).any()
+    # bad diagonal -> error
+    v2 = v.copy()
+    v2[(r == 7) & (c == 7)] = 0.0
+    A3 = coo_handle(900, r, c, v2)
+    with pytest.raises(SlaError) as e:
+        A3.solve_raw(dev(b), 1e-10, 10)
+    assert e.value.status == _lib.SLA_ERR_BAD_DIAGONAL
+
+
+def test_batched_mixed_outcomes():
+    # systems finish at different iterations; zero rhs and budget limits per system
+    w = make_workload("batched_diffusion2d_512x32", size=20, batch=5)
+    b = w.b.copy()
+    b[2] = 0.0
+    A = coo_handle(w.n, w.rows, w.cols, w.vals)
+    ref = oracle.coo_to_csr(w.n, w.rows, w.cols, w.vals)
+    x, info = A.solve_raw(dev(b), w.tol, 40)
+    xo, ito, rlo, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, w.tol, 40)
+    for s in range(5):
+        assert info.status[s] == oco[s]
+        assert abs(info.iterations[s] - ito[s]) <= 2
+        assert rel(host(x[s]), xo[s]) <= 1e-4
+    assert info.iterations[2] == 0 and info.status[2] == _lib.SLA_CONVERGED
+
+
+def test_irregular_spd_with_long_rows_and_duplicates():
+    n = 40000
+    r, c, v = adversarial.random_spd_coo(n, 10.0, 13, max_row=30000)
+    r, c, v = adversarial.split_duplicates(r, c, v, seed=3)
+    ref = oracle.coo_to_csr(n, r, c, v)
+    b = np.random.default_rng(1).standard_normal(n)
+    xo, ito, rlo, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, 1e-10, 5000)
+    A = coo_handle(n, r, c, v)
+    x, info = A.solve_raw(dev(b), 1e-10, 5000)
+    assert abs(info.iterations[0] - ito) <= 2 and rel(host(x), xo) <= 1e-8
+
+
+def test_int64_row_ptr_path():
+    w = make_workload("poisson2d_11548", size=90)
+    rows = np.repeat(np.arange(w.n), np.diff(w.row_ptr))
+    ref = oracle.coo_to_csr(w.n, rows, w.cols, w.vals)
+    xo, ito, rlo, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], w.b, 1e-10, 2000)
+    A = csr_handle(w.row_ptr, w.cols, w.vals, rp_dtype=torch.int64)
+    assert A.row_index_dtype == torch.int64
+    x, info = A.solve_raw(dev(w.b), 1e-10, 2000)
+    assert abs(info.iterations[0] - ito) <= 2 and rel(host(x), xo) <= 1e-8
+    # fixed budget, tol 0 (as the large-grid workload runs)
+    x, info = A.solve_raw(dev(w.b), 0.0, 25)
+    xo, ito, rlo, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], w.b, 0.0, 25)
+    assert info.iterations[0] == 25 and rel(host(x), xo) <= 1e-12
+    assert abs(info.rel_residual[0] - rlo) <= 1e-10 * rlo
+
+
+def test_repeatable_bitwise():
+    w = make_workload("knn_laplacian_2m", size=10000)
+    A = coo_handle(w.n, w.rows, w.cols, w.vals)
+    b = dev(w.b)
+    x1, i1 = A.solve_raw(b, w.tol, w.maxit)
+    x2, i2 = A.solve_raw(b, w.tol, w.maxit)
+    assert host(x1).tobytes() == host(x2).tobytes() and i1.iterations == i2.iterations
+
+
+def test_autograd_through_solve_with_duplicates():
+    n = 3000
+    r, c, v = adversarial.random_spd_coo(n, 6.0, 21)
+    r, c, v = adversarial.split_duplicates(r, c, v, seed=7)
+    rng = np.random.default_rng(4)
+    b, g = rng.standard_normal(n), rng.standard_normal(n)
+    A = coo_handle(n, r, c, v)
+    vals = dev(v).requires_grad_(True)
+    bt = dev(b).requires_grad_(True)
+    x = A.solve(bt, values=vals, tol=1e-12, maxit=5000)
+    (x * dev(g)).sum().backward()
+    ref = oracle.coo_to_csr(n, r, c, v)
+    xo, *_ = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, 1e-12, 5000)
+    lam, gv, *_ = oracle.adjoint(ref["row_ptr"], ref["col"], ref["vals"], xo, g, 1e-12, 5000)
+    assert rel(host(bt.grad), lam) <= 1e-9
+    # every duplicate receives the gradient of the entry it was merged into
+    assert rel(host(vals.grad), gv[ref["slot"]]) <= 1e-9
+    # new values through the same handle
+    v2 = v * 1.5
+    vals2 = dev(v2).requires_grad_(True)
+    x2 = A.solve(dev(b), values=vals2, tol=1e-12, maxit=5000)
+    assert rel(host(x2), xo / 1.5) <= 1e-9

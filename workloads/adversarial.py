@@ -55,7 +55,13 @@ def rows_of_lengths(lengths, ncols: int, seed: int, index_dtype=np.int64):
             continue
         if L > ncols:
             raise ValueError("row longer than the number of columns")
-        c = np.sort(rng.choice(ncols, size=L, replace=False))
+        if 4 * L < ncols:
+            c = np.unique(rng.integers(0, ncols, 2 * L + 8))
+            while c.size < L:
+                c = np.unique(np.concatenate([c, rng.integers(0, ncols, L)]))
+            c = np.sort(rng.permutation(c)[:L])
+        else:
+            c = np.sort(rng.choice(ncols, size=L, replace=False))
         rows.append(np.full(L, i, dtype=np.int64))
         cols.append(c.astype(np.int64))
     if rows:
