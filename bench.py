@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Throughput of the differentiable Jacobi-PCG path on one MI355X.
+
+A step is one pass of the whole hot path over the workload's matrix:
+  sla_csr_set_values  (values in input order -> CSR values, Jacobi reciprocal)
+  sla_pcg_solve       (Jacobi-PCG to the workload's tolerance / budget)
+  sla_adjoint_backward(adjoint solve + value gradient), for workloads with one
+The handle (pattern, tiles, workspace) is built once before timing, as the
+pattern is shared by every step. Inputs are resident in HBM before timing.
+
+value = PCG iterations (forward + adjoint) per second over the timed steps.
+
+Printed as one JSON line. `roofline` covers the dominant kernel (the fused
+SpMV + p.q kernel): its algorithmic bytes per launch over its average launch
+duration, timed with hipEvents by the library on the stream it launches on
+during one profiled step that follows the timed steps. `cpu_baseline` times
+the CPU oracle on a bounded sample of the same solve.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Jacobi-PCG iterations/sec and achieved HBM GB/s (% of peak) at 2M and 133M DOF"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "diffusion3d_128"
+KERNEL_SOURCES = ["spmv.hip", "common.h"]
+
+
+def algorithmic_bytes(n, nnz, B, V, R):
+    """Bytes one launch must move at minimum (each array touched once)."""
+    spmv = V * nnz * B + 4 * nnz + R * (n + 1) + 2 * V * n * B   # vals, cols, row_ptr, p in, q out
+    matrix = V * nnz * B + 4 * nnz + R * (n + 1)
+    return {
+        "spmv": spmv,
+        "iter_3k": matrix + 13 * V * n * B,   # fused SpMV (2 vectors) + update (7) + direction (4)
+        "iter_min": matrix + 7 * V * n * B,
+        "grad": 4 * nnz + R * (n + 1) + V * nnz * B + 2 * V * n * B,
+    }
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "differentiable_sparse_linear_csr_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """Per-launch HBM bytes of the fused SpMV from rocprofv3 counters, if they
+    were taken on the current kernel source (profiles/counters_<workload>.json)."""
+    path = os.path.join(ROOT, "profiles", f"spmv_dot_counters_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle as it stands, on the host cores: iterations/s of the forward
+    Jacobi-PCG on the same matrix and right-hand side, over a bounded number of
+    iterations (the first ones of the same solve)."""
+    import numpy as np
+    import oracle
+
+    rows = w.rows if w.rows is not None else np.repeat(np.arange(w.n), np.diff(w.row_ptr))
+    ref = oracle.coo_to_csr(w.n, rows, w.cols, w.vals)
+    vals = ref["vals"]
+    b = w.b
+    t0 = time.perf_counter()
+    oracle.pcg(ref["row_ptr"], ref["col"], vals, b, 0.0, 5)
+    probe = (time.perf_counter() - t0) / 5
+    iters = int(max(5, min(w.maxit, budget_s / max(probe, 1e-9))))
+    t0 = time.perf_counter()
+    _, it, _, _ = oracle.pcg(ref["row_ptr"], ref["col"], vals, b, 0.0, iters)
+    dt = time.perf_counter() - t0
+    it = int(np.sum(it))
+    per_sys = w.batch
+    return {"value": it / dt, "unit": "iterations/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"first {iters} Jacobi-PCG iterations (tol 0) of the forward solve of "
+                      f"{w.name} ({per_sys} system(s)), oracle CSR built from the same COO input; "
+                      f"{dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--check-interval", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library's path runs on a single MI355X "
+              "(multi-GPU sharding is described in DESIGN.md, not built). Use --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import differentiable_sparse_linear_csr_amd as sla
+    from differentiable_sparse_linear_csr_amd import _lib
+    from workloads import make_workload
+
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    w = make_workload(args.workload)
+    print(f"[bench] workload {w.name}: n={w.n} nnz={w.nnz} batch={w.batch} dtype={w.dtype} "
+          f"(generated in {time.perf_counter() - t_gen:.1f} s)", file=sys.stderr, flush=True)
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    cols = d(w.cols)
+    vals = d(w.vals)
+    b = d(w.b)
+    g = d(w.g) if w.adjoint else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if w.fmt == "coo":
+        A = sla.SparseCSR.from_coo(d(w.rows), cols, vals, w.n)
+    else:
+        A = sla.SparseCSR.from_csr(d(w.row_ptr), cols, vals)
+    torch.cuda.synchronize()
+    create_ms = (time.perf_counter() - t0) * 1e3
+    A.set_option(_lib.SLA_OPT_CHECK_INTERVAL, args.check_interval)
+    x = torch.empty_like(b)
+
+    def step():
+        A.set_values(vals)
+        _, info = A.solve_raw(b, w.tol, w.maxit, out=x)
+        its = sum(info.iterations)
+        if w.adjoint:
+            _, _, ainfo = A.adjoint_raw(x, g, w.tol, w.maxit)
+            its += sum(ainfo.iterations)
+        return its, info
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    total_its = 0
+    for _ in range(args.steps):
+        its, info = step()
+        total_its += its
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    value = total_its / elapsed
+    ms_per_step = elapsed / args.steps * 1e3
+    fwd_its = info.iterations
+
+    # profiled step: hipEvents around every kernel launch, on the launch stream
+    A.profile_reset()
+    A.set_option(_lib.SLA_OPT_PROFILE, 1)
+    step()
+    prof = A.profile()
+    A.set_option(_lib.SLA_OPT_PROFILE, 0)
+
+    V = 8 if w.dtype == "f64" else 4
+    R = 8 if A.row_index_dtype == torch.int64 else 4
+    ab = algorithmic_bytes(w.n, w.nnz, w.batch, V, R)
+    launches, total_ms = prof["spmv_dot"]
+    avg_ms = total_ms / max(launches, 1)
+    achieved = ab["spmv"] / (avg_ms * 1e-3) / 1e9
+    traffic = load_traffic(w.name)
+    per_iter_ms = sum(prof[k][1] for k in ("spmv_dot", "update", "direction")) / max(launches, 1)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "iterations/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "description": w.description,
+            "n": w.n, "nnz": w.nnz, "batch": w.batch,
+            "row_ptr": "int64" if R == 8 else "int32", "col_idx": "int32",
+            "tol": w.tol, "maxit": w.maxit,
+            "step": "set_values + pcg_solve" + (" + adjoint_backward" if w.adjoint else ""),
+            "forward_iterations": fwd_its,
+            "check_interval": args.check_interval,
+        },
+        "roofline": {
+            "kernel": "k_spmv_tile (fused q = A p, p.q partials, alpha)" if w.batch == 1
+            else "k_spmv_batched (fused q = A p, p.q partials, alpha)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": ab["spmv"],
+            "avg_launch_ms": round(avg_ms, 5),
+            "launches_timed": launches,
+        },
+        "extra": {
+            "create_ms": round(create_ms, 2),
+            "iteration_ms": round(per_iter_ms, 5),
+            "iteration_gbps_3k": round(ab["iter_3k"] / (per_iter_ms * 1e-3) / 1e9, 1),
+            "iteration_frac_3k": round(ab["iter_3k"] / (per_iter_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "spmv_gflops": round(2 * w.nnz * w.batch / (avg_ms * 1e-3) / 1e9, 1),
+            "kernel_avg_ms": {k: round(v[1] / max(v[0], 1), 5) for k, v in prof.items() if v[0]},
+            "handle_bytes": A.memory_bytes(),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

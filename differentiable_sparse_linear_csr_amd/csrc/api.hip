@@ -90,6 +90,9 @@ void alloc_workspace(Handle &h, hipStream_t s) {
     if (vec_part > plen) plen = vec_part;
     h.part_len = plen;
     h.part = (double *)dalloc(h, (size_t)plen * sizeof(double));
+    h.gpart = (double *)dalloc(h, (size_t)kGroups * 2 * kMaxBatch * sizeof(double));
+    h.sync = (uint32_t *)dalloc(h, (size_t)kCntKinds * kCountersPerKind * sizeof(uint32_t));
+    SLA_HIP(hipMemsetAsync(h.sync, 0, (size_t)kCntKinds * kCountersPerKind * sizeof(uint32_t), s));
     h.st = (SysState *)dalloc(h, sizeof(SysState) * h.B);
     h.ctl = (Ctl *)dalloc(h, sizeof(Ctl));
     SLA_HIP(hipMemsetAsync(h.ctl, 0, sizeof(Ctl), s));

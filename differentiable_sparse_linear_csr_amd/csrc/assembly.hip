@@ -169,6 +169,15 @@ __global__ __launch_bounds__(kBlock) void k_tile_fill(const int64_t *__restrict_
         if (flag[i]) tile_start[excl[i]] = (int32_t)i;
 }
 
+template <typename RP>
+__global__ __launch_bounds__(kBlock) void k_tile_k0(const RP *__restrict__ row_ptr,
+                                                   const int32_t *__restrict__ tile_start,
+                                                   int64_t nt, int64_t *__restrict__ tile_k0) {
+    for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t <= nt;
+         t += (int64_t)gridDim.x * kBlock)
+        tile_k0[t] = (int64_t)row_ptr[tile_start[t]];
+}
+
 // dinv[i][b] = 1 / A_ii (IEEE division; fp32 storage: formed in fp64, rounded
 // once). Missing, non-positive or non-finite diagonals are counted.
 template <typename T, typename RP>
@@ -483,6 +492,16 @@ void build_tiles(Handle &h, hipStream_t s) {
     SLA_HIP(hipGetLastError());
     const int32_t nn = (int32_t)n;
     SLA_HIP(hipMemcpyAsync(h.tile_start + nt, &nn, 4, hipMemcpyHostToDevice, s));
+    h.tile_k0 = (int64_t *)dalloc(h, (size_t)(nt + 1) * 8);
+    if (h.rp64)
+        hipLaunchKernelGGL(k_tile_k0<int64_t>, dim3(grid_for(nt + 1)), dim3(kBlock), 0, s,
+                           (const int64_t *)h.row_ptr, (const int32_t *)h.tile_start, nt,
+                           h.tile_k0);
+    else
+        hipLaunchKernelGGL(k_tile_k0<int32_t>, dim3(grid_for(nt + 1)), dim3(kBlock), 0, s,
+                           (const int32_t *)h.row_ptr, (const int32_t *)h.tile_start, nt,
+                           h.tile_k0);
+    SLA_HIP(hipGetLastError());
     SLA_HIP(hipStreamSynchronize(s));
 }
 

@@ -27,7 +27,7 @@ constexpr int kWaves = kBlock / 64;
 constexpr int kTileUnits = 2048;                   // rows + entries per SpMV tile window
 constexpr int kLongRow = 512;                      // longer rows get a workgroup each
 constexpr int kTileCap = kTileUnits + kLongRow;    // max entries of a short tile
-constexpr int kMaxGrid = 2048;                     // grid cap of grid-stride vector kernels
+constexpr int kMaxGrid = 2048;                     // grid cap of the persistent / grid-stride kernels
 constexpr int kMaxBatch = 256;
 
 // per-system status codes on the device: running, or an sla_outcome
@@ -47,10 +47,15 @@ struct Ctl {
     double tol;
     int32_t maxit;
     int32_t n_running;
-    uint32_t counter[4]; // last-block arrival counters (one per kernel kind)
 };
 
-enum CounterSlot { kCntSpmv = 0, kCntUpdate = 1, kCntInit = 2 };
+// Arrival counters of the grid reductions: per kernel kind, kGroups group
+// counters and one top counter, each on its own 256-byte line so that
+// arrivals at different counters do not serialize.
+constexpr int kGroups = 32;
+constexpr int kCounterStride = 64;                       // uint32 per line
+constexpr int kCountersPerKind = (kGroups + 1) * kCounterStride;
+enum CounterSlot { kCntSpmv = 0, kCntUpdate = 1, kCntInit = 2, kCntKinds = 3 };
 
 struct Error {
     sla_status st;
@@ -99,6 +104,9 @@ struct Handle {
     void *x = nullptr, *r = nullptr, *p = nullptr, *q = nullptr; // [n][B]
     double *part = nullptr;
     int64_t part_len = 0;
+    double *gpart = nullptr;      // [kGroups][C] group sums of the grid reductions
+    uint32_t *sync = nullptr;     // [kCntKinds][kCountersPerKind] arrival counters
+    int64_t *tile_k0 = nullptr;   // [ntiles+1] first entry of each tile
     SysState *st = nullptr;
     Ctl *ctl = nullptr;
     int32_t *h_running = nullptr; // pinned, mapped
@@ -216,50 +224,102 @@ __device__ __forceinline__ void block_sum_per_system(double v, const Lanes &L, d
     __syncthreads();
 }
 
-// Grid-wide combination of per-block partials part[blk][C]. Every block calls
-// it after thread 0 stored the block's C values. Returns true in the block
-// that arrived last; tot[0..C) (shared) then holds the column sums taken in
-// block order (deterministic). The arrival counter is reset for the next launch.
-__device__ __forceinline__ bool last_block_sums(double *part, uint32_t *counter, int64_t nblk,
-                                                int C, double *tmp, double *tot) {
-    __shared__ int s_last;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();
-        const uint32_t prev = atomicAdd(counter, 1u);
-        s_last = (prev == (uint32_t)(nblk - 1));
-    }
-    __syncthreads();
-    if (!s_last) return false;
-    __threadfence();
+// Cross-block partials go through device-scope atomic stores and loads
+// (written through to the device coherence point), so no L2 writeback is
+// needed: a block stores its partials with store_partial(), every thread
+// waits for its own stores to complete, then one thread bumps the arrival
+// counter. The block that arrives last reads all partials back with
+// device-scope loads.
+__device__ __forceinline__ void store_partial(double *p, double v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ double load_partial(const double *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Column sums of rows [j0, j1) of a [rows][C] partial table, in row order,
+// read with device-scope loads (8 in flight per lane). Result in out[0..C).
+__device__ __forceinline__ void sum_rows(const double *part, int64_t j0, int64_t j1, int C,
+                                         double *tmp, double *out) {
     const int t = threadIdx.x;
     const int Cc = C < kBlock ? C : kBlock;
     const int J = kBlock / Cc;
     for (int cb = 0; cb < C; cb += Cc) {
         const int c = cb + t % Cc;
-        const int j0 = t / Cc;
+        const int r0 = t / Cc;
         double s = 0.0;
-        if (c < C && j0 < J) {
-            const volatile double *vp = part;
-            for (int64_t j = j0; j < nblk; j += J) s += vp[j * C + c];
+        if (c < C && r0 < J) {
+            for (int64_t j = j0 + r0; j < j1; j += 8 * (int64_t)J) {
+                double v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int64_t jj = j + (int64_t)u * J;
+                    v[u] = jj < j1 ? load_partial(part + jj * C + c) : 0.0;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) s += v[u];
+            }
         }
         tmp[t] = s;
         __syncthreads();
         if (t < Cc && cb + t < C) {
             double a = 0.0;
             for (int k = 0; k < J; ++k) a += tmp[k * Cc + t];
-            tot[cb + t] = a;
+            out[cb + t] = a;
         }
         __syncthreads();
     }
-    if (t == 0) *counter = 0u;
+}
+
+// Arrive at a device-scope counter after this block's partial stores have
+// completed; true in the block whose arrival is number `expected`.
+__device__ __forceinline__ bool arrive(uint32_t *counter, uint32_t expected) {
+    __shared__ int s_last;
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev =
+            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == expected - 1);
+        if (s_last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    return s_last;
+}
+
+// Grid-wide combination of per-block partials part[blk][C] (C <= 2*kMaxBatch).
+// Every block calls it after its threads stored the block's C values with
+// store_partial(). Blocks are split into kGroups contiguous groups; the last
+// block of a group sums the group's rows (block order) into gpart[g][C]; the
+// last group to finish sums the group rows (group order) into tot[0..C)
+// (shared) and returns true. The summation tree depends only on nblk, so the
+// result is deterministic. Counters are reset for the next launch.
+__device__ __forceinline__ bool last_block_sums(double *part, double *gpart, uint32_t *counters,
+                                                int64_t nblk, int C, double *tmp, double *tot) {
+    const int64_t gb = (nblk + kGroups - 1) / kGroups;   // blocks per group
+    const int64_t ngroups = (nblk + gb - 1) / gb;
+    const int64_t g = blockIdx.x / gb;
+    const int64_t j0 = g * gb;
+    const int64_t j1 = (j0 + gb < nblk) ? j0 + gb : nblk;
+    if (!arrive(counters + g * kCounterStride, (uint32_t)(j1 - j0))) return false;
+    sum_rows(part, j0, j1, C, tmp, tot);
+    for (int c = threadIdx.x; c < C; c += kBlock) store_partial(gpart + g * C + c, tot[c]);
+    if (!arrive(counters + kGroups * kCounterStride, (uint32_t)ngroups)) return false;
+    sum_rows(gpart, 0, ngroups, C, tmp, tot);
     return true;
 }
+
+// Where a kernel's grid reduction keeps its partials and counters.
+struct Red {
+    double *part;
+    double *gpart;
+    uint32_t *sync;  // this kernel kind's kCountersPerKind counters
+};
 
 __device__ __forceinline__ void publish_running(Ctl *ctl, int32_t *h_running, int32_t v) {
     ctl->n_running = v;
     __hip_atomic_store(h_running, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    __threadfence_system();
 }
 
 template <typename T>

@@ -25,9 +25,11 @@ void launch_spmv_plain(Handle &h, const void *x, void *y, hipStream_t s);
 
 namespace {
 
+constexpr int kVecItems = 4;  // rows per lane and pass (loads issued together)
+
 int64_t vec_grid(int64_t n, int B) {
-    const int J = kBlock / B;
-    int64_t g = (n + J - 1) / J;
+    const int64_t rows = (int64_t)(kBlock / B) * kVecItems;
+    int64_t g = (n + rows - 1) / rows;
     if (g > kMaxGrid) g = kMaxGrid;
     if (g < 1) g = 1;
     return g;
@@ -39,7 +41,7 @@ template <typename T>
 __global__ __launch_bounds__(kBlock) void k_init(int64_t n, int B, const T *__restrict__ b_in,
                                                  T *__restrict__ x, T *__restrict__ r,
                                                  T *__restrict__ p, const T *__restrict__ dinv,
-                                                 double *__restrict__ part, Ctl *__restrict__ ctl,
+                                                 Red red, Ctl *__restrict__ ctl,
                                                  SysState *__restrict__ st,
                                                  int32_t *__restrict__ h_running) {
     __shared__ double tmp[kBlock];
@@ -48,23 +50,38 @@ __global__ __launch_bounds__(kBlock) void k_init(int64_t n, int B, const T *__re
     const Lanes L(B);
     double sbb = 0.0, srz = 0.0;
     if (L.on) {
-        for (int64_t i = (int64_t)blockIdx.x * L.J + L.jr; i < n; i += (int64_t)gridDim.x * L.J) {
-            const int64_t f = i * B + L.b;
-            const T bv = b_in[f];
-            const double z = (double)dinv[f] * (double)bv;
-            x[f] = (T)0;
-            r[f] = bv;
-            p[f] = (T)z;
-            sbb += (double)bv * (double)bv;
-            srz += (double)bv * z;
+        const int64_t step = (int64_t)gridDim.x * L.J * kVecItems;
+        for (int64_t base = (int64_t)blockIdx.x * L.J * kVecItems + L.jr; base < n; base += step) {
+            T bv[kVecItems], dv[kVecItems];
+#pragma unroll
+            for (int u = 0; u < kVecItems; ++u) {
+                const int64_t i = base + (int64_t)u * L.J;
+                const int64_t f = i * B + L.b;
+                bv[u] = i < n ? b_in[f] : (T)0;
+                dv[u] = i < n ? dinv[f] : (T)0;
+            }
+#pragma unroll
+            for (int u = 0; u < kVecItems; ++u) {
+                const int64_t i = base + (int64_t)u * L.J;
+                if (i >= n) break;
+                const int64_t f = i * B + L.b;
+                const double z = (double)dv[u] * (double)bv[u];
+                x[f] = (T)0;
+                r[f] = bv[u];
+                p[f] = (T)z;
+                sbb += (double)bv[u] * (double)bv[u];
+                srz += (double)bv[u] * z;
+            }
         }
     }
     block_sum_per_system(sbb, L, tmp, blk);
-    if (threadIdx.x < B) part[(int64_t)blockIdx.x * 2 * B + threadIdx.x] = blk[threadIdx.x];
+    if (threadIdx.x < B)
+        store_partial(red.part + (int64_t)blockIdx.x * 2 * B + threadIdx.x, blk[threadIdx.x]);
     __syncthreads();
     block_sum_per_system(srz, L, tmp, blk);
-    if (threadIdx.x < B) part[(int64_t)blockIdx.x * 2 * B + B + threadIdx.x] = blk[threadIdx.x];
-    if (last_block_sums(part, &ctl->counter[kCntInit], gridDim.x, 2 * B, tmp, tot)) {
+    if (threadIdx.x < B)
+        store_partial(red.part + (int64_t)blockIdx.x * 2 * B + B + threadIdx.x, blk[threadIdx.x]);
+    if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, 2 * B, tmp, tot)) {
         if (threadIdx.x == 0) {
             int running = 0;
             for (int b = 0; b < B; ++b) {
@@ -92,8 +109,7 @@ template <typename T>
 __global__ __launch_bounds__(kBlock) void k_update(int64_t n, int B, T *__restrict__ x,
                                                    T *__restrict__ r, const T *__restrict__ p,
                                                    const T *__restrict__ q,
-                                                   const T *__restrict__ dinv,
-                                                   double *__restrict__ part,
+                                                   const T *__restrict__ dinv, Red red,
                                                    Ctl *__restrict__ ctl,
                                                    SysState *__restrict__ st,
                                                    int32_t *__restrict__ h_running) {
@@ -106,23 +122,43 @@ __global__ __launch_bounds__(kBlock) void k_update(int64_t n, int B, T *__restri
     const double alpha = L.on ? st[L.b].alpha : 0.0;
     double srz = 0.0, srr = 0.0;
     if (active) {
-        for (int64_t i = (int64_t)blockIdx.x * L.J + L.jr; i < n; i += (int64_t)gridDim.x * L.J) {
-            const int64_t f = i * B + L.b;
-            const T xn = (T)((double)x[f] + alpha * (double)p[f]);
-            const T rn = (T)((double)r[f] - alpha * (double)q[f]);
-            x[f] = xn;
-            r[f] = rn;
-            const double z = (double)dinv[f] * (double)rn;
-            srz += (double)rn * z;
-            srr += (double)rn * (double)rn;
+        const int64_t step = (int64_t)gridDim.x * L.J * kVecItems;
+        for (int64_t base = (int64_t)blockIdx.x * L.J * kVecItems + L.jr; base < n; base += step) {
+            T xv[kVecItems], pv[kVecItems], rv[kVecItems], qv[kVecItems], dv[kVecItems];
+#pragma unroll
+            for (int u = 0; u < kVecItems; ++u) {
+                const int64_t i = base + (int64_t)u * L.J;
+                const int64_t f = i * B + L.b;
+                const bool in = i < n;
+                xv[u] = in ? x[f] : (T)0;
+                pv[u] = in ? p[f] : (T)0;
+                rv[u] = in ? r[f] : (T)0;
+                qv[u] = in ? q[f] : (T)0;
+                dv[u] = in ? dinv[f] : (T)0;
+            }
+#pragma unroll
+            for (int u = 0; u < kVecItems; ++u) {
+                const int64_t i = base + (int64_t)u * L.J;
+                if (i >= n) break;
+                const int64_t f = i * B + L.b;
+                const T xn = (T)((double)xv[u] + alpha * (double)pv[u]);
+                const T rn = (T)((double)rv[u] - alpha * (double)qv[u]);
+                x[f] = xn;
+                r[f] = rn;
+                const double z = (double)dv[u] * (double)rn;
+                srz += (double)rn * z;
+                srr += (double)rn * (double)rn;
+            }
         }
     }
     block_sum_per_system(srz, L, tmp, blk);
-    if (threadIdx.x < B) part[(int64_t)blockIdx.x * 2 * B + threadIdx.x] = blk[threadIdx.x];
+    if (threadIdx.x < B)
+        store_partial(red.part + (int64_t)blockIdx.x * 2 * B + threadIdx.x, blk[threadIdx.x]);
     __syncthreads();
     block_sum_per_system(srr, L, tmp, blk);
-    if (threadIdx.x < B) part[(int64_t)blockIdx.x * 2 * B + B + threadIdx.x] = blk[threadIdx.x];
-    if (last_block_sums(part, &ctl->counter[kCntUpdate], gridDim.x, 2 * B, tmp, tot)) {
+    if (threadIdx.x < B)
+        store_partial(red.part + (int64_t)blockIdx.x * 2 * B + B + threadIdx.x, blk[threadIdx.x]);
+    if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, 2 * B, tmp, tot)) {
         if (threadIdx.x == 0) {
             int running = 0;
             const double tol = ctl->tol;
@@ -157,9 +193,23 @@ __global__ __launch_bounds__(kBlock) void k_direction(int64_t n, int B, const T 
     const Lanes L(B);
     if (!L.on || st[L.b].status != kRunning) return;
     const double beta = st[L.b].beta;
-    for (int64_t i = (int64_t)blockIdx.x * L.J + L.jr; i < n; i += (int64_t)gridDim.x * L.J) {
-        const int64_t f = i * B + L.b;
-        p[f] = (T)((double)dinv[f] * (double)r[f] + beta * (double)p[f]);
+    const int64_t step = (int64_t)gridDim.x * L.J * kVecItems;
+    for (int64_t base = (int64_t)blockIdx.x * L.J * kVecItems + L.jr; base < n; base += step) {
+        T rv[kVecItems], pv[kVecItems], dv[kVecItems];
+#pragma unroll
+        for (int u = 0; u < kVecItems; ++u) {
+            const int64_t i = base + (int64_t)u * L.J;
+            const int64_t f = i * B + L.b;
+            const bool in = i < n;
+            rv[u] = in ? r[f] : (T)0;
+            pv[u] = in ? p[f] : (T)0;
+            dv[u] = in ? dinv[f] : (T)0;
+        }
+#pragma unroll
+        for (int u = 0; u < kVecItems; ++u) {
+            const int64_t i = base + (int64_t)u * L.J;
+            if (i < n) p[i * B + L.b] = (T)((double)dv[u] * (double)rv[u] + beta * (double)pv[u]);
+        }
     }
 }
 
@@ -223,8 +273,9 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
     launch_spmv_dot(h, s);
     if (lp) lp->end(SLA_KERNEL_SPMV_DOT, a);
     if (lp) lp->begin(SLA_KERNEL_UPDATE, &a);
+    const Red red{h.part, h.gpart, h.sync + kCntUpdate * kCountersPerKind};
     hipLaunchKernelGGL(k_update<T>, dim3((unsigned)g), dim3(kBlock), 0, s, h.n, h.B, (T *)h.x,
-                       (T *)h.r, (const T *)h.p, (const T *)h.q, (const T *)h.dinv, h.part, h.ctl,
+                       (T *)h.r, (const T *)h.p, (const T *)h.q, (const T *)h.dinv, red, h.ctl,
                        h.st, h.d_running);
     SLA_HIP(hipGetLastError());
     if (lp) lp->end(SLA_KERNEL_UPDATE, a);
@@ -271,8 +322,9 @@ void init_t(Handle &h, const void *b_int, hipStream_t s, Launcher *lp) {
     const int64_t g = vec_grid(h.n, h.B);
     hipEvent_t a = nullptr;
     if (lp) lp->begin(SLA_KERNEL_INIT, &a);
+    const Red red{h.part, h.gpart, h.sync + kCntInit * kCountersPerKind};
     hipLaunchKernelGGL(k_init<T>, dim3((unsigned)g), dim3(kBlock), 0, s, h.n, h.B, (const T *)b_int,
-                       (T *)h.x, (T *)h.r, (T *)h.p, (const T *)h.dinv, h.part, h.ctl, h.st,
+                       (T *)h.x, (T *)h.r, (T *)h.p, (const T *)h.dinv, red, h.ctl, h.st,
                        h.d_running);
     SLA_HIP(hipGetLastError());
     if (lp) lp->end(SLA_KERNEL_INIT, a);
@@ -324,7 +376,7 @@ void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit,
     h.h_ctl->tol = tol;
     h.h_ctl->maxit = maxit;
     h.h_ctl->n_running = 0;
-    SLA_HIP(hipMemcpyAsync(h.ctl, h.h_ctl, offsetof(Ctl, counter), hipMemcpyHostToDevice, s));
+    SLA_HIP(hipMemcpyAsync(h.ctl, h.h_ctl, sizeof(Ctl), hipMemcpyHostToDevice, s));
     const void *b_int = b_user;
     if (h.B > 1) {
         transpose(b_user, h.q, h.B, h.n, h.vbytes, s);  // q is free until the first SpMV

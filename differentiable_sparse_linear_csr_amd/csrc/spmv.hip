@@ -49,59 +49,101 @@ __device__ __forceinline__ void finish_alpha(double *tot, int B, Ctl *ctl, SysSt
     }
 }
 
+constexpr int kTileItems = (kTileCap + kBlock - 1) / kBlock;   // entries per lane, short tile
+constexpr int kRowItems = (kTileUnits + 1 + kBlock - 1) / kBlock; // row offsets per lane
+
+// Persistent over tiles: block b takes tiles b, b + grid, ... so the number
+// of blocks (and of reduction partials) stays bounded by kMaxGrid.
 template <typename T, typename RP, bool FUSED>
 __global__ __launch_bounds__(kBlock) void k_spmv_tile(
-    const int32_t *__restrict__ tile_start, const RP *__restrict__ row_ptr,
-    const int32_t *__restrict__ col, const T *__restrict__ val, const T *__restrict__ x,
-    T *__restrict__ y, int64_t ntiles, double *__restrict__ part, Ctl *__restrict__ ctl,
+    const int32_t *__restrict__ tile_start, const int64_t *__restrict__ tile_k0,
+    const RP *__restrict__ row_ptr, const int32_t *__restrict__ col, const T *__restrict__ val,
+    const T *__restrict__ x, T *__restrict__ y, int64_t ntiles, Red red, Ctl *__restrict__ ctl,
     SysState *__restrict__ st, int32_t *__restrict__ h_running) {
     __shared__ double prod[kTileCap];
+    __shared__ int32_t roff[kTileUnits + 1];
     __shared__ double lds4[kWaves];
     __shared__ double tmp[kBlock];
     __shared__ double tot[1];
     if (FUSED && st[0].status != kRunning) return;
 
     const int tid = threadIdx.x;
-    const int64_t t = blockIdx.x;
-    const int32_t rs = tile_start[t], re = tile_start[t + 1];
-    const int64_t k0 = row_ptr[rs], k1 = row_ptr[re];
     double dot = 0.0;
-
-    if (re - rs == 1 && k1 - k0 > kLongRow) {
-        double s = 0.0;
-        for (int64_t k = k0 + tid; k < k1; k += kBlock) s += (double)val[k] * (double)x[col[k]];
-        s = block_sum(s, lds4);
-        if (tid == 0) {
-            const T q = (T)s;
-            y[rs] = q;
-            if (FUSED) dot = (double)x[rs] * (double)q;
-        }
-    } else {
-        const int nk = (int)(k1 - k0);
-        for (int j = tid; j < nk; j += kBlock)
-            prod[j] = (double)val[k0 + j] * (double)x[col[k0 + j]];
-        __syncthreads();
-        const int nrows = re - rs;
-        const int G = group_size(nrows);
-        const int lg = tid & (G - 1);
-        const int grp = tid / G;
-        const int ngrp = kBlock / G;
-        for (int i = rs + grp; i < re; i += ngrp) {
-            const int a = (int)(row_ptr[i] - k0), b = (int)(row_ptr[i + 1] - k0);
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int32_t rs = tile_start[t], re = tile_start[t + 1];
+        const int64_t k0 = tile_k0[t], k1 = tile_k0[t + 1];
+        if (re - rs == 1 && k1 - k0 > kLongRow) {
+            // one long row: the workgroup strides over it, 4 entries in flight per lane
             double s = 0.0;
-            for (int j = a + lg; j < b; j += G) s += prod[j];
-            for (int off = G >> 1; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-            if (lg == 0) {
-                const T q = (T)s;
-                y[i] = q;
-                if (FUSED) dot += (double)x[i] * (double)q;
+            for (int64_t k = k0 + tid; k < k1; k += 4 * kBlock) {
+                int32_t c[4];
+                T v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int64_t kk = k + u * kBlock;
+                    c[u] = kk < k1 ? col[kk] : 0;
+                    v[u] = kk < k1 ? val[kk] : (T)0;
+                }
+                double xv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) xv[u] = (double)x[c[u]];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) s += (double)v[u] * xv[u];
             }
+            s = block_sum(s, lds4);
+            if (tid == 0) {
+                const T q = (T)s;
+                y[rs] = q;
+                if (FUSED) dot += (double)x[rs] * (double)q;
+            }
+        } else {
+            // short rows: every load of the tile is issued before any is consumed
+            const int nk = (int)(k1 - k0);
+            const int nrows = re - rs;
+            int32_t c[kTileItems];
+            T v[kTileItems];
+#pragma unroll
+            for (int u = 0; u < kTileItems; ++u) {
+                const int j = tid + u * kBlock;
+                c[u] = j < nk ? col[k0 + j] : 0;
+                v[u] = j < nk ? val[k0 + j] : (T)0;
+            }
+#pragma unroll
+            for (int u = 0; u < kRowItems; ++u) {
+                const int j = tid + u * kBlock;
+                if (j <= nrows) roff[j] = (int32_t)(row_ptr[rs + j] - k0);
+            }
+            double xv[kTileItems];
+#pragma unroll
+            for (int u = 0; u < kTileItems; ++u) xv[u] = (double)x[c[u]];
+#pragma unroll
+            for (int u = 0; u < kTileItems; ++u) {
+                const int j = tid + u * kBlock;
+                if (j < nk) prod[j] = (double)v[u] * xv[u];
+            }
+            __syncthreads();
+            const int G = group_size(nrows);
+            const int lg = tid & (G - 1);
+            const int grp = tid / G;
+            const int ngrp = kBlock / G;
+            for (int i = grp; i < nrows; i += ngrp) {
+                const int a = roff[i], b = roff[i + 1];
+                double s = 0.0;
+                for (int j = a + lg; j < b; j += G) s += prod[j];
+                for (int off = G >> 1; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+                if (lg == 0) {
+                    const T q = (T)s;
+                    y[rs + i] = q;
+                    if (FUSED) dot += (double)x[rs + i] * (double)q;
+                }
+            }
+            __syncthreads();  // LDS is reused by the next tile
         }
     }
     if (FUSED) {
         dot = block_sum(dot, lds4);
-        if (tid == 0) part[t] = dot;
-        if (last_block_sums(part, &ctl->counter[kCntSpmv], ntiles, 1, tmp, tot))
+        if (tid == 0) store_partial(red.part + blockIdx.x, dot);
+        if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, 1, tmp, tot))
             finish_alpha(tot, 1, ctl, st, h_running);
     }
 }
@@ -110,8 +152,8 @@ template <typename T, typename RP, bool FUSED>
 __global__ __launch_bounds__(kBlock) void k_spmv_batched(
     int64_t n, int B, int rows_per_lane, const RP *__restrict__ row_ptr,
     const int32_t *__restrict__ col, const T *__restrict__ val, const T *__restrict__ x,
-    T *__restrict__ y, double *__restrict__ part, Ctl *__restrict__ ctl,
-    SysState *__restrict__ st, int32_t *__restrict__ h_running) {
+    T *__restrict__ y, Red red, Ctl *__restrict__ ctl, SysState *__restrict__ st,
+    int32_t *__restrict__ h_running) {
     __shared__ double tmp[kBlock];
     __shared__ double tot[kMaxBatch];
     __shared__ double blk[kMaxBatch];
@@ -135,19 +177,22 @@ __global__ __launch_bounds__(kBlock) void k_spmv_batched(
     }
     if (FUSED) {
         block_sum_per_system(dot, L, tmp, blk);
-        if (threadIdx.x < B) part[(int64_t)blockIdx.x * B + threadIdx.x] = blk[threadIdx.x];
-        if (last_block_sums(part, &ctl->counter[kCntSpmv], gridDim.x, B, tmp, tot))
+        if (threadIdx.x < B)
+            store_partial(red.part + (int64_t)blockIdx.x * B + threadIdx.x, blk[threadIdx.x]);
+        if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, B, tmp, tot))
             finish_alpha(tot, B, ctl, st, h_running);
     }
 }
 
 template <typename T, typename RP, bool FUSED>
 void launch_spmv_t(Handle &h, const void *x, void *y, hipStream_t s) {
+    const Red red{h.part, h.gpart, h.sync + kCntSpmv * kCountersPerKind};
     if (h.B == 1) {
-        hipLaunchKernelGGL((k_spmv_tile<T, RP, FUSED>), dim3((unsigned)h.ntiles), dim3(kBlock), 0,
-                           s, (const int32_t *)h.tile_start, (const RP *)h.row_ptr,
-                           (const int32_t *)h.col, (const T *)h.vals, (const T *)x, (T *)y,
-                           h.ntiles, h.part, h.ctl, h.st, h.d_running);
+        const int64_t grid = h.ntiles < kMaxGrid ? h.ntiles : kMaxGrid;
+        hipLaunchKernelGGL((k_spmv_tile<T, RP, FUSED>), dim3((unsigned)grid), dim3(kBlock), 0, s,
+                           (const int32_t *)h.tile_start, (const int64_t *)h.tile_k0,
+                           (const RP *)h.row_ptr, (const int32_t *)h.col, (const T *)h.vals,
+                           (const T *)x, (T *)y, h.ntiles, red, h.ctl, h.st, h.d_running);
     } else {
         const int J = kBlock / h.B;
         int rpl = 1;
@@ -155,7 +200,7 @@ void launch_spmv_t(Handle &h, const void *x, void *y, hipStream_t s) {
         const int64_t grid = (h.n + (int64_t)J * rpl - 1) / ((int64_t)J * rpl);
         hipLaunchKernelGGL((k_spmv_batched<T, RP, FUSED>), dim3((unsigned)grid), dim3(kBlock), 0,
                            s, h.n, h.B, rpl, (const RP *)h.row_ptr, (const int32_t *)h.col,
-                           (const T *)h.vals, (const T *)x, (T *)y, h.part, h.ctl, h.st,
+                           (const T *)h.vals, (const T *)x, (T *)y, red, h.ctl, h.st,
                            h.d_running);
     }
     SLA_HIP(hipGetLastError());
@@ -164,7 +209,7 @@ void launch_spmv_t(Handle &h, const void *x, void *y, hipStream_t s) {
 }  // namespace
 
 int64_t spmv_grid(const Handle &h) {
-    if (h.B == 1) return h.ntiles;
+    if (h.B == 1) return h.ntiles < kMaxGrid ? h.ntiles : kMaxGrid;
     const int J = kBlock / h.B;
     int rpl = 1;
     while ((h.n + (int64_t)J * rpl - 1) / ((int64_t)J * rpl) > kMaxGrid && rpl < 1024) rpl *= 2;
