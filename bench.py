@@ -169,6 +169,12 @@ def main() -> int:
     A.set_option(_lib.SLA_OPT_PROFILE, 1)
     step()
     prof = A.profile()
+    # plain SpMV y = A x (sla_spmv), timed the same way, for SpMV GFLOP/s
+    A.profile_reset()
+    for _ in range(20):
+        A.matvec(b)
+    torch.cuda.synchronize()
+    plain_n, plain_ms = A.profile()["spmv"]
     A.set_option(_lib.SLA_OPT_PROFILE, 0)
 
     V = 8 if w.dtype == "f64" else 4
@@ -221,7 +227,10 @@ def main() -> int:
             "iteration_ms": round(per_iter_ms, 5),
             "iteration_gbps_3k": round(ab["iter_3k"] / (per_iter_ms * 1e-3) / 1e9, 1),
             "iteration_frac_3k": round(ab["iter_3k"] / (per_iter_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "spmv_gflops": round(2 * w.nnz * w.batch / (avg_ms * 1e-3) / 1e9, 1),
+            "spmv_dot_gflops": round(2 * w.nnz * w.batch / (avg_ms * 1e-3) / 1e9, 1),
+            "spmv_plain_ms": round(plain_ms / max(plain_n, 1), 5),
+            "spmv_plain_gflops": round(2 * w.nnz * w.batch / (plain_ms / max(plain_n, 1) * 1e-3) / 1e9, 1),
+            "spmv_plain_gbps": round(ab["spmv"] / (plain_ms / max(plain_n, 1) * 1e-3) / 1e9, 1),
             "kernel_avg_ms": {k: round(v[1] / max(v[0], 1), 5) for k, v in prof.items() if v[0]},
             "handle_bytes": A.memory_bytes(),
         },

@@ -24,10 +24,11 @@ namespace sla {
 
 constexpr int kBlock = 256;                        // threads per workgroup (4 wave64)
 constexpr int kWaves = kBlock / 64;
-constexpr int kTileUnits = 2048;                   // rows + entries per SpMV tile window
+constexpr int kTileUnits = 1024;                   // rows + entries per SpMV tile window
 constexpr int kLongRow = 512;                      // longer rows get a workgroup each
 constexpr int kTileCap = kTileUnits + kLongRow;    // max entries of a short tile
 constexpr int kMaxGrid = 2048;                     // grid cap of the persistent / grid-stride kernels
+constexpr int kXcds = 8;                           // workgroups go round-robin over 8 XCDs
 constexpr int kMaxBatch = 256;
 
 // per-system status codes on the device: running, or an sla_outcome

@@ -20,6 +20,8 @@
 
 namespace sla {
 
+int64_t spmv_grid(const Handle &h);
+
 namespace {
 
 __device__ __forceinline__ int group_size(int nrows) {
@@ -52,8 +54,12 @@ __device__ __forceinline__ void finish_alpha(double *tot, int B, Ctl *ctl, SysSt
 constexpr int kTileItems = (kTileCap + kBlock - 1) / kBlock;   // entries per lane, short tile
 constexpr int kRowItems = (kTileUnits + 1 + kBlock - 1) / kBlock; // row offsets per lane
 
-// Persistent over tiles: block b takes tiles b, b + grid, ... so the number
-// of blocks (and of reduction partials) stays bounded by kMaxGrid.
+// Persistent over tiles with an XCD-contiguous order: workgroup b runs on XCD
+// b % 8, and the workgroups of one XCD walk one contiguous eighth of the
+// tiles, so the gathered vector segments they share stay in that XCD's L2.
+// The loop is software-pipelined: the next tile's entries and row offsets are
+// loaded while the current tile's products are summed. The grid size is a
+// multiple of 8 and at most kMaxGrid, which also bounds the reduction partials.
 template <typename T, typename RP, bool FUSED>
 __global__ __launch_bounds__(kBlock) void k_spmv_tile(
     const int32_t *__restrict__ tile_start, const int64_t *__restrict__ tile_k0,
@@ -68,27 +74,69 @@ __global__ __launch_bounds__(kBlock) void k_spmv_tile(
     if (FUSED && st[0].status != kRunning) return;
 
     const int tid = threadIdx.x;
+    const int xcd = blockIdx.x % kXcds;
+    const int64_t per = gridDim.x / kXcds;
+    int64_t t = ntiles * xcd / kXcds + blockIdx.x / kXcds;
+    const int64_t t_end = ntiles * (xcd + 1) / kXcds;
     double dot = 0.0;
-    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const int32_t rs = tile_start[t], re = tile_start[t + 1];
-        const int64_t k0 = tile_k0[t], k1 = tile_k0[t + 1];
-        if (re - rs == 1 && k1 - k0 > kLongRow) {
+
+    int32_t rs = 0, re = 0;
+    int64_t k0 = 0, k1 = 0;
+    int32_t c[kTileItems];
+    T v[kTileItems];
+    int32_t ro[kRowItems];
+    auto is_long = [](int32_t a, int32_t b, int64_t ka, int64_t kb) {
+        return b - a == 1 && kb - ka > kLongRow;
+    };
+    auto fetch = [&](int32_t a, int32_t b, int64_t ka, int64_t kb) {
+        const int nk = is_long(a, b, ka, kb) ? 0 : (int)(kb - ka);
+        const int nr = is_long(a, b, ka, kb) ? -1 : b - a;
+#pragma unroll
+        for (int u = 0; u < kTileItems; ++u) {
+            const int j = tid + u * kBlock;
+            c[u] = j < nk ? col[ka + j] : 0;
+            v[u] = j < nk ? val[ka + j] : (T)0;
+        }
+#pragma unroll
+        for (int u = 0; u < kRowItems; ++u) {
+            const int j = tid + u * kBlock;
+            ro[u] = j <= nr ? (int32_t)(row_ptr[a + j] - ka) : 0;
+        }
+    };
+    if (t < t_end) {
+        rs = tile_start[t];
+        re = tile_start[t + 1];
+        k0 = tile_k0[t];
+        k1 = tile_k0[t + 1];
+        fetch(rs, re, k0, k1);
+    }
+    while (t < t_end) {
+        const int64_t tn = t + per;
+        int32_t rsn = 0, ren = 0;
+        int64_t k0n = 0, k1n = 0;
+        if (tn < t_end) {
+            rsn = tile_start[tn];
+            ren = tile_start[tn + 1];
+            k0n = tile_k0[tn];
+            k1n = tile_k0[tn + 1];
+        }
+        if (is_long(rs, re, k0, k1)) {
             // one long row: the workgroup strides over it, 4 entries in flight per lane
             double s = 0.0;
             for (int64_t k = k0 + tid; k < k1; k += 4 * kBlock) {
-                int32_t c[4];
-                T v[4];
+                int32_t cc[4];
+                T vv[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int64_t kk = k + u * kBlock;
-                    c[u] = kk < k1 ? col[kk] : 0;
-                    v[u] = kk < k1 ? val[kk] : (T)0;
+                    cc[u] = kk < k1 ? col[kk] : 0;
+                    vv[u] = kk < k1 ? val[kk] : (T)0;
                 }
                 double xv[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) xv[u] = (double)x[c[u]];
+                for (int u = 0; u < 4; ++u) xv[u] = (double)x[cc[u]];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) s += (double)v[u] * xv[u];
+                for (int u = 0; u < 4; ++u) s += (double)vv[u] * xv[u];
             }
             s = block_sum(s, lds4);
             if (tid == 0) {
@@ -96,23 +144,10 @@ __global__ __launch_bounds__(kBlock) void k_spmv_tile(
                 y[rs] = q;
                 if (FUSED) dot += (double)x[rs] * (double)q;
             }
+            if (tn < t_end) fetch(rsn, ren, k0n, k1n);
         } else {
-            // short rows: every load of the tile is issued before any is consumed
             const int nk = (int)(k1 - k0);
             const int nrows = re - rs;
-            int32_t c[kTileItems];
-            T v[kTileItems];
-#pragma unroll
-            for (int u = 0; u < kTileItems; ++u) {
-                const int j = tid + u * kBlock;
-                c[u] = j < nk ? col[k0 + j] : 0;
-                v[u] = j < nk ? val[k0 + j] : (T)0;
-            }
-#pragma unroll
-            for (int u = 0; u < kRowItems; ++u) {
-                const int j = tid + u * kBlock;
-                if (j <= nrows) roff[j] = (int32_t)(row_ptr[rs + j] - k0);
-            }
             double xv[kTileItems];
 #pragma unroll
             for (int u = 0; u < kTileItems; ++u) xv[u] = (double)x[c[u]];
@@ -121,6 +156,12 @@ __global__ __launch_bounds__(kBlock) void k_spmv_tile(
                 const int j = tid + u * kBlock;
                 if (j < nk) prod[j] = (double)v[u] * xv[u];
             }
+#pragma unroll
+            for (int u = 0; u < kRowItems; ++u) {
+                const int j = tid + u * kBlock;
+                if (j <= nrows) roff[j] = ro[u];
+            }
+            if (tn < t_end) fetch(rsn, ren, k0n, k1n);  // in flight during the sums below
             __syncthreads();
             const int G = group_size(nrows);
             const int lg = tid & (G - 1);
@@ -139,6 +180,11 @@ __global__ __launch_bounds__(kBlock) void k_spmv_tile(
             }
             __syncthreads();  // LDS is reused by the next tile
         }
+        t = tn;
+        rs = rsn;
+        re = ren;
+        k0 = k0n;
+        k1 = k1n;
     }
     if (FUSED) {
         dot = block_sum(dot, lds4);
@@ -188,7 +234,7 @@ template <typename T, typename RP, bool FUSED>
 void launch_spmv_t(Handle &h, const void *x, void *y, hipStream_t s) {
     const Red red{h.part, h.gpart, h.sync + kCntSpmv * kCountersPerKind};
     if (h.B == 1) {
-        const int64_t grid = h.ntiles < kMaxGrid ? h.ntiles : kMaxGrid;
+        const int64_t grid = spmv_grid(h);
         hipLaunchKernelGGL((k_spmv_tile<T, RP, FUSED>), dim3((unsigned)grid), dim3(kBlock), 0, s,
                            (const int32_t *)h.tile_start, (const int64_t *)h.tile_k0,
                            (const RP *)h.row_ptr, (const int32_t *)h.col, (const T *)h.vals,
@@ -209,7 +255,10 @@ void launch_spmv_t(Handle &h, const void *x, void *y, hipStream_t s) {
 }  // namespace
 
 int64_t spmv_grid(const Handle &h) {
-    if (h.B == 1) return h.ntiles < kMaxGrid ? h.ntiles : kMaxGrid;
+    if (h.B == 1) {
+        const int64_t g = (h.ntiles + kXcds - 1) / kXcds * kXcds;  // multiple of the XCD count
+        return g < kMaxGrid ? g : kMaxGrid;
+    }
     const int J = kBlock / h.B;
     int rpl = 1;
     while ((h.n + (int64_t)J * rpl - 1) / ((int64_t)J * rpl) > kMaxGrid && rpl < 1024) rpl *= 2;
