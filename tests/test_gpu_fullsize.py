@@ -1,0 +1,72 @@
+"""Full-size parity: the workloads at their benchmark sizes, in the launch
+configuration bench.py times, against reference values the CPU oracle wrote
+(tests/golden/<workload>.json, produced by tests/golden/make_golden.py).
+
+The oracle stores, per system, the iteration count, outcome, recursive
+residual, the 2-norm, values at seeded sample indices and projections onto
+seeded random vectors. A normwise relative error <= tol_x implies
+|dx_i| <= tol_x ||x|| for every sample and |<dx, w>| <= tol_x ||x|| ||w|| for
+every projection, which is what is asserted together with the norm itself.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from differentiable_sparse_linear_csr_amd import SparseCSR
+from workloads import make_workload
+
+from gpu_util import dev, host
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+NAMES = ["diffusion3d_128", "knn_laplacian_2m", "batched_diffusion2d_512x32", "poisson2d_11548"]
+
+
+def check_vector(v, ref, tol):
+    v = v.astype(np.float64)
+    norm = ref["norm"]
+    assert abs(np.linalg.norm(v) - norm) <= tol * norm
+    idx = np.random.default_rng(ref["sample_seed"]).integers(0, v.shape[0], len(ref["samples"]))
+    assert np.all(np.abs(v[idx] - np.asarray(ref["samples"])) <= tol * norm)
+    for k, pr in enumerate(ref["projections"]):
+        w = np.random.default_rng(ref["sample_seed"] + 1000 * k).standard_normal(v.shape[0])
+        assert abs(np.dot(w, v) - pr) <= tol * norm * np.linalg.norm(w)
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_full_size_against_oracle_reference(name):
+    path = os.path.join(HERE, "golden", f"{name}.json")
+    ref = json.load(open(path))
+    print(f"full-size {name}: building inputs", flush=True)
+    w = make_workload(name)
+    assert ref["n"] == w.n and ref["nnz"] == w.nnz and ref["batch"] == w.batch
+    if w.fmt == "coo":
+        A = SparseCSR.from_coo(dev(w.rows), dev(w.cols), dev(w.vals), w.n)
+    else:
+        A = SparseCSR.from_csr(dev(w.row_ptr), dev(w.cols), dev(w.vals))
+        assert A.row_index_dtype == torch.int64
+    print(f"full-size {name}: solving n={w.n} nnz={w.nnz} batch={w.batch}", flush=True)
+    x, info = A.solve_raw(dev(w.b), w.tol, w.maxit)
+    X = np.atleast_2d(host(x))
+    tol_x = 1e-8 if w.dtype == "f64" else 1e-4
+    for s, fr in enumerate(ref["forward"]):
+        assert info.status[s] == fr["status"], (s, info.status[s], fr["status"])
+        assert abs(info.iterations[s] - fr["iterations"]) <= 2, (s, info.iterations[s], fr["iterations"])
+        if w.tol > 0:
+            assert info.rel_residual[s] <= w.tol
+        if info.iterations[s] == fr["iterations"]:
+            assert abs(info.rel_residual[s] - fr["rel_residual"]) <= 1e-3 * fr["rel_residual"]
+        check_vector(X[s], fr, tol_x)
+    if "adjoint" in ref:
+        print(f"full-size {name}: adjoint", flush=True)
+        gb, gv, ainfo = A.adjoint_raw(x, dev(w.g), w.tol, w.maxit)
+        GB, GV = np.atleast_2d(host(gb)), np.atleast_2d(host(gv))
+        tol_g = 1e-8 if w.dtype == "f64" else 1e-3
+        for s, ar in enumerate(ref["adjoint"]):
+            assert ainfo.status[s] == ar["status"]
+            assert abs(ainfo.iterations[s] - ar["iterations"]) <= 2
+            check_vector(GB[s], ar["lambda"], tol_g)
+            check_vector(GV[s], ar["grad_vals"], tol_g)

@@ -55,33 +55,57 @@ def poisson2d_coo(N: int, index_dtype=np.int32):
     return rows, cols, np.ascontiguousarray(vals[valid], dtype=np.float64)
 
 
-def poisson2d_csr(N: int, rowptr_dtype=np.int64, col_dtype=np.int32, chunk: int = 1 << 22):
+def poisson2d_csr(N: int, rowptr_dtype=np.int64, col_dtype=np.int32):
     """Same matrix as :func:`poisson2d_coo`, emitted directly as CSR arrays.
 
-    Used for grids too large to hold a COO row array comfortably. Row lengths
-    follow in closed form from the grid position; the arrays are filled in row
-    chunks to bound host memory.
+    Built one grid row (N nodes) at a time from three templates (bottom,
+    interior and top grid row) broadcast over the grid rows, so that very
+    large grids are generated quickly. Entry order and values are identical to
+    the COO generator's.
     """
     n = N * N
     nnz = 5 * n - 4 * N
-    row_ptr = np.empty(n + 1, dtype=rowptr_dtype)
-    row_ptr[0] = 0
+    xs = np.arange(N, dtype=np.int64)
+
+    def template(has_down: bool, has_up: bool):
+        cand = np.stack([xs - N, xs - 1, xs, xs + 1, xs + N], axis=1)
+        valid = np.stack([np.full(N, has_down), xs > 0, np.ones(N, bool), xs < N - 1,
+                          np.full(N, has_up)], axis=1)
+        vals = np.broadcast_to(np.array([-1.0, -1.0, 4.0, -1.0, -1.0]), cand.shape)[valid]
+        off = np.zeros(N + 1, dtype=np.int64)
+        off[1:] = np.cumsum(valid.sum(axis=1))
+        return cand[valid], vals, off
+
+    if N == 1:
+        return (np.array([0, 1], dtype=rowptr_dtype), np.array([0], dtype=col_dtype),
+                np.array([4.0]))
+    c_bot, v_bot, o_bot = template(False, True)
+    c_mid, v_mid, o_mid = template(True, True)
+    c_top, v_top, o_top = template(True, False)
+    nb, nm = c_bot.shape[0], c_mid.shape[0]
     cols = np.empty(nnz, dtype=col_dtype)
     vals = np.empty(nnz, dtype=np.float64)
-    stencil = np.array([-1.0, -1.0, 4.0, -1.0, -1.0])
-    for a in range(0, n, chunk):
-        b = min(n, a + chunk)
-        ii = np.arange(a, b, dtype=np.int64)
-        y, x = np.divmod(ii, N)
-        valid = np.stack([y > 0, x > 0, np.ones(b - a, bool), x < N - 1, y < N - 1], axis=1)
-        cnt = valid.sum(axis=1)
-        start = int(row_ptr[a])
-        row_ptr[a + 1:b + 1] = start + np.cumsum(cnt)
-        end = int(row_ptr[b])
-        cand = np.stack([ii - N, ii - 1, ii, ii + 1, ii + N], axis=1)
-        cols[start:end] = cand[valid]
-        vals[start:end] = np.broadcast_to(stencil, cand.shape)[valid]
-    assert int(row_ptr[n]) == nnz
+    row_ptr = np.empty(n + 1, dtype=rowptr_dtype)
+    # bottom grid row
+    cols[:nb] = c_bot
+    vals[:nb] = v_bot
+    row_ptr[:N] = o_bot[:N]
+    # interior grid rows y = 1 .. N-2
+    ny = N - 2
+    if ny > 0:
+        ys = np.arange(1, N - 1, dtype=np.int64)
+        mid = cols[nb:nb + ny * nm].reshape(ny, nm)
+        np.add(c_mid[None, :], (ys * N)[:, None], out=mid, casting="unsafe")
+        vals[nb:nb + ny * nm].reshape(ny, nm)[:] = v_mid[None, :]
+        rp_mid = row_ptr[N:N + ny * N].reshape(ny, N)
+        np.add(o_mid[None, :N], (nb + (ys - 1) * nm)[:, None], out=rp_mid, casting="unsafe")
+    # top grid row
+    base = nb + ny * nm
+    cols[base:] = c_top + (N - 1) * N
+    vals[base:] = v_top
+    row_ptr[(N - 1) * N:n] = base + o_top[:N]
+    row_ptr[n] = nnz
+    assert base + c_top.shape[0] == nnz
     return row_ptr, cols, vals
 
 
