@@ -74,9 +74,12 @@ def cpu_baseline(w, budget_s: float):
     import numpy as np
     import oracle
 
-    rows = w.rows if w.rows is not None else np.repeat(np.arange(w.n), np.diff(w.row_ptr))
-    ref = oracle.coo_to_csr(w.n, rows, w.cols, w.vals)
-    vals = ref["vals"]
+    if w.fmt == "csr":
+        ref = {"row_ptr": w.row_ptr.astype(np.int64), "col": w.cols.astype(np.int64)}
+        vals = w.vals
+    else:
+        ref = oracle.coo_to_csr(w.n, w.rows, w.cols, w.vals)
+        vals = ref["vals"]
     b = w.b
     t0 = time.perf_counter()
     oracle.pcg(ref["row_ptr"], ref["col"], vals, b, 0.0, 5)
@@ -90,7 +93,7 @@ def cpu_baseline(w, budget_s: float):
     return {"value": it / dt, "unit": "iterations/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"first {iters} Jacobi-PCG iterations (tol 0) of the forward solve of "
-                      f"{w.name} ({per_sys} system(s)), oracle CSR built from the same COO input; "
+                      f"{w.name} ({per_sys} system(s)), oracle CSR built from the same input; "
                       f"{dt:.1f} s"}
 
 
@@ -103,6 +106,9 @@ def main() -> int:
     ap.add_argument("--check-interval", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after the measurement, copy a buffer of this size 3 times with a plain "
+                         "device copy kernel (reference for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -241,6 +247,13 @@ def main() -> int:
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+    if args.calibrate_copy_mib > 0:
+        src = torch.ones(args.calibrate_copy_mib << 17, dtype=torch.float64, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration: copied {args.calibrate_copy_mib} MiB x3", file=sys.stderr)
     return 0
 
 
