@@ -485,23 +485,45 @@ void build_tiles(Handle &h, hipStream_t s) {
     SLA_HIP(hipGetLastError());
     exclusive_scan_i64(flag, excl, n, s);
     const int64_t nt = read_i64(excl + (n - 1), s) + read_i64(flag + (n - 1), s);
-    h.ntiles = nt;
-    h.tile_start = (int32_t *)dalloc(h, (size_t)(nt + 1) * 4);
+    int32_t *tstart = sc.get<int32_t>(nt + 1);
+    int64_t *tk0 = sc.get<int64_t>(nt + 1);
     hipLaunchKernelGGL(k_tile_fill, dim3(grid_for(n)), dim3(kBlock), 0, s, (const int64_t *)flag,
-                       (const int64_t *)excl, n, h.tile_start);
+                       (const int64_t *)excl, n, tstart);
     SLA_HIP(hipGetLastError());
     const int32_t nn = (int32_t)n;
-    SLA_HIP(hipMemcpyAsync(h.tile_start + nt, &nn, 4, hipMemcpyHostToDevice, s));
-    h.tile_k0 = (int64_t *)dalloc(h, (size_t)(nt + 1) * 8);
+    SLA_HIP(hipMemcpyAsync(tstart + nt, &nn, 4, hipMemcpyHostToDevice, s));
     if (h.rp64)
         hipLaunchKernelGGL(k_tile_k0<int64_t>, dim3(grid_for(nt + 1)), dim3(kBlock), 0, s,
-                           (const int64_t *)h.row_ptr, (const int32_t *)h.tile_start, nt,
-                           h.tile_k0);
+                           (const int64_t *)h.row_ptr, (const int32_t *)tstart, nt, tk0);
     else
         hipLaunchKernelGGL(k_tile_k0<int32_t>, dim3(grid_for(nt + 1)), dim3(kBlock), 0, s,
-                           (const int32_t *)h.row_ptr, (const int32_t *)h.tile_start, nt,
-                           h.tile_k0);
+                           (const int32_t *)h.row_ptr, (const int32_t *)tstart, nt, tk0);
     SLA_HIP(hipGetLastError());
+    // split on the host: a one-row tile longer than kLongRow goes to the long-row list
+    std::vector<int32_t> hs((size_t)nt + 1);
+    std::vector<int64_t> hk((size_t)nt + 1);
+    SLA_HIP(hipMemcpyAsync(hs.data(), tstart, (size_t)(nt + 1) * 4, hipMemcpyDeviceToHost, s));
+    SLA_HIP(hipMemcpyAsync(hk.data(), tk0, (size_t)(nt + 1) * 8, hipMemcpyDeviceToHost, s));
+    SLA_HIP(hipStreamSynchronize(s));
+    std::vector<TileDesc> shorts;
+    std::vector<int32_t> longs;
+    shorts.reserve((size_t)nt);
+    for (int64_t t = 0; t < nt; ++t) {
+        const TileDesc d{hs[t], hs[t + 1], hk[t], hk[t + 1]};
+        if (d.re - d.rs == 1 && d.k1 - d.k0 > kLongRow) longs.push_back(d.rs);
+        else shorts.push_back(d);
+    }
+    h.ntiles = (int64_t)shorts.size();
+    h.nlong = (int64_t)longs.size();
+    h.tiles = (TileDesc *)dalloc(h, sizeof(TileDesc) * (shorts.size() + 1));
+    h.long_rows = (int32_t *)dalloc(h, sizeof(int32_t) * (longs.size() + 1));
+    h.long_dot = (double *)dalloc(h, sizeof(double) * (longs.size() + 1));
+    if (!shorts.empty())
+        SLA_HIP(hipMemcpyAsync(h.tiles, shorts.data(), sizeof(TileDesc) * shorts.size(),
+                               hipMemcpyHostToDevice, s));
+    if (!longs.empty())
+        SLA_HIP(hipMemcpyAsync(h.long_rows, longs.data(), sizeof(int32_t) * longs.size(),
+                               hipMemcpyHostToDevice, s));
     SLA_HIP(hipStreamSynchronize(s));
 }
 

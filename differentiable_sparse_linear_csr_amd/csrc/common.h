@@ -44,6 +44,12 @@ struct SysState {
     int32_t status; // kRunning or sla_outcome
 };
 
+// A run of short rows [rs, re) whose entries are [k0, k1), at most kTileCap.
+struct TileDesc {
+    int32_t rs, re;
+    int64_t k0, k1;
+};
+
 struct Ctl {
     double tol;
     int32_t maxit;
@@ -96,8 +102,11 @@ struct Handle {
     int64_t *slot = nullptr; // input entry -> CSR position (null: identity)
     int64_t *perm = nullptr; // sorted position -> input entry (null: identity)
     int64_t *run = nullptr;  // [nnz+1] first sorted position of each CSR entry
-    int32_t *tile_start = nullptr;
+    TileDesc *tiles = nullptr;   // short-row tiles, in row order
     int64_t ntiles = 0;
+    int32_t *long_rows = nullptr; // rows longer than kLongRow, in row order
+    int64_t nlong = 0;
+    double *long_dot = nullptr;   // [nlong] p_i q_i of the long rows (fused SpMV)
     void *dinv = nullptr;    // [n][B]
     bool diag_ok = false;
 
@@ -107,7 +116,6 @@ struct Handle {
     int64_t part_len = 0;
     double *gpart = nullptr;      // [kGroups][C] group sums of the grid reductions
     uint32_t *sync = nullptr;     // [kCntKinds][kCountersPerKind] arrival counters
-    int64_t *tile_k0 = nullptr;   // [ntiles+1] first entry of each tile
     SysState *st = nullptr;
     Ctl *ctl = nullptr;
     int32_t *h_running = nullptr; // pinned, mapped

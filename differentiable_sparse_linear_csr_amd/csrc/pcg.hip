@@ -213,10 +213,10 @@ __global__ __launch_bounds__(kBlock) void k_direction(int64_t n, int B, const T 
     }
 }
 
-// grad[b][k] = -lam[row(k)][b] * x[col(k)][b], tile by tile (rows of the
-// tile's entries are recovered through LDS).
+// grad[b][k] = -lam[row(k)][b] * x[col(k)][b], one short-row tile per
+// workgroup (the row of each entry is recovered through LDS).
 template <typename T, typename RP>
-__global__ __launch_bounds__(kBlock) void k_grad_tile(const int32_t *__restrict__ tile_start,
+__global__ __launch_bounds__(kBlock) void k_grad_tile(const TileDesc *__restrict__ tiles,
                                                       const RP *__restrict__ row_ptr,
                                                       const int32_t *__restrict__ col, int64_t nnz,
                                                       int B, const T *__restrict__ lam,
@@ -224,23 +224,35 @@ __global__ __launch_bounds__(kBlock) void k_grad_tile(const int32_t *__restrict_
                                                       T *__restrict__ grad) {
     __shared__ int32_t rowid[kTileCap];
     const int tid = threadIdx.x;
-    const int64_t t = blockIdx.x;
-    const int32_t rs = tile_start[t], re = tile_start[t + 1];
-    const int64_t k0 = row_ptr[rs], k1 = row_ptr[re];
-    const int64_t nk = k1 - k0;
-    const bool long_tile = (re - rs == 1 && nk > kLongRow);
-    if (!long_tile) {
-        for (int32_t i = rs + tid; i < re; i += kBlock)
-            for (int64_t k = row_ptr[i]; k < (int64_t)row_ptr[i + 1]; ++k) rowid[k - k0] = i;
-        __syncthreads();
-    }
+    const TileDesc d = tiles[blockIdx.x];
+    const int64_t nk = d.k1 - d.k0;
+    for (int32_t i = d.rs + tid; i < d.re; i += kBlock)
+        for (int64_t k = row_ptr[i]; k < (int64_t)row_ptr[i + 1]; ++k) rowid[k - d.k0] = i;
+    __syncthreads();
     for (int b = 0; b < B; ++b) {
         for (int64_t kk = tid; kk < nk; kk += kBlock) {
-            const int64_t i = long_tile ? rs : rowid[kk];
-            const int64_t k = k0 + kk;
+            const int64_t i = rowid[kk];
+            const int64_t k = d.k0 + kk;
             const double g = -((double)lam[i * B + b] * (double)x[(int64_t)col[k] * B + b]);
             grad[(int64_t)b * nnz + k] = (T)g;
         }
+    }
+}
+
+// the same for rows longer than kLongRow, one workgroup per row
+template <typename T, typename RP>
+__global__ __launch_bounds__(kBlock) void k_grad_long(const int32_t *__restrict__ long_rows,
+                                                      const RP *__restrict__ row_ptr,
+                                                      const int32_t *__restrict__ col, int64_t nnz,
+                                                      int B, const T *__restrict__ lam,
+                                                      const T *__restrict__ x,
+                                                      T *__restrict__ grad) {
+    const int64_t i = long_rows[blockIdx.x];
+    const int64_t k0 = row_ptr[i], k1 = row_ptr[i + 1];
+    for (int b = 0; b < B; ++b) {
+        const double li = (double)lam[i * B + b];
+        for (int64_t k = k0 + threadIdx.x; k < k1; k += kBlock)
+            grad[(int64_t)b * nnz + k] = (T)(-(li * (double)x[(int64_t)col[k] * B + b]));
     }
 }
 
@@ -434,10 +446,16 @@ void grad_vals(Handle &h, const void *lam_internal, const void *x_user, void *gr
     auto go = [&](auto ttag, auto rtag) {
         using T = decltype(ttag);
         using RP = decltype(rtag);
-        hipLaunchKernelGGL((k_grad_tile<T, RP>), dim3((unsigned)h.ntiles), dim3(kBlock), 0, s,
-                           (const int32_t *)h.tile_start, (const RP *)h.row_ptr,
-                           (const int32_t *)h.col, h.nnz, h.B, (const T *)lam_internal,
-                           (const T *)x_int, (T *)grad);
+        if (h.ntiles > 0)
+            hipLaunchKernelGGL((k_grad_tile<T, RP>), dim3((unsigned)h.ntiles), dim3(kBlock), 0, s,
+                               (const TileDesc *)h.tiles, (const RP *)h.row_ptr,
+                               (const int32_t *)h.col, h.nnz, h.B, (const T *)lam_internal,
+                               (const T *)x_int, (T *)grad);
+        if (h.nlong > 0)
+            hipLaunchKernelGGL((k_grad_long<T, RP>), dim3((unsigned)h.nlong), dim3(kBlock), 0, s,
+                               (const int32_t *)h.long_rows, (const RP *)h.row_ptr,
+                               (const int32_t *)h.col, h.nnz, h.B, (const T *)lam_internal,
+                               (const T *)x_int, (T *)grad);
     };
     if (h.vt == SLA_F64) {
         if (h.rp64) go(double(), int64_t());

@@ -54,18 +54,58 @@ __device__ __forceinline__ void finish_alpha(double *tot, int B, Ctl *ctl, SysSt
 constexpr int kTileItems = (kTileCap + kBlock - 1) / kBlock;   // entries per lane, short tile
 constexpr int kRowItems = (kTileUnits + 1 + kBlock - 1) / kBlock; // row offsets per lane
 
-// Persistent over tiles with an XCD-contiguous order: workgroup b runs on XCD
-// b % 8, and the workgroups of one XCD walk one contiguous eighth of the
+// Rows longer than kLongRow: one workgroup per row, 8 entries in flight per
+// lane. Runs before the tile kernel; in the fused form it also leaves
+// p_i q_i of each long row in long_dot for the tile kernel's reduction.
+template <typename T, typename RP, bool FUSED>
+__global__ __launch_bounds__(kBlock) void k_spmv_long(
+    const int32_t *__restrict__ long_rows, const RP *__restrict__ row_ptr,
+    const int32_t *__restrict__ col, const T *__restrict__ val, const T *__restrict__ x,
+    T *__restrict__ y, double *__restrict__ long_dot, const SysState *__restrict__ st) {
+    __shared__ double lds4[kWaves];
+    if (FUSED && st[0].status != kRunning) return;
+    const int tid = threadIdx.x;
+    const int64_t i = long_rows[blockIdx.x];
+    const int64_t k0 = row_ptr[i], len = (int64_t)row_ptr[i + 1] - k0;
+    const int32_t *cp = col + k0;
+    const T *vp = val + k0;
+    constexpr int kU = 8;
+    double s = 0.0;
+    for (int64_t base = 0; base < len; base += (int64_t)kU * kBlock) {
+        int32_t c[kU];
+        T v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t j = base + tid + u * kBlock;
+            c[u] = j < len ? cp[j] : 0;
+            v[u] = j < len ? vp[j] : (T)0;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) s += (double)v[u] * (double)x[c[u]];
+    }
+    s = block_sum(s, lds4);
+    if (tid == 0) {
+        const T q = (T)s;
+        y[i] = q;
+        if (FUSED) long_dot[blockIdx.x] = (double)x[i] * (double)q;
+    }
+}
+
+// Short-row tiles, persistent, in an XCD-contiguous order: workgroup b runs on
+// XCD b % 8, and the workgroups of one XCD walk one contiguous eighth of the
 // tiles, so the gathered vector segments they share stay in that XCD's L2.
 // The loop is software-pipelined: the next tile's entries and row offsets are
-// loaded while the current tile's products are summed. The grid size is a
-// multiple of 8 and at most kMaxGrid, which also bounds the reduction partials.
+// loaded while the current tile's products are summed. A tile's entries are
+// staged as fp64 products in LDS and its rows are summed by G lanes each (G
+// from the tile's row count). The grid is a multiple of 8, at most kMaxGrid,
+// which also bounds the reduction partials. The fused form adds p.q of its
+// rows (and of the long rows, taken in a fixed order) to the grid reduction.
 template <typename T, typename RP, bool FUSED>
 __global__ __launch_bounds__(kBlock) void k_spmv_tile(
-    const int32_t *__restrict__ tile_start, const int64_t *__restrict__ tile_k0,
-    const RP *__restrict__ row_ptr, const int32_t *__restrict__ col, const T *__restrict__ val,
-    const T *__restrict__ x, T *__restrict__ y, int64_t ntiles, Red red, Ctl *__restrict__ ctl,
-    SysState *__restrict__ st, int32_t *__restrict__ h_running) {
+    const TileDesc *__restrict__ tiles, int64_t ntiles, const RP *__restrict__ row_ptr,
+    const int32_t *__restrict__ col, const T *__restrict__ val, const T *__restrict__ x,
+    T *__restrict__ y, const double *__restrict__ long_dot, int64_t nlong, Red red,
+    Ctl *__restrict__ ctl, SysState *__restrict__ st, int32_t *__restrict__ h_running) {
     __shared__ double prod[kTileCap];
     __shared__ int32_t roff[kTileUnits + 1];
     __shared__ double lds4[kWaves];
@@ -80,113 +120,77 @@ __global__ __launch_bounds__(kBlock) void k_spmv_tile(
     const int64_t t_end = ntiles * (xcd + 1) / kXcds;
     double dot = 0.0;
 
-    int32_t rs = 0, re = 0;
-    int64_t k0 = 0, k1 = 0;
+    TileDesc d{0, 0, 0, 0};
     int32_t c[kTileItems];
     T v[kTileItems];
     int32_t ro[kRowItems];
-    auto is_long = [](int32_t a, int32_t b, int64_t ka, int64_t kb) {
-        return b - a == 1 && kb - ka > kLongRow;
-    };
-    auto fetch = [&](int32_t a, int32_t b, int64_t ka, int64_t kb) {
-        const int nk = is_long(a, b, ka, kb) ? 0 : (int)(kb - ka);
-        const int nr = is_long(a, b, ka, kb) ? -1 : b - a;
+    // tile-uniform base pointers keep the per-lane addressing to 32-bit offsets
+    auto fetch = [&](const TileDesc &e) {
+        const int nk = (int)(e.k1 - e.k0);
+        const int nr = e.re - e.rs;
+        const int32_t *cp = col + e.k0;
+        const T *vp = val + e.k0;
+        const RP *rp = row_ptr + e.rs;
 #pragma unroll
         for (int u = 0; u < kTileItems; ++u) {
             const int j = tid + u * kBlock;
-            c[u] = j < nk ? col[ka + j] : 0;
-            v[u] = j < nk ? val[ka + j] : (T)0;
+            c[u] = j < nk ? cp[j] : 0;
+            v[u] = j < nk ? vp[j] : (T)0;
         }
 #pragma unroll
         for (int u = 0; u < kRowItems; ++u) {
             const int j = tid + u * kBlock;
-            ro[u] = j <= nr ? (int32_t)(row_ptr[a + j] - ka) : 0;
+            ro[u] = j <= nr ? (int32_t)(rp[j] - e.k0) : 0;
         }
     };
     if (t < t_end) {
-        rs = tile_start[t];
-        re = tile_start[t + 1];
-        k0 = tile_k0[t];
-        k1 = tile_k0[t + 1];
-        fetch(rs, re, k0, k1);
+        d = tiles[t];
+        fetch(d);
     }
     while (t < t_end) {
         const int64_t tn = t + per;
-        int32_t rsn = 0, ren = 0;
-        int64_t k0n = 0, k1n = 0;
-        if (tn < t_end) {
-            rsn = tile_start[tn];
-            ren = tile_start[tn + 1];
-            k0n = tile_k0[tn];
-            k1n = tile_k0[tn + 1];
+        TileDesc dn{0, 0, 0, 0};
+        if (tn < t_end) dn = tiles[tn];
+        const int nk = (int)(d.k1 - d.k0);
+        const int nrows = d.re - d.rs;
+        double xv[kTileItems];
+#pragma unroll
+        for (int u = 0; u < kTileItems; ++u) xv[u] = (double)x[c[u]];
+#pragma unroll
+        for (int u = 0; u < kTileItems; ++u) {
+            const int j = tid + u * kBlock;
+            if (j < nk) prod[j] = (double)v[u] * xv[u];
         }
-        if (is_long(rs, re, k0, k1)) {
-            // one long row: the workgroup strides over it, 4 entries in flight per lane
+#pragma unroll
+        for (int u = 0; u < kRowItems; ++u) {
+            const int j = tid + u * kBlock;
+            if (j <= nrows) roff[j] = ro[u];
+        }
+        if (tn < t_end) fetch(dn);  // in flight during the sums below
+        __syncthreads();
+        const int G = group_size(nrows);
+        const int lg = tid & (G - 1);
+        const int grp = tid / G;
+        const int ngrp = kBlock / G;
+        for (int i = grp; i < nrows; i += ngrp) {
+            const int a = roff[i], b = roff[i + 1];
             double s = 0.0;
-            for (int64_t k = k0 + tid; k < k1; k += 4 * kBlock) {
-                int32_t cc[4];
-                T vv[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int64_t kk = k + u * kBlock;
-                    cc[u] = kk < k1 ? col[kk] : 0;
-                    vv[u] = kk < k1 ? val[kk] : (T)0;
-                }
-                double xv[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) xv[u] = (double)x[cc[u]];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) s += (double)vv[u] * xv[u];
-            }
-            s = block_sum(s, lds4);
-            if (tid == 0) {
+            for (int j = a + lg; j < b; j += G) s += prod[j];
+            for (int off = G >> 1; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+            if (lg == 0) {
                 const T q = (T)s;
-                y[rs] = q;
-                if (FUSED) dot += (double)x[rs] * (double)q;
+                y[d.rs + i] = q;
+                if (FUSED) dot += (double)x[d.rs + i] * (double)q;
             }
-            if (tn < t_end) fetch(rsn, ren, k0n, k1n);
-        } else {
-            const int nk = (int)(k1 - k0);
-            const int nrows = re - rs;
-            double xv[kTileItems];
-#pragma unroll
-            for (int u = 0; u < kTileItems; ++u) xv[u] = (double)x[c[u]];
-#pragma unroll
-            for (int u = 0; u < kTileItems; ++u) {
-                const int j = tid + u * kBlock;
-                if (j < nk) prod[j] = (double)v[u] * xv[u];
-            }
-#pragma unroll
-            for (int u = 0; u < kRowItems; ++u) {
-                const int j = tid + u * kBlock;
-                if (j <= nrows) roff[j] = ro[u];
-            }
-            if (tn < t_end) fetch(rsn, ren, k0n, k1n);  // in flight during the sums below
-            __syncthreads();
-            const int G = group_size(nrows);
-            const int lg = tid & (G - 1);
-            const int grp = tid / G;
-            const int ngrp = kBlock / G;
-            for (int i = grp; i < nrows; i += ngrp) {
-                const int a = roff[i], b = roff[i + 1];
-                double s = 0.0;
-                for (int j = a + lg; j < b; j += G) s += prod[j];
-                for (int off = G >> 1; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-                if (lg == 0) {
-                    const T q = (T)s;
-                    y[rs + i] = q;
-                    if (FUSED) dot += (double)x[rs + i] * (double)q;
-                }
-            }
-            __syncthreads();  // LDS is reused by the next tile
         }
+        __syncthreads();  // LDS is reused by the next tile
         t = tn;
-        rs = rsn;
-        re = ren;
-        k0 = k0n;
-        k1 = k1n;
+        d = dn;
     }
     if (FUSED) {
+        for (int64_t l = blockIdx.x + (int64_t)tid * gridDim.x; l < nlong;
+             l += (int64_t)kBlock * gridDim.x)
+            dot += long_dot[l];
         dot = block_sum(dot, lds4);
         if (tid == 0) store_partial(red.part + blockIdx.x, dot);
         if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, 1, tmp, tot))
@@ -234,11 +238,16 @@ template <typename T, typename RP, bool FUSED>
 void launch_spmv_t(Handle &h, const void *x, void *y, hipStream_t s) {
     const Red red{h.part, h.gpart, h.sync + kCntSpmv * kCountersPerKind};
     if (h.B == 1) {
+        if (h.nlong > 0)
+            hipLaunchKernelGGL((k_spmv_long<T, RP, FUSED>), dim3((unsigned)h.nlong), dim3(kBlock), 0,
+                               s, (const int32_t *)h.long_rows, (const RP *)h.row_ptr,
+                               (const int32_t *)h.col, (const T *)h.vals, (const T *)x, (T *)y,
+                               h.long_dot, (const SysState *)h.st);
         const int64_t grid = spmv_grid(h);
         hipLaunchKernelGGL((k_spmv_tile<T, RP, FUSED>), dim3((unsigned)grid), dim3(kBlock), 0, s,
-                           (const int32_t *)h.tile_start, (const int64_t *)h.tile_k0,
-                           (const RP *)h.row_ptr, (const int32_t *)h.col, (const T *)h.vals,
-                           (const T *)x, (T *)y, h.ntiles, red, h.ctl, h.st, h.d_running);
+                           (const TileDesc *)h.tiles, h.ntiles, (const RP *)h.row_ptr,
+                           (const int32_t *)h.col, (const T *)h.vals, (const T *)x, (T *)y,
+                           (const double *)h.long_dot, h.nlong, red, h.ctl, h.st, h.d_running);
     } else {
         const int J = kBlock / h.B;
         int rpl = 1;
@@ -256,7 +265,8 @@ void launch_spmv_t(Handle &h, const void *x, void *y, hipStream_t s) {
 
 int64_t spmv_grid(const Handle &h) {
     if (h.B == 1) {
-        const int64_t g = (h.ntiles + kXcds - 1) / kXcds * kXcds;  // multiple of the XCD count
+        int64_t g = (h.ntiles + kXcds - 1) / kXcds * kXcds;  // multiple of the XCD count
+        if (g < kXcds) g = kXcds;
         return g < kMaxGrid ? g : kMaxGrid;
     }
     const int J = kBlock / h.B;
