@@ -307,6 +307,13 @@ struct Scratch {
 
 }  // namespace
 
+// spare entries past nnz: column 0, value 0 (read by grouped loads, never used)
+void zero_padding(Handle &h, hipStream_t s) {
+    SLA_HIP(hipMemsetAsync(h.col + h.nnz, 0, (size_t)kEntryPad * 4, s));
+    SLA_HIP(hipMemsetAsync((char *)h.vals + (size_t)h.nnz * h.B * h.vbytes, 0,
+                           (size_t)kEntryPad * h.B * h.vbytes, s));
+}
+
 // ------------------------------------------------------------------ COO input
 
 void build_from_coo(Handle &h, sla_itype rit, const void *rows, sla_itype cit, const void *cols,
@@ -333,7 +340,7 @@ void build_from_coo(Handle &h, sla_itype rit, const void *rows, sla_itype cit, c
         h.nnz = m;
         h.rp64 = m >= (int64_t(1) << 31);
         h.row_ptr = dalloc(h, (size_t)(n + 1) * (h.rp64 ? 8 : 4));
-        h.col = (int32_t *)dalloc(h, (size_t)(m > 0 ? m : 1) * 4);
+        h.col = (int32_t *)dalloc(h, (size_t)(m + kEntryPad) * 4);
         auto launch = [&](auto rtag) {
             using RI = std::remove_const_t<std::remove_pointer_t<decltype(rtag)>>;
             if (h.rp64)
@@ -380,7 +387,7 @@ void build_from_coo(Handle &h, sla_itype rit, const void *rows, sla_itype cit, c
         const int64_t nnz_u = read_i64(excl + (m - 1), s) + read_i64(head + (m - 1), s);
         h.nnz = nnz_u;
         h.rp64 = nnz_u >= (int64_t(1) << 31);
-        h.col = (int32_t *)dalloc(h, (size_t)nnz_u * 4);
+        h.col = (int32_t *)dalloc(h, (size_t)(nnz_u + kEntryPad) * 4);
         h.run = (int64_t *)dalloc(h, (size_t)(nnz_u + 1) * 8);
         h.slot = (int64_t *)dalloc(h, (size_t)m * 8);
         int64_t *urow = sc.get<int64_t>(nnz_u);
@@ -401,7 +408,8 @@ void build_from_coo(Handle &h, sla_itype rit, const void *rows, sla_itype cit, c
         SLA_HIP(hipGetLastError());
         SLA_HIP(hipStreamSynchronize(s));  // host value m above must outlive the copy
     }
-    h.vals = dalloc(h, (size_t)(h.nnz > 0 ? h.nnz : 1) * h.B * h.vbytes);
+    h.vals = dalloc(h, (size_t)(h.nnz + kEntryPad) * h.B * h.vbytes);
+    zero_padding(h, s);
     load_values(h, values, s);
 }
 
@@ -433,7 +441,7 @@ void build_from_csr(Handle &h, sla_itype rit, const void *row_ptr, sla_itype cit
     const size_t rp_bytes = (size_t)(n + 1) * (h.rp64 ? 8 : 4);
     h.row_ptr = dalloc(h, rp_bytes);
     SLA_HIP(hipMemcpyAsync(h.row_ptr, row_ptr, rp_bytes, hipMemcpyDeviceToDevice, s));
-    h.col = (int32_t *)dalloc(h, (size_t)(nnz > 0 ? nnz : 1) * 4);
+    h.col = (int32_t *)dalloc(h, (size_t)(nnz + kEntryPad) * 4);
     if (nnz > 0) {
         if (cit == SLA_I32)
             SLA_HIP(hipMemcpyAsync(h.col, cols, (size_t)nnz * 4, hipMemcpyDeviceToDevice, s));
@@ -442,7 +450,8 @@ void build_from_csr(Handle &h, sla_itype rit, const void *row_ptr, sla_itype cit
                                s, (const int64_t *)cols, nnz, h.col);
         SLA_HIP(hipGetLastError());
     }
-    h.vals = dalloc(h, (size_t)(nnz > 0 ? nnz : 1) * h.B * h.vbytes);
+    h.vals = dalloc(h, (size_t)(nnz + kEntryPad) * h.B * h.vbytes);
+    zero_padding(h, s);
     load_values(h, values, s);
 }
 

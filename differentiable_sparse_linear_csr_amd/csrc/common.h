@@ -24,12 +24,16 @@ namespace sla {
 
 constexpr int kBlock = 256;                        // threads per workgroup (4 wave64)
 constexpr int kWaves = kBlock / 64;
-constexpr int kTileUnits = 1024;                   // rows + entries per SpMV tile window
-constexpr int kLongRow = 512;                      // longer rows get a workgroup each
+constexpr int kTileUnits = 256;                    // rows + entries per SpMV tile (one wavefront)
+constexpr int kLongRow = 128;                      // longer rows get a workgroup each
 constexpr int kTileCap = kTileUnits + kLongRow;    // max entries of a short tile
 constexpr int kMaxGrid = 2048;                     // grid cap of the persistent / grid-stride kernels
 constexpr int kXcds = 8;                           // workgroups go round-robin over 8 XCDs
 constexpr int kMaxBatch = 256;
+// col and values carry this many spare entries past nnz: the SpMV reads
+// entries in 16-byte groups from a 4-aligned base and may touch (never use)
+// up to 3 entries beyond a tile's end.
+constexpr int kEntryPad = 4;
 
 // per-system status codes on the device: running, or an sla_outcome
 constexpr int32_t kRunning = -1;
@@ -123,6 +127,10 @@ struct Handle {
     SysState *h_state = nullptr;  // pinned
     Ctl *h_ctl = nullptr;         // pinned staging for the control block
 
+    // resident workgroups of the persistent SpMV on this device (CUs x occupancy,
+    // a multiple of the XCD count): larger grids would run in two rounds
+    int64_t spmv_resident = kMaxGrid;
+
     // iteration driver
     int check_k = 16;
     bool use_graph = true;
@@ -165,6 +173,7 @@ void iota_i64(int64_t *out, int64_t m, hipStream_t s);
 
 // ------------------------------------------------------------------ SpMV / solve
 void spmv(Handle &h, const void *x, void *y, hipStream_t s);
+void init_launch_limits(Handle &h);
 void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit, sla_info *info,
          hipStream_t s, bool keep_internal_solution);
 void grad_vals(Handle &h, const void *lam_internal, const void *x_user, void *grad, hipStream_t s);
@@ -248,7 +257,7 @@ __device__ __forceinline__ double load_partial(const double *p) {
 }
 
 // Column sums of rows [j0, j1) of a [rows][C] partial table, in row order,
-// read with device-scope loads (8 in flight per lane). Result in out[0..C).
+// read with device-scope loads (4 in flight per lane). Result in out[0..C).
 __device__ __forceinline__ void sum_rows(const double *part, int64_t j0, int64_t j1, int C,
                                          double *tmp, double *out) {
     const int t = threadIdx.x;
@@ -259,15 +268,15 @@ __device__ __forceinline__ void sum_rows(const double *part, int64_t j0, int64_t
         const int r0 = t / Cc;
         double s = 0.0;
         if (c < C && r0 < J) {
-            for (int64_t j = j0 + r0; j < j1; j += 8 * (int64_t)J) {
-                double v[8];
+            for (int64_t j = j0 + r0; j < j1; j += 4 * (int64_t)J) {
+                double v[4];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
+                for (int u = 0; u < 4; ++u) {
                     const int64_t jj = j + (int64_t)u * J;
                     v[u] = jj < j1 ? load_partial(part + jj * C + c) : 0.0;
                 }
 #pragma unroll
-                for (int u = 0; u < 8; ++u) s += v[u];
+                for (int u = 0; u < 4; ++u) s += v[u];
             }
         }
         tmp[t] = s;

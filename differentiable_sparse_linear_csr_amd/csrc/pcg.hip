@@ -122,29 +122,37 @@ __global__ __launch_bounds__(kBlock) void k_update(int64_t n, int B, T *__restri
     const double alpha = L.on ? st[L.b].alpha : 0.0;
     double srz = 0.0, srr = 0.0;
     if (active) {
-        const int64_t step = (int64_t)gridDim.x * L.J * kVecItems;
-        for (int64_t base = (int64_t)blockIdx.x * L.J * kVecItems + L.jr; base < n; base += step) {
+        // pass base (uniform, 64-bit) + per-lane 32-bit offsets
+        const int64_t rows_pass = (int64_t)L.J * kVecItems;
+        for (int64_t r0 = (int64_t)blockIdx.x * rows_pass; r0 < n; r0 += (int64_t)gridDim.x * rows_pass) {
+            const int64_t fb = r0 * B;
+            T *xb = x + fb;
+            T *rb = r + fb;
+            const T *pb = p + fb;
+            const T *qb = q + fb;
+            const T *db = dinv + fb;
+            const int64_t left = n - r0;
             T xv[kVecItems], pv[kVecItems], rv[kVecItems], qv[kVecItems], dv[kVecItems];
 #pragma unroll
             for (int u = 0; u < kVecItems; ++u) {
-                const int64_t i = base + (int64_t)u * L.J;
-                const int64_t f = i * B + L.b;
-                const bool in = i < n;
-                xv[u] = in ? x[f] : (T)0;
-                pv[u] = in ? p[f] : (T)0;
-                rv[u] = in ? r[f] : (T)0;
-                qv[u] = in ? q[f] : (T)0;
-                dv[u] = in ? dinv[f] : (T)0;
+                const int ii = u * L.J + L.jr;
+                const int o = ii * B + L.b;
+                const bool in = ii < left;
+                xv[u] = in ? xb[o] : (T)0;
+                pv[u] = in ? pb[o] : (T)0;
+                rv[u] = in ? rb[o] : (T)0;
+                qv[u] = in ? qb[o] : (T)0;
+                dv[u] = in ? db[o] : (T)0;
             }
 #pragma unroll
             for (int u = 0; u < kVecItems; ++u) {
-                const int64_t i = base + (int64_t)u * L.J;
-                if (i >= n) break;
-                const int64_t f = i * B + L.b;
+                const int ii = u * L.J + L.jr;
+                if (ii >= left) break;
+                const int o = ii * B + L.b;
                 const T xn = (T)((double)xv[u] + alpha * (double)pv[u]);
                 const T rn = (T)((double)rv[u] - alpha * (double)qv[u]);
-                x[f] = xn;
-                r[f] = rn;
+                xb[o] = xn;
+                rb[o] = rn;
                 const double z = (double)dv[u] * (double)rn;
                 srz += (double)rn * z;
                 srr += (double)rn * (double)rn;
@@ -183,6 +191,160 @@ __global__ __launch_bounds__(kBlock) void k_update(int64_t n, int B, T *__restri
     }
 }
 
+// Single-system (B = 1) forms of the update and direction kernels: every
+// array access is 16 bytes per lane (W = 16 / sizeof(T) consecutive rows), so
+// each memory instruction moves twice (fp64) or four times (fp32) the data of
+// the per-row forms; rows past the last full group are done by block 0.
+template <typename T>
+struct VecW {
+    static constexpr int W = 16 / sizeof(T);
+};
+template <typename T>
+__device__ __forceinline__ void vload(const T *p, T (&o)[VecW<T>::W]) {
+    const int4 a = *reinterpret_cast<const int4 *>(p);
+    __builtin_memcpy(o, &a, 16);
+}
+template <typename T>
+__device__ __forceinline__ void vstore(T *p, const T (&o)[VecW<T>::W]) {
+    int4 a;
+    __builtin_memcpy(&a, o, 16);
+    *reinterpret_cast<int4 *>(p) = a;
+}
+
+constexpr int kVecGroups = 2;  // 16-byte groups per lane and pass
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_update1(int64_t n, T *__restrict__ x,
+                                                    T *__restrict__ r, const T *__restrict__ p,
+                                                    const T *__restrict__ q,
+                                                    const T *__restrict__ dinv, Red red,
+                                                    Ctl *__restrict__ ctl,
+                                                    SysState *__restrict__ st,
+                                                    int32_t *__restrict__ h_running) {
+    constexpr int W = VecW<T>::W;
+    __shared__ double lds4[kWaves];
+    __shared__ double tmp[kBlock];
+    __shared__ double tot[2];
+    if (ctl->n_running == 0) return;  // one system: running or not
+    const double alpha = st[0].alpha;
+    const int tid = threadIdx.x;
+    double srz = 0.0, srr = 0.0;
+    auto row = [&](T &xv, T &rv, T pv, T qv, T dv) {
+        xv = (T)((double)xv + alpha * (double)pv);
+        rv = (T)((double)rv - alpha * (double)qv);
+        const double z = (double)dv * (double)rv;
+        srz += (double)rv * z;
+        srr += (double)rv * (double)rv;
+    };
+    const int64_t ng = n / W;
+    const int64_t per_pass = (int64_t)kBlock * kVecGroups;
+    for (int64_t g0 = (int64_t)blockIdx.x * per_pass; g0 < ng; g0 += (int64_t)gridDim.x * per_pass) {
+        T xv[kVecGroups][W], pv[kVecGroups][W], rv[kVecGroups][W], qv[kVecGroups][W],
+            dv[kVecGroups][W];
+#pragma unroll
+        for (int u = 0; u < kVecGroups; ++u) {
+            const int64_t g = g0 + u * kBlock + tid;
+            if (g < ng) {
+                vload(x + g * W, xv[u]);
+                vload(p + g * W, pv[u]);
+                vload(r + g * W, rv[u]);
+                vload(q + g * W, qv[u]);
+                vload(dinv + g * W, dv[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kVecGroups; ++u) {
+            const int64_t g = g0 + u * kBlock + tid;
+            if (g < ng) {
+#pragma unroll
+                for (int k = 0; k < W; ++k) row(xv[u][k], rv[u][k], pv[u][k], qv[u][k], dv[u][k]);
+                vstore(x + g * W, xv[u]);
+                vstore(r + g * W, rv[u]);
+            }
+        }
+    }
+    if (blockIdx.x == 0 && tid < n - ng * W) {
+        const int64_t i = ng * W + tid;
+        T xi = x[i], ri = r[i];
+        row(xi, ri, p[i], q[i], dinv[i]);
+        x[i] = xi;
+        r[i] = ri;
+    }
+    srz = block_sum(srz, lds4);
+    srr = block_sum(srr, lds4);
+    if (tid == 0) {
+        store_partial(red.part + (int64_t)blockIdx.x * 2, srz);
+        store_partial(red.part + (int64_t)blockIdx.x * 2 + 1, srr);
+    }
+    if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, 2, tmp, tot)) {
+        if (tid == 0) {
+            SysState &sy = st[0];
+            const double rz = tot[0], rr = tot[1];
+            int running = 0;
+            sy.rr = rr;
+            sy.iter += 1;
+            if (sqrt(rr) <= ctl->tol * sqrt(sy.bb)) {
+                sy.status = SLA_CONVERGED;
+            } else if (sy.iter >= ctl->maxit) {
+                sy.status = SLA_MAXIT;
+            } else {
+                sy.beta = rz / sy.rho;
+                sy.rho = rz;
+                running = 1;
+            }
+            publish_running(ctl, h_running, running);
+        }
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_direction1(int64_t n, const T *__restrict__ r,
+                                                       T *__restrict__ p,
+                                                       const T *__restrict__ dinv,
+                                                       const Ctl *__restrict__ ctl,
+                                                       const SysState *__restrict__ st) {
+    constexpr int W = VecW<T>::W;
+    if (ctl->n_running == 0) return;
+    const double beta = st[0].beta;
+    const int tid = threadIdx.x;
+    const int64_t ng = n / W;
+    const int64_t per_pass = (int64_t)kBlock * kVecGroups;
+    for (int64_t g0 = (int64_t)blockIdx.x * per_pass; g0 < ng; g0 += (int64_t)gridDim.x * per_pass) {
+        T rv[kVecGroups][W], pv[kVecGroups][W], dv[kVecGroups][W];
+#pragma unroll
+        for (int u = 0; u < kVecGroups; ++u) {
+            const int64_t g = g0 + u * kBlock + tid;
+            if (g < ng) {
+                vload(r + g * W, rv[u]);
+                vload(p + g * W, pv[u]);
+                vload(dinv + g * W, dv[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kVecGroups; ++u) {
+            const int64_t g = g0 + u * kBlock + tid;
+            if (g < ng) {
+#pragma unroll
+                for (int k = 0; k < W; ++k)
+                    pv[u][k] = (T)((double)dv[u][k] * (double)rv[u][k] + beta * (double)pv[u][k]);
+                vstore(p + g * W, pv[u]);
+            }
+        }
+    }
+    if (blockIdx.x == 0 && tid < n - ng * W) {
+        const int64_t i = ng * W + tid;
+        p[i] = (T)((double)dinv[i] * (double)r[i] + beta * (double)p[i]);
+    }
+}
+
+int64_t vec1_grid(int64_t n, int W) {
+    const int64_t per = (int64_t)kBlock * kVecGroups * W;
+    int64_t g = (n + per - 1) / per;
+    if (g > kMaxGrid) g = kMaxGrid;
+    if (g < 1) g = 1;
+    return g;
+}
+
 // p = dinv r + beta p for systems still running
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_direction(int64_t n, int B, const T *__restrict__ r,
@@ -193,22 +355,27 @@ __global__ __launch_bounds__(kBlock) void k_direction(int64_t n, int B, const T 
     const Lanes L(B);
     if (!L.on || st[L.b].status != kRunning) return;
     const double beta = st[L.b].beta;
-    const int64_t step = (int64_t)gridDim.x * L.J * kVecItems;
-    for (int64_t base = (int64_t)blockIdx.x * L.J * kVecItems + L.jr; base < n; base += step) {
+    const int64_t rows_pass = (int64_t)L.J * kVecItems;
+    for (int64_t r0 = (int64_t)blockIdx.x * rows_pass; r0 < n; r0 += (int64_t)gridDim.x * rows_pass) {
+        const int64_t fb = r0 * B;
+        const T *rb = r + fb;
+        const T *db = dinv + fb;
+        T *pb = p + fb;
+        const int64_t left = n - r0;
         T rv[kVecItems], pv[kVecItems], dv[kVecItems];
 #pragma unroll
         for (int u = 0; u < kVecItems; ++u) {
-            const int64_t i = base + (int64_t)u * L.J;
-            const int64_t f = i * B + L.b;
-            const bool in = i < n;
-            rv[u] = in ? r[f] : (T)0;
-            pv[u] = in ? p[f] : (T)0;
-            dv[u] = in ? dinv[f] : (T)0;
+            const int ii = u * L.J + L.jr;
+            const int o = ii * B + L.b;
+            const bool in = ii < left;
+            rv[u] = in ? rb[o] : (T)0;
+            pv[u] = in ? pb[o] : (T)0;
+            dv[u] = in ? db[o] : (T)0;
         }
 #pragma unroll
         for (int u = 0; u < kVecItems; ++u) {
-            const int64_t i = base + (int64_t)u * L.J;
-            if (i < n) p[i * B + L.b] = (T)((double)dv[u] * (double)rv[u] + beta * (double)pv[u]);
+            const int ii = u * L.J + L.jr;
+            if (ii < left) pb[ii * B + L.b] = (T)((double)dv[u] * (double)rv[u] + beta * (double)pv[u]);
         }
     }
 }
@@ -286,15 +453,29 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
     if (lp) lp->end(SLA_KERNEL_SPMV_DOT, a);
     if (lp) lp->begin(SLA_KERNEL_UPDATE, &a);
     const Red red{h.part, h.gpart, h.sync + kCntUpdate * kCountersPerKind};
-    hipLaunchKernelGGL(k_update<T>, dim3((unsigned)g), dim3(kBlock), 0, s, h.n, h.B, (T *)h.x,
-                       (T *)h.r, (const T *)h.p, (const T *)h.q, (const T *)h.dinv, red, h.ctl,
-                       h.st, h.d_running);
+    if (h.B == 1) {
+        const int64_t g1 = vec1_grid(h.n, VecW<T>::W);
+        hipLaunchKernelGGL(k_update1<T>, dim3((unsigned)g1), dim3(kBlock), 0, s, h.n, (T *)h.x,
+                           (T *)h.r, (const T *)h.p, (const T *)h.q, (const T *)h.dinv, red, h.ctl,
+                           h.st, h.d_running);
+    } else {
+        hipLaunchKernelGGL(k_update<T>, dim3((unsigned)g), dim3(kBlock), 0, s, h.n, h.B, (T *)h.x,
+                           (T *)h.r, (const T *)h.p, (const T *)h.q, (const T *)h.dinv, red, h.ctl,
+                           h.st, h.d_running);
+    }
     SLA_HIP(hipGetLastError());
     if (lp) lp->end(SLA_KERNEL_UPDATE, a);
     if (lp) lp->begin(SLA_KERNEL_DIRECTION, &a);
-    hipLaunchKernelGGL(k_direction<T>, dim3((unsigned)g), dim3(kBlock), 0, s, h.n, h.B,
-                       (const T *)h.r, (T *)h.p, (const T *)h.dinv, (const Ctl *)h.ctl,
-                       (const SysState *)h.st);
+    if (h.B == 1) {
+        const int64_t g1 = vec1_grid(h.n, VecW<T>::W);
+        hipLaunchKernelGGL(k_direction1<T>, dim3((unsigned)g1), dim3(kBlock), 0, s, h.n,
+                           (const T *)h.r, (T *)h.p, (const T *)h.dinv, (const Ctl *)h.ctl,
+                           (const SysState *)h.st);
+    } else {
+        hipLaunchKernelGGL(k_direction<T>, dim3((unsigned)g), dim3(kBlock), 0, s, h.n, h.B,
+                           (const T *)h.r, (T *)h.p, (const T *)h.dinv, (const Ctl *)h.ctl,
+                           (const SysState *)h.st);
+    }
     SLA_HIP(hipGetLastError());
     if (lp) lp->end(SLA_KERNEL_DIRECTION, a);
 }

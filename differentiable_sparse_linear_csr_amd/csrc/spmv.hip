@@ -51,8 +51,35 @@ __device__ __forceinline__ void finish_alpha(double *tot, int B, Ctl *ctl, SysSt
     }
 }
 
-constexpr int kTileItems = (kTileCap + kBlock - 1) / kBlock;   // entries per lane, short tile
-constexpr int kRowItems = (kTileUnits + 1 + kBlock - 1) / kBlock; // row offsets per lane
+// A wave tile's entries are read as 4-entry groups from a 4-aligned base:
+// lane l holds entries base + 4*(l + 64*u) .. +3, u < kTileGroups.
+constexpr int kTileGroups = (kTileCap + 3 + 4 * 64 - 1) / (4 * 64);
+constexpr int kRowItems = (kTileUnits + 1 + 63) / 64;  // row offsets per lane
+
+// 16-byte vector types for grouped loads
+template <typename T>
+struct Vec4;
+template <>
+struct Vec4<double> {
+    double2 lo, hi;
+};
+template <>
+struct Vec4<float> {
+    float4 v;
+};
+__device__ __forceinline__ void load4(const double *p, double (&o)[4]) {
+    const double2 a = *reinterpret_cast<const double2 *>(p);
+    const double2 b = *reinterpret_cast<const double2 *>(p + 2);
+    o[0] = a.x; o[1] = a.y; o[2] = b.x; o[3] = b.y;
+}
+__device__ __forceinline__ void load4(const float *p, float (&o)[4]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+}
+__device__ __forceinline__ void load4(const int32_t *p, int32_t (&o)[4]) {
+    const int4 a = *reinterpret_cast<const int4 *>(p);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+}
 
 // Rows longer than kLongRow: one workgroup per row, 8 entries in flight per
 // lane. Runs before the tile kernel; in the fused form it also leaves
@@ -91,55 +118,74 @@ __global__ __launch_bounds__(kBlock) void k_spmv_long(
     }
 }
 
-// Short-row tiles, persistent, in an XCD-contiguous order: workgroup b runs on
-// XCD b % 8, and the workgroups of one XCD walk one contiguous eighth of the
+// Short-row tiles, one wavefront per tile. Every wavefront runs its own
+// software pipeline with its own LDS slice and no workgroup barrier: the next
+// tile's entries and row offsets are loaded while the current tile's fp64
+// products are parked in LDS and summed by G lanes per row (G from the tile's
+// row count). LDS accesses of one wavefront complete in order, so only a
+// wave-level scheduling barrier separates the stores from the sums.
+// Wavefronts walk the tiles in an XCD-contiguous order: workgroup b runs on
+// XCD b % 8, and the wavefronts of one XCD take one contiguous eighth of the
 // tiles, so the gathered vector segments they share stay in that XCD's L2.
-// The loop is software-pipelined: the next tile's entries and row offsets are
-// loaded while the current tile's products are summed. A tile's entries are
-// staged as fp64 products in LDS and its rows are summed by G lanes each (G
-// from the tile's row count). The grid is a multiple of 8, at most kMaxGrid,
+// The grid is persistent (a multiple of 8, at most kMaxGrid workgroups),
 // which also bounds the reduction partials. The fused form adds p.q of its
-// rows (and of the long rows, taken in a fixed order) to the grid reduction.
+// rows, and of the long rows in a fixed order, to the grid reduction.
 template <typename T, typename RP, bool FUSED>
 __global__ __launch_bounds__(kBlock) void k_spmv_tile(
     const TileDesc *__restrict__ tiles, int64_t ntiles, const RP *__restrict__ row_ptr,
     const int32_t *__restrict__ col, const T *__restrict__ val, const T *__restrict__ x,
     T *__restrict__ y, const double *__restrict__ long_dot, int64_t nlong, Red red,
     Ctl *__restrict__ ctl, SysState *__restrict__ st, int32_t *__restrict__ h_running) {
-    __shared__ double prod[kTileCap];
-    __shared__ int32_t roff[kTileUnits + 1];
+    __shared__ double prod_all[kWaves][kTileCap];
+    __shared__ int32_t roff_all[kWaves][kTileUnits + 1];
     __shared__ double lds4[kWaves];
     __shared__ double tmp[kBlock];
     __shared__ double tot[1];
     if (FUSED && st[0].status != kRunning) return;
 
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    double *prod = prod_all[wv];
+    int32_t *roff = roff_all[wv];
     const int xcd = blockIdx.x % kXcds;
-    const int64_t per = gridDim.x / kXcds;
-    int64_t t = ntiles * xcd / kXcds + blockIdx.x / kXcds;
+    const int64_t waves_per_xcd = (int64_t)(gridDim.x / kXcds) * kWaves;
+    const int64_t wid = (int64_t)(blockIdx.x / kXcds) * kWaves + wv;  // rank within its XCD
+    int64_t t = ntiles * xcd / kXcds + wid;
     const int64_t t_end = ntiles * (xcd + 1) / kXcds;
     double dot = 0.0;
 
     TileDesc d{0, 0, 0, 0};
-    int32_t c[kTileItems];
-    T v[kTileItems];
+    int32_t c[kTileGroups][4];
+    T v[kTileGroups][4];
     int32_t ro[kRowItems];
-    // tile-uniform base pointers keep the per-lane addressing to 32-bit offsets
+    // Entries come in 16-byte groups from base = k0 rounded down to a
+    // multiple of 4 (col and val are allocated 256-byte aligned); groups wholly
+    // outside [k0, k1) are not loaded, partial ones are masked when consumed.
+    // Row offsets use a tile-uniform base pointer and 32-bit lane offsets.
     auto fetch = [&](const TileDesc &e) {
-        const int nk = (int)(e.k1 - e.k0);
+        const int64_t base = e.k0 & ~(int64_t)3;
+        const int span = (int)(e.k1 - base);
         const int nr = e.re - e.rs;
-        const int32_t *cp = col + e.k0;
-        const T *vp = val + e.k0;
+        const int32_t *cp = col + base;
+        const T *vp = val + base;
         const RP *rp = row_ptr + e.rs;
 #pragma unroll
-        for (int u = 0; u < kTileItems; ++u) {
-            const int j = tid + u * kBlock;
-            c[u] = j < nk ? cp[j] : 0;
-            v[u] = j < nk ? vp[j] : (T)0;
+        for (int u = 0; u < kTileGroups; ++u) {
+            const int g = 4 * (lane + u * 64);
+            if (g < span) {
+                load4(cp + g, c[u]);
+                load4(vp + g, v[u]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    c[u][k] = 0;
+                    v[u][k] = (T)0;
+                }
+            }
         }
 #pragma unroll
         for (int u = 0; u < kRowItems; ++u) {
-            const int j = tid + u * kBlock;
+            const int j = lane + u * 64;
             ro[u] = j <= nr ? (int32_t)(rp[j] - e.k0) : 0;
         }
     };
@@ -148,30 +194,40 @@ __global__ __launch_bounds__(kBlock) void k_spmv_tile(
         fetch(d);
     }
     while (t < t_end) {
-        const int64_t tn = t + per;
+        const int64_t tn = t + waves_per_xcd;
         TileDesc dn{0, 0, 0, 0};
         if (tn < t_end) dn = tiles[tn];
-        const int nk = (int)(d.k1 - d.k0);
         const int nrows = d.re - d.rs;
-        double xv[kTileItems];
+        const int shift = (int)(d.k0 & 3);           // entries of the first group before k0
+        const int nk = (int)(d.k1 - d.k0);
 #pragma unroll
-        for (int u = 0; u < kTileItems; ++u) xv[u] = (double)x[c[u]];
+        for (int u = 0; u < kTileGroups; ++u) {
+            double xv[4];
 #pragma unroll
-        for (int u = 0; u < kTileItems; ++u) {
-            const int j = tid + u * kBlock;
-            if (j < nk) prod[j] = (double)v[u] * xv[u];
+            for (int k = 0; k < 4; ++k) {
+                const int j = 4 * (lane + u * 64) + k - shift;  // entry index within the tile
+                xv[k] = (double)x[(j >= 0 && j < nk) ? c[u][k] : 0];  // masked lanes read x[0]
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int j = 4 * (lane + u * 64) + k - shift;
+                if (j >= 0 && j < nk) prod[j] = (double)v[u][k] * xv[k];
+            }
         }
 #pragma unroll
         for (int u = 0; u < kRowItems; ++u) {
-            const int j = tid + u * kBlock;
+            const int j = lane + u * 64;
             if (j <= nrows) roff[j] = ro[u];
         }
         if (tn < t_end) fetch(dn);  // in flight during the sums below
-        __syncthreads();
-        const int G = group_size(nrows);
-        const int lg = tid & (G - 1);
-        const int grp = tid / G;
-        const int ngrp = kBlock / G;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        int G = 1;
+        while (G < 64 && G * 2 * nrows <= 64) G *= 2;
+        const int lg = lane & (G - 1);
+        const int grp = lane / G;
+        const int ngrp = 64 / G;
         for (int i = grp; i < nrows; i += ngrp) {
             const int a = roff[i], b = roff[i + 1];
             double s = 0.0;
@@ -183,16 +239,19 @@ __global__ __launch_bounds__(kBlock) void k_spmv_tile(
                 if (FUSED) dot += (double)x[d.rs + i] * (double)q;
             }
         }
-        __syncthreads();  // LDS is reused by the next tile
+        // this wavefront's next stores to its LDS slice come after these reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         t = tn;
         d = dn;
     }
     if (FUSED) {
-        for (int64_t l = blockIdx.x + (int64_t)tid * gridDim.x; l < nlong;
+        for (int64_t l = blockIdx.x + (int64_t)threadIdx.x * gridDim.x; l < nlong;
              l += (int64_t)kBlock * gridDim.x)
             dot += long_dot[l];
         dot = block_sum(dot, lds4);
-        if (tid == 0) store_partial(red.part + blockIdx.x, dot);
+        if (threadIdx.x == 0) store_partial(red.part + blockIdx.x, dot);
         if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, 1, tmp, tot))
             finish_alpha(tot, 1, ctl, st, h_running);
     }
@@ -265,14 +324,37 @@ void launch_spmv_t(Handle &h, const void *x, void *y, hipStream_t s) {
 
 int64_t spmv_grid(const Handle &h) {
     if (h.B == 1) {
-        int64_t g = (h.ntiles + kXcds - 1) / kXcds * kXcds;  // multiple of the XCD count
+        const int64_t blocks = (h.ntiles + kWaves - 1) / kWaves;   // one tile per wavefront
+        int64_t g = (blocks + kXcds - 1) / kXcds * kXcds;         // multiple of the XCD count
         if (g < kXcds) g = kXcds;
-        return g < kMaxGrid ? g : kMaxGrid;
+        return g < h.spmv_resident ? g : h.spmv_resident;
     }
     const int J = kBlock / h.B;
     int rpl = 1;
     while ((h.n + (int64_t)J * rpl - 1) / ((int64_t)J * rpl) > kMaxGrid && rpl < 1024) rpl *= 2;
     return (h.n + (int64_t)J * rpl - 1) / ((int64_t)J * rpl);
+}
+
+// Resident capacity of the persistent tile kernel: every workgroup of the
+// grid must be on a CU at once, or the later ones start only when earlier
+// ones finish and the kernel runs in two rounds.
+void init_launch_limits(Handle &h) {
+    int cus = 0;
+    SLA_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h.device));
+    int per_cu = 0;
+    const void *fn = nullptr;
+    if (h.vt == SLA_F64)
+        fn = h.rp64 ? (const void *)&k_spmv_tile<double, int64_t, true>
+                    : (const void *)&k_spmv_tile<double, int32_t, true>;
+    else
+        fn = h.rp64 ? (const void *)&k_spmv_tile<float, int64_t, true>
+                    : (const void *)&k_spmv_tile<float, int32_t, true>;
+    SLA_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kBlock, 0));
+    int64_t g = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    g = g / kXcds * kXcds;
+    if (g < kXcds) g = kXcds;
+    if (g > kMaxGrid) g = kMaxGrid;
+    h.spmv_resident = g;
 }
 
 // q = A p on the solve workspace, fused with the p.q partials and alpha.
