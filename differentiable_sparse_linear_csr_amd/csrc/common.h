@@ -119,6 +119,7 @@ struct Handle {
     double *part = nullptr;
     int64_t part_len = 0;
     double *gpart = nullptr;      // [kGroups][C] group sums of the grid reductions
+    double *spart = nullptr;      // [spmv grid] p.q partials of the single-system SpMV
     uint32_t *sync = nullptr;     // [kCntKinds][kCountersPerKind] arrival counters
     SysState *st = nullptr;
     Ctl *ctl = nullptr;

@@ -21,6 +21,7 @@
 namespace sla {
 
 void launch_spmv_dot(Handle &h, hipStream_t s);
+int64_t spmv_grid(const Handle &h);
 void launch_spmv_plain(Handle &h, const void *x, void *y, hipStream_t s);
 
 namespace {
@@ -217,7 +218,9 @@ template <typename T>
 __global__ __launch_bounds__(kBlock) void k_update1(int64_t n, T *__restrict__ x,
                                                     T *__restrict__ r, const T *__restrict__ p,
                                                     const T *__restrict__ q,
-                                                    const T *__restrict__ dinv, Red red,
+                                                    const T *__restrict__ dinv,
+                                                    const double *__restrict__ spart,
+                                                    int64_t spart_n, Red red,
                                                     Ctl *__restrict__ ctl,
                                                     SysState *__restrict__ st,
                                                     int32_t *__restrict__ h_running) {
@@ -226,8 +229,20 @@ __global__ __launch_bounds__(kBlock) void k_update1(int64_t n, T *__restrict__ x
     __shared__ double tmp[kBlock];
     __shared__ double tot[2];
     if (ctl->n_running == 0) return;  // one system: running or not
-    const double alpha = st[0].alpha;
     const int tid = threadIdx.x;
+    // sigma = p.q from the SpMV's per-workgroup partials, summed by every
+    // workgroup in the same order (identical in all of them)
+    double sg = 0.0;
+    for (int64_t j = tid; j < spart_n; j += 4 * kBlock) {
+        double v4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v4[u] = j + u * kBlock < spart_n ? spart[j + u * kBlock] : 0.0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sg += v4[u];
+    }
+    const double sigma = block_sum(sg, lds4);
+    const bool breakdown = !(sigma > 0.0) || !isfinite(sigma);
+    const double alpha = breakdown ? 0.0 : st[0].rho / sigma;
     double srz = 0.0, srr = 0.0;
     auto row = [&](T &xv, T &rv, T pv, T qv, T dv) {
         xv = (T)((double)xv + alpha * (double)pv);
@@ -236,7 +251,7 @@ __global__ __launch_bounds__(kBlock) void k_update1(int64_t n, T *__restrict__ x
         srz += (double)rv * z;
         srr += (double)rv * (double)rv;
     };
-    const int64_t ng = n / W;
+    const int64_t ng = breakdown ? 0 : n / W;   // breakdown: x and r stay as they are
     const int64_t per_pass = (int64_t)kBlock * kVecGroups;
     for (int64_t g0 = (int64_t)blockIdx.x * per_pass; g0 < ng; g0 += (int64_t)gridDim.x * per_pass) {
         T xv[kVecGroups][W], pv[kVecGroups][W], rv[kVecGroups][W], qv[kVecGroups][W],
@@ -263,7 +278,7 @@ __global__ __launch_bounds__(kBlock) void k_update1(int64_t n, T *__restrict__ x
             }
         }
     }
-    if (blockIdx.x == 0 && tid < n - ng * W) {
+    if (!breakdown && blockIdx.x == 0 && tid < n - ng * W) {
         const int64_t i = ng * W + tid;
         T xi = x[i], ri = r[i];
         row(xi, ri, p[i], q[i], dinv[i]);
@@ -281,9 +296,15 @@ __global__ __launch_bounds__(kBlock) void k_update1(int64_t n, T *__restrict__ x
             SysState &sy = st[0];
             const double rz = tot[0], rr = tot[1];
             int running = 0;
-            sy.rr = rr;
             sy.iter += 1;
-            if (sqrt(rr) <= ctl->tol * sqrt(sy.bb)) {
+            if (breakdown) {
+                sy.status = SLA_BREAKDOWN;  // x, r untouched; rr keeps the last residual
+            } else {
+                sy.rr = rr;
+            }
+            if (breakdown) {
+                // nothing more: the solve ends here
+            } else if (sqrt(rr) <= ctl->tol * sqrt(sy.bb)) {
                 sy.status = SLA_CONVERGED;
             } else if (sy.iter >= ctl->maxit) {
                 sy.status = SLA_MAXIT;
@@ -456,8 +477,8 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
     if (h.B == 1) {
         const int64_t g1 = vec1_grid(h.n, VecW<T>::W);
         hipLaunchKernelGGL(k_update1<T>, dim3((unsigned)g1), dim3(kBlock), 0, s, h.n, (T *)h.x,
-                           (T *)h.r, (const T *)h.p, (const T *)h.q, (const T *)h.dinv, red, h.ctl,
-                           h.st, h.d_running);
+                           (T *)h.r, (const T *)h.p, (const T *)h.q, (const T *)h.dinv,
+                           (const double *)h.spart, spmv_grid(h), red, h.ctl, h.st, h.d_running);
     } else {
         hipLaunchKernelGGL(k_update<T>, dim3((unsigned)g), dim3(kBlock), 0, s, h.n, h.B, (T *)h.x,
                            (T *)h.r, (const T *)h.p, (const T *)h.q, (const T *)h.dinv, red, h.ctl,

@@ -134,19 +134,19 @@ template <typename T, typename RP, bool FUSED>
 __global__ __launch_bounds__(kBlock) void k_spmv_tile(
     const TileDesc *__restrict__ tiles, int64_t ntiles, const RP *__restrict__ row_ptr,
     const int32_t *__restrict__ col, const T *__restrict__ val, const T *__restrict__ x,
-    T *__restrict__ y, const double *__restrict__ long_dot, int64_t nlong, Red red,
-    Ctl *__restrict__ ctl, SysState *__restrict__ st, int32_t *__restrict__ h_running) {
+    T *__restrict__ y, const double *__restrict__ long_dot, int64_t nlong,
+    double *__restrict__ spart, const SysState *__restrict__ st) {
     __shared__ double prod_all[kWaves][kTileCap];
     __shared__ int32_t roff_all[kWaves][kTileUnits + 1];
+    __shared__ double pown_all[FUSED ? kWaves : 1][FUSED ? kTileUnits : 1];
     __shared__ double lds4[kWaves];
-    __shared__ double tmp[kBlock];
-    __shared__ double tot[1];
     if (FUSED && st[0].status != kRunning) return;
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     double *prod = prod_all[wv];
     int32_t *roff = roff_all[wv];
+    double *pown = pown_all[FUSED ? wv : 0];  // p of the tile's own rows (fused form)
     const int xcd = blockIdx.x % kXcds;
     const int64_t waves_per_xcd = (int64_t)(gridDim.x / kXcds) * kWaves;
     const int64_t wid = (int64_t)(blockIdx.x / kXcds) * kWaves + wv;  // rank within its XCD
@@ -219,6 +219,15 @@ __global__ __launch_bounds__(kBlock) void k_spmv_tile(
             const int j = lane + u * 64;
             if (j <= nrows) roff[j] = ro[u];
         }
+        if (FUSED) {
+            // p of the tile's own rows, loaded next to the gathers (same latency)
+            const T *pp = x + d.rs;
+#pragma unroll
+            for (int u = 0; u < kTileUnits / 64; ++u) {
+                const int i = lane + u * 64;
+                if (i < nrows) pown[i] = (double)pp[i];
+            }
+        }
         if (tn < t_end) fetch(dn);  // in flight during the sums below
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -236,7 +245,7 @@ __global__ __launch_bounds__(kBlock) void k_spmv_tile(
             if (lg == 0) {
                 const T q = (T)s;
                 y[d.rs + i] = q;
-                if (FUSED) dot += (double)x[d.rs + i] * (double)q;
+                if (FUSED) dot += pown[i] * (double)q;
             }
         }
         // this wavefront's next stores to its LDS slice come after these reads
@@ -247,13 +256,14 @@ __global__ __launch_bounds__(kBlock) void k_spmv_tile(
         d = dn;
     }
     if (FUSED) {
+        // this workgroup's p.q partial; the update kernel sums them (every
+        // workgroup there, in block order) and forms alpha, so this kernel
+        // ends without a grid-wide arrival
         for (int64_t l = blockIdx.x + (int64_t)threadIdx.x * gridDim.x; l < nlong;
              l += (int64_t)kBlock * gridDim.x)
             dot += long_dot[l];
         dot = block_sum(dot, lds4);
-        if (threadIdx.x == 0) store_partial(red.part + blockIdx.x, dot);
-        if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, 1, tmp, tot))
-            finish_alpha(tot, 1, ctl, st, h_running);
+        if (threadIdx.x == 0) spart[blockIdx.x] = dot;
     }
 }
 
@@ -306,7 +316,8 @@ void launch_spmv_t(Handle &h, const void *x, void *y, hipStream_t s) {
         hipLaunchKernelGGL((k_spmv_tile<T, RP, FUSED>), dim3((unsigned)grid), dim3(kBlock), 0, s,
                            (const TileDesc *)h.tiles, h.ntiles, (const RP *)h.row_ptr,
                            (const int32_t *)h.col, (const T *)h.vals, (const T *)x, (T *)y,
-                           (const double *)h.long_dot, h.nlong, red, h.ctl, h.st, h.d_running);
+                           (const double *)h.long_dot, h.nlong, h.spart,
+                           (const SysState *)h.st);
     } else {
         const int J = kBlock / h.B;
         int rpl = 1;
