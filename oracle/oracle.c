@@ -411,7 +411,7 @@ int orc_pcg_batched(int64_t n, int32_t batch, const int64_t *row_ptr, const int6
     if (batch < 1 || (vbytes != 4 && vbytes != 8)) return ORC_ERR_INVALID_ARG;
     int64_t nnz = row_ptr[n];
     int err = ORC_OK;
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for schedule(dynamic, 1) if (batch > 1)
     for (int32_t s = 0; s < batch; ++s) {
         int st;
         if (vbytes == 8)
@@ -444,7 +444,7 @@ int orc_adjoint(int64_t n, int32_t batch, const int64_t *row_ptr, const int64_t 
     if (n < 1 || batch < 1 || (vbytes != 4 && vbytes != 8)) return ORC_ERR_INVALID_ARG;
     int64_t nnz = row_ptr[n];
     int err = ORC_OK;
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for schedule(dynamic, 1) if (batch > 1)
     for (int32_t s = 0; s < batch; ++s) {
         int st = ORC_OK;
         int64_t *tp = (int64_t *)malloc((size_t)(n + 1) * sizeof(int64_t));
