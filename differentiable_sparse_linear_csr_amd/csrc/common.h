@@ -329,6 +329,66 @@ __device__ __forceinline__ bool last_block_sums(double *part, double *gpart, uin
     return true;
 }
 
+// Last-block epilogue of a fused SpMV: sigma = p.q per system in tot[0..B);
+// alpha = rho / sigma, or a breakdown when sigma is not > 0 or not finite.
+__device__ __forceinline__ void finish_alpha(const double *tot, int B, Ctl *ctl, SysState *st,
+                                             int32_t *h_running);
+
+// 16-byte vector access: W = 16 / sizeof(T) consecutive elements per lane
+template <typename T>
+struct VecW {
+    static constexpr int W = 16 / sizeof(T);
+};
+template <typename T>
+__device__ __forceinline__ void vload(const T *p, T (&o)[VecW<T>::W]) {
+    const int4 a = *reinterpret_cast<const int4 *>(p);
+    __builtin_memcpy(o, &a, 16);
+}
+template <typename T>
+__device__ __forceinline__ void vstore(T *p, const T (&o)[VecW<T>::W]) {
+    int4 a;
+    __builtin_memcpy(&a, o, 16);
+    *reinterpret_cast<int4 *>(p) = a;
+}
+
+// Per-system block sums when lane t carries the W systems (t % Q) * W + w,
+// w < W (Q = B / W a power of two dividing kBlock): a fixed shuffle tree
+// inside each wavefront, then the wavefront (or lane) rows in order. Writes
+// out[s] for s < B. tmp must hold 4 * kMaxBatch doubles. Ends with a barrier.
+template <int W>
+__device__ __forceinline__ void block_sum_systems(const double (&v)[W], int Q, double *tmp,
+                                                  double *out) {
+    const int t = threadIdx.x;
+    const int B = Q * W;
+    double a[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) a[w] = v[w];
+    int R;
+    if (Q < 64) {
+        for (int off = 32; off >= Q; off >>= 1) {
+#pragma unroll
+            for (int w = 0; w < W; ++w) a[w] += __shfl_xor(a[w], off, 64);
+        }
+        const int l = t & 63;
+        if (l < Q) {
+#pragma unroll
+            for (int w = 0; w < W; ++w) tmp[((t >> 6) * Q + l) * W + w] = a[w];
+        }
+        R = kWaves;
+    } else {
+#pragma unroll
+        for (int w = 0; w < W; ++w) tmp[t * W + w] = a[w];
+        R = kBlock / Q;
+    }
+    __syncthreads();
+    for (int s = t; s < B; s += kBlock) {
+        double sum = 0.0;
+        for (int j = 0; j < R; ++j) sum += tmp[j * B + s];
+        out[s] = sum;
+    }
+    __syncthreads();
+}
+
 // Where a kernel's grid reduction keeps its partials and counters.
 struct Red {
     double *part;
@@ -339,6 +399,26 @@ struct Red {
 __device__ __forceinline__ void publish_running(Ctl *ctl, int32_t *h_running, int32_t v) {
     ctl->n_running = v;
     __hip_atomic_store(h_running, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+__device__ __forceinline__ void finish_alpha(const double *tot, int B, Ctl *ctl, SysState *st,
+                                             int32_t *h_running) {
+    if (threadIdx.x == 0) {
+        int running = 0;
+        for (int b = 0; b < B; ++b) {
+            SysState &s = st[b];
+            if (s.status != kRunning) continue;
+            const double sigma = tot[b];
+            if (!(sigma > 0.0) || !isfinite(sigma)) {
+                s.status = SLA_BREAKDOWN;
+                s.iter += 1;
+            } else {
+                s.alpha = s.rho / sigma;
+                ++running;
+            }
+        }
+        publish_running(ctl, h_running, running);
+    }
 }
 
 template <typename T>

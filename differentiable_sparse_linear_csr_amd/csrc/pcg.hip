@@ -27,6 +27,7 @@ void launch_spmv_plain(Handle &h, const void *x, void *y, hipStream_t s);
 namespace {
 
 constexpr int kVecItems = 4;  // rows per lane and pass (loads issued together)
+constexpr int kVecGroups = 2;  // 16-byte groups per lane and pass
 
 int64_t vec_grid(int64_t n, int B) {
     const int64_t rows = (int64_t)(kBlock / B) * kVecItems;
@@ -104,6 +105,33 @@ __global__ __launch_bounds__(kBlock) void k_init(int64_t n, int B, const T *__re
     }
 }
 
+// Last block of an update: r.z and r.r per system in tot[0..2B); applies the
+// stopping test, the iteration budget and beta.
+__device__ __forceinline__ void finish_update(const double *tot, int B, Ctl *ctl, SysState *st,
+                                              int32_t *h_running) {
+    if (threadIdx.x == 0) {
+        int running = 0;
+        const double tol = ctl->tol;
+        for (int b = 0; b < B; ++b) {
+            SysState &s = st[b];
+            if (s.status != kRunning) continue;
+            const double rz = tot[b], rr = tot[B + b];
+            s.rr = rr;
+            s.iter += 1;
+            if (sqrt(rr) <= tol * sqrt(s.bb)) {
+                s.status = SLA_CONVERGED;
+            } else if (s.iter >= ctl->maxit) {
+                s.status = SLA_MAXIT;
+            } else {
+                s.beta = rz / s.rho;
+                s.rho = rz;
+                ++running;
+            }
+        }
+        publish_running(ctl, h_running, running);
+    }
+}
+
 // x += alpha p, r -= alpha q; partials of r.z and r.r with z = dinv r; the
 // last block applies the stopping test, the iteration budget and beta.
 template <typename T>
@@ -167,52 +195,155 @@ __global__ __launch_bounds__(kBlock) void k_update(int64_t n, int B, T *__restri
     block_sum_per_system(srr, L, tmp, blk);
     if (threadIdx.x < B)
         store_partial(red.part + (int64_t)blockIdx.x * 2 * B + B + threadIdx.x, blk[threadIdx.x]);
-    if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, 2 * B, tmp, tot)) {
-        if (threadIdx.x == 0) {
-            int running = 0;
-            const double tol = ctl->tol;
-            for (int b = 0; b < B; ++b) {
-                SysState &s = st[b];
-                if (s.status != kRunning) continue;
-                const double rz = tot[b], rr = tot[B + b];
-                s.rr = rr;
-                s.iter += 1;
-                if (sqrt(rr) <= tol * sqrt(s.bb)) {
-                    s.status = SLA_CONVERGED;
-                } else if (s.iter >= ctl->maxit) {
-                    s.status = SLA_MAXIT;
-                } else {
-                    s.beta = rz / s.rho;
-                    s.rho = rz;
-                    ++running;
+    if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, 2 * B, tmp, tot))
+        finish_update(tot, B, ctl, st, h_running);
+}
+
+// Batched (B > 1) update and direction with 16-byte accesses, for Q = B / W a
+// power of two (W = 16 / sizeof(T)): chunk c of W consecutive values of the
+// [n][B] layout holds systems (c % Q) * W .. + W - 1 of row c / Q, and since
+// the chunk stride of every lane is a multiple of kBlock, lane t always holds
+// systems (t % Q) * W + w. Systems that are not running keep their values
+// (the stored chunk carries the old bits for them).
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_update_bv(int64_t nc, int B, T *__restrict__ x,
+                                                      T *__restrict__ r, const T *__restrict__ p,
+                                                      const T *__restrict__ q,
+                                                      const T *__restrict__ dinv, Red red,
+                                                      Ctl *__restrict__ ctl,
+                                                      SysState *__restrict__ st,
+                                                      int32_t *__restrict__ h_running) {
+    constexpr int W = VecW<T>::W;
+    __shared__ double tmp[4 * kMaxBatch];
+    __shared__ double blk[kMaxBatch];
+    __shared__ double tot[2 * kMaxBatch];
+    if (ctl->n_running == 0) return;
+    const int Q = B / W;
+    const int t = threadIdx.x;
+    const int s0 = (t & (Q - 1)) * W;
+    bool act[W];
+    double alpha[W];
+    bool any = false;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        act[w] = st[s0 + w].status == kRunning;
+        alpha[w] = act[w] ? st[s0 + w].alpha : 0.0;
+        any |= act[w];
+    }
+    double srz[W], srr[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) srz[w] = srr[w] = 0.0;
+    if (any) {
+        const int64_t per_pass = (int64_t)kBlock * kVecGroups;
+        for (int64_t c0 = (int64_t)blockIdx.x * per_pass; c0 < nc; c0 += (int64_t)gridDim.x * per_pass) {
+            T xv[kVecGroups][W], pv[kVecGroups][W], rv[kVecGroups][W], qv[kVecGroups][W],
+                dv[kVecGroups][W];
+#pragma unroll
+            for (int u = 0; u < kVecGroups; ++u) {
+                const int64_t c = c0 + u * kBlock + t;
+                if (c < nc) {
+                    vload(x + c * W, xv[u]);
+                    vload(p + c * W, pv[u]);
+                    vload(r + c * W, rv[u]);
+                    vload(q + c * W, qv[u]);
+                    vload(dinv + c * W, dv[u]);
                 }
             }
-            publish_running(ctl, h_running, running);
+#pragma unroll
+            for (int u = 0; u < kVecGroups; ++u) {
+                const int64_t c = c0 + u * kBlock + t;
+                if (c >= nc) continue;
+#pragma unroll
+                for (int w = 0; w < W; ++w) {
+                    if (!act[w]) continue;
+                    xv[u][w] = (T)((double)xv[u][w] + alpha[w] * (double)pv[u][w]);
+                    rv[u][w] = (T)((double)rv[u][w] - alpha[w] * (double)qv[u][w]);
+                    const double z = (double)dv[u][w] * (double)rv[u][w];
+                    srz[w] += (double)rv[u][w] * z;
+                    srr[w] += (double)rv[u][w] * (double)rv[u][w];
+                }
+                vstore(x + c * W, xv[u]);
+                vstore(r + c * W, rv[u]);
+            }
         }
     }
+    block_sum_systems<W>(srz, Q, tmp, blk);
+    for (int s = t; s < B; s += kBlock)
+        store_partial(red.part + (int64_t)blockIdx.x * 2 * B + s, blk[s]);
+    block_sum_systems<W>(srr, Q, tmp, blk);
+    for (int s = t; s < B; s += kBlock)
+        store_partial(red.part + (int64_t)blockIdx.x * 2 * B + B + s, blk[s]);
+    if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, 2 * B, tmp, tot))
+        finish_update(tot, B, ctl, st, h_running);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_direction_bv(int64_t nc, int B,
+                                                         const T *__restrict__ r,
+                                                         T *__restrict__ p,
+                                                         const T *__restrict__ dinv,
+                                                         const Ctl *__restrict__ ctl,
+                                                         const SysState *__restrict__ st) {
+    constexpr int W = VecW<T>::W;
+    if (ctl->n_running == 0) return;
+    const int Q = B / W;
+    const int t = threadIdx.x;
+    const int s0 = (t & (Q - 1)) * W;
+    bool act[W];
+    double beta[W];
+    bool any = false;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        act[w] = st[s0 + w].status == kRunning;
+        beta[w] = act[w] ? st[s0 + w].beta : 0.0;
+        any |= act[w];
+    }
+    if (!any) return;
+    const int64_t per_pass = (int64_t)kBlock * kVecGroups;
+    for (int64_t c0 = (int64_t)blockIdx.x * per_pass; c0 < nc; c0 += (int64_t)gridDim.x * per_pass) {
+        T rv[kVecGroups][W], pv[kVecGroups][W], dv[kVecGroups][W];
+#pragma unroll
+        for (int u = 0; u < kVecGroups; ++u) {
+            const int64_t c = c0 + u * kBlock + t;
+            if (c < nc) {
+                vload(r + c * W, rv[u]);
+                vload(p + c * W, pv[u]);
+                vload(dinv + c * W, dv[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kVecGroups; ++u) {
+            const int64_t c = c0 + u * kBlock + t;
+            if (c >= nc) continue;
+#pragma unroll
+            for (int w = 0; w < W; ++w)
+                if (act[w])
+                    pv[u][w] = (T)((double)dv[u][w] * (double)rv[u][w] + beta[w] * (double)pv[u][w]);
+            vstore(p + c * W, pv[u]);
+        }
+    }
+}
+
+template <typename T>
+bool bv_ok(const Handle &h) {
+    constexpr int W = VecW<T>::W;
+    if (h.B < 2 || h.B % W) return false;
+    const int Q = h.B / W;
+    return (Q & (Q - 1)) == 0 && Q <= kBlock;
+}
+
+int64_t bv_grid(int64_t nc) {
+    const int64_t per = (int64_t)kBlock * kVecGroups;
+    int64_t g = (nc + per - 1) / per;
+    if (g > kMaxGrid) g = kMaxGrid;
+    if (g < 1) g = 1;
+    return g;
 }
 
 // Single-system (B = 1) forms of the update and direction kernels: every
 // array access is 16 bytes per lane (W = 16 / sizeof(T) consecutive rows), so
 // each memory instruction moves twice (fp64) or four times (fp32) the data of
 // the per-row forms; rows past the last full group are done by block 0.
-template <typename T>
-struct VecW {
-    static constexpr int W = 16 / sizeof(T);
-};
-template <typename T>
-__device__ __forceinline__ void vload(const T *p, T (&o)[VecW<T>::W]) {
-    const int4 a = *reinterpret_cast<const int4 *>(p);
-    __builtin_memcpy(o, &a, 16);
-}
-template <typename T>
-__device__ __forceinline__ void vstore(T *p, const T (&o)[VecW<T>::W]) {
-    int4 a;
-    __builtin_memcpy(&a, o, 16);
-    *reinterpret_cast<int4 *>(p) = a;
-}
-
-constexpr int kVecGroups = 2;  // 16-byte groups per lane and pass
 
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_update1(int64_t n, T *__restrict__ x,
@@ -479,6 +610,11 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
         hipLaunchKernelGGL(k_update1<T>, dim3((unsigned)g1), dim3(kBlock), 0, s, h.n, (T *)h.x,
                            (T *)h.r, (const T *)h.p, (const T *)h.q, (const T *)h.dinv,
                            (const double *)h.spart, spmv_grid(h), red, h.ctl, h.st, h.d_running);
+    } else if (bv_ok<T>(h)) {
+        const int64_t nc = h.n * h.B / VecW<T>::W;
+        hipLaunchKernelGGL(k_update_bv<T>, dim3((unsigned)bv_grid(nc)), dim3(kBlock), 0, s, nc,
+                           h.B, (T *)h.x, (T *)h.r, (const T *)h.p, (const T *)h.q,
+                           (const T *)h.dinv, red, h.ctl, h.st, h.d_running);
     } else {
         hipLaunchKernelGGL(k_update<T>, dim3((unsigned)g), dim3(kBlock), 0, s, h.n, h.B, (T *)h.x,
                            (T *)h.r, (const T *)h.p, (const T *)h.q, (const T *)h.dinv, red, h.ctl,
@@ -491,6 +627,11 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
         const int64_t g1 = vec1_grid(h.n, VecW<T>::W);
         hipLaunchKernelGGL(k_direction1<T>, dim3((unsigned)g1), dim3(kBlock), 0, s, h.n,
                            (const T *)h.r, (T *)h.p, (const T *)h.dinv, (const Ctl *)h.ctl,
+                           (const SysState *)h.st);
+    } else if (bv_ok<T>(h)) {
+        const int64_t nc = h.n * h.B / VecW<T>::W;
+        hipLaunchKernelGGL(k_direction_bv<T>, dim3((unsigned)bv_grid(nc)), dim3(kBlock), 0, s, nc,
+                           h.B, (const T *)h.r, (T *)h.p, (const T *)h.dinv, (const Ctl *)h.ctl,
                            (const SysState *)h.st);
     } else {
         hipLaunchKernelGGL(k_direction<T>, dim3((unsigned)g), dim3(kBlock), 0, s, h.n, h.B,

@@ -30,29 +30,6 @@ __device__ __forceinline__ int group_size(int nrows) {
     return g;
 }
 
-// Last-block epilogue of the fused SpMV: sigma = p.q per system.
-__device__ __forceinline__ void finish_alpha(double *tot, int B, Ctl *ctl, SysState *st,
-                                             int32_t *h_running) {
-    if (threadIdx.x == 0) {
-        int running = 0;
-        for (int b = 0; b < B; ++b) {
-            SysState &s = st[b];
-            if (s.status != kRunning) continue;
-            const double sigma = tot[b];
-            if (!(sigma > 0.0) || !isfinite(sigma)) {
-                s.status = SLA_BREAKDOWN;
-                s.iter += 1;
-            } else {
-                s.alpha = s.rho / sigma;
-                ++running;
-            }
-        }
-        publish_running(ctl, h_running, running);
-    }
-}
-
-// A wave tile's entries are read as 4-entry groups from a 4-aligned base:
-// lane l holds entries base + 4*(l + 64*u) .. +3, u < kTileGroups.
 constexpr int kTileGroups = (kTileCap + 3 + 4 * 64 - 1) / (4 * 64);
 constexpr int kRowItems = (kTileUnits + 1 + 63) / 64;  // row offsets per lane
 
@@ -267,6 +244,9 @@ __global__ __launch_bounds__(kBlock) void k_spmv_tile(
     }
 }
 
+// Batch sharing one pattern (B > 1), general B: lane (row slot jr, system b)
+// walks its row; the B lanes of a row read one index and B consecutive
+// values, so col_idx / row_ptr are read once for all systems.
 template <typename T, typename RP, bool FUSED>
 __global__ __launch_bounds__(kBlock) void k_spmv_batched(
     int64_t n, int B, int rows_per_lane, const RP *__restrict__ row_ptr,
@@ -303,6 +283,169 @@ __global__ __launch_bounds__(kBlock) void k_spmv_batched(
     }
 }
 
+static int batched_rows_per_lane(const Handle &h) {
+    const int64_t J = kBlock / h.B;
+    int rpl = 1;
+    while ((h.n + J * rpl - 1) / (J * rpl) > kMaxGrid) rpl *= 2;
+    return rpl;
+}
+
+// Batch with Q = B / W a power of two (W = 16 / sizeof(T)): a lane carries W
+// adjacent systems of a row, so each value load, gather, p load and q store
+// is one 16-byte access, and the Q lanes of a row cover an entry's B values
+// as one contiguous run (index and values of an entry are read once for the
+// whole batch). A pass takes kBvRows rows per lane; the loads of a row's
+// first kBvEntries entries are issued together (row pointers, then indices
+// and values, then the gathers), longer rows finish in a loop. Workgroups
+// take contiguous row ranges, XCD-contiguous (workgroup b runs on XCD
+// b % 8; consecutive ranges go to the same XCD so stencil neighbours share
+// its L2).
+constexpr int kBvRows = 2;
+constexpr int kBvEntries = 5;
+
+template <typename T, typename RP, bool FUSED>
+__global__ __launch_bounds__(kBlock) void k_spmv_bvec(
+    int64_t n, int B, int64_t rows_block, const RP *__restrict__ row_ptr,
+    const int32_t *__restrict__ col, const T *__restrict__ val, const T *__restrict__ x,
+    T *__restrict__ y, Red red, Ctl *__restrict__ ctl, SysState *__restrict__ st,
+    int32_t *__restrict__ h_running) {
+    constexpr int W = VecW<T>::W;
+    __shared__ double tmp[4 * kMaxBatch];
+    __shared__ double tot[kMaxBatch];
+    __shared__ double blk[kMaxBatch];
+    if (FUSED && ctl->n_running == 0) return;
+    const int Q = B / W;
+    const int t = threadIdx.x;
+    const int s0 = (t & (Q - 1)) * W;
+    const int J = kBlock / Q;
+    const int jr = t / Q;
+    bool any = !FUSED;
+    if (FUSED) {
+#pragma unroll
+        for (int k = 0; k < W; ++k) any |= st[s0 + k].status == kRunning;
+    }
+    const int64_t G = gridDim.x;  // a multiple of kXcds
+    const int64_t lb = (int64_t)(blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
+    const int64_t r_begin = lb * rows_block;
+    const int64_t r_end = r_begin + rows_block < n ? r_begin + rows_block : n;
+    double dot[W];
+#pragma unroll
+    for (int k = 0; k < W; ++k) dot[k] = 0.0;
+    if (any) {
+        for (int64_t r0 = r_begin; r0 < r_end; r0 += (int64_t)J * kBvRows) {
+            int64_t ri[kBvRows], ka[kBvRows], kb[kBvRows];
+#pragma unroll
+            for (int u = 0; u < kBvRows; ++u) {
+                ri[u] = r0 + (int64_t)u * J + jr;
+                const bool in = ri[u] < r_end;
+                ka[u] = in ? (int64_t)row_ptr[ri[u]] : 0;
+                kb[u] = in ? (int64_t)row_ptr[ri[u] + 1] : 0;
+            }
+            int32_t c[kBvRows][kBvEntries];
+            T v[kBvRows][kBvEntries][W], xv[kBvRows][kBvEntries][W], pv[kBvRows][W];
+#pragma unroll
+            for (int u = 0; u < kBvRows; ++u)
+#pragma unroll
+                for (int e = 0; e < kBvEntries; ++e) {
+                    const int64_t k = ka[u] + e;
+                    if (k < kb[u]) {
+                        c[u][e] = col[k];
+                        vload(val + k * B + s0, v[u][e]);
+                    } else {
+                        c[u][e] = 0;
+#pragma unroll
+                        for (int w = 0; w < W; ++w) v[u][e][w] = (T)0;
+                    }
+                }
+#pragma unroll
+            for (int u = 0; u < kBvRows; ++u) {
+#pragma unroll
+                for (int e = 0; e < kBvEntries; ++e) {
+                    if (ka[u] + e < kb[u]) {
+                        vload(x + (int64_t)c[u][e] * B + s0, xv[u][e]);
+                    } else {
+#pragma unroll
+                        for (int w = 0; w < W; ++w) xv[u][e][w] = (T)0;
+                    }
+                }
+                if (FUSED) {
+                    if (ri[u] < r_end) {
+                        vload(x + ri[u] * B + s0, pv[u]);
+                    } else {
+#pragma unroll
+                        for (int w = 0; w < W; ++w) pv[u][w] = (T)0;
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kBvRows; ++u) {
+                if (ri[u] >= r_end) continue;
+                double sum[W];
+#pragma unroll
+                for (int w = 0; w < W; ++w) sum[w] = 0.0;
+#pragma unroll
+                for (int e = 0; e < kBvEntries; ++e)
+#pragma unroll
+                    for (int w = 0; w < W; ++w) sum[w] += (double)v[u][e][w] * (double)xv[u][e][w];
+                for (int64_t k = ka[u] + kBvEntries; k < kb[u]; ++k) {
+                    T a[W], b[W];
+                    vload(val + k * B + s0, a);
+                    vload(x + (int64_t)col[k] * B + s0, b);
+#pragma unroll
+                    for (int w = 0; w < W; ++w) sum[w] += (double)a[w] * (double)b[w];
+                }
+                T qv[W];
+#pragma unroll
+                for (int w = 0; w < W; ++w) qv[w] = (T)sum[w];
+                vstore(y + ri[u] * B + s0, qv);
+                if (FUSED) {
+#pragma unroll
+                    for (int w = 0; w < W; ++w) dot[w] += (double)pv[u][w] * (double)qv[w];
+                }
+            }
+        }
+    }
+    if (FUSED) {
+        block_sum_systems<W>(dot, Q, tmp, blk);
+        for (int s = t; s < B; s += kBlock)
+            store_partial(red.part + (int64_t)blockIdx.x * B + s, blk[s]);
+        if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, B, tmp, tot))
+            finish_alpha(tot, B, ctl, st, h_running);
+    }
+}
+
+template <typename T>
+bool bvec_ok(const Handle &h) {
+    constexpr int W = VecW<T>::W;
+    if (h.B < 2 || h.B % W) return false;
+    const int Q = h.B / W;
+    return (Q & (Q - 1)) == 0 && Q <= kBlock;
+}
+
+// rows per workgroup of the vectorized batched kernel: whole passes, grid
+// within kMaxGrid
+template <typename T>
+int64_t bvec_rows_block(const Handle &h) {
+    const int64_t rows_pass = (int64_t)(kBlock / (h.B / VecW<T>::W)) * kBvRows;
+    int64_t passes = 1;
+    while ((h.n + rows_pass * passes - 1) / (rows_pass * passes) > kMaxGrid) passes *= 2;
+    return rows_pass * passes;
+}
+
+template <typename T>
+int64_t bvec_grid(const Handle &h) {
+    const int64_t rb = bvec_rows_block<T>(h);
+    const int64_t g = (h.n + rb - 1) / rb;
+    return (g + kXcds - 1) / kXcds * kXcds;
+}
+
+template <typename T>
+int64_t batched_grid_t(const Handle &h) {
+    if (bvec_ok<T>(h)) return bvec_grid<T>(h);
+    const int64_t rows_block = (int64_t)(kBlock / h.B) * batched_rows_per_lane(h);
+    return (h.n + rows_block - 1) / rows_block;
+}
+
 template <typename T, typename RP, bool FUSED>
 void launch_spmv_t(Handle &h, const void *x, void *y, hipStream_t s) {
     const Red red{h.part, h.gpart, h.sync + kCntSpmv * kCountersPerKind};
@@ -318,15 +461,16 @@ void launch_spmv_t(Handle &h, const void *x, void *y, hipStream_t s) {
                            (const int32_t *)h.col, (const T *)h.vals, (const T *)x, (T *)y,
                            (const double *)h.long_dot, h.nlong, h.spart,
                            (const SysState *)h.st);
+    } else if (bvec_ok<T>(h)) {
+        hipLaunchKernelGGL((k_spmv_bvec<T, RP, FUSED>), dim3((unsigned)bvec_grid<T>(h)),
+                           dim3(kBlock), 0, s, h.n, h.B, bvec_rows_block<T>(h),
+                           (const RP *)h.row_ptr, (const int32_t *)h.col, (const T *)h.vals,
+                           (const T *)x, (T *)y, red, h.ctl, h.st, h.d_running);
     } else {
-        const int J = kBlock / h.B;
-        int rpl = 1;
-        while ((h.n + (int64_t)J * rpl - 1) / ((int64_t)J * rpl) > kMaxGrid && rpl < 1024) rpl *= 2;
-        const int64_t grid = (h.n + (int64_t)J * rpl - 1) / ((int64_t)J * rpl);
-        hipLaunchKernelGGL((k_spmv_batched<T, RP, FUSED>), dim3((unsigned)grid), dim3(kBlock), 0,
-                           s, h.n, h.B, rpl, (const RP *)h.row_ptr, (const int32_t *)h.col,
-                           (const T *)h.vals, (const T *)x, (T *)y, red, h.ctl, h.st,
-                           h.d_running);
+        hipLaunchKernelGGL((k_spmv_batched<T, RP, FUSED>), dim3((unsigned)batched_grid_t<T>(h)),
+                           dim3(kBlock), 0, s, h.n, h.B, batched_rows_per_lane(h),
+                           (const RP *)h.row_ptr, (const int32_t *)h.col, (const T *)h.vals,
+                           (const T *)x, (T *)y, red, h.ctl, h.st, h.d_running);
     }
     SLA_HIP(hipGetLastError());
 }
@@ -340,10 +484,7 @@ int64_t spmv_grid(const Handle &h) {
         if (g < kXcds) g = kXcds;
         return g < h.spmv_resident ? g : h.spmv_resident;
     }
-    const int J = kBlock / h.B;
-    int rpl = 1;
-    while ((h.n + (int64_t)J * rpl - 1) / ((int64_t)J * rpl) > kMaxGrid && rpl < 1024) rpl *= 2;
-    return (h.n + (int64_t)J * rpl - 1) / ((int64_t)J * rpl);
+    return h.vt == SLA_F64 ? batched_grid_t<double>(h) : batched_grid_t<float>(h);
 }
 
 // Resident capacity of the persistent tile kernel: every workgroup of the

@@ -19,6 +19,7 @@ CASES = [
     ("diffusion3d_128", 24, None),
     ("knn_laplacian_2m", 20000, None),
     ("batched_diffusion2d_512x32", 48, 6),
+    ("batched_diffusion2d_512x32", 40, 8),
 ]
 
 
@@ -135,6 +136,47 @@ def test_batched_mixed_outcomes():
         assert abs(info.iterations[s] - ito[s]) <= 2
         assert rel(host(x[s]), xo[s]) <= 1e-4
     assert info.iterations[2] == 0 and info.status[2] == _lib.SLA_CONVERGED
+
+
+def shifted_batch(N, B, dtype, broken=None, seed=0):
+    """B value sets on the N x N five-point pattern: system s has its diagonal
+    raised by 0.05 s (different iteration counts); system `broken` has its
+    off-diagonals scaled by 5 (positive diagonal, indefinite)."""
+    r, c, v = poisson2d_coo(N)
+    V = np.tile(v, (B, 1))
+    diag = r == c
+    for s in range(B):
+        V[s, diag] += 0.05 * s
+    if broken is not None:
+        V[broken, ~diag] *= 5.0
+    b = np.random.default_rng(seed).standard_normal((B, N * N))
+    return r, c, V.astype(dtype), b.astype(dtype)
+
+
+@pytest.mark.parametrize("dtype,B", [(np.float32, 8), (np.float64, 8), (np.float32, 256),
+                                     (np.float64, 256)])
+def test_batched_vector_lanes_mixed_outcomes(dtype, B):
+    # systems of one lane (4 in fp32, 2 in fp64) converge, break down and stop
+    # at different iterations; frozen systems must keep x untouched
+    N = 20 if B == 8 else 12
+    r, c, V, b = shifted_batch(N, B, dtype, broken=5)
+    b[2] = 0.0
+    b[5] = 1.0   # z = D^-1 1 makes p.Ap < 0 at the first step
+    A = coo_handle(N * N, r, c, V)
+    ref = oracle.coo_to_csr(N * N, r, c, V)
+    tol = 1e-6 if dtype == np.float32 else 1e-10
+    x, info = A.solve_raw(dev(b), tol, 300)
+    xo, ito, rlo, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, tol, 300)
+    X = host(x)
+    xtol = 1e-4 if dtype == np.float32 else 1e-8
+    assert info.status[2] == _lib.SLA_CONVERGED and info.iterations[2] == 0
+    assert info.status[5] == _lib.SLA_BREAKDOWN and info.iterations[5] == 1
+    assert not X[2].any() and not X[5].any()
+    assert len(set(info.iterations)) > 3
+    for s in range(B):
+        assert info.status[s] == oco[s], s
+        assert abs(info.iterations[s] - ito[s]) <= 2, (s, info.iterations[s], ito[s])
+        assert rel(X[s], xo[s]) <= xtol, (s, rel(X[s], xo[s]))
 
 
 def test_irregular_spd_with_long_rows_and_duplicates():

@@ -75,6 +75,23 @@ def test_batched(B):
     check(A, w.rows, w.cols, v64, w.n, w.b.astype(np.float64), 1e-12)
 
 
+@pytest.mark.parametrize("dtype,B", [(np.float32, 4), (np.float32, 8), (np.float32, 12),
+                                     (np.float32, 256), (np.float64, 2), (np.float64, 16),
+                                     (np.float64, 256)])
+def test_batched_irregular(dtype, B):
+    # empty, short and long rows (past the batched kernels' prefetch window and
+    # the long-row limit) with B value sets; a ragged last workgroup
+    n = 2003
+    lengths = np.random.default_rng(3).integers(0, 12, n)
+    lengths[[3, 4, n - 1]] = 0
+    lengths[10], lengths[500], lengths[n - 2] = 40, 700, 9
+    r, c, v = adversarial.rows_of_lengths(lengths, n, seed=3)
+    V = np.random.default_rng(4).standard_normal((B, v.shape[0])).astype(dtype)
+    A = coo_handle(n, r, c, V)
+    x = np.random.default_rng(5).standard_normal((B, n)).astype(dtype)
+    check(A, r, c, V, n, x, 1e-12 if dtype == np.float64 else 1e-5)
+
+
 def test_deterministic_bitwise():
     n = 50000
     r, c, v = adversarial.random_spd_coo(n, 12.0, 3, max_row=20000)
