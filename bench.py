@@ -31,7 +31,10 @@ sys.path.insert(0, ROOT)
 METRIC = "Jacobi-PCG iterations/sec and achieved HBM GB/s (% of peak) at 2M and 133M DOF"
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "diffusion3d_128"
-KERNEL_SOURCES = ["spmv.hip", "common.h"]
+# sources of the kernel the roofline covers, per kernel tag (counter files are
+# only used while these sources are unchanged)
+KERNEL_SOURCES = {"spmv_dot": ["spmv.hip", "common.h"],
+                  "cg_resident": ["resident.hip", "common.h"]}
 
 
 def algorithmic_bytes(n, nnz, B, V, R):
@@ -46,23 +49,24 @@ def algorithmic_bytes(n, nnz, B, V, R):
     }
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(tag: str) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[tag]:
         with open(os.path.join(ROOT, "differentiable_sparse_linear_csr_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
-    """Per-launch HBM bytes of the fused SpMV from rocprofv3 counters, if they
-    were taken on the current kernel source (profiles/counters_<workload>.json)."""
-    path = os.path.join(ROOT, "profiles", f"spmv_dot_counters_{workload}.json")
+def load_traffic(workload: str, tag: str):
+    """Per-launch HBM bytes of the roofline kernel from rocprofv3 counters, if
+    they were taken on the current kernel source
+    (profiles/<tag>_counters_<workload>.json)."""
+    path = os.path.join(ROOT, "profiles", f"{tag}_counters_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(tag):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -173,7 +177,7 @@ def main() -> int:
     # profiled step: hipEvents around every kernel launch, on the launch stream
     A.profile_reset()
     A.set_option(_lib.SLA_OPT_PROFILE, 1)
-    step()
+    prof_its, _ = step()
     prof = A.profile()
     # plain SpMV y = A x (sla_spmv), timed the same way, for SpMV GFLOP/s
     A.profile_reset()
@@ -186,11 +190,25 @@ def main() -> int:
     V = 8 if w.dtype == "f64" else 4
     R = 8 if A.row_index_dtype == torch.int64 else 4
     ab = algorithmic_bytes(w.n, w.nnz, w.batch, V, R)
-    launches, total_ms = prof["spmv_dot"]
-    avg_ms = total_ms / max(launches, 1)
-    achieved = ab["spmv"] / (avg_ms * 1e-3) / 1e9
-    traffic = load_traffic(w.name)
-    per_iter_ms = sum(prof[k][1] for k in ("spmv_dot", "update", "direction")) / max(launches, 1)
+    res_launches, res_ms = prof["cg_resident"]
+    if res_launches > 0:
+        # whole solves in one cooperative kernel: per iteration the matrix, the
+        # p gathers and the p store (x, r, p, dinv stay on chip); plus b and
+        # dinv read and x written once per solve
+        launches, total_ms = res_launches, res_ms
+        avg_ms = total_ms / launches
+        bytes_launch = prof_its / launches * ab["spmv"] + 3 * V * w.n * w.batch
+        per_iter_ms = total_ms / max(prof_its, 1)
+        kernel = "k_cg_resident (whole solve per launch: SpMV, p.q, update, r.z/r.r, direction)"
+    else:
+        launches, total_ms = prof["spmv_dot"]
+        avg_ms = total_ms / max(launches, 1)
+        bytes_launch = ab["spmv"]
+        per_iter_ms = sum(prof[k][1] for k in ("spmv_dot", "update", "direction")) / max(launches, 1)
+        kernel = ("k_spmv_tile (fused q = A p, p.q partials)" if w.batch == 1
+                  else "k_spmv_bvec (fused q = A p, p.q partials, alpha)")
+    achieved = bytes_launch / (avg_ms * 1e-3) / 1e9
+    traffic = load_traffic(w.name, "cg_resident" if res_launches > 0 else "spmv_dot")
 
     out = {
         "metric": METRIC,
@@ -216,15 +234,14 @@ def main() -> int:
             "check_interval": args.check_interval,
         },
         "roofline": {
-            "kernel": "k_spmv_tile (fused q = A p, p.q partials, alpha)" if w.batch == 1
-            else "k_spmv_batched (fused q = A p, p.q partials, alpha)",
+            "kernel": kernel,
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": ab["spmv"],
+            "algorithmic_bytes_per_launch": round(bytes_launch),
             "avg_launch_ms": round(avg_ms, 5),
             "launches_timed": launches,
         },
@@ -233,7 +250,8 @@ def main() -> int:
             "iteration_ms": round(per_iter_ms, 5),
             "iteration_gbps_3k": round(ab["iter_3k"] / (per_iter_ms * 1e-3) / 1e9, 1),
             "iteration_frac_3k": round(ab["iter_3k"] / (per_iter_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "spmv_dot_gflops": round(2 * w.nnz * w.batch / (avg_ms * 1e-3) / 1e9, 1),
+            "iteration_gbps_min": round(ab["iter_min"] / (per_iter_ms * 1e-3) / 1e9, 1),
+            "path": "single cooperative kernel" if res_launches > 0 else "per-step kernels",
             "spmv_plain_ms": round(plain_ms / max(plain_n, 1), 5),
             "spmv_plain_gflops": round(2 * w.nnz * w.batch / (plain_ms / max(plain_n, 1) * 1e-3) / 1e9, 1),
             "spmv_plain_gbps": round(ab["spmv"] / (plain_ms / max(plain_n, 1) * 1e-3) / 1e9, 1),

@@ -30,8 +30,9 @@ SLA_I32, SLA_I64 = 0, 1
 SLA_INPUT_COO, SLA_INPUT_CSR = 0, 1
 SLA_FLAG_CHECK_SYMMETRIC = 1
 SLA_CONVERGED, SLA_MAXIT, SLA_BREAKDOWN = 0, 1, 2
-SLA_OPT_CHECK_INTERVAL, SLA_OPT_USE_GRAPH, SLA_OPT_PROFILE = 1, 2, 3
-KERNELS = {"spmv_dot": 0, "update": 1, "direction": 2, "init": 3, "spmv": 4, "grad": 5}
+SLA_OPT_CHECK_INTERVAL, SLA_OPT_USE_GRAPH, SLA_OPT_PROFILE, SLA_OPT_RESIDENT = 1, 2, 3, 4
+KERNELS = {"spmv_dot": 0, "update": 1, "direction": 2, "init": 3, "spmv": 4, "grad": 5,
+           "cg_resident": 6}
 
 EXPORTS = ["sla_csr_create", "sla_csr_set_values", "sla_csr_get", "sla_csr_get_pattern",
            "sla_csr_get_values",

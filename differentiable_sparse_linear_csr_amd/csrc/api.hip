@@ -257,6 +257,10 @@ sla_status sla_csr_set_option(sla_csr hd, int32_t key, int64_t value) {
             case SLA_OPT_PROFILE:
                 h->profile = value != 0;
                 break;
+            case SLA_OPT_RESIDENT:
+                if (value < 0 || value > 2) fail(SLA_ERR_INVALID_ARG, "resident mode in [0, 2]");
+                h->res_mode = (int)value;
+                break;
             default:
                 fail(SLA_ERR_INVALID_ARG, "unknown option");
         }

@@ -132,6 +132,16 @@ struct Handle {
     // a multiple of the XCD count): larger grids would run in two rounds
     int64_t spmv_resident = kMaxGrid;
 
+    // single-system solve as one cooperative kernel with on-chip vectors
+    // (built at the first solve that can use it; -1: not applicable)
+    int res_state = 0;
+    int res_mode = 1;              // 0 never, 1 automatic, 2 whenever applicable
+    int64_t res_grid = 0;          // workgroups (one per CU at most)
+    int64_t res_rows_per_wave = 0;
+    TileDesc *res_tiles = nullptr; // tiles that never cross a wavefront's row range
+    int32_t *res_wave = nullptr;   // [2][waves+1]: first row, first tile of each wavefront
+    uint64_t *res_slot = nullptr;  // [2][res_grid][4] stamped all-reduce partials
+
     // iteration driver
     int check_k = 16;
     bool use_graph = true;
@@ -178,6 +188,8 @@ void init_launch_limits(Handle &h);
 void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit, sla_info *info,
          hipStream_t s, bool keep_internal_solution);
 void grad_vals(Handle &h, const void *lam_internal, const void *x_user, void *grad, hipStream_t s);
+bool resident_ready(Handle &h, hipStream_t s);   // builds the plan on first use
+void resident_solve(Handle &h, const void *b, double tol, int32_t maxit, hipStream_t s);
 void flush_profile(Handle &h);
 
 // ------------------------------------------------------------------ device helpers
@@ -349,6 +361,21 @@ __device__ __forceinline__ void vstore(T *p, const T (&o)[VecW<T>::W]) {
     int4 a;
     __builtin_memcpy(&a, o, 16);
     *reinterpret_cast<int4 *>(p) = a;
+}
+
+// Four consecutive elements through 16-byte loads (p 16-byte aligned)
+__device__ __forceinline__ void load4(const double *p, double (&o)[4]) {
+    const double2 a = *reinterpret_cast<const double2 *>(p);
+    const double2 b = *reinterpret_cast<const double2 *>(p + 2);
+    o[0] = a.x; o[1] = a.y; o[2] = b.x; o[3] = b.y;
+}
+__device__ __forceinline__ void load4(const float *p, float (&o)[4]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+}
+__device__ __forceinline__ void load4(const int32_t *p, int32_t (&o)[4]) {
+    const int4 a = *reinterpret_cast<const int4 *>(p);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
 }
 
 // Per-system block sums when lane t carries the W systems (t % Q) * W + w,

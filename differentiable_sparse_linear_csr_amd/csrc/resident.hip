@@ -1,0 +1,495 @@
+// Single-system Jacobi-PCG as one cooperative kernel whose vectors stay on
+// chip. The recurrence is the textbook PCG of the multi-kernel path (torch-sla,
+// pytorch-native CG backend with Jacobi preconditioning; distributed-CG
+// paragraph: every tensor stays on the device and the step sizes come from
+// global reductions); only where the data lives changes.
+//
+// One workgroup of kRT = 512 threads per CU at most, all co-resident
+// (cooperative launch). Wavefront w owns a contiguous range of at most
+// 64 * kRJ rows and holds x, r, p and dinv of those rows in registers for the
+// whole solve (lane l holds rows R0 + l + 64 j). Per iteration:
+//   A   q = A p over the wavefront's own tiles, gathering p from a global copy;
+//       q goes to the wavefront's LDS slice; p.q from registers and LDS
+//   R1  grid all-reduce of p.q -> alpha, or breakdown
+//   B   x += alpha p, r -= alpha q, z = dinv r; r.z and r.r
+//   R2  grid all-reduce -> stopping test, iteration budget, beta
+//   C   p = z + beta p; own rows written to the global copy
+//   R3  grid barrier: the copy is complete before the next gathers
+// so HBM sees the matrix, the p gathers and the p store per iteration.
+//
+// All-reduces: every workgroup stores its partials, stamped with a sequence
+// number, with device-coherent stores; every workgroup polls all stamped
+// partials and sums them itself in block order with one fixed tree, so every
+// workgroup holds the same bits and takes the same stopping decisions. Polls are bounded: a workgroup that waits
+// longer than kSpinLimit polls reports a failure instead of hanging.
+#include "common.h"
+
+#include <vector>
+
+namespace sla {
+
+namespace {
+
+constexpr int kRT = 512;              // threads per workgroup
+constexpr int kRW = kRT / 64;         // wavefronts per workgroup
+constexpr int kRJ = 16;               // rows per lane held in registers, at most
+// tiles of at most kRUnits rows + entries: with the up-to-3 entries before k0
+// of the first 16-byte group, a tile's entries fit one group per lane
+constexpr int kRUnits = 4 * 64 - 3;
+constexpr int kRGroups = 1;
+constexpr int kRRowItems = (kRUnits + 1 + 63) / 64;
+constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr int kResFailed = 100;       // status written when a wait timed out
+constexpr int64_t kResidentAutoRows = 1 << 15;
+
+// sum over the workgroup with a fixed tree (identical in every workgroup)
+__device__ __forceinline__ double rblock_sum(double v, double *lds) {
+    v = wave_sum(v);
+    const int wv = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) lds[wv] = v;
+    __syncthreads();
+    double s = 0.0;
+#pragma unroll
+    for (int w = 0; w < kRW; ++w) s += lds[w];
+    __syncthreads();
+    return s;
+}
+
+// a value that is the same in every lane, moved to scalar registers
+__device__ __forceinline__ double uniform(double v) {
+    const uint64_t u = __double_as_longlong(v);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return __longlong_as_double((int64_t)(((uint64_t)hi << 32) | lo));
+}
+
+struct GridSync {
+    uint64_t *slot;  // [2][G][2 * kMaxC] stamped halves of each workgroup's partials
+    int G;
+};
+constexpr int kMaxC = 2;
+
+// Grid all-reduce of C values (block totals, valid in every thread).
+// A partial travels as two 64-bit words, (seq << 32 | upper half) and
+// (seq << 32 | lower half), each written and read single-copy atomically,
+// so a poll that sees both stamps equal to seq has the partial: arrival and
+// value arrive in one round trip, with no separate flag and no ordering
+// between the two stores. Slots alternate with the parity of seq: a
+// workgroup rewrites a slot only after every workgroup has passed the next
+// all-reduce, i.e. has read this one. With `publish`, every global store this
+// workgroup made before the call is complete before its partials are written,
+// so other workgroups see that data once they return. Returns false on a
+// timed-out wait.
+template <int C>
+__device__ __forceinline__ bool grid_allreduce(const GridSync &gs, uint32_t seq, const double (&v)[C],
+                                               double (&tot)[C], double *lds, bool publish) {
+    const int t = threadIdx.x;
+    uint64_t *slot = gs.slot + (size_t)(seq & 1u) * gs.G * (2 * kMaxC);
+    if (publish) {
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+    const uint64_t stamp = (uint64_t)seq << 32;
+    if (t < 2 * C) {
+        const uint64_t bits = (uint64_t)__double_as_longlong(v[t >> 1]);
+        const uint64_t half = (t & 1) ? (bits & 0xffffffffull) : (bits >> 32);
+        __hip_atomic_store(slot + blockIdx.x * (2 * kMaxC) + t, stamp | half, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    uint64_t w[2 * C];
+    uint32_t spins = 0;
+    while (true) {
+        bool arrived = true;
+        if (t < gs.G) {
+#pragma unroll
+            for (int k = 0; k < 2 * C; ++k)
+                w[k] = __hip_atomic_load(slot + t * (2 * kMaxC) + k, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int k = 0; k < 2 * C; ++k) arrived &= (w[k] >> 32) == seq;
+        }
+        if (__syncthreads_and(arrived)) break;
+        if (++spins > kSpinLimit) return false;
+        __builtin_amdgcn_s_sleep(1);
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        double a = 0.0;
+        if (t < gs.G)
+            a = __longlong_as_double((int64_t)(((w[2 * c] & 0xffffffffull) << 32) |
+                                               (w[2 * c + 1] & 0xffffffffull)));
+        tot[c] = uniform(rblock_sum(a, lds));
+    }
+    return true;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_shared(T *p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T, typename RP>
+__global__ __launch_bounds__(kRT, 1) void k_cg_resident(
+    const TileDesc *__restrict__ tiles, const int32_t *__restrict__ wave_row0,
+    const int32_t *__restrict__ wave_tile0, const RP *__restrict__ row_ptr,
+    const int32_t *__restrict__ col, const T *__restrict__ val, const T *__restrict__ dinv,
+    const T *__restrict__ b, T *__restrict__ x_out, T *pg, GridSync gs, double tol,
+    int32_t maxit, SysState *__restrict__ st) {
+    __shared__ double prod_all[kRW][4 * 64];
+    __shared__ int32_t roff_all[kRW][kRUnits + 1];
+    __shared__ T qbuf_all[kRW][64 * kRJ];
+    __shared__ double lds[kRW];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    // XCD-contiguous order: workgroup b runs on XCD b % 8; each XCD takes one
+    // contiguous eighth of the rows, so halo lines are shared inside its L2
+    const int lb = (blockIdx.x % kXcds) * (gs.G / kXcds) + blockIdx.x / kXcds;
+    const int w = lb * kRW + wv;
+    const int R0 = wave_row0[w], R1 = wave_row0[w + 1];
+    const int t0 = wave_tile0[w], t1 = wave_tile0[w + 1];
+    double *prod = prod_all[wv];
+    int32_t *roff = roff_all[wv];
+    T *qbuf = qbuf_all[wv];
+    T *ql = qbuf + lane;             // this lane's rows: ql[64 j]
+    T *pgl = pg + R0 + lane;          // and their global p: pgl[64 j]
+    const int nl = R1 - R0 - lane;    // row j of this lane exists iff 64 j < nl
+
+    // Register arrays are updated unconditionally (a lane's rows past the
+    // wavefront's range hold zeros and contribute nothing); only global
+    // accesses are masked. Conditional writes to the arrays would make the
+    // compiler copy them whole.
+    for (int j = lane; j < 64 * kRJ; j += 64) qbuf[j] = (T)0;
+    T xr[kRJ], rr[kRJ], pr[kRJ], dr[kRJ];
+    double s_bb = 0.0, s_rz = 0.0;
+#pragma unroll
+    for (int j = 0; j < kRJ; ++j) {
+        const bool in = 64 * j < nl;
+        const T bv = in ? b[R0 + lane + 64 * j] : (T)0;
+        dr[j] = in ? dinv[R0 + lane + 64 * j] : (T)0;
+        rr[j] = bv;
+        xr[j] = (T)0;
+        const double z = (double)dr[j] * (double)bv;
+        pr[j] = (T)z;
+        if (in) store_shared(pgl + 64 * j, pr[j]);
+        s_bb += (double)bv * (double)bv;
+        s_rz += (double)bv * z;
+    }
+    uint32_t seq = 1;
+    bool ok;
+    double bb, rho;
+    {
+        const double v[2] = {rblock_sum(s_bb, lds), rblock_sum(s_rz, lds)};
+        double tot[2];
+        ok = grid_allreduce<2>(gs, seq++, v, tot, lds, true);
+        bb = tot[0];
+        rho = tot[1];
+    }
+    int status = bb == 0.0 ? SLA_CONVERGED : (maxit <= 0 ? SLA_MAXIT : kRunning);
+    int iter = 0;
+    double rrv = bb, alpha = 0.0, beta = 0.0;
+    const double thresh = tol * sqrt(bb);
+
+    int32_t c[kRGroups][4];
+    T v[kRGroups][4];
+    int32_t ro[kRRowItems];
+    auto fetch = [&](const TileDesc &e) {
+        const int64_t base = e.k0 & ~(int64_t)3;
+        const int span = (int)(e.k1 - base);
+        const int nr = e.re - e.rs;
+        const int32_t *cp = col + base;
+        const T *vp = val + base;
+        const RP *rp = row_ptr + e.rs;
+#pragma unroll
+        for (int u = 0; u < kRGroups; ++u) {
+            const int g = 4 * (lane + u * 64);
+            if (g < span) {
+                load4(cp + g, c[u]);
+                load4(vp + g, v[u]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    c[u][k] = 0;
+                    v[u][k] = (T)0;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kRRowItems; ++u) {
+            const int j = lane + u * 64;
+            ro[u] = j <= nr ? (int32_t)(rp[j] - e.k0) : 0;
+        }
+    };
+
+    while (ok && status == kRunning) {
+        // p written by other workgroups (other XCDs) since these caches last
+        // held it: drop stale lines before gathering
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        // ---- A: q = A p on this wavefront's tiles, into its LDS slice
+        TileDesc d{0, 0, 0, 0};
+        if (t0 < t1) {
+            d = tiles[t0];
+            fetch(d);
+        }
+        for (int t = t0; t < t1; ++t) {
+            TileDesc dn{0, 0, 0, 0};
+            if (t + 1 < t1) dn = tiles[t + 1];
+            const int nrows = d.re - d.rs;
+            const int shift = (int)(d.k0 & 3);
+            const int nk = (int)(d.k1 - d.k0);
+#pragma unroll
+            for (int u = 0; u < kRGroups; ++u) {
+                double xv[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int j = 4 * (lane + u * 64) + k - shift;
+                    xv[k] = (double)pg[(j >= 0 && j < nk) ? c[u][k] : 0];
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int j = 4 * (lane + u * 64) + k - shift;
+                    if (j >= 0 && j < nk) prod[j] = (double)v[u][k] * xv[k];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kRRowItems; ++u) {
+                const int j = lane + u * 64;
+                if (j <= nrows) roff[j] = ro[u];
+            }
+            if (t + 1 < t1) fetch(dn);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            int G = 1;
+            while (G < 64 && G * 2 * nrows <= 64) G *= 2;
+            const int lg = lane & (G - 1);
+            const int grp = lane / G;
+            const int ngrp = 64 / G;
+            for (int i = grp; i < nrows; i += ngrp) {
+                const int a = roff[i], e = roff[i + 1];
+                double s = 0.0;
+                for (int j = a + lg; j < e; j += G) s += prod[j];
+                for (int off = G >> 1; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+                if (lg == 0) qbuf[d.rs - R0 + i] = (T)s;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            d = dn;
+        }
+        // ---- sigma = p.q
+        double s_pq = 0.0;
+#pragma unroll
+        for (int j = 0; j < kRJ; ++j) {
+            s_pq += (double)pr[j] * (double)ql[64 * j];
+        }
+        double sigma;
+        {
+            const double vv[1] = {rblock_sum(s_pq, lds)};
+            double tot[1];
+            ok = grid_allreduce<1>(gs, seq++, vv, tot, lds, false);
+            sigma = tot[0];
+        }
+        if (!ok) break;
+        if (!(sigma > 0.0) || !isfinite(sigma)) {
+            status = SLA_BREAKDOWN;
+            iter += 1;
+            break;
+        }
+        alpha = rho / sigma;
+        // ---- B: x += alpha p, r -= alpha q, z = dinv r; r.z and r.r
+        double s_rz2 = 0.0, s_rr = 0.0;
+#pragma unroll
+        for (int j = 0; j < kRJ; ++j) {
+            const T qv = ql[64 * j];
+            xr[j] = (T)((double)xr[j] + alpha * (double)pr[j]);
+            rr[j] = (T)((double)rr[j] - alpha * (double)qv);
+            const double z = (double)dr[j] * (double)rr[j];
+            s_rz2 += (double)rr[j] * z;
+            s_rr += (double)rr[j] * (double)rr[j];
+        }
+        double rz;
+        {
+            const double vv[2] = {rblock_sum(s_rz2, lds), rblock_sum(s_rr, lds)};
+            double tot[2];
+            ok = grid_allreduce<2>(gs, seq++, vv, tot, lds, false);
+            rz = tot[0];
+            rrv = tot[1];
+        }
+        if (!ok) break;
+        iter += 1;
+        if (sqrt(rrv) <= thresh) {
+            status = SLA_CONVERGED;
+            break;
+        }
+        if (iter >= maxit) {
+            status = SLA_MAXIT;
+            break;
+        }
+        beta = rz / rho;
+        rho = rz;
+        // ---- C: p = z + beta p, own rows to the global copy. The base is
+        // redefined here so that the compiler forms the row addresses in this
+        // phase instead of keeping all of them live across the loop.
+        T *pw = pgl;
+        __asm__ volatile("" : "+v"(pw));
+#pragma unroll
+        for (int j = 0; j < kRJ; ++j) {
+            pr[j] = (T)((double)dr[j] * (double)rr[j] + beta * (double)pr[j]);
+            if (64 * j < nl) store_shared(pw + 64 * j, pr[j]);
+        }
+        {
+            const double vv[1] = {0.0};
+            double tot[1];
+            ok = grid_allreduce<1>(gs, seq++, vv, tot, lds, true);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kRJ; ++j)
+        if (64 * j < nl) x_out[R0 + lane + 64 * j] = xr[j];
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        SysState s;
+        s.bb = bb;
+        s.rho = rho;
+        s.alpha = alpha;
+        s.beta = beta;
+        s.rr = rrv;
+        s.iter = iter;
+        s.status = ok ? status : kResFailed;
+        st[0] = s;
+    }
+}
+
+template <typename T, typename RP>
+const void *resident_kernel() {
+    return (const void *)&k_cg_resident<T, RP>;
+}
+
+const void *kernel_for(const Handle &h) {
+    if (h.vt == SLA_F64) return h.rp64 ? resident_kernel<double, int64_t>() : resident_kernel<double, int32_t>();
+    return h.rp64 ? resident_kernel<float, int64_t>() : resident_kernel<float, int32_t>();
+}
+
+template <typename RP>
+void build_plan(Handle &h, int64_t G, int64_t rpw, hipStream_t s) {
+    const int64_t n = h.n;
+    const int64_t waves = G * kRW;
+    std::vector<RP> rp((size_t)n + 1);
+    SLA_HIP(hipMemcpyAsync(rp.data(), h.row_ptr, sizeof(RP) * (size_t)(n + 1),
+                           hipMemcpyDeviceToHost, s));
+    SLA_HIP(hipStreamSynchronize(s));
+    std::vector<int32_t> wave((size_t)(2 * (waves + 1)));
+    std::vector<TileDesc> tiles;
+    tiles.reserve((size_t)(n / 16 + waves + 1));
+    for (int64_t w = 0; w <= waves; ++w) {
+        const int64_t r0 = w * rpw < n ? w * rpw : n;
+        wave[(size_t)w] = (int32_t)r0;
+        wave[(size_t)(waves + 1 + w)] = (int32_t)tiles.size();
+        if (w == waves) break;
+        const int64_t r1 = (w + 1) * rpw < n ? (w + 1) * rpw : n;
+        // tiles of at most kRUnits rows + entries inside [r0, r1) (a lone row
+        // has at most kLongRow entries, well within one group per lane)
+        int64_t a = r0;
+        while (a < r1) {
+            int64_t e = a + 1;
+            while (e < r1 && (e + 1 - a) + (int64_t)(rp[(size_t)e + 1] - rp[(size_t)a]) <= kRUnits)
+                ++e;
+            tiles.push_back(TileDesc{(int32_t)a, (int32_t)e, (int64_t)rp[(size_t)a], (int64_t)rp[(size_t)e]});
+            a = e;
+        }
+    }
+    h.res_tiles = (TileDesc *)dalloc(h, sizeof(TileDesc) * (tiles.size() + 1));
+    h.res_wave = (int32_t *)dalloc(h, sizeof(int32_t) * wave.size());
+    h.res_slot = (uint64_t *)dalloc(h, sizeof(uint64_t) * (size_t)(2 * G * 2 * kMaxC));
+    if (!tiles.empty())
+        SLA_HIP(hipMemcpyAsync(h.res_tiles, tiles.data(), sizeof(TileDesc) * tiles.size(),
+                               hipMemcpyHostToDevice, s));
+    SLA_HIP(hipMemcpyAsync(h.res_wave, wave.data(), sizeof(int32_t) * wave.size(),
+                           hipMemcpyHostToDevice, s));
+    SLA_HIP(hipStreamSynchronize(s));
+}
+
+template <typename T, typename RP>
+void launch(Handle &h, const void *b, double tol, int32_t maxit, hipStream_t s) {
+    const int64_t waves = h.res_grid * kRW;
+    const TileDesc *tiles = h.res_tiles;
+    const int32_t *wrow = h.res_wave;
+    const int32_t *wtile = h.res_wave + waves + 1;
+    const RP *rp = (const RP *)h.row_ptr;
+    const int32_t *col = h.col;
+    const T *val = (const T *)h.vals;
+    const T *dinv = (const T *)h.dinv;
+    const T *bp = (const T *)b;
+    T *xo = (T *)h.x;
+    T *pg = (T *)h.p;
+    GridSync gs{h.res_slot, (int)h.res_grid};
+    SysState *st = h.st;
+    void *args[] = {(void *)&tiles, (void *)&wrow, (void *)&wtile, (void *)&rp, (void *)&col,
+                    (void *)&val, (void *)&dinv, (void *)&bp, (void *)&xo, (void *)&pg,
+                    (void *)&gs, (void *)&tol, (void *)&maxit, (void *)&st};
+    SLA_HIP(hipLaunchCooperativeKernel(kernel_for(h), dim3((unsigned)h.res_grid), dim3(kRT), args,
+                                       0, s));
+}
+
+}  // namespace
+
+// Whether the single-system solve can run as one cooperative kernel with
+// on-chip vectors; builds the per-wavefront plan on first use.
+bool resident_ready(Handle &h, hipStream_t s) {
+    if (h.res_mode == 0) return false;
+    // automatic choice: up to kResidentAutoRows rows three grid-wide waits
+    // cost less than three kernel launches per iteration (measured on MI355X:
+    // 11.6 against 15.7 us per iteration at 4096 rows, 21.3 against 17.3 at
+    // 64000); past it the per-step kernels keep more loads in flight than 8
+    // wavefronts per CU can
+    if (h.res_mode == 1 && h.n > kResidentAutoRows) return false;
+    if (h.res_state != 0) return h.res_state > 0;
+    h.res_state = -1;
+    if (h.B != 1 || h.nlong != 0) return false;
+    int coop = 0, cus = 0, per_cu = 0;
+    SLA_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, h.device));
+    SLA_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h.device));
+    SLA_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel_for(h), kRT, 0));
+    if (!coop || per_cu < 1) return false;
+    // one workgroup per CU at most, a multiple of the XCD count
+    int64_t gmax = (int64_t)cus / kXcds * kXcds;
+    if (gmax < kXcds) return false;
+    // at least one row per lane for every wavefront
+    int64_t G = (h.n + (int64_t)kRW * 64 - 1) / ((int64_t)kRW * 64);
+    G = (G + kXcds - 1) / kXcds * kXcds;
+    if (G > gmax) G = gmax;
+    const int64_t waves = G * kRW;
+    const int64_t rpw = (h.n + waves - 1) / waves;
+    if (rpw > 64 * kRJ) return false;
+    h.res_grid = G;
+    h.res_rows_per_wave = rpw;
+    if (h.rp64) build_plan<int64_t>(h, G, rpw, s);
+    else build_plan<int32_t>(h, G, rpw, s);
+    h.res_state = 1;
+    return true;
+}
+
+// Whole solve from x0 = 0: x (internal copy h.x) and the state st[0]. The
+// stamps restart at zero for every solve (sequence numbers start at 1).
+void resident_solve(Handle &h, const void *b, double tol, int32_t maxit, hipStream_t s) {
+    SLA_HIP(hipMemsetAsync(h.res_slot, 0, sizeof(uint64_t) * (size_t)(2 * h.res_grid * 2 * kMaxC), s));
+    hipEvent_t a = nullptr, e = nullptr;
+    if (h.profile) {
+        SLA_HIP(hipEventCreate(&a));
+        SLA_HIP(hipEventCreate(&e));
+        SLA_HIP(hipEventRecord(a, s));
+    }
+    if (h.vt == SLA_F64) {
+        if (h.rp64) launch<double, int64_t>(h, b, tol, maxit, s);
+        else launch<double, int32_t>(h, b, tol, maxit, s);
+    } else {
+        if (h.rp64) launch<float, int64_t>(h, b, tol, maxit, s);
+        else launch<float, int32_t>(h, b, tol, maxit, s);
+    }
+    if (h.profile) {
+        SLA_HIP(hipEventRecord(e, s));
+        h.pending.push_back({SLA_KERNEL_CG_RESIDENT, a, e});
+    }
+}
+
+}  // namespace sla

@@ -33,31 +33,6 @@ __device__ __forceinline__ int group_size(int nrows) {
 constexpr int kTileGroups = (kTileCap + 3 + 4 * 64 - 1) / (4 * 64);
 constexpr int kRowItems = (kTileUnits + 1 + 63) / 64;  // row offsets per lane
 
-// 16-byte vector types for grouped loads
-template <typename T>
-struct Vec4;
-template <>
-struct Vec4<double> {
-    double2 lo, hi;
-};
-template <>
-struct Vec4<float> {
-    float4 v;
-};
-__device__ __forceinline__ void load4(const double *p, double (&o)[4]) {
-    const double2 a = *reinterpret_cast<const double2 *>(p);
-    const double2 b = *reinterpret_cast<const double2 *>(p + 2);
-    o[0] = a.x; o[1] = a.y; o[2] = b.x; o[3] = b.y;
-}
-__device__ __forceinline__ void load4(const float *p, float (&o)[4]) {
-    const float4 a = *reinterpret_cast<const float4 *>(p);
-    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-}
-__device__ __forceinline__ void load4(const int32_t *p, int32_t (&o)[4]) {
-    const int4 a = *reinterpret_cast<const int4 *>(p);
-    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-}
-
 // Rows longer than kLongRow: one workgroup per row, 8 entries in flight per
 // lane. Runs before the tile kernel; in the fused form it also leaves
 // p_i q_i of each long row in long_dot for the tile kernel's reduction.

@@ -78,8 +78,14 @@ enum {
                                    default 16); results do not depend on it */
     SLA_OPT_USE_GRAPH = 2,      /* 1 (default): replay the polled iteration block as a
                                    hipGraph; 0: launch kernels one by one */
-    SLA_OPT_PROFILE = 3         /* 1: time every kernel launch of later calls with hipEvents
+    SLA_OPT_PROFILE = 3,        /* 1: time every kernel launch of later calls with hipEvents
                                    (implies eager launches); 0 (default): off */
+    SLA_OPT_RESIDENT = 4        /* single-system solve as one cooperative kernel that keeps
+                                   x, r, p and dinv on chip (same recurrence, same
+                                   outcomes): 0 never; 1 (default) when applicable and
+                                   n <= 2^15; 2 whenever applicable. Applicable: batch 1,
+                                   no row longer than 128 entries, n <= 8192 rows per CU
+                                   (2^21 on 256 CUs), cooperative launch available. */
 };
 
 /* kernel kinds reported by sla_profile_get */
@@ -90,7 +96,8 @@ enum {
     SLA_KERNEL_INIT = 3,      /* r = b, x = 0, p = z, b.b and r.z */
     SLA_KERNEL_SPMV = 4,      /* plain y = A x */
     SLA_KERNEL_GRAD = 5,      /* grad_vals[k] = -lambda[row k] x[col k] */
-    SLA_KERNEL_COUNT = 6
+    SLA_KERNEL_CG_RESIDENT = 6, /* a whole single-system solve in one cooperative kernel */
+    SLA_KERNEL_COUNT = 7
 };
 
 /*

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 import torch
 
-from differentiable_sparse_linear_csr_amd import SparseCSR
+from differentiable_sparse_linear_csr_amd import SparseCSR, _lib
 from workloads import make_workload
 
 from gpu_util import dev, host
@@ -36,8 +36,12 @@ def check_vector(v, ref, tol):
         assert abs(np.dot(w, v) - pr) <= tol * norm * np.linalg.norm(w)
 
 
-@pytest.mark.parametrize("name", NAMES)
-def test_full_size_against_oracle_reference(name):
+# resident mode 2 forces the single-kernel solve where it applies (n <= 2^21)
+CASES = [(n, 1) for n in NAMES] + [("diffusion3d_128", 2), ("knn_laplacian_2m", 2)]
+
+
+@pytest.mark.parametrize("name,resident", CASES)
+def test_full_size_against_oracle_reference(name, resident):
     path = os.path.join(HERE, "golden", f"{name}.json")
     ref = json.load(open(path))
     print(f"full-size {name}: building inputs", flush=True)
@@ -48,8 +52,14 @@ def test_full_size_against_oracle_reference(name):
     else:
         A = SparseCSR.from_csr(dev(w.row_ptr), dev(w.cols), dev(w.vals))
         assert A.row_index_dtype == torch.int64
+    A.set_option(_lib.SLA_OPT_RESIDENT, resident)
+    if resident == 2:
+        A.set_option(_lib.SLA_OPT_PROFILE, 1)
     print(f"full-size {name}: solving n={w.n} nnz={w.nnz} batch={w.batch}", flush=True)
     x, info = A.solve_raw(dev(w.b), w.tol, w.maxit)
+    if resident == 2:
+        assert A.profile()["cg_resident"][0] == 1
+        A.set_option(_lib.SLA_OPT_PROFILE, 0)
     X = np.atleast_2d(host(x))
     tol_x = 1e-8 if w.dtype == "f64" else 1e-4
     for s, fr in enumerate(ref["forward"]):

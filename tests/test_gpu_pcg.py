@@ -70,6 +70,7 @@ def test_adjoint_matches_oracle(name, size, batch):
 def test_check_interval_and_graph_do_not_change_results():
     w = make_workload("diffusion3d_128", size=20)
     A = coo_handle(w.n, w.rows, w.cols, w.vals)
+    A.set_option(_lib.SLA_OPT_RESIDENT, 0)   # the polled multi-kernel path
     b = dev(w.b)
     outs = []
     for k, graph in [(1, 1), (7, 1), (16, 1), (64, 1), (16, 0)]:
@@ -91,9 +92,11 @@ def test_batched_slices_equal_single_solves():
         assert rel(host(xs), host(X[s])) <= 1e-5
 
 
-def test_outcomes():
+@pytest.mark.parametrize("resident", [1, 0])
+def test_outcomes(resident):
     r, c, v = poisson2d_coo(30)
     A = coo_handle(900, r, c, v)
+    A.set_option(_lib.SLA_OPT_RESIDENT, resident)
     b = np.random.default_rng(0).standard_normal(900)
     x, info = A.solve_raw(dev(np.zeros(900)), 1e-10, 100)
     assert info.iterations[0] == 0 and info.status[0] == _lib.SLA_CONVERGED
@@ -111,12 +114,14 @@ def test_outcomes():
     assert info.iterations[0] == 50 and info.status[0] == _lib.SLA_MAXIT
     # indefinite -> breakdown at the first step, x untouched
     A2 = coo_handle(2, np.array([0, 0, 1, 1]), np.array([0, 1, 0, 1]), np.array([1.0, 2, 2, 1]))
+    A2.set_option(_lib.SLA_OPT_RESIDENT, resident)
     x, info = A2.solve_raw(dev(np.array([1.0, -1.0])), 1e-10, 10)
     assert info.status[0] == _lib.SLA_BREAKDOWN and info.iterations[0] == 1 and not host(x).any()
     # bad diagonal -> error
     v2 = v.copy()
     v2[(r == 7) & (c == 7)] = 0.0
     A3 = coo_handle(900, r, c, v2)
+    A3.set_option(_lib.SLA_OPT_RESIDENT, resident)
     with pytest.raises(SlaError) as e:
         A3.solve_raw(dev(b), 1e-10, 10)
     assert e.value.status == _lib.SLA_ERR_BAD_DIAGONAL
@@ -238,3 +243,77 @@ def test_autograd_through_solve_with_duplicates():
     vals2 = dev(v2).requires_grad_(True)
     x2 = A.solve(dev(b), values=vals2, tol=1e-12, maxit=5000)
     assert rel(host(x2), xo / 1.5) <= 1e-9
+
+
+def resident_cases():
+    r, c, v = adversarial.random_spd_coo(30011, 9.0, 21, skew=False)  # irregular, none past 128
+    return {
+        "poisson2d_64": make_workload("poisson2d_64"),
+        "diffusion3d_128_s40": make_workload("diffusion3d_128", size=40),
+        "knn_laplacian_2m_s60000": make_workload("knn_laplacian_2m", size=60000),
+        "random_spd_30011": (30011, r, c, v),
+        "diffusion3d_128_s70": make_workload("diffusion3d_128", size=70),
+    }
+
+
+@pytest.mark.parametrize("name", ["poisson2d_64", "diffusion3d_128_s40", "knn_laplacian_2m_s60000",
+                                  "random_spd_30011", "diffusion3d_128_s70"])
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_single_kernel_solve_matches_oracle_and_multi_kernel_path(name, dtype):
+    case = resident_cases()[name]
+    if isinstance(case, tuple):
+        n, r, c, v = case
+        b = np.random.default_rng(3).standard_normal(n)
+        tol, maxit = 1e-8, 2000
+    else:
+        n, r, c, v, b, tol, maxit = case.n, case.rows, case.cols, case.vals, case.b, case.tol, case.maxit
+    v, b = v.astype(dtype), b.astype(dtype)
+    if dtype == np.float32:
+        tol = max(tol, 1e-5)
+    print(f"single-kernel {name} n={n} {np.dtype(dtype).name}", flush=True)
+    ref = oracle.coo_to_csr(n, r, c, v)
+    xo, ito, rlo, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, tol, maxit)
+    A = coo_handle(n, r, c, v)
+    if n > 1 << 15:
+        # the automatic choice takes the per-step kernels here; force the other
+        A.profile_reset()
+        A.set_option(_lib.SLA_OPT_PROFILE, 1)
+        A.solve_raw(dev(b), tol, 3)
+        assert A.profile()["cg_resident"][0] == 0
+        A.set_option(_lib.SLA_OPT_RESIDENT, 2)
+    A.profile_reset()
+    A.set_option(_lib.SLA_OPT_PROFILE, 1)
+    x1, i1 = A.solve_raw(dev(b), tol, maxit)
+    prof = A.profile()
+    A.set_option(_lib.SLA_OPT_PROFILE, 0)
+    assert prof["cg_resident"][0] == 1 and prof["spmv_dot"][0] == 0, prof
+    A.set_option(_lib.SLA_OPT_RESIDENT, 0)
+    x0, i0 = A.solve_raw(dev(b), tol, maxit)
+    xtol = 1e-8 if dtype == np.float64 else 1e-4
+    for x, info in ((x1, i1), (x0, i0)):
+        assert info.status[0] == oco == oracle.CONVERGED
+        assert abs(info.iterations[0] - ito) <= 2, (info.iterations[0], ito)
+        assert rel(host(x), xo) <= xtol, rel(host(x), xo)
+        assert info.rel_residual[0] <= tol
+    # deterministic: the same bits on a second run
+    A.set_option(_lib.SLA_OPT_RESIDENT, 2)
+    x2, i2 = A.solve_raw(dev(b), tol, maxit)
+    assert host(x2).tobytes() == host(x1).tobytes() and i2.iterations[0] == i1.iterations[0]
+
+
+def test_single_kernel_int64_row_ptr_and_adjoint():
+    w = make_workload("poisson2d_11548", size=200)     # CSR input with int64 row_ptr
+    A = csr_handle(w.row_ptr, w.cols, w.vals)
+    A.set_option(_lib.SLA_OPT_RESIDENT, 2)
+    g = np.random.default_rng(9).standard_normal(w.n)
+    ref = {"row_ptr": w.row_ptr.astype(np.int64), "col": w.cols.astype(np.int64), "vals": w.vals}
+    xo, ito, _, _ = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], w.b, 1e-10, 5000)
+    lam_o, gv_o, *_ = oracle.adjoint(ref["row_ptr"], ref["col"], ref["vals"], xo, g, 1e-10, 5000)
+    A.profile_reset()
+    A.set_option(_lib.SLA_OPT_PROFILE, 1)
+    x, info = A.solve_raw(dev(w.b), 1e-10, 5000)
+    gb, gv, ainfo = A.adjoint_raw(x, dev(g), 1e-10, 5000)
+    assert A.profile()["cg_resident"][0] == 2
+    assert abs(info.iterations[0] - ito) <= 2
+    assert rel(host(x), xo) <= 1e-8
+    assert rel(host(gb), lam_o) <= 1e-8 and rel(host(gv), gv_o) <= 1e-8

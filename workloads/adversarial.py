@@ -8,18 +8,20 @@ from __future__ import annotations
 import numpy as np
 
 
-def random_spd_coo(n: int, avg_offdiag: float, seed: int, max_row: int = 0, index_dtype=np.int64):
+def random_spd_coo(n: int, avg_offdiag: float, seed: int, max_row: int = 0, index_dtype=np.int64,
+                   skew: bool = True):
     """Symmetric, strictly diagonally dominant matrix with positive diagonal (hence SPD).
 
     The off-diagonal pattern is a random symmetric graph whose degrees vary
-    strongly between rows; if ``max_row`` > 0, row 0 additionally couples to
+    strongly between rows (``skew``; otherwise endpoints are uniform and the
+    degrees stay near the mean); if ``max_row`` > 0, row 0 additionally couples to
     ``max_row`` random other rows (one long row plus a long column).
     Returns sorted (rows, cols, vals) without duplicates.
     """
     rng = np.random.default_rng(seed)
     m = max(1, int(n * avg_offdiag / 2))
     # skewed endpoint distribution -> irregular degrees
-    a = (rng.random(m) ** 2 * n).astype(np.int64)
+    a = (rng.random(m) ** 2 * n).astype(np.int64) if skew else rng.integers(0, n, m)
     b = rng.integers(0, n, m)
     keep = a != b
     a, b = a[keep], b[keep]
