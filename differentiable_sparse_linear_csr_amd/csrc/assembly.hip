@@ -480,6 +480,46 @@ void load_values(Handle &h, const void *values, hipStream_t s) {
 
 // ------------------------------------------------------------------ tiles
 
+// One wavefront per tile: the tile's column range decides whether its
+// columns fit 16 bits relative to the smallest one (narrow); narrow tiles get
+// col16, every tile gets its row offsets relative to k0 in roff16.
+template <typename RP>
+__global__ __launch_bounds__(kBlock) void k_tile_compress(TileDesc *__restrict__ tiles,
+                                                          int64_t ntiles,
+                                                          const RP *__restrict__ row_ptr,
+                                                          const int32_t *__restrict__ col,
+                                                          uint16_t *__restrict__ col16,
+                                                          uint16_t *__restrict__ roff16,
+                                                          int *__restrict__ wide) {
+    const int64_t t = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (t >= ntiles) return;  // whole wavefronts; no workgroup barrier below
+    const int lane = threadIdx.x & 63;
+    const TileDesc d = tiles[t];
+    int32_t mn = INT32_MAX, mx = INT32_MIN;
+    for (int64_t k = d.k0 + lane; k < d.k1; k += 64) {
+        const int32_t c = col[k];
+        mn = c < mn ? c : mn;
+        mx = c > mx ? c : mx;
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        const int32_t a = __shfl_xor(mn, off, 64), b = __shfl_xor(mx, off, 64);
+        mn = a < mn ? a : mn;
+        mx = b > mx ? b : mx;
+    }
+    const bool empty = d.k1 == d.k0;
+    const bool narrow = empty || (int64_t)mx - (int64_t)mn < 65536;
+    const int32_t cbase = empty ? 0 : mn;
+    if (narrow)
+        for (int64_t k = d.k0 + lane; k < d.k1; k += 64) col16[k] = (uint16_t)(col[k] - cbase);
+    const int nr = d.re - d.rs;
+    for (int j = lane; j <= nr; j += 64) roff16[d.rpos + j] = (uint16_t)(row_ptr[d.rs + j] - d.k0);
+    if (lane == 0) {
+        tiles[t].cbase = cbase;
+        tiles[t].narrow = narrow ? 1 : 0;
+        if (!narrow) atomicOr(wide, 1);
+    }
+}
+
 void build_tiles(Handle &h, hipStream_t s) {
     const int64_t n = h.n;
     Scratch sc(s);
@@ -517,10 +557,16 @@ void build_tiles(Handle &h, hipStream_t s) {
     std::vector<TileDesc> shorts;
     std::vector<int32_t> longs;
     shorts.reserve((size_t)nt);
+    int64_t rpos = 0;
     for (int64_t t = 0; t < nt; ++t) {
-        const TileDesc d{hs[t], hs[t + 1], hk[t], hk[t + 1]};
-        if (d.re - d.rs == 1 && d.k1 - d.k0 > kLongRow) longs.push_back(d.rs);
-        else shorts.push_back(d);
+        TileDesc d{hs[t], hs[t + 1], hk[t], hk[t + 1], 0, 0, 0};
+        if (d.re - d.rs == 1 && d.k1 - d.k0 > kLongRow) {
+            longs.push_back(d.rs);
+        } else {
+            d.rpos = rpos;
+            rpos += d.re - d.rs + 1;
+            shorts.push_back(d);
+        }
     }
     h.ntiles = (int64_t)shorts.size();
     h.nlong = (int64_t)longs.size();
@@ -533,6 +579,27 @@ void build_tiles(Handle &h, hipStream_t s) {
     if (!longs.empty())
         SLA_HIP(hipMemcpyAsync(h.long_rows, longs.data(), sizeof(int32_t) * longs.size(),
                                hipMemcpyHostToDevice, s));
+    // 16-bit index forms for the single-system SpMV
+    h.col16 = (uint16_t *)dalloc(h, sizeof(uint16_t) * (size_t)(h.nnz + kEntryPad));
+    h.roff16 = (uint16_t *)dalloc(h, sizeof(uint16_t) * (size_t)(rpos + kEntryPad));
+    SLA_HIP(hipMemsetAsync(h.col16, 0, sizeof(uint16_t) * (size_t)(h.nnz + kEntryPad), s));
+    SLA_HIP(hipMemsetAsync(h.roff16, 0, sizeof(uint16_t) * (size_t)(rpos + kEntryPad), s));
+    h.all_narrow = false;
+    if (h.ntiles > 0) {
+        int *wide = sc.get<int>(1);
+        SLA_HIP(hipMemsetAsync(wide, 0, sizeof(int), s));
+        const unsigned g = (unsigned)((h.ntiles + kWaves - 1) / kWaves);
+        if (h.rp64)
+            hipLaunchKernelGGL(k_tile_compress<int64_t>, dim3(g), dim3(kBlock), 0, s, h.tiles,
+                               h.ntiles, (const int64_t *)h.row_ptr, (const int32_t *)h.col,
+                               h.col16, h.roff16, wide);
+        else
+            hipLaunchKernelGGL(k_tile_compress<int32_t>, dim3(g), dim3(kBlock), 0, s, h.tiles,
+                               h.ntiles, (const int32_t *)h.row_ptr, (const int32_t *)h.col,
+                               h.col16, h.roff16, wide);
+        SLA_HIP(hipGetLastError());
+        h.all_narrow = read_flag(wide, s) == 0;
+    }
     SLA_HIP(hipStreamSynchronize(s));
 }
 

@@ -49,9 +49,16 @@ struct SysState {
 };
 
 // A run of short rows [rs, re) whose entries are [k0, k1), at most kTileCap.
+// A run of short rows [rs, re) with entries [k0, k1). The single-system SpMV
+// reads its indices in 16-bit form: row offsets relative to k0 at
+// roff16[rpos ...], and, when every tile's columns span less than 2^16
+// (narrow), columns as col16[k] = col[k] - cbase.
 struct TileDesc {
     int32_t rs, re;
     int64_t k0, k1;
+    int64_t rpos;
+    int32_t cbase;
+    int32_t narrow;
 };
 
 struct Ctl {
@@ -108,6 +115,9 @@ struct Handle {
     int64_t *run = nullptr;  // [nnz+1] first sorted position of each CSR entry
     TileDesc *tiles = nullptr;   // short-row tiles, in row order
     int64_t ntiles = 0;
+    uint16_t *col16 = nullptr;   // [nnz + pad] tile-relative columns of narrow tiles
+    uint16_t *roff16 = nullptr;  // per tile: row offsets relative to the tile's k0
+    bool all_narrow = false;     // every tile narrow: the SpMV reads col16 only
     int32_t *long_rows = nullptr; // rows longer than kLongRow, in row order
     int64_t nlong = 0;
     double *long_dot = nullptr;   // [nlong] p_i q_i of the long rows (fused SpMV)

@@ -226,13 +226,13 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
         // held it: drop stale lines before gathering
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         // ---- A: q = A p on this wavefront's tiles, into its LDS slice
-        TileDesc d{0, 0, 0, 0};
+        TileDesc d{0, 0, 0, 0, 0, 0, 0};
         if (t0 < t1) {
             d = tiles[t0];
             fetch(d);
         }
         for (int t = t0; t < t1; ++t) {
-            TileDesc dn{0, 0, 0, 0};
+            TileDesc dn{0, 0, 0, 0, 0, 0, 0};
             if (t + 1 < t1) dn = tiles[t + 1];
             const int nrows = d.re - d.rs;
             const int shift = (int)(d.k0 & 3);
@@ -394,7 +394,7 @@ void build_plan(Handle &h, int64_t G, int64_t rpw, hipStream_t s) {
             int64_t e = a + 1;
             while (e < r1 && (e + 1 - a) + (int64_t)(rp[(size_t)e + 1] - rp[(size_t)a]) <= kRUnits)
                 ++e;
-            tiles.push_back(TileDesc{(int32_t)a, (int32_t)e, (int64_t)rp[(size_t)a], (int64_t)rp[(size_t)e]});
+            tiles.push_back(TileDesc{(int32_t)a, (int32_t)e, (int64_t)rp[(size_t)a], (int64_t)rp[(size_t)e], 0, 0, 0});
             a = e;
         }
     }

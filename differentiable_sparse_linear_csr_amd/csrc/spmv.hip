@@ -82,11 +82,11 @@ __global__ __launch_bounds__(kBlock) void k_spmv_long(
 // The grid is persistent (a multiple of 8, at most kMaxGrid workgroups),
 // which also bounds the reduction partials. The fused form adds p.q of its
 // rows, and of the long rows in a fixed order, to the grid reduction.
-template <typename T, typename RP, bool FUSED>
-__global__ __launch_bounds__(kBlock) void k_spmv_tile(
-    const TileDesc *__restrict__ tiles, int64_t ntiles, const RP *__restrict__ row_ptr,
-    const int32_t *__restrict__ col, const T *__restrict__ val, const T *__restrict__ x,
-    T *__restrict__ y, const double *__restrict__ long_dot, int64_t nlong,
+template <typename T, typename RP, bool FUSED, bool NARROW>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void k_spmv_tile(
+    const TileDesc *__restrict__ tiles, int64_t ntiles, const uint16_t *__restrict__ roff16,
+    const int32_t *__restrict__ col, const uint16_t *__restrict__ col16, const T *__restrict__ val,
+    const T *__restrict__ x, T *__restrict__ y, const double *__restrict__ long_dot, int64_t nlong,
     double *__restrict__ spart, const SysState *__restrict__ st) {
     __shared__ double prod_all[kWaves][kTileCap];
     __shared__ int32_t roff_all[kWaves][kTileUnits + 1];
@@ -106,39 +106,64 @@ __global__ __launch_bounds__(kBlock) void k_spmv_tile(
     const int64_t t_end = ntiles * (xcd + 1) / kXcds;
     double dot = 0.0;
 
-    TileDesc d{0, 0, 0, 0};
+    TileDesc d{0, 0, 0, 0, 0, 0, 0};
     int32_t c[kTileGroups][4];
     T v[kTileGroups][4];
     int32_t ro[kRowItems];
-    // Entries come in 16-byte groups from base = k0 rounded down to a
-    // multiple of 4 (col and val are allocated 256-byte aligned); groups wholly
-    // outside [k0, k1) are not loaded, partial ones are masked when consumed.
-    // Row offsets use a tile-uniform base pointer and 32-bit lane offsets.
+    // Entries come in groups of 4 from base = k0 rounded down to a multiple
+    // of 4 (index and value arrays are allocated 256-byte aligned): 16-byte
+    // value loads, and 8-byte loads of 16-bit columns when every tile is
+    // narrow (the tile's smallest column added back) or 16-byte loads of
+    // 32-bit columns otherwise. Groups wholly outside [k0, k1) are not loaded, partial ones
+    // are masked when consumed. Row offsets are the tile's 16-bit ones.
     auto fetch = [&](const TileDesc &e) {
         const int64_t base = e.k0 & ~(int64_t)3;
         const int span = (int)(e.k1 - base);
         const int nr = e.re - e.rs;
-        const int32_t *cp = col + base;
         const T *vp = val + base;
-        const RP *rp = row_ptr + e.rs;
+        if (NARROW) {
+            const uint16_t *cp = col16 + base;
+            const int32_t cb = e.cbase;
 #pragma unroll
-        for (int u = 0; u < kTileGroups; ++u) {
-            const int g = 4 * (lane + u * 64);
-            if (g < span) {
-                load4(cp + g, c[u]);
-                load4(vp + g, v[u]);
-            } else {
+            for (int u = 0; u < kTileGroups; ++u) {
+                const int g = 4 * (lane + u * 64);
+                if (g < span) {
+                    const uint2 raw = *reinterpret_cast<const uint2 *>(cp + g);
+                    c[u][0] = cb + (int32_t)(raw.x & 0xffffu);
+                    c[u][1] = cb + (int32_t)(raw.x >> 16);
+                    c[u][2] = cb + (int32_t)(raw.y & 0xffffu);
+                    c[u][3] = cb + (int32_t)(raw.y >> 16);
+                    load4(vp + g, v[u]);
+                } else {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    c[u][k] = 0;
-                    v[u][k] = (T)0;
+                    for (int k = 0; k < 4; ++k) {
+                        c[u][k] = 0;
+                        v[u][k] = (T)0;
+                    }
+                }
+            }
+        } else {
+            const int32_t *cp = col + base;
+#pragma unroll
+            for (int u = 0; u < kTileGroups; ++u) {
+                const int g = 4 * (lane + u * 64);
+                if (g < span) {
+                    load4(cp + g, c[u]);
+                    load4(vp + g, v[u]);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        c[u][k] = 0;
+                        v[u][k] = (T)0;
+                    }
                 }
             }
         }
+        const uint16_t *rp = roff16 + e.rpos;
 #pragma unroll
         for (int u = 0; u < kRowItems; ++u) {
             const int j = lane + u * 64;
-            ro[u] = j <= nr ? (int32_t)(rp[j] - e.k0) : 0;
+            ro[u] = j <= nr ? (int32_t)rp[j] : 0;
         }
     };
     if (t < t_end) {
@@ -147,7 +172,7 @@ __global__ __launch_bounds__(kBlock) void k_spmv_tile(
     }
     while (t < t_end) {
         const int64_t tn = t + waves_per_xcd;
-        TileDesc dn{0, 0, 0, 0};
+        TileDesc dn{0, 0, 0, 0, 0, 0, 0};
         if (tn < t_end) dn = tiles[tn];
         const int nrows = d.re - d.rs;
         const int shift = (int)(d.k0 & 3);           // entries of the first group before k0
@@ -431,10 +456,11 @@ void launch_spmv_t(Handle &h, const void *x, void *y, hipStream_t s) {
                                (const int32_t *)h.col, (const T *)h.vals, (const T *)x, (T *)y,
                                h.long_dot, (const SysState *)h.st);
         const int64_t grid = spmv_grid(h);
-        hipLaunchKernelGGL((k_spmv_tile<T, RP, FUSED>), dim3((unsigned)grid), dim3(kBlock), 0, s,
-                           (const TileDesc *)h.tiles, h.ntiles, (const RP *)h.row_ptr,
-                           (const int32_t *)h.col, (const T *)h.vals, (const T *)x, (T *)y,
-                           (const double *)h.long_dot, h.nlong, h.spart,
+        auto kern = h.all_narrow ? k_spmv_tile<T, RP, FUSED, true> : k_spmv_tile<T, RP, FUSED, false>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBlock), 0, s,
+                           (const TileDesc *)h.tiles, h.ntiles, (const uint16_t *)h.roff16,
+                           (const int32_t *)h.col, (const uint16_t *)h.col16, (const T *)h.vals,
+                           (const T *)x, (T *)y, (const double *)h.long_dot, h.nlong, h.spart,
                            (const SysState *)h.st);
     } else if (bvec_ok<T>(h)) {
         hipLaunchKernelGGL((k_spmv_bvec<T, RP, FUSED>), dim3((unsigned)bvec_grid<T>(h)),
@@ -470,12 +496,21 @@ void init_launch_limits(Handle &h) {
     SLA_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h.device));
     int per_cu = 0;
     const void *fn = nullptr;
-    if (h.vt == SLA_F64)
-        fn = h.rp64 ? (const void *)&k_spmv_tile<double, int64_t, true>
-                    : (const void *)&k_spmv_tile<double, int32_t, true>;
-    else
-        fn = h.rp64 ? (const void *)&k_spmv_tile<float, int64_t, true>
-                    : (const void *)&k_spmv_tile<float, int32_t, true>;
+    if (h.vt == SLA_F64) {
+        if (h.all_narrow)
+            fn = h.rp64 ? (const void *)&k_spmv_tile<double, int64_t, true, true>
+                        : (const void *)&k_spmv_tile<double, int32_t, true, true>;
+        else
+            fn = h.rp64 ? (const void *)&k_spmv_tile<double, int64_t, true, false>
+                        : (const void *)&k_spmv_tile<double, int32_t, true, false>;
+    } else {
+        if (h.all_narrow)
+            fn = h.rp64 ? (const void *)&k_spmv_tile<float, int64_t, true, true>
+                        : (const void *)&k_spmv_tile<float, int32_t, true, true>;
+        else
+            fn = h.rp64 ? (const void *)&k_spmv_tile<float, int64_t, true, false>
+                        : (const void *)&k_spmv_tile<float, int32_t, true, false>;
+    }
     SLA_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kBlock, 0));
     int64_t g = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
     g = g / kXcds * kXcds;

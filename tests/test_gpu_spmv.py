@@ -92,6 +92,22 @@ def test_batched_irregular(dtype, B):
     check(A, r, c, V, n, x, 1e-12 if dtype == np.float64 else 1e-5)
 
 
+@pytest.mark.parametrize("D", [1000, 65000, 65535, 65536, 70000])
+def test_column_span_around_16_bits(D):
+    # rows hold columns i and i + D (and i - D): tiles whose columns span less
+    # than 2^16 read 16-bit tile-relative indices, the others 32-bit ones
+    n = 140000
+    i = np.arange(n)
+    rows = np.concatenate([i, i[i + D < n], i[i - D >= 0]])
+    cols = np.concatenate([i, (i + D)[i + D < n], (i - D)[i - D >= 0]])
+    order = np.lexsort((cols, rows))
+    rows, cols = rows[order], cols[order]
+    vals = np.random.default_rng(D).standard_normal(rows.shape[0])
+    A = coo_handle(n, rows, cols, vals)
+    x = np.random.default_rng(D + 1).standard_normal(n)
+    check(A, rows, cols, vals, n, x, 1e-12)
+
+
 def test_deterministic_bitwise():
     n = 50000
     r, c, v = adversarial.random_spd_coo(n, 12.0, 3, max_row=20000)
