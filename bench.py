@@ -10,11 +10,19 @@ pattern is shared by every step. Inputs are resident in HBM before timing.
 
 value = PCG iterations (forward + adjoint) per second over the timed steps.
 
-Printed as one JSON line. `roofline` covers the dominant kernel (the fused
-SpMV + p.q kernel): its algorithmic bytes per launch over its average launch
-duration, timed with hipEvents by the library on the stream it launches on
-during one profiled step that follows the timed steps. `cpu_baseline` times
-the CPU oracle on a bounded sample of the same solve.
+Printed as one JSON line. `roofline` covers the dominant kernel: its
+algorithmic bytes per launch over its average launch duration, measured with
+hipEvents on the stream it is launched on after the timed steps:
+  - single system, per-step kernels: the SpMV tile kernel, 50 back-to-back
+    sla_spmv launches between one event pair (the solve runs its fused form,
+    which adds the p.q partials);
+  - single system solved by the one-kernel path: that kernel, one launch per
+    solve, per-launch events (whole solves of milliseconds);
+  - batch: the fused SpMV of the solve, per-launch events.
+`traffic` is the HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE
+counters (profiles/), while the kernel source they were taken on is
+unchanged. `cpu_baseline` times the CPU oracle on a bounded sample of the
+same solve.
 """
 from __future__ import annotations
 
@@ -179,13 +187,21 @@ def main() -> int:
     A.set_option(_lib.SLA_OPT_PROFILE, 1)
     prof_its, _ = step()
     prof = A.profile()
-    # plain SpMV y = A x (sla_spmv), timed the same way, for SpMV GFLOP/s
-    A.profile_reset()
-    for _ in range(20):
-        A.matvec(b)
-    torch.cuda.synchronize()
-    plain_n, plain_ms = A.profile()["spmv"]
     A.set_option(_lib.SLA_OPT_PROFILE, 0)
+    # the same SpMV kernel launched back to back, one event pair around all of
+    # them on the launch stream: its average duration without per-launch
+    # event overhead (the figure rocprofv3's kernel trace reports)
+    stream = torch.cuda.current_stream()
+    y = A.matvec(b)
+    reps = 50
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        A.matvec(b)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    b2b_ms = e0.elapsed_time(e1) / reps
 
     V = 8 if w.dtype == "f64" else 4
     R = 8 if A.row_index_dtype == torch.int64 else 4
@@ -200,13 +216,22 @@ def main() -> int:
         bytes_launch = prof_its / launches * ab["spmv"] + 3 * V * w.n * w.batch
         per_iter_ms = total_ms / max(prof_its, 1)
         kernel = "k_cg_resident (whole solve per launch: SpMV, p.q, update, r.z/r.r, direction)"
+    elif w.batch == 1:
+        # the SpMV tile kernel (the solve runs its fused form, which adds the
+        # p.q partials): back-to-back launches of sla_spmv
+        launches, avg_ms = reps, b2b_ms
+        bytes_launch = ab["spmv"]
+        n_it = max(prof["spmv_dot"][0], 1)
+        per_iter_ms = sum(prof[k][1] for k in ("spmv_dot", "update", "direction")) / n_it
+        kernel = "k_spmv_tile (q = A p; 50 back-to-back sla_spmv launches)"
     else:
+        # batched: sla_spmv also transposes x and y, so the fused kernel of the
+        # solve is timed per launch (events around each launch)
         launches, total_ms = prof["spmv_dot"]
         avg_ms = total_ms / max(launches, 1)
         bytes_launch = ab["spmv"]
         per_iter_ms = sum(prof[k][1] for k in ("spmv_dot", "update", "direction")) / max(launches, 1)
-        kernel = ("k_spmv_tile (fused q = A p, p.q partials)" if w.batch == 1
-                  else "k_spmv_bvec (fused q = A p, p.q partials, alpha)")
+        kernel = "k_spmv_bvec (fused q = A p, p.q partials, alpha; per-launch events)"
     achieved = bytes_launch / (avg_ms * 1e-3) / 1e9
     traffic = load_traffic(w.name, "cg_resident" if res_launches > 0 else "spmv_dot")
 
@@ -247,14 +272,18 @@ def main() -> int:
         },
         "extra": {
             "create_ms": round(create_ms, 2),
-            "iteration_ms": round(per_iter_ms, 5),
-            "iteration_gbps_3k": round(ab["iter_3k"] / (per_iter_ms * 1e-3) / 1e9, 1),
-            "iteration_frac_3k": round(ab["iter_3k"] / (per_iter_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "iteration_gbps_min": round(ab["iter_min"] / (per_iter_ms * 1e-3) / 1e9, 1),
+            # whole-job figures: every second of the timed steps counted
+            "iteration_ms": round(1e3 / value, 5),
+            "iteration_gbps_3k": round(ab["iter_3k"] * value / 1e9, 1),
+            "iteration_frac_3k": round(ab["iter_3k"] * value / 1e9 / HBM_PEAK_GBS, 4),
+            "iteration_gbps_min": round(ab["iter_min"] * value / 1e9, 1),
+            # the kernels of one iteration alone (per-launch events, which add
+            # a few microseconds of event overhead per launch)
+            "iteration_kernels_ms": round(per_iter_ms, 5),
             "path": "single cooperative kernel" if res_launches > 0 else "per-step kernels",
-            "spmv_plain_ms": round(plain_ms / max(plain_n, 1), 5),
-            "spmv_plain_gflops": round(2 * w.nnz * w.batch / (plain_ms / max(plain_n, 1) * 1e-3) / 1e9, 1),
-            "spmv_plain_gbps": round(ab["spmv"] / (plain_ms / max(plain_n, 1) * 1e-3) / 1e9, 1),
+            "spmv_ms": round(b2b_ms, 5),
+            "spmv_gflops": round(2 * w.nnz * w.batch / (b2b_ms * 1e-3) / 1e9, 1),
+            "spmv_gbps": round(ab["spmv"] / (b2b_ms * 1e-3) / 1e9, 1),
             "kernel_avg_ms": {k: round(v[1] / max(v[0], 1), 5) for k, v in prof.items() if v[0]},
             "handle_bytes": A.memory_bytes(),
         },
