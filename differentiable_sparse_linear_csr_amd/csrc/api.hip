@@ -164,6 +164,7 @@ sla_status sla_csr_create(sla_csr *out, sla_format fmt, int64_t n, int64_t nnz_i
             build_from_csr(*h, row_itype, rows_or_row_ptr, col_itype, cols, values, s);
         build_tiles(*h, s);
         init_launch_limits(*h);
+        init_vector_limits(*h);
         alloc_workspace(*h, s);
         compute_dinv(*h, s);
         if ((flags & SLA_FLAG_CHECK_SYMMETRIC) && !check_symmetric(*h, s))

@@ -141,6 +141,10 @@ struct Handle {
     // resident workgroups of the persistent SpMV on this device (CUs x occupancy,
     // a multiple of the XCD count): larger grids would run in two rounds
     int64_t spmv_resident = kMaxGrid;
+    // the same for the batched 16-byte-lane kernels: SpMV (plain, fused),
+    // update, direction
+    int64_t bvec_resident[2] = {kMaxGrid, kMaxGrid};
+    int64_t bv_update_resident = kMaxGrid, bv_direction_resident = kMaxGrid;
 
     // single-system solve as one cooperative kernel with on-chip vectors
     // (built at the first solve that can use it; -1: not applicable)
@@ -195,6 +199,8 @@ void iota_i64(int64_t *out, int64_t m, hipStream_t s);
 // ------------------------------------------------------------------ SpMV / solve
 void spmv(Handle &h, const void *x, void *y, hipStream_t s);
 void init_launch_limits(Handle &h);
+void init_vector_limits(Handle &h);
+int64_t resident_workgroups(const void *kernel, int device);
 void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit, sla_info *info,
          hipStream_t s, bool keep_internal_solution);
 void grad_vals(Handle &h, const void *lam_internal, const void *x_user, void *grad, hipStream_t s);

@@ -332,10 +332,12 @@ bool bv_ok(const Handle &h) {
     return (Q & (Q - 1)) == 0 && Q <= kBlock;
 }
 
-int64_t bv_grid(int64_t nc) {
+// at most the workgroups resident at once: a larger grid would run a second,
+// partial round
+int64_t bv_grid(int64_t nc, int64_t resident) {
     const int64_t per = (int64_t)kBlock * kVecGroups;
     int64_t g = (nc + per - 1) / per;
-    if (g > kMaxGrid) g = kMaxGrid;
+    if (g > resident) g = resident;
     if (g < 1) g = 1;
     return g;
 }
@@ -612,7 +614,8 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
                            (const double *)h.spart, spmv_grid(h), red, h.ctl, h.st, h.d_running);
     } else if (bv_ok<T>(h)) {
         const int64_t nc = h.n * h.B / VecW<T>::W;
-        hipLaunchKernelGGL(k_update_bv<T>, dim3((unsigned)bv_grid(nc)), dim3(kBlock), 0, s, nc,
+        hipLaunchKernelGGL(k_update_bv<T>, dim3((unsigned)bv_grid(nc, h.bv_update_resident)),
+                           dim3(kBlock), 0, s, nc,
                            h.B, (T *)h.x, (T *)h.r, (const T *)h.p, (const T *)h.q,
                            (const T *)h.dinv, red, h.ctl, h.st, h.d_running);
     } else {
@@ -630,7 +633,8 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
                            (const SysState *)h.st);
     } else if (bv_ok<T>(h)) {
         const int64_t nc = h.n * h.B / VecW<T>::W;
-        hipLaunchKernelGGL(k_direction_bv<T>, dim3((unsigned)bv_grid(nc)), dim3(kBlock), 0, s, nc,
+        hipLaunchKernelGGL(k_direction_bv<T>, dim3((unsigned)bv_grid(nc, h.bv_direction_resident)),
+                           dim3(kBlock), 0, s, nc,
                            h.B, (const T *)h.r, (T *)h.p, (const T *)h.dinv, (const Ctl *)h.ctl,
                            (const SysState *)h.st);
     } else {
@@ -686,6 +690,17 @@ void init_t(Handle &h, const void *b_int, hipStream_t s, Launcher *lp) {
 }
 
 }  // namespace
+
+void init_vector_limits(Handle &h) {
+    if (h.B < 2) return;
+    if (h.vt == SLA_F64) {
+        h.bv_update_resident = resident_workgroups((const void *)&k_update_bv<double>, h.device);
+        h.bv_direction_resident = resident_workgroups((const void *)&k_direction_bv<double>, h.device);
+    } else {
+        h.bv_update_resident = resident_workgroups((const void *)&k_update_bv<float>, h.device);
+        h.bv_direction_resident = resident_workgroups((const void *)&k_direction_bv<float>, h.device);
+    }
+}
 
 void flush_profile(Handle &h) {
     for (auto &rec : h.pending) {

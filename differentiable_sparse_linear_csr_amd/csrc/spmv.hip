@@ -422,26 +422,28 @@ bool bvec_ok(const Handle &h) {
     return (Q & (Q - 1)) == 0 && Q <= kBlock;
 }
 
-// rows per workgroup of the vectorized batched kernel: whole passes, grid
-// within kMaxGrid
-template <typename T>
+// rows per workgroup of the vectorized batched kernel: whole passes, spread
+// over at most the workgroups that are resident at once
+template <typename T, bool FUSED>
 int64_t bvec_rows_block(const Handle &h) {
     const int64_t rows_pass = (int64_t)(kBlock / (h.B / VecW<T>::W)) * kBvRows;
-    int64_t passes = 1;
-    while ((h.n + rows_pass * passes - 1) / (rows_pass * passes) > kMaxGrid) passes *= 2;
-    return rows_pass * passes;
+    const int64_t total = (h.n + rows_pass - 1) / rows_pass;
+    const int64_t g = h.bvec_resident[FUSED ? 1 : 0];
+    const int64_t passes = (total + g - 1) / g;
+    return rows_pass * (passes > 0 ? passes : 1);
 }
 
-template <typename T>
+// a multiple of the XCD count, at most the resident count (itself one)
+template <typename T, bool FUSED>
 int64_t bvec_grid(const Handle &h) {
-    const int64_t rb = bvec_rows_block<T>(h);
+    const int64_t rb = bvec_rows_block<T, FUSED>(h);
     const int64_t g = (h.n + rb - 1) / rb;
     return (g + kXcds - 1) / kXcds * kXcds;
 }
 
 template <typename T>
 int64_t batched_grid_t(const Handle &h) {
-    if (bvec_ok<T>(h)) return bvec_grid<T>(h);
+    if (bvec_ok<T>(h)) return bvec_grid<T, true>(h);
     const int64_t rows_block = (int64_t)(kBlock / h.B) * batched_rows_per_lane(h);
     return (h.n + rows_block - 1) / rows_block;
 }
@@ -463,8 +465,8 @@ void launch_spmv_t(Handle &h, const void *x, void *y, hipStream_t s) {
                            (const T *)x, (T *)y, (const double *)h.long_dot, h.nlong, h.spart,
                            (const SysState *)h.st);
     } else if (bvec_ok<T>(h)) {
-        hipLaunchKernelGGL((k_spmv_bvec<T, RP, FUSED>), dim3((unsigned)bvec_grid<T>(h)),
-                           dim3(kBlock), 0, s, h.n, h.B, bvec_rows_block<T>(h),
+        hipLaunchKernelGGL((k_spmv_bvec<T, RP, FUSED>), dim3((unsigned)bvec_grid<T, FUSED>(h)),
+                           dim3(kBlock), 0, s, h.n, h.B, bvec_rows_block<T, FUSED>(h),
                            (const RP *)h.row_ptr, (const int32_t *)h.col, (const T *)h.vals,
                            (const T *)x, (T *)y, red, h.ctl, h.st, h.d_running);
     } else {
@@ -491,10 +493,18 @@ int64_t spmv_grid(const Handle &h) {
 // Resident capacity of the persistent tile kernel: every workgroup of the
 // grid must be on a CU at once, or the later ones start only when earlier
 // ones finish and the kernel runs in two rounds.
+int64_t resident_workgroups(const void *kernel, int device) {
+    int cus = 0, per_cu = 0;
+    SLA_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device));
+    SLA_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0));
+    int64_t g = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    g = g / kXcds * kXcds;
+    if (g < kXcds) g = kXcds;
+    if (g > kMaxGrid) g = kMaxGrid;
+    return g;
+}
+
 void init_launch_limits(Handle &h) {
-    int cus = 0;
-    SLA_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h.device));
-    int per_cu = 0;
     const void *fn = nullptr;
     if (h.vt == SLA_F64) {
         if (h.all_narrow)
@@ -511,12 +521,22 @@ void init_launch_limits(Handle &h) {
             fn = h.rp64 ? (const void *)&k_spmv_tile<float, int64_t, true, false>
                         : (const void *)&k_spmv_tile<float, int32_t, true, false>;
     }
-    SLA_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kBlock, 0));
-    int64_t g = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
-    g = g / kXcds * kXcds;
-    if (g < kXcds) g = kXcds;
-    if (g > kMaxGrid) g = kMaxGrid;
-    h.spmv_resident = g;
+    h.spmv_resident = resident_workgroups(fn, h.device);
+    if (h.B > 1) {
+        auto pick = [&](auto ttag, auto rtag) {
+            using T = decltype(ttag);
+            using RP = decltype(rtag);
+            h.bvec_resident[0] = resident_workgroups((const void *)&k_spmv_bvec<T, RP, false>, h.device);
+            h.bvec_resident[1] = resident_workgroups((const void *)&k_spmv_bvec<T, RP, true>, h.device);
+        };
+        if (h.vt == SLA_F64) {
+            if (h.rp64) pick(double(), int64_t());
+            else pick(double(), int32_t());
+        } else {
+            if (h.rp64) pick(float(), int64_t());
+            else pick(float(), int32_t());
+        }
+    }
 }
 
 // q = A p on the solve workspace, fused with the p.q partials and alpha.
