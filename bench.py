@@ -18,7 +18,9 @@ hipEvents on the stream it is launched on after the timed steps:
     which adds the p.q partials);
   - single system solved by the one-kernel path: that kernel, one launch per
     solve, per-launch events (whole solves of milliseconds);
-  - batch: the fused SpMV of the solve, per-launch events.
+  - batch, or a matrix the library reordered for locality (sla_spmv then
+    also transposes or permutes the vectors): the fused SpMV of the solve,
+    per-launch events.
 `traffic` is the HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE
 counters (profiles/), while the kernel source they were taken on is
 unchanged. `cpu_baseline` times the CPU oracle on a bounded sample of the
@@ -156,6 +158,7 @@ def main() -> int:
         A = sla.SparseCSR.from_csr(d(w.row_ptr), cols, vals)
     torch.cuda.synchronize()
     create_ms = (time.perf_counter() - t0) * 1e3
+    layout = A.layout()
     A.set_option(_lib.SLA_OPT_CHECK_INTERVAL, args.check_interval)
     x = torch.empty_like(b)
 
@@ -216,7 +219,7 @@ def main() -> int:
         bytes_launch = prof_its / launches * ab["spmv"] + 3 * V * w.n * w.batch
         per_iter_ms = total_ms / max(prof_its, 1)
         kernel = "k_cg_resident (whole solve per launch: SpMV, p.q, update, r.z/r.r, direction)"
-    elif w.batch == 1:
+    elif w.batch == 1 and not layout["reordered"]:
         # the SpMV tile kernel (the solve runs its fused form, which adds the
         # p.q partials): back-to-back launches of sla_spmv
         launches, avg_ms = reps, b2b_ms
@@ -225,13 +228,15 @@ def main() -> int:
         per_iter_ms = sum(prof[k][1] for k in ("spmv_dot", "update", "direction")) / n_it
         kernel = "k_spmv_tile (q = A p; 50 back-to-back sla_spmv launches)"
     else:
-        # batched: sla_spmv also transposes x and y, so the fused kernel of the
-        # solve is timed per launch (events around each launch)
+        # batched, or reordered: sla_spmv also transposes or permutes x and y,
+        # so the fused SpMV of the solve is timed per launch (events around
+        # each launch)
         launches, total_ms = prof["spmv_dot"]
         avg_ms = total_ms / max(launches, 1)
         bytes_launch = ab["spmv"]
         per_iter_ms = sum(prof[k][1] for k in ("spmv_dot", "update", "direction")) / max(launches, 1)
-        kernel = "k_spmv_bvec (fused q = A p, p.q partials, alpha; per-launch events)"
+        kernel = ("k_spmv_bvec (fused q = A p, p.q partials, alpha; per-launch events)" if w.batch > 1
+                  else "k_spmv_tile on P A P^T (fused q = A p, p.q partials; per-launch events)")
     achieved = bytes_launch / (avg_ms * 1e-3) / 1e9
     traffic = load_traffic(w.name, "cg_resident" if res_launches > 0 else "spmv_dot")
 
@@ -286,6 +291,7 @@ def main() -> int:
             "spmv_gbps": round(ab["spmv"] / (b2b_ms * 1e-3) / 1e9, 1),
             "kernel_avg_ms": {k: round(v[1] / max(v[0], 1), 5) for k, v in prof.items() if v[0]},
             "handle_bytes": A.memory_bytes(),
+            "layout": layout,
         },
     }
     if not args.no_cpu_baseline:

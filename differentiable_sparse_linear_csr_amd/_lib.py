@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "SLA_OK", 1: "SLA_ERR_INVALID_ARG", 2: "SLA_ERR_INDEX_RANGE",
 SLA_F32, SLA_F64 = 0, 1
 SLA_I32, SLA_I64 = 0, 1
 SLA_INPUT_COO, SLA_INPUT_CSR = 0, 1
-SLA_FLAG_CHECK_SYMMETRIC = 1
+SLA_FLAG_CHECK_SYMMETRIC, SLA_FLAG_REORDER, SLA_FLAG_NO_REORDER = 1, 2, 4
 SLA_CONVERGED, SLA_MAXIT, SLA_BREAKDOWN = 0, 1, 2
 SLA_OPT_CHECK_INTERVAL, SLA_OPT_USE_GRAPH, SLA_OPT_PROFILE, SLA_OPT_RESIDENT = 1, 2, 3, 4
 KERNELS = {"spmv_dot": 0, "update": 1, "direction": 2, "init": 3, "spmv": 4, "grad": 5,
@@ -38,7 +38,7 @@ EXPORTS = ["sla_csr_create", "sla_csr_set_values", "sla_csr_get", "sla_csr_get_p
            "sla_csr_get_values",
            "sla_csr_gather_to_input", "sla_csr_set_option", "sla_spmv", "sla_pcg_solve",
            "sla_adjoint_backward", "sla_profile_get", "sla_profile_reset", "sla_csr_memory",
-           "sla_csr_destroy", "sla_last_error", "sla_version"]
+           "sla_csr_get_layout", "sla_csr_destroy", "sla_last_error", "sla_version"]
 
 
 class SlaError(RuntimeError):
@@ -82,6 +82,7 @@ def load() -> ctypes.CDLL:
     L.sla_profile_get.argtypes = [P, i32, pi64, pf64]
     L.sla_profile_reset.argtypes = [P]
     L.sla_csr_memory.argtypes = [P, pi64]
+    L.sla_csr_get_layout.argtypes = [P, pi32, pi32, pi64, pi64]
     L.sla_csr_destroy.argtypes = [P]
     L.sla_csr_destroy.restype = None
     L.sla_last_error.argtypes = []

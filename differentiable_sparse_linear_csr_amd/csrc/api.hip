@@ -60,9 +60,12 @@ sla_status guard(F &&f) {
     }
 }
 
-void destroy(Handle *h) {
+}  // namespace
+
+void destroy_handle(Handle *h) {
     if (!h) return;
     (void)hipSetDevice(h->device);
+    if (h->inner) destroy_handle(h->inner);
     if (h->graph) (void)hipGraphExecDestroy(h->graph);
     for (auto &rec : h->pending) {
         (void)hipEventDestroy(rec.a);
@@ -113,6 +116,10 @@ void alloc_workspace(Handle &h, hipStream_t s) {
     SLA_HIP(hipStreamCreateWithFlags(&h.cap_stream, hipStreamNonBlocking));
 }
 
+namespace {
+
+void destroy(Handle *h) { destroy_handle(h); }
+
 Handle *checked(sla_csr h) {
     if (!h) fail(SLA_ERR_INVALID_ARG, "null handle");
     Handle *hh = reinterpret_cast<Handle *>(h);
@@ -143,7 +150,10 @@ sla_status sla_csr_create(sla_csr *out, sla_format fmt, int64_t n, int64_t nnz_i
             (col_itype != SLA_I32 && col_itype != SLA_I64))
             fail(SLA_ERR_INVALID_ARG, "bad index type");
         if (vtype != SLA_F32 && vtype != SLA_F64) fail(SLA_ERR_INVALID_ARG, "bad value type");
-        if (flags & ~(uint32_t)SLA_FLAG_CHECK_SYMMETRIC) fail(SLA_ERR_INVALID_ARG, "unknown flag");
+        if (flags & ~(uint32_t)(SLA_FLAG_CHECK_SYMMETRIC | SLA_FLAG_REORDER | SLA_FLAG_NO_REORDER))
+            fail(SLA_ERR_INVALID_ARG, "unknown flag");
+        if ((flags & SLA_FLAG_REORDER) && (flags & SLA_FLAG_NO_REORDER))
+            fail(SLA_ERR_INVALID_ARG, "SLA_FLAG_REORDER and SLA_FLAG_NO_REORDER exclude each other");
         if (fmt == SLA_INPUT_CSR && !rows_or_row_ptr) fail(SLA_ERR_INVALID_ARG, "row_ptr is null");
         if (nnz_in > 0 && (!rows_or_row_ptr || !cols || !values))
             fail(SLA_ERR_INVALID_ARG, "null index or value pointer");
@@ -169,6 +179,7 @@ sla_status sla_csr_create(sla_csr *out, sla_format fmt, int64_t n, int64_t nnz_i
         compute_dinv(*h, s);
         if ((flags & SLA_FLAG_CHECK_SYMMETRIC) && !check_symmetric(*h, s))
             fail(SLA_ERR_NOT_SYMMETRIC, "matrix is not symmetric (bitwise)");
+        if (want_reorder(*h)) build_reordered(*h, s);
         SLA_HIP(hipStreamSynchronize(s));
         *out = reinterpret_cast<sla_csr>(h);
     });
@@ -185,6 +196,7 @@ sla_status sla_csr_set_values(sla_csr hd, const void *values, void *stream) {
         compute_dinv(*h, s);
         if ((h->flags & SLA_FLAG_CHECK_SYMMETRIC) && !check_symmetric(*h, s))
             fail(SLA_ERR_NOT_SYMMETRIC, "matrix is not symmetric (bitwise)");
+        if (h->inner) reordered_set_values(*h, s);
     });
 }
 
@@ -244,28 +256,34 @@ sla_status sla_csr_gather_to_input(sla_csr hd, const void *csr_order, void *inpu
     });
 }
 
+namespace sla {
+namespace {
+void set_option(Handle *h, int32_t key, int64_t value) {
+    switch (key) {
+        case SLA_OPT_CHECK_INTERVAL:
+            if (value < 1 || value > 4096) fail(SLA_ERR_INVALID_ARG, "check interval in [1, 4096]");
+            h->check_k = (int)value;
+            break;
+        case SLA_OPT_USE_GRAPH:
+            h->use_graph = value != 0;
+            break;
+        case SLA_OPT_PROFILE:
+            h->profile = value != 0;
+            break;
+        case SLA_OPT_RESIDENT:
+            if (value < 0 || value > 2) fail(SLA_ERR_INVALID_ARG, "resident mode in [0, 2]");
+            h->res_mode = (int)value;
+            break;
+        default:
+            fail(SLA_ERR_INVALID_ARG, "unknown option");
+    }
+    if (h->inner) set_option(h->inner, key, value);
+}
+}  // namespace
+}  // namespace sla
+
 sla_status sla_csr_set_option(sla_csr hd, int32_t key, int64_t value) {
-    return guard([&] {
-        Handle *h = checked(hd);
-        switch (key) {
-            case SLA_OPT_CHECK_INTERVAL:
-                if (value < 1 || value > 4096) fail(SLA_ERR_INVALID_ARG, "check interval in [1, 4096]");
-                h->check_k = (int)value;
-                break;
-            case SLA_OPT_USE_GRAPH:
-                h->use_graph = value != 0;
-                break;
-            case SLA_OPT_PROFILE:
-                h->profile = value != 0;
-                break;
-            case SLA_OPT_RESIDENT:
-                if (value < 0 || value > 2) fail(SLA_ERR_INVALID_ARG, "resident mode in [0, 2]");
-                h->res_mode = (int)value;
-                break;
-            default:
-                fail(SLA_ERR_INVALID_ARG, "unknown option");
-        }
-    });
+    return guard([&] { set_option(checked(hd), key, value); });
 }
 
 sla_status sla_spmv(sla_csr hd, const void *x, void *y, void *stream) {
@@ -273,7 +291,8 @@ sla_status sla_spmv(sla_csr hd, const void *x, void *y, void *stream) {
         Handle *h = checked(hd);
         if (!x || !y) fail(SLA_ERR_INVALID_ARG, "null vector");
         if (x == y) fail(SLA_ERR_INVALID_ARG, "x and y must not alias");
-        spmv(*h, x, y, (hipStream_t)stream);
+        if (h->inner) reordered_spmv(*h, x, y, (hipStream_t)stream);
+        else spmv(*h, x, y, (hipStream_t)stream);
     });
 }
 
@@ -286,7 +305,8 @@ sla_status sla_pcg_solve(sla_csr hd, const void *b, void *x, double tol, int32_t
         if (!h->diag_ok)
             fail(SLA_ERR_BAD_DIAGONAL,
                  "Jacobi preconditioning needs every diagonal entry present, positive and finite");
-        pcg(*h, b, x, tol, maxit, info, (hipStream_t)stream, false);
+        if (h->inner) reordered_pcg(*h, b, x, tol, maxit, info, (hipStream_t)stream);
+        else pcg(*h, b, x, tol, maxit, info, (hipStream_t)stream, false);
     });
 }
 
@@ -301,6 +321,10 @@ sla_status sla_adjoint_backward(sla_csr hd, const void *x, const void *grad_x, v
             fail(SLA_ERR_BAD_DIAGONAL,
                  "Jacobi preconditioning needs every diagonal entry present, positive and finite");
         hipStream_t s = (hipStream_t)stream;
+        if (h->inner) {
+            reordered_adjoint(*h, x, grad_x, grad_b, grad_vals_out, tol, maxit, info, s);
+            return;
+        }
         pcg(*h, grad_x, nullptr, tol, maxit, info, s, true);  // lambda stays in the workspace
         if (grad_b) {
             if (h->B == 1)
@@ -320,6 +344,7 @@ sla_status sla_profile_get(sla_csr hd, int32_t kind, int64_t *launches, double *
         if (!hd) fail(SLA_ERR_INVALID_ARG, "null handle");
         if (kind < 0 || kind >= SLA_KERNEL_COUNT) fail(SLA_ERR_INVALID_ARG, "bad kernel kind");
         const Handle *h = reinterpret_cast<const Handle *>(hd);
+        if (h->inner) h = h->inner;  // kernels run on the reordered handle
         if (launches) *launches = h->prof_launches[kind];
         if (total_ms) *total_ms = h->prof_ms[kind];
     });
@@ -328,18 +353,32 @@ sla_status sla_profile_get(sla_csr hd, int32_t kind, int64_t *launches, double *
 sla_status sla_profile_reset(sla_csr hd) {
     return guard([&] {
         if (!hd) fail(SLA_ERR_INVALID_ARG, "null handle");
-        Handle *h = reinterpret_cast<Handle *>(hd);
-        for (int k = 0; k < SLA_KERNEL_COUNT; ++k) {
-            h->prof_launches[k] = 0;
-            h->prof_ms[k] = 0.0;
-        }
+        for (Handle *h = reinterpret_cast<Handle *>(hd); h; h = h->inner)
+            for (int k = 0; k < SLA_KERNEL_COUNT; ++k) {
+                h->prof_launches[k] = 0;
+                h->prof_ms[k] = 0.0;
+            }
     });
 }
 
 sla_status sla_csr_memory(sla_csr hd, int64_t *bytes) {
     return guard([&] {
         if (!hd || !bytes) fail(SLA_ERR_INVALID_ARG, "null pointer");
-        *bytes = reinterpret_cast<const Handle *>(hd)->bytes;
+        const Handle *h = reinterpret_cast<const Handle *>(hd);
+        *bytes = h->bytes + (h->inner ? h->inner->bytes : 0);
+    });
+}
+
+sla_status sla_csr_get_layout(sla_csr hd, int32_t *reordered, int32_t *narrow_columns,
+                              int64_t *tiles, int64_t *long_rows) {
+    return guard([&] {
+        if (!hd) fail(SLA_ERR_INVALID_ARG, "null handle");
+        const Handle *h = reinterpret_cast<const Handle *>(hd);
+        if (reordered) *reordered = h->inner ? 1 : 0;
+        const Handle *sv = h->inner ? h->inner : h;
+        if (narrow_columns) *narrow_columns = sv->all_narrow ? 1 : 0;
+        if (tiles) *tiles = sv->ntiles;
+        if (long_rows) *long_rows = sv->nlong;
     });
 }
 

@@ -516,7 +516,7 @@ __global__ __launch_bounds__(kBlock) void k_tile_compress(TileDesc *__restrict__
     if (lane == 0) {
         tiles[t].cbase = cbase;
         tiles[t].narrow = narrow ? 1 : 0;
-        if (!narrow) atomicOr(wide, 1);
+        if (!narrow) atomicAdd(wide, 1);
     }
 }
 
@@ -598,7 +598,8 @@ void build_tiles(Handle &h, hipStream_t s) {
                                h.ntiles, (const int32_t *)h.row_ptr, (const int32_t *)h.col,
                                h.col16, h.roff16, wide);
         SLA_HIP(hipGetLastError());
-        h.all_narrow = read_flag(wide, s) == 0;
+        h.wide_tiles = read_flag(wide, s);
+        h.all_narrow = h.wide_tiles == 0;
     }
     SLA_HIP(hipStreamSynchronize(s));
 }

@@ -156,6 +156,17 @@ struct Handle {
     int32_t *res_wave = nullptr;   // [2][waves+1]: first row, first tile of each wavefront
     uint64_t *res_slot = nullptr;  // [2][res_grid][4] stamped all-reduce partials
 
+    // symmetric reordering for locality (reverse Cuthill-McKee): the solver
+    // runs on `inner`, a handle of P A P^T; this handle keeps the caller's CSR
+    // and maps vectors, values and gradients between the two orders
+    Handle *inner = nullptr;
+    int32_t *new2old = nullptr;   // [n]: row of A that is row i of P A P^T
+    int64_t *map_in = nullptr;    // [nnz]: inner CSR position -> this CSR position
+    int64_t *map_out = nullptr;   // [nnz]: this CSR position -> inner CSR position
+    void *rtmp[2] = {nullptr, nullptr};  // [B][n] vectors in the inner order
+    void *rtmp_grad = nullptr;    // [B][nnz] value gradient in the inner order
+    int64_t wide_tiles = 0;       // tiles whose columns span 2^16 or more
+
     // iteration driver
     int check_k = 16;
     bool use_graph = true;
@@ -200,6 +211,17 @@ void iota_i64(int64_t *out, int64_t m, hipStream_t s);
 void spmv(Handle &h, const void *x, void *y, hipStream_t s);
 void init_launch_limits(Handle &h);
 void init_vector_limits(Handle &h);
+void alloc_workspace(Handle &h, hipStream_t s);
+void destroy_handle(Handle *h);
+// reordering (reorder.hip)
+bool want_reorder(const Handle &h);
+void build_reordered(Handle &h, hipStream_t s);
+void reordered_set_values(Handle &h, hipStream_t s);
+void reordered_spmv(Handle &h, const void *x, void *y, hipStream_t s);
+void reordered_pcg(Handle &h, const void *b, void *x, double tol, int32_t maxit, sla_info *info,
+                   hipStream_t s);
+void reordered_adjoint(Handle &h, const void *x, const void *g, void *grad_b, void *grad_vals,
+                       double tol, int32_t maxit, sla_info *info, hipStream_t s);
 int64_t resident_workgroups(const void *kernel, int device);
 void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit, sla_info *info,
          hipStream_t s, bool keep_internal_solution);

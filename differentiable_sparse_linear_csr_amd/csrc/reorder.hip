@@ -1,0 +1,406 @@
+// Symmetric reordering for locality. A matrix whose rows gather from far
+// apart (a graph of random points, say) makes every 8-byte gather of the SpMV
+// fetch its own cache line. Reverse Cuthill-McKee on the pattern gives a
+// permutation P with P A P^T banded; the solver then runs on a second handle
+// holding P A P^T, and this handle maps vectors (b, x, lambda: permuted
+// gathers), values (CSR position maps) and the value gradient between the
+// caller's order and the solver's.
+//
+// Jacobi-PCG is invariant under symmetric permutation in exact arithmetic:
+// diag(P A P^T) = P diag(A) P^T, and CG on (P A P^T, P b) produces P x_k at
+// every step. Only the order of the terms inside each row sum changes (the
+// columns of a row are sorted in the new numbering), so results agree with
+// the unpermuted solve to rounding.
+#include "common.h"
+
+#include <algorithm>
+#include <thread>
+#include <vector>
+
+namespace sla {
+
+namespace {
+
+// Reverse Cuthill-McKee order (new -> old) of the graph of the pattern
+// (row_ptr, col). Components are started from a pseudo-peripheral node (two
+// breadth-first sweeps from a node of least degree); each node's unvisited
+// neighbours are appended in order of increasing degree.
+void rcm_order(int64_t n, const std::vector<int64_t> &rp, const std::vector<int32_t> &col,
+               std::vector<int32_t> &order) {
+    std::vector<int32_t> deg((size_t)n);
+    for (int64_t i = 0; i < n; ++i) deg[(size_t)i] = (int32_t)(rp[(size_t)i + 1] - rp[(size_t)i]);
+    std::vector<int32_t> by_deg((size_t)n);
+    for (int64_t i = 0; i < n; ++i) by_deg[(size_t)i] = (int32_t)i;
+    std::stable_sort(by_deg.begin(), by_deg.end(),
+                     [&](int32_t a, int32_t b) { return deg[(size_t)a] < deg[(size_t)b]; });
+    std::vector<char> done((size_t)n, 0);
+    std::vector<int32_t> stamp((size_t)n, -1);
+    std::vector<int32_t> queue;
+    queue.reserve((size_t)n);
+    order.clear();
+    order.reserve((size_t)n);
+    std::vector<int32_t> nb;
+    int32_t sweep = 0;
+    // last level of a breadth-first sweep from r (nodes not yet ordered)
+    auto last_level_min = [&](int32_t r) {
+        ++sweep;
+        queue.clear();
+        queue.push_back(r);
+        stamp[(size_t)r] = sweep;
+        size_t head = 0, level_start = 0;
+        while (head < queue.size()) {
+            level_start = head;
+            const size_t level_end = queue.size();
+            for (; head < level_end; ++head) {
+                const int32_t u = queue[head];
+                for (int64_t k = rp[(size_t)u]; k < rp[(size_t)u + 1]; ++k) {
+                    const int32_t v = col[(size_t)k];
+                    if (!done[(size_t)v] && stamp[(size_t)v] != sweep) {
+                        stamp[(size_t)v] = sweep;
+                        queue.push_back(v);
+                    }
+                }
+            }
+        }
+        int32_t best = queue[level_start];
+        for (size_t i = level_start; i < queue.size(); ++i)
+            if (deg[(size_t)queue[i]] < deg[(size_t)best]) best = queue[i];
+        return best;
+    };
+    size_t next = 0;
+    while ((int64_t)order.size() < n) {
+        while (done[(size_t)by_deg[next]]) ++next;
+        int32_t root = by_deg[next];
+        root = last_level_min(root);
+        root = last_level_min(root);
+        size_t head = order.size();
+        order.push_back(root);
+        done[(size_t)root] = 1;
+        while (head < order.size()) {
+            const int32_t u = order[head++];
+            nb.clear();
+            for (int64_t k = rp[(size_t)u]; k < rp[(size_t)u + 1]; ++k) {
+                const int32_t v = col[(size_t)k];
+                if (!done[(size_t)v]) {
+                    done[(size_t)v] = 1;
+                    nb.push_back(v);
+                }
+            }
+            std::sort(nb.begin(), nb.end(), [&](int32_t a, int32_t b) {
+                return deg[(size_t)a] != deg[(size_t)b] ? deg[(size_t)a] < deg[(size_t)b] : a < b;
+            });
+            order.insert(order.end(), nb.begin(), nb.end());
+        }
+    }
+    std::reverse(order.begin(), order.end());
+}
+
+template <typename F>
+void parallel_rows(int64_t n, F &&f) {
+    unsigned nt = std::thread::hardware_concurrency();
+    if (nt < 1) nt = 1;
+    if (nt > 16) nt = 16;
+    if (n < 65536) nt = 1;
+    std::vector<std::thread> th;
+    for (unsigned t = 0; t < nt; ++t)
+        th.emplace_back([&, t] {
+            const int64_t a = n * t / nt, b = n * (t + 1) / nt;
+            f(a, b);
+        });
+    for (auto &x : th) x.join();
+}
+
+// out[b][i] = in[b][new2old[i]]   (caller order -> solver order)
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_to_inner(const T *__restrict__ in, T *__restrict__ out,
+                                                     const int32_t *__restrict__ new2old, int64_t n,
+                                                     int B) {
+    const int64_t total = n * B;
+    for (int64_t f = (int64_t)blockIdx.x * kBlock + threadIdx.x; f < total;
+         f += (int64_t)gridDim.x * kBlock) {
+        const int64_t b = f / n, i = f - b * n;
+        out[f] = in[b * n + new2old[i]];
+    }
+}
+
+// out[b][new2old[i]] = in[b][i]   (solver order -> caller order)
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_to_outer(const T *__restrict__ in, T *__restrict__ out,
+                                                     const int32_t *__restrict__ new2old, int64_t n,
+                                                     int B) {
+    const int64_t total = n * B;
+    for (int64_t f = (int64_t)blockIdx.x * kBlock + threadIdx.x; f < total;
+         f += (int64_t)gridDim.x * kBlock) {
+        const int64_t b = f / n, i = f - b * n;
+        out[b * n + new2old[i]] = in[f];
+    }
+}
+
+// inner values [nnz][B] from this handle's [nnz][B]: row k of the inner CSR
+// is row map_in[k] here
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_vals_to_inner(const T *__restrict__ vals,
+                                                          T *__restrict__ inner,
+                                                          const int64_t *__restrict__ map_in,
+                                                          int64_t nnz, int B) {
+    const int64_t total = nnz * B;
+    for (int64_t f = (int64_t)blockIdx.x * kBlock + threadIdx.x; f < total;
+         f += (int64_t)gridDim.x * kBlock) {
+        const int64_t k = f / B, b = f - k * B;
+        inner[f] = vals[map_in[k] * B + b];
+    }
+}
+
+// the same, written batch-major [B][nnz] (the layout create takes)
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_vals_to_inner_bm(const T *__restrict__ vals,
+                                                             T *__restrict__ inner,
+                                                             const int64_t *__restrict__ map_in,
+                                                             int64_t nnz, int B) {
+    const int64_t total = nnz * B;
+    for (int64_t f = (int64_t)blockIdx.x * kBlock + threadIdx.x; f < total;
+         f += (int64_t)gridDim.x * kBlock) {
+        const int64_t b = f / nnz, k = f - b * nnz;
+        inner[f] = vals[map_in[k] * B + b];
+    }
+}
+
+// gradient [B][nnz] in this handle's CSR order from the inner one's
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_grad_to_outer(const T *__restrict__ in,
+                                                          T *__restrict__ out,
+                                                          const int64_t *__restrict__ map_out,
+                                                          int64_t nnz, int B) {
+    const int64_t total = nnz * B;
+    for (int64_t f = (int64_t)blockIdx.x * kBlock + threadIdx.x; f < total;
+         f += (int64_t)gridDim.x * kBlock) {
+        const int64_t b = f / nnz, k = f - b * nnz;
+        out[f] = in[b * nnz + map_out[k]];
+    }
+}
+
+unsigned grid_of(int64_t total) {
+    int64_t g = (total + kBlock - 1) / kBlock;
+    if (g > 8192) g = 8192;
+    if (g < 1) g = 1;
+    return (unsigned)g;
+}
+
+void to_inner(Handle &h, const void *in, void *out, hipStream_t s) {
+    const int64_t total = h.n * h.B;
+    if (h.vt == SLA_F64)
+        hipLaunchKernelGGL(k_to_inner<double>, dim3(grid_of(total)), dim3(kBlock), 0, s,
+                           (const double *)in, (double *)out, (const int32_t *)h.new2old, h.n, h.B);
+    else
+        hipLaunchKernelGGL(k_to_inner<float>, dim3(grid_of(total)), dim3(kBlock), 0, s,
+                           (const float *)in, (float *)out, (const int32_t *)h.new2old, h.n, h.B);
+    SLA_HIP(hipGetLastError());
+}
+
+void to_outer(Handle &h, const void *in, void *out, hipStream_t s) {
+    const int64_t total = h.n * h.B;
+    if (h.vt == SLA_F64)
+        hipLaunchKernelGGL(k_to_outer<double>, dim3(grid_of(total)), dim3(kBlock), 0, s,
+                           (const double *)in, (double *)out, (const int32_t *)h.new2old, h.n, h.B);
+    else
+        hipLaunchKernelGGL(k_to_outer<float>, dim3(grid_of(total)), dim3(kBlock), 0, s,
+                           (const float *)in, (float *)out, (const int32_t *)h.new2old, h.n, h.B);
+    SLA_HIP(hipGetLastError());
+}
+
+}  // namespace
+
+// Reorder when asked to, or automatically when most SpMV tiles gather from
+// column ranges of 2^16 or more (poor locality) on a matrix large enough for
+// it to matter (n >= 2^16) and small enough for the host ordering (nnz < 2^28).
+bool want_reorder(const Handle &h) {
+    if (h.flags & SLA_FLAG_NO_REORDER) return false;
+    if (h.flags & SLA_FLAG_REORDER) return h.n > 1;
+    return h.n >= (1 << 16) && h.nnz < ((int64_t)1 << 28) && 2 * h.wide_tiles > h.ntiles;
+}
+
+// Build the solver handle of P A P^T from this handle's CSR (already
+// assembled, values loaded).
+void build_reordered(Handle &h, hipStream_t s) {
+    const int64_t n = h.n, nnz = h.nnz;
+    std::vector<int64_t> rp((size_t)n + 1);
+    std::vector<int32_t> col((size_t)nnz);
+    if (h.rp64) {
+        SLA_HIP(hipMemcpyAsync(rp.data(), h.row_ptr, 8 * (size_t)(n + 1), hipMemcpyDeviceToHost, s));
+    } else {
+        std::vector<int32_t> r32((size_t)n + 1);
+        SLA_HIP(hipMemcpyAsync(r32.data(), h.row_ptr, 4 * (size_t)(n + 1), hipMemcpyDeviceToHost, s));
+        SLA_HIP(hipStreamSynchronize(s));
+        for (int64_t i = 0; i <= n; ++i) rp[(size_t)i] = r32[(size_t)i];
+    }
+    if (nnz > 0)
+        SLA_HIP(hipMemcpyAsync(col.data(), h.col, 4 * (size_t)nnz, hipMemcpyDeviceToHost, s));
+    SLA_HIP(hipStreamSynchronize(s));
+
+    std::vector<int32_t> order;  // new -> old
+    rcm_order(n, rp, col, order);
+    std::vector<int32_t> old2new((size_t)n);
+    for (int64_t i = 0; i < n; ++i) old2new[(size_t)order[(size_t)i]] = (int32_t)i;
+
+    // P A P^T in CSR: row i is row order[i] of A with columns renumbered and
+    // sorted; map_in[k'] = position in A's CSR of entry k'
+    std::vector<int64_t> irp((size_t)n + 1);
+    irp[0] = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const int32_t o = order[(size_t)i];
+        irp[(size_t)i + 1] = irp[(size_t)i] + (rp[(size_t)o + 1] - rp[(size_t)o]);
+    }
+    std::vector<int32_t> icol((size_t)nnz);
+    std::vector<int64_t> map_in((size_t)nnz), map_out((size_t)nnz);
+    parallel_rows(n, [&](int64_t a, int64_t b) {
+        std::vector<std::pair<int32_t, int64_t>> e;
+        for (int64_t i = a; i < b; ++i) {
+            const int32_t o = order[(size_t)i];
+            e.clear();
+            for (int64_t k = rp[(size_t)o]; k < rp[(size_t)o + 1]; ++k)
+                e.emplace_back(old2new[(size_t)col[(size_t)k]], k);
+            std::sort(e.begin(), e.end());
+            int64_t pos = irp[(size_t)i];
+            for (const auto &pr : e) {
+                icol[(size_t)pos] = pr.first;
+                map_in[(size_t)pos] = pr.second;
+                map_out[(size_t)pr.second] = pos;
+                ++pos;
+            }
+        }
+    });
+
+    // device copies: maps, permutation, inner pattern and values
+    h.new2old = (int32_t *)dalloc(h, sizeof(int32_t) * (size_t)n);
+    h.map_in = (int64_t *)dalloc(h, sizeof(int64_t) * (size_t)(nnz + 1));
+    h.map_out = (int64_t *)dalloc(h, sizeof(int64_t) * (size_t)(nnz + 1));
+    const size_t vec = (size_t)n * h.B * h.vbytes;
+    h.rtmp[0] = dalloc(h, vec);
+    h.rtmp[1] = dalloc(h, vec);
+    h.rtmp_grad = dalloc(h, (size_t)(nnz + 1) * h.B * h.vbytes);
+    SLA_HIP(hipMemcpyAsync(h.new2old, order.data(), sizeof(int32_t) * (size_t)n,
+                           hipMemcpyHostToDevice, s));
+    if (nnz > 0) {
+        SLA_HIP(hipMemcpyAsync(h.map_in, map_in.data(), 8 * (size_t)nnz, hipMemcpyHostToDevice, s));
+        SLA_HIP(hipMemcpyAsync(h.map_out, map_out.data(), 8 * (size_t)nnz, hipMemcpyHostToDevice, s));
+    }
+    const bool rp64 = nnz >= ((int64_t)1 << 31);
+    void *d_rp = nullptr, *d_col = nullptr, *d_vals = nullptr;
+    SLA_HIP(hipMalloc(&d_rp, (size_t)(n + 1) * (rp64 ? 8 : 4)));
+    SLA_HIP(hipMalloc(&d_col, 4 * (size_t)(nnz + 1)));
+    SLA_HIP(hipMalloc(&d_vals, (size_t)(nnz + 1) * h.B * h.vbytes));
+    Handle *in = nullptr;
+    try {
+        if (rp64) {
+            SLA_HIP(hipMemcpyAsync(d_rp, irp.data(), 8 * (size_t)(n + 1), hipMemcpyHostToDevice, s));
+        } else {
+            std::vector<int32_t> r32((size_t)n + 1);
+            for (int64_t i = 0; i <= n; ++i) r32[(size_t)i] = (int32_t)irp[(size_t)i];
+            SLA_HIP(hipMemcpyAsync(d_rp, r32.data(), 4 * (size_t)(n + 1), hipMemcpyHostToDevice, s));
+            SLA_HIP(hipStreamSynchronize(s));
+        }
+        if (nnz > 0)
+            SLA_HIP(hipMemcpyAsync(d_col, icol.data(), 4 * (size_t)nnz, hipMemcpyHostToDevice, s));
+        if (nnz > 0) {
+            if (h.vt == SLA_F64)
+                hipLaunchKernelGGL(k_vals_to_inner_bm<double>, dim3(grid_of(nnz * h.B)), dim3(kBlock),
+                                   0, s, (const double *)h.vals, (double *)d_vals,
+                                   (const int64_t *)h.map_in, nnz, h.B);
+            else
+                hipLaunchKernelGGL(k_vals_to_inner_bm<float>, dim3(grid_of(nnz * h.B)), dim3(kBlock),
+                                   0, s, (const float *)h.vals, (float *)d_vals,
+                                   (const int64_t *)h.map_in, nnz, h.B);
+            SLA_HIP(hipGetLastError());
+        }
+        in = new Handle();
+        in->device = h.device;
+        in->n = n;
+        in->nnz_in = nnz;
+        in->B = h.B;
+        in->vt = h.vt;
+        in->vbytes = h.vbytes;
+        in->flags = 0;
+        build_from_csr(*in, rp64 ? SLA_I64 : SLA_I32, d_rp, SLA_I32, d_col, d_vals, s);
+        build_tiles(*in, s);
+        init_launch_limits(*in);
+        init_vector_limits(*in);
+        alloc_workspace(*in, s);
+        compute_dinv(*in, s);
+        SLA_HIP(hipStreamSynchronize(s));
+    } catch (...) {
+        (void)hipFree(d_rp);
+        (void)hipFree(d_col);
+        (void)hipFree(d_vals);
+        if (in) destroy_handle(in);
+        throw;
+    }
+    SLA_HIP(hipFree(d_rp));
+    SLA_HIP(hipFree(d_col));
+    SLA_HIP(hipFree(d_vals));
+    h.inner = in;
+}
+
+// after this handle's values changed: the inner values and Jacobi diagonal
+void reordered_set_values(Handle &h, hipStream_t s) {
+    Handle &in = *h.inner;
+    if (h.nnz > 0) {
+        if (h.vt == SLA_F64)
+            hipLaunchKernelGGL(k_vals_to_inner<double>, dim3(grid_of(h.nnz * h.B)), dim3(kBlock), 0,
+                               s, (const double *)h.vals, (double *)in.vals,
+                               (const int64_t *)h.map_in, h.nnz, h.B);
+        else
+            hipLaunchKernelGGL(k_vals_to_inner<float>, dim3(grid_of(h.nnz * h.B)), dim3(kBlock), 0,
+                               s, (const float *)h.vals, (float *)in.vals,
+                               (const int64_t *)h.map_in, h.nnz, h.B);
+        SLA_HIP(hipGetLastError());
+    }
+    compute_dinv(in, s);
+}
+
+void reordered_spmv(Handle &h, const void *x, void *y, hipStream_t s) {
+    to_inner(h, x, h.rtmp[0], s);
+    spmv(*h.inner, h.rtmp[0], h.rtmp[1], s);
+    to_outer(h, h.rtmp[1], y, s);
+}
+
+void reordered_pcg(Handle &h, const void *b, void *x, double tol, int32_t maxit, sla_info *info,
+                   hipStream_t s) {
+    to_inner(h, b, h.rtmp[0], s);
+    pcg(*h.inner, h.rtmp[0], h.rtmp[1], tol, maxit, info, s, false);
+    to_outer(h, h.rtmp[1], x, s);
+    SLA_HIP(hipStreamSynchronize(s));
+}
+
+void reordered_adjoint(Handle &h, const void *x, const void *g, void *grad_b, void *grad_vals_out,
+                       double tol, int32_t maxit, sla_info *info, hipStream_t s) {
+    Handle &in = *h.inner;
+    to_inner(h, g, h.rtmp[0], s);
+    pcg(in, h.rtmp[0], nullptr, tol, maxit, info, s, true);  // lambda stays in in.x
+    if (grad_b) {
+        if (in.B == 1)
+            SLA_HIP(hipMemcpyAsync(h.rtmp[1], in.x, (size_t)in.n * in.vbytes,
+                                   hipMemcpyDeviceToDevice, s));
+        else
+            transpose(in.x, h.rtmp[1], in.n, in.B, in.vbytes, s);
+        to_outer(h, h.rtmp[1], grad_b, s);
+    }
+    if (grad_vals_out) {
+        to_inner(h, x, h.rtmp[1], s);
+        grad_vals(in, in.x, h.rtmp[1], h.rtmp_grad, s);
+        if (h.nnz > 0) {
+            if (h.vt == SLA_F64)
+                hipLaunchKernelGGL(k_grad_to_outer<double>, dim3(grid_of(h.nnz * h.B)),
+                                   dim3(kBlock), 0, s, (const double *)h.rtmp_grad,
+                                   (double *)grad_vals_out, (const int64_t *)h.map_out, h.nnz, h.B);
+            else
+                hipLaunchKernelGGL(k_grad_to_outer<float>, dim3(grid_of(h.nnz * h.B)),
+                                   dim3(kBlock), 0, s, (const float *)h.rtmp_grad,
+                                   (float *)grad_vals_out, (const int64_t *)h.map_out, h.nnz, h.B);
+            SLA_HIP(hipGetLastError());
+        }
+    }
+    SLA_HIP(hipStreamSynchronize(s));
+    if (in.profile) flush_profile(in);
+}
+
+}  // namespace sla

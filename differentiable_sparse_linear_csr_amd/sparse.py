@@ -77,11 +77,15 @@ class SparseCSR:
 
     # ------------------------------------------------------------------ construction
     @classmethod
-    def _create(cls, fmt, n, nnz_in, batch, a, b, values, check_symmetric):
+    def _create(cls, fmt, n, nnz_in, batch, a, b, values, check_symmetric, reorder):
         L = _lib.load()
         dev = values.device
         h = ctypes.c_void_p()
         flags = _lib.SLA_FLAG_CHECK_SYMMETRIC if check_symmetric else 0
+        if reorder is True:
+            flags |= _lib.SLA_FLAG_REORDER
+        elif reorder is False:
+            flags |= _lib.SLA_FLAG_NO_REORDER
         with torch.cuda.device(dev):
             check(L.sla_csr_create(ctypes.byref(h), fmt, n, nnz_in, batch, _IT[a.dtype], _ptr(a),
                                    _IT[b.dtype], _ptr(b), _VT[values.dtype], _ptr(values), flags,
@@ -92,8 +96,10 @@ class SparseCSR:
 
     @classmethod
     def from_coo(cls, row: torch.Tensor, col: torch.Tensor, values: torch.Tensor, n: int,
-                 check_symmetric: bool = False) -> "SparseCSR":
-        """COO triples; duplicates are summed in input order (stable (row, col) order)."""
+                 check_symmetric: bool = False, reorder: Optional[bool] = None) -> "SparseCSR":
+        """COO triples; duplicates are summed in input order (stable (row, col) order).
+        reorder: None lets the library decide whether the solver runs on a
+        reverse Cuthill-McKee permutation (for locality), True/False force it."""
         for t, w in ((row, "row"), (col, "col"), (values, "values")):
             _need_cuda(t, w)
         if values.dtype not in _VT or row.dtype not in _IT or col.dtype not in _IT:
@@ -103,11 +109,11 @@ class SparseCSR:
         if col.shape[0] != nnz_in or values.shape[-1] != nnz_in:
             raise ValueError("row, col and values disagree on the number of entries")
         return cls._create(_lib.SLA_INPUT_COO, int(n), nnz_in, batch, row, col, values,
-                           check_symmetric)
+                           check_symmetric, reorder)
 
     @classmethod
     def from_csr(cls, row_ptr: torch.Tensor, col: torch.Tensor, values: torch.Tensor,
-                 check_symmetric: bool = False) -> "SparseCSR":
+                 check_symmetric: bool = False, reorder: Optional[bool] = None) -> "SparseCSR":
         """CSR arrays (columns strictly increasing inside each row), adopted as is."""
         for t, w in ((row_ptr, "row_ptr"), (col, "col"), (values, "values")):
             _need_cuda(t, w)
@@ -116,7 +122,7 @@ class SparseCSR:
         n = row_ptr.shape[0] - 1
         batch = 1 if values.dim() == 1 else values.shape[0]
         return cls._create(_lib.SLA_INPUT_CSR, n, col.shape[0], batch, row_ptr, col, values,
-                           check_symmetric)
+                           check_symmetric, reorder)
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -181,6 +187,16 @@ class SparseCSR:
             check(L.sla_profile_get(self._h, k, ctypes.byref(n), ctypes.byref(ms)))
             out[name] = (n.value, ms.value)
         return out
+
+    def layout(self) -> dict:
+        """How the solver holds the matrix: reordered (P A P^T), 16-bit column
+        offsets in every SpMV tile, tile and long-row counts."""
+        r, nc = ctypes.c_int32(), ctypes.c_int32()
+        t, lr = ctypes.c_int64(), ctypes.c_int64()
+        check(_lib.load().sla_csr_get_layout(self._h, ctypes.byref(r), ctypes.byref(nc),
+                                             ctypes.byref(t), ctypes.byref(lr)))
+        return {"reordered": bool(r.value), "narrow_columns": bool(nc.value), "tiles": t.value,
+                "long_rows": lr.value}
 
     def profile_reset(self) -> None:
         check(_lib.load().sla_profile_reset(self._h))

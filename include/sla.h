@@ -60,7 +60,12 @@ typedef enum { SLA_F32 = 0, SLA_F64 = 1 } sla_dtype;
 typedef enum { SLA_I32 = 0, SLA_I64 = 1 } sla_itype;
 typedef enum { SLA_INPUT_COO = 0, SLA_INPUT_CSR = 1 } sla_format;
 
-enum { SLA_FLAG_CHECK_SYMMETRIC = 1u };
+enum {
+    SLA_FLAG_CHECK_SYMMETRIC = 1u, /* reject A != A^T (bitwise) at create and set_values */
+    SLA_FLAG_REORDER = 2u,         /* always solve on P A P^T, P a reverse Cuthill-McKee
+                                      permutation of the pattern (see sla_csr_create) */
+    SLA_FLAG_NO_REORDER = 4u       /* never reorder */
+};
 
 /* per-system outcome of a solve */
 typedef enum { SLA_CONVERGED = 0, SLA_MAXIT = 1, SLA_BREAKDOWN = 2 } sla_outcome;
@@ -113,6 +118,17 @@ enum {
  *  values: [batch][nnz_in] of vtype, in input order.
  *  flags: SLA_FLAG_CHECK_SYMMETRIC rejects matrices that are not bitwise
  *    symmetric (for every value set).
+ *  Reordering for locality: the solver may run on P A P^T with P a reverse
+ *    Cuthill-McKee permutation of the pattern (computed on the host at
+ *    create), which turns scattered gathers into nearby ones. Jacobi-PCG is
+ *    invariant under symmetric permutation in exact arithmetic (diag(P A P^T)
+ *    = P diag(A) P^T), so only the summation order inside each row changes.
+ *    Every argument and result of every call stays in the caller's order and
+ *    the caller's CSR (sla_csr_get returns A's arrays). Default: reorder when
+ *    more than half of the SpMV tiles gather from a column range of 2^16 or
+ *    more, n >= 2^16 and nnz < 2^28; SLA_FLAG_REORDER forces it (n > 1),
+ *    SLA_FLAG_NO_REORDER disables it. A reordered handle holds a second copy
+ *    of the matrix and its solver workspace.
  * Synchronizes `stream` before returning (validation results are read back).
  * On failure *out is set to NULL.
  */
@@ -184,6 +200,13 @@ sla_status sla_pcg_solve(sla_csr h, const void *b, void *x, double tol, int32_t 
 sla_status sla_adjoint_backward(sla_csr h, const void *x, const void *grad_x, void *grad_b,
                                 void *grad_vals, double tol, int32_t maxit, sla_info *info,
                                 void *stream);
+
+/* How the solver holds the matrix (host outputs; any may be NULL): reordered
+ * = 1 when it runs on P A P^T; narrow_columns = 1 when every SpMV tile reads
+ * 16-bit column offsets; tiles and long_rows count the SpMV's short-row tiles
+ * and its rows longer than 128 entries. */
+sla_status sla_csr_get_layout(sla_csr h, int32_t *reordered, int32_t *narrow_columns,
+                              int64_t *tiles, int64_t *long_rows);
 
 /* Accumulated kernel timings of calls made while SLA_OPT_PROFILE was on
  * (host outputs): number of launches and total milliseconds per kind. */
