@@ -100,6 +100,8 @@ void alloc_workspace(Handle &h, hipStream_t s) {
     h.st = (SysState *)dalloc(h, sizeof(SysState) * h.B);
     h.ctl = (Ctl *)dalloc(h, sizeof(Ctl));
     SLA_HIP(hipMemsetAsync(h.ctl, 0, sizeof(Ctl), s));
+    h.bcast = (Bcast *)dalloc(h, sizeof(Bcast));
+    SLA_HIP(hipMemsetAsync(h.bcast, 0, sizeof(Bcast), s));
     SLA_HIP(hipMemsetAsync(h.st, 0, sizeof(SysState) * h.B, s));
     if (hipHostMalloc((void **)&h.h_running, sizeof(int32_t), hipHostMallocMapped) != hipSuccess)
         fail(SLA_ERR_OOM, "pinned host allocation failed");
@@ -273,6 +275,9 @@ void set_option(Handle *h, int32_t key, int64_t value) {
         case SLA_OPT_RESIDENT:
             if (value < 0 || value > 2) fail(SLA_ERR_INVALID_ARG, "resident mode in [0, 2]");
             h->res_mode = (int)value;
+            break;
+        case SLA_OPT_FUSED_UPDATE:
+            h->fuse_update = value != 0;
             break;
         default:
             fail(SLA_ERR_INVALID_ARG, "unknown option");

@@ -65,6 +65,17 @@ struct Ctl {
     double tol;
     int32_t maxit;
     int32_t n_running;
+    uint32_t epoch;   // solve counter: with the iteration count it names a broadcast
+    int32_t error;    // set by a kernel whose bounded wait timed out
+};
+
+// Step scalars broadcast by the last workgroup of the fused update +
+// direction kernel to the others: gen = epoch << 32 | iteration number.
+struct Bcast {
+    uint64_t gen;
+    double beta;
+    int32_t running;
+    int32_t pad;
 };
 
 // Arrival counters of the grid reductions: per kernel kind, kGroups group
@@ -133,6 +144,10 @@ struct Handle {
     uint32_t *sync = nullptr;     // [kCntKinds][kCountersPerKind] arrival counters
     SysState *st = nullptr;
     Ctl *ctl = nullptr;
+    Bcast *bcast = nullptr;
+    uint32_t epoch = 0;            // solves started on this handle
+    int64_t upd_dir_resident = 0;  // resident workgroups of the fused update + direction
+    bool fuse_update = true;       // single system: update and direction in one kernel
     int32_t *h_running = nullptr; // pinned, mapped
     int32_t *d_running = nullptr; // device alias of h_running
     SysState *h_state = nullptr;  // pinned

@@ -451,6 +451,161 @@ __global__ __launch_bounds__(kBlock) void k_update1(int64_t n, T *__restrict__ x
     }
 }
 
+// Single system, update and direction in one kernel: every workgroup does
+// one pass of kFusedGroups 16-byte groups per lane, keeps r, p and dinv of
+// its rows in registers, and waits for the last workgroup of the r.z / r.r
+// reduction to broadcast beta (and whether the system still runs); then it
+// writes p = z + beta p for the same rows. This saves reading r, p and dinv
+// a second time. All workgroups must be resident at once (the grid is at
+// most the occupancy-API count, launched on an otherwise idle stream); the
+// wait is bounded and a timeout is reported through ctl->error.
+constexpr int kFusedGroups = 4;
+constexpr uint32_t kBcastSpins = 1u << 22;
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_update_dir1(int64_t n, T *__restrict__ x,
+                                                        T *__restrict__ r, T *__restrict__ p,
+                                                        const T *__restrict__ q,
+                                                        const T *__restrict__ dinv,
+                                                        const double *__restrict__ spart,
+                                                        int64_t spart_n, Red red,
+                                                        Ctl *__restrict__ ctl,
+                                                        SysState *__restrict__ st,
+                                                        int32_t *__restrict__ h_running,
+                                                        Bcast *__restrict__ bc) {
+    constexpr int W = VecW<T>::W;
+    __shared__ double lds4[kWaves];
+    __shared__ double tmp[kBlock];
+    __shared__ double tot[2];
+    __shared__ double s_beta;
+    __shared__ int s_run;
+    if (ctl->n_running == 0) return;  // one system: running or not
+    const int tid = threadIdx.x;
+    const uint64_t gen = ((uint64_t)ctl->epoch << 32) | (uint32_t)(st[0].iter + 1);
+    double sg = 0.0;
+    for (int64_t j = tid; j < spart_n; j += 4 * kBlock) {
+        double v4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v4[u] = j + u * kBlock < spart_n ? spart[j + u * kBlock] : 0.0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sg += v4[u];
+    }
+    const double sigma = block_sum(sg, lds4);
+    const bool breakdown = !(sigma > 0.0) || !isfinite(sigma);
+    const double alpha = breakdown ? 0.0 : st[0].rho / sigma;
+    double srz = 0.0, srr = 0.0;
+    const int64_t ng = breakdown ? 0 : n / W;
+    const int64_t g0 = (int64_t)blockIdx.x * kBlock * kFusedGroups;
+    T xv[kFusedGroups][W], pv[kFusedGroups][W], rv[kFusedGroups][W], qv[kFusedGroups][W],
+        dv[kFusedGroups][W];
+#pragma unroll
+    for (int u = 0; u < kFusedGroups; ++u) {
+        const int64_t g = g0 + u * kBlock + tid;
+        if (g < ng) {
+            vload(x + g * W, xv[u]);
+            vload(p + g * W, pv[u]);
+            vload(r + g * W, rv[u]);
+            vload(q + g * W, qv[u]);
+            vload(dinv + g * W, dv[u]);
+        }
+    }
+    auto row = [&](T &xe, T &re, T pe, T qe, T de) {
+        xe = (T)((double)xe + alpha * (double)pe);
+        re = (T)((double)re - alpha * (double)qe);
+        const double z = (double)de * (double)re;
+        srz += (double)re * z;
+        srr += (double)re * (double)re;
+    };
+#pragma unroll
+    for (int u = 0; u < kFusedGroups; ++u) {
+        const int64_t g = g0 + u * kBlock + tid;
+        if (g < ng) {
+#pragma unroll
+            for (int k = 0; k < W; ++k) row(xv[u][k], rv[u][k], pv[u][k], qv[u][k], dv[u][k]);
+            vstore(x + g * W, xv[u]);
+            vstore(r + g * W, rv[u]);
+        }
+    }
+    // rows past the last whole group: workgroup 0, one per lane
+    const bool tail = !breakdown && blockIdx.x == 0 && tid < n - ng * W;
+    T xt = (T)0, rt = (T)0, pt = (T)0, dt = (T)0;
+    if (tail) {
+        const int64_t i = ng * W + tid;
+        xt = x[i];
+        rt = r[i];
+        pt = p[i];
+        dt = dinv[i];
+        row(xt, rt, pt, q[i], dt);
+        x[i] = xt;
+        r[i] = rt;
+    }
+    srz = block_sum(srz, lds4);
+    srr = block_sum(srr, lds4);
+    if (tid == 0) {
+        store_partial(red.part + (int64_t)blockIdx.x * 2, srz);
+        store_partial(red.part + (int64_t)blockIdx.x * 2 + 1, srr);
+    }
+    if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, 2, tmp, tot)) {
+        if (tid == 0) {
+            SysState &sy = st[0];
+            const double rz = tot[0], rr = tot[1];
+            int running = 0;
+            sy.iter += 1;
+            if (breakdown) {
+                sy.status = SLA_BREAKDOWN;  // x, r untouched; rr keeps the last residual
+            } else {
+                sy.rr = rr;
+                if (sqrt(rr) <= ctl->tol * sqrt(sy.bb)) {
+                    sy.status = SLA_CONVERGED;
+                } else if (sy.iter >= ctl->maxit) {
+                    sy.status = SLA_MAXIT;
+                } else {
+                    sy.beta = rz / sy.rho;
+                    sy.rho = rz;
+                    running = 1;
+                }
+            }
+            publish_running(ctl, h_running, running);
+            __hip_atomic_store(&bc->beta, sy.beta, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&bc->running, running, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __hip_atomic_store(&bc->gen, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (tid == 0) {
+        uint32_t spins = 0;
+        bool ok = true;
+        while (__hip_atomic_load(&bc->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != gen) {
+            if (++spins > kBcastSpins) {
+                ok = false;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (ok) {
+            s_beta = __hip_atomic_load(&bc->beta, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_run = __hip_atomic_load(&bc->running, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            __hip_atomic_store(&ctl->error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_run = 0;
+        }
+    }
+    __syncthreads();
+    if (!s_run) return;
+    const double beta = s_beta;
+#pragma unroll
+    for (int u = 0; u < kFusedGroups; ++u) {
+        const int64_t g = g0 + u * kBlock + tid;
+        if (g < ng) {
+#pragma unroll
+            for (int k = 0; k < W; ++k)
+                pv[u][k] = (T)((double)dv[u][k] * (double)rv[u][k] + beta * (double)pv[u][k]);
+            vstore(p + g * W, pv[u]);
+        }
+    }
+    if (tail) p[ng * W + tid] = (T)((double)dt * (double)rt + beta * (double)pt);
+}
+
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_direction1(int64_t n, const T *__restrict__ r,
                                                        T *__restrict__ p,
@@ -489,6 +644,16 @@ __global__ __launch_bounds__(kBlock) void k_direction1(int64_t n, const T *__res
         const int64_t i = ng * W + tid;
         p[i] = (T)((double)dinv[i] * (double)r[i] + beta * (double)p[i]);
     }
+}
+
+// grid of the fused update + direction: one pass per workgroup, all of them
+// resident at once; 0 when the system does not fit (or B > 1)
+int64_t fused_grid(const Handle &h, int W) {
+    if (h.B != 1 || !h.fuse_update || h.upd_dir_resident <= 0) return 0;
+    const int64_t per = (int64_t)kBlock * kFusedGroups;
+    int64_t g = (h.n / W + per - 1) / per;
+    if (g < 1) g = 1;
+    return g <= h.upd_dir_resident ? g : 0;
 }
 
 int64_t vec1_grid(int64_t n, int W) {
@@ -607,6 +772,16 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
     if (lp) lp->end(SLA_KERNEL_SPMV_DOT, a);
     if (lp) lp->begin(SLA_KERNEL_UPDATE, &a);
     const Red red{h.part, h.gpart, h.sync + kCntUpdate * kCountersPerKind};
+    const int64_t gf = fused_grid(h, VecW<T>::W);
+    if (gf > 0) {
+        hipLaunchKernelGGL(k_update_dir1<T>, dim3((unsigned)gf), dim3(kBlock), 0, s, h.n, (T *)h.x,
+                           (T *)h.r, (T *)h.p, (const T *)h.q, (const T *)h.dinv,
+                           (const double *)h.spart, spmv_grid(h), red, h.ctl, h.st, h.d_running,
+                           h.bcast);
+        SLA_HIP(hipGetLastError());
+        if (lp) lp->end(SLA_KERNEL_UPDATE, a);
+        return;
+    }
     if (h.B == 1) {
         const int64_t g1 = vec1_grid(h.n, VecW<T>::W);
         hipLaunchKernelGGL(k_update1<T>, dim3((unsigned)g1), dim3(kBlock), 0, s, h.n, (T *)h.x,
@@ -692,7 +867,12 @@ void init_t(Handle &h, const void *b_int, hipStream_t s, Launcher *lp) {
 }  // namespace
 
 void init_vector_limits(Handle &h) {
-    if (h.B < 2) return;
+    if (h.B == 1) {
+        h.upd_dir_resident = resident_workgroups(
+            h.vt == SLA_F64 ? (const void *)&k_update_dir1<double> : (const void *)&k_update_dir1<float>,
+            h.device);
+        return;
+    }
     if (h.vt == SLA_F64) {
         h.bv_update_resident = resident_workgroups((const void *)&k_update_bv<double>, h.device);
         h.bv_direction_resident = resident_workgroups((const void *)&k_direction_bv<double>, h.device);
@@ -746,6 +926,8 @@ void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit,
     h.h_ctl->tol = tol;
     h.h_ctl->maxit = maxit;
     h.h_ctl->n_running = 0;
+    h.h_ctl->epoch = ++h.epoch;
+    h.h_ctl->error = 0;
     SLA_HIP(hipMemcpyAsync(h.ctl, h.h_ctl, sizeof(Ctl), hipMemcpyHostToDevice, s));
     if (h.B == 1 && resident_ready(h, s)) {
         // the whole solve in one cooperative kernel (same recurrence)
@@ -795,8 +977,11 @@ void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit,
             transpose(h.x, x_user, h.n, h.B, h.vbytes, s);
     }
     SLA_HIP(hipMemcpyAsync(h.h_state, h.st, sizeof(SysState) * h.B, hipMemcpyDeviceToHost, s));
+    SLA_HIP(hipMemcpyAsync(h.h_ctl, h.ctl, sizeof(Ctl), hipMemcpyDeviceToHost, s));
     SLA_HIP(hipStreamSynchronize(s));
     if (h.profile) flush_profile(h);
+    if (h.h_ctl->error)
+        fail(SLA_ERR_HIP, "fused update: a grid-wide wait timed out (workgroups not co-resident)");
     for (int b = 0; b < h.B; ++b) {
         const SysState &st = h.h_state[b];
         info[b].iterations = st.iter;

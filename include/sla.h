@@ -85,18 +85,23 @@ enum {
                                    hipGraph; 0: launch kernels one by one */
     SLA_OPT_PROFILE = 3,        /* 1: time every kernel launch of later calls with hipEvents
                                    (implies eager launches); 0 (default): off */
-    SLA_OPT_RESIDENT = 4        /* single-system solve as one cooperative kernel that keeps
+    SLA_OPT_RESIDENT = 4,       /* single-system solve as one cooperative kernel that keeps
                                    x, r, p and dinv on chip (same recurrence, same
                                    outcomes): 0 never; 1 (default) when applicable and
                                    n <= 2^15; 2 whenever applicable. Applicable: batch 1,
                                    no row longer than 128 entries, n <= 8192 rows per CU
                                    (2^21 on 256 CUs), cooperative launch available. */
+    SLA_OPT_FUSED_UPDATE = 5    /* 1 (default): a single system whose update fits one pass of
+                                   the resident workgroups runs the update and the direction
+                                   as one kernel (r, p, dinv stay in registers while beta is
+                                   formed); 0: two kernels. Same arithmetic either way. */
 };
 
 /* kernel kinds reported by sla_profile_get */
 enum {
     SLA_KERNEL_SPMV_DOT = 0,  /* q = A p fused with the per-block p.q partials and alpha */
-    SLA_KERNEL_UPDATE = 1,    /* x += alpha p, r -= alpha q, r.z and r.r partials, beta, test */
+    SLA_KERNEL_UPDATE = 1,    /* x += alpha p, r -= alpha q, r.z and r.r partials, beta, test
+                                 (and p = z + beta p when fused, see SLA_OPT_FUSED_UPDATE) */
     SLA_KERNEL_DIRECTION = 2, /* p = z + beta p */
     SLA_KERNEL_INIT = 3,      /* r = b, x = 0, p = z, b.b and r.z */
     SLA_KERNEL_SPMV = 4,      /* plain y = A x */
