@@ -50,6 +50,9 @@ def lib() -> ctypes.CDLL:
         L.orc_is_symmetric_f64.argtypes = [i64, P, P, P]
         L.orc_spmv_f64.argtypes = [i64, P, P, P, P, P]
         L.orc_spmv_f32.argtypes = [i64, P, P, P, P, P]
+        L.orc_spmv_backward_f64.argtypes = [i64, P, P, P, P, P, P, P]
+        L.orc_spmv_backward_f64.restype = None
+        L.orc_spmv_backward_f32.argtypes = [i64, P, P, P, P, P, P, P]
         L.orc_jacobi_f64.argtypes = [i64, P, P, P, P]
         L.orc_jacobi_f32.argtypes = [i64, P, P, P, P]
         L.orc_pcg_f64.argtypes = [i64, P, P, P, P, f64, i32, P, P, P, P]
@@ -57,7 +60,8 @@ def lib() -> ctypes.CDLL:
         L.orc_pcg_batched.argtypes = [i64, i32, P, P, i32, P, P, f64, i32, P, P, P, P]
         L.orc_adjoint.argtypes = [i64, i32, P, P, i32, P, P, P, f64, i32, P, P, P, P, P]
         for name in ("orc_coo_to_csr", "orc_check_csr", "orc_is_symmetric_f64", "orc_jacobi_f64",
-                     "orc_jacobi_f32", "orc_pcg_f64", "orc_pcg_f32", "orc_pcg_batched", "orc_adjoint"):
+                     "orc_jacobi_f32", "orc_pcg_f64", "orc_pcg_f32", "orc_pcg_batched", "orc_adjoint",
+                     "orc_spmv_backward_f32"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -147,6 +151,34 @@ def spmv(row_ptr, col, val, x):
         vs, xs, ys = np.ascontiguousarray(val[s]), np.ascontiguousarray(x[s]), y[s]
         fn(n, _p(row_ptr), _p(col), _p(vs), _p(xs), _p(ys))
     return y
+
+
+def spmv_backward(row_ptr, col, val, x, g):
+    """Backward of y = A x for an upstream gradient g = dL/dy: returns
+    (A^T g, grad_vals) with grad_vals[k] = g[row k] * x[col k] in CSR order;
+    batched when val is [B, nnz] (x, g [B, n])."""
+    row_ptr, col = _i64(row_ptr), _i64(col)
+    val = _vals(val)
+    x, g = _vals(x, val.dtype), _vals(g, val.dtype)
+    n = row_ptr.shape[0] - 1
+    f32 = val.dtype == np.float32
+
+    def one(vs, xs, gs):
+        gx = np.empty(n, val.dtype)
+        gv = np.empty(vs.shape[0], val.dtype)
+        if f32:
+            _check(lib().orc_spmv_backward_f32(n, _p(row_ptr), _p(col), _p(vs), _p(xs), _p(gs),
+                                               _p(gx), _p(gv)), "spmv_backward")
+        else:
+            lib().orc_spmv_backward_f64(n, _p(row_ptr), _p(col), _p(vs), _p(xs), _p(gs), _p(gx),
+                                        _p(gv))
+        return gx, gv
+
+    if val.ndim == 1:
+        return one(val, x, g)
+    out = [one(np.ascontiguousarray(val[s]), np.ascontiguousarray(x[s]), np.ascontiguousarray(g[s]))
+           for s in range(val.shape[0])]
+    return np.stack([o[0] for o in out]), np.stack([o[1] for o in out])
 
 
 def jacobi(row_ptr, col, val):

@@ -248,6 +248,40 @@ void orc_spmv_f32(int64_t n, const int64_t *row_ptr, const int64_t *col, const f
     }
 }
 
+/* ------------------------------------------------------------------ SpMV backward
+ * torch-sla counts matvec among the operations that carry gradients (the
+ * tensor-types passage; Table 1's operation list). For y = A x and an upstream
+ * gradient g = dL/dy the definitions are
+ *   dL/dx_j    = sum over stored entries (i, j) of a_ij g_i   (A^T g)
+ *   dL/da_ij   = g_i x_j                                      (stored entries)
+ * A^T g is accumulated while walking A row by row, so for each j the terms
+ * arrive in increasing i; fp32 storage keeps the sums in fp64 and rounds
+ * once per stored value. */
+void orc_spmv_backward_f64(int64_t n, const int64_t *row_ptr, const int64_t *col,
+                           const double *val, const double *x, const double *g, double *grad_x,
+                           double *grad_vals) {
+    for (int64_t j = 0; j < n; ++j) grad_x[j] = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t k = row_ptr[i]; k < row_ptr[i + 1]; ++k) {
+            grad_x[col[k]] = grad_x[col[k]] + val[k] * g[i];
+            grad_vals[k] = g[i] * x[col[k]];
+        }
+}
+
+int orc_spmv_backward_f32(int64_t n, const int64_t *row_ptr, const int64_t *col, const float *val,
+                          const float *x, const float *g, float *grad_x, float *grad_vals) {
+    double *acc = (double *)calloc((size_t)(n > 0 ? n : 1), sizeof(double));
+    if (!acc) return ORC_ERR_OOM;
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t k = row_ptr[i]; k < row_ptr[i + 1]; ++k) {
+            acc[col[k]] = acc[col[k]] + (double)val[k] * (double)g[i];
+            grad_vals[k] = (float)((double)g[i] * (double)x[col[k]]);
+        }
+    for (int64_t j = 0; j < n; ++j) grad_x[j] = (float)acc[j];
+    free(acc);
+    return ORC_OK;
+}
+
 /* ------------------------------------------------------------------ Jacobi
  * M = diag(A): d_i is the stored entry (i, i); it must exist, be finite and
  * positive (the matrix is SPD). dinv_i = 1/d_i; the preconditioner is applied
