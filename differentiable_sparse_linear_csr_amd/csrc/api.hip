@@ -66,6 +66,7 @@ void destroy_handle(Handle *h) {
     if (!h) return;
     (void)hipSetDevice(h->device);
     if (h->inner) destroy_handle(h->inner);
+    if (h->tr) destroy_handle(h->tr);
     if (h->graph) (void)hipGraphExecDestroy(h->graph);
     for (auto &rec : h->pending) {
         (void)hipEventDestroy(rec.a);
@@ -199,6 +200,7 @@ sla_status sla_csr_set_values(sla_csr hd, const void *values, void *stream) {
         if ((h->flags & SLA_FLAG_CHECK_SYMMETRIC) && !check_symmetric(*h, s))
             fail(SLA_ERR_NOT_SYMMETRIC, "matrix is not symmetric (bitwise)");
         if (h->inner) reordered_set_values(*h, s);
+        h->tr_stale = h->tr != nullptr;
     });
 }
 
@@ -301,6 +303,31 @@ sla_status sla_spmv(sla_csr hd, const void *x, void *y, void *stream) {
     });
 }
 
+sla_status sla_spmv_backward(sla_csr hd, const void *x, const void *grad_y, void *grad_x,
+                             void *grad_vals_out, void *stream) {
+    return guard([&] {
+        Handle *h = checked(hd);
+        if (!x || !grad_y) fail(SLA_ERR_INVALID_ARG, "null pointer");
+        if (grad_x && (grad_x == grad_y || grad_x == x))
+            fail(SLA_ERR_INVALID_ARG, "grad_x must not alias x or grad_y");
+        hipStream_t s = (hipStream_t)stream;
+        if (grad_x) any_spmv(*transpose_for_backward(*h, s), grad_y, grad_x, s);
+        if (grad_vals_out && h->nnz > 0) {
+            // grad_y in the internal layout [n][B] (the workspace q holds it)
+            const void *g_int = grad_y;
+            if (h->B > 1) {
+                transpose(grad_y, h->q, h->B, h->n, h->vbytes, s);
+                g_int = h->q;
+            }
+            grad_vals(*h, g_int, x, grad_vals_out, s, 1.0);
+        }
+        if (h->profile) {
+            SLA_HIP(hipStreamSynchronize(s));
+            flush_profile(*h);
+        }
+    });
+}
+
 sla_status sla_pcg_solve(sla_csr hd, const void *b, void *x, double tol, int32_t maxit,
                          sla_info *info, void *stream) {
     return guard([&] {
@@ -370,7 +397,11 @@ sla_status sla_csr_memory(sla_csr hd, int64_t *bytes) {
     return guard([&] {
         if (!hd || !bytes) fail(SLA_ERR_INVALID_ARG, "null pointer");
         const Handle *h = reinterpret_cast<const Handle *>(hd);
-        *bytes = h->bytes + (h->inner ? h->inner->bytes : 0);
+        int64_t b = 0;
+        for (const Handle *c : {h, (const Handle *)h->inner, (const Handle *)h->tr,
+                                h->tr ? (const Handle *)h->tr->inner : nullptr})
+            if (c) b += c->bytes;
+        *bytes = b;
     });
 }
 

@@ -181,6 +181,10 @@ struct Handle {
     void *rtmp[2] = {nullptr, nullptr};  // [B][n] vectors in the inner order
     void *rtmp_grad = nullptr;    // [B][nnz] value gradient in the inner order
     int64_t wide_tiles = 0;       // tiles whose columns span 2^16 or more
+    // A^T for the backward of y = A x (built at the first backward)
+    Handle *tr = nullptr;
+    int64_t *tr_map = nullptr;    // [nnz]: A^T CSR position -> this CSR position
+    bool tr_stale = false;        // values changed since A^T's were gathered
 
     // iteration driver
     int check_k = 16;
@@ -237,10 +241,18 @@ void reordered_pcg(Handle &h, const void *b, void *x, double tol, int32_t maxit,
                    hipStream_t s);
 void reordered_adjoint(Handle &h, const void *x, const void *g, void *grad_b, void *grad_vals,
                        double tol, int32_t maxit, sla_info *info, hipStream_t s);
+Handle *make_child(Handle &h, const std::vector<int64_t> &rp, const std::vector<int32_t> &col,
+                   const int64_t *map, uint32_t flags, hipStream_t s);
+void child_values(Handle &h, Handle &child, const int64_t *map, hipStream_t s);
+void any_spmv(Handle &h, const void *x, void *y, hipStream_t s);
+Handle *transpose_for_backward(Handle &h, hipStream_t s);
 int64_t resident_workgroups(const void *kernel, int device);
 void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit, sla_info *info,
          hipStream_t s, bool keep_internal_solution);
-void grad_vals(Handle &h, const void *lam_internal, const void *x_user, void *grad, hipStream_t s);
+// grad[b][k] = sign * a[row k][b] * x[b][col k]: a in the internal layout
+// [n][B], x in the caller's [B][n], grad [B][nnz] in CSR order
+void grad_vals(Handle &h, const void *a_internal, const void *x_user, void *grad, hipStream_t s,
+               double sign = -1.0);
 bool resident_ready(Handle &h, hipStream_t s);   // builds the plan on first use
 void resident_solve(Handle &h, const void *b, double tol, int32_t maxit, hipStream_t s);
 void flush_profile(Handle &h);

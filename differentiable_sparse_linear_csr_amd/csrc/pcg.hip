@@ -707,7 +707,7 @@ __global__ __launch_bounds__(kBlock) void k_grad_tile(const TileDesc *__restrict
                                                       const int32_t *__restrict__ col, int64_t nnz,
                                                       int B, const T *__restrict__ lam,
                                                       const T *__restrict__ x,
-                                                      T *__restrict__ grad) {
+                                                      T *__restrict__ grad, double sign) {
     __shared__ int32_t rowid[kTileCap];
     const int tid = threadIdx.x;
     const TileDesc d = tiles[blockIdx.x];
@@ -719,7 +719,7 @@ __global__ __launch_bounds__(kBlock) void k_grad_tile(const TileDesc *__restrict
         for (int64_t kk = tid; kk < nk; kk += kBlock) {
             const int64_t i = rowid[kk];
             const int64_t k = d.k0 + kk;
-            const double g = -((double)lam[i * B + b] * (double)x[(int64_t)col[k] * B + b]);
+            const double g = sign * ((double)lam[i * B + b] * (double)x[(int64_t)col[k] * B + b]);
             grad[(int64_t)b * nnz + k] = (T)g;
         }
     }
@@ -732,13 +732,13 @@ __global__ __launch_bounds__(kBlock) void k_grad_long(const int32_t *__restrict_
                                                       const int32_t *__restrict__ col, int64_t nnz,
                                                       int B, const T *__restrict__ lam,
                                                       const T *__restrict__ x,
-                                                      T *__restrict__ grad) {
+                                                      T *__restrict__ grad, double sign) {
     const int64_t i = long_rows[blockIdx.x];
     const int64_t k0 = row_ptr[i], k1 = row_ptr[i + 1];
     for (int b = 0; b < B; ++b) {
         const double li = (double)lam[i * B + b];
         for (int64_t k = k0 + threadIdx.x; k < k1; k += kBlock)
-            grad[(int64_t)b * nnz + k] = (T)(-(li * (double)x[(int64_t)col[k] * B + b]));
+            grad[(int64_t)b * nnz + k] = (T)(sign * (li * (double)x[(int64_t)col[k] * B + b]));
     }
 }
 
@@ -992,7 +992,8 @@ void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit,
 
 // grad [B][nnz] (CSR order) from lambda (internal layout, h.x) and the
 // forward solution x_user [B][n].
-void grad_vals(Handle &h, const void *lam_internal, const void *x_user, void *grad, hipStream_t s) {
+void grad_vals(Handle &h, const void *lam_internal, const void *x_user, void *grad, hipStream_t s,
+               double sign) {
     if (h.nnz == 0) return;
     Launcher L{h, s, h.profile};
     const void *x_int = x_user;
@@ -1009,12 +1010,12 @@ void grad_vals(Handle &h, const void *lam_internal, const void *x_user, void *gr
             hipLaunchKernelGGL((k_grad_tile<T, RP>), dim3((unsigned)h.ntiles), dim3(kBlock), 0, s,
                                (const TileDesc *)h.tiles, (const RP *)h.row_ptr,
                                (const int32_t *)h.col, h.nnz, h.B, (const T *)lam_internal,
-                               (const T *)x_int, (T *)grad);
+                               (const T *)x_int, (T *)grad, sign);
         if (h.nlong > 0)
             hipLaunchKernelGGL((k_grad_long<T, RP>), dim3((unsigned)h.nlong), dim3(kBlock), 0, s,
                                (const int32_t *)h.long_rows, (const RP *)h.row_ptr,
                                (const int32_t *)h.col, h.nnz, h.B, (const T *)lam_internal,
-                               (const T *)x_int, (T *)grad);
+                               (const T *)x_int, (T *)grad, sign);
     };
     if (h.vt == SLA_F64) {
         if (h.rp64) go(double(), int64_t());

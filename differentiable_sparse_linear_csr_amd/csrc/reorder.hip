@@ -210,6 +210,87 @@ void to_outer(Handle &h, const void *in, void *out, hipStream_t s) {
 
 }  // namespace
 
+// A handle for a matrix with the same entries as h in another arrangement:
+// CSR (rp, col) on the host, and map[k] = position in h's CSR of entry k
+// (device array, kept by the caller). Values are gathered from h's.
+Handle *make_child(Handle &h, const std::vector<int64_t> &rp, const std::vector<int32_t> &col,
+                   const int64_t *map, uint32_t flags, hipStream_t s) {
+    const int64_t n = (int64_t)rp.size() - 1, nnz = (int64_t)col.size();
+    const bool rp64 = nnz >= ((int64_t)1 << 31);
+    void *d_rp = nullptr, *d_col = nullptr, *d_vals = nullptr;
+    SLA_HIP(hipMalloc(&d_rp, (size_t)(n + 1) * (rp64 ? 8 : 4)));
+    SLA_HIP(hipMalloc(&d_col, 4 * (size_t)(nnz + 1)));
+    SLA_HIP(hipMalloc(&d_vals, (size_t)(nnz + 1) * h.B * h.vbytes));
+    Handle *in = nullptr;
+    try {
+        if (rp64) {
+            SLA_HIP(hipMemcpyAsync(d_rp, rp.data(), 8 * (size_t)(n + 1), hipMemcpyHostToDevice, s));
+        } else {
+            std::vector<int32_t> r32((size_t)n + 1);
+            for (int64_t i = 0; i <= n; ++i) r32[(size_t)i] = (int32_t)rp[(size_t)i];
+            SLA_HIP(hipMemcpyAsync(d_rp, r32.data(), 4 * (size_t)(n + 1), hipMemcpyHostToDevice, s));
+            SLA_HIP(hipStreamSynchronize(s));
+        }
+        if (nnz > 0) {
+            SLA_HIP(hipMemcpyAsync(d_col, col.data(), 4 * (size_t)nnz, hipMemcpyHostToDevice, s));
+            if (h.vt == SLA_F64)
+                hipLaunchKernelGGL(k_vals_to_inner_bm<double>, dim3(grid_of(nnz * h.B)), dim3(kBlock),
+                                   0, s, (const double *)h.vals, (double *)d_vals, map, nnz, h.B);
+            else
+                hipLaunchKernelGGL(k_vals_to_inner_bm<float>, dim3(grid_of(nnz * h.B)), dim3(kBlock),
+                                   0, s, (const float *)h.vals, (float *)d_vals, map, nnz, h.B);
+            SLA_HIP(hipGetLastError());
+        }
+        in = new Handle();
+        in->device = h.device;
+        in->n = n;
+        in->nnz_in = nnz;
+        in->B = h.B;
+        in->vt = h.vt;
+        in->vbytes = h.vbytes;
+        in->flags = flags;
+        build_from_csr(*in, rp64 ? SLA_I64 : SLA_I32, d_rp, SLA_I32, d_col, d_vals, s);
+        build_tiles(*in, s);
+        init_launch_limits(*in);
+        init_vector_limits(*in);
+        alloc_workspace(*in, s);
+        compute_dinv(*in, s);
+        if (want_reorder(*in)) build_reordered(*in, s);
+        SLA_HIP(hipStreamSynchronize(s));
+    } catch (...) {
+        (void)hipFree(d_rp);
+        (void)hipFree(d_col);
+        (void)hipFree(d_vals);
+        if (in) destroy_handle(in);
+        throw;
+    }
+    SLA_HIP(hipFree(d_rp));
+    SLA_HIP(hipFree(d_col));
+    SLA_HIP(hipFree(d_vals));
+    return in;
+}
+
+// values of a child from h's (same map as at make_child)
+void child_values(Handle &h, Handle &child, const int64_t *map, hipStream_t s) {
+    if (h.nnz > 0) {
+        if (h.vt == SLA_F64)
+            hipLaunchKernelGGL(k_vals_to_inner<double>, dim3(grid_of(h.nnz * h.B)), dim3(kBlock), 0,
+                               s, (const double *)h.vals, (double *)child.vals, map, h.nnz, h.B);
+        else
+            hipLaunchKernelGGL(k_vals_to_inner<float>, dim3(grid_of(h.nnz * h.B)), dim3(kBlock), 0,
+                               s, (const float *)h.vals, (float *)child.vals, map, h.nnz, h.B);
+        SLA_HIP(hipGetLastError());
+    }
+    compute_dinv(child, s);
+    if (child.inner) reordered_set_values(child, s);
+}
+
+// y = A x for any handle (reordered or not), vectors in the caller's order
+void any_spmv(Handle &h, const void *x, void *y, hipStream_t s) {
+    if (h.inner) reordered_spmv(h, x, y, s);
+    else spmv(h, x, y, s);
+}
+
 // Reorder when asked to, or automatically when most SpMV tiles gather from
 // column ranges of 2^16 or more (poor locality) on a matrix large enough for
 // it to matter (n >= 2^16) and small enough for the host ordering (nnz < 2^28).
@@ -270,7 +351,7 @@ void build_reordered(Handle &h, hipStream_t s) {
         }
     });
 
-    // device copies: maps, permutation, inner pattern and values
+    // device copies: maps, permutation, and the solver handle of P A P^T
     h.new2old = (int32_t *)dalloc(h, sizeof(int32_t) * (size_t)n);
     h.map_in = (int64_t *)dalloc(h, sizeof(int64_t) * (size_t)(nnz + 1));
     h.map_out = (int64_t *)dalloc(h, sizeof(int64_t) * (size_t)(nnz + 1));
@@ -284,78 +365,11 @@ void build_reordered(Handle &h, hipStream_t s) {
         SLA_HIP(hipMemcpyAsync(h.map_in, map_in.data(), 8 * (size_t)nnz, hipMemcpyHostToDevice, s));
         SLA_HIP(hipMemcpyAsync(h.map_out, map_out.data(), 8 * (size_t)nnz, hipMemcpyHostToDevice, s));
     }
-    const bool rp64 = nnz >= ((int64_t)1 << 31);
-    void *d_rp = nullptr, *d_col = nullptr, *d_vals = nullptr;
-    SLA_HIP(hipMalloc(&d_rp, (size_t)(n + 1) * (rp64 ? 8 : 4)));
-    SLA_HIP(hipMalloc(&d_col, 4 * (size_t)(nnz + 1)));
-    SLA_HIP(hipMalloc(&d_vals, (size_t)(nnz + 1) * h.B * h.vbytes));
-    Handle *in = nullptr;
-    try {
-        if (rp64) {
-            SLA_HIP(hipMemcpyAsync(d_rp, irp.data(), 8 * (size_t)(n + 1), hipMemcpyHostToDevice, s));
-        } else {
-            std::vector<int32_t> r32((size_t)n + 1);
-            for (int64_t i = 0; i <= n; ++i) r32[(size_t)i] = (int32_t)irp[(size_t)i];
-            SLA_HIP(hipMemcpyAsync(d_rp, r32.data(), 4 * (size_t)(n + 1), hipMemcpyHostToDevice, s));
-            SLA_HIP(hipStreamSynchronize(s));
-        }
-        if (nnz > 0)
-            SLA_HIP(hipMemcpyAsync(d_col, icol.data(), 4 * (size_t)nnz, hipMemcpyHostToDevice, s));
-        if (nnz > 0) {
-            if (h.vt == SLA_F64)
-                hipLaunchKernelGGL(k_vals_to_inner_bm<double>, dim3(grid_of(nnz * h.B)), dim3(kBlock),
-                                   0, s, (const double *)h.vals, (double *)d_vals,
-                                   (const int64_t *)h.map_in, nnz, h.B);
-            else
-                hipLaunchKernelGGL(k_vals_to_inner_bm<float>, dim3(grid_of(nnz * h.B)), dim3(kBlock),
-                                   0, s, (const float *)h.vals, (float *)d_vals,
-                                   (const int64_t *)h.map_in, nnz, h.B);
-            SLA_HIP(hipGetLastError());
-        }
-        in = new Handle();
-        in->device = h.device;
-        in->n = n;
-        in->nnz_in = nnz;
-        in->B = h.B;
-        in->vt = h.vt;
-        in->vbytes = h.vbytes;
-        in->flags = 0;
-        build_from_csr(*in, rp64 ? SLA_I64 : SLA_I32, d_rp, SLA_I32, d_col, d_vals, s);
-        build_tiles(*in, s);
-        init_launch_limits(*in);
-        init_vector_limits(*in);
-        alloc_workspace(*in, s);
-        compute_dinv(*in, s);
-        SLA_HIP(hipStreamSynchronize(s));
-    } catch (...) {
-        (void)hipFree(d_rp);
-        (void)hipFree(d_col);
-        (void)hipFree(d_vals);
-        if (in) destroy_handle(in);
-        throw;
-    }
-    SLA_HIP(hipFree(d_rp));
-    SLA_HIP(hipFree(d_col));
-    SLA_HIP(hipFree(d_vals));
-    h.inner = in;
+    h.inner = make_child(h, irp, icol, h.map_in, SLA_FLAG_NO_REORDER, s);
 }
 
 // after this handle's values changed: the inner values and Jacobi diagonal
-void reordered_set_values(Handle &h, hipStream_t s) {
-    Handle &in = *h.inner;
-    if (h.nnz > 0) {
-        if (h.vt == SLA_F64)
-            hipLaunchKernelGGL(k_vals_to_inner<double>, dim3(grid_of(h.nnz * h.B)), dim3(kBlock), 0,
-                               s, (const double *)h.vals, (double *)in.vals,
-                               (const int64_t *)h.map_in, h.nnz, h.B);
-        else
-            hipLaunchKernelGGL(k_vals_to_inner<float>, dim3(grid_of(h.nnz * h.B)), dim3(kBlock), 0,
-                               s, (const float *)h.vals, (float *)in.vals,
-                               (const int64_t *)h.map_in, h.nnz, h.B);
-        SLA_HIP(hipGetLastError());
-    }
-    compute_dinv(in, s);
-}
+void reordered_set_values(Handle &h, hipStream_t s) { child_values(h, *h.inner, h.map_in, s); }
 
 void reordered_spmv(Handle &h, const void *x, void *y, hipStream_t s) {
     to_inner(h, x, h.rtmp[0], s);
@@ -401,6 +415,56 @@ void reordered_adjoint(Handle &h, const void *x, const void *g, void *grad_b, vo
     }
     SLA_HIP(hipStreamSynchronize(s));
     if (in.profile) flush_profile(in);
+}
+
+// ------------------------------------------------------------------ A^T for the matvec backward
+// The backward of y = A x needs A^T g. A handle checked for bitwise symmetry
+// uses itself (row i of A^T holds the same values in the same column order as
+// row i of A). Otherwise the first backward builds a child handle of A^T:
+// the pattern by a counting sort of the columns on the host (rows of A^T list
+// their entries in increasing row of A), values gathered from A's through a
+// position map, refreshed after set_values.
+Handle *transpose_for_backward(Handle &h, hipStream_t s) {
+    if (h.flags & SLA_FLAG_CHECK_SYMMETRIC) return &h;
+    if (h.tr) {
+        if (h.tr_stale) {
+            child_values(h, *h.tr, h.tr_map, s);
+            h.tr_stale = false;
+        }
+        return h.tr;
+    }
+    const int64_t n = h.n, nnz = h.nnz;
+    std::vector<int64_t> rp((size_t)n + 1);
+    std::vector<int32_t> col((size_t)nnz);
+    if (h.rp64) {
+        SLA_HIP(hipMemcpyAsync(rp.data(), h.row_ptr, 8 * (size_t)(n + 1), hipMemcpyDeviceToHost, s));
+    } else {
+        std::vector<int32_t> r32((size_t)n + 1);
+        SLA_HIP(hipMemcpyAsync(r32.data(), h.row_ptr, 4 * (size_t)(n + 1), hipMemcpyDeviceToHost, s));
+        SLA_HIP(hipStreamSynchronize(s));
+        for (int64_t i = 0; i <= n; ++i) rp[(size_t)i] = r32[(size_t)i];
+    }
+    if (nnz > 0)
+        SLA_HIP(hipMemcpyAsync(col.data(), h.col, 4 * (size_t)nnz, hipMemcpyDeviceToHost, s));
+    SLA_HIP(hipStreamSynchronize(s));
+    std::vector<int64_t> trp((size_t)n + 1, 0);
+    for (int64_t k = 0; k < nnz; ++k) ++trp[(size_t)col[(size_t)k] + 1];
+    for (int64_t j = 0; j < n; ++j) trp[(size_t)j + 1] += trp[(size_t)j];
+    std::vector<int64_t> fill(trp.begin(), trp.end() - 1);
+    std::vector<int32_t> tcol((size_t)nnz);
+    std::vector<int64_t> tmap((size_t)nnz);
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t k = rp[(size_t)i]; k < rp[(size_t)i + 1]; ++k) {
+            const int64_t pos = fill[(size_t)col[(size_t)k]]++;
+            tcol[(size_t)pos] = (int32_t)i;
+            tmap[(size_t)pos] = k;
+        }
+    h.tr_map = (int64_t *)dalloc(h, sizeof(int64_t) * (size_t)(nnz + 1));
+    if (nnz > 0)
+        SLA_HIP(hipMemcpyAsync(h.tr_map, tmap.data(), 8 * (size_t)nnz, hipMemcpyHostToDevice, s));
+    h.tr = make_child(h, trp, tcol, h.tr_map, 0, s);
+    h.tr_stale = false;
+    return h.tr;
 }
 
 }  // namespace sla

@@ -209,6 +209,27 @@ class SparseCSR:
         check(_lib.load().sla_spmv(self._h, _ptr(x), _ptr(y), _stream(self.device)))
         return y
 
+    def matvec_backward_raw(self, x: torch.Tensor, grad_y: torch.Tensor, want_x: bool = True,
+                            want_vals: bool = True):
+        """Backward of y = A x: (A^T grad_y, grad_vals in CSR order); either may be None."""
+        self._check_vec(x, "x")
+        self._check_vec(grad_y, "grad_y")
+        gx = torch.empty_like(x) if want_x else None
+        gv = None
+        if want_vals:
+            shape = (self.nnz,) if self.batch == 1 else (self.batch, self.nnz)
+            gv = torch.empty(shape, dtype=self.dtype, device=self.device)
+        check(_lib.load().sla_spmv_backward(self._h, _ptr(x), _ptr(grad_y), _ptr(gx), _ptr(gv),
+                                            _stream(self.device)))
+        return gx, gv
+
+    def mv(self, x: torch.Tensor, values: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Differentiable y = A x: gradients flow to ``x`` and to ``values`` (the
+        input-order value tensor this handle was built or last set with, or
+        the one passed here, which is loaded into the handle)."""
+        vals = self._values_ref if values is None else values
+        return _MatvecFn.apply(self, vals, x)
+
     def solve_raw(self, b: torch.Tensor, tol: float = 1e-10, maxit: int = 10000,
                   out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, SolveInfo]:
         """x = A^{-1} b by Jacobi-PCG (no autograd). Returns (x, info)."""
@@ -293,3 +314,27 @@ class _SolveFn(torch.autograd.Function):
         _report(info, "adjoint solve")
         g_vals = A.gather_to_input(gv) if want_vals else None
         return None, g_vals, (gb if want_b else None), None, None, None
+
+
+class _MatvecFn(torch.autograd.Function):
+    """y = A x as one autograd node: backward is sla_spmv_backward."""
+
+    @staticmethod
+    def forward(ctx, A: SparseCSR, values: torch.Tensor, x: torch.Tensor):
+        if values is not None and values is not A._values_ref:
+            A.set_values(values.detach())
+        xd = x.detach().contiguous()
+        y = A.matvec(xd)
+        ctx.A = A
+        ctx.save_for_backward(xd)
+        return y
+
+    @staticmethod
+    def backward(ctx, grad_y: torch.Tensor):
+        (x,) = ctx.saved_tensors
+        A: SparseCSR = ctx.A
+        want_vals, want_x = ctx.needs_input_grad[1], ctx.needs_input_grad[2]
+        if not (want_vals or want_x):
+            return None, None, None
+        gx, gv = A.matvec_backward_raw(x, grad_y.contiguous(), want_x=want_x, want_vals=want_vals)
+        return None, (A.gather_to_input(gv) if want_vals else None), gx

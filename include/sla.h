@@ -178,6 +178,20 @@ sla_status sla_csr_set_option(sla_csr h, int32_t key, int64_t value);
  * products and sums in fp64 and round once. Asynchronous. */
 sla_status sla_spmv(sla_csr h, const void *x, void *y, void *stream);
 
+/* Backward of y = A x (.matvec under autograd; torch-sla counts matvec among
+ * the operations that carry gradients, tensor-types passage and Table 1) for
+ * an upstream gradient grad_y = dL/dy:
+ *   grad_x = A^T grad_y                          [batch][n], or NULL
+ *   grad_vals[b][k] = grad_y[b][row k] x[b][col k]   [batch][nnz], CSR order, or NULL
+ * x, grad_y: [batch][n]. grad_x must not alias x or grad_y. fp32 handles form
+ * products and sums in fp64. Asynchronous. A handle created with
+ * SLA_FLAG_CHECK_SYMMETRIC uses A itself for A^T; otherwise the first call
+ * builds A^T's pattern (host counting sort of the columns; allocates, once per
+ * handle) and later calls only refresh its values after sla_csr_set_values.
+ * grad_vals reaches input order through sla_csr_gather_to_input. */
+sla_status sla_spmv_backward(sla_csr h, const void *x, const void *grad_y, void *grad_x,
+                             void *grad_vals, void *stream);
+
 /*
  * Jacobi-preconditioned CG from x0 = 0 for every batch member (.solve):
  *   r = b, z = D^-1 r, p = z; per iteration q = A p, alpha = r.z / p.q,
