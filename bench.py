@@ -205,6 +205,20 @@ def main() -> int:
     e1.record(stream)
     torch.cuda.synchronize()
     b2b_ms = e0.elapsed_time(e1) / reps
+    # the matvec backward (A^T g and the value gradient), timed the same way;
+    # the first call builds A^T's pattern (on the host), outside the timed
+    # region; skipped for very large matrices, where that build takes minutes
+    bwd_ms = None
+    if w.nnz < (1 << 28):
+        gy = torch.ones_like(b)
+        A.matvec_backward_raw(b, gy)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(10):
+            A.matvec_backward_raw(b, gy)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = e0.elapsed_time(e1) / 10
 
     V = 8 if w.dtype == "f64" else 4
     R = 8 if A.row_index_dtype == torch.int64 else 4
@@ -289,6 +303,10 @@ def main() -> int:
             "spmv_ms": round(b2b_ms, 5),
             "spmv_gflops": round(2 * w.nnz * w.batch / (b2b_ms * 1e-3) / 1e9, 1),
             "spmv_gbps": round(ab["spmv"] / (b2b_ms * 1e-3) / 1e9, 1),
+            # matvec backward: A^T g (SpMV bytes) + grad_vals (gradient bytes)
+            "spmv_backward_ms": round(bwd_ms, 5) if bwd_ms else None,
+            "spmv_backward_gbps": (round((ab["spmv"] + ab["grad"]) / (bwd_ms * 1e-3) / 1e9, 1)
+                                   if bwd_ms else None),
             "kernel_avg_ms": {k: round(v[1] / max(v[0], 1), 5) for k, v in prof.items() if v[0]},
             "handle_bytes": A.memory_bytes(),
             "layout": layout,

@@ -5,7 +5,7 @@ HIP kernels for gfx950 (libsla.so, C ABI in include/sla.h); PyTorch supplies
 device memory and streams. See :class:`SparseCSR`.
 """
 from ._lib import SlaError, LIB_PATH  # noqa: F401
-from .sparse import SparseCSR, SolveInfo  # noqa: F401
+from .sparse import SparseCSR, SparseTensorList, SolveInfo  # noqa: F401
 from . import _lib  # noqa: F401
 
 
@@ -14,4 +14,4 @@ def solve(A: "SparseCSR", b, tol: float = 1e-10, maxit: int = 10000, values=None
     return A.solve(b, values=values, tol=tol, maxit=maxit)
 
 
-__all__ = ["SparseCSR", "SolveInfo", "SlaError", "solve"]
+__all__ = ["SparseCSR", "SparseTensorList", "SolveInfo", "SlaError", "solve"]

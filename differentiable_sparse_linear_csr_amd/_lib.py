@@ -35,7 +35,8 @@ SLA_OPT_FUSED_UPDATE = 5
 KERNELS = {"spmv_dot": 0, "update": 1, "direction": 2, "init": 3, "spmv": 4, "grad": 5,
            "cg_resident": 6}
 
-EXPORTS = ["sla_csr_create", "sla_csr_set_values", "sla_csr_get", "sla_csr_get_pattern",
+EXPORTS = ["sla_csr_create", "sla_csr_create_segmented", "sla_csr_get_segments",
+           "sla_csr_set_values", "sla_csr_get", "sla_csr_get_pattern",
            "sla_csr_get_values",
            "sla_csr_gather_to_input", "sla_csr_set_option", "sla_spmv", "sla_spmv_backward",
            "sla_pcg_solve",
@@ -72,6 +73,8 @@ def load() -> ctypes.CDLL:
     pi32 = ctypes.POINTER(ctypes.c_int32)
     pf64 = ctypes.POINTER(ctypes.c_double)
     L.sla_csr_create.argtypes = [pP, i32, i64, i64, i32, i32, P, i32, P, i32, P, u32, P]
+    L.sla_csr_create_segmented.argtypes = [pP, i32, i64, i64, i32, P, i32, P, i32, P, i32, P, u32, P]
+    L.sla_csr_get_segments.argtypes = [P, pi32, P]
     L.sla_csr_set_values.argtypes = [P, P, P]
     L.sla_csr_get.argtypes = [P, pi64, pi64, pi64, pi32, pi32, pi32, pP, pP, pP]
     L.sla_csr_get_pattern.argtypes = [P, P, P, P, P]

@@ -98,17 +98,17 @@ void alloc_workspace(Handle &h, hipStream_t s) {
     h.spart = (double *)dalloc(h, (size_t)kMaxGrid * sizeof(double));
     h.sync = (uint32_t *)dalloc(h, (size_t)kCntKinds * kCountersPerKind * sizeof(uint32_t));
     SLA_HIP(hipMemsetAsync(h.sync, 0, (size_t)kCntKinds * kCountersPerKind * sizeof(uint32_t), s));
-    h.st = (SysState *)dalloc(h, sizeof(SysState) * h.B);
+    h.st = (SysState *)dalloc(h, sizeof(SysState) * num_systems(h));
     h.ctl = (Ctl *)dalloc(h, sizeof(Ctl));
     SLA_HIP(hipMemsetAsync(h.ctl, 0, sizeof(Ctl), s));
     h.bcast = (Bcast *)dalloc(h, sizeof(Bcast));
     SLA_HIP(hipMemsetAsync(h.bcast, 0, sizeof(Bcast), s));
-    SLA_HIP(hipMemsetAsync(h.st, 0, sizeof(SysState) * h.B, s));
+    SLA_HIP(hipMemsetAsync(h.st, 0, sizeof(SysState) * num_systems(h), s));
     if (hipHostMalloc((void **)&h.h_running, sizeof(int32_t), hipHostMallocMapped) != hipSuccess)
         fail(SLA_ERR_OOM, "pinned host allocation failed");
     *h.h_running = 0;
     SLA_HIP(hipHostGetDevicePointer((void **)&h.d_running, h.h_running, 0));
-    if (hipHostMalloc((void **)&h.h_state, sizeof(SysState) * h.B, hipHostMallocDefault) !=
+    if (hipHostMalloc((void **)&h.h_state, sizeof(SysState) * num_systems(h), hipHostMallocDefault) !=
         hipSuccess)
         fail(SLA_ERR_OOM, "pinned host allocation failed");
     if (hipHostMalloc((void **)&h.h_ctl, sizeof(Ctl), hipHostMallocDefault) != hipSuccess)
@@ -135,12 +135,12 @@ Handle *checked(sla_csr h) {
 
 using namespace sla;
 
-extern "C" {
-
-sla_status sla_csr_create(sla_csr *out, sla_format fmt, int64_t n, int64_t nnz_in, int32_t batch,
-                          sla_itype row_itype, const void *rows_or_row_ptr, sla_itype col_itype,
-                          const void *cols, sla_dtype vtype, const void *values, uint32_t flags,
-                          void *stream) {
+namespace sla {
+namespace {
+sla_status create_impl(sla_csr *out, sla_format fmt, int64_t n, int64_t nnz_in, int32_t batch,
+                       sla_itype row_itype, const void *rows_or_row_ptr, sla_itype col_itype,
+                       const void *cols, sla_dtype vtype, const void *values, uint32_t flags,
+                       int32_t nseg, const int64_t *seg_rows, void *stream) {
     Handle *h = nullptr;
     const sla_status st = guard([&] {
         if (!out) fail(SLA_ERR_INVALID_ARG, "out is null");
@@ -162,6 +162,18 @@ sla_status sla_csr_create(sla_csr *out, sla_format fmt, int64_t n, int64_t nnz_i
             fail(SLA_ERR_INVALID_ARG, "null index or value pointer");
         if (fmt == SLA_INPUT_CSR && row_itype == SLA_I32 && nnz_in >= (int64_t(1) << 31))
             fail(SLA_ERR_INVALID_ARG, "int32 row_ptr cannot address nnz >= 2^31");
+        if (nseg > 0) {
+            if (!seg_rows) fail(SLA_ERR_INVALID_ARG, "seg_rows is null");
+            if (batch != 1) fail(SLA_ERR_INVALID_ARG, "a segmented handle has batch 1");
+            if (flags & SLA_FLAG_REORDER)
+                fail(SLA_ERR_INVALID_ARG, "a segmented handle is not reordered");
+            if (seg_rows[0] != 0 || seg_rows[nseg] != n)
+                fail(SLA_ERR_INVALID_ARG, "seg_rows must run from 0 to n");
+            for (int32_t q = 0; q < nseg; ++q)
+                if (seg_rows[q + 1] <= seg_rows[q])
+                    fail(SLA_ERR_INVALID_ARG, "segments must be non-empty and in order");
+            flags |= SLA_FLAG_NO_REORDER;
+        }
         hipStream_t s = (hipStream_t)stream;
         h = new Handle();
         SLA_HIP(hipGetDevice(&h->device));
@@ -178,6 +190,7 @@ sla_status sla_csr_create(sla_csr *out, sla_format fmt, int64_t n, int64_t nnz_i
         build_tiles(*h, s);
         init_launch_limits(*h);
         init_vector_limits(*h);
+        if (nseg > 0) build_segments(*h, seg_rows, nseg, s);
         alloc_workspace(*h, s);
         compute_dinv(*h, s);
         if ((flags & SLA_FLAG_CHECK_SYMMETRIC) && !check_symmetric(*h, s))
@@ -188,6 +201,41 @@ sla_status sla_csr_create(sla_csr *out, sla_format fmt, int64_t n, int64_t nnz_i
     });
     if (st != SLA_OK && h) destroy(h);
     return st;
+}
+}  // namespace
+}  // namespace sla
+
+extern "C" {
+
+sla_status sla_csr_create(sla_csr *out, sla_format fmt, int64_t n, int64_t nnz_in, int32_t batch,
+                          sla_itype row_itype, const void *rows_or_row_ptr, sla_itype col_itype,
+                          const void *cols, sla_dtype vtype, const void *values, uint32_t flags,
+                          void *stream) {
+    return create_impl(out, fmt, n, nnz_in, batch, row_itype, rows_or_row_ptr, col_itype, cols,
+                       vtype, values, flags, 0, nullptr, stream);
+}
+
+sla_status sla_csr_create_segmented(sla_csr *out, sla_format fmt, int64_t n, int64_t nnz_in,
+                                    sla_itype row_itype, const void *rows_or_row_ptr,
+                                    sla_itype col_itype, const void *cols, sla_dtype vtype,
+                                    const void *values, int32_t nseg, const int64_t *seg_rows,
+                                    uint32_t flags, void *stream) {
+    if (nseg < 1) {
+        g_last_error = "nseg must be >= 1";
+        return SLA_ERR_INVALID_ARG;
+    }
+    return create_impl(out, fmt, n, nnz_in, 1, row_itype, rows_or_row_ptr, col_itype, cols, vtype,
+                       values, flags, nseg, seg_rows, stream);
+}
+
+sla_status sla_csr_get_segments(sla_csr hd, int32_t *nseg, int64_t *seg_rows) {
+    return guard([&] {
+        Handle *h = checked(hd);
+        if (nseg) *nseg = h->nseg;
+        if (seg_rows && h->nseg > 0)
+            SLA_HIP(hipMemcpy(seg_rows, h->seg_rows, sizeof(int64_t) * ((size_t)h->nseg + 1),
+                              hipMemcpyDeviceToHost));
+    });
 }
 
 sla_status sla_csr_set_values(sla_csr hd, const void *values, void *stream) {

@@ -181,6 +181,15 @@ struct Handle {
     void *rtmp[2] = {nullptr, nullptr};  // [B][n] vectors in the inner order
     void *rtmp_grad = nullptr;    // [B][nnz] value gradient in the inner order
     int64_t wide_tiles = 0;       // tiles whose columns span 2^16 or more
+    // segmented handle: a block-diagonal matrix of nseg independent systems
+    // (distinct patterns) solved together, each with its own scalars and test
+    int32_t nseg = 0;
+    int64_t *seg_rows = nullptr;  // [nseg+1] first row of each segment
+    int32_t *blk_seg = nullptr;   // [seg_grid] segment of each workgroup of the vector kernels
+    int64_t *seg_blk0 = nullptr;  // [nseg+1] first workgroup of each segment
+    int64_t seg_grid = 0;
+    uint32_t *seg_sync = nullptr; // [nseg] arrival counters (one line each)
+    double *seg_part = nullptr;   // [2 * seg_grid] workgroup partials
     // A^T for the backward of y = A x (built at the first backward)
     Handle *tr = nullptr;
     int64_t *tr_map = nullptr;    // [nnz]: A^T CSR position -> this CSR position
@@ -246,6 +255,10 @@ Handle *make_child(Handle &h, const std::vector<int64_t> &rp, const std::vector<
 void child_values(Handle &h, Handle &child, const int64_t *map, hipStream_t s);
 void any_spmv(Handle &h, const void *x, void *y, hipStream_t s);
 Handle *transpose_for_backward(Handle &h, hipStream_t s);
+// segmented handles (seg.hip)
+void build_segments(Handle &h, const int64_t *seg_rows, int32_t nseg, hipStream_t s);
+void launch_spmv_plain(Handle &h, const void *x, void *y, hipStream_t s);
+inline int32_t num_systems(const Handle &h) { return h.nseg > 0 ? h.nseg : h.B; }
 int64_t resident_workgroups(const void *kernel, int device);
 void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit, sla_info *info,
          hipStream_t s, bool keep_internal_solution);
@@ -256,6 +269,31 @@ void grad_vals(Handle &h, const void *a_internal, const void *x_user, void *grad
 bool resident_ready(Handle &h, hipStream_t s);   // builds the plan on first use
 void resident_solve(Handle &h, const void *b, double tol, int32_t maxit, hipStream_t s);
 void flush_profile(Handle &h);
+
+// hipEvents around kernel launches of a call (profiling on)
+struct Launcher {
+    Handle &h;
+    hipStream_t s;
+    bool prof;
+    void begin(int kind, hipEvent_t *a) {
+        (void)kind;
+        if (prof) {
+            SLA_HIP(hipEventCreate(a));
+            SLA_HIP(hipEventRecord(*a, s));
+        }
+    }
+    void end(int kind, hipEvent_t a) {
+        if (prof) {
+            hipEvent_t b;
+            SLA_HIP(hipEventCreate(&b));
+            SLA_HIP(hipEventRecord(b, s));
+            h.pending.push_back({kind, a, b});
+        }
+    }
+};
+
+void seg_init(Handle &h, const void *b, hipStream_t s, Launcher *lp);
+void seg_iter_kernels(Handle &h, hipStream_t s, Launcher *lp);
 
 // ------------------------------------------------------------------ device helpers
 

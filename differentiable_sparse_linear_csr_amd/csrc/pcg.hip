@@ -649,7 +649,7 @@ __global__ __launch_bounds__(kBlock) void k_direction1(int64_t n, const T *__res
 // grid of the fused update + direction: one pass per workgroup, all of them
 // resident at once; 0 when the system does not fit (or B > 1)
 int64_t fused_grid(const Handle &h, int W) {
-    if (h.B != 1 || !h.fuse_update || h.upd_dir_resident <= 0) return 0;
+    if (h.B != 1 || h.nseg > 0 || !h.fuse_update || h.upd_dir_resident <= 0) return 0;
     const int64_t per = (int64_t)kBlock * kFusedGroups;
     int64_t g = (h.n / W + per - 1) / per;
     if (g < 1) g = 1;
@@ -742,26 +742,6 @@ __global__ __launch_bounds__(kBlock) void k_grad_long(const int32_t *__restrict_
     }
 }
 
-struct Launcher {
-    Handle &h;
-    hipStream_t s;
-    bool prof;
-    void begin(int kind, hipEvent_t *a) {
-        (void)kind;
-        if (prof) {
-            SLA_HIP(hipEventCreate(a));
-            SLA_HIP(hipEventRecord(*a, s));
-        }
-    }
-    void end(int kind, hipEvent_t a) {
-        if (prof) {
-            hipEvent_t b;
-            SLA_HIP(hipEventCreate(&b));
-            SLA_HIP(hipEventRecord(b, s));
-            h.pending.push_back({kind, a, b});
-        }
-    }
-};
 
 template <typename T>
 void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
@@ -822,6 +802,10 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
 }
 
 void iter_kernels(Handle &h, hipStream_t s, Launcher *lp) {
+    if (h.nseg > 0) {
+        seg_iter_kernels(h, s, lp);
+        return;
+    }
     if (h.vt == SLA_F64) iter_kernels_t<double>(h, s, lp);
     else iter_kernels_t<float>(h, s, lp);
 }
@@ -929,7 +913,7 @@ void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit,
     h.h_ctl->epoch = ++h.epoch;
     h.h_ctl->error = 0;
     SLA_HIP(hipMemcpyAsync(h.ctl, h.h_ctl, sizeof(Ctl), hipMemcpyHostToDevice, s));
-    if (h.B == 1 && resident_ready(h, s)) {
+    if (h.B == 1 && h.nseg == 0 && resident_ready(h, s)) {
         // the whole solve in one cooperative kernel (same recurrence)
         resident_solve(h, b_user, tol, maxit, s);
         if (!keep_internal_solution)
@@ -950,7 +934,8 @@ void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit,
         transpose(b_user, h.q, h.B, h.n, h.vbytes, s);  // q is free until the first SpMV
         b_int = h.q;
     }
-    if (h.vt == SLA_F64) init_t<double>(h, b_int, s, lp);
+    if (h.nseg > 0) seg_init(h, b_int, s, lp);
+    else if (h.vt == SLA_F64) init_t<double>(h, b_int, s, lp);
     else init_t<float>(h, b_int, s, lp);
 
     const bool graph = h.use_graph && !h.profile;
@@ -976,13 +961,14 @@ void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit,
         else
             transpose(h.x, x_user, h.n, h.B, h.vbytes, s);
     }
-    SLA_HIP(hipMemcpyAsync(h.h_state, h.st, sizeof(SysState) * h.B, hipMemcpyDeviceToHost, s));
+    const int32_t nsys = num_systems(h);
+    SLA_HIP(hipMemcpyAsync(h.h_state, h.st, sizeof(SysState) * nsys, hipMemcpyDeviceToHost, s));
     SLA_HIP(hipMemcpyAsync(h.h_ctl, h.ctl, sizeof(Ctl), hipMemcpyDeviceToHost, s));
     SLA_HIP(hipStreamSynchronize(s));
     if (h.profile) flush_profile(h);
     if (h.h_ctl->error)
         fail(SLA_ERR_HIP, "fused update: a grid-wide wait timed out (workgroups not co-resident)");
-    for (int b = 0; b < h.B; ++b) {
+    for (int b = 0; b < nsys; ++b) {
         const SysState &st = h.h_state[b];
         info[b].iterations = st.iter;
         info[b].status = st.status == kRunning ? SLA_MAXIT : st.status;

@@ -445,7 +445,7 @@ bool resident_ready(Handle &h, hipStream_t s) {
     if (h.res_mode == 1 && h.n > kResidentAutoRows) return false;
     if (h.res_state != 0) return h.res_state > 0;
     h.res_state = -1;
-    if (h.B != 1 || h.nlong != 0) return false;
+    if (h.B != 1 || h.nlong != 0 || h.nseg > 0) return false;
     int coop = 0, cus = 0, per_cu = 0;
     SLA_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, h.device));
     SLA_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h.device));

@@ -71,6 +71,10 @@ class SparseCSR:
                             ctypes.byref(rp), ctypes.byref(ci), ctypes.byref(sl)))
         self.n, self.nnz, self.nnz_in, self.batch = n.value, nnz.value, nnz_in.value, batch.value
         self.row_index_dtype = torch.int64 if rit.value == _lib.SLA_I64 else torch.int32
+        nseg = ctypes.c_int32()
+        check(L.sla_csr_get_segments(self._h, ctypes.byref(nseg), None))
+        self.nseg = nseg.value
+        self.nsys = self.nseg if self.nseg > 0 else self.batch   # entries of a solve's info
         self._values_ref: Optional[torch.Tensor] = None
         self.last_info: Optional[SolveInfo] = None
         self.last_adjoint_info: Optional[SolveInfo] = None
@@ -235,7 +239,7 @@ class SparseCSR:
         """x = A^{-1} b by Jacobi-PCG (no autograd). Returns (x, info)."""
         self._check_vec(b, "b")
         x = torch.empty_like(b) if out is None else out
-        infos = (Info * self.batch)()
+        infos = (Info * self.nsys)()
         check(_lib.load().sla_pcg_solve(self._h, _ptr(b), _ptr(x), float(tol), int(maxit), infos,
                                         _stream(self.device)))
         info = SolveInfo(list(infos))
@@ -252,7 +256,7 @@ class SparseCSR:
         if want_vals:
             shape = (self.nnz,) if self.batch == 1 else (self.batch, self.nnz)
             gv = torch.empty(shape, dtype=self.dtype, device=self.device)
-        infos = (Info * self.batch)()
+        infos = (Info * self.nsys)()
         check(_lib.load().sla_adjoint_backward(self._h, _ptr(x), _ptr(grad_x), _ptr(gb), _ptr(gv),
                                                float(tol), int(maxit), infos,
                                                _stream(self.device)))
@@ -338,3 +342,61 @@ class _MatvecFn(torch.autograd.Function):
             return None, None, None
         gx, gv = A.matvec_backward_raw(x, grad_y.contiguous(), want_x=want_x, want_vals=want_vals)
         return None, (A.gather_to_input(gv) if want_vals else None), gx
+
+
+class SparseTensorList(SparseCSR):
+    """Independent systems with distinct patterns solved together: one
+    block-diagonal handle whose segments each run their own Jacobi-PCG.
+
+    Build with :meth:`from_coo_list`. Vectors are either the concatenation of
+    the members' vectors ([sum n_q]) or lists of per-member tensors (``split``
+    and ``cat`` convert); ``solve`` takes and returns lists."""
+
+    @classmethod
+    def from_coo_list(cls, rows: List[torch.Tensor], cols: List[torch.Tensor],
+                      values: List[torch.Tensor], sizes: List[int],
+                      check_symmetric: bool = False) -> "SparseTensorList":
+        if not (len(rows) == len(cols) == len(values) == len(sizes)) or not sizes:
+            raise ValueError("rows, cols, values and sizes must be non-empty lists of one length")
+        offs = [0]
+        for n in sizes:
+            offs.append(offs[-1] + int(n))
+        # argument marshalling: member indices shifted to their diagonal block
+        r = torch.cat([ri.to(torch.int64) + o for ri, o in zip(rows, offs)])
+        c = torch.cat([ci.to(torch.int64) + o for ci, o in zip(cols, offs)])
+        v = torch.cat(list(values))
+        for t, w in ((r, "rows"), (c, "cols"), (v, "values")):
+            _need_cuda(t, w)
+        L = _lib.load()
+        h = ctypes.c_void_p()
+        seg = (ctypes.c_int64 * (len(sizes) + 1))(*offs)
+        flags = _lib.SLA_FLAG_CHECK_SYMMETRIC if check_symmetric else 0
+        with torch.cuda.device(v.device):
+            check(L.sla_csr_create_segmented(ctypes.byref(h), _lib.SLA_INPUT_COO, offs[-1],
+                                             r.shape[0], _lib.SLA_I64, _ptr(r), _lib.SLA_I64,
+                                             _ptr(c), _VT[v.dtype], _ptr(v), len(sizes), seg,
+                                             flags, _stream(v.device)))
+        obj = cls(h, v.device, v.dtype)
+        obj._values_ref = v
+        obj.sizes = [int(n) for n in sizes]
+        obj.offsets = offs
+        obj.nnz_sizes = [int(t.shape[0]) for t in values]
+        return obj
+
+    def split(self, v: torch.Tensor) -> List[torch.Tensor]:
+        return list(torch.split(v, self.sizes))
+
+    def cat(self, vs: List[torch.Tensor]) -> torch.Tensor:
+        return torch.cat(list(vs))
+
+    def split_values(self, v: torch.Tensor) -> List[torch.Tensor]:
+        """an input-order value tensor ([sum nnz_q]) -> per-member tensors"""
+        return list(torch.split(v, self.nnz_sizes))
+
+    def solve(self, b, values=None, tol: float = 1e-10, maxit: int = 10000,
+              adjoint_tol: Optional[float] = None):
+        """Differentiable solves of every member: b (list or concatenation) ->
+        list of x_q. Gradients flow to b and to the concatenated values."""
+        bc = self.cat(b) if isinstance(b, (list, tuple)) else b
+        x = super().solve(bc, values=values, tol=tol, maxit=maxit, adjoint_tol=adjoint_tol)
+        return self.split(x)

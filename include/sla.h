@@ -142,6 +142,30 @@ sla_status sla_csr_create(sla_csr *out, sla_format fmt, int64_t n, int64_t nnz_i
                           sla_itype col_itype, const void *cols,
                           sla_dtype vtype, const void *values, uint32_t flags, void *stream);
 
+/*
+ * A list of independent systems with distinct patterns solved together
+ * (torch-sla's SparseTensorList: matrices of different patterns batched, the
+ * tensor-types passage), held as one block-diagonal matrix. The caller passes
+ * that matrix exactly as to sla_csr_create (batch 1; indices already offset
+ * so that system q owns rows and columns [seg_rows[q], seg_rows[q+1])) and
+ * seg_rows: host [nseg+1], seg_rows[0] = 0, strictly increasing,
+ * seg_rows[nseg] = n. An entry outside its row's diagonal block gives
+ * SLA_ERR_INDEX_RANGE. sla_spmv multiplies the whole block-diagonal matrix;
+ * sla_pcg_solve and sla_adjoint_backward run every system's own Jacobi-PCG
+ * (its own step sizes, stopping test and iteration count, as if solved alone)
+ * and fill info[0..nseg). SLA_FLAG_REORDER is rejected (segments are never
+ * reordered); the single-kernel solve and the fused update do not apply.
+ */
+sla_status sla_csr_create_segmented(sla_csr *out, sla_format fmt, int64_t n, int64_t nnz_in,
+                                    sla_itype row_itype, const void *rows_or_row_ptr,
+                                    sla_itype col_itype, const void *cols, sla_dtype vtype,
+                                    const void *values, int32_t nseg, const int64_t *seg_rows,
+                                    uint32_t flags, void *stream);
+
+/* Segments of a handle (host outputs): *nseg = 0 for an unsegmented handle;
+ * seg_rows (host [nseg+1], may be NULL) receives the row boundaries. */
+sla_status sla_csr_get_segments(sla_csr h, int32_t *nseg, int64_t *seg_rows);
+
 /* Replace the values (same pattern, same input order and count as at create):
  * values [batch][nnz_in] of the handle's vtype. Duplicate positions are merged
  * exactly as at create. Synchronizes `stream`. */
@@ -198,7 +222,8 @@ sla_status sla_spmv_backward(sla_csr h, const void *x, const void *grad_y, void 
  *   x += alpha p, r -= alpha q, stop when ||r|| <= tol ||b||, else
  *   beta = r'.z' / r.z, p = z' + beta p.
  * Each system stops on its own test; p.q <= 0 or non-finite ends it with
- * SLA_BREAKDOWN (A not SPD). b, x: [batch][n]; info: host [batch].
+ * SLA_BREAKDOWN (A not SPD). b, x: [batch][n]; info: host [batch] ([nseg] for a
+ * segmented handle).
  * maxit >= 0, tol >= 0 (tol = 0 runs exactly maxit iterations).
  * Returns SLA_ERR_BAD_DIAGONAL if some d_i is missing, <= 0 or not finite.
  * fp32 handles store vectors in fp32 and compute in fp64.
