@@ -383,6 +383,32 @@ class SparseTensorList(SparseCSR):
         obj.nnz_sizes = [int(t.shape[0]) for t in values]
         return obj
 
+    @classmethod
+    def from_block_diagonal_coo(cls, rows: torch.Tensor, cols: torch.Tensor,
+                                values: torch.Tensor, seg_rows: List[int],
+                                check_symmetric: bool = False) -> "SparseTensorList":
+        """COO triples of the block-diagonal matrix itself (indices already
+        offset) and the segment row boundaries [0, ..., n]."""
+        for t, w in ((rows, "rows"), (cols, "cols"), (values, "values")):
+            _need_cuda(t, w)
+        L = _lib.load()
+        h = ctypes.c_void_p()
+        nseg = len(seg_rows) - 1
+        seg = (ctypes.c_int64 * (nseg + 1))(*[int(v) for v in seg_rows])
+        flags = _lib.SLA_FLAG_CHECK_SYMMETRIC if check_symmetric else 0
+        with torch.cuda.device(values.device):
+            check(L.sla_csr_create_segmented(ctypes.byref(h), _lib.SLA_INPUT_COO, int(seg_rows[-1]),
+                                             rows.shape[0], _IT[rows.dtype], _ptr(rows),
+                                             _IT[cols.dtype], _ptr(cols), _VT[values.dtype],
+                                             _ptr(values), nseg, seg, flags,
+                                             _stream(values.device)))
+        obj = cls(h, values.device, values.dtype)
+        obj._values_ref = values
+        obj.offsets = [int(v) for v in seg_rows]
+        obj.sizes = [obj.offsets[q + 1] - obj.offsets[q] for q in range(nseg)]
+        obj.nnz_sizes = None
+        return obj
+
     def split(self, v: torch.Tensor) -> List[torch.Tensor]:
         return list(torch.split(v, self.sizes))
 

@@ -230,6 +230,7 @@ WORKLOADS = {
     "batched_diffusion2d_512x32": (3000, 512),
     "knn_laplacian_2m": (4000, 2_000_000),
     "poisson2d_11548": (5000, 11548),
+    "list_diffusion2d_16": (6000, 16),
 }
 
 
@@ -287,6 +288,30 @@ def make_workload(name: str, size: Optional[int] = None, batch: Optional[int] = 
         return Workload(name, f"16-NN Gaussian graph Laplacian + 0.01 I, {n} points, fp64", n, 1,
                         "f64", "coo", rows, None, cols, vals, normal_vector(s + 1, n),
                         normal_vector(s + 2, n), 1e-8, 20000, True, {"h": h})
+
+    if name == "list_diffusion2d_16":
+        # a list of systems with distinct patterns (SparseTensorList): member q
+        # is 2D 5-point diffusion on a (128 + 16 q)^2 grid (scaled down with
+        # size: grids 8 (size + 2 q)), face coefficients log-uniform in
+        # [0.1, 10]; returned as one block-diagonal COO with its segment rows
+        M = N
+        grids = [128 + 16 * q for q in range(M)] if size is None else [8 * (2 + q) for q in range(M)]
+        rng = np.random.default_rng(s + 3)
+        rs, cs, vs, seg = [], [], [], [0]
+        for G in grids:
+            cx = _log_uniform(rng, -1, 1, (G, G + 1))
+            cy = _log_uniform(rng, -1, 1, (G + 1, G))
+            r, c, v = diffusion2d_coo(G, cx, cy)
+            rs.append(r.astype(np.int64) + seg[-1])
+            cs.append(c.astype(np.int64) + seg[-1])
+            vs.append(v)
+            seg.append(seg[-1] + G * G)
+        n = seg[-1]
+        return Workload(name, f"list of {M} 2D 5-point diffusion grids {grids[0]}^2..{grids[-1]}^2 "
+                        "(distinct patterns, one block-diagonal handle), fp64", n, 1, "f64", "coo",
+                        np.concatenate(rs), None, np.concatenate(cs), np.concatenate(vs),
+                        normal_vector(s + 1, n), normal_vector(s + 2, n), 1e-8, 20000, True,
+                        {"seg_rows": seg, "grids": grids})
 
     # poisson2d_11548: CSR input, int64 row pointer, fixed iteration budget
     row_ptr, cols, vals = poisson2d_csr(N)
