@@ -59,9 +59,13 @@ def lib() -> ctypes.CDLL:
         L.orc_pcg_f32.argtypes = [i64, P, P, P, P, f64, i32, P, P, P, P]
         L.orc_pcg_batched.argtypes = [i64, i32, P, P, i32, P, P, f64, i32, P, P, P, P]
         L.orc_adjoint.argtypes = [i64, i32, P, P, i32, P, P, P, f64, i32, P, P, P, P, P]
+        L.orc_bicgstab_f64.argtypes = [i64, P, P, P, P, f64, i32, P, P, P, P]
+        L.orc_bicgstab_f32.argtypes = [i64, P, P, P, P, f64, i32, P, P, P, P]
+        L.orc_bicgstab_adjoint.argtypes = [i64, P, P, i32, P, P, P, f64, i32, P, P, P, P, P]
         for name in ("orc_coo_to_csr", "orc_check_csr", "orc_is_symmetric_f64", "orc_jacobi_f64",
                      "orc_jacobi_f32", "orc_pcg_f64", "orc_pcg_f32", "orc_pcg_batched", "orc_adjoint",
-                     "orc_spmv_backward_f32"):
+                     "orc_spmv_backward_f32", "orc_bicgstab_f64", "orc_bicgstab_f32",
+                     "orc_bicgstab_adjoint"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -239,3 +243,37 @@ def adjoint(row_ptr, col, val, x, g, tol: float, maxit: int):
     if batched:
         return lam, grad, iters, rel, outc
     return lam[0], grad[0], int(iters[0]), float(rel[0]), int(outc[0])
+
+
+def bicgstab(row_ptr, col, val, b, tol: float, maxit: int):
+    """Jacobi-preconditioned BiCGStab for a general (non-symmetric) system.
+    Returns (x, iterations, rel_residual, outcome)."""
+    row_ptr, col = _i64(row_ptr), _i64(col)
+    val = _vals(val)
+    b = _vals(b, val.dtype)
+    n = row_ptr.shape[0] - 1
+    x = np.empty(n, val.dtype)
+    it, outc = ctypes.c_int32(0), ctypes.c_int32(0)
+    rel = ctypes.c_double(0.0)
+    fn = lib().orc_bicgstab_f32 if val.dtype == np.float32 else lib().orc_bicgstab_f64
+    _check(fn(n, _p(row_ptr), _p(col), _p(val), _p(b), float(tol), int(maxit), _p(x),
+              ctypes.byref(it), ctypes.byref(rel), ctypes.byref(outc)), "bicgstab")
+    return x, it.value, rel.value, outc.value
+
+
+def bicgstab_adjoint(row_ptr, col, val, x, g, tol: float, maxit: int):
+    """Backward of x = A^{-1} b solved by BiCGStab, for upstream g: returns
+    (lambda = dL/db, grad_vals [CSR order], iterations, rel_residual, outcome)."""
+    row_ptr, col = _i64(row_ptr), _i64(col)
+    val = _vals(val)
+    x, g = _vals(x, val.dtype), _vals(g, val.dtype)
+    n = row_ptr.shape[0] - 1
+    lam = np.empty(n, val.dtype)
+    grad = np.empty(max(col.shape[0], 1), val.dtype)
+    it, outc = ctypes.c_int32(0), ctypes.c_int32(0)
+    rel = ctypes.c_double(0.0)
+    _check(lib().orc_bicgstab_adjoint(n, _p(row_ptr), _p(col), val.dtype.itemsize, _p(val), _p(x),
+                                      _p(g), float(tol), int(maxit), _p(lam), _p(grad),
+                                      ctypes.byref(it), ctypes.byref(rel), ctypes.byref(outc)),
+           "bicgstab_adjoint")
+    return lam, grad[:col.shape[0]], it.value, rel.value, outc.value

@@ -20,9 +20,12 @@
  *    preconditioning (backend list; Table 3 and Table 4 text);
  *  - backward solves A^T lambda = dL/dx and assembles matrix gradients
  *    -lambda_i x_j on the stored entries (adjoint paragraph of the distributed
- *    section, referring to the adjoint derivation of Section 3.2).
+ *    section, referring to the adjoint derivation of Section 3.2);
+ *  - the same backend also solves general systems by BiCGStab (backend list),
+ *    which the distributed section says follows the CG template.
  * The pages print no PCG recurrence; the textbook preconditioned CG
- * (Hestenes-Stiefel with M = diag(A), x0 = 0) is used. Readings of the places
+ * (Hestenes-Stiefel with M = diag(A), x0 = 0) is used, and for BiCGStab van
+ * der Vorst's preconditioned recurrence. Readings of the places
  * where the pages are silent are stated at each function.
  */
 #include <math.h>
@@ -518,4 +521,268 @@ int orc_adjoint(int64_t n, int32_t batch, const int64_t *row_ptr, const int64_t 
         }
     }
     return err;
+}
+
+/* ------------------------------------------------------------------ BiCGStab
+ * torch-sla's pytorch-native backend also offers BiCGStab for general
+ * (non-symmetric) systems (backend list of the API section; the distributed
+ * section notes that BiCGStab follows the CG template with more inner
+ * products). The pages print no recurrence; the one used is van der Vorst's
+ * preconditioned BiCGStab (SIAM J. Sci. Stat. Comput. 13, 1992; the
+ * "Templates" book's preconditioned form), with the Jacobi preconditioner
+ * M = diag(A) applied on the right, x0 = 0 and shadow residual r^ = b:
+ *   r = b, rho = r^.r
+ *   each iteration k = 1..maxit:
+ *     p = r                         (k = 1)
+ *     p = r + beta (p - omega v)    (k > 1)
+ *     p^ = M^-1 p; v = A p^; sigma = r^.v       breakdown: sigma = 0
+ *     alpha = rho / sigma; s = r - alpha v
+ *     ||s|| <= tol ||b||: x += alpha p^, r = s, converged (half step)
+ *     s^ = M^-1 s; t = A s^; omega = t.s / t.t  breakdown: t.t = 0 or omega = 0
+ *     x += alpha p^ + omega s^; r = s - omega t
+ *     ||r|| <= tol ||b||: converged; k = maxit: budget spent
+ *     rho' = r^.r                               breakdown: rho' = 0
+ *     beta = (rho'/rho)(alpha/omega); rho = rho'
+ * Readings (the pages fix none of these): breakdown is an exact zero or a
+ * non-finite value of the quantity named; a breakdown at sigma (or a
+ * non-finite ||s||) leaves x and r as they were; one at omega keeps the half
+ * step (x += alpha p^, r = s), which is a valid iterate; iterations count the
+ * loop passes started, including the one that stopped. b = 0 returns x = 0
+ * after 0 iterations. rel_res is ||r||/||b|| of the last residual formed (s
+ * after a half step). Jacobi here needs a present, non-zero, finite diagonal
+ * of either sign. x += alpha p^ + omega s^ is formed as (x + alpha p^) +
+ * omega s^. */
+static int jacobi_nonzero_f64(int64_t n, const int64_t *row_ptr, const int64_t *col,
+                              const double *val, double *dinv) {
+    for (int64_t i = 0; i < n; ++i) {
+        int found = 0;
+        double d = 0.0;
+        for (int64_t k = row_ptr[i]; k < row_ptr[i + 1]; ++k)
+            if (col[k] == i) { d = val[k]; found = 1; }
+        if (!found || d == 0.0 || !isfinite(d)) return ORC_ERR_BAD_DIAGONAL;
+        dinv[i] = 1.0 / d;
+    }
+    return ORC_OK;
+}
+
+static int jacobi_nonzero_f32(int64_t n, const int64_t *row_ptr, const int64_t *col,
+                              const float *val, float *dinv) {
+    for (int64_t i = 0; i < n; ++i) {
+        int found = 0;
+        float d = 0.0f;
+        for (int64_t k = row_ptr[i]; k < row_ptr[i + 1]; ++k)
+            if (col[k] == i) { d = val[k]; found = 1; }
+        if (!found || d == 0.0f || !isfinite(d)) return ORC_ERR_BAD_DIAGONAL;
+        dinv[i] = (float)(1.0 / (double)d);
+    }
+    return ORC_OK;
+}
+
+int orc_bicgstab_f64(int64_t n, const int64_t *row_ptr, const int64_t *col, const double *val,
+                     const double *b, double tol, int32_t maxit, double *x, int32_t *iters,
+                     double *rel_res, int32_t *outcome) {
+    if (n < 1 || maxit < 0) return ORC_ERR_INVALID_ARG;
+    double *w[9];
+    int st = ORC_OK;
+    for (int j = 0; j < 9; ++j) {
+        w[j] = (double *)malloc((size_t)n * sizeof(double));
+        if (!w[j]) st = ORC_ERR_OOM;
+    }
+    double *dinv = w[0], *r = w[1], *rh = w[2], *p = w[3], *ph = w[4], *v = w[5], *s = w[6],
+           *sh = w[7], *t = w[8];
+    if (st == ORC_OK) st = jacobi_nonzero_f64(n, row_ptr, col, val, dinv);
+    if (st != ORC_OK) {
+        for (int j = 0; j < 9; ++j) free(w[j]);
+        return st;
+    }
+    for (int64_t i = 0; i < n; ++i) { x[i] = 0.0; r[i] = b[i]; rh[i] = b[i]; }
+    double bb = dot_f64(n, b, b);
+    double rr = bb, rho = bb, alpha = 0.0, omega = 0.0, beta = 0.0;
+    *iters = 0; *rel_res = 0.0; *outcome = ORC_CONVERGED;
+    if (bb == 0.0) goto done;
+    *outcome = ORC_MAXIT;
+    *iters = maxit;
+    for (int32_t k = 1; k <= maxit; ++k) {
+        if (k == 1)
+            for (int64_t i = 0; i < n; ++i) p[i] = r[i];
+        else
+#pragma omp parallel for schedule(static)
+            for (int64_t i = 0; i < n; ++i) p[i] = r[i] + beta * (p[i] - omega * v[i]);
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < n; ++i) ph[i] = dinv[i] * p[i];
+        orc_spmv_f64(n, row_ptr, col, val, ph, v);
+        double sigma = dot_f64(n, rh, v);
+        if (sigma == 0.0 || !isfinite(sigma)) { *outcome = ORC_BREAKDOWN; *iters = k; break; }
+        alpha = rho / sigma;
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < n; ++i) s[i] = r[i] - alpha * v[i];
+        double ss = dot_f64(n, s, s);
+        if (!isfinite(ss)) { *outcome = ORC_BREAKDOWN; *iters = k; break; }
+        if (sqrt(ss) <= tol * sqrt(bb)) {
+            for (int64_t i = 0; i < n; ++i) { x[i] = x[i] + alpha * ph[i]; r[i] = s[i]; }
+            rr = ss;
+            *outcome = ORC_CONVERGED; *iters = k;
+            break;
+        }
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < n; ++i) sh[i] = dinv[i] * s[i];
+        orc_spmv_f64(n, row_ptr, col, val, sh, t);
+        double tt = dot_f64(n, t, t), ts = dot_f64(n, t, s);
+        omega = tt == 0.0 ? 0.0 : ts / tt;
+        if (tt == 0.0 || !isfinite(tt) || !isfinite(omega) || omega == 0.0) {
+            for (int64_t i = 0; i < n; ++i) { x[i] = x[i] + alpha * ph[i]; r[i] = s[i]; }
+            rr = ss;
+            *outcome = ORC_BREAKDOWN; *iters = k;
+            break;
+        }
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < n; ++i) {
+            x[i] = (x[i] + alpha * ph[i]) + omega * sh[i];
+            r[i] = s[i] - omega * t[i];
+        }
+        rr = dot_f64(n, r, r);
+        if (sqrt(rr) <= tol * sqrt(bb)) { *outcome = ORC_CONVERGED; *iters = k; break; }
+        if (!isfinite(rr)) { *outcome = ORC_BREAKDOWN; *iters = k; break; }
+        if (k == maxit) break;
+        double rho_new = dot_f64(n, rh, r);
+        if (rho_new == 0.0 || !isfinite(rho_new)) { *outcome = ORC_BREAKDOWN; *iters = k; break; }
+        beta = (rho_new / rho) * (alpha / omega);
+        rho = rho_new;
+    }
+    *rel_res = sqrt(rr / bb);
+done:
+    for (int j = 0; j < 9; ++j) free(w[j]);
+    return ORC_OK;
+}
+
+/* fp32 storage, fp64 arithmetic (as for PCG): every stored vector (x, r, p,
+ * p^, v, s, s^, t) and dinv is float, each element formed in double from the
+ * stored floats and rounded once on store; inner products accumulate in
+ * double over the stored floats; r^ is b itself. */
+static double dot_f32(int64_t n, const float *a, const float *b) {
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i) s = s + (double)a[i] * (double)b[i];
+    return s;
+}
+
+int orc_bicgstab_f32(int64_t n, const int64_t *row_ptr, const int64_t *col, const float *val,
+                     const float *b, double tol, int32_t maxit, float *x, int32_t *iters,
+                     double *rel_res, int32_t *outcome) {
+    if (n < 1 || maxit < 0) return ORC_ERR_INVALID_ARG;
+    float *w[8];
+    int st = ORC_OK;
+    for (int j = 0; j < 8; ++j) {
+        w[j] = (float *)malloc((size_t)n * sizeof(float));
+        if (!w[j]) st = ORC_ERR_OOM;
+    }
+    float *dinv = w[0], *r = w[1], *p = w[2], *ph = w[3], *v = w[4], *s = w[5], *sh = w[6],
+          *t = w[7];
+    const float *rh = b;
+    if (st == ORC_OK) st = jacobi_nonzero_f32(n, row_ptr, col, val, dinv);
+    if (st != ORC_OK) {
+        for (int j = 0; j < 8; ++j) free(w[j]);
+        return st;
+    }
+    for (int64_t i = 0; i < n; ++i) { x[i] = 0.0f; r[i] = b[i]; }
+    double bb = dot_f32(n, b, b);
+    double rr = bb, rho = bb, alpha = 0.0, omega = 0.0, beta = 0.0;
+    *iters = 0; *rel_res = 0.0; *outcome = ORC_CONVERGED;
+    if (bb == 0.0) goto done32;
+    *outcome = ORC_MAXIT;
+    *iters = maxit;
+    for (int32_t k = 1; k <= maxit; ++k) {
+        if (k == 1)
+            for (int64_t i = 0; i < n; ++i) p[i] = r[i];
+        else
+            for (int64_t i = 0; i < n; ++i)
+                p[i] = (float)((double)r[i] + beta * ((double)p[i] - omega * (double)v[i]));
+        for (int64_t i = 0; i < n; ++i) ph[i] = (float)((double)dinv[i] * (double)p[i]);
+        orc_spmv_f32(n, row_ptr, col, val, ph, v);
+        double sigma = dot_f32(n, rh, v);
+        if (sigma == 0.0 || !isfinite(sigma)) { *outcome = ORC_BREAKDOWN; *iters = k; break; }
+        alpha = rho / sigma;
+        for (int64_t i = 0; i < n; ++i) s[i] = (float)((double)r[i] - alpha * (double)v[i]);
+        double ss = dot_f32(n, s, s);
+        if (!isfinite(ss)) { *outcome = ORC_BREAKDOWN; *iters = k; break; }
+        if (sqrt(ss) <= tol * sqrt(bb)) {
+            for (int64_t i = 0; i < n; ++i) {
+                x[i] = (float)((double)x[i] + alpha * (double)ph[i]);
+                r[i] = s[i];
+            }
+            rr = ss;
+            *outcome = ORC_CONVERGED; *iters = k;
+            break;
+        }
+        for (int64_t i = 0; i < n; ++i) sh[i] = (float)((double)dinv[i] * (double)s[i]);
+        orc_spmv_f32(n, row_ptr, col, val, sh, t);
+        double tt = dot_f32(n, t, t), ts = dot_f32(n, t, s);
+        omega = tt == 0.0 ? 0.0 : ts / tt;
+        if (tt == 0.0 || !isfinite(tt) || !isfinite(omega) || omega == 0.0) {
+            for (int64_t i = 0; i < n; ++i) {
+                x[i] = (float)((double)x[i] + alpha * (double)ph[i]);
+                r[i] = s[i];
+            }
+            rr = ss;
+            *outcome = ORC_BREAKDOWN; *iters = k;
+            break;
+        }
+        for (int64_t i = 0; i < n; ++i) {
+            x[i] = (float)(((double)x[i] + alpha * (double)ph[i]) + omega * (double)sh[i]);
+            r[i] = (float)((double)s[i] - omega * (double)t[i]);
+        }
+        rr = dot_f32(n, r, r);
+        if (sqrt(rr) <= tol * sqrt(bb)) { *outcome = ORC_CONVERGED; *iters = k; break; }
+        if (!isfinite(rr)) { *outcome = ORC_BREAKDOWN; *iters = k; break; }
+        if (k == maxit) break;
+        double rho_new = dot_f32(n, rh, r);
+        if (rho_new == 0.0 || !isfinite(rho_new)) { *outcome = ORC_BREAKDOWN; *iters = k; break; }
+        beta = (rho_new / rho) * (alpha / omega);
+        rho = rho_new;
+    }
+    *rel_res = sqrt(rr / bb);
+done32:
+    for (int j = 0; j < 8; ++j) free(w[j]);
+    return ORC_OK;
+}
+
+/* Backward of x = A^{-1} b solved by BiCGStab, for upstream g = dL/dx: the
+ * same adjoint as for PCG (solve A^T lambda = g, then dL/db = lambda and
+ * dL/dval[k] = -lambda_i x_j for stored entry k = (i, j)), with the adjoint
+ * system solved by the BiCGStab above on the explicitly formed A^T (same tol
+ * and maxit). One system (the solver takes one). */
+int orc_bicgstab_adjoint(int64_t n, const int64_t *row_ptr, const int64_t *col, int32_t vbytes,
+                         const void *vals, const void *x, const void *g, double tol,
+                         int32_t maxit, void *lambda, void *grad_vals, int32_t *iters,
+                         double *rel_res, int32_t *outcome) {
+    if (n < 1 || (vbytes != 4 && vbytes != 8)) return ORC_ERR_INVALID_ARG;
+    int64_t nnz = row_ptr[n];
+    int st = ORC_OK;
+    int64_t *tp = (int64_t *)malloc((size_t)(n + 1) * sizeof(int64_t));
+    int64_t *tc = (int64_t *)malloc((size_t)(nnz > 0 ? nnz : 1) * sizeof(int64_t));
+    void *tv = malloc((size_t)(nnz > 0 ? nnz : 1) * (size_t)vbytes);
+    if (!tp || !tc || !tv) st = ORC_ERR_OOM;
+    else if (vbytes == 8) {
+        const double *xs = (const double *)x;
+        double *ls = (double *)lambda, *gr = (double *)grad_vals;
+        st = transpose_f64(n, row_ptr, col, (const double *)vals, tp, tc, (double *)tv);
+        if (st == ORC_OK)
+            st = orc_bicgstab_f64(n, tp, tc, (const double *)tv, (const double *)g, tol, maxit, ls,
+                                  iters, rel_res, outcome);
+        if (st == ORC_OK)
+            for (int64_t i = 0; i < n; ++i)
+                for (int64_t k = row_ptr[i]; k < row_ptr[i + 1]; ++k) gr[k] = -ls[i] * xs[col[k]];
+    } else {
+        const float *xs = (const float *)x;
+        float *ls = (float *)lambda, *gr = (float *)grad_vals;
+        st = transpose_f32(n, row_ptr, col, (const float *)vals, tp, tc, (float *)tv);
+        if (st == ORC_OK)
+            st = orc_bicgstab_f32(n, tp, tc, (const float *)tv, (const float *)g, tol, maxit, ls,
+                                  iters, rel_res, outcome);
+        if (st == ORC_OK)
+            for (int64_t i = 0; i < n; ++i)
+                for (int64_t k = row_ptr[i]; k < row_ptr[i + 1]; ++k)
+                    gr[k] = (float)(-(double)ls[i] * (double)xs[col[k]]);
+    }
+    free(tp); free(tc); free(tv);
+    return st;
 }

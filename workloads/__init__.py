@@ -13,6 +13,8 @@ from .generators import (  # noqa: F401
     poisson2d_csr,
     diffusion2d_coo,
     diffusion3d_coo,
+    convdiff2d_coo,
+    rotating_flow,
     knn_laplacian_coo,
     normal_vector,
 )

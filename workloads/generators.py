@@ -137,6 +137,38 @@ def diffusion2d_coo(N: int, cx: np.ndarray, cy: np.ndarray, index_dtype=np.int32
     return rows, cols, np.ascontiguousarray(vals)
 
 
+def convdiff2d_coo(N: int, wx: np.ndarray, wy: np.ndarray, index_dtype=np.int32):
+    """Convection-diffusion -Laplace(u) + w . grad(u) on an N x N grid with unit
+    spacing, the convection term by first-order upwind differences, Dirichlet
+    boundaries (outside neighbours dropped): a non-symmetric, row-wise weakly
+    diagonally dominant M-matrix. wx, wy [N, N] are node velocities. Row i:
+    diagonal 4 + |wx| + |wy|; west -1 - max(wx, 0), east -1 - max(-wx, 0),
+    south -1 - max(wy, 0), north -1 - max(-wy, 0).
+    """
+    n = N * N
+    idx = np.arange(n, dtype=np.int64)
+    y, x = np.divmod(idx, N)
+    ux, uy = wx.reshape(n), wy.reshape(n)
+    diag = (4.0 + np.abs(ux)) + np.abs(uy)
+    cand = np.stack([idx - N, idx - 1, idx, idx + 1, idx + N], axis=1)
+    valid = np.stack([y > 0, x > 0, np.ones(n, bool), x < N - 1, y < N - 1], axis=1)
+    v = np.stack([-1.0 - np.maximum(uy, 0.0), -1.0 - np.maximum(ux, 0.0), diag,
+                  -1.0 - np.maximum(-ux, 0.0), -1.0 - np.maximum(-uy, 0.0)], axis=1)
+    rows = np.broadcast_to(idx[:, None], cand.shape)[valid].astype(index_dtype)
+    cols = cand[valid].astype(index_dtype)
+    return rows, cols, np.ascontiguousarray(v[valid])
+
+
+def rotating_flow(N: int, peak: float):
+    """Node velocities of a solid-body rotation about the grid centre, scaled so
+    that the largest speed is ``peak`` (cells per unit time)."""
+    c = (N - 1) / 2.0
+    y, x = np.mgrid[0:N, 0:N].astype(np.float64)
+    wx, wy = -(y - c), (x - c)
+    scale = peak / max(np.sqrt(wx * wx + wy * wy).max(), 1.0)
+    return wx * scale, wy * scale
+
+
 def diffusion3d_coo(N: int, cx: np.ndarray, cy: np.ndarray, cz: np.ndarray, index_dtype=np.int32):
     """Seven-point variable-coefficient diffusion on an N^3 grid, index z*N*N + y*N + x.
 
