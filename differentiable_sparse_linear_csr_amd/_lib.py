@@ -39,9 +39,8 @@ EXPORTS = ["sla_csr_create", "sla_csr_create_segmented", "sla_csr_get_segments",
            "sla_csr_set_values", "sla_csr_get", "sla_csr_get_pattern",
            "sla_csr_get_values",
            "sla_csr_gather_to_input", "sla_csr_set_option", "sla_spmv", "sla_spmv_backward",
-           "sla_pcg_solve",
-           "sla_adjoint_backward", "sla_profile_get", "sla_profile_reset", "sla_csr_memory",
-           "sla_csr_get_layout", "sla_csr_destroy", "sla_last_error", "sla_version"]
+           "sla_pcg_solve", "sla_adjoint_backward", "sla_bicgstab_solve", "sla_bicgstab_adjoint",
+           "sla_profile_get", "sla_profile_reset", "sla_csr_memory", "sla_csr_get_layout", "sla_csr_destroy", "sla_last_error", "sla_version"]
 
 
 class SlaError(RuntimeError):
@@ -85,6 +84,8 @@ def load() -> ctypes.CDLL:
     L.sla_spmv_backward.argtypes = [P, P, P, P, P, P]
     L.sla_pcg_solve.argtypes = [P, P, P, f64, i32, ctypes.POINTER(Info), P]
     L.sla_adjoint_backward.argtypes = [P, P, P, P, P, f64, i32, ctypes.POINTER(Info), P]
+    L.sla_bicgstab_solve.argtypes = [P, P, P, f64, i32, ctypes.POINTER(Info), P]
+    L.sla_bicgstab_adjoint.argtypes = [P, P, P, P, P, f64, i32, ctypes.POINTER(Info), P]
     L.sla_profile_get.argtypes = [P, i32, pi64, pf64]
     L.sla_profile_reset.argtypes = [P]
     L.sla_csr_memory.argtypes = [P, pi64]

@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsla.so")
 ARCH = "gfx950"
 
-SOURCES = ["util.hip", "assembly.hip", "spmv.hip", "pcg.hip", "resident.hip", "reorder.hip",
+SOURCES = ["util.hip", "assembly.hip", "spmv.hip", "pcg.hip", "bicgstab.hip", "resident.hip",
+           "reorder.hip",
            "seg.hip", "api.hip"]
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", f"-I{INCLUDE}"]

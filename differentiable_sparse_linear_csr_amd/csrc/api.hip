@@ -68,6 +68,7 @@ void destroy_handle(Handle *h) {
     if (h->inner) destroy_handle(h->inner);
     if (h->tr) destroy_handle(h->tr);
     if (h->graph) (void)hipGraphExecDestroy(h->graph);
+    if (h->bi_graph) (void)hipGraphExecDestroy(h->bi_graph);
     for (auto &rec : h->pending) {
         (void)hipEventDestroy(rec.a);
         (void)hipEventDestroy(rec.b);
@@ -414,6 +415,51 @@ sla_status sla_adjoint_backward(sla_csr hd, const void *x, const void *grad_x, v
                 transpose(h->x, grad_b, h->n, h->B, h->vbytes, s);
         }
         if (grad_vals_out) grad_vals(*h, h->x, x, grad_vals_out, s);
+        SLA_HIP(hipStreamSynchronize(s));
+        if (h->profile) flush_profile(*h);
+    });
+}
+
+sla_status sla_bicgstab_solve(sla_csr hd, const void *b, void *x, double tol, int32_t maxit,
+                              sla_info *info, void *stream) {
+    return guard([&] {
+        Handle *h = checked(hd);
+        if (!b || !x || !info) fail(SLA_ERR_INVALID_ARG, "null pointer");
+        if (!(tol >= 0.0) || maxit < 0) fail(SLA_ERR_INVALID_ARG, "need tol >= 0 and maxit >= 0");
+        if (h->B != 1 || h->nseg > 0)
+            fail(SLA_ERR_INVALID_ARG, "BiCGStab solves one system: batch 1, not segmented");
+        if (!h->diag_nonzero)
+            fail(SLA_ERR_BAD_DIAGONAL,
+                 "Jacobi preconditioning needs every diagonal entry present, non-zero and finite");
+        any_bicgstab(*h, b, x, tol, maxit, info, (hipStream_t)stream);
+    });
+}
+
+sla_status sla_bicgstab_adjoint(sla_csr hd, const void *x, const void *grad_x, void *grad_b,
+                                void *grad_vals_out, double tol, int32_t maxit, sla_info *info,
+                                void *stream) {
+    return guard([&] {
+        Handle *h = checked(hd);
+        if (!x || !grad_x || !info) fail(SLA_ERR_INVALID_ARG, "null pointer");
+        if (!(tol >= 0.0) || maxit < 0) fail(SLA_ERR_INVALID_ARG, "need tol >= 0 and maxit >= 0");
+        if (h->B != 1 || h->nseg > 0)
+            fail(SLA_ERR_INVALID_ARG, "BiCGStab solves one system: batch 1, not segmented");
+        if (!h->diag_nonzero)
+            fail(SLA_ERR_BAD_DIAGONAL,
+                 "Jacobi preconditioning needs every diagonal entry present, non-zero and finite");
+        if (grad_b && (grad_b == x || grad_b == grad_x))
+            fail(SLA_ERR_INVALID_ARG, "grad_b must not alias x or grad_x");
+        hipStream_t s = (hipStream_t)stream;
+        // A^T lambda = grad_x by BiCGStab on A^T (the handle itself when it was
+        // checked symmetric)
+        Handle &at = *transpose_for_backward(*h, s);
+        void *lam = grad_b;
+        if (!lam) {
+            if (!h->lam_tmp) h->lam_tmp = dalloc(*h, (size_t)h->n * h->vbytes);
+            lam = h->lam_tmp;
+        }
+        any_bicgstab(at, grad_x, lam, tol, maxit, info, s);
+        if (grad_vals_out) grad_vals(*h, lam, x, grad_vals_out, s);
         SLA_HIP(hipStreamSynchronize(s));
         if (h->profile) flush_profile(*h);
     });

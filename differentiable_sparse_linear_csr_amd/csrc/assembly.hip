@@ -179,13 +179,17 @@ __global__ __launch_bounds__(kBlock) void k_tile_k0(const RP *__restrict__ row_p
 }
 
 // dinv[i][b] = 1 / A_ii (IEEE division; fp32 storage: formed in fp64, rounded
-// once). Missing, non-positive or non-finite diagonals are counted.
+// once) for every present, non-zero, finite diagonal; 0 otherwise. Flags:
+// kDiagUnusable for a missing, zero or non-finite diagonal (no Jacobi at
+// all), kDiagNegative for a negative one (Jacobi-PCG needs positive ones).
+constexpr int kDiagUnusable = 1, kDiagNegative = 2;
+
 template <typename T, typename RP>
 __global__ __launch_bounds__(kBlock) void k_dinv(const RP *__restrict__ row_ptr,
                                                  const int32_t *__restrict__ col,
                                                  const T *__restrict__ vals, int64_t n, int B,
                                                  T *__restrict__ dinv, int *__restrict__ bad) {
-    int nbad = 0;
+    int flags = 0;
     const int64_t total = n * B;
     for (int64_t f = (int64_t)blockIdx.x * kBlock + threadIdx.x; f < total;
          f += (int64_t)gridDim.x * kBlock) {
@@ -199,14 +203,15 @@ __global__ __launch_bounds__(kBlock) void k_dinv(const RP *__restrict__ row_ptr,
         }
         const bool found = lo < (int64_t)row_ptr[i + 1] && col[lo] == i;
         const double d = found ? (double)vals[lo * B + b] : 0.0;
-        if (!found || !(d > 0.0) || !isfinite(d)) {
-            ++nbad;
+        if (!found || d == 0.0 || !isfinite(d)) {
+            flags |= kDiagUnusable;
             dinv[f] = (T)0;
         } else {
+            if (d < 0.0) flags |= kDiagNegative;
             dinv[f] = (T)(1.0 / d);
         }
     }
-    if (nbad) atomicAdd(bad, nbad);
+    if (flags) atomicOr(bad, flags);
 }
 
 template <typename T>
@@ -572,7 +577,7 @@ void build_tiles(Handle &h, hipStream_t s) {
     h.nlong = (int64_t)longs.size();
     h.tiles = (TileDesc *)dalloc(h, sizeof(TileDesc) * (shorts.size() + 1));
     h.long_rows = (int32_t *)dalloc(h, sizeof(int32_t) * (longs.size() + 1));
-    h.long_dot = (double *)dalloc(h, sizeof(double) * (longs.size() + 1));
+    h.long_dot = (double *)dalloc(h, sizeof(double) * 2 * (longs.size() + 1));  // two dots
     if (!shorts.empty())
         SLA_HIP(hipMemcpyAsync(h.tiles, shorts.data(), sizeof(TileDesc) * shorts.size(),
                                hipMemcpyHostToDevice, s));
@@ -625,7 +630,9 @@ void compute_dinv(Handle &h, hipStream_t s) {
         else go(float(), int32_t());
     }
     SLA_HIP(hipGetLastError());
-    h.diag_ok = read_flag(bad, s) == 0;
+    const int flags = read_flag(bad, s);
+    h.diag_ok = flags == 0;
+    h.diag_nonzero = (flags & kDiagUnusable) == 0;
 }
 
 bool check_symmetric(Handle &h, hipStream_t s) {

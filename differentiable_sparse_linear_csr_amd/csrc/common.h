@@ -133,7 +133,8 @@ struct Handle {
     int64_t nlong = 0;
     double *long_dot = nullptr;   // [nlong] p_i q_i of the long rows (fused SpMV)
     void *dinv = nullptr;    // [n][B]
-    bool diag_ok = false;
+    bool diag_ok = false;     // every diagonal present, positive, finite (PCG)
+    bool diag_nonzero = false; // every diagonal present, non-zero, finite (BiCGStab)
 
     // solve workspace
     void *x = nullptr, *r = nullptr, *p = nullptr, *q = nullptr; // [n][B]
@@ -195,6 +196,16 @@ struct Handle {
     int64_t *tr_map = nullptr;    // [nnz]: A^T CSR position -> this CSR position
     bool tr_stale = false;        // values changed since A^T's were gathered
 
+    // BiCGStab workspace (allocated at the first BiCGStab solve): r^, p^, s^,
+    // t; partials and counters of its reductions; its scalars; its graph
+    void *bi_vec[4] = {nullptr, nullptr, nullptr, nullptr};
+    double *bi_part = nullptr, *bi_gpart = nullptr, *bi_spart2 = nullptr;
+    uint32_t *bi_sync = nullptr;
+    void *bi_state = nullptr;
+    hipGraphExec_t bi_graph = nullptr;
+    int bi_graph_k = 0;
+    void *lam_tmp = nullptr;      // [n] adjoint solution when the caller wants no grad_b
+
     // iteration driver
     int check_k = 16;
     bool use_graph = true;
@@ -250,6 +261,14 @@ void reordered_pcg(Handle &h, const void *b, void *x, double tol, int32_t maxit,
                    hipStream_t s);
 void reordered_adjoint(Handle &h, const void *x, const void *g, void *grad_b, void *grad_vals,
                        double tol, int32_t maxit, sla_info *info, hipStream_t s);
+void reordered_bicgstab(Handle &h, const void *b, void *x, double tol, int32_t maxit,
+                        sla_info *info, hipStream_t s);
+// BiCGStab on one system (bicgstab.hip); b, x device vectors of n elements
+void bicgstab(Handle &h, const void *b, void *x, double tol, int32_t maxit, sla_info *info,
+              hipStream_t s, bool keep_internal);
+// BiCGStab for any single-system handle (reordered or not), caller's order
+void any_bicgstab(Handle &h, const void *b, void *x, double tol, int32_t maxit, sla_info *info,
+                  hipStream_t s);
 Handle *make_child(Handle &h, const std::vector<int64_t> &rp, const std::vector<int32_t> &col,
                    const int64_t *map, uint32_t flags, hipStream_t s);
 void child_values(Handle &h, Handle &child, const int64_t *map, hipStream_t s);

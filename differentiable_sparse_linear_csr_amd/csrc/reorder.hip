@@ -385,6 +385,20 @@ void reordered_pcg(Handle &h, const void *b, void *x, double tol, int32_t maxit,
     SLA_HIP(hipStreamSynchronize(s));
 }
 
+void reordered_bicgstab(Handle &h, const void *b, void *x, double tol, int32_t maxit,
+                        sla_info *info, hipStream_t s) {
+    to_inner(h, b, h.rtmp[0], s);
+    bicgstab(*h.inner, h.rtmp[0], h.rtmp[1], tol, maxit, info, s, false);
+    to_outer(h, h.rtmp[1], x, s);
+    SLA_HIP(hipStreamSynchronize(s));
+}
+
+void any_bicgstab(Handle &h, const void *b, void *x, double tol, int32_t maxit, sla_info *info,
+                  hipStream_t s) {
+    if (h.inner) reordered_bicgstab(h, b, x, tol, maxit, info, s);
+    else bicgstab(h, b, x, tol, maxit, info, s, false);
+}
+
 void reordered_adjoint(Handle &h, const void *x, const void *g, void *grad_b, void *grad_vals_out,
                        double tol, int32_t maxit, sla_info *info, hipStream_t s) {
     Handle &in = *h.inner;

@@ -34,15 +34,18 @@ constexpr int kTileGroups = (kTileCap + 3 + 4 * 64 - 1) / (4 * 64);
 constexpr int kRowItems = (kTileUnits + 1 + 63) / 64;  // row offsets per lane
 
 // Rows longer than kLongRow: one workgroup per row, 8 entries in flight per
-// lane. Runs before the tile kernel; in the fused form it also leaves
-// p_i q_i of each long row in long_dot for the tile kernel's reduction.
-template <typename T, typename RP, bool FUSED>
+// lane. Runs before the tile kernel. With DOT >= 1 it also leaves w_i q_i of
+// each long row in long_dot[l] (and q_i q_i in long_dot[nlong + l] with
+// DOT = 2) for the tile kernel's reduction; it does nothing unless *status is
+// still running.
+template <typename T, typename RP, int DOT>
 __global__ __launch_bounds__(kBlock) void k_spmv_long(
-    const int32_t *__restrict__ long_rows, const RP *__restrict__ row_ptr,
+    const int32_t *__restrict__ long_rows, int64_t nlong, const RP *__restrict__ row_ptr,
     const int32_t *__restrict__ col, const T *__restrict__ val, const T *__restrict__ x,
-    T *__restrict__ y, double *__restrict__ long_dot, const SysState *__restrict__ st) {
+    T *__restrict__ y, const T *__restrict__ w, double *__restrict__ long_dot,
+    const int32_t *__restrict__ status) {
     __shared__ double lds4[kWaves];
-    if (FUSED && st[0].status != kRunning) return;
+    if (DOT > 0 && *status != kRunning) return;
     const int tid = threadIdx.x;
     const int64_t i = long_rows[blockIdx.x];
     const int64_t k0 = row_ptr[i], len = (int64_t)row_ptr[i + 1] - k0;
@@ -66,7 +69,8 @@ __global__ __launch_bounds__(kBlock) void k_spmv_long(
     if (tid == 0) {
         const T q = (T)s;
         y[i] = q;
-        if (FUSED) long_dot[blockIdx.x] = (double)x[i] * (double)q;
+        if (DOT > 0) long_dot[blockIdx.x] = (double)w[i] * (double)q;
+        if (DOT > 1) long_dot[nlong + blockIdx.x] = (double)q * (double)q;
     }
 }
 
@@ -80,31 +84,35 @@ __global__ __launch_bounds__(kBlock) void k_spmv_long(
 // XCD b % 8, and the wavefronts of one XCD take one contiguous eighth of the
 // tiles, so the gathered vector segments they share stay in that XCD's L2.
 // The grid is persistent (a multiple of 8, at most kMaxGrid workgroups),
-// which also bounds the reduction partials. The fused form adds p.q of its
-// rows, and of the long rows in a fixed order, to the grid reduction.
-template <typename T, typename RP, bool FUSED, bool NARROW>
+// which also bounds the reduction partials. With DOT >= 1 (the fused forms)
+// it adds w.q of its rows, and of the long rows in a fixed order, to a
+// per-workgroup partial spart[DOT * block], and with DOT = 2 also q.q to
+// spart[2 * block + 1]; the fused forms do nothing unless *status is running.
+template <typename T, typename RP, int DOT, bool NARROW>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void k_spmv_tile(
     const TileDesc *__restrict__ tiles, int64_t ntiles, const uint16_t *__restrict__ roff16,
     const int32_t *__restrict__ col, const uint16_t *__restrict__ col16, const T *__restrict__ val,
-    const T *__restrict__ x, T *__restrict__ y, const double *__restrict__ long_dot, int64_t nlong,
-    double *__restrict__ spart, const SysState *__restrict__ st) {
+    const T *__restrict__ x, T *__restrict__ y, const T *__restrict__ w,
+    const double *__restrict__ long_dot, int64_t nlong, double *__restrict__ spart,
+    const int32_t *__restrict__ status) {
+    constexpr bool FUSED = DOT > 0;
     __shared__ double prod_all[kWaves][kTileCap];
     __shared__ int32_t roff_all[kWaves][kTileUnits + 1];
     __shared__ double pown_all[FUSED ? kWaves : 1][FUSED ? kTileUnits : 1];
     __shared__ double lds4[kWaves];
-    if (FUSED && st[0].status != kRunning) return;
+    if (FUSED && *status != kRunning) return;
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     double *prod = prod_all[wv];
     int32_t *roff = roff_all[wv];
-    double *pown = pown_all[FUSED ? wv : 0];  // p of the tile's own rows (fused form)
+    double *pown = pown_all[FUSED ? wv : 0];  // w of the tile's own rows (fused forms)
     const int xcd = blockIdx.x % kXcds;
     const int64_t waves_per_xcd = (int64_t)(gridDim.x / kXcds) * kWaves;
     const int64_t wid = (int64_t)(blockIdx.x / kXcds) * kWaves + wv;  // rank within its XCD
     int64_t t = ntiles * xcd / kXcds + wid;
     const int64_t t_end = ntiles * (xcd + 1) / kXcds;
-    double dot = 0.0;
+    double dot = 0.0, dot2 = 0.0;
 
     TileDesc d{0, 0, 0, 0, 0, 0, 0};
     int32_t c[kTileGroups][4];
@@ -197,8 +205,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
             if (j <= nrows) roff[j] = ro[u];
         }
         if (FUSED) {
-            // p of the tile's own rows, loaded next to the gathers (same latency)
-            const T *pp = x + d.rs;
+            // w of the tile's own rows, loaded next to the gathers (same latency)
+            const T *pp = w + d.rs;
 #pragma unroll
             for (int u = 0; u < kTileUnits / 64; ++u) {
                 const int i = lane + u * 64;
@@ -223,6 +231,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
                 const T q = (T)s;
                 y[d.rs + i] = q;
                 if (FUSED) dot += pown[i] * (double)q;
+                if (DOT > 1) dot2 += (double)q * (double)q;
             }
         }
         // this wavefront's next stores to its LDS slice come after these reads
@@ -233,14 +242,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
         d = dn;
     }
     if (FUSED) {
-        // this workgroup's p.q partial; the update kernel sums them (every
-        // workgroup there, in block order) and forms alpha, so this kernel
-        // ends without a grid-wide arrival
+        // this workgroup's partials; the next kernel sums them (every
+        // workgroup there, in block order) and forms its step, so this
+        // kernel ends without a grid-wide arrival
         for (int64_t l = blockIdx.x + (int64_t)threadIdx.x * gridDim.x; l < nlong;
-             l += (int64_t)kBlock * gridDim.x)
+             l += (int64_t)kBlock * gridDim.x) {
             dot += long_dot[l];
+            if (DOT > 1) dot2 += long_dot[nlong + l];
+        }
         dot = block_sum(dot, lds4);
-        if (threadIdx.x == 0) spart[blockIdx.x] = dot;
+        if (DOT > 1) dot2 = block_sum(dot2, lds4);
+        if (threadIdx.x == 0) {
+            spart[(int64_t)DOT * blockIdx.x] = dot;
+            if (DOT > 1) spart[2 * (int64_t)blockIdx.x + 1] = dot2;
+        }
     }
 }
 
@@ -448,22 +463,29 @@ int64_t batched_grid_t(const Handle &h) {
     return (h.n + rows_block - 1) / rows_block;
 }
 
+// Single system: the long-row kernel (if any) and the tile kernel, with DOT
+// fused inner products against w (see k_spmv_tile).
+template <typename T, typename RP, int DOT>
+void launch_tiles(Handle &h, const void *x, void *y, const void *w, double *spart,
+                  const int32_t *status, hipStream_t s) {
+    if (h.nlong > 0)
+        hipLaunchKernelGGL((k_spmv_long<T, RP, DOT>), dim3((unsigned)h.nlong), dim3(kBlock), 0, s,
+                           (const int32_t *)h.long_rows, h.nlong, (const RP *)h.row_ptr,
+                           (const int32_t *)h.col, (const T *)h.vals, (const T *)x, (T *)y,
+                           (const T *)w, h.long_dot, status);
+    const int64_t grid = spmv_grid(h);
+    auto kern = h.all_narrow ? k_spmv_tile<T, RP, DOT, true> : k_spmv_tile<T, RP, DOT, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBlock), 0, s, (const TileDesc *)h.tiles,
+                       h.ntiles, (const uint16_t *)h.roff16, (const int32_t *)h.col,
+                       (const uint16_t *)h.col16, (const T *)h.vals, (const T *)x, (T *)y,
+                       (const T *)w, (const double *)h.long_dot, h.nlong, spart, status);
+}
+
 template <typename T, typename RP, bool FUSED>
 void launch_spmv_t(Handle &h, const void *x, void *y, hipStream_t s) {
     const Red red{h.part, h.gpart, h.sync + kCntSpmv * kCountersPerKind};
     if (h.B == 1) {
-        if (h.nlong > 0)
-            hipLaunchKernelGGL((k_spmv_long<T, RP, FUSED>), dim3((unsigned)h.nlong), dim3(kBlock), 0,
-                               s, (const int32_t *)h.long_rows, (const RP *)h.row_ptr,
-                               (const int32_t *)h.col, (const T *)h.vals, (const T *)x, (T *)y,
-                               h.long_dot, (const SysState *)h.st);
-        const int64_t grid = spmv_grid(h);
-        auto kern = h.all_narrow ? k_spmv_tile<T, RP, FUSED, true> : k_spmv_tile<T, RP, FUSED, false>;
-        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBlock), 0, s,
-                           (const TileDesc *)h.tiles, h.ntiles, (const uint16_t *)h.roff16,
-                           (const int32_t *)h.col, (const uint16_t *)h.col16, (const T *)h.vals,
-                           (const T *)x, (T *)y, (const double *)h.long_dot, h.nlong, h.spart,
-                           (const SysState *)h.st);
+        launch_tiles<T, RP, FUSED ? 1 : 0>(h, x, y, x, h.spart, &h.st[0].status, s);
     } else if (bvec_ok<T>(h)) {
         hipLaunchKernelGGL((k_spmv_bvec<T, RP, FUSED>), dim3((unsigned)bvec_grid<T, FUSED>(h)),
                            dim3(kBlock), 0, s, h.n, h.B, bvec_rows_block<T, FUSED>(h),
@@ -508,18 +530,18 @@ void init_launch_limits(Handle &h) {
     const void *fn = nullptr;
     if (h.vt == SLA_F64) {
         if (h.all_narrow)
-            fn = h.rp64 ? (const void *)&k_spmv_tile<double, int64_t, true, true>
-                        : (const void *)&k_spmv_tile<double, int32_t, true, true>;
+            fn = h.rp64 ? (const void *)&k_spmv_tile<double, int64_t, 1, true>
+                        : (const void *)&k_spmv_tile<double, int32_t, 1, true>;
         else
-            fn = h.rp64 ? (const void *)&k_spmv_tile<double, int64_t, true, false>
-                        : (const void *)&k_spmv_tile<double, int32_t, true, false>;
+            fn = h.rp64 ? (const void *)&k_spmv_tile<double, int64_t, 1, false>
+                        : (const void *)&k_spmv_tile<double, int32_t, 1, false>;
     } else {
         if (h.all_narrow)
-            fn = h.rp64 ? (const void *)&k_spmv_tile<float, int64_t, true, true>
-                        : (const void *)&k_spmv_tile<float, int32_t, true, true>;
+            fn = h.rp64 ? (const void *)&k_spmv_tile<float, int64_t, 1, true>
+                        : (const void *)&k_spmv_tile<float, int32_t, 1, true>;
         else
-            fn = h.rp64 ? (const void *)&k_spmv_tile<float, int64_t, true, false>
-                        : (const void *)&k_spmv_tile<float, int32_t, true, false>;
+            fn = h.rp64 ? (const void *)&k_spmv_tile<float, int64_t, 1, false>
+                        : (const void *)&k_spmv_tile<float, int32_t, 1, false>;
     }
     h.spmv_resident = resident_workgroups(fn, h.device);
     if (h.B > 1) {
@@ -559,6 +581,29 @@ void launch_spmv_plain(Handle &h, const void *x, void *y, hipStream_t s) {
         if (h.rp64) launch_spmv_t<float, int64_t, false>(h, x, y, s);
         else launch_spmv_t<float, int32_t, false>(h, x, y, s);
     }
+}
+
+// Single system: y = A x with ndot (0, 1 or 2) inner products fused: w.y into
+// spart[ndot * block] and, for ndot = 2, y.y into spart[2 * block + 1], one
+// partial per workgroup of spmv_grid(h); skipped unless *status is running
+// (ndot > 0). spart holds ndot * spmv_grid(h) doubles.
+void launch_spmv_dots(Handle &h, const void *x, void *y, const void *w, int ndot, double *spart,
+                      const int32_t *status, hipStream_t s) {
+    auto go = [&](auto ttag, auto rtag) {
+        using T = decltype(ttag);
+        using RP = decltype(rtag);
+        if (ndot == 0) launch_tiles<T, RP, 0>(h, x, y, w, spart, status, s);
+        else if (ndot == 1) launch_tiles<T, RP, 1>(h, x, y, w, spart, status, s);
+        else launch_tiles<T, RP, 2>(h, x, y, w, spart, status, s);
+    };
+    if (h.vt == SLA_F64) {
+        if (h.rp64) go(double(), int64_t());
+        else go(double(), int32_t());
+    } else {
+        if (h.rp64) go(float(), int64_t());
+        else go(float(), int32_t());
+    }
+    SLA_HIP(hipGetLastError());
 }
 
 }  // namespace sla

@@ -235,20 +235,25 @@ class SparseCSR:
         return _MatvecFn.apply(self, vals, x)
 
     def solve_raw(self, b: torch.Tensor, tol: float = 1e-10, maxit: int = 10000,
-                  out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, SolveInfo]:
-        """x = A^{-1} b by Jacobi-PCG (no autograd). Returns (x, info)."""
+                  out: Optional[torch.Tensor] = None,
+                  method: str = "cg") -> Tuple[torch.Tensor, SolveInfo]:
+        """x = A^{-1} b (no autograd) by Jacobi-PCG (method "cg", SPD A) or
+        Jacobi-BiCGStab (method "bicgstab", general A, one system). Returns
+        (x, info)."""
         self._check_vec(b, "b")
         x = torch.empty_like(b) if out is None else out
         infos = (Info * self.nsys)()
-        check(_lib.load().sla_pcg_solve(self._h, _ptr(b), _ptr(x), float(tol), int(maxit), infos,
-                                        _stream(self.device)))
+        fn = _solver(method)[0]
+        check(fn(self._h, _ptr(b), _ptr(x), float(tol), int(maxit), infos, _stream(self.device)))
         info = SolveInfo(list(infos))
         self.last_info = info
         return x, info
 
     def adjoint_raw(self, x: torch.Tensor, grad_x: torch.Tensor, tol: float = 1e-10,
-                    maxit: int = 10000, want_b: bool = True, want_vals: bool = True):
-        """(grad_b [like x] or None, grad_vals [batch?, nnz] in CSR order or None, info)."""
+                    maxit: int = 10000, want_b: bool = True, want_vals: bool = True,
+                    method: str = "cg"):
+        """(grad_b [like x] or None, grad_vals [batch?, nnz] in CSR order or None, info);
+        the adjoint system is solved by the forward solve's method."""
         self._check_vec(x, "x")
         self._check_vec(grad_x, "grad_x")
         gb = torch.empty_like(x) if want_b else None
@@ -257,9 +262,9 @@ class SparseCSR:
             shape = (self.nnz,) if self.batch == 1 else (self.batch, self.nnz)
             gv = torch.empty(shape, dtype=self.dtype, device=self.device)
         infos = (Info * self.nsys)()
-        check(_lib.load().sla_adjoint_backward(self._h, _ptr(x), _ptr(grad_x), _ptr(gb), _ptr(gv),
-                                               float(tol), int(maxit), infos,
-                                               _stream(self.device)))
+        fn = _solver(method)[1]
+        check(fn(self._h, _ptr(x), _ptr(grad_x), _ptr(gb), _ptr(gv), float(tol), int(maxit), infos,
+                 _stream(self.device)))
         info = SolveInfo(list(infos))
         self.last_adjoint_info = info
         return gb, gv, info
@@ -273,18 +278,32 @@ class SparseCSR:
         return out
 
     def solve(self, b: torch.Tensor, values: Optional[torch.Tensor] = None, tol: float = 1e-10,
-              maxit: int = 10000, adjoint_tol: Optional[float] = None) -> torch.Tensor:
+              maxit: int = 10000, adjoint_tol: Optional[float] = None,
+              method: str = "cg") -> torch.Tensor:
         """Differentiable x = A^{-1} b: gradients flow to ``b`` and to ``values``
         (the input-order value tensor this handle was built or last set with,
-        or the one passed here, which is loaded into the handle)."""
+        or the one passed here, which is loaded into the handle). ``method``:
+        "cg" (Jacobi-PCG, SPD A) or "bicgstab" (Jacobi-BiCGStab, general A;
+        the backward solves A^T lambda = dL/dx with it)."""
         vals = self._values_ref if values is None else values
         return _SolveFn.apply(self, vals, b, float(tol), int(maxit),
-                              float(tol if adjoint_tol is None else adjoint_tol))
+                              float(tol if adjoint_tol is None else adjoint_tol), method)
 
 
-def _report(info: SolveInfo, what: str) -> None:
+def _solver(method: str):
+    L = _lib.load()
+    if method == "cg":
+        return L.sla_pcg_solve, L.sla_adjoint_backward
+    if method == "bicgstab":
+        return L.sla_bicgstab_solve, L.sla_bicgstab_adjoint
+    raise ValueError(f"unknown method {method!r} (\"cg\" or \"bicgstab\")")
+
+
+def _report(info: SolveInfo, what: str, method: str = "cg") -> None:
     if any(s == _lib.SLA_BREAKDOWN for s in info.status):
-        raise FloatingPointError(f"{what}: PCG breakdown (p.Ap <= 0: matrix not SPD?) {info}")
+        why = ("PCG breakdown (p.Ap <= 0: matrix not SPD?)" if method == "cg" else
+               "BiCGStab breakdown (a zero r^.v, t.t, omega or r^.r)")
+        raise FloatingPointError(f"{what}: {why} {info}")
     if any(s == _lib.SLA_MAXIT for s in info.status):
         warnings.warn(f"{what}: iteration budget reached before the tolerance {info}",
                       RuntimeWarning, stacklevel=3)
@@ -295,13 +314,13 @@ class _SolveFn(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, A: SparseCSR, values: torch.Tensor, b: torch.Tensor, tol: float, maxit: int,
-                adjoint_tol: float):
+                adjoint_tol: float, method: str = "cg"):
         if values is not None and values is not A._values_ref:
             A.set_values(values.detach())
-        x, info = A.solve_raw(b.detach(), tol, maxit)
-        _report(info, "solve")
+        x, info = A.solve_raw(b.detach(), tol, maxit, method=method)
+        _report(info, "solve", method)
         ctx.A = A
-        ctx.tol, ctx.maxit = adjoint_tol, maxit
+        ctx.tol, ctx.maxit, ctx.method = adjoint_tol, maxit, method
         ctx.save_for_backward(x)
         return x
 
@@ -312,12 +331,12 @@ class _SolveFn(torch.autograd.Function):
         want_vals = ctx.needs_input_grad[1]
         want_b = ctx.needs_input_grad[2]
         if not (want_vals or want_b):
-            return None, None, None, None, None, None
+            return None, None, None, None, None, None, None
         gb, gv, info = A.adjoint_raw(x, grad_x.contiguous(), ctx.tol, ctx.maxit, want_b=True,
-                                     want_vals=want_vals)
-        _report(info, "adjoint solve")
+                                     want_vals=want_vals, method=ctx.method)
+        _report(info, "adjoint solve", ctx.method)
         g_vals = A.gather_to_input(gv) if want_vals else None
-        return None, g_vals, (gb if want_b else None), None, None, None
+        return None, g_vals, (gb if want_b else None), None, None, None, None
 
 
 class _MatvecFn(torch.autograd.Function):

@@ -50,8 +50,9 @@ typedef enum {
     SLA_ERR_INVALID_CSR = 3,   /* CSR input: row_ptr not 0..nnz non-decreasing, or columns
                                   not strictly increasing inside a row */
     SLA_ERR_NOT_SYMMETRIC = 4, /* SLA_FLAG_CHECK_SYMMETRIC given and A != A^T bit for bit */
-    SLA_ERR_BAD_DIAGONAL = 5,  /* solve on a matrix with a missing, non-positive or
-                                  non-finite diagonal entry (Jacobi needs d_i > 0) */
+    SLA_ERR_BAD_DIAGONAL = 5,  /* solve on a matrix with a diagonal entry Jacobi cannot
+                                  use: missing, non-finite, or <= 0 for PCG (d_i > 0),
+                                  = 0 for BiCGStab (d_i != 0) */
     SLA_ERR_OOM = 6,           /* device or pinned-host allocation failed */
     SLA_ERR_HIP = 7            /* a HIP runtime call failed */
 } sla_status;
@@ -242,6 +243,49 @@ sla_status sla_pcg_solve(sla_csr h, const void *b, void *x, double tol, int32_t 
  * adjoint solve. Blocks the host until done.
  */
 sla_status sla_adjoint_backward(sla_csr h, const void *x, const void *grad_x, void *grad_b,
+                                void *grad_vals, double tol, int32_t maxit, sla_info *info,
+                                void *stream);
+
+/*
+ * Jacobi-preconditioned BiCGStab from x0 = 0 for a general (non-symmetric)
+ * system. torch-sla lists BiCGStab beside CG in its pytorch-native backend
+ * (backend list of the API section; the distributed section: the CG template
+ * with more inner products). The recurrence is van der Vorst's preconditioned
+ * BiCGStab with D = diag(A) and shadow residual r^ = b:
+ *   p = r (first) or r + beta (p - omega v); p^ = D^-1 p; v = A p^;
+ *   alpha = r^.r / r^.v; s = r - alpha v; if ||s|| <= tol ||b||: x += alpha p^,
+ *   converged; s^ = D^-1 s; t = A s^; omega = t.s / t.t;
+ *   x += alpha p^ + omega s^; r = s - omega t; stop when ||r|| <= tol ||b||;
+ *   beta = (r^.r' / r^.r)(alpha / omega).
+ * SLA_BREAKDOWN when r^.v, t.t, omega or the new r^.r is exactly 0 or not
+ * finite: at r^.v, x keeps its value; at omega, x takes the half step x +
+ * alpha p^. Iterations count the steps started (a half step counts as one).
+ * One system per handle: batch 1 and not segmented (else
+ * SLA_ERR_INVALID_ARG). b, x: [n] device vectors; info: host [1].
+ * maxit >= 0, tol >= 0. Returns SLA_ERR_BAD_DIAGONAL if some d_i is missing,
+ * zero or not finite (negative entries are fine). fp32 handles store vectors
+ * in fp32 and compute in fp64. Blocks the host until the solve has finished.
+ * Profiling (SLA_OPT_PROFILE) books the two SpMVs under SLA_KERNEL_SPMV_DOT,
+ * the half-step and update kernels under SLA_KERNEL_UPDATE and the p, p^
+ * kernel under SLA_KERNEL_DIRECTION.
+ */
+sla_status sla_bicgstab_solve(sla_csr h, const void *b, void *x, double tol, int32_t maxit,
+                              sla_info *info, void *stream);
+
+/*
+ * Adjoint backward of x = A^{-1} b solved by BiCGStab, for upstream grad_x =
+ * dL/dx (the adjoint of the distributed section, with the adjoint system
+ * A^T lambda = dL/dx solved by the same BiCGStab): then
+ *   grad_b = lambda                              ([n], or NULL)
+ *   grad_vals[k] = -lambda[row(k)] * x[col(k)]    ([nnz] in CSR order, or NULL)
+ * A^T is the handle itself when it was created with SLA_FLAG_CHECK_SYMMETRIC;
+ * otherwise the first call builds a handle of A^T (pattern sorted on the
+ * host, values gathered on the device and refreshed after set_values), as
+ * sla_spmv_backward does. x is the forward solution [n]; grad_b must not
+ * alias x or grad_x. info (host [1]) reports the adjoint solve. Same
+ * restrictions and errors as sla_bicgstab_solve. Blocks the host until done.
+ */
+sla_status sla_bicgstab_adjoint(sla_csr h, const void *x, const void *grad_x, void *grad_b,
                                 void *grad_vals, double tol, int32_t maxit, sla_info *info,
                                 void *stream);
 

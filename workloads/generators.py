@@ -263,6 +263,7 @@ WORKLOADS = {
     "knn_laplacian_2m": (4000, 2_000_000),
     "poisson2d_11548": (5000, 11548),
     "list_diffusion2d_16": (6000, 16),
+    "convdiff2d_1448": (7000, 1448),
 }
 
 
@@ -324,7 +325,7 @@ def make_workload(name: str, size: Optional[int] = None, batch: Optional[int] = 
     if name == "list_diffusion2d_16":
         # a list of systems with distinct patterns (SparseTensorList): member q
         # is 2D 5-point diffusion on a (128 + 16 q)^2 grid (scaled down with
-        # size: grids 8 (size + 2 q)), face coefficients log-uniform in
+        # size: size members on grids 8 (2 + q)), face coefficients log-uniform in
         # [0.1, 10]; returned as one block-diagonal COO with its segment rows
         M = N
         grids = [128 + 16 * q for q in range(M)] if size is None else [8 * (2 + q) for q in range(M)]
@@ -344,6 +345,18 @@ def make_workload(name: str, size: Optional[int] = None, batch: Optional[int] = 
                         np.concatenate(rs), None, np.concatenate(cs), np.concatenate(vs),
                         normal_vector(s + 1, n), normal_vector(s + 2, n), 1e-8, 20000, True,
                         {"seg_rows": seg, "grids": grids})
+
+    if name == "convdiff2d_1448":
+        # non-symmetric system for BiCGStab: upwind convection-diffusion in a
+        # solid-body rotation (peak speed 4 cells), N^2 = 2.1M unknowns at the
+        # default size; fixed iteration budget
+        wx, wy = rotating_flow(N, 4.0)
+        rows, cols, vals = convdiff2d_coo(N, wx, wy)
+        n = N * N
+        return Workload(name, f"2D upwind convection-diffusion {N}x{N} (rotating flow, peak "
+                        "cell speed 4), non-symmetric, fp64", n, 1, "f64", "coo", rows, None,
+                        cols, vals, normal_vector(s + 1, n), normal_vector(s + 2, n), 1e-8, 1000,
+                        True, {"grid": N, "method": "bicgstab"})
 
     # poisson2d_11548: CSR input, int64 row pointer, fixed iteration budget
     row_ptr, cols, vals = poisson2d_csr(N)
