@@ -83,8 +83,9 @@ def load_traffic(workload: str, tag: str):
 
 def cpu_baseline(w, budget_s: float):
     """The oracle as it stands, on the host cores: iterations/s of the forward
-    Jacobi-PCG on the same matrix and right-hand side, over a bounded number of
-    iterations (the first ones of the same solve)."""
+    solve (Jacobi-PCG, or Jacobi-BiCGStab for a non-symmetric workload) on the
+    same matrix and right-hand side, over a bounded number of iterations (the
+    first ones of the same solve)."""
     import numpy as np
     import oracle
 
@@ -120,20 +121,108 @@ def cpu_baseline(w, budget_s: float):
         ref = oracle.coo_to_csr(w.n, w.rows, w.cols, w.vals)
         vals = ref["vals"]
     b = w.b
+    bicg = w.extra.get("method") == "bicgstab"
+    solve = oracle.bicgstab if bicg else oracle.pcg
     t0 = time.perf_counter()
-    oracle.pcg(ref["row_ptr"], ref["col"], vals, b, 0.0, 5)
+    solve(ref["row_ptr"], ref["col"], vals, b, 0.0, 5)
     probe = (time.perf_counter() - t0) / 5
     iters = int(max(5, min(w.maxit, budget_s / max(probe, 1e-9))))
     t0 = time.perf_counter()
-    _, it, _, _ = oracle.pcg(ref["row_ptr"], ref["col"], vals, b, 0.0, iters)
+    _, it, _, _ = solve(ref["row_ptr"], ref["col"], vals, b, 0.0, iters)
     dt = time.perf_counter() - t0
     it = int(np.sum(it))
     per_sys = w.batch
+    name = "Jacobi-BiCGStab" if bicg else "Jacobi-PCG"
     return {"value": it / dt, "unit": "iterations/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"first {iters} Jacobi-PCG iterations (tol 0) of the forward solve of "
+            "sample": f"first {iters} {name} iterations (tol 0) of the forward solve of "
                       f"{w.name} ({per_sys} system(s)), oracle CSR built from the same input; "
                       f"{dt:.1f} s"}
+
+
+def run_inverse(args, N: int = 128, S: int = 4) -> int:
+    """The inverse-conductivity demonstration as a workload: a step is one Adam
+    step (assembly of A(kappa), batched PCG of the S experiments, batched
+    adjoint, chain to kappa, update). warmup + steps Adam steps run on one
+    trajectory (cosine decay over all of them); value counts the PCG
+    iterations (forward + adjoint, summed over experiments) of the timed steps."""
+    import numpy as np
+    import torch
+    from differentiable_sparse_linear_csr_amd import _lib
+    from differentiable_sparse_linear_csr_amd.inverse import ConductivityRecovery
+
+    total = args.warmup + args.steps
+    t_gen = time.perf_counter()
+    rec = ConductivityRecovery(N, sources=S, total_steps=total, device="cuda:0")
+    A = rec.A
+    A.set_option(_lib.SLA_OPT_CHECK_INTERVAL, args.check_interval)
+    print(f"[bench] inverse conductivity {N}x{N}, {S} experiments, {total} Adam steps "
+          f"(set up in {time.perf_counter() - t_gen:.1f} s)", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        rec.step()
+    torch.cuda.synchronize()
+    it0 = rec.iterations
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        rec.step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    value = (rec.iterations - it0) / elapsed
+    rep = rec.report()
+    # profiled SpMV launches of one more solve (after the trajectory)
+    A.profile_reset()
+    A.set_option(_lib.SLA_OPT_PROFILE, 1)
+    with torch.no_grad():
+        A.solve_raw(rec.F, rec.tol, rec.maxit)
+    prof = A.profile()
+    A.set_option(_lib.SLA_OPT_PROFILE, 0)
+    launches, total_ms = prof["spmv_dot"]
+    avg_ms = total_ms / max(launches, 1)
+    n, nnz = rec.grid.n, A.nnz
+    V, R = 8, (8 if A.row_index_dtype == torch.int64 else 4)
+    ab = algorithmic_bytes(n, nnz, S, V, R)
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "iterations/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed / max(args.steps, 1) * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": f"inverse_conductivity_{N}",
+                   "description": f"Adam recovery of kappa in -div(kappa grad u) = f_s, {N}x{N} "
+                                  f"grid, {S} Gaussian sources solved as one batch",
+                   "n": n, "nnz": nnz, "batch": S, "tol": rec.tol, "maxit": rec.maxit,
+                   "step": "assemble A(kappa) + pcg_solve (batch) + adjoint_backward + Adam",
+                   "adam_steps_total": total, "check_interval": args.check_interval},
+        "roofline": {"kernel": "k_spmv_bvec (fused q = A p, p.q partials, alpha; per-launch events)",
+                     "bound": "hbm", "achieved": round(ab["spmv"] / (avg_ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ab["spmv"] / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": round(ab["spmv"]),
+                     "avg_launch_ms": round(avg_ms, 5), "launches_timed": launches},
+        "extra": {"recovery": rep,
+                  "pages_figure": "1500 Adam steps, kappa error 2.3e-3, misfit 3.0e-5, "
+                                  "32 ms/step on RTX PRO 6000 (grid not stated)",
+                  "kernel_avg_ms": {k: round(v[1] / max(v[0], 1), 5) for k, v in prof.items()
+                                    if v[0]}},
+    }
+    if not args.no_cpu_baseline:
+        # the oracle's batched PCG on the same systems (true kappa, the S sources)
+        class W:
+            pass
+        w = W()
+        g = rec.grid
+        w.name, w.n, w.batch, w.fmt, w.maxit, w.extra = f"inverse_conductivity_{N}", n, S, "coo", \
+            rec.maxit, {}
+        w.rows, w.cols = g.rows.cpu().numpy(), g.cols.cpu().numpy()
+        w.vals = np.ascontiguousarray(
+            g.values(rec.kappa_true).expand(S, -1).detach().cpu().numpy())
+        w.b = rec.F.cpu().numpy()
+        print("[bench] timing the CPU oracle ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def main() -> int:
@@ -155,6 +244,9 @@ def main() -> int:
               "(multi-GPU sharding is described in DESIGN.md, not built). Use --gpus 1.",
               file=sys.stderr)
         return 2
+
+    if args.workload == "inverse_conductivity_128":
+        return run_inverse(args)
 
     import numpy as np
     import torch
@@ -189,12 +281,14 @@ def main() -> int:
     A.set_option(_lib.SLA_OPT_CHECK_INTERVAL, args.check_interval)
     x = torch.empty_like(b)
 
+    method = w.extra.get("method", "cg")
+
     def step():
         A.set_values(vals)
-        _, info = A.solve_raw(b, w.tol, w.maxit, out=x)
+        _, info = A.solve_raw(b, w.tol, w.maxit, out=x, method=method)
         its = list(info.iterations)
         if w.adjoint:
-            _, _, ainfo = A.adjoint_raw(x, g, w.tol, w.maxit)
+            _, _, ainfo = A.adjoint_raw(x, g, w.tol, w.maxit, method=method)
             its = [i + j for i, j in zip(its, ainfo.iterations)]
         return its, info
 
@@ -252,7 +346,14 @@ def main() -> int:
     ab = algorithmic_bytes(w.n, w.nnz, w.batch, V, R)
     # whole-job bytes per second of the iterations the steps performed: a
     # list's member iteration moves that member's bytes only
-    if "seg_rows" in w.extra:
+    if method == "bicgstab":
+        # two SpMVs (matrix twice, one gather and one store each, the fused
+        # dot partner read) and 25 vector passes in the five kernels (dir 6,
+        # SpMVs 3 + 3, half 5, update 8)
+        mat = ab["iter_3k"] - 13 * V * w.n * w.batch
+        bicg_iter = 2 * mat + 25 * V * w.n * w.batch
+        job_bps = {"iter_3k": bicg_iter * value, "iter_min": bicg_iter * value}
+    elif "seg_rows" in w.extra:
         seg = w.extra["seg_rows"]
         seg_nnz = np.bincount(np.searchsorted(seg, w.rows, side="right") - 1,
                               minlength=len(seg) - 1)
@@ -276,7 +377,8 @@ def main() -> int:
         # p.q partials): back-to-back launches of sla_spmv
         launches, avg_ms = reps, b2b_ms
         bytes_launch = ab["spmv"]
-        n_it = max(prof["spmv_dot"][0], 1)
+        # iterations: one direction-kernel launch each (two SpMVs in BiCGStab)
+        n_it = max(prof["direction"][0] if method == "bicgstab" else prof["spmv_dot"][0], 1)
         per_iter_ms = sum(prof[k][1] for k in ("spmv_dot", "update", "direction")) / n_it
         kernel = "k_spmv_tile (q = A p; 50 back-to-back sla_spmv launches)"
     else:
@@ -311,7 +413,9 @@ def main() -> int:
             "n": w.n, "nnz": w.nnz, "batch": w.batch,
             "row_ptr": "int64" if R == 8 else "int32", "col_idx": "int32",
             "tol": w.tol, "maxit": w.maxit,
-            "step": "set_values + pcg_solve" + (" + adjoint_backward" if w.adjoint else ""),
+            "step": ("set_values + bicgstab_solve" + (" + bicgstab_adjoint" if w.adjoint else "")
+                     if method == "bicgstab" else
+                     "set_values + pcg_solve" + (" + adjoint_backward" if w.adjoint else "")),
             "forward_iterations": fwd_its,
             "check_interval": args.check_interval,
         },
@@ -331,6 +435,9 @@ def main() -> int:
             "create_ms": round(create_ms, 2),
             # whole-job figures: every second of the timed steps counted
             "iteration_ms": round(1e3 / value, 5),
+            "iteration_model": ("BiCGStab: 2 matrix reads + 25 vector passes per iteration"
+                                if method == "bicgstab" else
+                                "PCG: matrix + 13 vector passes (3k) / + 7 (min) per iteration"),
             "iteration_gbps_3k": round(job_bps["iter_3k"] / 1e9, 1),
             "iteration_frac_3k": round(job_bps["iter_3k"] / 1e9 / HBM_PEAK_GBS, 4),
             "iteration_gbps_min": round(job_bps["iter_min"] / 1e9, 1),

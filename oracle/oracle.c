@@ -43,6 +43,10 @@
 #define ORC_ERR_BAD_DIAGONAL 5
 #define ORC_ERR_OOM 6
 
+/* loops over fewer rows than this run on one thread (thread start-up would
+ * dominate; results do not depend on it) */
+#define ORC_MIN_PARALLEL 65536
+
 #define ORC_CONVERGED 0
 #define ORC_MAXIT 1
 #define ORC_BREAKDOWN 2
@@ -232,7 +236,7 @@ int orc_is_symmetric_f64(int64_t n, const int64_t *row_ptr, const int64_t *col, 
  * (reading: the pages fix no precision for the fp32 case). */
 void orc_spmv_f64(int64_t n, const int64_t *row_ptr, const int64_t *col, const double *val,
                   const double *x, double *y) {
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n >= ORC_MIN_PARALLEL)
     for (int64_t i = 0; i < n; ++i) {
         double s = 0.0;
         for (int64_t k = row_ptr[i]; k < row_ptr[i + 1]; ++k) s = s + val[k] * x[col[k]];
@@ -242,7 +246,7 @@ void orc_spmv_f64(int64_t n, const int64_t *row_ptr, const int64_t *col, const d
 
 void orc_spmv_f32(int64_t n, const int64_t *row_ptr, const int64_t *col, const float *val,
                   const float *x, float *y) {
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n >= ORC_MIN_PARALLEL)
     for (int64_t i = 0; i < n; ++i) {
         double s = 0.0;
         for (int64_t k = row_ptr[i]; k < row_ptr[i + 1]; ++k)
@@ -363,15 +367,15 @@ int orc_pcg_f64(int64_t n, const int64_t *row_ptr, const int64_t *col, const dou
         double sigma = dot_f64(n, p, q);
         if (!(sigma > 0.0) || !isfinite(sigma)) { *outcome = ORC_BREAKDOWN; *iters = k; break; }
         double alpha = rho / sigma;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n >= ORC_MIN_PARALLEL)
         for (int64_t i = 0; i < n; ++i) { x[i] = x[i] + alpha * p[i]; r[i] = r[i] - alpha * q[i]; }
         rr = dot_f64(n, r, r);
         if (sqrt(rr) <= tol * sqrt(bb)) { *outcome = ORC_CONVERGED; *iters = k; break; }
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n >= ORC_MIN_PARALLEL)
         for (int64_t i = 0; i < n; ++i) z[i] = dinv[i] * r[i];
         double rho_new = dot_f64(n, r, z);
         double beta = rho_new / rho;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n >= ORC_MIN_PARALLEL)
         for (int64_t i = 0; i < n; ++i) p[i] = z[i] + beta * p[i];
         rho = rho_new;
     }
@@ -416,7 +420,7 @@ int orc_pcg_f32(int64_t n, const int64_t *row_ptr, const int64_t *col, const flo
         for (int64_t i = 0; i < n; ++i) sigma = sigma + (double)p[i] * (double)q[i];
         if (!(sigma > 0.0) || !isfinite(sigma)) { *outcome = ORC_BREAKDOWN; *iters = k; break; }
         double alpha = rho / sigma;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n >= ORC_MIN_PARALLEL)
         for (int64_t i = 0; i < n; ++i) {
             x[i] = (float)((double)x[i] + alpha * (double)p[i]);
             r[i] = (float)((double)r[i] - alpha * (double)q[i]);
@@ -427,7 +431,7 @@ int orc_pcg_f32(int64_t n, const int64_t *row_ptr, const int64_t *col, const flo
         double rho_new = 0.0;
         for (int64_t i = 0; i < n; ++i) rho_new = rho_new + (double)r[i] * ((double)dinv[i] * (double)r[i]);
         double beta = rho_new / rho;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n >= ORC_MIN_PARALLEL)
         for (int64_t i = 0; i < n; ++i)
             p[i] = (float)((double)dinv[i] * (double)r[i] + beta * (double)p[i]);
         rho = rho_new;
@@ -606,15 +610,15 @@ int orc_bicgstab_f64(int64_t n, const int64_t *row_ptr, const int64_t *col, cons
         if (k == 1)
             for (int64_t i = 0; i < n; ++i) p[i] = r[i];
         else
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n >= ORC_MIN_PARALLEL)
             for (int64_t i = 0; i < n; ++i) p[i] = r[i] + beta * (p[i] - omega * v[i]);
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n >= ORC_MIN_PARALLEL)
         for (int64_t i = 0; i < n; ++i) ph[i] = dinv[i] * p[i];
         orc_spmv_f64(n, row_ptr, col, val, ph, v);
         double sigma = dot_f64(n, rh, v);
         if (sigma == 0.0 || !isfinite(sigma)) { *outcome = ORC_BREAKDOWN; *iters = k; break; }
         alpha = rho / sigma;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n >= ORC_MIN_PARALLEL)
         for (int64_t i = 0; i < n; ++i) s[i] = r[i] - alpha * v[i];
         double ss = dot_f64(n, s, s);
         if (!isfinite(ss)) { *outcome = ORC_BREAKDOWN; *iters = k; break; }
@@ -624,7 +628,7 @@ int orc_bicgstab_f64(int64_t n, const int64_t *row_ptr, const int64_t *col, cons
             *outcome = ORC_CONVERGED; *iters = k;
             break;
         }
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n >= ORC_MIN_PARALLEL)
         for (int64_t i = 0; i < n; ++i) sh[i] = dinv[i] * s[i];
         orc_spmv_f64(n, row_ptr, col, val, sh, t);
         double tt = dot_f64(n, t, t), ts = dot_f64(n, t, s);
@@ -635,7 +639,7 @@ int orc_bicgstab_f64(int64_t n, const int64_t *row_ptr, const int64_t *col, cons
             *outcome = ORC_BREAKDOWN; *iters = k;
             break;
         }
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n >= ORC_MIN_PARALLEL)
         for (int64_t i = 0; i < n; ++i) {
             x[i] = (x[i] + alpha * ph[i]) + omega * sh[i];
             r[i] = s[i] - omega * t[i];
