@@ -185,6 +185,25 @@ __global__ __launch_bounds__(kBlock) void k_bi_half(int64_t n, T *__restrict__ r
     __shared__ double tmp[kBlock];
     __shared__ double tot[1];
     if (st->status != kRunning) return;
+    const int tid = threadIdx.x;
+    const int64_t ngl = n / W;
+    const int64_t per_pass = (int64_t)kBlock * kBiGroups;
+    T rv[kBiGroups][W], vv[kBiGroups][W], dv[kBiGroups][W], hv[kBiGroups][W];
+    auto load = [&](int64_t g0) {
+#pragma unroll
+        for (int u = 0; u < kBiGroups; ++u) {
+            const int64_t g = g0 + u * kBlock + tid;
+            if (g < ngl) {
+                vload(r + g * W, rv[u]);
+                vload(v + g * W, vv[u]);
+                vload(dinv + g * W, dv[u]);
+            }
+        }
+    };
+    // the first pass's rows are loaded before the SpMV's partials are read,
+    // so the two latencies overlap
+    int64_t g0 = (int64_t)blockIdx.x * per_pass;
+    load(g0);
     const double sigma = sum_parts(spart, spart_n, 1, 0, lds4);
     const bool bad = sigma == 0.0 || !isfinite(sigma);
     const double alpha = bad ? 0.0 : st->rho / sigma;
@@ -194,20 +213,8 @@ __global__ __launch_bounds__(kBlock) void k_bi_half(int64_t n, T *__restrict__ r
         shv = (T)((double)dv * (double)rv);
         sss += (double)rv * (double)rv;
     };
-    const int tid = threadIdx.x;
-    const int64_t ng = bad ? 0 : n / W;   // breakdown: r stays as it is
-    const int64_t per_pass = (int64_t)kBlock * kBiGroups;
-    for (int64_t g0 = (int64_t)blockIdx.x * per_pass; g0 < ng; g0 += (int64_t)gridDim.x * per_pass) {
-        T rv[kBiGroups][W], vv[kBiGroups][W], dv[kBiGroups][W], hv[kBiGroups][W];
-#pragma unroll
-        for (int u = 0; u < kBiGroups; ++u) {
-            const int64_t g = g0 + u * kBlock + tid;
-            if (g < ng) {
-                vload(r + g * W, rv[u]);
-                vload(v + g * W, vv[u]);
-                vload(dinv + g * W, dv[u]);
-            }
-        }
+    const int64_t ng = bad ? 0 : ngl;   // breakdown: r stays as it is
+    for (; g0 < ng; g0 += (int64_t)gridDim.x * per_pass) {
 #pragma unroll
         for (int u = 0; u < kBiGroups; ++u) {
             const int64_t g = g0 + u * kBlock + tid;
@@ -218,6 +225,7 @@ __global__ __launch_bounds__(kBlock) void k_bi_half(int64_t n, T *__restrict__ r
                 vstore(sh + g * W, hv[u]);
             }
         }
+        if (g0 + (int64_t)gridDim.x * per_pass < ng) load(g0 + (int64_t)gridDim.x * per_pass);
     }
     if (!bad && blockIdx.x == 0 && tid < n - (n / W) * W) {
         const int64_t i = (n / W) * W + tid;
@@ -273,6 +281,31 @@ __global__ __launch_bounds__(kBlock) void k_bi_update(int64_t n, T *__restrict__
     __shared__ double tot[2];
     if (st->status != kRunning && st->half == 0) return;
     const bool half = st->half != 0;
+    const int tid = threadIdx.x;
+    const int64_t ng = n / W;
+    const int64_t per_pass = (int64_t)kBlock * kBiGroups;
+    T xv[kBiGroups][W], rv[kBiGroups][W], rhv[kBiGroups][W], phv[kBiGroups][W],
+        shv[kBiGroups][W], tv[kBiGroups][W];
+    // a half step needs x and p^ only; otherwise all six (a breakdown at
+    // omega, known only after the partials, then ignores four of them)
+    auto load = [&](int64_t g0) {
+#pragma unroll
+        for (int u = 0; u < kBiGroups; ++u) {
+            const int64_t g = g0 + u * kBlock + tid;
+            if (g < ng) {
+                vload(x + g * W, xv[u]);
+                vload(ph + g * W, phv[u]);
+                if (!half) {
+                    vload(r + g * W, rv[u]);
+                    vload(rh + g * W, rhv[u]);
+                    vload(sh + g * W, shv[u]);
+                    vload(t + g * W, tv[u]);
+                }
+            }
+        }
+    };
+    int64_t g0 = (int64_t)blockIdx.x * per_pass;
+    load(g0);   // overlaps the reading of the SpMV's partials
     double omega = 0.0;
     bool obad = false;
     if (!half) {
@@ -294,26 +327,7 @@ __global__ __launch_bounds__(kBlock) void k_bi_update(int64_t n, T *__restrict__
             xv = (T)((double)xv + alpha * (double)phv);
         }
     };
-    const int tid = threadIdx.x;
-    const int64_t ng = n / W;
-    const int64_t per_pass = (int64_t)kBlock * kBiGroups;
-    for (int64_t g0 = (int64_t)blockIdx.x * per_pass; g0 < ng; g0 += (int64_t)gridDim.x * per_pass) {
-        T xv[kBiGroups][W], rv[kBiGroups][W], rhv[kBiGroups][W], phv[kBiGroups][W],
-            shv[kBiGroups][W], tv[kBiGroups][W];
-#pragma unroll
-        for (int u = 0; u < kBiGroups; ++u) {
-            const int64_t g = g0 + u * kBlock + tid;
-            if (g < ng) {
-                vload(x + g * W, xv[u]);
-                vload(ph + g * W, phv[u]);
-                if (full) {
-                    vload(r + g * W, rv[u]);
-                    vload(rh + g * W, rhv[u]);
-                    vload(sh + g * W, shv[u]);
-                    vload(t + g * W, tv[u]);
-                }
-            }
-        }
+    for (; g0 < ng; g0 += (int64_t)gridDim.x * per_pass) {
 #pragma unroll
         for (int u = 0; u < kBiGroups; ++u) {
             const int64_t g = g0 + u * kBlock + tid;
@@ -325,6 +339,7 @@ __global__ __launch_bounds__(kBlock) void k_bi_update(int64_t n, T *__restrict__
                 if (full) vstore(r + g * W, rv[u]);
             }
         }
+        if (g0 + (int64_t)gridDim.x * per_pass < ng) load(g0 + (int64_t)gridDim.x * per_pass);
     }
     if (blockIdx.x == 0 && tid < n - ng * W) {
         const int64_t i = ng * W + tid;

@@ -482,6 +482,23 @@ __global__ __launch_bounds__(kBlock) void k_update_dir1(int64_t n, T *__restrict
     if (ctl->n_running == 0) return;  // one system: running or not
     const int tid = threadIdx.x;
     const uint64_t gen = ((uint64_t)ctl->epoch << 32) | (uint32_t)(st[0].iter + 1);
+    // this workgroup's rows are loaded first, so their latency overlaps the
+    // reading of the SpMV's partials below
+    const int64_t ngl = n / W;
+    const int64_t g0 = (int64_t)blockIdx.x * kBlock * kFusedGroups;
+    T xv[kFusedGroups][W], pv[kFusedGroups][W], rv[kFusedGroups][W], qv[kFusedGroups][W],
+        dv[kFusedGroups][W];
+#pragma unroll
+    for (int u = 0; u < kFusedGroups; ++u) {
+        const int64_t g = g0 + u * kBlock + tid;
+        if (g < ngl) {
+            vload(x + g * W, xv[u]);
+            vload(p + g * W, pv[u]);
+            vload(r + g * W, rv[u]);
+            vload(q + g * W, qv[u]);
+            vload(dinv + g * W, dv[u]);
+        }
+    }
     double sg = 0.0;
     for (int64_t j = tid; j < spart_n; j += 4 * kBlock) {
         double v4[4];
@@ -494,21 +511,7 @@ __global__ __launch_bounds__(kBlock) void k_update_dir1(int64_t n, T *__restrict
     const bool breakdown = !(sigma > 0.0) || !isfinite(sigma);
     const double alpha = breakdown ? 0.0 : st[0].rho / sigma;
     double srz = 0.0, srr = 0.0;
-    const int64_t ng = breakdown ? 0 : n / W;
-    const int64_t g0 = (int64_t)blockIdx.x * kBlock * kFusedGroups;
-    T xv[kFusedGroups][W], pv[kFusedGroups][W], rv[kFusedGroups][W], qv[kFusedGroups][W],
-        dv[kFusedGroups][W];
-#pragma unroll
-    for (int u = 0; u < kFusedGroups; ++u) {
-        const int64_t g = g0 + u * kBlock + tid;
-        if (g < ng) {
-            vload(x + g * W, xv[u]);
-            vload(p + g * W, pv[u]);
-            vload(r + g * W, rv[u]);
-            vload(q + g * W, qv[u]);
-            vload(dinv + g * W, dv[u]);
-        }
-    }
+    const int64_t ng = breakdown ? 0 : ngl;   // breakdown: x and r stay as they are
     auto row = [&](T &xe, T &re, T pe, T qe, T de) {
         xe = (T)((double)xe + alpha * (double)pe);
         re = (T)((double)re - alpha * (double)qe);
