@@ -224,3 +224,53 @@ def test_full_size_first_iterates():
                                               w.g, 0.0, 20)
     gb, gv, _ = A.adjoint_raw(x, dev(w.g), 0.0, 20, method="bicgstab")
     assert rel(host(gb), lam_o) <= 1e-9 and rel(host(gv), gv_o) <= 1e-9
+
+
+def test_results_independent_of_poll_interval_and_graphs():
+    """The device freezes a finished solve, so neither the iterate nor the
+    count depends on how often the host polls or on graph replay."""
+    n, r, c, v = (10201,) + convdiff(101)
+    b = dev(np.random.default_rng(61).standard_normal(n))
+    A = handle(n, r, c, v)
+    ref_x, ref_info = None, None
+    for k, graph in [(16, 1), (1, 1), (7, 1), (64, 1), (16, 0)]:
+        A.set_option(_lib.SLA_OPT_CHECK_INTERVAL, k)
+        A.set_option(_lib.SLA_OPT_USE_GRAPH, graph)
+        x, info = A.solve_raw(b, 1e-9, 3000, method="bicgstab")
+        X = host(x)
+        if ref_x is None:
+            ref_x, ref_info = X, (info.iterations[0], info.status[0], info.rel_residual[0])
+        assert (info.iterations[0], info.status[0], info.rel_residual[0]) == ref_info, (k, graph)
+        assert np.array_equal(X, ref_x), (k, graph)
+
+
+def test_fp32_converged_and_reordered_adjoint():
+    n, r, c, v = (30001,) + irregular(30001, 70)
+    ref32 = oracle.coo_to_csr(n, r, c, v.astype(np.float32))
+    b = np.random.default_rng(62).standard_normal(n).astype(np.float32)
+    g = np.random.default_rng(63).standard_normal(n).astype(np.float32)
+    for reorder in (False, True):
+        A = handle(n, r, c, v.astype(np.float32), reorder=reorder)
+        x, info = A.solve_raw(dev(b), 1e-5, 500, method="bicgstab")
+        xo, ito, _, oco = oracle.bicgstab(ref32["row_ptr"], ref32["col"], ref32["vals"], b, 1e-5, 500)
+        assert info.status[0] == oco == oracle.CONVERGED
+        assert abs(info.iterations[0] - ito) <= 2
+        assert rel(host(x), xo) <= 1e-4
+        gb, gv, ainfo = A.adjoint_raw(x, dev(g), 1e-5, 500, method="bicgstab")
+        lam, gvo, ita, _, oca = oracle.bicgstab_adjoint(ref32["row_ptr"], ref32["col"],
+                                                        ref32["vals"], host(x), g, 1e-5, 500)
+        assert ainfo.status[0] == oca == oracle.CONVERGED
+        assert rel(host(gb), lam) <= 1e-4 and rel(host(gv), gvo) <= 1e-4
+
+
+def test_list_handle_is_refused():
+    from differentiable_sparse_linear_csr_amd import SparseTensorList
+    rp, cp, vp = poisson2d_coo(10)
+    L = SparseTensorList.from_coo_list([dev(rp, torch.int64)] * 2, [dev(cp, torch.int64)] * 2,
+                                       [dev(vp)] * 2, [100, 100])
+    with pytest.raises(SlaError) as e:
+        L.solve_raw(dev(np.ones(200)), 1e-8, 10, method="bicgstab")
+    assert e.value.status == _lib.SLA_ERR_INVALID_ARG
+    with pytest.raises(SlaError) as e:
+        L.adjoint_raw(dev(np.ones(200)), dev(np.ones(200)), 1e-8, 10, method="bicgstab")
+    assert e.value.status == _lib.SLA_ERR_INVALID_ARG
