@@ -702,29 +702,48 @@ __global__ __launch_bounds__(kBlock) void k_direction(int64_t n, int B, const T 
     }
 }
 
-// grad[b][k] = -lam[row(k)][b] * x[col(k)][b], one short-row tile per
-// workgroup (the row of each entry is recovered through LDS).
-template <typename T, typename RP>
+// grad[b][k] = sign * a[row(k)][b] * x[col(k)][b] over the short-row tiles:
+// one wavefront per tile (no workgroup barrier), wavefronts striding over the
+// tiles. The row of each entry comes from the tile's 16-bit row offsets
+// through a per-wavefront LDS table, and narrow tiles read 16-bit columns.
+template <typename T>
 __global__ __launch_bounds__(kBlock) void k_grad_tile(const TileDesc *__restrict__ tiles,
-                                                      const RP *__restrict__ row_ptr,
-                                                      const int32_t *__restrict__ col, int64_t nnz,
-                                                      int B, const T *__restrict__ lam,
+                                                      int64_t ntiles,
+                                                      const uint16_t *__restrict__ roff16,
+                                                      const int32_t *__restrict__ col,
+                                                      const uint16_t *__restrict__ col16,
+                                                      int64_t nnz, int B, const T *__restrict__ lam,
                                                       const T *__restrict__ x,
                                                       T *__restrict__ grad, double sign) {
-    __shared__ int32_t rowid[kTileCap];
-    const int tid = threadIdx.x;
-    const TileDesc d = tiles[blockIdx.x];
-    const int64_t nk = d.k1 - d.k0;
-    for (int32_t i = d.rs + tid; i < d.re; i += kBlock)
-        for (int64_t k = row_ptr[i]; k < (int64_t)row_ptr[i + 1]; ++k) rowid[k - d.k0] = i;
-    __syncthreads();
-    for (int b = 0; b < B; ++b) {
-        for (int64_t kk = tid; kk < nk; kk += kBlock) {
-            const int64_t i = rowid[kk];
-            const int64_t k = d.k0 + kk;
-            const double g = sign * ((double)lam[i * B + b] * (double)x[(int64_t)col[k] * B + b]);
-            grad[(int64_t)b * nnz + k] = (T)g;
+    __shared__ uint16_t rowid_all[kWaves][kTileCap];
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    uint16_t *rowid = rowid_all[wv];
+    const int64_t stride = (int64_t)gridDim.x * kWaves;
+    for (int64_t t = (int64_t)blockIdx.x * kWaves + wv; t < ntiles; t += stride) {
+        const TileDesc d = tiles[t];
+        const int nrows = d.re - d.rs;
+        const int nk = (int)(d.k1 - d.k0);
+        const uint16_t *rp = roff16 + d.rpos;
+        for (int j = lane; j < nrows; j += 64) {
+            const int a = rp[j], e = rp[j + 1];
+            for (int k = a; k < e; ++k) rowid[k] = (uint16_t)j;
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int kk = lane; kk < nk; kk += 64) {
+            const int64_t i = d.rs + rowid[kk];
+            const int64_t k = d.k0 + kk;
+            const int64_t c = d.narrow ? (int64_t)d.cbase + col16[k] : (int64_t)col[k];
+            for (int b = 0; b < B; ++b)
+                grad[(int64_t)b * nnz + k] =
+                    (T)(sign * ((double)lam[i * B + b] * (double)x[c * B + b]));
+        }
+        // the next tile's table is written after these reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -995,11 +1014,14 @@ void grad_vals(Handle &h, const void *lam_internal, const void *x_user, void *gr
     auto go = [&](auto ttag, auto rtag) {
         using T = decltype(ttag);
         using RP = decltype(rtag);
-        if (h.ntiles > 0)
-            hipLaunchKernelGGL((k_grad_tile<T, RP>), dim3((unsigned)h.ntiles), dim3(kBlock), 0, s,
-                               (const TileDesc *)h.tiles, (const RP *)h.row_ptr,
-                               (const int32_t *)h.col, h.nnz, h.B, (const T *)lam_internal,
-                               (const T *)x_int, (T *)grad, sign);
+        if (h.ntiles > 0) {
+            int64_t g = (h.ntiles + kWaves - 1) / kWaves;
+            if (g > 4 * kMaxGrid) g = 4 * kMaxGrid;
+            hipLaunchKernelGGL(k_grad_tile<T>, dim3((unsigned)g), dim3(kBlock), 0, s,
+                               (const TileDesc *)h.tiles, h.ntiles, (const uint16_t *)h.roff16,
+                               (const int32_t *)h.col, (const uint16_t *)h.col16, h.nnz, h.B,
+                               (const T *)lam_internal, (const T *)x_int, (T *)grad, sign);
+        }
         if (h.nlong > 0)
             hipLaunchKernelGGL((k_grad_long<T, RP>), dim3((unsigned)h.nlong), dim3(kBlock), 0, s,
                                (const int32_t *)h.long_rows, (const RP *)h.row_ptr,
