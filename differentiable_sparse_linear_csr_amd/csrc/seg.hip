@@ -47,6 +47,39 @@ __device__ __forceinline__ Range seg_range(const Seg &g) {
     return q;
 }
 
+// A workgroup's rows as 16-byte groups of W rows ([g0, g1), W-aligned in
+// absolute row numbers) plus the fewer than W rows before and after them,
+// done one per lane
+struct VecRows {
+    int64_t g0, g1;   // groups
+    int64_t h0, h1;   // head rows
+    int64_t t0, t1;   // tail rows
+};
+
+template <int W>
+__device__ __forceinline__ VecRows vec_rows(const Range &q) {
+    int64_t a0 = (q.r0 + W - 1) / W * W;
+    if (a0 > q.r1) a0 = q.r1;
+    int64_t a1 = q.r1 / W * W;
+    if (a1 < a0) a1 = a0;
+    return VecRows{a0 / W, a1 / W, q.r0, a0, a1, q.r1};
+}
+
+// the single row a lane takes outside the groups (head rows on lanes 0..,
+// tail rows on lanes 64..), or -1
+__device__ __forceinline__ int64_t edge_row(const VecRows &v) {
+    const int t = threadIdx.x;
+    if (t < v.h1 - v.h0) return v.h0 + t;
+    if (t >= 64 && t - 64 < v.t1 - v.t0) return v.t0 + (t - 64);
+    return -1;
+}
+
+// 16-byte groups per lane that cover a workgroup's kSegBlockRows rows
+template <typename T>
+constexpr int seg_groups() {
+    return (int)((kSegBlockRows / VecW<T>::W + kBlock - 1) / kBlock);
+}
+
 // Stores this workgroup's C partials and arrives at its segment's counter;
 // true in the segment's last workgroup, which then holds the segment totals
 // in tot[0..C) (partials summed in workgroup order by a fixed tree).
@@ -117,12 +150,28 @@ __global__ __launch_bounds__(kBlock) void k_seg_dot(Seg g, const T *__restrict__
     if (ctl->n_running == 0) return;
     const Range q = seg_range(g);
     if (st[q.s].status != kRunning) return;
+    constexpr int W = VecW<T>::W, G = seg_groups<T>();
+    const VecRows vr = vec_rows<W>(q);
     double spq = 0.0;
+    T pv[G][W], qq[G][W];
 #pragma unroll
-    for (int u = 0; u < kSegRows; ++u) {
-        const int64_t i = q.r0 + threadIdx.x + (int64_t)u * kBlock;
-        if (i < q.r1) spq += (double)p[i] * (double)qv[i];
+    for (int u = 0; u < G; ++u) {
+        const int64_t gi = vr.g0 + u * kBlock + threadIdx.x;
+        if (gi < vr.g1) {
+            vload(p + gi * W, pv[u]);
+            vload(qv + gi * W, qq[u]);
+        }
     }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+        const int64_t gi = vr.g0 + u * kBlock + threadIdx.x;
+        if (gi < vr.g1) {
+#pragma unroll
+            for (int k = 0; k < W; ++k) spq += (double)pv[u][k] * (double)qq[u][k];
+        }
+    }
+    const int64_t ie = edge_row(vr);
+    if (ie >= 0) spq += (double)p[ie] * (double)qv[ie];
     const double v[1] = {block_sum(spq, lds4)};
     if (seg_reduce<1>(g, q, v, lds4, tot) && threadIdx.x == 0) {
         SysState &s = st[q.s];
@@ -151,18 +200,43 @@ __global__ __launch_bounds__(kBlock) void k_seg_update(Seg g, T *__restrict__ x,
     if (st[q.s].status != kRunning) return;
     const double alpha = st[q.s].alpha;
     double srz = 0.0, srr = 0.0;
+    auto row = [&](T &xe, T &re, T pe, T qe, T de) {
+        xe = (T)((double)xe + alpha * (double)pe);
+        re = (T)((double)re - alpha * (double)qe);
+        const double z = (double)de * (double)re;
+        srz += (double)re * z;
+        srr += (double)re * (double)re;
+    };
+    constexpr int W = VecW<T>::W, G = seg_groups<T>();
+    const VecRows vr = vec_rows<W>(q);
+    T xv[G][W], rv[G][W], pv[G][W], qq[G][W], dv[G][W];
 #pragma unroll
-    for (int u = 0; u < kSegRows; ++u) {
-        const int64_t i = q.r0 + threadIdx.x + (int64_t)u * kBlock;
-        if (i < q.r1) {
-            const T xn = (T)((double)x[i] + alpha * (double)p[i]);
-            const T rn = (T)((double)r[i] - alpha * (double)qv[i]);
-            x[i] = xn;
-            r[i] = rn;
-            const double z = (double)dinv[i] * (double)rn;
-            srz += (double)rn * z;
-            srr += (double)rn * (double)rn;
+    for (int u = 0; u < G; ++u) {
+        const int64_t gi = vr.g0 + u * kBlock + threadIdx.x;
+        if (gi < vr.g1) {
+            vload(x + gi * W, xv[u]);
+            vload(r + gi * W, rv[u]);
+            vload(p + gi * W, pv[u]);
+            vload(qv + gi * W, qq[u]);
+            vload(dinv + gi * W, dv[u]);
         }
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+        const int64_t gi = vr.g0 + u * kBlock + threadIdx.x;
+        if (gi < vr.g1) {
+#pragma unroll
+            for (int k = 0; k < W; ++k) row(xv[u][k], rv[u][k], pv[u][k], qq[u][k], dv[u][k]);
+            vstore(x + gi * W, xv[u]);
+            vstore(r + gi * W, rv[u]);
+        }
+    }
+    const int64_t ie = edge_row(vr);
+    if (ie >= 0) {
+        T xe = x[ie], re = r[ie];
+        row(xe, re, p[ie], qv[ie], dinv[ie]);
+        x[ie] = xe;
+        r[ie] = re;
     }
     const double v[2] = {block_sum(srz, lds4), block_sum(srr, lds4)};
     if (seg_reduce<2>(g, q, v, lds4, tot) && threadIdx.x == 0) {
@@ -197,11 +271,30 @@ __global__ __launch_bounds__(kBlock) void k_seg_direction(Seg g, const T *__rest
     const Range q = seg_range(g);
     if (st[q.s].status != kRunning) return;
     const double beta = st[q.s].beta;
+    constexpr int W = VecW<T>::W, G = seg_groups<T>();
+    const VecRows vr = vec_rows<W>(q);
+    T rv[G][W], pv[G][W], dv[G][W];
 #pragma unroll
-    for (int u = 0; u < kSegRows; ++u) {
-        const int64_t i = q.r0 + threadIdx.x + (int64_t)u * kBlock;
-        if (i < q.r1) p[i] = (T)((double)dinv[i] * (double)r[i] + beta * (double)p[i]);
+    for (int u = 0; u < G; ++u) {
+        const int64_t gi = vr.g0 + u * kBlock + threadIdx.x;
+        if (gi < vr.g1) {
+            vload(r + gi * W, rv[u]);
+            vload(p + gi * W, pv[u]);
+            vload(dinv + gi * W, dv[u]);
+        }
     }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+        const int64_t gi = vr.g0 + u * kBlock + threadIdx.x;
+        if (gi < vr.g1) {
+#pragma unroll
+            for (int k = 0; k < W; ++k)
+                pv[u][k] = (T)((double)dv[u][k] * (double)rv[u][k] + beta * (double)pv[u][k]);
+            vstore(p + gi * W, pv[u]);
+        }
+    }
+    const int64_t ie = edge_row(vr);
+    if (ie >= 0) p[ie] = (T)((double)dinv[ie] * (double)r[ie] + beta * (double)p[ie]);
 }
 
 // every entry (i, j) must lie in row i's segment block
