@@ -188,7 +188,7 @@ sla_status create_impl(sla_csr *out, sla_format fmt, int64_t n, int64_t nnz_in, 
             build_from_coo(*h, row_itype, rows_or_row_ptr, col_itype, cols, values, s);
         else
             build_from_csr(*h, row_itype, rows_or_row_ptr, col_itype, cols, values, s);
-        build_tiles(*h, s);
+        build_tiles(*h, s, nseg > 0 ? seg_rows : nullptr, nseg);
         init_launch_limits(*h);
         init_vector_limits(*h);
         if (nseg > 0) build_segments(*h, seg_rows, nseg, s);

@@ -525,7 +525,15 @@ __global__ __launch_bounds__(kBlock) void k_tile_compress(TileDesc *__restrict__
     }
 }
 
-void build_tiles(Handle &h, hipStream_t s) {
+template <typename RP>
+__global__ __launch_bounds__(kBlock) void k_gather_rp(const RP *__restrict__ row_ptr,
+                                                      const int64_t *__restrict__ rows, int64_t m,
+                                                      int64_t *__restrict__ out) {
+    const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (j < m) out[j] = (int64_t)row_ptr[rows[j]];
+}
+
+void build_tiles(Handle &h, hipStream_t s, const int64_t *seg_rows, int32_t nseg) {
     const int64_t n = h.n;
     Scratch sc(s);
     int64_t *flag = sc.get<int64_t>(n);
@@ -559,12 +567,29 @@ void build_tiles(Handle &h, hipStream_t s) {
     SLA_HIP(hipMemcpyAsync(hs.data(), tstart, (size_t)(nt + 1) * 4, hipMemcpyDeviceToHost, s));
     SLA_HIP(hipMemcpyAsync(hk.data(), tk0, (size_t)(nt + 1) * 8, hipMemcpyDeviceToHost, s));
     SLA_HIP(hipStreamSynchronize(s));
+    // row_ptr at the member boundaries (segmented handles)
+    std::vector<int64_t> bk((size_t)(nseg > 0 ? nseg + 1 : 0));
+    if (nseg > 0) {
+        int64_t *drows = sc.get<int64_t>(nseg + 1);
+        int64_t *dk = sc.get<int64_t>(nseg + 1);
+        SLA_HIP(hipMemcpyAsync(drows, seg_rows, 8 * (size_t)(nseg + 1), hipMemcpyHostToDevice, s));
+        const unsigned gg = (unsigned)((nseg + 1 + kBlock - 1) / kBlock);
+        if (h.rp64)
+            hipLaunchKernelGGL(k_gather_rp<int64_t>, dim3(gg), dim3(kBlock), 0, s,
+                               (const int64_t *)h.row_ptr, drows, (int64_t)nseg + 1, dk);
+        else
+            hipLaunchKernelGGL(k_gather_rp<int32_t>, dim3(gg), dim3(kBlock), 0, s,
+                               (const int32_t *)h.row_ptr, drows, (int64_t)nseg + 1, dk);
+        SLA_HIP(hipGetLastError());
+        SLA_HIP(hipMemcpyAsync(bk.data(), dk, 8 * (size_t)(nseg + 1), hipMemcpyDeviceToHost, s));
+    }
+    SLA_HIP(hipStreamSynchronize(s));
     std::vector<TileDesc> shorts;
     std::vector<int32_t> longs;
     shorts.reserve((size_t)nt);
     int64_t rpos = 0;
-    for (int64_t t = 0; t < nt; ++t) {
-        TileDesc d{hs[t], hs[t + 1], hk[t], hk[t + 1], 0, 0, 0};
+    auto add = [&](const TileDesc &e) {
+        TileDesc d = e;
         if (d.re - d.rs == 1 && d.k1 - d.k0 > kLongRow) {
             longs.push_back(d.rs);
         } else {
@@ -572,9 +597,45 @@ void build_tiles(Handle &h, hipStream_t s) {
             rpos += d.re - d.rs + 1;
             shorts.push_back(d);
         }
+    };
+    int32_t nb = 1;  // next member boundary to look at
+    for (int64_t t = 0; t < nt; ++t) {
+        TileDesc d{hs[t], hs[t + 1], hk[t], hk[t + 1], 0, 0, 0};
+        // a tile that spans member boundaries becomes one piece per member
+        while (nb < nseg && seg_rows[nb] <= d.rs) ++nb;
+        while (nb < nseg && seg_rows[nb] < d.re) {
+            const int32_t b = (int32_t)seg_rows[nb];
+            add(TileDesc{d.rs, b, d.k0, bk[(size_t)nb], 0, 0, 0});
+            d.rs = b;
+            d.k0 = bk[(size_t)nb];
+            ++nb;
+        }
+        add(d);
     }
     h.ntiles = (int64_t)shorts.size();
     h.nlong = (int64_t)longs.size();
+    if (nseg > 0) {
+        // each member's first tile and first long row (both lists in row order)
+        std::vector<int64_t> t0((size_t)nseg + 1), l0((size_t)nseg + 1);
+        size_t it = 0, il = 0;
+        for (int32_t q = 0; q <= nseg; ++q) {
+            const int64_t r = seg_rows[q];
+            while (it < shorts.size() && shorts[it].rs < r) ++it;
+            while (il < longs.size() && longs[il] < r) ++il;
+            t0[(size_t)q] = (int64_t)it;
+            l0[(size_t)q] = (int64_t)il;
+        }
+        h.seg_tile0 = (int64_t *)dalloc(h, 8 * ((size_t)nseg + 1));
+        h.seg_long0 = (int64_t *)dalloc(h, 8 * ((size_t)nseg + 1));
+        h.tile_live = (uint8_t *)dalloc(h, shorts.size() + 1);
+        h.tile_dot = (double *)dalloc(h, sizeof(double) * (shorts.size() + 1));
+        SLA_HIP(hipMemcpyAsync(h.seg_tile0, t0.data(), 8 * ((size_t)nseg + 1), hipMemcpyHostToDevice,
+                               s));
+        SLA_HIP(hipMemcpyAsync(h.seg_long0, l0.data(), 8 * ((size_t)nseg + 1), hipMemcpyHostToDevice,
+                               s));
+        SLA_HIP(hipMemsetAsync(h.tile_live, 1, shorts.size() + 1, s));
+        SLA_HIP(hipStreamSynchronize(s));
+    }
     h.tiles = (TileDesc *)dalloc(h, sizeof(TileDesc) * (shorts.size() + 1));
     h.long_rows = (int32_t *)dalloc(h, sizeof(int32_t) * (longs.size() + 1));
     h.long_dot = (double *)dalloc(h, sizeof(double) * 2 * (longs.size() + 1));  // two dots

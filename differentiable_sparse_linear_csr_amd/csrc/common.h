@@ -191,6 +191,13 @@ struct Handle {
     int64_t seg_grid = 0;
     uint32_t *seg_sync = nullptr; // [nseg] arrival counters (one line each)
     double *seg_part = nullptr;   // [2 * seg_grid] workgroup partials
+    // SpMV tiles of a segmented handle never straddle two members: the tiles
+    // and long rows of member q are [seg_tile0[q], seg_tile0[q+1]) and
+    // [seg_long0[q], seg_long0[q+1]); the solve's SpMV skips tiles whose
+    // member has finished (tile_live 0) and leaves each tile's p.q in tile_dot
+    int64_t *seg_tile0 = nullptr, *seg_long0 = nullptr;
+    uint8_t *tile_live = nullptr;
+    double *tile_dot = nullptr;
     // A^T for the backward of y = A x (built at the first backward)
     Handle *tr = nullptr;
     int64_t *tr_map = nullptr;    // [nnz]: A^T CSR position -> this CSR position
@@ -234,7 +241,8 @@ void build_from_coo(Handle &h, sla_itype rit, const void *rows, sla_itype cit, c
 void build_from_csr(Handle &h, sla_itype rit, const void *row_ptr, sla_itype cit, const void *cols,
                     const void *values, hipStream_t s);
 void load_values(Handle &h, const void *values, hipStream_t s);
-void build_tiles(Handle &h, hipStream_t s);
+// seg_rows (host, [nseg+1]) splits tiles at member boundaries (nseg = 0: none)
+void build_tiles(Handle &h, hipStream_t s, const int64_t *seg_rows = nullptr, int32_t nseg = 0);
 void compute_dinv(Handle &h, hipStream_t s);       // sets h.diag_ok (synchronizes)
 bool check_symmetric(Handle &h, hipStream_t s);    // synchronizes
 void gather_to_input(Handle &h, const void *in, void *out, hipStream_t s);

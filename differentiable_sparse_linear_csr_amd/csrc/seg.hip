@@ -18,6 +18,9 @@
 
 namespace sla {
 
+void launch_spmv_dots(Handle &h, const void *x, void *y, const void *w, int ndot, double *spart,
+                      const int32_t *status, hipStream_t s);
+
 namespace {
 
 constexpr int kSegRows = 4;                          // rows per lane
@@ -29,7 +32,17 @@ struct Seg {
     const int64_t *blk0;   // [nseg+1] first workgroup of each segment
     double *part;          // [2 * grid]
     uint32_t *sync;        // [nseg * kCounterStride]
+    const int64_t *tile0;  // [nseg+1] first SpMV tile of each segment
+    const int64_t *long0;  // [nseg+1] first long row of each segment
+    uint8_t *live;         // [ntiles] 1 while the tile's segment runs
+    const double *tdot;    // [ntiles] p.q of each tile (from the SpMV)
+    const double *ldot;    // [nlong] p.q of each long row
 };
+
+// mark the tiles of segment s live or not (every thread of the calling block)
+__device__ __forceinline__ void set_live(const Seg &g, int32_t s, uint8_t v) {
+    for (int64_t t = g.tile0[s] + threadIdx.x; t < g.tile0[s + 1]; t += kBlock) g.live[t] = v;
+}
 
 struct Range {
     int32_t s;
@@ -123,7 +136,7 @@ __global__ __launch_bounds__(kBlock) void k_seg_init(Seg g, const T *__restrict_
         }
     }
     const double v[2] = {block_sum(sbb, lds4), block_sum(srz, lds4)};
-    if (seg_reduce<2>(g, q, v, lds4, tot) && threadIdx.x == 0) {
+    if (seg_reduce<2>(g, q, v, lds4, tot)) {
         SysState s;
         s.bb = tot[0];
         s.rho = tot[1];
@@ -134,54 +147,10 @@ __global__ __launch_bounds__(kBlock) void k_seg_init(Seg g, const T *__restrict_
         if (s.bb == 0.0) s.status = SLA_CONVERGED;
         else if (ctl->maxit <= 0) s.status = SLA_MAXIT;
         else s.status = kRunning;
-        st[q.s] = s;
-        if (s.status == kRunning) atomicAdd(&ctl->n_running, 1);
-    }
-}
-
-// sigma = p.q per segment (q from the SpMV), then alpha or a breakdown
-template <typename T>
-__global__ __launch_bounds__(kBlock) void k_seg_dot(Seg g, const T *__restrict__ p,
-                                                    const T *__restrict__ qv,
-                                                    Ctl *__restrict__ ctl,
-                                                    SysState *__restrict__ st) {
-    __shared__ double lds4[kWaves];
-    __shared__ double tot[1];
-    if (ctl->n_running == 0) return;
-    const Range q = seg_range(g);
-    if (st[q.s].status != kRunning) return;
-    constexpr int W = VecW<T>::W, G = seg_groups<T>();
-    const VecRows vr = vec_rows<W>(q);
-    double spq = 0.0;
-    T pv[G][W], qq[G][W];
-#pragma unroll
-    for (int u = 0; u < G; ++u) {
-        const int64_t gi = vr.g0 + u * kBlock + threadIdx.x;
-        if (gi < vr.g1) {
-            vload(p + gi * W, pv[u]);
-            vload(qv + gi * W, qq[u]);
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < G; ++u) {
-        const int64_t gi = vr.g0 + u * kBlock + threadIdx.x;
-        if (gi < vr.g1) {
-#pragma unroll
-            for (int k = 0; k < W; ++k) spq += (double)pv[u][k] * (double)qq[u][k];
-        }
-    }
-    const int64_t ie = edge_row(vr);
-    if (ie >= 0) spq += (double)p[ie] * (double)qv[ie];
-    const double v[1] = {block_sum(spq, lds4)};
-    if (seg_reduce<1>(g, q, v, lds4, tot) && threadIdx.x == 0) {
-        SysState &s = st[q.s];
-        const double sigma = tot[0];
-        if (!(sigma > 0.0) || !isfinite(sigma)) {
-            s.status = SLA_BREAKDOWN;
-            s.iter += 1;
-            atomicSub(&ctl->n_running, 1);
-        } else {
-            s.alpha = s.rho / sigma;
+        set_live(g, q.s, s.status == kRunning ? 1 : 0);
+        if (threadIdx.x == 0) {
+            st[q.s] = s;
+            if (s.status == kRunning) atomicAdd(&ctl->n_running, 1);
         }
     }
 }
@@ -198,7 +167,23 @@ __global__ __launch_bounds__(kBlock) void k_seg_update(Seg g, T *__restrict__ x,
     if (ctl->n_running == 0) return;
     const Range q = seg_range(g);
     if (st[q.s].status != kRunning) return;
-    const double alpha = st[q.s].alpha;
+    // sigma = p.q of the segment from the SpMV's per-tile and per-long-row
+    // partials, summed in one fixed order by every workgroup of the segment
+    double sg = 0.0;
+    {
+        const int64_t t1 = g.tile0[q.s + 1];
+        for (int64_t t = g.tile0[q.s] + threadIdx.x; t < t1; t += 8 * kBlock) {
+            double v8[8];   // 8 loads in flight per lane
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v8[u] = t + u * kBlock < t1 ? g.tdot[t + u * kBlock] : 0.0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) sg += v8[u];
+        }
+    }
+    for (int64_t l = g.long0[q.s] + threadIdx.x; l < g.long0[q.s + 1]; l += kBlock) sg += g.ldot[l];
+    const double sigma = block_sum(sg, lds4);
+    const bool breakdown = !(sigma > 0.0) || !isfinite(sigma);
+    const double alpha = breakdown ? 0.0 : st[q.s].rho / sigma;
     double srz = 0.0, srr = 0.0;
     auto row = [&](T &xe, T &re, T pe, T qe, T de) {
         xe = (T)((double)xe + alpha * (double)pe);
@@ -208,7 +193,8 @@ __global__ __launch_bounds__(kBlock) void k_seg_update(Seg g, T *__restrict__ x,
         srr += (double)re * (double)re;
     };
     constexpr int W = VecW<T>::W, G = seg_groups<T>();
-    const VecRows vr = vec_rows<W>(q);
+    VecRows vr = vec_rows<W>(q);
+    if (breakdown) vr = VecRows{0, 0, 0, 0, 0, 0};   // x and r stay as they are
     T xv[G][W], rv[G][W], pv[G][W], qq[G][W], dv[G][W];
 #pragma unroll
     for (int u = 0; u < G; ++u) {
@@ -239,20 +225,28 @@ __global__ __launch_bounds__(kBlock) void k_seg_update(Seg g, T *__restrict__ x,
         r[ie] = re;
     }
     const double v[2] = {block_sum(srz, lds4), block_sum(srr, lds4)};
-    if (seg_reduce<2>(g, q, v, lds4, tot) && threadIdx.x == 0) {
-        SysState &s = st[q.s];
+    if (seg_reduce<2>(g, q, v, lds4, tot)) {
+        // every thread takes the same decision; thread 0 records it
         const double rz = tot[0], rr = tot[1];
-        s.rr = rr;
-        s.iter += 1;
-        if (sqrt(rr) <= ctl->tol * sqrt(s.bb)) {
-            s.status = SLA_CONVERGED;
-            atomicSub(&ctl->n_running, 1);
-        } else if (s.iter >= ctl->maxit) {
-            s.status = SLA_MAXIT;
-            atomicSub(&ctl->n_running, 1);
-        } else {
-            s.beta = rz / s.rho;
-            s.rho = rz;
+        const SysState s0 = st[q.s];
+        const int32_t iter = s0.iter + 1;
+        int32_t status = kRunning;
+        if (breakdown) status = SLA_BREAKDOWN;   // rr keeps the last residual
+        else if (sqrt(rr) <= ctl->tol * sqrt(s0.bb)) status = SLA_CONVERGED;
+        else if (iter >= ctl->maxit) status = SLA_MAXIT;
+        if (status != kRunning) set_live(g, q.s, 0);
+        if (threadIdx.x == 0) {
+            SysState &s = st[q.s];
+            s.iter = iter;
+            s.alpha = alpha;
+            if (!breakdown) s.rr = rr;
+            s.status = status;
+            if (status != kRunning) {
+                atomicSub(&ctl->n_running, 1);
+            } else {
+                s.beta = rz / s.rho;
+                s.rho = rz;
+            }
         }
     }
 }
@@ -313,7 +307,8 @@ __global__ __launch_bounds__(kBlock) void k_seg_check(const RP *__restrict__ row
 }
 
 Seg seg_of(Handle &h) {
-    return Seg{h.seg_rows, h.blk_seg, h.seg_blk0, h.seg_part, h.seg_sync};
+    return Seg{h.seg_rows,  h.blk_seg,   h.seg_blk0, h.seg_part, h.seg_sync,
+               h.seg_tile0, h.seg_long0, h.tile_live, h.tile_dot, h.long_dot};
 }
 
 template <typename T>
@@ -322,9 +317,8 @@ void seg_iter_t(Handle &h, hipStream_t s, Launcher *lp) {
     const dim3 grid((unsigned)h.seg_grid), blk(kBlock);
     hipEvent_t a = nullptr;
     if (lp) lp->begin(SLA_KERNEL_SPMV_DOT, &a);
-    launch_spmv_plain(h, h.p, h.q, s);
-    hipLaunchKernelGGL(k_seg_dot<T>, grid, blk, 0, s, g, (const T *)h.p, (const T *)h.q, h.ctl, h.st);
-    SLA_HIP(hipGetLastError());
+    // q = A p over the live tiles, p.q per tile and long row
+    launch_spmv_dots(h, h.p, h.q, h.p, 3, nullptr, nullptr, s);
     if (lp) lp->end(SLA_KERNEL_SPMV_DOT, a);
     if (lp) lp->begin(SLA_KERNEL_UPDATE, &a);
     hipLaunchKernelGGL(k_seg_update<T>, grid, blk, 0, s, g, (T *)h.x, (T *)h.r, (const T *)h.p,

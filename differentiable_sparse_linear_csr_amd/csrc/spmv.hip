@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kBlock) void k_spmv_long(
     T *__restrict__ y, const T *__restrict__ w, double *__restrict__ long_dot,
     const int32_t *__restrict__ status) {
     __shared__ double lds4[kWaves];
-    if (DOT > 0 && *status != kRunning) return;
+    if (DOT > 0 && DOT != 3 && *status != kRunning) return;
     const int tid = threadIdx.x;
     const int64_t i = long_rows[blockIdx.x];
     const int64_t k0 = row_ptr[i], len = (int64_t)row_ptr[i + 1] - k0;
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kBlock) void k_spmv_long(
         const T q = (T)s;
         y[i] = q;
         if (DOT > 0) long_dot[blockIdx.x] = (double)w[i] * (double)q;
-        if (DOT > 1) long_dot[nlong + blockIdx.x] = (double)q * (double)q;
+        if (DOT == 2) long_dot[nlong + blockIdx.x] = (double)q * (double)q;
     }
 }
 
@@ -88,19 +88,25 @@ __global__ __launch_bounds__(kBlock) void k_spmv_long(
 // it adds w.q of its rows, and of the long rows in a fixed order, to a
 // per-workgroup partial spart[DOT * block], and with DOT = 2 also q.q to
 // spart[2 * block + 1]; the fused forms do nothing unless *status is running.
+//
+// DOT = 3 is the form of a list of systems (segmented handle, tiles never
+// straddle two members): tiles whose member has finished (live[t] = 0) are
+// skipped, and each tile's w.q goes to tile_dot[t] for its member's update.
 template <typename T, typename RP, int DOT, bool NARROW>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void k_spmv_tile(
     const TileDesc *__restrict__ tiles, int64_t ntiles, const uint16_t *__restrict__ roff16,
     const int32_t *__restrict__ col, const uint16_t *__restrict__ col16, const T *__restrict__ val,
     const T *__restrict__ x, T *__restrict__ y, const T *__restrict__ w,
     const double *__restrict__ long_dot, int64_t nlong, double *__restrict__ spart,
-    const int32_t *__restrict__ status) {
+    const int32_t *__restrict__ status, const uint8_t *__restrict__ live,
+    double *__restrict__ tile_dot) {
     constexpr bool FUSED = DOT > 0;
+    constexpr bool PERTILE = DOT == 3;
     __shared__ double prod_all[kWaves][kTileCap];
     __shared__ int32_t roff_all[kWaves][kTileUnits + 1];
     __shared__ double pown_all[FUSED ? kWaves : 1][FUSED ? kTileUnits : 1];
     __shared__ double lds4[kWaves];
-    if (FUSED && *status != kRunning) return;
+    if (FUSED && !PERTILE && *status != kRunning) return;
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
@@ -174,12 +180,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
             ro[u] = j <= nr ? (int32_t)rp[j] : 0;
         }
     };
+    // first live tile at or after u in this wavefront's sequence
+    auto next_live = [&](int64_t u) {
+        if (PERTILE)
+            while (u < t_end && !live[u]) u += waves_per_xcd;
+        return u;
+    };
+    t = next_live(t);
     if (t < t_end) {
         d = tiles[t];
         fetch(d);
     }
     while (t < t_end) {
-        const int64_t tn = t + waves_per_xcd;
+        const int64_t tn = next_live(t + waves_per_xcd);
         TileDesc dn{0, 0, 0, 0, 0, 0, 0};
         if (tn < t_end) dn = tiles[tn];
         const int nrows = d.re - d.rs;
@@ -231,8 +244,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
                 const T q = (T)s;
                 y[d.rs + i] = q;
                 if (FUSED) dot += pown[i] * (double)q;
-                if (DOT > 1) dot2 += (double)q * (double)q;
+                if (DOT == 2) dot2 += (double)q * (double)q;
             }
+        }
+        if (PERTILE) {
+            // the tile's w.q (lanes summed by a fixed tree) for its member
+            const double td = wave_sum(dot);
+            if (lane == 0) tile_dot[t] = td;
+            dot = 0.0;
         }
         // this wavefront's next stores to its LDS slice come after these reads
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -241,20 +260,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
         t = tn;
         d = dn;
     }
-    if (FUSED) {
+    if (FUSED && !PERTILE) {
         // this workgroup's partials; the next kernel sums them (every
         // workgroup there, in block order) and forms its step, so this
         // kernel ends without a grid-wide arrival
         for (int64_t l = blockIdx.x + (int64_t)threadIdx.x * gridDim.x; l < nlong;
              l += (int64_t)kBlock * gridDim.x) {
             dot += long_dot[l];
-            if (DOT > 1) dot2 += long_dot[nlong + l];
+            if (DOT == 2) dot2 += long_dot[nlong + l];
         }
         dot = block_sum(dot, lds4);
-        if (DOT > 1) dot2 = block_sum(dot2, lds4);
+        if (DOT == 2) dot2 = block_sum(dot2, lds4);
         if (threadIdx.x == 0) {
             spart[(int64_t)DOT * blockIdx.x] = dot;
-            if (DOT > 1) spart[2 * (int64_t)blockIdx.x + 1] = dot2;
+            if (DOT == 2) spart[2 * (int64_t)blockIdx.x + 1] = dot2;
         }
     }
 }
@@ -478,7 +497,8 @@ void launch_tiles(Handle &h, const void *x, void *y, const void *w, double *spar
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBlock), 0, s, (const TileDesc *)h.tiles,
                        h.ntiles, (const uint16_t *)h.roff16, (const int32_t *)h.col,
                        (const uint16_t *)h.col16, (const T *)h.vals, (const T *)x, (T *)y,
-                       (const T *)w, (const double *)h.long_dot, h.nlong, spart, status);
+                       (const T *)w, (const double *)h.long_dot, h.nlong, spart, status,
+                       (const uint8_t *)h.tile_live, h.tile_dot);
 }
 
 template <typename T, typename RP, bool FUSED>
@@ -586,7 +606,9 @@ void launch_spmv_plain(Handle &h, const void *x, void *y, hipStream_t s) {
 // Single system: y = A x with ndot (0, 1 or 2) inner products fused: w.y into
 // spart[ndot * block] and, for ndot = 2, y.y into spart[2 * block + 1], one
 // partial per workgroup of spmv_grid(h); skipped unless *status is running
-// (ndot > 0). spart holds ndot * spmv_grid(h) doubles.
+// (ndot > 0). spart holds ndot * spmv_grid(h) doubles. ndot = 3: segmented
+// handle, w.y per tile into h.tile_dot (and per long row into h.long_dot),
+// tiles with h.tile_live[t] = 0 skipped; status and spart unused.
 void launch_spmv_dots(Handle &h, const void *x, void *y, const void *w, int ndot, double *spart,
                       const int32_t *status, hipStream_t s) {
     auto go = [&](auto ttag, auto rtag) {
@@ -594,7 +616,8 @@ void launch_spmv_dots(Handle &h, const void *x, void *y, const void *w, int ndot
         using RP = decltype(rtag);
         if (ndot == 0) launch_tiles<T, RP, 0>(h, x, y, w, spart, status, s);
         else if (ndot == 1) launch_tiles<T, RP, 1>(h, x, y, w, spart, status, s);
-        else launch_tiles<T, RP, 2>(h, x, y, w, spart, status, s);
+        else if (ndot == 2) launch_tiles<T, RP, 2>(h, x, y, w, spart, status, s);
+        else launch_tiles<T, RP, 3>(h, x, y, w, spart, status, s);
     };
     if (h.vt == SLA_F64) {
         if (h.rp64) go(double(), int64_t());
