@@ -14,8 +14,8 @@ Printed as one JSON line. `roofline` covers the dominant kernel: its
 algorithmic bytes per launch over its average launch duration, measured with
 hipEvents on the stream it is launched on after the timed steps:
   - single system, per-step kernels: the SpMV tile kernel, 50 back-to-back
-    sla_spmv launches between one event pair (the solve runs its fused form,
-    which adds the p.q partials);
+    sla_spmv launches between one event pair, the median of three such
+    batches (the solve runs its fused form, which adds the p.q partials);
   - single system solved by the one-kernel path: that kernel, one launch per
     solve, per-launch events (whole solves of milliseconds);
   - batch, or a matrix the library reordered for locality (sla_spmv then
@@ -319,13 +319,16 @@ def main() -> int:
     y = A.matvec(b)
     reps = 50
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(reps):
-        A.matvec(b)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    b2b_ms = e0.elapsed_time(e1) / reps
+    batches = []
+    for _ in range(3):   # the median of three batches (a batch now and then runs slow)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            A.matvec(b)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        batches.append(e0.elapsed_time(e1) / reps)
+    b2b_ms = sorted(batches)[1]
     # the matvec backward (A^T g and the value gradient), timed the same way;
     # the first call builds A^T's pattern (on the host), outside the timed
     # region; skipped for very large matrices, where that build takes minutes
@@ -380,7 +383,7 @@ def main() -> int:
         # iterations: one direction-kernel launch each (two SpMVs in BiCGStab)
         n_it = max(prof["direction"][0] if method == "bicgstab" else prof["spmv_dot"][0], 1)
         per_iter_ms = sum(prof[k][1] for k in ("spmv_dot", "update", "direction")) / n_it
-        kernel = "k_spmv_tile (q = A p; 50 back-to-back sla_spmv launches)"
+        kernel = "k_spmv_tile (q = A p; 50 back-to-back sla_spmv launches, median of 3 batches)"
     else:
         # batched, or reordered: sla_spmv also transposes or permutes x and y,
         # so the fused SpMV of the solve is timed per launch (events around
