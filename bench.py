@@ -355,7 +355,7 @@ def main() -> int:
         # SpMVs 3 + 3, half 5, update 8)
         mat = ab["iter_3k"] - 13 * V * w.n * w.batch
         bicg_iter = 2 * mat + 25 * V * w.n * w.batch
-        job_bps = {"iter_3k": bicg_iter * value, "iter_min": bicg_iter * value}
+        job_bps = {"iter_3k": bicg_iter / w.batch * value, "iter_min": bicg_iter / w.batch * value}
     elif "seg_rows" in w.extra:
         seg = w.extra["seg_rows"]
         seg_nnz = np.bincount(np.searchsorted(seg, w.rows, side="right") - 1,
@@ -364,7 +364,9 @@ def main() -> int:
                            for q, i in enumerate(its)) for k in ("iter_3k", "iter_min")}
         job_bps = {k: v * args.steps / elapsed for k, v in per_step.items()}
     else:
-        job_bps = {k: ab[k] * value for k in ("iter_3k", "iter_min")}
+        # value counts system-iterations; one batched iteration moves ab[k]
+        # for all B systems
+        job_bps = {k: ab[k] / w.batch * value for k in ("iter_3k", "iter_min")}
     res_launches, res_ms = prof["cg_resident"]
     if res_launches > 0:
         # whole solves in one cooperative kernel: per iteration the matrix, the
