@@ -57,9 +57,50 @@ def csr_of(w):
     return ref["row_ptr"], ref["col"], ref["vals"]
 
 
+def list_members(w):
+    """(row range, CSR, b, g) of each member of a list workload"""
+    seg = w.extra["seg_rows"]
+    out = []
+    for q in range(len(seg) - 1):
+        sel = (w.rows >= seg[q]) & (w.rows < seg[q + 1])
+        ref = oracle.coo_to_csr(seg[q + 1] - seg[q], w.rows[sel] - seg[q], w.cols[sel] - seg[q],
+                                w.vals[sel])
+        out.append(((seg[q], seg[q + 1]), ref, w.b[seg[q]:seg[q + 1]], w.g[seg[q]:seg[q + 1]]))
+    return out
+
+
+def main_list(name):
+    """A list of systems: every member solved alone (forward and adjoint)."""
+    t0 = time.time()
+    w = make_workload(name)
+    rec = {"workload": name, "n": w.n, "nnz": int(w.nnz), "members": len(w.extra["seg_rows"]) - 1,
+           "dtype": w.dtype, "tol": w.tol, "maxit": w.maxit,
+           "written_by": "tests/golden/make_golden.py (CPU oracle)", "forward": [], "adjoint": []}
+    for q, ((r0, r1), ref, b, g) in enumerate(list_members(w)):
+        x, it, rel, oc = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, w.tol, w.maxit)
+        d = {"rows": [int(r0), int(r1)], "iterations": int(it), "status": int(oc),
+             "rel_residual": float(rel)}
+        d.update(summarize(x, SAMPLE_SEED + q))
+        rec["forward"].append(d)
+        lam, gv, it2, rel2, oc2 = oracle.adjoint(ref["row_ptr"], ref["col"], ref["vals"], x, g, w.tol,
+                                                 w.maxit)
+        rec["adjoint"].append({"iterations": int(it2), "status": int(oc2), "rel_residual": float(rel2),
+                               "nnz": int(ref["col"].shape[0]),
+                               "lambda": summarize(lam, SAMPLE_SEED + 100 + q),
+                               "grad_vals": summarize(gv, SAMPLE_SEED + 200 + q)})
+        print(f"  member {q}: n={r1 - r0} iterations {it} / {it2} ({time.time() - t0:.0f} s)",
+              flush=True)
+    with open(os.path.join(HERE, f"{name}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+
+
 def main(names):
     for name in names:
         t0 = time.time()
+        if name.startswith("list_"):
+            main_list(name)
+            continue
         w = make_workload(name)
         rp, col, vals = csr_of(w)
         print(f"{name}: n={w.n} nnz={col.shape[0]} batch={w.batch} threads={oracle.num_threads()}",

@@ -83,3 +83,36 @@ def test_full_size_against_oracle_reference(name, resident):
             assert abs(ainfo.iterations[s] - ar["iterations"]) <= 2
             check_vector(GB[s], ar["lambda"], tol_g)
             check_vector(GV[s], ar["grad_vals"], tol_g)
+
+
+def test_full_size_list_against_oracle_reference():
+    """The 16-member list at its benchmark size, built as bench.py builds it
+    (one block-diagonal handle), against each member's own oracle solve
+    (tests/golden/list_diffusion2d_16.json). Both sides run the same
+    recurrence from the same start and differ by rounding only, far below the
+    tolerance-level error of either; 1e-6 bounds it with room."""
+    from differentiable_sparse_linear_csr_amd import SparseTensorList
+    name = "list_diffusion2d_16"
+    ref = json.load(open(os.path.join(HERE, "golden", f"{name}.json")))
+    print(f"full-size {name}: building inputs", flush=True)
+    w = make_workload(name)
+    assert ref["n"] == w.n and ref["members"] == len(w.extra["seg_rows"]) - 1
+    A = SparseTensorList.from_block_diagonal_coo(dev(w.rows), dev(w.cols), dev(w.vals),
+                                                 w.extra["seg_rows"])
+    print(f"full-size {name}: solving n={w.n} nnz={w.nnz}", flush=True)
+    x, info = A.solve_raw(dev(w.b), w.tol, w.maxit)
+    X = host(x)
+    gb, gv, ainfo = A.adjoint_raw(x, dev(w.g), w.tol, w.maxit)
+    GB, GV = host(gb), host(gv)
+    k0 = 0
+    for q, (fr, ar) in enumerate(zip(ref["forward"], ref["adjoint"])):
+        r0, r1 = fr["rows"]
+        assert info.status[q] == fr["status"] and ainfo.status[q] == ar["status"], q
+        assert abs(info.iterations[q] - fr["iterations"]) <= 2, (q, info.iterations[q])
+        assert abs(ainfo.iterations[q] - ar["iterations"]) <= 2, (q, ainfo.iterations[q])
+        assert info.rel_residual[q] <= w.tol and ainfo.rel_residual[q] <= w.tol
+        check_vector(X[r0:r1], fr, 1e-6)
+        check_vector(GB[r0:r1], ar["lambda"], 1e-6)
+        check_vector(GV[k0:k0 + ar["nnz"]], ar["grad_vals"], 1e-6)
+        k0 += ar["nnz"]
+    assert k0 == w.nnz
