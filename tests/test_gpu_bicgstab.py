@@ -274,3 +274,34 @@ def test_list_handle_is_refused():
     with pytest.raises(SlaError) as e:
         L.adjoint_raw(dev(np.ones(200)), dev(np.ones(200)), 1e-8, 10, method="bicgstab")
     assert e.value.status == _lib.SLA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 7, 65])
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_tiny_systems_and_ragged_tails(n, dtype):
+    """Sizes below one 16-byte group and with every tail length (the vector
+    kernels' last rows are done one per lane)."""
+    rng = np.random.default_rng(100 + n)
+    r, c = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    keep = (np.abs(r - c) <= 2).ravel()
+    r, c = r.ravel()[keep], c.ravel()[keep]
+    v = rng.uniform(-1.0, 1.0, r.shape[0])
+    v[r == c] = np.where(rng.random(n) < 0.5, -1.0, 1.0) * 6.0
+    v = v.astype(dtype)
+    b = rng.standard_normal(n).astype(dtype)
+    ref = oracle.coo_to_csr(n, r, c, v)
+    A = handle(n, r, c, v)
+    tol = 1e-9 if dtype == np.float64 else 1e-4
+    for k in (1, 3):
+        xo, ito, relo, oco = oracle.bicgstab(ref["row_ptr"], ref["col"], ref["vals"], b, 0.0, k)
+        if relo < 1e-9:
+            # solved to rounding: from here on the steps act on rounding noise,
+            # which differs between the two sides (fused multiply-adds)
+            continue
+        x, info = A.solve_raw(dev(b), 0.0, k, method="bicgstab")
+        assert (info.iterations[0], info.status[0]) == (ito, oco)
+        assert rel(host(x), xo) <= tol, (k, rel(host(x), xo))
+    xo, ito, _, oco = oracle.bicgstab(ref["row_ptr"], ref["col"], ref["vals"], b, 1e-12 if dtype == np.float64 else 1e-5, 200)
+    x, info = A.solve_raw(dev(b), 1e-12 if dtype == np.float64 else 1e-5, 200, method="bicgstab")
+    assert info.status[0] == oco == oracle.CONVERGED and abs(info.iterations[0] - ito) <= 1
+    assert rel(host(x), xo) <= (1e-9 if dtype == np.float64 else 1e-4)
