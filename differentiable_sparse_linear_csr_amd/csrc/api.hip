@@ -104,6 +104,7 @@ void alloc_workspace(Handle &h, hipStream_t s) {
     SLA_HIP(hipMemsetAsync(h.ctl, 0, sizeof(Ctl), s));
     h.bcast = (Bcast *)dalloc(h, sizeof(Bcast));
     SLA_HIP(hipMemsetAsync(h.bcast, 0, sizeof(Bcast), s));
+    h.bcast_bv = (double *)dalloc(h, sizeof(double) * 2 * kMaxBatch);
     SLA_HIP(hipMemsetAsync(h.st, 0, sizeof(SysState) * num_systems(h), s));
     if (hipHostMalloc((void **)&h.h_running, sizeof(int32_t), hipHostMallocMapped) != hipSuccess)
         fail(SLA_ERR_OOM, "pinned host allocation failed");
@@ -328,6 +329,14 @@ void set_option(Handle *h, int32_t key, int64_t value) {
             h->res_mode = (int)value;
             break;
         case SLA_OPT_FUSED_UPDATE:
+            if (h->fuse_update != (value != 0)) {
+                // the captured iteration graphs hold the other kernel sequence
+                if (h->graph) (void)hipGraphExecDestroy(h->graph);
+                if (h->bi_graph) (void)hipGraphExecDestroy(h->bi_graph);
+                h->graph = nullptr;
+                h->bi_graph = nullptr;
+                h->graph_k = h->bi_graph_k = 0;
+            }
             h->fuse_update = value != 0;
             break;
         default:

@@ -148,6 +148,8 @@ struct Handle {
     Bcast *bcast = nullptr;
     uint32_t epoch = 0;            // solves started on this handle
     int64_t upd_dir_resident = 0;  // resident workgroups of the fused update + direction
+    int64_t upd_dir_bv_resident = 0;  // the same for batches
+    double *bcast_bv = nullptr;    // [2][kMaxBatch] beta and running flag per system
     bool fuse_update = true;       // single system: update and direction in one kernel
     int32_t *h_running = nullptr; // pinned, mapped
     int32_t *d_running = nullptr; // device alias of h_running

@@ -324,6 +324,156 @@ __global__ __launch_bounds__(kBlock) void k_direction_bv(int64_t nc, int B,
     }
 }
 
+// Batched update and direction in one kernel (bv layout, Q = B / W a power of
+// two), for grids that are resident at once: one pass of kFusedGroups
+// 16-byte chunks per lane. After the per-system reductions the last
+// workgroup publishes every system's beta and whether it still runs
+// (device-scope stores, then a generation word one above the one every
+// workgroup read at its start); the others wait for it (bounded; a timeout is
+// reported through ctl->error) and write p = z + beta p for their chunks from
+// registers, which saves reading r, p and dinv again and a launch.
+constexpr int kBvFusedGroups = 4;
+constexpr uint32_t kBcastSpins = 1u << 22;   // bounded waits for a broadcast
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_update_dir_bv(int64_t nc, int B, T *__restrict__ x,
+                                                          T *__restrict__ r, T *__restrict__ p,
+                                                          const T *__restrict__ q,
+                                                          const T *__restrict__ dinv, Red red,
+                                                          Ctl *__restrict__ ctl,
+                                                          SysState *__restrict__ st,
+                                                          int32_t *__restrict__ h_running,
+                                                          Bcast *__restrict__ bc,
+                                                          double *__restrict__ bcv) {
+    constexpr int W = VecW<T>::W;
+    constexpr int U = kBvFusedGroups;
+    __shared__ double tmp[4 * kMaxBatch];
+    __shared__ double blk[kMaxBatch];
+    __shared__ double tot[2 * kMaxBatch];
+    __shared__ int s_ok;
+    if (ctl->n_running == 0) return;
+    const uint64_t gen =
+        __hip_atomic_load(&bc->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+    const int Q = B / W;
+    const int t = threadIdx.x;
+    const int s0 = (t & (Q - 1)) * W;
+    bool act[W];
+    double alpha[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        act[w] = st[s0 + w].status == kRunning;
+        alpha[w] = act[w] ? st[s0 + w].alpha : 0.0;
+    }
+    double srz[W], srr[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) srz[w] = srr[w] = 0.0;
+    const int64_t c0 = (int64_t)blockIdx.x * kBlock * U;
+    T xv[U][W], pv[U][W], rv[U][W], qv[U][W], dv[U][W];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + u * kBlock + t;
+        if (c < nc) {
+            vload(x + c * W, xv[u]);
+            vload(p + c * W, pv[u]);
+            vload(r + c * W, rv[u]);
+            vload(q + c * W, qv[u]);
+            vload(dinv + c * W, dv[u]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + u * kBlock + t;
+        if (c >= nc) continue;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            if (!act[w]) continue;
+            xv[u][w] = (T)((double)xv[u][w] + alpha[w] * (double)pv[u][w]);
+            rv[u][w] = (T)((double)rv[u][w] - alpha[w] * (double)qv[u][w]);
+            const double z = (double)dv[u][w] * (double)rv[u][w];
+            srz[w] += (double)rv[u][w] * z;
+            srr[w] += (double)rv[u][w] * (double)rv[u][w];
+        }
+        vstore(x + c * W, xv[u]);
+        vstore(r + c * W, rv[u]);
+    }
+    block_sum_systems<W>(srz, Q, tmp, blk);
+    for (int s = t; s < B; s += kBlock)
+        store_partial(red.part + (int64_t)blockIdx.x * 2 * B + s, blk[s]);
+    block_sum_systems<W>(srr, Q, tmp, blk);
+    for (int s = t; s < B; s += kBlock)
+        store_partial(red.part + (int64_t)blockIdx.x * 2 * B + B + s, blk[s]);
+    if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, 2 * B, tmp, tot)) {
+        // the stopping test, budget and beta of every system (as in
+        // finish_update), one thread per system, then the broadcast
+        const double tol = ctl->tol;
+        int running = 0;
+        for (int b = t; b < B; b += kBlock) {
+            SysState &sy = st[b];
+            int run = 0;
+            if (sy.status == kRunning) {
+                const double rz = tot[b], rr = tot[B + b];
+                sy.rr = rr;
+                sy.iter += 1;
+                if (sqrt(rr) <= tol * sqrt(sy.bb)) {
+                    sy.status = SLA_CONVERGED;
+                } else if (sy.iter >= ctl->maxit) {
+                    sy.status = SLA_MAXIT;
+                } else {
+                    sy.beta = rz / sy.rho;
+                    sy.rho = rz;
+                    run = 1;
+                }
+            }
+            store_partial(bcv + 2 * b, sy.beta);
+            store_partial(bcv + 2 * b + 1, run ? 1.0 : 0.0);
+            running += run;
+        }
+        tmp[t] = (double)running;
+        __syncthreads();
+        if (t == 0) {
+            int total = 0;
+            const int nt = B < kBlock ? B : kBlock;
+            for (int j = 0; j < nt; ++j) total += (int)tmp[j];
+            publish_running(ctl, h_running, total);
+        }
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (t == 0) __hip_atomic_store(&bc->gen, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (t == 0) {
+        uint32_t spins = 0;
+        int ok = 1;
+        while (__hip_atomic_load(&bc->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != gen) {
+            if (++spins > kBcastSpins) {
+                ok = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (!ok) __hip_atomic_store(&ctl->error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_ok = ok;
+    }
+    __syncthreads();
+    if (!s_ok) return;
+    double beta[W];
+    bool run[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        beta[w] = load_partial(bcv + 2 * (s0 + w));
+        run[w] = act[w] && load_partial(bcv + 2 * (s0 + w) + 1) != 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + u * kBlock + t;
+        if (c >= nc) continue;
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+            if (run[w])
+                pv[u][w] = (T)((double)dv[u][w] * (double)rv[u][w] + beta[w] * (double)pv[u][w]);
+        vstore(p + c * W, pv[u]);
+    }
+}
+
 template <typename T>
 bool bv_ok(const Handle &h) {
     constexpr int W = VecW<T>::W;
@@ -460,7 +610,6 @@ __global__ __launch_bounds__(kBlock) void k_update1(int64_t n, T *__restrict__ x
 // most the occupancy-API count, launched on an otherwise idle stream); the
 // wait is bounded and a timeout is reported through ctl->error.
 constexpr int kFusedGroups = 4;
-constexpr uint32_t kBcastSpins = 1u << 22;
 
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_update_dir1(int64_t n, T *__restrict__ x,
@@ -659,6 +808,17 @@ int64_t fused_grid(const Handle &h, int W) {
     return g <= h.upd_dir_resident ? g : 0;
 }
 
+// grid of the batched fused update + direction (one pass per workgroup, all
+// resident); 0 when it does not fit or fusion is off
+int64_t fused_bv_grid(const Handle &h, int W) {
+    if (h.B < 2 || h.nseg > 0 || !h.fuse_update || h.upd_dir_bv_resident <= 0) return 0;
+    const int64_t nc = h.n * h.B / W;
+    const int64_t per = (int64_t)kBlock * kBvFusedGroups;
+    int64_t g = (nc + per - 1) / per;
+    if (g < 1) g = 1;
+    return g <= h.upd_dir_bv_resident ? g : 0;
+}
+
 int64_t vec1_grid(int64_t n, int W) {
     const int64_t per = (int64_t)kBlock * kVecGroups * W;
     int64_t g = (n + per - 1) / per;
@@ -789,6 +949,15 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
         hipLaunchKernelGGL(k_update1<T>, dim3((unsigned)g1), dim3(kBlock), 0, s, h.n, (T *)h.x,
                            (T *)h.r, (const T *)h.p, (const T *)h.q, (const T *)h.dinv,
                            (const double *)h.spart, spmv_grid(h), red, h.ctl, h.st, h.d_running);
+    } else if (bv_ok<T>(h) && fused_bv_grid(h, VecW<T>::W) > 0) {
+        const int64_t nc = h.n * h.B / VecW<T>::W;
+        hipLaunchKernelGGL(k_update_dir_bv<T>, dim3((unsigned)fused_bv_grid(h, VecW<T>::W)),
+                           dim3(kBlock), 0, s, nc, h.B, (T *)h.x, (T *)h.r, (T *)h.p,
+                           (const T *)h.q, (const T *)h.dinv, red, h.ctl, h.st, h.d_running,
+                           h.bcast, h.bcast_bv);
+        SLA_HIP(hipGetLastError());
+        if (lp) lp->end(SLA_KERNEL_UPDATE, a);
+        return;
     } else if (bv_ok<T>(h)) {
         const int64_t nc = h.n * h.B / VecW<T>::W;
         hipLaunchKernelGGL(k_update_bv<T>, dim3((unsigned)bv_grid(nc, h.bv_update_resident)),
@@ -873,6 +1042,11 @@ void init_t(Handle &h, const void *b_int, hipStream_t s, Launcher *lp) {
 }  // namespace
 
 void init_vector_limits(Handle &h) {
+    if (h.B > 1)
+        h.upd_dir_bv_resident = resident_workgroups(
+            h.vt == SLA_F64 ? (const void *)&k_update_dir_bv<double>
+                            : (const void *)&k_update_dir_bv<float>,
+            h.device);
     if (h.B == 1) {
         h.upd_dir_resident = resident_workgroups(
             h.vt == SLA_F64 ? (const void *)&k_update_dir1<double> : (const void *)&k_update_dir1<float>,

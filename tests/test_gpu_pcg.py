@@ -97,6 +97,37 @@ def test_fused_update_direction_matches_two_kernels(name, size, dtype):
     assert rel(out[0], out[1]) <= (1e-8 if dtype == np.float64 else 1e-4)
 
 
+@pytest.mark.parametrize("B,dtype", [(4, np.float64), (8, np.float64), (8, np.float32),
+                                     (16, np.float32)])
+def test_batched_fused_update_direction(B, dtype):
+    """Batches that fit one resident pass: update + direction in one kernel
+    with a per-system beta broadcast, against the two-kernel form (graphs on,
+    toggled between solves) and every system's oracle solve."""
+    w = make_workload("batched_diffusion2d_512x32", size=40, batch=B)
+    v, b = w.vals.astype(dtype), w.b.astype(dtype)
+    tol = 1e-10 if dtype == np.float64 else 1e-5
+    ref = oracle.coo_to_csr(w.n, w.rows, w.cols, v)
+    xo, ito, _, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, tol, 5000)
+    A = coo_handle(w.n, w.rows, w.cols, v)
+    out = []
+    for fused in (1, 0, 1):
+        A.set_option(_lib.SLA_OPT_FUSED_UPDATE, fused)
+        x, info = A.solve_raw(dev(b), tol, 5000)
+        X = host(x)
+        for s in range(B):
+            assert info.status[s] == oco[s] and abs(info.iterations[s] - ito[s]) <= 2, s
+            assert rel(X[s], xo[s]) <= (1e-8 if dtype == np.float64 else 1e-4), s
+        out.append(X)
+        # the fused path runs no separate direction kernel
+        A.profile_reset()
+        A.set_option(_lib.SLA_OPT_PROFILE, 1)
+        A.solve_raw(dev(b), tol, 3)
+        A.set_option(_lib.SLA_OPT_PROFILE, 0)
+        assert (A.profile()["direction"][0] == 0) == bool(fused)
+    assert np.array_equal(out[0], out[2])          # bitwise repeatable
+    assert rel(out[0], out[1]) <= (1e-8 if dtype == np.float64 else 1e-4)
+
+
 def test_check_interval_and_graph_do_not_change_results():
     w = make_workload("diffusion3d_128", size=20)
     A = coo_handle(w.n, w.rows, w.cols, w.vals)
