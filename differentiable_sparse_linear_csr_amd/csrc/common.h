@@ -172,7 +172,8 @@ struct Handle {
     int64_t res_rows_per_wave = 0;
     TileDesc *res_tiles = nullptr; // tiles that never cross a wavefront's row range
     int32_t *res_wave = nullptr;   // [2][waves+1]: first row, first tile of each wavefront
-    uint64_t *res_slot = nullptr;  // [2][res_grid][4] stamped all-reduce partials
+    uint64_t *res_slot = nullptr;  // [B][2][res_grid][4] stamped all-reduce partials
+    void *res_vals = nullptr;      // [B][padded nnz] batch-major values (B > 1)
 
     // symmetric reordering for locality (reverse Cuthill-McKee): the solver
     // runs on `inner`, a handle of P A P^T; this handle keeps the caller's CSR
@@ -296,7 +297,7 @@ void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit,
 void grad_vals(Handle &h, const void *a_internal, const void *x_user, void *grad, hipStream_t s,
                double sign = -1.0);
 bool resident_ready(Handle &h, hipStream_t s);   // builds the plan on first use
-void resident_solve(Handle &h, const void *b, double tol, int32_t maxit, hipStream_t s);
+void resident_solve(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStream_t s);
 void flush_profile(Handle &h);
 
 // hipEvents around kernel launches of a call (profiling on)

@@ -1109,20 +1109,31 @@ void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit,
     h.h_ctl->epoch = ++h.epoch;
     h.h_ctl->error = 0;
     SLA_HIP(hipMemcpyAsync(h.ctl, h.h_ctl, sizeof(Ctl), hipMemcpyHostToDevice, s));
-    if (h.B == 1 && h.nseg == 0 && resident_ready(h, s)) {
-        // the whole solve in one cooperative kernel (same recurrence)
-        resident_solve(h, b_user, tol, maxit, s);
-        if (!keep_internal_solution)
-            SLA_HIP(hipMemcpyAsync(x_user, h.x, (size_t)h.n * h.vbytes, hipMemcpyDeviceToDevice, s));
-        SLA_HIP(hipMemcpyAsync(h.h_state, h.st, sizeof(SysState), hipMemcpyDeviceToHost, s));
+    if (h.nseg == 0 && resident_ready(h, s)) {
+        // the whole solve in one cooperative kernel (same recurrence); a
+        // batch leaves x as [B][n] in q
+        const size_t bytes = (size_t)h.n * h.B * h.vbytes;
+        void *xo = h.B == 1 ? h.x : h.q;
+        resident_solve(h, b_user, xo, tol, maxit, s);
+        if (h.B == 1) {
+            if (!keep_internal_solution)
+                SLA_HIP(hipMemcpyAsync(x_user, h.x, bytes, hipMemcpyDeviceToDevice, s));
+        } else if (keep_internal_solution) {
+            transpose(h.q, h.x, h.B, h.n, h.vbytes, s);
+        } else {
+            SLA_HIP(hipMemcpyAsync(x_user, h.q, bytes, hipMemcpyDeviceToDevice, s));
+        }
+        SLA_HIP(hipMemcpyAsync(h.h_state, h.st, sizeof(SysState) * h.B, hipMemcpyDeviceToHost, s));
         SLA_HIP(hipStreamSynchronize(s));
         if (h.profile) flush_profile(h);
-        const SysState &st = h.h_state[0];
-        if (st.status != kRunning && (st.status < 0 || st.status > SLA_BREAKDOWN))
-            fail(SLA_ERR_HIP, "single-kernel solve: a grid-wide wait timed out");
-        info[0].iterations = st.iter;
-        info[0].status = st.status == kRunning ? SLA_MAXIT : st.status;
-        info[0].rel_residual = st.bb == 0.0 ? 0.0 : sqrt(st.rr / st.bb);
+        for (int b = 0; b < h.B; ++b) {
+            const SysState &st = h.h_state[b];
+            if (st.status != kRunning && (st.status < 0 || st.status > SLA_BREAKDOWN))
+                fail(SLA_ERR_HIP, "single-kernel solve: a grid-wide wait timed out");
+            info[b].iterations = st.iter;
+            info[b].status = st.status == kRunning ? SLA_MAXIT : st.status;
+            info[b].rel_residual = st.bb == 0.0 ? 0.0 : sqrt(st.rr / st.bb);
+        }
         return;
     }
     const void *b_int = b_user;

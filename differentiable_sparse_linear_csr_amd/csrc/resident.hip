@@ -17,6 +17,11 @@
 //   R3  grid barrier: the copy is complete before the next gathers
 // so HBM sees the matrix, the p gathers and the p store per iteration.
 //
+// A batch of B systems sharing the pattern runs as B independent groups of
+// workgroups in the same launch: group b solves system b with its own values
+// (a batch-major copy made at the start of the solve), its own stamps, its
+// own stopping test and iteration count.
+//
 // All-reduces: every workgroup stores its partials, stamped with a sequence
 // number, with device-coherent stores; every workgroup polls all stamped
 // partials and sums them itself in block order with one fixed tree, so every
@@ -65,7 +70,8 @@ __device__ __forceinline__ double uniform(double v) {
 
 struct GridSync {
     uint64_t *slot;  // [2][G][2 * kMaxC] stamped halves of each workgroup's partials
-    int G;
+    int G;           // workgroups of one system
+    int lb;          // this workgroup's index among them
 };
 constexpr int kMaxC = 2;
 
@@ -93,7 +99,7 @@ __device__ __forceinline__ bool grid_allreduce(const GridSync &gs, uint32_t seq,
     if (t < 2 * C) {
         const uint64_t bits = (uint64_t)__double_as_longlong(v[t >> 1]);
         const uint64_t half = (t & 1) ? (bits & 0xffffffffull) : (bits >> 32);
-        __hip_atomic_store(slot + blockIdx.x * (2 * kMaxC) + t, stamp | half, __ATOMIC_RELAXED,
+        __hip_atomic_store(slot + gs.lb * (2 * kMaxC) + t, stamp | half, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
     uint64_t w[2 * C];
@@ -128,23 +134,38 @@ __device__ __forceinline__ void store_shared(T *p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// System sys = blockIdx.x / G of B: values val + sys * vstride (batch-major),
+// dinv[row * B + sys] (the internal interleaved layout), b, x_out and the
+// global p copy pg at sys * n, stamps at sys * 2 * G * 2 * kMaxC, st[sys].
 template <typename T, typename RP>
 __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
     const TileDesc *__restrict__ tiles, const int32_t *__restrict__ wave_row0,
     const int32_t *__restrict__ wave_tile0, const RP *__restrict__ row_ptr,
-    const int32_t *__restrict__ col, const T *__restrict__ val, const T *__restrict__ dinv,
-    const T *__restrict__ b, T *__restrict__ x_out, T *pg, GridSync gs, double tol,
-    int32_t maxit, SysState *__restrict__ st) {
+    const int32_t *__restrict__ col, const T *__restrict__ val_all, int64_t vstride,
+    const T *__restrict__ dinv_all, const T *__restrict__ b_all, T *__restrict__ x_all,
+    T *pg_all, GridSync gs, int B, int64_t n, double tol, int32_t maxit,
+    SysState *__restrict__ st_all) {
     __shared__ double prod_all[kRW][4 * 64];
     __shared__ int32_t roff_all[kRW][kRUnits + 1];
     __shared__ T qbuf_all[kRW][64 * kRJ];
     __shared__ double lds[kRW];
 
+    const int sys = blockIdx.x / gs.G;
+    const int lbk = blockIdx.x - sys * gs.G;   // index inside the system's group
+    const T *__restrict__ val = val_all + (int64_t)sys * vstride;
+    const T *__restrict__ b = b_all + (int64_t)sys * n;
+    T *__restrict__ x_out = x_all + (int64_t)sys * n;
+    T *pg = pg_all + (int64_t)sys * n;
+    SysState *__restrict__ st = st_all + sys;
+    gs.slot += (size_t)sys * 2 * gs.G * (2 * kMaxC);
+    gs.lb = lbk;
+
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
-    // XCD-contiguous order: workgroup b runs on XCD b % 8; each XCD takes one
-    // contiguous eighth of the rows, so halo lines are shared inside its L2
-    const int lb = (blockIdx.x % kXcds) * (gs.G / kXcds) + blockIdx.x / kXcds;
+    // XCD-contiguous order: workgroup b runs on XCD b % 8 (G is a multiple of
+    // 8, so the same holds inside every group); each XCD takes one contiguous
+    // eighth of the rows, so halo lines are shared inside its L2
+    const int lb = (lbk % kXcds) * (gs.G / kXcds) + lbk / kXcds;
     const int w = lb * kRW + wv;
     const int R0 = wave_row0[w], R1 = wave_row0[w + 1];
     const int t0 = wave_tile0[w], t1 = wave_tile0[w + 1];
@@ -166,7 +187,7 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
     for (int j = 0; j < kRJ; ++j) {
         const bool in = 64 * j < nl;
         const T bv = in ? b[R0 + lane + 64 * j] : (T)0;
-        dr[j] = in ? dinv[R0 + lane + 64 * j] : (T)0;
+        dr[j] = in ? dinv_all[(int64_t)(R0 + lane + 64 * j) * B + sys] : (T)0;
         rr[j] = bv;
         xr[j] = (T)0;
         const double z = (double)dr[j] * (double)bv;
@@ -347,7 +368,7 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
 #pragma unroll
     for (int j = 0; j < kRJ; ++j)
         if (64 * j < nl) x_out[R0 + lane + 64 * j] = xr[j];
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (lbk == 0 && threadIdx.x == 0) {
         SysState s;
         s.bb = bb;
         s.rho = rho;
@@ -356,7 +377,20 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
         s.rr = rrv;
         s.iter = iter;
         s.status = ok ? status : kResFailed;
-        st[0] = s;
+        *st = s;
+    }
+}
+
+// out[b * stride + k] = vals[k * B + b]
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_vals_bm(const T *__restrict__ vals, int64_t nnz, int B,
+                                                    T *__restrict__ out, int64_t stride) {
+    const int64_t total = nnz * B;
+    for (int64_t f = (int64_t)blockIdx.x * kBlock + threadIdx.x; f < total;
+         f += (int64_t)gridDim.x * kBlock) {
+        const int64_t k = f / B;
+        const int b = (int)(f - k * B);
+        out[(int64_t)b * stride + k] = vals[f];
     }
 }
 
@@ -400,7 +434,9 @@ void build_plan(Handle &h, int64_t G, int64_t rpw, hipStream_t s) {
     }
     h.res_tiles = (TileDesc *)dalloc(h, sizeof(TileDesc) * (tiles.size() + 1));
     h.res_wave = (int32_t *)dalloc(h, sizeof(int32_t) * wave.size());
-    h.res_slot = (uint64_t *)dalloc(h, sizeof(uint64_t) * (size_t)(2 * G * 2 * kMaxC));
+    h.res_slot = (uint64_t *)dalloc(h, sizeof(uint64_t) * (size_t)(2 * G * 2 * kMaxC) * h.B);
+    if (h.B > 1)
+        h.res_vals = dalloc(h, (size_t)((h.nnz + 31) / 32 * 32) * h.B * h.vbytes + 256);
     if (!tiles.empty())
         SLA_HIP(hipMemcpyAsync(h.res_tiles, tiles.data(), sizeof(TileDesc) * tiles.size(),
                                hipMemcpyHostToDevice, s));
@@ -410,7 +446,7 @@ void build_plan(Handle &h, int64_t G, int64_t rpw, hipStream_t s) {
 }
 
 template <typename T, typename RP>
-void launch(Handle &h, const void *b, double tol, int32_t maxit, hipStream_t s) {
+void launch(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStream_t s) {
     const int64_t waves = h.res_grid * kRW;
     const TileDesc *tiles = h.res_tiles;
     const int32_t *wrow = h.res_wave;
@@ -418,17 +454,33 @@ void launch(Handle &h, const void *b, double tol, int32_t maxit, hipStream_t s) 
     const RP *rp = (const RP *)h.row_ptr;
     const int32_t *col = h.col;
     const T *val = (const T *)h.vals;
+    int64_t vstride = 0;
+    if (h.B > 1) {
+        // batch-major values, each system's row 256-byte aligned
+        vstride = (h.nnz + 31) / 32 * 32;
+        if (h.nnz > 0) {
+            int64_t g = (h.nnz * h.B + kBlock - 1) / kBlock;
+            if (g > 4 * kMaxGrid) g = 4 * kMaxGrid;
+            hipLaunchKernelGGL(k_vals_bm<T>, dim3((unsigned)g), dim3(kBlock), 0, s,
+                               (const T *)h.vals, h.nnz, h.B, (T *)h.res_vals, vstride);
+            SLA_HIP(hipGetLastError());
+        }
+        val = (const T *)h.res_vals;
+    }
     const T *dinv = (const T *)h.dinv;
     const T *bp = (const T *)b;
-    T *xo = (T *)h.x;
+    T *xo = (T *)x;
     T *pg = (T *)h.p;
-    GridSync gs{h.res_slot, (int)h.res_grid};
+    GridSync gs{h.res_slot, (int)h.res_grid, 0};
+    const int B = h.B;
+    const int64_t n = h.n;
     SysState *st = h.st;
     void *args[] = {(void *)&tiles, (void *)&wrow, (void *)&wtile, (void *)&rp, (void *)&col,
-                    (void *)&val, (void *)&dinv, (void *)&bp, (void *)&xo, (void *)&pg,
-                    (void *)&gs, (void *)&tol, (void *)&maxit, (void *)&st};
-    SLA_HIP(hipLaunchCooperativeKernel(kernel_for(h), dim3((unsigned)h.res_grid), dim3(kRT), args,
-                                       0, s));
+                    (void *)&val, (void *)&vstride, (void *)&dinv, (void *)&bp, (void *)&xo,
+                    (void *)&pg, (void *)&gs, (void *)&B, (void *)&n, (void *)&tol,
+                    (void *)&maxit, (void *)&st};
+    SLA_HIP(hipLaunchCooperativeKernel(kernel_for(h), dim3((unsigned)(h.res_grid * h.B)),
+                                       dim3(kRT), args, 0, s));
 }
 
 }  // namespace
@@ -445,14 +497,15 @@ bool resident_ready(Handle &h, hipStream_t s) {
     if (h.res_mode == 1 && h.n > kResidentAutoRows) return false;
     if (h.res_state != 0) return h.res_state > 0;
     h.res_state = -1;
-    if (h.B != 1 || h.nlong != 0 || h.nseg > 0) return false;
+    if (h.nlong != 0 || h.nseg > 0) return false;
     int coop = 0, cus = 0, per_cu = 0;
     SLA_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, h.device));
     SLA_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h.device));
     SLA_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel_for(h), kRT, 0));
     if (!coop || per_cu < 1) return false;
-    // one workgroup per CU at most, a multiple of the XCD count
-    int64_t gmax = (int64_t)cus / kXcds * kXcds;
+    // one workgroup per CU at most, a multiple of the XCD count, shared by
+    // the B systems' groups
+    int64_t gmax = (int64_t)cus / kXcds * kXcds / h.B / kXcds * kXcds;
     if (gmax < kXcds) return false;
     // at least one row per lane for every wavefront
     int64_t G = (h.n + (int64_t)kRW * 64 - 1) / ((int64_t)kRW * 64);
@@ -469,10 +522,12 @@ bool resident_ready(Handle &h, hipStream_t s) {
     return true;
 }
 
-// Whole solve from x0 = 0: x (internal copy h.x) and the state st[0]. The
-// stamps restart at zero for every solve (sequence numbers start at 1).
-void resident_solve(Handle &h, const void *b, double tol, int32_t maxit, hipStream_t s) {
-    SLA_HIP(hipMemsetAsync(h.res_slot, 0, sizeof(uint64_t) * (size_t)(2 * h.res_grid * 2 * kMaxC), s));
+// Whole solve from x0 = 0 of every system: b and x are [B][n] (the caller's
+// layout), the state st[0..B). The stamps restart at zero for every solve
+// (sequence numbers start at 1).
+void resident_solve(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStream_t s) {
+    SLA_HIP(hipMemsetAsync(h.res_slot, 0,
+                           sizeof(uint64_t) * (size_t)(2 * h.res_grid * 2 * kMaxC) * h.B, s));
     hipEvent_t a = nullptr, e = nullptr;
     if (h.profile) {
         SLA_HIP(hipEventCreate(&a));
@@ -480,11 +535,11 @@ void resident_solve(Handle &h, const void *b, double tol, int32_t maxit, hipStre
         SLA_HIP(hipEventRecord(a, s));
     }
     if (h.vt == SLA_F64) {
-        if (h.rp64) launch<double, int64_t>(h, b, tol, maxit, s);
-        else launch<double, int32_t>(h, b, tol, maxit, s);
+        if (h.rp64) launch<double, int64_t>(h, b, x, tol, maxit, s);
+        else launch<double, int32_t>(h, b, x, tol, maxit, s);
     } else {
-        if (h.rp64) launch<float, int64_t>(h, b, tol, maxit, s);
-        else launch<float, int32_t>(h, b, tol, maxit, s);
+        if (h.rp64) launch<float, int64_t>(h, b, x, tol, maxit, s);
+        else launch<float, int32_t>(h, b, x, tol, maxit, s);
     }
     if (h.profile) {
         SLA_HIP(hipEventRecord(e, s));

@@ -109,6 +109,7 @@ def test_batched_fused_update_direction(B, dtype):
     ref = oracle.coo_to_csr(w.n, w.rows, w.cols, v)
     xo, ito, _, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, tol, 5000)
     A = coo_handle(w.n, w.rows, w.cols, v)
+    A.set_option(_lib.SLA_OPT_RESIDENT, 0)   # the per-step kernels
     out = []
     for fused in (1, 0, 1):
         A.set_option(_lib.SLA_OPT_FUSED_UPDATE, fused)
@@ -378,3 +379,59 @@ def test_single_kernel_int64_row_ptr_and_adjoint():
     assert abs(info.iterations[0] - ito) <= 2
     assert rel(host(x), xo) <= 1e-8
     assert rel(host(gb), lam_o) <= 1e-8 and rel(host(gv), gv_o) <= 1e-8
+
+
+@pytest.mark.parametrize("B,dtype", [(2, np.float64), (3, np.float64), (4, np.float64),
+                                     (8, np.float32), (32, np.float32), (5, np.float32)])
+def test_batched_single_kernel_solve(B, dtype):
+    """A batch as B independent groups of the single-kernel solve: each system
+    against its own oracle solve and against the per-step batched kernels,
+    with a zero right-hand side and an indefinite member among them, and the
+    adjoint (lambda and grad_vals) of the converged ones."""
+    w = make_workload("batched_diffusion2d_512x32", size=48, batch=B)
+    v = w.vals.astype(dtype).copy()
+    b = w.b.astype(dtype).copy()
+    b[0] = 0.0                                   # converged at iteration 0
+    if B > 2:
+        # off-diagonal couplings four times the diagonal's share: indefinite,
+        # the CG step breaks down
+        v[1] = np.where(w.rows == w.cols, v[1], 4 * v[1])
+    tol = 1e-10 if dtype == np.float64 else 1e-5
+    ref = oracle.coo_to_csr(w.n, w.rows, w.cols, v)
+    xo, ito, _, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, tol, 4000)
+    g = np.random.default_rng(7).standard_normal((B, w.n)).astype(dtype)
+    A = coo_handle(w.n, w.rows, w.cols, v)
+    print(f"batched single-kernel B={B} n={w.n} {np.dtype(dtype).name}", flush=True)
+    A.profile_reset()
+    A.set_option(_lib.SLA_OPT_PROFILE, 1)
+    x1, i1 = A.solve_raw(dev(b), tol, 4000)
+    prof = A.profile()
+    A.set_option(_lib.SLA_OPT_PROFILE, 0)
+    assert prof["cg_resident"][0] == 1 and prof["spmv_dot"][0] == 0, prof
+    A.set_option(_lib.SLA_OPT_RESIDENT, 0)
+    x0, i0 = A.solve_raw(dev(b), tol, 4000)
+    A.set_option(_lib.SLA_OPT_RESIDENT, 1)
+    xtol = 1e-8 if dtype == np.float64 else 1e-4
+    for x, info in ((x1, i1), (x0, i0)):
+        X = host(x)
+        for s in range(B):
+            assert info.status[s] == oco[s], (s, info.status[s], oco[s])
+            if oco[s] == oracle.CONVERGED and ito[s] > 0:
+                assert abs(info.iterations[s] - ito[s]) <= 2, (s, info.iterations[s], ito[s])
+                assert rel(X[s], xo[s]) <= xtol, (s, rel(X[s], xo[s]))
+            else:
+                assert info.iterations[s] == ito[s], s
+    assert not host(x1)[0].any()
+    # the adjoint on the same path
+    gb, gv, ainfo = A.adjoint_raw(x1, dev(g), tol, 4000)
+    lam, gvo, ita, _, oca = oracle.adjoint(ref["row_ptr"], ref["col"], ref["vals"], host(x1), g,
+                                           tol, 4000)
+    GB, GV = host(gb), host(gv)
+    gtol = 1e-8 if dtype == np.float64 else 1e-3
+    for s in range(B):
+        assert ainfo.status[s] == oca[s]
+        if oca[s] == oracle.CONVERGED:
+            assert rel(GB[s], lam[s]) <= gtol and rel(GV[s], gvo[s]) <= gtol, s
+    # deterministic
+    x2, i2 = A.solve_raw(dev(b), tol, 4000)
+    assert host(x2).tobytes() == host(x1).tobytes()
