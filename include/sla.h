@@ -86,16 +86,20 @@ enum {
                                    hipGraph; 0: launch kernels one by one */
     SLA_OPT_PROFILE = 3,        /* 1: time every kernel launch of later calls with hipEvents
                                    (implies eager launches); 0 (default): off */
-    SLA_OPT_RESIDENT = 4,       /* single-system solve as one cooperative kernel that keeps
-                                   x, r, p and dinv on chip (same recurrence, same
-                                   outcomes): 0 never; 1 (default) when applicable and
-                                   n <= 2^15; 2 whenever applicable. Applicable: batch 1,
-                                   no row longer than 128 entries, n <= 8192 rows per CU
-                                   (2^21 on 256 CUs), cooperative launch available. */
-    SLA_OPT_FUSED_UPDATE = 5    /* 1 (default): a single system whose update fits one pass of
-                                   the resident workgroups runs the update and the direction
-                                   as one kernel (r, p, dinv stay in registers while beta is
-                                   formed); 0: two kernels. Same arithmetic either way. */
+    SLA_OPT_RESIDENT = 4,       /* PCG solve as one cooperative kernel that keeps x, r, p
+                                   and dinv on chip (same recurrence, same outcomes); a
+                                   batch runs as one independent group of workgroups per
+                                   system: 0 never; 1 (default) when applicable and
+                                   n <= 2^15; 2 whenever applicable. Applicable: not
+                                   segmented, no row longer than 128 entries, n <= 8192
+                                   rows per CU of each system's share of the CUs (a
+                                   multiple of 8 CUs per system), cooperative launch
+                                   available. */
+    SLA_OPT_FUSED_UPDATE = 5    /* 1 (default): a single system, or a batch, whose update
+                                   fits one pass of the resident workgroups runs the update
+                                   and the direction as one kernel (r, p, dinv stay in
+                                   registers while beta is formed and broadcast); 0: two
+                                   kernels. Same arithmetic either way. */
 };
 
 /* kernel kinds reported by sla_profile_get */
@@ -107,7 +111,8 @@ enum {
     SLA_KERNEL_INIT = 3,      /* r = b, x = 0, p = z, b.b and r.z */
     SLA_KERNEL_SPMV = 4,      /* plain y = A x */
     SLA_KERNEL_GRAD = 5,      /* grad_vals[k] = -lambda[row k] x[col k] */
-    SLA_KERNEL_CG_RESIDENT = 6, /* a whole single-system solve in one cooperative kernel */
+    SLA_KERNEL_CG_RESIDENT = 6, /* a whole solve (every system of a batch) in one cooperative
+                                   kernel */
     SLA_KERNEL_COUNT = 7
 };
 
