@@ -43,6 +43,27 @@ def _compile(src: str) -> str:
     return obj
 
 
+C_EXAMPLE = os.path.join(ROOT, "tests", "c", "abi_solve.c")
+
+
+def build_c_example(verbose: bool = False) -> str:
+    """The plain-C program the ABI test runs (links libsla.so and the HIP
+    runtime; no C++ and no PyTorch)."""
+    out = os.path.splitext(C_EXAMPLE)[0]
+    clang = "/opt/rocm/llvm/bin/clang"
+    cmd = [clang if os.path.exists(clang) else "clang", "-x", "c", "-std=c99", "-O2", "-Wall",
+           "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", f"-I{INCLUDE}", C_EXAMPLE, "-o", out,
+           f"-L{PKG}", "-lsla", "-L/opt/rocm/lib", "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN/../../differentiable_sparse_linear_csr_amd",
+           "-Wl,-rpath,/opt/rocm/lib"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"building {C_EXAMPLE} failed:\n{res.stdout}\n{res.stderr}")
+    if verbose:
+        print(f"built {out}", file=sys.stderr)
+    return out
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
@@ -55,6 +76,8 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}", file=sys.stderr)
+    if os.path.exists(C_EXAMPLE):
+        build_c_example(verbose)
     return LIB
 
 
