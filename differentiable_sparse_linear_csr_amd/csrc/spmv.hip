@@ -24,13 +24,12 @@ int64_t spmv_grid(const Handle &h);
 
 namespace {
 
-__device__ __forceinline__ int group_size(int nrows) {
-    int g = 1;
-    while (g < 64 && g * 2 * nrows <= kBlock) g *= 2;
-    return g;
-}
-
 constexpr int kTileGroups = (kTileCap + 3 + 4 * 64 - 1) / (4 * 64);
+// products sit at their place in the lane's 4-entry groups (entry k0 of a
+// tile at slot k0 % 4); a group that holds any of the tile's entries is
+// written whole
+constexpr int kProdSlots = (kTileCap + 3 + 3) / 4 * 4;
+constexpr int kSumBatch = 4;   // LDS reads issued together per row sum
 constexpr int kRowItems = (kTileUnits + 1 + 63) / 64;  // row offsets per lane
 
 // Rows longer than kLongRow: one workgroup per row, 8 entries in flight per
@@ -102,7 +101,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
     double *__restrict__ tile_dot) {
     constexpr bool FUSED = DOT > 0;
     constexpr bool PERTILE = DOT == 3;
-    __shared__ double prod_all[kWaves][kTileCap];
+    __shared__ __align__(16) double prod_all[kWaves][kProdSlots];
     __shared__ int32_t roff_all[kWaves][kTileUnits + 1];
     __shared__ double pown_all[FUSED ? kWaves : 1][FUSED ? kTileUnits : 1];
     __shared__ double lds4[kWaves];
@@ -206,10 +205,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
                 const int j = 4 * (lane + u * 64) + k - shift;  // entry index within the tile
                 xv[k] = (double)x[(j >= 0 && j < nk) ? c[u][k] : 0];  // masked lanes read x[0]
             }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int j = 4 * (lane + u * 64) + k - shift;
-                if (j >= 0 && j < nk) prod[j] = (double)v[u][k] * xv[k];
+            // 32 consecutive bytes per lane (no bank conflicts); slots of
+            // entries outside [k0, k1) are never read
+            const int g = 4 * (lane + u * 64);
+            if (g < nk + shift) {
+                double2 *pd = reinterpret_cast<double2 *>(prod + g);
+                pd[0] = make_double2((double)v[u][0] * xv[0], (double)v[u][1] * xv[1]);
+                pd[1] = make_double2((double)v[u][2] * xv[2], (double)v[u][3] * xv[3]);
             }
         }
 #pragma unroll
@@ -236,9 +238,22 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
         const int grp = lane / G;
         const int ngrp = 64 / G;
         for (int i = grp; i < nrows; i += ngrp) {
-            const int a = roff[i], b = roff[i + 1];
+            const int a = roff[i] + shift, b = roff[i + 1] + shift;
+            // the lane's first kSB entries are read together, then added in
+            // order (fewer in the forms with more live partials, to stay in
+            // registers)
+            constexpr int kSB = DOT >= 2 ? 2 : kSumBatch;
+            double pv[kSB];
+#pragma unroll
+            for (int q = 0; q < kSB; ++q) {
+                const int j = a + lg + q * G;
+                pv[q] = prod[j < kProdSlots - 1 ? j : kProdSlots - 1];   // clamped; unused past b
+            }
             double s = 0.0;
-            for (int j = a + lg; j < b; j += G) s += prod[j];
+#pragma unroll
+            for (int q = 0; q < kSB; ++q)
+                if (a + lg + q * G < b) s += pv[q];
+            for (int j = a + lg + kSB * G; j < b; j += G) s += prod[j];
             for (int off = G >> 1; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
             if (lg == 0) {
                 const T q = (T)s;
