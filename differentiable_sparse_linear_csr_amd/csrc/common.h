@@ -174,6 +174,9 @@ struct Handle {
     int32_t *res_wave = nullptr;   // [2][waves+1]: first row, first tile of each wavefront
     uint64_t *res_slot = nullptr;  // [B][2][res_grid][4] stamped all-reduce partials
     void *res_vals = nullptr;      // [B][padded nnz] batch-major values (B > 1)
+    uint8_t *res_roff8 = nullptr;  // row offsets of the tiles as bytes (TileDesc.rpos)
+    uint16_t *res_col16 = nullptr; // columns minus their tile's smallest (res_narrow)
+    bool res_narrow = false;       // every tile's columns span less than 2^16
 
     // symmetric reordering for locality (reverse Cuthill-McKee): the solver
     // runs on `inner`, a handle of P A P^T; this handle keeps the caller's CSR

@@ -6,10 +6,13 @@
 //
 // One workgroup of kRT = 512 threads per CU at most, all co-resident
 // (cooperative launch). Wavefront w owns a contiguous range of at most
-// 64 * kRJ rows and holds x, r, p and dinv of those rows in registers for the
-// whole solve (lane l holds rows R0 + l + 64 j). Per iteration:
-//   A   q = A p over the wavefront's own tiles, gathering p from a global copy;
-//       q goes to the wavefront's LDS slice; p.q from registers and LDS
+// 64 * kRJ rows and holds x, r and p of those rows in registers and dinv in
+// its LDS slice for the whole solve (lane l holds rows R0 + l + 64 j). Per
+// iteration:
+//   A   q = A p over the wavefront's own tiles, gathering p from a global copy,
+//       with kRD tiles in flight (the entries of the next tiles and the
+//       gathers of the next one are loading while a tile is summed); q goes
+//       to the wavefront's LDS slice; p.q from registers and LDS
 //   R1  grid all-reduce of p.q -> alpha, or breakdown
 //   B   x += alpha p, r -= alpha q, z = dinv r; r.z and r.r
 //   R2  grid all-reduce -> stopping test, iteration budget, beta
@@ -41,8 +44,9 @@ constexpr int kRJ = 16;               // rows per lane held in registers, at mos
 // tiles of at most kRUnits rows + entries: with the up-to-3 entries before k0
 // of the first 16-byte group, a tile's entries fit one group per lane
 constexpr int kRUnits = 4 * 64 - 3;
-constexpr int kRGroups = 1;
-constexpr int kRRowItems = (kRUnits + 1 + 63) / 64;
+static_assert(kRUnits < 256, "a tile's row offsets are bytes, at most 4 per lane");
+constexpr int kSumBatch = 8;          // LDS reads issued together per row sum
+constexpr int kRD = 4;                // tiles in flight per wavefront (even)
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kResFailed = 100;       // status written when a wait timed out
 constexpr int64_t kResidentAutoRows = 1 << 15;
@@ -137,17 +141,19 @@ __device__ __forceinline__ void store_shared(T *p, T v) {
 // System sys = blockIdx.x / G of B: values val + sys * vstride (batch-major),
 // dinv[row * B + sys] (the internal interleaved layout), b, x_out and the
 // global p copy pg at sys * n, stamps at sys * 2 * G * 2 * kMaxC, st[sys].
-template <typename T, typename RP>
+template <typename T, bool NARROW>
 __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
     const TileDesc *__restrict__ tiles, const int32_t *__restrict__ wave_row0,
-    const int32_t *__restrict__ wave_tile0, const RP *__restrict__ row_ptr,
-    const int32_t *__restrict__ col, const T *__restrict__ val_all, int64_t vstride,
+    const int32_t *__restrict__ wave_tile0, const uint8_t *__restrict__ roff8,
+    const int32_t *__restrict__ col, const uint16_t *__restrict__ col16,
+    const T *__restrict__ val_all, int64_t vstride,
     const T *__restrict__ dinv_all, const T *__restrict__ b_all, T *__restrict__ x_all,
     T *pg_all, GridSync gs, int B, int64_t n, double tol, int32_t maxit,
     SysState *__restrict__ st_all) {
-    __shared__ double prod_all[kRW][4 * 64];
-    __shared__ int32_t roff_all[kRW][kRUnits + 1];
+    __shared__ __align__(16) double prod_all[kRW][4 * 64];
+    __shared__ __align__(16) int32_t roff_all[kRW][256];
     __shared__ T qbuf_all[kRW][64 * kRJ];
+    __shared__ T dinv_lds_all[kRW][64 * kRJ];
     __shared__ double lds[kRW];
 
     const int sys = blockIdx.x / gs.G;
@@ -161,7 +167,9 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
     gs.lb = lbk;
 
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    // wave-uniform (scalar registers): the row range, the tile range and
+    // every tile descriptor then come through scalar loads
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // XCD-contiguous order: workgroup b runs on XCD b % 8 (G is a multiple of
     // 8, so the same holds inside every group); each XCD takes one contiguous
     // eighth of the rows, so halo lines are shared inside its L2
@@ -174,6 +182,7 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
     T *qbuf = qbuf_all[wv];
     T *ql = qbuf + lane;             // this lane's rows: ql[64 j]
     T *pgl = pg + R0 + lane;          // and their global p: pgl[64 j]
+    T *dl = dinv_lds_all[wv] + lane;  // and their dinv: dl[64 j]
     const int nl = R1 - R0 - lane;    // row j of this lane exists iff 64 j < nl
 
     // Register arrays are updated unconditionally (a lane's rows past the
@@ -181,16 +190,17 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
     // accesses are masked. Conditional writes to the arrays would make the
     // compiler copy them whole.
     for (int j = lane; j < 64 * kRJ; j += 64) qbuf[j] = (T)0;
-    T xr[kRJ], rr[kRJ], pr[kRJ], dr[kRJ];
+    T xr[kRJ], rr[kRJ], pr[kRJ];
     double s_bb = 0.0, s_rz = 0.0;
 #pragma unroll
     for (int j = 0; j < kRJ; ++j) {
         const bool in = 64 * j < nl;
         const T bv = in ? b[R0 + lane + 64 * j] : (T)0;
-        dr[j] = in ? dinv_all[(int64_t)(R0 + lane + 64 * j) * B + sys] : (T)0;
+        const T dv = in ? dinv_all[(int64_t)(R0 + lane + 64 * j) * B + sys] : (T)0;
+        dl[64 * j] = dv;
         rr[j] = bv;
         xr[j] = (T)0;
-        const double z = (double)dr[j] * (double)bv;
+        const double z = (double)dv * (double)bv;
         pr[j] = (T)z;
         if (in) store_shared(pgl + 64 * j, pr[j]);
         s_bb += (double)bv * (double)bv;
@@ -211,92 +221,146 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
     double rrv = bb, alpha = 0.0, beta = 0.0;
     const double thresh = tol * sqrt(bb);
 
-    int32_t c[kRGroups][4];
-    T v[kRGroups][4];
-    int32_t ro[kRRowItems];
-    auto fetch = [&](const TileDesc &e) {
+    // ring of kRD tiles: slot u holds the entries (columns, values, row
+    // offsets relative to k0) of the wavefront's tiles i with i % kRD == u,
+    // as loaded (no arithmetic on them before they are used, so no load is
+    // waited for early); xv[h] holds the gathered p of tile i with
+    // i % 2 == h. Tile i's entries are requested kRD steps and its gathers
+    // two steps before it is summed. Columns are 16-bit offsets from the
+    // tile's smallest one (NARROW) or 32-bit; row offsets are bytes, lane l
+    // holding those of rows 4 l .. 4 l + 3.
+    int32_t cs[kRD][NARROW ? 2 : 4];
+    T vs[kRD][4];
+    uint32_t ros[kRD];
+    int32_t d_rs[kRD], d_re[kRD], d_cb[kRD];
+    int64_t d_k0[kRD], d_k1[kRD];
+    double xv[2][4];
+    auto fetch = [&](int u, const TileDesc &e) {
+        d_rs[u] = e.rs;
+        d_re[u] = e.re;
+        d_k0[u] = e.k0;
+        d_k1[u] = e.k1;
+        d_cb[u] = e.cbase;
         const int64_t base = e.k0 & ~(int64_t)3;
         const int span = (int)(e.k1 - base);
         const int nr = e.re - e.rs;
-        const int32_t *cp = col + base;
-        const T *vp = val + base;
-        const RP *rp = row_ptr + e.rs;
-#pragma unroll
-        for (int u = 0; u < kRGroups; ++u) {
-            const int g = 4 * (lane + u * 64);
-            if (g < span) {
-                load4(cp + g, c[u]);
-                load4(vp + g, v[u]);
+        const int g = 4 * lane;
+        if (g < span) {
+            if constexpr (NARROW) {
+                const uint2 raw = *reinterpret_cast<const uint2 *>(col16 + base + g);
+                cs[u][0] = (int32_t)raw.x;
+                cs[u][1] = (int32_t)raw.y;
             } else {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    c[u][k] = 0;
-                    v[u][k] = (T)0;
-                }
+                load4(col + base + g, cs[u]);
             }
-        }
+            load4(val + base + g, vs[u]);
+        } else {
 #pragma unroll
-        for (int u = 0; u < kRRowItems; ++u) {
-            const int j = lane + u * 64;
-            ro[u] = j <= nr ? (int32_t)(rp[j] - e.k0) : 0;
+            for (int k = 0; k < (NARROW ? 2 : 4); ++k) cs[u][k] = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) vs[u][k] = (T)0;
+        }
+        ros[u] = g <= nr ? *reinterpret_cast<const uint32_t *>(roff8 + e.rpos + g) : 0u;
+    };
+    // masked lanes read pg[0]
+    auto gather = [&](int u, int h) {
+        const int shift = (int)(d_k0[u] & 3);
+        const int nk = (int)(d_k1[u] - d_k0[u]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int j = 4 * lane + k - shift;
+            int32_t c;
+            if constexpr (NARROW)
+                c = d_cb[u] + (int32_t)(((uint32_t)cs[u][k >> 1] >> (16 * (k & 1))) & 0xffffu);
+            else
+                c = cs[u][k];
+            xv[h][k] = (double)pg[(j >= 0 && j < nk) ? c : 0];
         }
     };
 
     while (ok && status == kRunning) {
         // p written by other workgroups (other XCDs) since these caches last
-        // held it: drop stale lines before gathering
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        // ---- A: q = A p on this wavefront's tiles, into its LDS slice
-        TileDesc d{0, 0, 0, 0, 0, 0, 0};
-        if (t0 < t1) {
-            d = tiles[t0];
-            fetch(d);
+        // held it: drop stale lines before gathering. The CU's L1 and the
+        // XCD's L2 are shared by the workgroup's wavefronts, so one of them
+        // invalidates (an invalidation per wavefront costs ~13 us per
+        // iteration on a full chip) and the barrier orders the others after it.
+        if (wv == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
-        for (int t = t0; t < t1; ++t) {
-            TileDesc dn{0, 0, 0, 0, 0, 0, 0};
-            if (t + 1 < t1) dn = tiles[t + 1];
-            const int nrows = d.re - d.rs;
-            const int shift = (int)(d.k0 & 3);
-            const int nk = (int)(d.k1 - d.k0);
+        __syncthreads();
+        // ---- A: q = A p on this wavefront's tiles, into its LDS slice
+        const int nt = t1 - t0;
+        TileDesc dq[kRD + 1];
 #pragma unroll
-            for (int u = 0; u < kRGroups; ++u) {
-                double xv[4];
+        for (int u = 0; u <= kRD; ++u) dq[u] = u < nt ? tiles[t0 + u] : TileDesc{0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int j = 4 * (lane + u * 64) + k - shift;
-                    xv[k] = (double)pg[(j >= 0 && j < nk) ? c[u][k] : 0];
+        for (int u = 0; u < kRD; ++u)
+            if (u < nt) fetch(u, dq[u]);
+        if (nt > 0) gather(0, 0);
+        if (nt > 1) gather(1, 1);
+        // descriptor of the tile fetched next, read one step before its fetch
+        TileDesc en = dq[kRD];
+        for (int i0 = 0; i0 < nt; i0 += kRD) {
+#pragma unroll
+            for (int u = 0; u < kRD; ++u) {
+                const int i = i0 + u;
+                if (i >= nt) break;
+                const TileDesc ef = en;
+                if (i + kRD + 1 < nt) en = tiles[t0 + i + kRD + 1];
+                const int rs = d_rs[u];
+                const int nrows = d_re[u] - rs;
+                const int shift = (int)(d_k0[u] & 3);
+                // products at their place in the lane's 16-byte group (entry
+                // k0 of the tile is prod[shift]); lanes write 32 consecutive
+                // bytes each, the row offsets 16 (no bank conflicts). Slots
+                // outside [k0, k1) hold products nobody reads.
+                {
+                    double2 *pd = reinterpret_cast<double2 *>(prod + 4 * lane);
+                    pd[0] = make_double2((double)vs[u][0] * xv[u & 1][0], (double)vs[u][1] * xv[u & 1][1]);
+                    pd[1] = make_double2((double)vs[u][2] * xv[u & 1][2], (double)vs[u][3] * xv[u & 1][3]);
+                    const uint32_t rw = ros[u];
+                    int4 q4;
+                    q4.x = (int32_t)(rw & 0xffu) + shift;
+                    q4.y = (int32_t)((rw >> 8) & 0xffu) + shift;
+                    q4.z = (int32_t)((rw >> 16) & 0xffu) + shift;
+                    q4.w = (int32_t)(rw >> 24) + shift;
+                    *reinterpret_cast<int4 *>(roff + 4 * lane) = q4;
                 }
+                // slot u and xv[u & 1] are free again: tile i + kRD's
+                // entries and tile i + 2's gathers load during the sums
+                if (i + kRD < nt) fetch(u, ef);
+                if (i + 2 < nt) gather((u + 2) % kRD, u & 1);
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                int G = 1;
+                while (G < 64 && G * 2 * nrows <= 64) G *= 2;
+                const int lg = lane & (G - 1);
+                const int grp = lane / G;
+                const int ngrp = 64 / G;
+                for (int r = grp; r < nrows; r += ngrp) {
+                    const int a = roff[r], e = roff[r + 1];
+                    // the lane's first kSumBatch entries are read together,
+                    // then added in order
+                    double pv[kSumBatch];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int j = 4 * (lane + u * 64) + k - shift;
-                    if (j >= 0 && j < nk) prod[j] = (double)v[u][k] * xv[k];
+                    for (int q = 0; q < kSumBatch; ++q) {
+                        const int j = a + lg + q * G;
+                        pv[q] = prod[j < 4 * 64 - 1 ? j : 4 * 64 - 1];   // clamped; unused past e
+                    }
+                    double sm = 0.0;
+#pragma unroll
+                    for (int q = 0; q < kSumBatch; ++q)
+                        if (a + lg + q * G < e) sm += pv[q];
+                    for (int j = a + lg + kSumBatch * G; j < e; j += G) sm += prod[j];
+                    for (int off = G >> 1; off > 0; off >>= 1) sm += __shfl_xor(sm, off, 64);
+                    if (lg == 0) qbuf[rs - R0 + r] = (T)sm;
                 }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
-#pragma unroll
-            for (int u = 0; u < kRRowItems; ++u) {
-                const int j = lane + u * 64;
-                if (j <= nrows) roff[j] = ro[u];
-            }
-            if (t + 1 < t1) fetch(dn);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            int G = 1;
-            while (G < 64 && G * 2 * nrows <= 64) G *= 2;
-            const int lg = lane & (G - 1);
-            const int grp = lane / G;
-            const int ngrp = 64 / G;
-            for (int i = grp; i < nrows; i += ngrp) {
-                const int a = roff[i], e = roff[i + 1];
-                double s = 0.0;
-                for (int j = a + lg; j < e; j += G) s += prod[j];
-                for (int off = G >> 1; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-                if (lg == 0) qbuf[d.rs - R0 + i] = (T)s;
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            d = dn;
         }
         // ---- sigma = p.q
         double s_pq = 0.0;
@@ -325,7 +389,7 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
             const T qv = ql[64 * j];
             xr[j] = (T)((double)xr[j] + alpha * (double)pr[j]);
             rr[j] = (T)((double)rr[j] - alpha * (double)qv);
-            const double z = (double)dr[j] * (double)rr[j];
+            const double z = (double)dl[64 * j] * (double)rr[j];
             s_rz2 += (double)rr[j] * z;
             s_rr += (double)rr[j] * (double)rr[j];
         }
@@ -356,7 +420,7 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
         __asm__ volatile("" : "+v"(pw));
 #pragma unroll
         for (int j = 0; j < kRJ; ++j) {
-            pr[j] = (T)((double)dr[j] * (double)rr[j] + beta * (double)pr[j]);
+            pr[j] = (T)((double)dl[64 * j] * (double)rr[j] + beta * (double)pr[j]);
             if (64 * j < nl) store_shared(pw + 64 * j, pr[j]);
         }
         {
@@ -394,14 +458,12 @@ __global__ __launch_bounds__(kBlock) void k_vals_bm(const T *__restrict__ vals, 
     }
 }
 
-template <typename T, typename RP>
-const void *resident_kernel() {
-    return (const void *)&k_cg_resident<T, RP>;
-}
-
 const void *kernel_for(const Handle &h) {
-    if (h.vt == SLA_F64) return h.rp64 ? resident_kernel<double, int64_t>() : resident_kernel<double, int32_t>();
-    return h.rp64 ? resident_kernel<float, int64_t>() : resident_kernel<float, int32_t>();
+    if (h.vt == SLA_F64)
+        return h.res_narrow ? (const void *)&k_cg_resident<double, true>
+                            : (const void *)&k_cg_resident<double, false>;
+    return h.res_narrow ? (const void *)&k_cg_resident<float, true>
+                        : (const void *)&k_cg_resident<float, false>;
 }
 
 template <typename RP>
@@ -409,12 +471,21 @@ void build_plan(Handle &h, int64_t G, int64_t rpw, hipStream_t s) {
     const int64_t n = h.n;
     const int64_t waves = G * kRW;
     std::vector<RP> rp((size_t)n + 1);
+    std::vector<int32_t> col((size_t)h.nnz);
     SLA_HIP(hipMemcpyAsync(rp.data(), h.row_ptr, sizeof(RP) * (size_t)(n + 1),
                            hipMemcpyDeviceToHost, s));
+    if (h.nnz > 0)
+        SLA_HIP(hipMemcpyAsync(col.data(), h.col, sizeof(int32_t) * (size_t)h.nnz,
+                               hipMemcpyDeviceToHost, s));
     SLA_HIP(hipStreamSynchronize(s));
     std::vector<int32_t> wave((size_t)(2 * (waves + 1)));
     std::vector<TileDesc> tiles;
     tiles.reserve((size_t)(n / 16 + waves + 1));
+    // row offsets of every tile as bytes, each tile's run starting at a
+    // multiple of 4 (rpos)
+    std::vector<uint8_t> roff8;
+    roff8.reserve((size_t)(n + 4 * (n / 16 + waves + 1)));
+    bool narrow = true;
     for (int64_t w = 0; w <= waves; ++w) {
         const int64_t r0 = w * rpw < n ? w * rpw : n;
         wave[(size_t)w] = (int32_t)r0;
@@ -428,10 +499,38 @@ void build_plan(Handle &h, int64_t G, int64_t rpw, hipStream_t s) {
             int64_t e = a + 1;
             while (e < r1 && (e + 1 - a) + (int64_t)(rp[(size_t)e + 1] - rp[(size_t)a]) <= kRUnits)
                 ++e;
-            tiles.push_back(TileDesc{(int32_t)a, (int32_t)e, (int64_t)rp[(size_t)a], (int64_t)rp[(size_t)e], 0, 0, 0});
+            const int64_t k0 = (int64_t)rp[(size_t)a], k1 = (int64_t)rp[(size_t)e];
+            int32_t mn = 0, mx = 0;
+            for (int64_t k = k0; k < k1; ++k) {
+                const int32_t c = col[(size_t)k];
+                if (k == k0 || c < mn) mn = c;
+                if (k == k0 || c > mx) mx = c;
+            }
+            if ((int64_t)mx - (int64_t)mn >= 65536) narrow = false;
+            const int64_t rpos = (int64_t)roff8.size();
+            for (int64_t r = a; r <= e; ++r) roff8.push_back((uint8_t)(rp[(size_t)r] - (RP)k0));
+            while (roff8.size() % 4) roff8.push_back(0);
+            tiles.push_back(TileDesc{(int32_t)a, (int32_t)e, k0, k1, rpos, mn, 0});
             a = e;
         }
     }
+    // a lane reads 4 bytes at rpos + 4 l for 4 l <= the tile's row count
+    roff8.resize(roff8.size() + 256, 0);
+    h.res_narrow = narrow;
+    if (narrow) {
+        // columns as offsets from their tile's smallest one; the 16-byte
+        // groups a tile reads start up to 3 entries before its first
+        std::vector<uint16_t> c16((size_t)h.nnz + 8, 0);
+        for (const TileDesc &t : tiles)
+            for (int64_t k = t.k0; k < t.k1; ++k)
+                c16[(size_t)k] = (uint16_t)(col[(size_t)k] - t.cbase);
+        h.res_col16 = (uint16_t *)dalloc(h, sizeof(uint16_t) * c16.size());
+        SLA_HIP(hipMemcpyAsync(h.res_col16, c16.data(), sizeof(uint16_t) * c16.size(),
+                               hipMemcpyHostToDevice, s));
+        SLA_HIP(hipStreamSynchronize(s));
+    }
+    h.res_roff8 = (uint8_t *)dalloc(h, roff8.size());
+    SLA_HIP(hipMemcpyAsync(h.res_roff8, roff8.data(), roff8.size(), hipMemcpyHostToDevice, s));
     h.res_tiles = (TileDesc *)dalloc(h, sizeof(TileDesc) * (tiles.size() + 1));
     h.res_wave = (int32_t *)dalloc(h, sizeof(int32_t) * wave.size());
     h.res_slot = (uint64_t *)dalloc(h, sizeof(uint64_t) * (size_t)(2 * G * 2 * kMaxC) * h.B);
@@ -445,14 +544,15 @@ void build_plan(Handle &h, int64_t G, int64_t rpw, hipStream_t s) {
     SLA_HIP(hipStreamSynchronize(s));
 }
 
-template <typename T, typename RP>
+template <typename T>
 void launch(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStream_t s) {
     const int64_t waves = h.res_grid * kRW;
     const TileDesc *tiles = h.res_tiles;
     const int32_t *wrow = h.res_wave;
     const int32_t *wtile = h.res_wave + waves + 1;
-    const RP *rp = (const RP *)h.row_ptr;
+    const uint8_t *roff8 = h.res_roff8;
     const int32_t *col = h.col;
+    const uint16_t *col16 = h.res_col16;
     const T *val = (const T *)h.vals;
     int64_t vstride = 0;
     if (h.B > 1) {
@@ -475,8 +575,8 @@ void launch(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStr
     const int B = h.B;
     const int64_t n = h.n;
     SysState *st = h.st;
-    void *args[] = {(void *)&tiles, (void *)&wrow, (void *)&wtile, (void *)&rp, (void *)&col,
-                    (void *)&val, (void *)&vstride, (void *)&dinv, (void *)&bp, (void *)&xo,
+    void *args[] = {(void *)&tiles, (void *)&wrow, (void *)&wtile, (void *)&roff8, (void *)&col,
+                    (void *)&col16, (void *)&val, (void *)&vstride, (void *)&dinv, (void *)&bp, (void *)&xo,
                     (void *)&pg, (void *)&gs, (void *)&B, (void *)&n, (void *)&tol,
                     (void *)&maxit, (void *)&st};
     SLA_HIP(hipLaunchCooperativeKernel(kernel_for(h), dim3((unsigned)(h.res_grid * h.B)),
@@ -534,13 +634,8 @@ void resident_solve(Handle &h, const void *b, void *x, double tol, int32_t maxit
         SLA_HIP(hipEventCreate(&e));
         SLA_HIP(hipEventRecord(a, s));
     }
-    if (h.vt == SLA_F64) {
-        if (h.rp64) launch<double, int64_t>(h, b, x, tol, maxit, s);
-        else launch<double, int32_t>(h, b, x, tol, maxit, s);
-    } else {
-        if (h.rp64) launch<float, int64_t>(h, b, x, tol, maxit, s);
-        else launch<float, int32_t>(h, b, x, tol, maxit, s);
-    }
+    if (h.vt == SLA_F64) launch<double>(h, b, x, tol, maxit, s);
+    else launch<float>(h, b, x, tol, maxit, s);
     if (h.profile) {
         SLA_HIP(hipEventRecord(e, s));
         h.pending.push_back({SLA_KERNEL_CG_RESIDENT, a, e});
