@@ -16,8 +16,9 @@ hipEvents on the stream it is launched on after the timed steps:
   - single system, per-step kernels: the SpMV tile kernel, 50 back-to-back
     sla_spmv launches between one event pair, the median of three such
     batches (the solve runs its fused form, which adds the p.q partials);
-  - single system solved by the one-kernel path: that kernel, one launch per
-    solve, per-launch events (whole solves of milliseconds);
+  - single system solved by the one-kernel path (the automatic choice
+    wherever it applies, e.g. the default 2.1M-row workload): that kernel,
+    one launch per solve, per-launch events (whole solves of milliseconds);
   - batch, or a matrix the library reordered for locality (sla_spmv then
     also transposes or permutes the vectors): the fused SpMV of the solve,
     per-launch events.
@@ -454,10 +455,17 @@ def main() -> int:
             "iteration_ms": round(1e3 / value, 5),
             "iteration_model": ("BiCGStab: 2 matrix reads + 25 vector passes per iteration"
                                 if method == "bicgstab" else
+                                "PCG in one kernel: the matrix, p gathered and p stored per "
+                                "iteration (x, r, p, dinv stay on chip) = 'moved'; 3k/min: what "
+                                "the per-step kernels would move for the same iterations"
+                                if res_launches > 0 else
                                 "PCG: matrix + 13 vector passes (3k) / + 7 (min) per iteration"),
             "iteration_gbps_3k": round(job_bps["iter_3k"] / 1e9, 1),
             "iteration_frac_3k": round(job_bps["iter_3k"] / 1e9 / HBM_PEAK_GBS, 4),
             "iteration_gbps_min": round(job_bps["iter_min"] / 1e9, 1),
+            **({"iteration_gbps_moved": round(ab["spmv"] / w.batch * value / 1e9, 1),
+                "iteration_frac_moved": round(ab["spmv"] / w.batch * value / 1e9 / HBM_PEAK_GBS, 4)}
+               if res_launches > 0 else {}),
             # the kernels of one iteration alone (per-launch events, which add
             # a few microseconds of event overhead per launch)
             "iteration_kernels_ms": round(per_iter_ms, 5),

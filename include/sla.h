@@ -89,8 +89,9 @@ enum {
     SLA_OPT_RESIDENT = 4,       /* PCG solve as one cooperative kernel that keeps x, r, p
                                    and dinv on chip (same recurrence, same outcomes); a
                                    batch runs as one independent group of workgroups per
-                                   system: 0 never; 1 (default) when applicable and
-                                   n <= 2^15; 2 whenever applicable. Applicable: not
+                                   system: 0 never; 1 (default) and 2 whenever
+                                   applicable (the faster path wherever it applies, as
+                                   measured; 2 is kept as the explicit form). Applicable: not
                                    segmented, no row longer than 128 entries, n <= 8192
                                    rows per CU of each system's share of the CUs (a
                                    multiple of 8 CUs per system), cooperative launch

@@ -36,8 +36,9 @@ def check_vector(v, ref, tol):
         assert abs(np.dot(w, v) - pr) <= tol * norm * np.linalg.norm(w)
 
 
-# resident mode 2 forces the single-kernel solve where it applies (n <= 2^21)
-CASES = [(n, 1) for n in NAMES] + [("diffusion3d_128", 2), ("knn_laplacian_2m", 2)]
+# resident 0: the per-step kernels; 1: the automatic choice, which is the
+# single-kernel solve where it applies (n <= 2^21, one system)
+CASES = [(n, 0) for n in NAMES] + [("diffusion3d_128", 1), ("knn_laplacian_2m", 1)]
 
 
 @pytest.mark.parametrize("name,resident", CASES)
@@ -53,11 +54,11 @@ def test_full_size_against_oracle_reference(name, resident):
         A = SparseCSR.from_csr(dev(w.row_ptr), dev(w.cols), dev(w.vals))
         assert A.row_index_dtype == torch.int64
     A.set_option(_lib.SLA_OPT_RESIDENT, resident)
-    if resident == 2:
+    if resident == 1:
         A.set_option(_lib.SLA_OPT_PROFILE, 1)
     print(f"full-size {name}: solving n={w.n} nnz={w.nnz} batch={w.batch}", flush=True)
     x, info = A.solve_raw(dev(w.b), w.tol, w.maxit)
-    if resident == 2:
+    if resident == 1:
         assert A.profile()["cg_resident"][0] == 1
         A.set_option(_lib.SLA_OPT_PROFILE, 0)
     X = np.atleast_2d(host(x))

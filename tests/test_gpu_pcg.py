@@ -29,12 +29,16 @@ def oracle_solve(w):
     return ref, x, np.atleast_1d(it), np.atleast_1d(rl), np.atleast_1d(oc)
 
 
+# resident 0: the per-step kernels; 1: the automatic choice (the single-kernel
+# solve wherever it applies)
+@pytest.mark.parametrize("resident", [0, 1])
 @pytest.mark.parametrize("name,size,batch", CASES)
-def test_solve_matches_oracle(name, size, batch):
+def test_solve_matches_oracle(name, size, batch, resident):
     w = make_workload(name, size=size, batch=batch)
-    print(f"pcg {name} n={w.n} nnz={w.nnz} batch={w.batch}", flush=True)
+    print(f"pcg {name} n={w.n} nnz={w.nnz} batch={w.batch} resident={resident}", flush=True)
     ref, xo, ito, rlo, oco = oracle_solve(w)
     A = coo_handle(w.n, w.rows, w.cols, w.vals)
+    A.set_option(_lib.SLA_OPT_RESIDENT, resident)
     x, info = A.solve_raw(dev(w.b), w.tol, w.maxit)
     xg = np.atleast_2d(host(x))
     xo = np.atleast_2d(xo)
@@ -48,13 +52,15 @@ def test_solve_matches_oracle(name, size, batch):
             assert abs(info.rel_residual[s] - rlo[s]) <= 1e-3 * rlo[s]
 
 
+@pytest.mark.parametrize("resident", [0, 1])
 @pytest.mark.parametrize("name,size,batch", CASES)
-def test_adjoint_matches_oracle(name, size, batch):
+def test_adjoint_matches_oracle(name, size, batch, resident):
     w = make_workload(name, size=size, batch=batch)
     ref, xo, *_ = oracle_solve(w)
     lam_o, gv_o, it_o, rl_o, oc_o = oracle.adjoint(ref["row_ptr"], ref["col"], ref["vals"], xo, w.g,
                                                    w.tol, w.maxit)
     A = coo_handle(w.n, w.rows, w.cols, w.vals)
+    A.set_option(_lib.SLA_OPT_RESIDENT, resident)
     x, _ = A.solve_raw(dev(w.b), w.tol, w.maxit)
     gb, gv, info = A.adjoint_raw(x, dev(w.g), w.tol, w.maxit)
     tol = 1e-8 if w.dtype == "f64" else 1e-3
@@ -335,14 +341,7 @@ def test_single_kernel_solve_matches_oracle_and_multi_kernel_path(name, dtype):
     print(f"single-kernel {name} n={n} {np.dtype(dtype).name}", flush=True)
     ref = oracle.coo_to_csr(n, r, c, v)
     xo, ito, rlo, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, tol, maxit)
-    A = coo_handle(n, r, c, v)
-    if n > 1 << 15:
-        # the automatic choice takes the per-step kernels here; force the other
-        A.profile_reset()
-        A.set_option(_lib.SLA_OPT_PROFILE, 1)
-        A.solve_raw(dev(b), tol, 3)
-        assert A.profile()["cg_resident"][0] == 0
-        A.set_option(_lib.SLA_OPT_RESIDENT, 2)
+    A = coo_handle(n, r, c, v)      # the automatic choice: the single-kernel solve
     A.profile_reset()
     A.set_option(_lib.SLA_OPT_PROFILE, 1)
     x1, i1 = A.solve_raw(dev(b), tol, maxit)
