@@ -157,6 +157,8 @@ def run_inverse(args, N: int = 128, S: int = 4) -> int:
     rec = ConductivityRecovery(N, sources=S, total_steps=total, device="cuda:0")
     A = rec.A
     A.set_option(_lib.SLA_OPT_CHECK_INTERVAL, args.check_interval)
+    if args.ordinary_launch:
+        A.set_option(_lib.SLA_OPT_COOPERATIVE, 0)
     print(f"[bench] inverse conductivity {N}x{N}, {S} experiments, {total} Adam steps "
           f"(set up in {time.perf_counter() - t_gen:.1f} s)", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -245,6 +247,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--check-interval", type=int, default=16)
+    ap.add_argument("--ordinary-launch", action="store_true",
+                    help="start the single-kernel solve with an ordinary launch instead of "
+                         "a cooperative one (for profilers that cannot follow cooperative "
+                         "launches); same kernel, same grid")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -292,6 +298,8 @@ def main() -> int:
     create_ms = (time.perf_counter() - t0) * 1e3
     layout = A.layout()
     A.set_option(_lib.SLA_OPT_CHECK_INTERVAL, args.check_interval)
+    if args.ordinary_launch:
+        A.set_option(_lib.SLA_OPT_COOPERATIVE, 0)
     x = torch.empty_like(b)
 
     method = w.extra.get("method", "cg")

@@ -32,6 +32,7 @@ SLA_FLAG_CHECK_SYMMETRIC, SLA_FLAG_REORDER, SLA_FLAG_NO_REORDER = 1, 2, 4
 SLA_CONVERGED, SLA_MAXIT, SLA_BREAKDOWN = 0, 1, 2
 SLA_OPT_CHECK_INTERVAL, SLA_OPT_USE_GRAPH, SLA_OPT_PROFILE, SLA_OPT_RESIDENT = 1, 2, 3, 4
 SLA_OPT_FUSED_UPDATE = 5
+SLA_OPT_COOPERATIVE = 6
 KERNELS = {"spmv_dot": 0, "update": 1, "direction": 2, "init": 3, "spmv": 4, "grad": 5,
            "cg_resident": 6}
 

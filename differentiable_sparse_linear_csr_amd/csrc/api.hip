@@ -328,6 +328,9 @@ void set_option(Handle *h, int32_t key, int64_t value) {
             if (value < 0 || value > 2) fail(SLA_ERR_INVALID_ARG, "resident mode in [0, 2]");
             h->res_mode = (int)value;
             break;
+        case SLA_OPT_COOPERATIVE:
+            h->res_coop = value != 0;
+            break;
         case SLA_OPT_FUSED_UPDATE:
             if (h->fuse_update != (value != 0)) {
                 // the captured iteration graphs hold the other kernel sequence

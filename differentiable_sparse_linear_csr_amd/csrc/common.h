@@ -177,6 +177,7 @@ struct Handle {
     uint8_t *res_roff8 = nullptr;  // row offsets of the tiles as bytes (TileDesc.rpos)
     uint16_t *res_col16 = nullptr; // columns minus their tile's smallest (res_narrow)
     bool res_narrow = false;       // every tile's columns span less than 2^16
+    bool res_coop = true;          // cooperative launch (else an ordinary one)
 
     // symmetric reordering for locality (reverse Cuthill-McKee): the solver
     // runs on `inner`, a handle of P A P^T; this handle keeps the caller's CSR

@@ -578,8 +578,12 @@ void launch(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStr
                     (void *)&col16, (void *)&val, (void *)&vstride, (void *)&dinv, (void *)&bp, (void *)&xo,
                     (void *)&pg, (void *)&gs, (void *)&B, (void *)&n, (void *)&tol,
                     (void *)&maxit, (void *)&st};
-    SLA_HIP(hipLaunchCooperativeKernel(kernel_for(h), dim3((unsigned)(h.res_grid * h.B)),
-                                       dim3(kRT), args, 0, s));
+    if (h.res_coop)
+        SLA_HIP(hipLaunchCooperativeKernel(kernel_for(h), dim3((unsigned)(h.res_grid * h.B)),
+                                           dim3(kRT), args, 0, s));
+    else
+        SLA_HIP(hipLaunchKernel(kernel_for(h), dim3((unsigned)(h.res_grid * h.B)), dim3(kRT),
+                                args, 0, s));
 }
 
 }  // namespace

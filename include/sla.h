@@ -96,11 +96,19 @@ enum {
                                    rows per CU of each system's share of the CUs (a
                                    multiple of 8 CUs per system), cooperative launch
                                    available. */
-    SLA_OPT_FUSED_UPDATE = 5    /* 1 (default): a single system, or a batch, whose update
+    SLA_OPT_FUSED_UPDATE = 5,   /* 1 (default): a single system, or a batch, whose update
                                    fits one pass of the resident workgroups runs the update
                                    and the direction as one kernel (r, p, dinv stay in
                                    registers while beta is formed and broadcast); 0: two
                                    kernels. Same arithmetic either way. */
+    SLA_OPT_COOPERATIVE = 6     /* 1 (default): the single-kernel solve is started with
+                                   hipLaunchCooperativeKernel, which guarantees that all its
+                                   workgroups (one per CU at most) run at once; 0: an
+                                   ordinary launch of the same grid, for tools that cannot
+                                   follow cooperative launches. Without the guarantee a
+                                   workgroup that does not start (the GPU shared with other
+                                   work) makes the others' bounded waits expire: the solve
+                                   then fails with SLA_ERR_HIP instead of hanging. */
 };
 
 /* kernel kinds reported by sla_profile_get */

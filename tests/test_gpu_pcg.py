@@ -434,3 +434,26 @@ def test_batched_single_kernel_solve(B, dtype):
     # deterministic
     x2, i2 = A.solve_raw(dev(b), tol, 4000)
     assert host(x2).tobytes() == host(x1).tobytes()
+
+
+def test_ordinary_launch_of_the_single_kernel_solve():
+    """SLA_OPT_COOPERATIVE = 0 starts the same kernel on the same grid with an
+    ordinary launch: the same bits and the same iteration count as the
+    cooperative launch, forward and adjoint."""
+    w = make_workload("diffusion3d_128", size=32)
+    g = np.random.default_rng(11).standard_normal(w.n)
+    A = coo_handle(w.n, w.rows, w.cols, w.vals)
+    out = []
+    for coop in (1, 0):
+        A.set_option(_lib.SLA_OPT_COOPERATIVE, coop)
+        A.profile_reset()
+        A.set_option(_lib.SLA_OPT_PROFILE, 1)
+        x, info = A.solve_raw(dev(w.b), w.tol, w.maxit)
+        gb, gv, ainfo = A.adjoint_raw(x, dev(g), w.tol, w.maxit)
+        assert A.profile()["cg_resident"][0] == 2
+        A.set_option(_lib.SLA_OPT_PROFILE, 0)
+        out.append((host(x), host(gb), host(gv), info.iterations[0], ainfo.iterations[0]))
+    (x1, gb1, gv1, i1, a1), (x0, gb0, gv0, i0, a0) = out
+    assert i1 == i0 and a1 == a0
+    assert x1.tobytes() == x0.tobytes() and gb1.tobytes() == gb0.tobytes()
+    assert gv1.tobytes() == gv0.tobytes()
