@@ -63,6 +63,27 @@ __device__ __forceinline__ double rblock_sum(double v, double *lds) {
     return s;
 }
 
+// two sums over the workgroup at once (one LDS round trip, one tree each)
+__device__ __forceinline__ void rblock_sum2(double &a, double &b, double *lds2) {
+    a = wave_sum(a);
+    b = wave_sum(b);
+    const int wv = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        lds2[wv] = a;
+        lds2[kRW + wv] = b;
+    }
+    __syncthreads();
+    double sa = 0.0, sb = 0.0;
+#pragma unroll
+    for (int w = 0; w < kRW; ++w) {
+        sa += lds2[w];
+        sb += lds2[kRW + w];
+    }
+    __syncthreads();
+    a = sa;
+    b = sb;
+}
+
 // a value that is the same in every lane, moved to scalar registers
 __device__ __forceinline__ double uniform(double v) {
     const uint64_t u = __double_as_longlong(v);
@@ -121,13 +142,21 @@ __device__ __forceinline__ bool grid_allreduce(const GridSync &gs, uint32_t seq,
         if (++spins > kSpinLimit) return false;
         __builtin_amdgcn_s_sleep(1);
     }
+    double a[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-        double a = 0.0;
+        a[c] = 0.0;
         if (t < gs.G)
-            a = __longlong_as_double((int64_t)(((w[2 * c] & 0xffffffffull) << 32) |
-                                               (w[2 * c + 1] & 0xffffffffull)));
-        tot[c] = uniform(rblock_sum(a, lds));
+            a[c] = __longlong_as_double((int64_t)(((w[2 * c] & 0xffffffffull) << 32) |
+                                                  (w[2 * c + 1] & 0xffffffffull)));
+    }
+    if constexpr (C == 2) {
+        rblock_sum2(a[0], a[1], lds);
+        tot[0] = uniform(a[0]);
+        tot[1] = uniform(a[1]);
+    } else {
+#pragma unroll
+        for (int c = 0; c < C; ++c) tot[c] = uniform(rblock_sum(a[c], lds));
     }
     return true;
 }
@@ -153,7 +182,7 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
     __shared__ __align__(16) int32_t roff_all[kRW][256];
     __shared__ T qbuf_all[kRW][64 * kRJ];
     __shared__ T dinv_lds_all[kRW][64 * kRJ];
-    __shared__ double lds[kRW];
+    __shared__ double lds[2 * kRW];
 
     const int sys = blockIdx.x / gs.G;
     const int lbk = blockIdx.x - sys * gs.G;   // index inside the system's group
@@ -209,7 +238,8 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
     bool ok;
     double bb, rho;
     {
-        const double v[2] = {rblock_sum(s_bb, lds), rblock_sum(s_rz, lds)};
+        rblock_sum2(s_bb, s_rz, lds);
+        const double v[2] = {s_bb, s_rz};
         double tot[2];
         ok = grid_allreduce<2>(gs, seq++, v, tot, lds, true);
         bb = tot[0];
@@ -277,6 +307,16 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
         }
     };
 
+    // the matrix does not change: the entries of the first kRD tiles are
+    // loaded before the loop and again at the end of every SpMV phase, for
+    // the next iteration, while the all-reduces and updates run
+    const int nt = t1 - t0;
+    auto fetch_head = [&]() {
+#pragma unroll
+        for (int u = 0; u < kRD; ++u)
+            if (u < nt) fetch(u, tiles[t0 + u]);
+    };
+    fetch_head();
     while (ok && status == kRunning) {
         // p written by other workgroups (other XCDs) since these caches last
         // held it: drop stale lines before gathering. The CU's L1 and the
@@ -288,18 +328,12 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
             __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
         __syncthreads();
-        // ---- A: q = A p on this wavefront's tiles, into its LDS slice
-        const int nt = t1 - t0;
-        TileDesc dq[kRD + 1];
-#pragma unroll
-        for (int u = 0; u <= kRD; ++u) dq[u] = u < nt ? tiles[t0 + u] : TileDesc{0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int u = 0; u < kRD; ++u)
-            if (u < nt) fetch(u, dq[u]);
+        // ---- A: q = A p on this wavefront's tiles, into its LDS slice (the
+        // entries of its first kRD tiles are already in the ring)
         if (nt > 0) gather(0, 0);
         if (nt > 1) gather(1, 1);
         // descriptor of the tile fetched next, read one step before its fetch
-        TileDesc en = dq[kRD];
+        TileDesc en = kRD < nt ? tiles[t0 + kRD] : TileDesc{0, 0, 0, 0, 0, 0, 0};
         for (int i0 = 0; i0 < nt; i0 += kRD) {
 #pragma unroll
             for (int u = 0; u < kRD; ++u) {
@@ -361,6 +395,7 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
         }
+        fetch_head();
         // ---- sigma = p.q
         double s_pq = 0.0;
 #pragma unroll
@@ -394,7 +429,8 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
         }
         double rz;
         {
-            const double vv[2] = {rblock_sum(s_rz2, lds), rblock_sum(s_rr, lds)};
+            rblock_sum2(s_rz2, s_rr, lds);
+            const double vv[2] = {s_rz2, s_rr};
             double tot[2];
             ok = grid_allreduce<2>(gs, seq++, vv, tot, lds, false);
             rz = tot[0];
