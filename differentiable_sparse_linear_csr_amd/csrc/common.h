@@ -301,7 +301,8 @@ void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit,
 void grad_vals(Handle &h, const void *a_internal, const void *x_user, void *grad, hipStream_t s,
                double sign = -1.0);
 bool resident_ready(Handle &h, hipStream_t s);   // builds the plan on first use
-void resident_solve(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStream_t s);
+// false (nothing launched) when the cooperative launch is refused
+bool resident_solve(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStream_t s);
 void flush_profile(Handle &h);
 
 // hipEvents around kernel launches of a call (profiling on)

@@ -1109,12 +1109,12 @@ void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit,
     h.h_ctl->epoch = ++h.epoch;
     h.h_ctl->error = 0;
     SLA_HIP(hipMemcpyAsync(h.ctl, h.h_ctl, sizeof(Ctl), hipMemcpyHostToDevice, s));
-    if (h.nseg == 0 && resident_ready(h, s)) {
-        // the whole solve in one cooperative kernel (same recurrence); a
-        // batch leaves x as [B][n] in q
+    // the whole solve in one cooperative kernel (same recurrence; a batch
+    // leaves x as [B][n] in q), unless the cooperative launch is refused
+    // (see resident_solve): then the per-step kernels
+    if (h.nseg == 0 && resident_ready(h, s) &&
+        resident_solve(h, b_user, h.B == 1 ? h.x : h.q, tol, maxit, s)) {
         const size_t bytes = (size_t)h.n * h.B * h.vbytes;
-        void *xo = h.B == 1 ? h.x : h.q;
-        resident_solve(h, b_user, xo, tol, maxit, s);
         if (h.B == 1) {
             if (!keep_internal_solution)
                 SLA_HIP(hipMemcpyAsync(x_user, h.x, bytes, hipMemcpyDeviceToDevice, s));

@@ -579,8 +579,11 @@ void build_plan(Handle &h, int64_t G, int64_t rpw, hipStream_t s) {
     SLA_HIP(hipStreamSynchronize(s));
 }
 
+// false when the cooperative launch is refused: not all workgroups can run
+// at once now (CUs taken by other work), or another process holds the
+// device's cooperative-launch resource
 template <typename T>
-void launch(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStream_t s) {
+bool launch(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStream_t s) {
     const int64_t waves = h.res_grid * kRW;
     const TileDesc *tiles = h.res_tiles;
     const int32_t *wrow = h.res_wave;
@@ -614,12 +617,19 @@ void launch(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStr
                     (void *)&col16, (void *)&val, (void *)&vstride, (void *)&dinv, (void *)&bp, (void *)&xo,
                     (void *)&pg, (void *)&gs, (void *)&B, (void *)&n, (void *)&tol,
                     (void *)&maxit, (void *)&st};
-    if (h.res_coop)
-        SLA_HIP(hipLaunchCooperativeKernel(kernel_for(h), dim3((unsigned)(h.res_grid * h.B)),
-                                           dim3(kRT), args, 0, s));
-    else
+    if (h.res_coop) {
+        const hipError_t e = hipLaunchCooperativeKernel(
+            kernel_for(h), dim3((unsigned)(h.res_grid * h.B)), dim3(kRT), args, 0, s);
+        if (e == hipErrorCooperativeLaunchTooLarge || e == hipErrorIllegalState) {
+            (void)hipGetLastError();
+            return false;
+        }
+        SLA_HIP(e);
+    } else {
         SLA_HIP(hipLaunchKernel(kernel_for(h), dim3((unsigned)(h.res_grid * h.B)), dim3(kRT),
                                 args, 0, s));
+    }
+    return true;
 }
 
 }  // namespace
@@ -664,7 +674,7 @@ bool resident_ready(Handle &h, hipStream_t s) {
 // Whole solve from x0 = 0 of every system: b and x are [B][n] (the caller's
 // layout), the state st[0..B). The stamps restart at zero for every solve
 // (sequence numbers start at 1).
-void resident_solve(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStream_t s) {
+bool resident_solve(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStream_t s) {
     SLA_HIP(hipMemsetAsync(h.res_slot, 0,
                            sizeof(uint64_t) * (size_t)(2 * h.res_grid * 2 * kMaxC) * h.B, s));
     hipEvent_t a = nullptr, e = nullptr;
@@ -673,12 +683,18 @@ void resident_solve(Handle &h, const void *b, void *x, double tol, int32_t maxit
         SLA_HIP(hipEventCreate(&e));
         SLA_HIP(hipEventRecord(a, s));
     }
-    if (h.vt == SLA_F64) launch<double>(h, b, x, tol, maxit, s);
-    else launch<float>(h, b, x, tol, maxit, s);
+    const bool launched = h.vt == SLA_F64 ? launch<double>(h, b, x, tol, maxit, s)
+                                          : launch<float>(h, b, x, tol, maxit, s);
     if (h.profile) {
-        SLA_HIP(hipEventRecord(e, s));
-        h.pending.push_back({SLA_KERNEL_CG_RESIDENT, a, e});
+        if (launched) {
+            SLA_HIP(hipEventRecord(e, s));
+            h.pending.push_back({SLA_KERNEL_CG_RESIDENT, a, e});
+        } else {
+            (void)hipEventDestroy(a);
+            (void)hipEventDestroy(e);
+        }
     }
+    return launched;
 }
 
 }  // namespace sla

@@ -95,7 +95,10 @@ enum {
                                    segmented, no row longer than 128 entries, n <= 8192
                                    rows per CU of each system's share of the CUs (a
                                    multiple of 8 CUs per system), cooperative launch
-                                   available. */
+                                   available. A cooperative launch refused at solve time
+                                   (not all workgroups can run at once, or another process
+                                   holds the device's cooperative-launch resource) falls
+                                   back to the per-step kernels. */
     SLA_OPT_FUSED_UPDATE = 5,   /* 1 (default): a single system, or a batch, whose update
                                    fits one pass of the resident workgroups runs the update
                                    and the direction as one kernel (r, p, dinv stay in
