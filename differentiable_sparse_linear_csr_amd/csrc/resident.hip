@@ -84,20 +84,6 @@ __device__ __forceinline__ void rblock_sum2(double &a, double &b, double *lds2) 
     b = sb;
 }
 
-// A tile descriptor read through the vector memory path and moved to scalar
-// registers. A scalar load would count against the counter that LDS accesses
-// share with scalar loads, so every LDS wait of the row sums would also wait
-// for it; a vector load counts with the tile's other loads.
-struct TileDescV {
-    int32_t rs, re, cbase;
-    int64_t k0, k1, rpos;
-};
-__device__ __forceinline__ int64_t first_lane64(int64_t v) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
 // a value that is the same in every lane, moved to scalar registers
 __device__ __forceinline__ double uniform(double v) {
     const uint64_t u = __double_as_longlong(v);
