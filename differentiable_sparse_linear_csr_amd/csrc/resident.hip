@@ -26,10 +26,11 @@
 // own stopping test and iteration count.
 //
 // All-reduces: every workgroup stores its partials, stamped with a sequence
-// number, with device-coherent stores; every workgroup polls all stamped
-// partials and sums them itself in block order with one fixed tree, so every
-// workgroup holds the same bits and takes the same stopping decisions. Polls are bounded: a workgroup that waits
-// longer than kSpinLimit polls reports a failure instead of hanging.
+// number, with device-coherent stores; one wavefront of every workgroup polls
+// all stamped partials and sums them itself in one fixed order, so every
+// workgroup holds the same bits and takes the same stopping decisions. Polls
+// are bounded: a workgroup that waits longer than kSpinLimit polls reports a
+// failure instead of hanging.
 #include "common.h"
 
 #include <vector>
@@ -126,38 +127,51 @@ __device__ __forceinline__ bool grid_allreduce(const GridSync &gs, uint32_t seq,
         __hip_atomic_store(slot + gs.lb * (2 * kMaxC) + t, stamp | half, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
-    uint64_t w[2 * C];
-    uint32_t spins = 0;
-    while (true) {
-        bool arrived = true;
-        if (t < gs.G) {
+    // wavefront 0 polls every partial (lane l: workgroups l, l + 64, ...)
+    // until all carry this stamp, and sums them: lane l in workgroup order,
+    // then the wavefront tree, the same in every workgroup
+    if (t < 64) {
+        uint32_t spins = 0;
+        double a[C];
+        bool done = false;
+        while (true) {
+            bool arrived = true;
 #pragma unroll
-            for (int k = 0; k < 2 * C; ++k)
-                w[k] = __hip_atomic_load(slot + t * (2 * kMaxC) + k, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
+            for (int c = 0; c < C; ++c) a[c] = 0.0;
+            for (int q = t; q < gs.G; q += 64) {
+                uint64_t w[2 * C];
 #pragma unroll
-            for (int k = 0; k < 2 * C; ++k) arrived &= (w[k] >> 32) == seq;
+                for (int k = 0; k < 2 * C; ++k) {
+                    w[k] = __hip_atomic_load(slot + q * (2 * kMaxC) + k, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+                    arrived &= (w[k] >> 32) == seq;
+                }
+#pragma unroll
+                for (int c = 0; c < C; ++c)
+                    a[c] += __longlong_as_double((int64_t)(((w[2 * c] & 0xffffffffull) << 32) |
+                                                           (w[2 * c + 1] & 0xffffffffull)));
+            }
+            if (__all(arrived)) {
+                done = true;
+                break;
+            }
+            if (++spins > kSpinLimit) break;
+            __builtin_amdgcn_s_sleep(1);
         }
-        if (__syncthreads_and(arrived)) break;
-        if (++spins > kSpinLimit) return false;
-        __builtin_amdgcn_s_sleep(1);
-    }
-    double a[C];
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-        a[c] = 0.0;
-        if (t < gs.G)
-            a[c] = __longlong_as_double((int64_t)(((w[2 * c] & 0xffffffffull) << 32) |
-                                                  (w[2 * c + 1] & 0xffffffffull)));
-    }
-    if constexpr (C == 2) {
-        rblock_sum2(a[0], a[1], lds);
-        tot[0] = uniform(a[0]);
-        tot[1] = uniform(a[1]);
-    } else {
+        for (int c = 0; c < C; ++c) a[c] = wave_sum(a[c]);
+        if (t == 0) {
 #pragma unroll
-        for (int c = 0; c < C; ++c) tot[c] = uniform(rblock_sum(a[c], lds));
+            for (int c = 0; c < C; ++c) lds[c] = a[c];
+            lds[kMaxC] = done ? 1.0 : 0.0;
+        }
     }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < C; ++c) tot[c] = uniform(lds[c]);
+    const bool arrived_all = lds[kMaxC] != 0.0;
+    __syncthreads();
+    if (!arrived_all) return false;
     return true;
 }
 
