@@ -47,6 +47,7 @@ constexpr int kRJ = 16;               // rows per lane held in registers, at mos
 constexpr int kRUnits = 4 * 64 - 3;
 static_assert(kRUnits < 256, "a tile's row offsets are bytes, at most 4 per lane");
 constexpr int kSumBatch = 8;          // LDS reads issued together per row sum
+constexpr double kFastShare = 1.0625;   // tile share of a SIMD's first wavefront (vs 0.9375)
 constexpr int kRD = 4;                // tiles in flight per wavefront (even)
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kResFailed = 100;       // status written when a wait timed out
@@ -221,6 +222,10 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
     const int t0 = wave_tile0[w], t1 = wave_tile0[w + 1];
     double *prod = prod_all[wv];
     int32_t *roff = roff_all[wv];
+    // q of the workgroup's rows (wavefront v's rows in qbuf_all[v]); a tile
+    // may be summed by another wavefront of the workgroup than its rows'
+    // owner, and its descriptor gives its first row's slot
+    T *qwg = &qbuf_all[0][0];
     T *qbuf = qbuf_all[wv];
     T *ql = qbuf + lane;             // this lane's rows: ql[64 j]
     T *pgl = pg + R0 + lane;          // and their global p: pgl[64 j]
@@ -275,7 +280,7 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
     int32_t cs[kRD][NARROW ? 2 : 4];
     T vs[kRD][4];
     uint32_t ros[kRD];
-    int32_t d_rs[kRD], d_re[kRD], d_cb[kRD];
+    int32_t d_rs[kRD], d_re[kRD], d_cb[kRD], d_qb[kRD];
     int64_t d_k0[kRD], d_k1[kRD];
     double xv[2][4];
     auto fetch = [&](int u, const TileDesc &e) {
@@ -284,6 +289,7 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
         d_k0[u] = e.k0;
         d_k1[u] = e.k1;
         d_cb[u] = e.cbase;
+        d_qb[u] = e.narrow;   // single-kernel tiles: the slot of row rs in qwg
         const int64_t base = e.k0 & ~(int64_t)3;
         const int span = (int)(e.k1 - base);
         const int nr = e.re - e.rs;
@@ -355,8 +361,8 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
                 if (i >= nt) break;
                 const TileDesc ef = en;
                 if (i + kRD + 1 < nt) en = tiles[t0 + i + kRD + 1];
-                const int rs = d_rs[u];
-                const int nrows = d_re[u] - rs;
+                const int nrows = d_re[u] - d_rs[u];
+                const int qb = d_qb[u];
                 const int shift = (int)(d_k0[u] & 3);
                 // products at their place in the lane's 16-byte group (entry
                 // k0 of the tile is prod[shift]); lanes write 32 consecutive
@@ -402,7 +408,7 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
                         if (a + lg + q * G < e) sm += pv[q];
                     for (int j = a + lg + kSumBatch * G; j < e; j += G) sm += prod[j];
                     for (int off = G >> 1; off > 0; off >>= 1) sm += __shfl_xor(sm, off, 64);
-                    if (lg == 0) qbuf[rs - R0 + r] = (T)sm;
+                    if (lg == 0) qwg[qb + r] = (T)sm;
                 }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
@@ -410,6 +416,8 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
             }
         }
         fetch_head();
+        // q rows summed by other wavefronts
+        __syncthreads();
         // ---- sigma = p.q
         double s_pq = 0.0;
 #pragma unroll
@@ -559,8 +567,35 @@ void build_plan(Handle &h, int64_t G, int64_t rpw, hipStream_t s) {
             const int64_t rpos = (int64_t)roff8.size();
             for (int64_t r = a; r <= e; ++r) roff8.push_back((uint8_t)(rp[(size_t)r] - (RP)k0));
             while (roff8.size() % 4) roff8.push_back(0);
-            tiles.push_back(TileDesc{(int32_t)a, (int32_t)e, k0, k1, rpos, mn, 0});
+            // narrow: the slot of row a in the workgroup's q buffer (wavefront
+            // w % kRW holds its rows from kRJ * 64 * (w % kRW))
+            const int32_t qslot = (int32_t)((w % kRW) * 64 * kRJ + (a - r0));
+            tiles.push_back(TileDesc{(int32_t)a, (int32_t)e, k0, k1, rpos, mn, qslot});
             a = e;
+        }
+    }
+    // Which wavefront sums which tiles: a workgroup's tiles are re-split among
+    // its wavefronts by rows + entries, the first wavefront of each SIMD
+    // (kRW / 2 of them, older, more issue slots) taking kFastShare of an even
+    // share and the second the rest, so that the two finish together. Row
+    // ownership (x, r, p in registers) does not change; a tile's q goes to
+    // its owner's slot.
+    for (int64_t g = 0; g < waves / kRW; ++g) {
+        const int64_t ta = wave[(size_t)(waves + 1 + g * kRW)];
+        const int64_t tb = wave[(size_t)(waves + 1 + (g + 1) * kRW)];
+        std::vector<double> cum((size_t)(tb - ta + 1), 0.0);
+        for (int64_t t = ta; t < tb; ++t) {
+            const TileDesc &d = tiles[(size_t)t];
+            cum[(size_t)(t - ta + 1)] = cum[(size_t)(t - ta)] + (double)(d.re - d.rs) + (double)(d.k1 - d.k0);
+        }
+        const double total = cum.back();
+        double acc = 0.0;
+        int64_t t = ta;
+        for (int v = 1; v < kRW; ++v) {
+            acc += (v - 1 < kRW / 2 ? kFastShare : 2.0 - kFastShare) / kRW;
+            while (t < tb && cum[(size_t)(t - ta + 1)] <= acc * total + 0.5 * (cum[(size_t)(t - ta + 1)] - cum[(size_t)(t - ta)]))
+                ++t;
+            wave[(size_t)(waves + 1 + g * kRW + v)] = (int32_t)t;
         }
     }
     // a lane reads 4 bytes at rpos + 4 l for 4 l <= the tile's row count
