@@ -9,10 +9,11 @@
 // 64 * kRJ rows and holds x, r and p of those rows in registers and dinv in
 // its LDS slice for the whole solve (lane l holds rows R0 + l + 64 j). Per
 // iteration:
-//   A   q = A p over the wavefront's own tiles, gathering p from a global copy,
+//   A   q = A p over the workgroup's tiles (each wavefront a run of them,
+//       weighted by the SIMD slot it holds), gathering p from a global copy,
 //       with kRD tiles in flight (the entries of the next tiles and the
-//       gathers of the next one are loading while a tile is summed); q goes
-//       to the wavefront's LDS slice; p.q from registers and LDS
+//       gathers of the tile two on are loading while a tile is summed); q
+//       goes to the LDS slot of its rows' owner; p.q from registers and LDS
 //   R1  grid all-reduce of p.q -> alpha, or breakdown
 //   B   x += alpha p, r -= alpha q, z = dinv r; r.z and r.r
 //   R2  grid all-reduce -> stopping test, iteration budget, beta
