@@ -61,6 +61,17 @@ struct TileDesc {
     int32_t narrow;
 };
 
+// A tile of the single-kernel solve in 16 bytes, so that the descriptors of
+// a CU's wavefronts stay in the scalar cache from one iteration to the next:
+// first entry (the solve needs nnz < 2^31), smallest column, position of its
+// byte row offsets, and rows | entries << 8 | q slot of its first row << 16.
+struct ResTile {
+    int32_t k0;
+    int32_t cbase;
+    int32_t rpos;
+    uint32_t packed;
+};
+
 struct Ctl {
     double tol;
     int32_t maxit;
@@ -170,7 +181,7 @@ struct Handle {
     int res_mode = 1;              // 0 never, 1 automatic, 2 whenever applicable
     int64_t res_grid = 0;          // workgroups (one per CU at most)
     int64_t res_rows_per_wave = 0;
-    TileDesc *res_tiles = nullptr; // tiles that never cross a wavefront's row range
+    ResTile *res_tiles = nullptr;  // tiles that never cross a wavefront's row range
     int32_t *res_wave = nullptr;   // [2][waves+1]: first row, first tile of each wavefront
     uint64_t *res_slot = nullptr;  // [B][2][res_grid][4] stamped all-reduce partials
     void *res_vals = nullptr;      // [B][padded nnz] batch-major values (B > 1)

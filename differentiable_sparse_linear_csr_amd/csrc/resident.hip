@@ -187,7 +187,7 @@ __device__ __forceinline__ void store_shared(T *p, T v) {
 // global p copy pg at sys * n, stamps at sys * 2 * G * 2 * kMaxC, st[sys].
 template <typename T, bool NARROW>
 __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
-    const TileDesc *__restrict__ tiles, const int32_t *__restrict__ wave_row0,
+    const ResTile *__restrict__ tiles, const int32_t *__restrict__ wave_row0,
     const int32_t *__restrict__ wave_tile0, const uint8_t *__restrict__ roff8,
     const int32_t *__restrict__ col, const uint16_t *__restrict__ col16,
     const T *__restrict__ val_all, int64_t vstride,
@@ -281,19 +281,17 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
     int32_t cs[kRD][NARROW ? 2 : 4];
     T vs[kRD][4];
     uint32_t ros[kRD];
-    int32_t d_rs[kRD], d_re[kRD], d_cb[kRD], d_qb[kRD];
-    int64_t d_k0[kRD], d_k1[kRD];
+    int32_t d_nr[kRD], d_nk[kRD], d_k0[kRD], d_cb[kRD], d_qb[kRD];
     double xv[2][4];
-    auto fetch = [&](int u, const TileDesc &e) {
-        d_rs[u] = e.rs;
-        d_re[u] = e.re;
+    auto fetch = [&](int u, const ResTile &e) {
+        const int nr = (int)(e.packed & 0xffu);
+        d_nr[u] = nr;
+        d_nk[u] = (int)((e.packed >> 8) & 0xffu);
         d_k0[u] = e.k0;
-        d_k1[u] = e.k1;
         d_cb[u] = e.cbase;
-        d_qb[u] = e.narrow;   // single-kernel tiles: the slot of row rs in qwg
-        const int64_t base = e.k0 & ~(int64_t)3;
-        const int span = (int)(e.k1 - base);
-        const int nr = e.re - e.rs;
+        d_qb[u] = (int)(e.packed >> 16);
+        const int64_t base = (int64_t)(e.k0 & ~3);
+        const int span = (int)(e.k0 + d_nk[u] - base);
         const int g = 4 * lane;
         if (g < span) {
             if constexpr (NARROW) {
@@ -314,8 +312,8 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
     };
     // masked lanes read pg[0]
     auto gather = [&](int u, int h) {
-        const int shift = (int)(d_k0[u] & 3);
-        const int nk = (int)(d_k1[u] - d_k0[u]);
+        const int shift = d_k0[u] & 3;
+        const int nk = d_nk[u];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int j = 4 * lane + k - shift;
@@ -354,17 +352,17 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
         if (nt > 0) gather(0, 0);
         if (nt > 1) gather(1, 1);
         // descriptor of the tile fetched next, read one step before its fetch
-        TileDesc en = kRD < nt ? tiles[t0 + kRD] : TileDesc{0, 0, 0, 0, 0, 0, 0};
+        ResTile en = kRD < nt ? tiles[t0 + kRD] : ResTile{0, 0, 0, 0};
         for (int i0 = 0; i0 < nt; i0 += kRD) {
 #pragma unroll
             for (int u = 0; u < kRD; ++u) {
                 const int i = i0 + u;
                 if (i >= nt) break;
-                const TileDesc ef = en;
+                const ResTile ef = en;
                 if (i + kRD + 1 < nt) en = tiles[t0 + i + kRD + 1];
-                const int nrows = d_re[u] - d_rs[u];
+                const int nrows = d_nr[u];
                 const int qb = d_qb[u];
-                const int shift = (int)(d_k0[u] & 3);
+                const int shift = d_k0[u] & 3;
                 // products at their place in the lane's 16-byte group (entry
                 // k0 of the tile is prod[shift]); lanes write 32 consecutive
                 // bytes each, the row offsets 16 (no bank conflicts). Slots
@@ -616,13 +614,20 @@ void build_plan(Handle &h, int64_t G, int64_t rpw, hipStream_t s) {
     }
     h.res_roff8 = (uint8_t *)dalloc(h, roff8.size());
     SLA_HIP(hipMemcpyAsync(h.res_roff8, roff8.data(), roff8.size(), hipMemcpyHostToDevice, s));
-    h.res_tiles = (TileDesc *)dalloc(h, sizeof(TileDesc) * (tiles.size() + 1));
+    std::vector<ResTile> rt(tiles.size());
+    for (size_t t = 0; t < tiles.size(); ++t) {
+        const TileDesc &d = tiles[t];
+        rt[t] = ResTile{(int32_t)d.k0, d.cbase, (int32_t)d.rpos,
+                        (uint32_t)(d.re - d.rs) | ((uint32_t)(d.k1 - d.k0) << 8) |
+                            ((uint32_t)d.narrow << 16)};
+    }
+    h.res_tiles = (ResTile *)dalloc(h, sizeof(ResTile) * (rt.size() + 1));
     h.res_wave = (int32_t *)dalloc(h, sizeof(int32_t) * wave.size());
     h.res_slot = (uint64_t *)dalloc(h, sizeof(uint64_t) * (size_t)(2 * G * 2 * kMaxC) * h.B);
     if (h.B > 1)
         h.res_vals = dalloc(h, (size_t)((h.nnz + 31) / 32 * 32) * h.B * h.vbytes + 256);
-    if (!tiles.empty())
-        SLA_HIP(hipMemcpyAsync(h.res_tiles, tiles.data(), sizeof(TileDesc) * tiles.size(),
+    if (!rt.empty())
+        SLA_HIP(hipMemcpyAsync(h.res_tiles, rt.data(), sizeof(ResTile) * rt.size(),
                                hipMemcpyHostToDevice, s));
     SLA_HIP(hipMemcpyAsync(h.res_wave, wave.data(), sizeof(int32_t) * wave.size(),
                            hipMemcpyHostToDevice, s));
@@ -635,7 +640,7 @@ void build_plan(Handle &h, int64_t G, int64_t rpw, hipStream_t s) {
 template <typename T>
 bool launch(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStream_t s) {
     const int64_t waves = h.res_grid * kRW;
-    const TileDesc *tiles = h.res_tiles;
+    const ResTile *tiles = h.res_tiles;
     const int32_t *wrow = h.res_wave;
     const int32_t *wtile = h.res_wave + waves + 1;
     const uint8_t *roff8 = h.res_roff8;
@@ -696,7 +701,9 @@ bool resident_ready(Handle &h, hipStream_t s) {
     if (h.res_mode == 0) return false;
     if (h.res_state != 0) return h.res_state > 0;
     h.res_state = -1;
-    if (h.nlong != 0 || h.nseg > 0) return false;
+    // tiles address entries with 32-bit offsets (rows of at most 128
+    // entries and 8192 rows per CU keep nnz far below that on this chip)
+    if (h.nlong != 0 || h.nseg > 0 || h.nnz >= ((int64_t)1 << 31)) return false;
     int coop = 0, cus = 0, per_cu = 0;
     SLA_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, h.device));
     SLA_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h.device));
