@@ -511,6 +511,31 @@ __device__ __forceinline__ void vstore(T *p, const T (&o)[VecW<T>::W]) {
     __builtin_memcpy(&a, o, 16);
     *reinterpret_cast<int4 *>(p) = a;
 }
+// The same with the non-temporal hint, for vectors far larger than the
+// caches (they are not re-read before they are evicted, and keeping them out
+// of the Infinity Cache leaves it to the matrix stream)
+typedef int nt_v4i __attribute__((ext_vector_type(4)));
+template <bool NT, typename T>
+__device__ __forceinline__ void vload_h(const T *p, T (&o)[VecW<T>::W]) {
+    if constexpr (NT) {
+        const nt_v4i a = __builtin_nontemporal_load(reinterpret_cast<const nt_v4i *>(p));
+        __builtin_memcpy(o, &a, 16);
+    } else {
+        vload(p, o);
+    }
+}
+template <bool NT, typename T>
+__device__ __forceinline__ void vstore_h(T *p, const T (&o)[VecW<T>::W]) {
+    if constexpr (NT) {
+        nt_v4i a;
+        __builtin_memcpy(&a, o, 16);
+        __builtin_nontemporal_store(a, reinterpret_cast<nt_v4i *>(p));
+    } else {
+        vstore(p, o);
+    }
+}
+// vectors of at least this many bytes take the non-temporal accesses
+constexpr int64_t kNtVectorBytes = (int64_t)128 << 20;
 
 // Four consecutive elements through 16-byte loads (p 16-byte aligned)
 __device__ __forceinline__ void load4(const double *p, double (&o)[4]) {

@@ -497,7 +497,7 @@ int64_t bv_grid(int64_t nc, int64_t resident) {
 // each memory instruction moves twice (fp64) or four times (fp32) the data of
 // the per-row forms; rows past the last full group are done by block 0.
 
-template <typename T>
+template <typename T, bool NT>
 __global__ __launch_bounds__(kBlock) void k_update1(int64_t n, T *__restrict__ x,
                                                     T *__restrict__ r, const T *__restrict__ p,
                                                     const T *__restrict__ q,
@@ -543,11 +543,11 @@ __global__ __launch_bounds__(kBlock) void k_update1(int64_t n, T *__restrict__ x
         for (int u = 0; u < kVecGroups; ++u) {
             const int64_t g = g0 + u * kBlock + tid;
             if (g < ng) {
-                vload(x + g * W, xv[u]);
-                vload(p + g * W, pv[u]);
-                vload(r + g * W, rv[u]);
-                vload(q + g * W, qv[u]);
-                vload(dinv + g * W, dv[u]);
+                vload_h<NT>(x + g * W, xv[u]);
+                vload_h<NT>(p + g * W, pv[u]);
+                vload_h<NT>(r + g * W, rv[u]);
+                vload_h<NT>(q + g * W, qv[u]);
+                vload_h<NT>(dinv + g * W, dv[u]);
             }
         }
 #pragma unroll
@@ -556,8 +556,8 @@ __global__ __launch_bounds__(kBlock) void k_update1(int64_t n, T *__restrict__ x
             if (g < ng) {
 #pragma unroll
                 for (int k = 0; k < W; ++k) row(xv[u][k], rv[u][k], pv[u][k], qv[u][k], dv[u][k]);
-                vstore(x + g * W, xv[u]);
-                vstore(r + g * W, rv[u]);
+                vstore_h<NT>(x + g * W, xv[u]);
+                vstore_h<NT>(r + g * W, rv[u]);
             }
         }
     }
@@ -758,7 +758,7 @@ __global__ __launch_bounds__(kBlock) void k_update_dir1(int64_t n, T *__restrict
     if (tail) p[ng * W + tid] = (T)((double)dt * (double)rt + beta * (double)pt);
 }
 
-template <typename T>
+template <typename T, bool NT>
 __global__ __launch_bounds__(kBlock) void k_direction1(int64_t n, const T *__restrict__ r,
                                                        T *__restrict__ p,
                                                        const T *__restrict__ dinv,
@@ -776,9 +776,9 @@ __global__ __launch_bounds__(kBlock) void k_direction1(int64_t n, const T *__res
         for (int u = 0; u < kVecGroups; ++u) {
             const int64_t g = g0 + u * kBlock + tid;
             if (g < ng) {
-                vload(r + g * W, rv[u]);
-                vload(p + g * W, pv[u]);
-                vload(dinv + g * W, dv[u]);
+                vload_h<NT>(r + g * W, rv[u]);
+                vload_h<NT>(p + g * W, pv[u]);
+                vload_h<NT>(dinv + g * W, dv[u]);
             }
         }
 #pragma unroll
@@ -788,7 +788,7 @@ __global__ __launch_bounds__(kBlock) void k_direction1(int64_t n, const T *__res
 #pragma unroll
                 for (int k = 0; k < W; ++k)
                     pv[u][k] = (T)((double)dv[u][k] * (double)rv[u][k] + beta * (double)pv[u][k]);
-                vstore(p + g * W, pv[u]);
+                vstore_h<NT>(p + g * W, pv[u]);
             }
         }
     }
@@ -946,7 +946,9 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
     }
     if (h.B == 1) {
         const int64_t g1 = vec1_grid(h.n, VecW<T>::W);
-        hipLaunchKernelGGL(k_update1<T>, dim3((unsigned)g1), dim3(kBlock), 0, s, h.n, (T *)h.x,
+        const bool nt = h.n * (int64_t)sizeof(T) >= kNtVectorBytes;
+        hipLaunchKernelGGL((nt ? k_update1<T, true> : k_update1<T, false>), dim3((unsigned)g1),
+                           dim3(kBlock), 0, s, h.n, (T *)h.x,
                            (T *)h.r, (const T *)h.p, (const T *)h.q, (const T *)h.dinv,
                            (const double *)h.spart, spmv_grid(h), red, h.ctl, h.st, h.d_running);
     } else if (bv_ok<T>(h) && fused_bv_grid(h, VecW<T>::W) > 0) {
@@ -974,7 +976,9 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
     if (lp) lp->begin(SLA_KERNEL_DIRECTION, &a);
     if (h.B == 1) {
         const int64_t g1 = vec1_grid(h.n, VecW<T>::W);
-        hipLaunchKernelGGL(k_direction1<T>, dim3((unsigned)g1), dim3(kBlock), 0, s, h.n,
+        const bool nt = h.n * (int64_t)sizeof(T) >= kNtVectorBytes;
+        hipLaunchKernelGGL((nt ? k_direction1<T, true> : k_direction1<T, false>), dim3((unsigned)g1),
+                           dim3(kBlock), 0, s, h.n,
                            (const T *)h.r, (T *)h.p, (const T *)h.dinv, (const Ctl *)h.ctl,
                            (const SysState *)h.st);
     } else if (bv_ok<T>(h)) {
