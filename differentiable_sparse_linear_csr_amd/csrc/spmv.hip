@@ -29,7 +29,7 @@ constexpr int kTileGroups = (kTileCap + 3 + 4 * 64 - 1) / (4 * 64);
 // tile at slot k0 % 4); a group that holds any of the tile's entries is
 // written whole
 constexpr int kProdSlots = (kTileCap + 3 + 3) / 4 * 4;
-constexpr int kSumBatch = 4;   // LDS reads issued together per row sum
+constexpr int kSumBatch = 2;   // LDS reads issued together per row sum (4: 4% slower)
 constexpr int kRowItems = (kTileUnits + 1 + 63) / 64;  // row offsets per lane
 
 // Rows longer than kLongRow: one workgroup per row, 8 entries in flight per
@@ -240,9 +240,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
         for (int i = grp; i < nrows; i += ngrp) {
             const int a = roff[i] + shift, b = roff[i + 1] + shift;
             // the lane's first kSB entries are read together, then added in
-            // order (fewer in the forms with more live partials, to stay in
-            // registers)
-            constexpr int kSB = DOT >= 2 ? 2 : kSumBatch;
+            // order
+            constexpr int kSB = kSumBatch;
             double pv[kSB];
 #pragma unroll
             for (int q = 0; q < kSB; ++q) {
