@@ -182,8 +182,10 @@ struct Handle {
     int64_t res_grid = 0;          // workgroups (one per CU at most)
     int64_t res_rows_per_wave = 0;
     ResTile *res_tiles = nullptr;  // tiles that never cross a wavefront's row range
-    int32_t *res_wave = nullptr;   // [2][waves+1]: first row, first tile of each wavefront
-    uint64_t *res_slot = nullptr;  // [B][2][res_grid][4] stamped all-reduce partials
+    int32_t *res_wave = nullptr;   // [2][waves+1]: first row, first tile of each wavefront;
+                                   // then each workgroup's barrier dependencies
+    uint64_t *res_slot = nullptr;  // [B][2][res_grid][4] stamped all-reduce partials, then
+                                   // [B][res_grid] barrier stamps
     void *res_vals = nullptr;      // [B][padded nnz] batch-major values (B > 1)
     uint8_t *res_roff8 = nullptr;  // row offsets of the tiles as bytes (TileDesc.rpos)
     uint16_t *res_col16 = nullptr; // columns minus their tile's smallest (res_narrow)

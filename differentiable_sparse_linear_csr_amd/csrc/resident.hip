@@ -34,6 +34,7 @@
 // failure instead of hanging.
 #include "common.h"
 
+#include <algorithm>
 #include <vector>
 
 namespace sla {
@@ -96,9 +97,12 @@ __device__ __forceinline__ double uniform(double v) {
 }
 
 struct GridSync {
-    uint64_t *slot;  // [2][G][2 * kMaxC] stamped halves of each workgroup's partials
-    int G;           // workgroups of one system
-    int lb;          // this workgroup's index among them
+    uint64_t *slot;      // [2][G][2 * kMaxC] stamped halves of each workgroup's partials
+    uint64_t *flag;      // [G] the last barrier each workgroup has arrived at
+    const int32_t *dep;  // [G + 1] starts (absolute), then the lists: whose rows a
+                         // workgroup's rows read, for each one in row order
+    int G;               // workgroups of one system
+    int lb;              // this workgroup's index among them
 };
 constexpr int kMaxC = 2;
 
@@ -177,6 +181,42 @@ __device__ __forceinline__ bool grid_allreduce(const GridSync &gs, uint32_t seq,
     return true;
 }
 
+// Point-to-point barrier: every global store this workgroup made before the
+// call is complete, then it stamps its flag with bseq and waits only for the
+// workgroups its rows read from (list L of gs.dep, launch indices) to stamp
+// theirs. A workgroup stamps its flag again only after the next all-reduce,
+// which it cannot pass before every other workgroup has left this wait, so
+// one flag per workgroup suffices. Returns false on a timed-out wait.
+__device__ __forceinline__ bool grid_wait_deps(const GridSync &gs, uint32_t bseq, int L, double *lds) {
+    const int t = threadIdx.x;
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t == 0)
+        __hip_atomic_store(gs.flag + gs.lb, (uint64_t)bseq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t < 64) {
+        const int d0 = gs.dep[L], d1 = gs.dep[L + 1];
+        uint32_t spins = 0;
+        bool done = false;
+        while (true) {
+            bool arrived = true;
+            for (int q = d0 + t; q < d1; q += 64)
+                arrived &= __hip_atomic_load(gs.flag + gs.dep[q], __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) == (uint64_t)bseq;
+            if (__all(arrived)) {
+                done = true;
+                break;
+            }
+            if (++spins > kSpinLimit) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (t == 0) lds[kMaxC] = done ? 1.0 : 0.0;
+    }
+    __syncthreads();
+    const bool ok = lds[kMaxC] != 0.0;
+    __syncthreads();
+    return ok;
+}
+
 template <typename T>
 __device__ __forceinline__ void store_shared(T *p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -208,6 +248,7 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
     T *pg = pg_all + (int64_t)sys * n;
     SysState *__restrict__ st = st_all + sys;
     gs.slot += (size_t)sys * 2 * gs.G * (2 * kMaxC);
+    gs.flag += (size_t)sys * gs.G;
     gs.lb = lbk;
 
     const int lane = threadIdx.x & 63;
@@ -254,7 +295,7 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
         s_bb += (double)bv * (double)bv;
         s_rz += (double)bv * z;
     }
-    uint32_t seq = 1;
+    uint32_t seq = 1, bseq = 1;
     bool ok;
     double bb, rho;
     {
@@ -479,11 +520,9 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
             pr[j] = (T)((double)dl[64 * j] * (double)rr[j] + beta * (double)pr[j]);
             if (64 * j < nl) store_shared(pw + 64 * j, pr[j]);
         }
-        {
-            const double vv[1] = {0.0};
-            double tot[1];
-            ok = grid_allreduce<1>(gs, seq++, vv, tot, lds, true);
-        }
+        // only the workgroups whose rows the next product reads need to
+        // have written theirs
+        ok = grid_wait_deps(gs, bseq++, lb, lds);
     }
 #pragma unroll
     for (int j = 0; j < kRJ; ++j)
@@ -597,6 +636,30 @@ void build_plan(Handle &h, int64_t G, int64_t rpw, hipStream_t s) {
             wave[(size_t)(waves + 1 + g * kRW + v)] = (int32_t)t;
         }
     }
+    // For the barrier before each product: for every workgroup (rows
+    // [L per, (L + 1) per)), the other workgroups owning a column of its rows,
+    // as launch indices (logical L runs as (L % (G / 8)) * 8 + L / (G / 8))
+    {
+        const int64_t per = rpw * kRW, X = G / kXcds;
+        const size_t base = wave.size();
+        wave.resize(base + (size_t)G + 1);
+        std::vector<int64_t> seen((size_t)G, -1);
+        for (int64_t L = 0; L < G; ++L) {
+            wave[base + (size_t)L] = (int32_t)(wave.size() - base);
+            const int64_t ra = L * per < n ? L * per : n, rb = (L + 1) * per < n ? (L + 1) * per : n;
+            std::vector<int32_t> list;
+            for (int64_t k = (int64_t)rp[(size_t)ra]; k < (int64_t)rp[(size_t)rb]; ++k) {
+                const int64_t o = col[(size_t)k] / per;
+                if (o != L && seen[(size_t)o] != L) {
+                    seen[(size_t)o] = L;
+                    list.push_back((int32_t)((o % X) * kXcds + o / X));
+                }
+            }
+            std::sort(list.begin(), list.end());
+            wave.insert(wave.end(), list.begin(), list.end());
+        }
+        wave[base + (size_t)G] = (int32_t)(wave.size() - base);
+    }
     // a lane reads 4 bytes at rpos + 4 l for 4 l <= the tile's row count
     roff8.resize(roff8.size() + 256, 0);
     h.res_narrow = narrow;
@@ -623,7 +686,7 @@ void build_plan(Handle &h, int64_t G, int64_t rpw, hipStream_t s) {
     }
     h.res_tiles = (ResTile *)dalloc(h, sizeof(ResTile) * (rt.size() + 1));
     h.res_wave = (int32_t *)dalloc(h, sizeof(int32_t) * wave.size());
-    h.res_slot = (uint64_t *)dalloc(h, sizeof(uint64_t) * (size_t)(2 * G * 2 * kMaxC) * h.B);
+    h.res_slot = (uint64_t *)dalloc(h, sizeof(uint64_t) * (size_t)(2 * G * 2 * kMaxC + G) * h.B);
     if (h.B > 1)
         h.res_vals = dalloc(h, (size_t)((h.nnz + 31) / 32 * 32) * h.B * h.vbytes + 256);
     if (!rt.empty())
@@ -664,7 +727,8 @@ bool launch(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStr
     const T *bp = (const T *)b;
     T *xo = (T *)x;
     T *pg = (T *)h.p;
-    GridSync gs{h.res_slot, (int)h.res_grid, 0};
+    GridSync gs{h.res_slot, h.res_slot + (size_t)(2 * h.res_grid * 2 * kMaxC) * h.B,
+                h.res_wave + 2 * (waves + 1), (int)h.res_grid, 0};
     const int B = h.B;
     const int64_t n = h.n;
     SysState *st = h.st;
@@ -733,7 +797,7 @@ bool resident_ready(Handle &h, hipStream_t s) {
 // (sequence numbers start at 1).
 bool resident_solve(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStream_t s) {
     SLA_HIP(hipMemsetAsync(h.res_slot, 0,
-                           sizeof(uint64_t) * (size_t)(2 * h.res_grid * 2 * kMaxC) * h.B, s));
+                           sizeof(uint64_t) * (size_t)(2 * h.res_grid * 2 * kMaxC + h.res_grid) * h.B, s));
     hipEvent_t a = nullptr, e = nullptr;
     if (h.profile) {
         SLA_HIP(hipEventCreate(&a));
