@@ -18,7 +18,8 @@
 //   B   x += alpha p, r -= alpha q, z = dinv r; r.z and r.r
 //   R2  grid all-reduce -> stopping test, iteration budget, beta
 //   C   p = z + beta p; own rows written to the global copy
-//   R3  grid barrier: the copy is complete before the next gathers
+//   R3  barrier: the copy is complete before the next gathers, waiting only
+//       for the workgroups that own columns of this workgroup's rows
 // so HBM sees the matrix, the p gathers and the p store per iteration.
 //
 // A batch of B systems sharing the pattern runs as B independent groups of
