@@ -313,9 +313,25 @@ def test_autograd_through_solve_with_duplicates():
     assert rel(host(x2), xo / 1.5) <= 1e-9
 
 
+def block_chains_coo(n=65536, block=512, seed=5):
+    """Block-diagonal SPD matrix: independent 1D chains of `block` rows
+    (diagonal 2 + U(0, 1), couplings -1 inside a chain). At 65 536 rows the
+    single-kernel solve runs 128 workgroups of 512 rows, one chain each, so no
+    workgroup waits for another before a product (empty dependency lists)."""
+    rng = np.random.default_rng(seed)
+    i = np.arange(n)
+    inner = (i % block) != block - 1          # row i couples to i + 1
+    up = i[inner]
+    r = np.concatenate([i, up, up + 1])
+    c = np.concatenate([i, up + 1, up])
+    v = np.concatenate([2.0 + rng.uniform(0.0, 1.0, n), -np.ones(2 * up.size)])
+    return n, r.astype(np.int64), c.astype(np.int64), v
+
+
 def resident_cases():
     r, c, v = adversarial.random_spd_coo(30011, 9.0, 21, skew=False)  # irregular, none past 128
     return {
+        "block_chains_65536": block_chains_coo(),
         "poisson2d_64": make_workload("poisson2d_64"),
         "diffusion3d_128_s40": make_workload("diffusion3d_128", size=40),
         "knn_laplacian_2m_s60000": make_workload("knn_laplacian_2m", size=60000),
@@ -325,7 +341,7 @@ def resident_cases():
 
 
 @pytest.mark.parametrize("name", ["poisson2d_64", "diffusion3d_128_s40", "knn_laplacian_2m_s60000",
-                                  "random_spd_30011", "diffusion3d_128_s70"])
+                                  "random_spd_30011", "diffusion3d_128_s70", "block_chains_65536"])
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
 def test_single_kernel_solve_matches_oracle_and_multi_kernel_path(name, dtype):
     case = resident_cases()[name]
