@@ -260,7 +260,7 @@ def main() -> int:
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library's path runs on a single MI355X "
-              "(multi-GPU sharding is described in DESIGN.md, not built). Use --gpus 1.",
+              "(sharding across GPUs is designed, not built). Use --gpus 1.",
               file=sys.stderr)
         return 2
 
