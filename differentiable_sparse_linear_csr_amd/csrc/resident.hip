@@ -106,6 +106,9 @@ struct GridSync {
     int lb;              // this workgroup's index among them
 };
 constexpr int kMaxC = 2;
+// workgroups one polling lane covers: a system has at most 64 * kPollSlots
+// workgroups, so every poll round issues all its loads before waiting on any
+constexpr int kPollSlots = 4;
 
 // Grid all-reduce of C values (block totals, valid in every thread).
 // A partial travels as two 64-bit words, (seq << 32 | upper half) and
@@ -145,18 +148,26 @@ __device__ __forceinline__ bool grid_allreduce(const GridSync &gs, uint32_t seq,
             bool arrived = true;
 #pragma unroll
             for (int c = 0; c < C; ++c) a[c] = 0.0;
-            for (int q = t; q < gs.G; q += 64) {
-                uint64_t w[2 * C];
+            // a slot past G reads as arrived +0.0, which leaves the sum's bits
+            // unchanged (it starts at +0.0, so it is never -0.0)
+            uint64_t w[kPollSlots][2 * C];
 #pragma unroll
-                for (int k = 0; k < 2 * C; ++k) {
-                    w[k] = __hip_atomic_load(slot + q * (2 * kMaxC) + k, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-                    arrived &= (w[k] >> 32) == seq;
-                }
+            for (int i = 0; i < kPollSlots; ++i) {
+                const int q = t + 64 * i;
+#pragma unroll
+                for (int k = 0; k < 2 * C; ++k)
+                    w[i][k] = q < gs.G ? __hip_atomic_load(slot + q * (2 * kMaxC) + k, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT)
+                                       : stamp;
+            }
+#pragma unroll
+            for (int i = 0; i < kPollSlots; ++i) {
+#pragma unroll
+                for (int k = 0; k < 2 * C; ++k) arrived &= (w[i][k] >> 32) == seq;
 #pragma unroll
                 for (int c = 0; c < C; ++c)
-                    a[c] += __longlong_as_double((int64_t)(((w[2 * c] & 0xffffffffull) << 32) |
-                                                           (w[2 * c + 1] & 0xffffffffull)));
+                    a[c] += __longlong_as_double((int64_t)(((w[i][2 * c] & 0xffffffffull) << 32) |
+                                                           (w[i][2 * c + 1] & 0xffffffffull)));
             }
             if (__all(arrived)) {
                 done = true;
@@ -200,9 +211,16 @@ __device__ __forceinline__ bool grid_wait_deps(const GridSync &gs, uint32_t bseq
         bool done = false;
         while (true) {
             bool arrived = true;
-            for (int q = d0 + t; q < d1; q += 64)
-                arrived &= __hip_atomic_load(gs.flag + gs.dep[q], __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT) == (uint64_t)bseq;
+            uint64_t f[kPollSlots];
+#pragma unroll
+            for (int i = 0; i < kPollSlots; ++i) {
+                const int q = d0 + t + 64 * i;
+                f[i] = q < d1 ? __hip_atomic_load(gs.flag + gs.dep[q], __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT)
+                              : (uint64_t)bseq;
+            }
+#pragma unroll
+            for (int i = 0; i < kPollSlots; ++i) arrived &= f[i] == (uint64_t)bseq;
             if (__all(arrived)) {
                 done = true;
                 break;
@@ -782,6 +800,7 @@ bool resident_ready(Handle &h, hipStream_t s) {
     int64_t G = (h.n + (int64_t)kRW * 64 - 1) / ((int64_t)kRW * 64);
     G = (G + kXcds - 1) / kXcds * kXcds;
     if (G > gmax) G = gmax;
+    if (G > 64 * kPollSlots) G = 64 * kPollSlots;
     const int64_t waves = G * kRW;
     const int64_t rpw = (h.n + waves - 1) / waves;
     if (rpw > 64 * kRJ) return false;
