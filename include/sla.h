@@ -94,7 +94,7 @@ enum {
                                    measured; 2 is kept as the explicit form). Applicable: not
                                    segmented, no row longer than 128 entries, n <= 8192
                                    rows per CU of each system's share of the CUs (a
-                                   multiple of 8 CUs per system), cooperative launch
+                                   multiple of 8 CUs per system, at most 256), cooperative launch
                                    available. A cooperative launch refused at solve time
                                    (not all workgroups can run at once, or another process
                                    holds the device's cooperative-launch resource) falls
