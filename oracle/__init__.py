@@ -45,6 +45,8 @@ def lib() -> ctypes.CDLL:
         P = ctypes.c_void_p
         i64, i32, f64 = ctypes.c_int64, ctypes.c_int32, ctypes.c_double
         L.orc_num_threads.restype = ctypes.c_int
+        L.orc_set_num_threads.argtypes = [ctypes.c_int]
+        L.orc_set_num_threads.restype = None
         L.orc_coo_to_csr.argtypes = [i64, i64, i32, P, P, i32, P, P, P, P, P, P]
         L.orc_check_csr.argtypes = [i64, i64, P, P]
         L.orc_is_symmetric_f64.argtypes = [i64, P, P, P]
@@ -99,6 +101,12 @@ def _check(code: int, what: str):
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(k: int) -> None:
+    """Threads of the oracle's later parallel loops in this thread (results
+    do not depend on it)."""
+    lib().orc_set_num_threads(int(k))
 
 
 def coo_to_csr(n: int, rows, cols, vals):

@@ -59,6 +59,16 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* threads for the calling thread's later parallel loops (timing only:
+ * results do not depend on it) */
+void orc_set_num_threads(int k) {
+#ifdef _OPENMP
+    if (k > 0) omp_set_num_threads(k);
+#else
+    (void)k;
+#endif
+}
+
 /* ------------------------------------------------------------------ assembly
  * COO -> CSR. Reading (pages silent on format and duplicates): entries are
  * ordered by (row, col) with a stable sort, so equal positions keep their
