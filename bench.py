@@ -10,6 +10,11 @@ pattern is shared by every step. Inputs are resident in HBM before timing.
 
 value = PCG iterations (forward + adjoint) per second over the timed steps.
 
+With no --workload, the run covers both points of the metric: the 2.1M-DOF
+3D diffusion (the line's own figures) and then the 133M-DOF 2D Poisson share
+(extra.dof_133m: 1 warm-up + 3 timed 500-iteration solves, its own roofline
+and CPU baseline).
+
 Printed as one JSON line. `roofline` covers the dominant kernel: its
 algorithmic bytes per launch over its average launch duration, measured with
 hipEvents on the stream it is launched on after the timed steps:
@@ -42,6 +47,7 @@ sys.path.insert(0, ROOT)
 METRIC = "Jacobi-PCG iterations/sec and achieved HBM GB/s (% of peak) at 2M and 133M DOF"
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "diffusion3d_128"
+LARGE_WORKLOAD = "poisson2d_11548"
 # sources of the kernel the roofline covers, per kernel tag (counter files are
 # only used while these sources are unchanged)
 KERNEL_SOURCES = {"spmv_dot": ["spmv.hip", "common.h"],
@@ -71,25 +77,48 @@ def kernel_source_hash(tag: str) -> str:
 def load_traffic(workload: str, tag: str):
     """Per-launch HBM bytes of the roofline kernel from rocprofv3 counters, if
     they were taken on the current kernel source
-    (profiles/<tag>_counters_<workload>.json)."""
-    path = os.path.join(ROOT, "profiles", f"{tag}_counters_{workload}.json")
+    (profiles/<tag>_counters_<workload>.json), and where they come from."""
+    rel = f"profiles/{tag}_counters_{workload}.json"
+    path = os.path.join(ROOT, rel)
     if not os.path.exists(path):
-        return None
+        return None, None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_source_hash") != kernel_source_hash(tag):
-        return None
-    return rec.get("hbm_bytes_per_launch")
+        return None, f"{rel} was taken on another kernel source: not used"
+    return rec.get("hbm_bytes_per_launch"), (
+        f"{rel}: rocprofv3 FETCH_SIZE + WRITE_SIZE per launch of this kernel in a separate run "
+        f"of the same command, each scaled by the counter's reading for a 1 GiB device copy "
+        f"(fetch x{rec['calibration']['fetch_factor']:.2f}, write "
+        f"x{rec['calibration']['write_factor']:.2f}); not measured in this run")
 
 
-def cpu_baseline(w, budget_s: float):
+def host_info() -> dict:
+    """CPU model, NUMA nodes and the CPUs this process may run on."""
+    import glob
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    numa = len(glob.glob("/sys/devices/system/node/node[0-9]*")) or None
+    return {"cpu_model": model, "numa_nodes": numa, "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline(w, budget_s: float, budget_1t_s: float = 0.0):
     """The oracle as it stands, on the host cores: iterations/s of the forward
     solve (Jacobi-PCG, or Jacobi-BiCGStab for a non-symmetric workload) on the
     same matrix and right-hand side, over a bounded number of iterations (the
-    first ones of the same solve)."""
+    first ones of the same solve), with all threads and (budget_1t_s > 0)
+    with one thread."""
     import numpy as np
     import oracle
 
+    threads = oracle.num_threads()
     if "seg_rows" in w.extra:
         # every member is its own system: the oracle solves them one by one,
         # each for the same bounded number of iterations
@@ -100,45 +129,57 @@ def cpu_baseline(w, budget_s: float):
             ref = oracle.coo_to_csr(seg[q + 1] - seg[q], w.rows[sel] - seg[q], w.cols[sel] - seg[q],
                                     w.vals[sel])
             members.append((ref, w.b[seg[q]:seg[q + 1]]))
-        t0 = time.perf_counter()
-        for ref, bq in members:
-            oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], bq, 0.0, 2)
-        probe = (time.perf_counter() - t0) / 2
-        iters = int(max(2, min(w.maxit, budget_s / max(probe, 1e-9))))
-        t0 = time.perf_counter()
-        total = 0
-        for ref, bq in members:
-            _, it, _, _ = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], bq, 0.0, iters)
-            total += int(it)
-        dt = time.perf_counter() - t0
-        return {"value": total / dt, "unit": "iterations/s", "cores": oracle.num_threads(),
-                "kind": "oracle",
-                "sample": f"first {iters} Jacobi-PCG iterations (tol 0) of each of the "
-                          f"{len(members)} members of {w.name}, solved one by one; {dt:.1f} s"}
-    if w.fmt == "csr":
-        ref = {"row_ptr": w.row_ptr.astype(np.int64), "col": w.cols.astype(np.int64)}
-        vals = w.vals
+
+        def run(iters):
+            total = 0
+            for ref, bq in members:
+                _, it, _, _ = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], bq, 0.0, iters)
+                total += int(it)
+            return total
+        what = f"Jacobi-PCG iterations (tol 0) of each of the {len(members)} members of {w.name}, " \
+               f"solved one by one"
+        probe_iters = 2
     else:
-        ref = oracle.coo_to_csr(w.n, w.rows, w.cols, w.vals)
-        vals = ref["vals"]
-    b = w.b
-    bicg = w.extra.get("method") == "bicgstab"
-    solve = oracle.bicgstab if bicg else oracle.pcg
-    t0 = time.perf_counter()
-    solve(ref["row_ptr"], ref["col"], vals, b, 0.0, 5)
-    probe = (time.perf_counter() - t0) / 5
-    iters = int(max(5, min(w.maxit, budget_s / max(probe, 1e-9))))
-    t0 = time.perf_counter()
-    _, it, _, _ = solve(ref["row_ptr"], ref["col"], vals, b, 0.0, iters)
-    dt = time.perf_counter() - t0
-    it = int(np.sum(it))
-    per_sys = w.batch
-    name = "Jacobi-BiCGStab" if bicg else "Jacobi-PCG"
-    return {"value": it / dt, "unit": "iterations/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"first {iters} {name} iterations (tol 0) of the forward solve of "
-                      f"{w.name} ({per_sys} system(s)), oracle CSR built from the same input; "
-                      f"{dt:.1f} s"}
+        if w.fmt == "csr":
+            ref = {"row_ptr": w.row_ptr.astype(np.int64), "col": w.cols.astype(np.int64)}
+            vals = w.vals
+        else:
+            ref = oracle.coo_to_csr(w.n, w.rows, w.cols, w.vals)
+            vals = ref["vals"]
+        bicg = w.extra.get("method") == "bicgstab"
+        solve = oracle.bicgstab if bicg else oracle.pcg
+
+        def run(iters):
+            _, it, _, _ = solve(ref["row_ptr"], ref["col"], vals, w.b, 0.0, iters)
+            return int(np.sum(it))
+        name = "Jacobi-BiCGStab" if bicg else "Jacobi-PCG"
+        what = f"{name} iterations (tol 0) of the forward solve of {w.name} ({w.batch} " \
+               f"system(s)), oracle CSR built from the same input"
+        probe_iters = 5 if w.n * w.batch < (1 << 24) else 1
+
+    def timed(budget, probe):
+        t0 = time.perf_counter()
+        run(probe)
+        per = (time.perf_counter() - t0) / probe
+        iters = int(max(1, min(w.maxit, budget / max(per, 1e-9))))
+        t0 = time.perf_counter()
+        it = run(iters)
+        dt = time.perf_counter() - t0
+        return it / dt, iters, dt
+
+    rate, iters, dt = timed(budget_s, probe_iters)
+    out = {"value": round(rate, 3), "unit": "iterations/s", "cores": threads, "kind": "oracle",
+           "sample": f"first {iters} {what}; {dt:.1f} s on {threads} threads"}
+    if budget_1t_s > 0:
+        oracle.set_num_threads(1)
+        try:
+            rate1, iters1, dt1 = timed(budget_1t_s, 1)
+        finally:
+            oracle.set_num_threads(threads)
+        out["value_1_thread"] = round(rate1, 3)
+        out["sample_1_thread"] = f"first {iters1} iterations of the same solve; {dt1:.1f} s"
+    out.update(host_info())
+    return out
 
 
 def run_inverse(args, N: int = 128, S: int = 4) -> int:
@@ -240,33 +281,12 @@ def run_inverse(args, N: int = 128, S: int = 4) -> int:
     return 0
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--check-interval", type=int, default=16)
-    ap.add_argument("--ordinary-launch", action="store_true",
-                    help="start the single-kernel solve with an ordinary launch instead of "
-                         "a cooperative one (for profilers that cannot follow cooperative "
-                         "launches); same kernel, same grid")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
-    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
-                    help="after the measurement, copy a buffer of this size 3 times with a plain "
-                         "device copy kernel (reference for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
-    args = ap.parse_args()
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this library's path runs on a single MI355X "
-              "(sharding across GPUs is designed, not built). Use --gpus 1.",
-              file=sys.stderr)
-        return 2
-
-    if args.workload == "inverse_conductivity_128":
-        return run_inverse(args)
-
+def measure(args, name: str, steps: int, warmup: int, cpu_budget: float,
+            cpu_1t_budget: float) -> dict:
+    """One workload: handle built once, `warmup` untimed and `steps` timed
+    steps, the roofline kernel's launches timed on its stream, and the CPU
+    oracle's rate (cpu_budget seconds of work with all threads, cpu_1t_budget
+    with one; 0 skips it). Returns the JSON record."""
     import numpy as np
     import torch
     import differentiable_sparse_linear_csr_amd as sla
@@ -275,7 +295,7 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
-    w = make_workload(args.workload)
+    w = make_workload(name)
     print(f"[bench] workload {w.name}: n={w.n} nnz={w.nnz} batch={w.batch} dtype={w.dtype} "
           f"(generated in {time.perf_counter() - t_gen:.1f} s)", file=sys.stderr, flush=True)
 
@@ -313,18 +333,18 @@ def main() -> int:
             its = [i + j for i, j in zip(its, ainfo.iterations)]
         return its, info
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     total_its = 0
-    for _ in range(args.steps):
+    for _ in range(steps):
         its, info = step()
         total_its += sum(its)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     value = total_its / elapsed
-    ms_per_step = elapsed / args.steps * 1e3
+    ms_per_step = elapsed / steps * 1e3
     fwd_its = info.iterations
 
     # profiled step: hipEvents around every kernel launch, on the launch stream
@@ -383,7 +403,7 @@ def main() -> int:
                               minlength=len(seg) - 1)
         per_step = {k: sum(i * algorithmic_bytes(seg[q + 1] - seg[q], int(seg_nnz[q]), 1, V, R)[k]
                            for q, i in enumerate(its)) for k in ("iter_3k", "iter_min")}
-        job_bps = {k: v * args.steps / elapsed for k, v in per_step.items()}
+        job_bps = {k: v * steps / elapsed for k, v in per_step.items()}
     else:
         # value counts system-iterations; one batched iteration moves ab[k]
         # for all B systems
@@ -418,15 +438,15 @@ def main() -> int:
         kernel = ("k_spmv_bvec (fused q = A p, p.q partials, alpha; per-launch events)" if w.batch > 1
                   else "k_spmv_tile on P A P^T (fused q = A p, p.q partials; per-launch events)")
     achieved = bytes_launch / (avg_ms * 1e-3) / 1e9
-    traffic = load_traffic(w.name, "cg_resident" if res_launches > 0 else "spmv_dot")
+    traffic, traffic_src = load_traffic(w.name, "cg_resident" if res_launches > 0 else "spmv_dot")
 
     out = {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "iterations/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 3),
         "higher_is_better": True,
         "scaling": "weak",
@@ -453,6 +473,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "traffic_source": traffic_src,
             "algorithmic_bytes_per_launch": round(bytes_launch),
             "avg_launch_ms": round(avg_ms, 5),
             "launches_timed": launches,
@@ -490,20 +511,89 @@ def main() -> int:
             "layout": layout,
         },
     }
-    if not args.no_cpu_baseline:
+    matrix_mb = (ab["spmv"] - 2 * V * w.n * w.batch) / 1e6
+    if matrix_mb < 256.0:
+        out["roofline"]["note"] = (
+            f"the matrix ({matrix_mb:.0f} MB as counted here) fits the 256 MB Infinity Cache, "
+            f"which can serve it from one iteration to the next: 'achieved' and 'traffic' count "
+            f"bytes the L2 reads from the Infinity Cache or HBM"
+            + ("; extra.dof_133m is the point whose matrix cannot stay there"
+               if name == DEFAULT_WORKLOAD else ""))
+    if cpu_budget > 0:
         print("[bench] timing the CPU oracle ...", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(w, cpu_budget, cpu_1t_budget)
     else:
         out["cpu_baseline"] = None
+    del A, cols, vals, b, g, x
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None,
+                    help=f"one workload only (default: {DEFAULT_WORKLOAD}, then {LARGE_WORKLOAD} "
+                         f"as extra.dof_133m)")
+    ap.add_argument("--check-interval", type=int, default=16)
+    ap.add_argument("--ordinary-launch", action="store_true",
+                    help="start the single-kernel solve with an ordinary launch instead of "
+                         "a cooperative one (for profilers that cannot follow cooperative "
+                         "launches); same kernel, same grid")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--cpu-budget-1t", type=float, default=5.0,
+                    help="seconds of oracle work on one thread")
+    ap.add_argument("--large-steps", type=int, default=3,
+                    help=f"timed steps of {LARGE_WORKLOAD} in the default run")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after the measurement, copy a buffer of this size 3 times with a plain "
+                         "device copy kernel (reference for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library's path runs on a single MI355X "
+              "(sharding across GPUs is designed, not built). Use --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    if args.workload == "inverse_conductivity_128":
+        return run_inverse(args)
+
+    import torch
+
+    cpu = 0.0 if args.no_cpu_baseline else args.cpu_budget
+    cpu1 = 0.0 if args.no_cpu_baseline else args.cpu_budget_1t
+    if args.workload is not None:
+        out = measure(args, args.workload, args.steps, args.warmup, cpu, cpu1)
+    else:
+        out = measure(args, DEFAULT_WORKLOAD, args.steps, args.warmup, cpu, cpu1)
+        # the metric's second point: one GPU's share of the 400M-DOF solve
+        big = measure(args, LARGE_WORKLOAD, args.large_steps, 1, 0.0 if cpu == 0 else 10.0,
+                      0.0 if cpu1 == 0 else 8.0)
+        out["extra"]["dof_133m"] = {
+            "workload": big["config"]["workload"], "n": big["config"]["n"],
+            "nnz": big["config"]["nnz"], "value": big["value"], "unit": big["unit"],
+            "steps": big["steps"], "warmup": big["warmup"], "ms_per_step": big["ms_per_step"],
+            "step": big["config"]["step"], "tol": big["config"]["tol"],
+            "maxit": big["config"]["maxit"], "roofline": big["roofline"],
+            **{k: big["extra"][k] for k in ("path", "iteration_ms", "iteration_gbps_3k",
+                                            "iteration_frac_3k", "iteration_kernels_ms",
+                                            "spmv_ms", "spmv_gbps", "kernel_avg_ms")},
+            "cpu_baseline": big["cpu_baseline"]}
     print(json.dumps(out), flush=True)
     if args.calibrate_copy_mib > 0:
-        src = torch.ones(args.calibrate_copy_mib << 17, dtype=torch.float64, device=dev)
+        src = torch.ones(args.calibrate_copy_mib << 17, dtype=torch.float64, device="cuda:0")
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
         print(f"[bench] calibration: copied {args.calibrate_copy_mib} MiB x3", file=sys.stderr)
     return 0
+
 
 
 if __name__ == "__main__":

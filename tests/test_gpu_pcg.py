@@ -473,3 +473,38 @@ def test_ordinary_launch_of_the_single_kernel_solve():
     assert i1 == i0 and a1 == a0
     assert x1.tobytes() == x0.tobytes() and gb1.tobytes() == gb0.tobytes()
     assert gv1.tobytes() == gv0.tobytes()
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_batched_single_kernel_largest_register_shape(dtype):
+    """32 systems of 65 536 rows: each system's group has 8 workgroups (256
+    CUs shared by 32 groups), so every wavefront owns 1024 rows, 16 per lane,
+    the largest register shape of the single-kernel solve. Every system's x
+    and adjoint against its own oracle solve, whole vectors."""
+    N, B = 256, 32
+    r, c, V, b = shifted_batch(N, B, dtype, seed=12)
+    n = N * N
+    tol = 1e-10 if dtype == np.float64 else 1e-5
+    ref = oracle.coo_to_csr(n, r, c, V)
+    xo, ito, _, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, tol, 4000)
+    g = np.random.default_rng(13).standard_normal((B, n)).astype(dtype)
+    lam, gvo, ita, _, oca = oracle.adjoint(ref["row_ptr"], ref["col"], ref["vals"], xo, g, tol,
+                                           4000)
+    A = coo_handle(n, r, c, V)
+    print(f"batched single-kernel B={B} n={n} {np.dtype(dtype).name}", flush=True)
+    A.profile_reset()
+    A.set_option(_lib.SLA_OPT_PROFILE, 1)
+    x, info = A.solve_raw(dev(b), tol, 4000)
+    gb, gv, ainfo = A.adjoint_raw(x, dev(g), tol, 4000)
+    prof = A.profile()
+    A.set_option(_lib.SLA_OPT_PROFILE, 0)
+    assert prof["cg_resident"][0] == 2 and prof["spmv_dot"][0] == 0, prof
+    X, GB, GV = host(x), host(gb), host(gv)
+    xtol, gtol = (1e-8, 1e-8) if dtype == np.float64 else (1e-4, 1e-3)
+    for s in range(B):
+        assert info.status[s] == oco[s] == oracle.CONVERGED, s
+        assert abs(info.iterations[s] - ito[s]) <= 2, (s, info.iterations[s], ito[s])
+        assert rel(X[s], xo[s]) <= xtol, (s, rel(X[s], xo[s]))
+        assert ainfo.status[s] == oca[s] == oracle.CONVERGED, s
+        assert abs(ainfo.iterations[s] - ita[s]) <= 2, s
+        assert rel(GB[s], lam[s]) <= gtol and rel(GV[s], gvo[s]) <= gtol, s
