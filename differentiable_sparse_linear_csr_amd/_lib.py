@@ -33,6 +33,9 @@ SLA_CONVERGED, SLA_MAXIT, SLA_BREAKDOWN = 0, 1, 2
 SLA_OPT_CHECK_INTERVAL, SLA_OPT_USE_GRAPH, SLA_OPT_PROFILE, SLA_OPT_RESIDENT = 1, 2, 3, 4
 SLA_OPT_FUSED_UPDATE = 5
 SLA_OPT_COOPERATIVE = 6
+SLA_OPT_SPIN_LIMIT = 7
+SLA_PATH_NONE, SLA_PATH_SINGLE_KERNEL, SLA_PATH_PER_STEP = 0, 1, 2
+SLA_FALLBACK_COOPERATIVE_REFUSED, SLA_FALLBACK_WAIT_TIMED_OUT = 1, 2
 KERNELS = {"spmv_dot": 0, "update": 1, "direction": 2, "init": 3, "spmv": 4, "grad": 5,
            "cg_resident": 6}
 
@@ -41,7 +44,8 @@ EXPORTS = ["sla_csr_create", "sla_csr_create_segmented", "sla_csr_get_segments",
            "sla_csr_get_values",
            "sla_csr_gather_to_input", "sla_csr_set_option", "sla_spmv", "sla_spmv_backward",
            "sla_pcg_solve", "sla_adjoint_backward", "sla_bicgstab_solve", "sla_bicgstab_adjoint",
-           "sla_profile_get", "sla_profile_reset", "sla_csr_memory", "sla_csr_get_layout", "sla_csr_destroy", "sla_last_error", "sla_version"]
+           "sla_profile_get", "sla_profile_reset", "sla_csr_memory", "sla_csr_get_layout",
+           "sla_csr_get_last_path", "sla_csr_destroy", "sla_last_error", "sla_version"]
 
 
 class SlaError(RuntimeError):
@@ -91,6 +95,7 @@ def load() -> ctypes.CDLL:
     L.sla_profile_reset.argtypes = [P]
     L.sla_csr_memory.argtypes = [P, pi64]
     L.sla_csr_get_layout.argtypes = [P, pi32, pi32, pi64, pi64]
+    L.sla_csr_get_last_path.argtypes = [P, pi32, ctypes.POINTER(ctypes.c_uint32)]
     L.sla_csr_destroy.argtypes = [P]
     L.sla_csr_destroy.restype = None
     L.sla_last_error.argtypes = []

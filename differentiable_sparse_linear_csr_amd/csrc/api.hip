@@ -312,6 +312,14 @@ sla_status sla_csr_gather_to_input(sla_csr hd, const void *csr_order, void *inpu
 
 namespace sla {
 namespace {
+// a solve of `caller` ran on `ran` (the reordered or transposed handle, or
+// caller itself): record on the caller how it ran
+void record_path(Handle &caller, const Handle &ran) {
+    const Handle &r = ran.inner ? *ran.inner : ran;
+    caller.last_path = r.last_path;
+    caller.last_fallback = r.last_fallback;
+}
+
 void set_option(Handle *h, int32_t key, int64_t value) {
     switch (key) {
         case SLA_OPT_CHECK_INTERVAL:
@@ -330,6 +338,11 @@ void set_option(Handle *h, int32_t key, int64_t value) {
             break;
         case SLA_OPT_COOPERATIVE:
             h->res_coop = value != 0;
+            break;
+        case SLA_OPT_SPIN_LIMIT:
+            if (value < 0 || value > (int64_t)0xffffffffu)
+                fail(SLA_ERR_INVALID_ARG, "spin limit in [0, 2^32)");
+            h->spin_limit = (uint32_t)value;
             break;
         case SLA_OPT_FUSED_UPDATE:
             if (h->fuse_update != (value != 0)) {
@@ -400,6 +413,7 @@ sla_status sla_pcg_solve(sla_csr hd, const void *b, void *x, double tol, int32_t
                  "Jacobi preconditioning needs every diagonal entry present, positive and finite");
         if (h->inner) reordered_pcg(*h, b, x, tol, maxit, info, (hipStream_t)stream);
         else pcg(*h, b, x, tol, maxit, info, (hipStream_t)stream, false);
+        record_path(*h, *h);
     });
 }
 
@@ -416,6 +430,7 @@ sla_status sla_adjoint_backward(sla_csr hd, const void *x, const void *grad_x, v
         hipStream_t s = (hipStream_t)stream;
         if (h->inner) {
             reordered_adjoint(*h, x, grad_x, grad_b, grad_vals_out, tol, maxit, info, s);
+            record_path(*h, *h);
             return;
         }
         pcg(*h, grad_x, nullptr, tol, maxit, info, s, true);  // lambda stays in the workspace
@@ -444,6 +459,7 @@ sla_status sla_bicgstab_solve(sla_csr hd, const void *b, void *x, double tol, in
             fail(SLA_ERR_BAD_DIAGONAL,
                  "Jacobi preconditioning needs every diagonal entry present, non-zero and finite");
         any_bicgstab(*h, b, x, tol, maxit, info, (hipStream_t)stream);
+        record_path(*h, *h);
     });
 }
 
@@ -471,6 +487,7 @@ sla_status sla_bicgstab_adjoint(sla_csr hd, const void *x, const void *grad_x, v
             lam = h->lam_tmp;
         }
         any_bicgstab(at, grad_x, lam, tol, maxit, info, s);
+        record_path(*h, at);
         if (grad_vals_out) grad_vals(*h, lam, x, grad_vals_out, s);
         SLA_HIP(hipStreamSynchronize(s));
         if (h->profile) flush_profile(*h);
@@ -521,6 +538,15 @@ sla_status sla_csr_get_layout(sla_csr hd, int32_t *reordered, int32_t *narrow_co
         if (narrow_columns) *narrow_columns = sv->all_narrow ? 1 : 0;
         if (tiles) *tiles = sv->ntiles;
         if (long_rows) *long_rows = sv->nlong;
+    });
+}
+
+sla_status sla_csr_get_last_path(sla_csr hd, int32_t *path, uint32_t *fallbacks) {
+    return guard([&] {
+        if (!hd) fail(SLA_ERR_INVALID_ARG, "null handle");
+        const Handle *h = reinterpret_cast<const Handle *>(hd);
+        if (path) *path = h->last_path;
+        if (fallbacks) *fallbacks = h->last_fallback;
     });
 }
 

@@ -481,7 +481,10 @@ void bicgstab(Handle &h, const void *b, void *x, double tol, int32_t maxit, sla_
     h.h_ctl->n_running = 0;
     h.h_ctl->epoch = ++h.epoch;
     h.h_ctl->error = 0;
+    h.h_ctl->spin_limit = h.spin_limit;
     SLA_HIP(hipMemcpyAsync(h.ctl, h.h_ctl, sizeof(Ctl), hipMemcpyHostToDevice, s));
+    h.last_path = kPathPerStep;   // its own kernels, none of which waits on another workgroup
+    h.last_fallback = 0;
     {
         int64_t g = (h.n + kBlock - 1) / kBlock;
         if (g > kMaxGrid) g = kMaxGrid;

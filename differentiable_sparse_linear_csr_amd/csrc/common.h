@@ -77,8 +77,17 @@ struct Ctl {
     int32_t maxit;
     int32_t n_running;
     uint32_t epoch;   // solve counter: with the iteration count it names a broadcast
-    int32_t error;    // set by a kernel whose bounded wait timed out
+    int32_t error;    // set by a kernel whose bounded wait timed out (sticky for the solve)
+    uint32_t spin_limit;  // polls a bounded grid-wide wait makes before it gives up
+    int32_t pad;
 };
+
+// polls of a bounded grid-wide wait before it gives up (about a second)
+constexpr uint32_t kDefaultSpinLimit = 1u << 22;
+
+// how the last solve on a handle ran (sla_csr_get_last_path)
+constexpr int32_t kPathNone = 0, kPathSingleKernel = 1, kPathPerStep = 2;
+constexpr uint32_t kFallbackCoopRefused = 1u, kFallbackWaitTimedOut = 2u;
 
 // Step scalars broadcast by the last workgroup of the fused update +
 // direction kernel to the others: gen = epoch << 32 | iteration number.
@@ -158,6 +167,9 @@ struct Handle {
     Ctl *ctl = nullptr;
     Bcast *bcast = nullptr;
     uint32_t epoch = 0;            // solves started on this handle
+    uint32_t spin_limit = kDefaultSpinLimit;  // bounded grid-wide waits (SLA_OPT_SPIN_LIMIT)
+    int32_t last_path = kPathNone; // how the last solve ran, and why not the preferred way
+    uint32_t last_fallback = 0;
     int64_t upd_dir_resident = 0;  // resident workgroups of the fused update + direction
     int64_t upd_dir_bv_resident = 0;  // the same for batches
     double *bcast_bv = nullptr;    // [2][kMaxBatch] beta and running flag per system

@@ -333,7 +333,19 @@ __global__ __launch_bounds__(kBlock) void k_direction_bv(int64_t nc, int B,
 // reported through ctl->error) and write p = z + beta p for their chunks from
 // registers, which saves reading r, p and dinv again and a launch.
 constexpr int kBvFusedGroups = 4;
-constexpr uint32_t kBcastSpins = 1u << 22;   // bounded waits for a broadcast
+
+// Entry check of the kernels of a fused step: nothing to do once no system
+// runs, or once a bounded wait of this solve has given up (ctl->error is
+// sticky). In the second case the first workgroup publishes "none running",
+// so the host stops launching and re-runs the solve on kernels without
+// grid-wide waits.
+__device__ __forceinline__ bool fused_step_idle(Ctl *ctl, int32_t *h_running) {
+    if (__hip_atomic_load(&ctl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) publish_running(ctl, h_running, 0);
+        return true;
+    }
+    return ctl->n_running == 0;
+}
 
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_update_dir_bv(int64_t nc, int B, T *__restrict__ x,
@@ -351,7 +363,7 @@ __global__ __launch_bounds__(kBlock) void k_update_dir_bv(int64_t nc, int B, T *
     __shared__ double blk[kMaxBatch];
     __shared__ double tot[2 * kMaxBatch];
     __shared__ int s_ok;
-    if (ctl->n_running == 0) return;
+    if (fused_step_idle(ctl, h_running)) return;
     const uint64_t gen =
         __hip_atomic_load(&bc->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
     const int Q = B / W;
@@ -441,16 +453,20 @@ __global__ __launch_bounds__(kBlock) void k_update_dir_bv(int64_t nc, int B, T *
         if (t == 0) __hip_atomic_store(&bc->gen, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (t == 0) {
+        const uint32_t limit = ctl->spin_limit;
         uint32_t spins = 0;
         int ok = 1;
         while (__hip_atomic_load(&bc->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != gen) {
-            if (++spins > kBcastSpins) {
+            if (++spins > limit) {
                 ok = 0;
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
         }
-        if (!ok) __hip_atomic_store(&ctl->error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!ok) {
+            __hip_atomic_store(&ctl->error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            publish_running(ctl, h_running, 0);
+        }
         s_ok = ok;
     }
     __syncthreads();
@@ -628,7 +644,7 @@ __global__ __launch_bounds__(kBlock) void k_update_dir1(int64_t n, T *__restrict
     __shared__ double tot[2];
     __shared__ double s_beta;
     __shared__ int s_run;
-    if (ctl->n_running == 0) return;  // one system: running or not
+    if (fused_step_idle(ctl, h_running)) return;  // one system: running or not
     const int tid = threadIdx.x;
     const uint64_t gen = ((uint64_t)ctl->epoch << 32) | (uint32_t)(st[0].iter + 1);
     // this workgroup's rows are loaded first, so their latency overlaps the
@@ -725,10 +741,11 @@ __global__ __launch_bounds__(kBlock) void k_update_dir1(int64_t n, T *__restrict
         }
     }
     if (tid == 0) {
+        const uint32_t limit = ctl->spin_limit;
         uint32_t spins = 0;
         bool ok = true;
         while (__hip_atomic_load(&bc->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != gen) {
-            if (++spins > kBcastSpins) {
+            if (++spins > limit) {
                 ok = false;
                 break;
             }
@@ -739,6 +756,7 @@ __global__ __launch_bounds__(kBlock) void k_update_dir1(int64_t n, T *__restrict
             s_run = __hip_atomic_load(&bc->running, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
             __hip_atomic_store(&ctl->error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            publish_running(ctl, h_running, 0);
             s_run = 0;
         }
     }
@@ -1099,11 +1117,13 @@ void spmv(Handle &h, const void *x, void *y, hipStream_t s) {
     }
 }
 
-// Solve A x = b for every system. b_user / x_user are [B][n]. With
-// keep_internal_solution the iterate stays in h.x (internal layout) and
-// x_user may be null.
-void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit, sla_info *info,
-         hipStream_t s, bool keep_internal_solution) {
+namespace {
+
+// One attempt at a solve (see pcg). Returns false, having done nothing the
+// caller can see, when a bounded grid-wide wait gave up; with allow_resident
+// false the single-kernel solve is not tried.
+bool pcg_attempt(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit,
+                 sla_info *info, hipStream_t s, bool keep_internal_solution, bool allow_resident) {
     Launcher L{h, s, h.profile};
     Launcher *lp = h.profile ? &L : nullptr;
     // control block: tolerance and budget (the counters stay zero between launches)
@@ -1112,33 +1132,45 @@ void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit,
     h.h_ctl->n_running = 0;
     h.h_ctl->epoch = ++h.epoch;
     h.h_ctl->error = 0;
+    h.h_ctl->spin_limit = h.spin_limit;
     SLA_HIP(hipMemcpyAsync(h.ctl, h.h_ctl, sizeof(Ctl), hipMemcpyHostToDevice, s));
     // the whole solve in one cooperative kernel (same recurrence; a batch
     // leaves x as [B][n] in q), unless the cooperative launch is refused
     // (see resident_solve): then the per-step kernels
-    if (h.nseg == 0 && resident_ready(h, s) &&
-        resident_solve(h, b_user, h.B == 1 ? h.x : h.q, tol, maxit, s)) {
-        const size_t bytes = (size_t)h.n * h.B * h.vbytes;
-        if (h.B == 1) {
-            if (!keep_internal_solution)
-                SLA_HIP(hipMemcpyAsync(x_user, h.x, bytes, hipMemcpyDeviceToDevice, s));
-        } else if (keep_internal_solution) {
-            transpose(h.q, h.x, h.B, h.n, h.vbytes, s);
-        } else {
-            SLA_HIP(hipMemcpyAsync(x_user, h.q, bytes, hipMemcpyDeviceToDevice, s));
+    if (allow_resident && h.nseg == 0 && resident_ready(h, s)) {
+        if (resident_solve(h, b_user, h.B == 1 ? h.x : h.q, tol, maxit, s)) {
+            // (if a wait gave up, the re-run overwrites what is copied here)
+            const size_t bytes = (size_t)h.n * h.B * h.vbytes;
+            if (h.B == 1) {
+                if (!keep_internal_solution)
+                    SLA_HIP(hipMemcpyAsync(x_user, h.x, bytes, hipMemcpyDeviceToDevice, s));
+            } else if (keep_internal_solution) {
+                transpose(h.q, h.x, h.B, h.n, h.vbytes, s);
+            } else {
+                SLA_HIP(hipMemcpyAsync(x_user, h.q, bytes, hipMemcpyDeviceToDevice, s));
+            }
+            SLA_HIP(hipMemcpyAsync(h.h_state, h.st, sizeof(SysState) * h.B, hipMemcpyDeviceToHost,
+                                   s));
+            SLA_HIP(hipStreamSynchronize(s));
+            if (h.profile) flush_profile(h);
+            for (int b = 0; b < h.B; ++b) {
+                const int32_t stb = h.h_state[b].status;
+                if (stb != kRunning && (stb < 0 || stb > SLA_BREAKDOWN)) {
+                    // a grid-wide wait gave up (workgroups not all running)
+                    h.last_fallback |= kFallbackWaitTimedOut;
+                    return false;
+                }
+            }
+            for (int b = 0; b < h.B; ++b) {
+                const SysState &st = h.h_state[b];
+                info[b].iterations = st.iter;
+                info[b].status = st.status == kRunning ? SLA_MAXIT : st.status;
+                info[b].rel_residual = st.bb == 0.0 ? 0.0 : sqrt(st.rr / st.bb);
+            }
+            h.last_path = kPathSingleKernel;
+            return true;
         }
-        SLA_HIP(hipMemcpyAsync(h.h_state, h.st, sizeof(SysState) * h.B, hipMemcpyDeviceToHost, s));
-        SLA_HIP(hipStreamSynchronize(s));
-        if (h.profile) flush_profile(h);
-        for (int b = 0; b < h.B; ++b) {
-            const SysState &st = h.h_state[b];
-            if (st.status != kRunning && (st.status < 0 || st.status > SLA_BREAKDOWN))
-                fail(SLA_ERR_HIP, "single-kernel solve: a grid-wide wait timed out");
-            info[b].iterations = st.iter;
-            info[b].status = st.status == kRunning ? SLA_MAXIT : st.status;
-            info[b].rel_residual = st.bb == 0.0 ? 0.0 : sqrt(st.rr / st.bb);
-        }
-        return;
+        h.last_fallback |= kFallbackCoopRefused;
     }
     const void *b_int = b_user;
     if (h.B > 1) {
@@ -1167,6 +1199,7 @@ void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit,
         }
     }
     if (!keep_internal_solution) {
+        // (if a wait gave up, the re-run overwrites what is copied here)
         if (h.B == 1)
             SLA_HIP(hipMemcpyAsync(x_user, h.x, (size_t)h.n * h.vbytes, hipMemcpyDeviceToDevice, s));
         else
@@ -1177,14 +1210,47 @@ void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit,
     SLA_HIP(hipMemcpyAsync(h.h_ctl, h.ctl, sizeof(Ctl), hipMemcpyDeviceToHost, s));
     SLA_HIP(hipStreamSynchronize(s));
     if (h.profile) flush_profile(h);
-    if (h.h_ctl->error)
-        fail(SLA_ERR_HIP, "fused update: a grid-wide wait timed out (workgroups not co-resident)");
+    if (h.h_ctl->error) {
+        // the fused update's broadcast wait gave up: its workgroups are not
+        // all running at once on this GPU now. The handle keeps to the two
+        // kernels without grid-wide waits from here on (SLA_OPT_FUSED_UPDATE
+        // turns the fused form back on).
+        h.last_fallback |= kFallbackWaitTimedOut;
+        h.fuse_update = false;
+        if (h.graph) (void)hipGraphExecDestroy(h.graph);
+        h.graph = nullptr;
+        h.graph_k = 0;
+        return false;
+    }
     for (int b = 0; b < nsys; ++b) {
         const SysState &st = h.h_state[b];
         info[b].iterations = st.iter;
         info[b].status = st.status == kRunning ? SLA_MAXIT : st.status;
         info[b].rel_residual = st.bb == 0.0 ? 0.0 : sqrt(st.rr / st.bb);
     }
+    h.last_path = kPathPerStep;
+    return true;
+}
+
+}  // namespace
+
+// Solve A x = b for every system. b_user / x_user are [B][n]. With
+// keep_internal_solution the iterate stays in h.x (internal layout) and
+// x_user may be null. The single-kernel solve and the fused update wait for
+// other workgroups, with bounded waits; if a wait gives up (the GPU shared
+// with other work, so that not all workgroups run at once), the solve is
+// run again from the start without that kernel: first the per-step kernels,
+// then, if the fused update's wait gives up too, the unfused ones, which
+// never wait on other workgroups. h.last_path and h.last_fallback record
+// what ran.
+void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit, sla_info *info,
+         hipStream_t s, bool keep_internal_solution) {
+    h.last_path = kPathNone;
+    h.last_fallback = 0;
+    if (pcg_attempt(h, b_user, x_user, tol, maxit, info, s, keep_internal_solution, true)) return;
+    if (pcg_attempt(h, b_user, x_user, tol, maxit, info, s, keep_internal_solution, false)) return;
+    if (pcg_attempt(h, b_user, x_user, tol, maxit, info, s, keep_internal_solution, false)) return;
+    fail(SLA_ERR_HIP, "a grid-wide wait gave up on a path that has none");
 }
 
 // grad [B][nnz] (CSR order) from lambda (internal layout, h.x) and the

@@ -31,8 +31,9 @@
 // number, with device-coherent stores; one wavefront of every workgroup polls
 // all stamped partials and sums them itself in one fixed order, so every
 // workgroup holds the same bits and takes the same stopping decisions. Polls
-// are bounded: a workgroup that waits longer than kSpinLimit polls reports a
-// failure instead of hanging.
+// are bounded: a workgroup that waits longer than a set number of polls
+// reports a failure instead of hanging (the host then re-runs the solve on
+// the per-step kernels).
 #include "common.h"
 
 #include <algorithm>
@@ -52,7 +53,6 @@ static_assert(kRUnits < 256, "a tile's row offsets are bytes, at most 4 per lane
 constexpr int kSumBatch = 4;          // LDS reads issued together per row sum (2: 42.9, 6: 43.2, 8: 44.4 us per iteration at 2.1M rows against 42.0)
 constexpr double kFastShare = 1.0625;   // tile share of a SIMD's first wavefront (vs 0.9375)
 constexpr int kRD = 4;                // tiles in flight per wavefront (even)
-constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kResFailed = 100;       // status written when a wait timed out
 
 // sum over the workgroup with a fixed tree (identical in every workgroup)
@@ -104,6 +104,7 @@ struct GridSync {
                          // workgroup's rows read, for each one in row order
     int G;               // workgroups of one system
     int lb;              // this workgroup's index among them
+    uint32_t spin_limit; // polls of a wait before it gives up
 };
 constexpr int kMaxC = 2;
 // workgroups one polling lane covers: a system has at most 64 * kPollSlots
@@ -173,7 +174,7 @@ __device__ __forceinline__ bool grid_allreduce(const GridSync &gs, uint32_t seq,
                 done = true;
                 break;
             }
-            if (++spins > kSpinLimit) break;
+            if (++spins > gs.spin_limit) break;
             __builtin_amdgcn_s_sleep(1);
         }
 #pragma unroll
@@ -225,7 +226,7 @@ __device__ __forceinline__ bool grid_wait_deps(const GridSync &gs, uint32_t bseq
                 done = true;
                 break;
             }
-            if (++spins > kSpinLimit) break;
+            if (++spins > gs.spin_limit) break;
             __builtin_amdgcn_s_sleep(1);
         }
         if (t == 0) lds[kMaxC] = done ? 1.0 : 0.0;
@@ -747,7 +748,7 @@ bool launch(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStr
     T *xo = (T *)x;
     T *pg = (T *)h.p;
     GridSync gs{h.res_slot, h.res_slot + (size_t)(2 * h.res_grid * 2 * kMaxC) * h.B,
-                h.res_wave + 2 * (waves + 1), (int)h.res_grid, 0};
+                h.res_wave + 2 * (waves + 1), (int)h.res_grid, 0, h.spin_limit};
     const int B = h.B;
     const int64_t n = h.n;
     SysState *st = h.st;

@@ -205,6 +205,16 @@ class SparseCSR:
     def profile_reset(self) -> None:
         check(_lib.load().sla_profile_reset(self._h))
 
+    def last_path(self) -> dict:
+        """How the last solve ran: path ("none", "single_kernel", "per_step")
+        and the fallback bits (cooperative launch refused; a grid-wide wait
+        gave up and the solve ran again without it)."""
+        p, f = ctypes.c_int32(), ctypes.c_uint32()
+        check(_lib.load().sla_csr_get_last_path(self._h, ctypes.byref(p), ctypes.byref(f)))
+        return {"path": {0: "none", 1: "single_kernel", 2: "per_step"}[p.value],
+                "cooperative_refused": bool(f.value & _lib.SLA_FALLBACK_COOPERATIVE_REFUSED),
+                "wait_timed_out": bool(f.value & _lib.SLA_FALLBACK_WAIT_TIMED_OUT)}
+
     # ------------------------------------------------------------------ operations
     def matvec(self, x: torch.Tensor) -> torch.Tensor:
         """y = A x (no autograd)."""

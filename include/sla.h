@@ -98,20 +98,49 @@ enum {
                                    available. A cooperative launch refused at solve time
                                    (not all workgroups can run at once, or another process
                                    holds the device's cooperative-launch resource) falls
-                                   back to the per-step kernels. */
+                                   back to the per-step kernels; so does a solve whose
+                                   bounded grid-wide wait gave up (see SLA_OPT_SPIN_LIMIT).
+                                   sla_csr_get_last_path tells which path ran. */
     SLA_OPT_FUSED_UPDATE = 5,   /* 1 (default): a single system, or a batch, whose update
                                    fits one pass of the resident workgroups runs the update
                                    and the direction as one kernel (r, p, dinv stay in
                                    registers while beta is formed and broadcast); 0: two
-                                   kernels. Same arithmetic either way. */
-    SLA_OPT_COOPERATIVE = 6     /* 1 (default): the single-kernel solve is started with
+                                   kernels. Same arithmetic either way. If the broadcast
+                                   wait of the fused kernel gives up (its workgroups do not
+                                   all run at once: the GPU is shared), the solve is run
+                                   again with two kernels and the handle keeps to them
+                                   (this option set to 0) until it is set to 1 again. */
+    SLA_OPT_COOPERATIVE = 6,    /* 1 (default): the single-kernel solve is started with
                                    hipLaunchCooperativeKernel, which guarantees that all its
                                    workgroups (one per CU at most) run at once; 0: an
                                    ordinary launch of the same grid, for tools that cannot
                                    follow cooperative launches. Without the guarantee a
                                    workgroup that does not start (the GPU shared with other
                                    work) makes the others' bounded waits expire: the solve
-                                   then fails with SLA_ERR_HIP instead of hanging. */
+                                   then runs again on the per-step kernels (same result;
+                                   reported by sla_csr_get_last_path), never hangs. */
+    SLA_OPT_SPIN_LIMIT = 7      /* polls a bounded grid-wide wait (single-kernel solve,
+                                   fused update) makes before it gives up; default 2^22
+                                   (about a second), 0 .. 2^32 - 1. A wait that gives up
+                                   never changes a result: the solve is run again from the
+                                   start on kernels without such waits. 0 makes every wait
+                                   that is not already satisfied give up at once, which
+                                   exercises that path. */
+};
+
+/* How the last sla_pcg_solve / sla_adjoint_backward / BiCGStab call on a
+ * handle ran (sla_csr_get_last_path). */
+enum {
+    SLA_PATH_NONE = 0,          /* no solve yet */
+    SLA_PATH_SINGLE_KERNEL = 1, /* the whole solve in one cooperative kernel */
+    SLA_PATH_PER_STEP = 2       /* kernels per step, k steps per polled hipGraph */
+};
+/* why the preferred path was not the one that produced the result (bits) */
+enum {
+    SLA_FALLBACK_COOPERATIVE_REFUSED = 1u, /* the single-kernel solve applied, but its
+                                              cooperative launch was refused */
+    SLA_FALLBACK_WAIT_TIMED_OUT = 2u       /* a bounded grid-wide wait gave up and the solve
+                                              was run again without that kernel */
 };
 
 /* kernel kinds reported by sla_profile_get */
@@ -312,6 +341,11 @@ sla_status sla_bicgstab_adjoint(sla_csr h, const void *x, const void *grad_x, vo
  * and its rows longer than 128 entries. */
 sla_status sla_csr_get_layout(sla_csr h, int32_t *reordered, int32_t *narrow_columns,
                               int64_t *tiles, int64_t *long_rows);
+
+/* How the last solve on the handle ran (host outputs; either may be NULL):
+ * *path an SLA_PATH_* value, *fallbacks a mask of SLA_FALLBACK_* bits (0
+ * when the preferred path ran). Results do not depend on the path. */
+sla_status sla_csr_get_last_path(sla_csr h, int32_t *path, uint32_t *fallbacks);
 
 /* Accumulated kernel timings of calls made while SLA_OPT_PROFILE was on
  * (host outputs): number of launches and total milliseconds per kind. */

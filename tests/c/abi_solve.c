@@ -92,6 +92,9 @@ int main(int argc, char **argv) {
                              d_val, SLA_FLAG_CHECK_SYMMETRIC, NULL));
     sla_info info, ainfo, binfo;
     CHECK_SLA(sla_pcg_solve(A, d_b, d_x, 1e-10, 5000, &info, NULL));
+    int32_t path = 0;
+    uint32_t fallbacks = 0;
+    CHECK_SLA(sla_csr_get_last_path(A, &path, &fallbacks));
     CHECK_SLA(sla_spmv(A, d_x, d_y, NULL));
     CHECK_HIP(hipMemcpy(x, d_x, sizeof(double) * n, hipMemcpyDeviceToHost));
     CHECK_HIP(hipMemcpy(y, d_y, sizeof(double) * n, hipMemcpyDeviceToHost));
@@ -113,9 +116,11 @@ int main(int argc, char **argv) {
     if (!f || fwrite(x, sizeof(double), (size_t)n, f) != (size_t)n) return 4;
     fclose(f);
     printf("iterations=%d status=%d rel_residual=%.3e true_residual=%.3e adjoint_iterations=%d "
-           "adjoint_status=%d bicgstab_iterations=%d bicgstab_status=%d refused=%d version=%s\n",
+           "adjoint_status=%d bicgstab_iterations=%d bicgstab_status=%d refused=%d path=%d "
+           "fallbacks=%u version=%s\n",
            info.iterations, info.status, info.rel_residual, true_res, ainfo.iterations,
-           ainfo.status, binfo.iterations, binfo.status, bad_ok, sla_version());
+           ainfo.status, binfo.iterations, binfo.status, bad_ok, (int)path, (unsigned)fallbacks,
+           sla_version());
     sla_csr_destroy(A);
     sla_csr_destroy(C);
     hipFree(d_rp); hipFree(d_col); hipFree(d_val); hipFree(d_conv); hipFree(d_b);

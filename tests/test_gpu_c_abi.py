@@ -1,7 +1,8 @@
 """The C ABI from plain C (tests/c/abi_solve.c, built with the library): a
 2D Poisson CSR in caller-owned device memory through create, PCG, matvec,
 adjoint, BiCGStab on a non-symmetric variant and a refused call; the PCG
-solution it writes is compared with the oracle's on the same matrix."""
+solution it writes is compared with the oracle's on the same matrix, and the
+path the solve took (sla_csr_get_last_path) is checked for consistency."""
 import os
 import subprocess
 
@@ -23,6 +24,16 @@ def test_plain_c_program(tmp_path):
     assert res.returncode == 0, (res.returncode, res.stdout, res.stderr)
     fields = dict(kv.split("=", 1) for kv in res.stdout.split() if "=" in kv)
     assert fields["status"] == "0" and fields["refused"] == "1"
+    # the 48^2 Poisson system fits the single-kernel solve; if the per-step
+    # kernels ran instead, it must be because the cooperative launch was
+    # refused (a process started by one that made cooperative launches can
+    # be refused on this GPU), and the library must say so
+    path, fallbacks = int(fields["path"]), int(fields["fallbacks"])
+    assert path in (1, 2)
+    if path == 1:
+        assert fallbacks == 0
+    else:
+        assert fallbacks == 1
     x = np.fromfile(out, dtype=np.float64)
     r, c, v = poisson2d_coo(N)
     ref = oracle.coo_to_csr(N * N, r, c, v)
