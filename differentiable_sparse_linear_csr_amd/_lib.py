@@ -45,7 +45,8 @@ EXPORTS = ["sla_csr_create", "sla_csr_create_segmented", "sla_csr_get_segments",
            "sla_csr_gather_to_input", "sla_csr_set_option", "sla_spmv", "sla_spmv_backward",
            "sla_pcg_solve", "sla_adjoint_backward", "sla_bicgstab_solve", "sla_bicgstab_adjoint",
            "sla_profile_get", "sla_profile_reset", "sla_csr_memory", "sla_csr_get_layout",
-           "sla_csr_get_last_path", "sla_csr_destroy", "sla_last_error", "sla_version"]
+           "sla_csr_get_last_path", "sla_csr_destroy", "sla_last_error", "sla_version",
+           "sla_pcg_solve_noalloc"]
 
 
 class SlaError(RuntimeError):
@@ -96,6 +97,7 @@ def load() -> ctypes.CDLL:
     L.sla_csr_memory.argtypes = [P, pi64]
     L.sla_csr_get_layout.argtypes = [P, pi32, pi32, pi64, pi64]
     L.sla_csr_get_last_path.argtypes = [P, pi32, ctypes.POINTER(ctypes.c_uint32)]
+    L.sla_pcg_solve_noalloc.argtypes = [i64, i64, P, P, P, P, P, f64, i32, ctypes.POINTER(Info), P]
     L.sla_csr_destroy.argtypes = [P]
     L.sla_csr_destroy.restype = None
     L.sla_last_error.argtypes = []

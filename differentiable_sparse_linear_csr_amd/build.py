@@ -22,7 +22,7 @@ ARCH = "gfx950"
 
 SOURCES = ["util.hip", "assembly.hip", "spmv.hip", "pcg.hip", "bicgstab.hip", "resident.hip",
            "reorder.hip",
-           "seg.hip", "api.hip"]
+           "seg.hip", "noalloc.hip", "api.hip"]
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", f"-I{INCLUDE}"]
 

@@ -447,6 +447,20 @@ sla_status sla_adjoint_backward(sla_csr hd, const void *x, const void *grad_x, v
     });
 }
 
+sla_status sla_pcg_solve_noalloc(int64_t n, int64_t nnz, const int32_t *row_ptr,
+                                 const int32_t *col_idx, const double *values, const double *b,
+                                 double *x, double tol, int32_t maxit, sla_info *info,
+                                 void *stream) {
+    return guard([&] {
+        if (!row_ptr || !b || !x || !info || (nnz > 0 && (!col_idx || !values)))
+            fail(SLA_ERR_INVALID_ARG, "null pointer");
+        if (!(tol >= 0.0) || maxit < 0) fail(SLA_ERR_INVALID_ARG, "need tol >= 0 and maxit >= 0");
+        if ((const void *)x == (const void *)b) fail(SLA_ERR_INVALID_ARG, "x and b must not alias");
+        pcg_noalloc(n, nnz, row_ptr, col_idx, values, b, x, tol, maxit, kDefaultSpinLimit, info,
+                    (hipStream_t)stream);
+    });
+}
+
 sla_status sla_bicgstab_solve(sla_csr hd, const void *b, void *x, double tol, int32_t maxit,
                               sla_info *info, void *stream) {
     return guard([&] {

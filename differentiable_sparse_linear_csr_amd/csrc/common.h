@@ -610,6 +610,23 @@ struct Red {
     double *gpart;
     uint32_t *sync;  // this kernel kind's kCountersPerKind counters
 };
+// the general per-step kernels on caller-given buffers (allocation-free solve)
+void launch_init_raw(int64_t n, const double *b, double *x, double *r, double *p,
+                     const double *dinv, Red red, Ctl *ctl, SysState *st, int32_t *running,
+                     hipStream_t s);
+void launch_update_raw(int64_t n, double *x, double *r, const double *p, const double *q,
+                       const double *dinv, Red red, Ctl *ctl, SysState *st, int32_t *running,
+                       hipStream_t s);
+void launch_direction_raw(int64_t n, const double *r, double *p, const double *dinv,
+                          const Ctl *ctl, const SysState *st, hipStream_t s);
+int64_t raw_vec_grid(int64_t n);
+void launch_spmv_csr_dot_raw(int64_t n, const int32_t *row_ptr, const int32_t *col,
+                             const double *val, const double *p, double *q, Red red, Ctl *ctl,
+                             SysState *st, int32_t *running, hipStream_t s);
+// the allocation-free solve (noalloc.hip)
+void pcg_noalloc(int64_t n, int64_t nnz, const int32_t *row_ptr, const int32_t *col,
+                 const double *val, const double *b, double *x, double tol, int32_t maxit,
+                 uint32_t spin_limit, sla_info *info, hipStream_t s);
 
 __device__ __forceinline__ void publish_running(Ctl *ctl, int32_t *h_running, int32_t v) {
     ctl->n_running = v;

@@ -1084,6 +1084,37 @@ void init_vector_limits(Handle &h) {
     }
 }
 
+// The general per-step kernels (fp64, one system) on caller-given buffers,
+// for the allocation-free solve: every pointer is device memory, the
+// reductions' partials, group sums and arrival counters come in `red` (the
+// counters zero), `running` is device memory that receives the number of
+// systems still running.
+void launch_init_raw(int64_t n, const double *b, double *x, double *r, double *p,
+                     const double *dinv, Red red, Ctl *ctl, SysState *st, int32_t *running,
+                     hipStream_t s) {
+    hipLaunchKernelGGL(k_init<double>, dim3((unsigned)vec_grid(n, 1)), dim3(kBlock), 0, s, n, 1, b,
+                       x, r, p, dinv, red, ctl, st, running);
+    SLA_HIP(hipGetLastError());
+}
+
+void launch_update_raw(int64_t n, double *x, double *r, const double *p, const double *q,
+                       const double *dinv, Red red, Ctl *ctl, SysState *st, int32_t *running,
+                       hipStream_t s) {
+    hipLaunchKernelGGL(k_update<double>, dim3((unsigned)vec_grid(n, 1)), dim3(kBlock), 0, s, n, 1,
+                       x, r, p, q, dinv, red, ctl, st, running);
+    SLA_HIP(hipGetLastError());
+}
+
+void launch_direction_raw(int64_t n, const double *r, double *p, const double *dinv,
+                          const Ctl *ctl, const SysState *st, hipStream_t s) {
+    hipLaunchKernelGGL(k_direction<double>, dim3((unsigned)vec_grid(n, 1)), dim3(kBlock), 0, s, n, 1,
+                       r, p, dinv, ctl, st);
+    SLA_HIP(hipGetLastError());
+}
+
+// workgroups of those kernels (the rows of their partial tables)
+int64_t raw_vec_grid(int64_t n) { return vec_grid(n, 1); }
+
 void flush_profile(Handle &h) {
     for (auto &rec : h.pending) {
         float ms = 0.f;

@@ -595,6 +595,21 @@ void init_launch_limits(Handle &h) {
     }
 }
 
+// q = A p fused with the p.q partials and alpha, for one fp64 system held
+// only as caller CSR arrays (int32 row_ptr and columns), on caller-given
+// buffers (the allocation-free solve): one lane per row, rows_per_lane rows
+// per lane so that the grid stays within kMaxGrid (the rows of red.part).
+void launch_spmv_csr_dot_raw(int64_t n, const int32_t *row_ptr, const int32_t *col,
+                             const double *val, const double *p, double *q, Red red, Ctl *ctl,
+                             SysState *st, int32_t *running, hipStream_t s) {
+    int rpl = 1;
+    while ((n + (int64_t)kBlock * rpl - 1) / ((int64_t)kBlock * rpl) > kMaxGrid) rpl *= 2;
+    const int64_t grid = (n + (int64_t)kBlock * rpl - 1) / ((int64_t)kBlock * rpl);
+    hipLaunchKernelGGL((k_spmv_batched<double, int32_t, true>), dim3((unsigned)grid), dim3(kBlock),
+                       0, s, n, 1, rpl, row_ptr, col, val, p, q, red, ctl, st, running);
+    SLA_HIP(hipGetLastError());
+}
+
 // q = A p on the solve workspace, fused with the p.q partials and alpha.
 void launch_spmv_dot(Handle &h, hipStream_t s) {
     if (h.vt == SLA_F64) {

@@ -293,6 +293,35 @@ sla_status sla_adjoint_backward(sla_csr h, const void *x, const void *grad_x, vo
                                 void *stream);
 
 /*
+ * Jacobi-PCG for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): one
+ * fp64 system given directly as CSR arrays, no handle, no allocation. The
+ * recurrence, stopping test and outcomes are those of sla_pcg_solve (the
+ * same results up to rounding order: iteration counts within 2).
+ *  n: 1 <= n <= SLA_NOALLOC_MAX_ROWS (2^21), else SLA_ERR_INVALID_ARG;
+ *  0 <= nnz < 2^31. row_ptr int32 [n+1] (0 .. nnz, non-decreasing), col_idx
+ *  int32 [nnz] (in [0, n), strictly increasing inside a row), values fp64
+ *  [nnz]: checked on the device first (SLA_ERR_INVALID_CSR,
+ *  SLA_ERR_INDEX_RANGE; SLA_ERR_BAD_DIAGONAL unless every diagonal entry is
+ *  present, positive and finite). b, x: fp64 [n]; x receives the solution
+ *  and must not alias b. info: host [1].
+ *  Workspace: a fixed array of this library in device memory, 64 MiB for
+ *  four vectors of 2^21 doubles plus 58 KiB for the reductions' partials and
+ *  counters and the solve's scalars, which every GPU the library runs on
+ *  holds until the process ends. Every call on one GPU uses that
+ *  GPU's array: calls that overlap on one GPU (other host threads, other
+ *  streams) race and give wrong results. Work is ordered on `stream`; the
+ *  call blocks the host until the solve has finished (it reads the running
+ *  flag every 16 iterations). The product is the general one-lane-per-row
+ *  SpMV, slower than a handle's tiled one.
+ */
+#define SLA_NOALLOC_MAX_ROWS (1 << 21)
+sla_status sla_pcg_solve_noalloc(int64_t n, int64_t nnz, const int32_t *row_ptr,
+                                 const int32_t *col_idx, const double *values, const double *b,
+                                 double *x, double tol, int32_t maxit, sla_info *info,
+                                 void *stream);
+
+/*
  * Jacobi-preconditioned BiCGStab from x0 = 0 for a general (non-symmetric)
  * system. torch-sla lists BiCGStab beside CG in its pytorch-native backend
  * (backend list of the API section; the distributed section: the CG template
