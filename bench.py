@@ -371,19 +371,19 @@ def measure(args, name: str, steps: int, warmup: int, cpu_budget: float,
         batches.append(e0.elapsed_time(e1) / reps)
     b2b_ms = sorted(batches)[1]
     # the matvec backward (A^T g and the value gradient), timed the same way;
-    # the first call builds A^T's pattern (on the host), outside the timed
-    # region; skipped for very large matrices, where that build takes minutes
-    bwd_ms = None
-    if w.nnz < (1 << 28):
-        gy = torch.ones_like(b)
+    # the first call builds A^T's pattern (a device sort), outside the timed
+    # region
+    gy = torch.ones_like(b)
+    t_tr = time.perf_counter()
+    A.matvec_backward_raw(b, gy)
+    torch.cuda.synchronize()
+    transpose_build_ms = (time.perf_counter() - t_tr) * 1e3
+    e0.record(stream)
+    for _ in range(10):
         A.matvec_backward_raw(b, gy)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(10):
-            A.matvec_backward_raw(b, gy)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        bwd_ms = e0.elapsed_time(e1) / 10
+    e1.record(stream)
+    torch.cuda.synchronize()
+    bwd_ms = e0.elapsed_time(e1) / 10
 
     V = 8 if w.dtype == "f64" else 4
     R = 8 if A.row_index_dtype == torch.int64 else 4
@@ -503,6 +503,7 @@ def measure(args, name: str, steps: int, warmup: int, cpu_budget: float,
             "spmv_gflops": round(2 * w.nnz * w.batch / (b2b_ms * 1e-3) / 1e9, 1),
             "spmv_gbps": round(ab["spmv"] / (b2b_ms * 1e-3) / 1e9, 1),
             # matvec backward: A^T g (SpMV bytes) + grad_vals (gradient bytes)
+            "spmv_backward_first_call_ms": round(transpose_build_ms, 1),
             "spmv_backward_ms": round(bwd_ms, 5) if bwd_ms else None,
             "spmv_backward_gbps": (round((ab["spmv"] + ab["grad"]) / (bwd_ms * 1e-3) / 1e9, 1)
                                    if bwd_ms else None),

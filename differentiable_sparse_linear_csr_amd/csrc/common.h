@@ -633,24 +633,40 @@ __device__ __forceinline__ void publish_running(Ctl *ctl, int32_t *h_running, in
     __hip_atomic_store(h_running, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// Sum of one integer per thread over the block (integer LDS atomics: exact
+// in any order). Every thread of the block calls it; ends with a barrier.
+__device__ __forceinline__ int block_count(int v) {
+    __shared__ int s_cnt;
+    if (threadIdx.x == 0) s_cnt = 0;
+    __syncthreads();
+    if (v) atomicAdd(&s_cnt, v);
+    __syncthreads();
+    const int r = s_cnt;
+    __syncthreads();
+    return r;
+}
+
+// Last block of a fused SpMV (every thread of it calls this), one thread per
+// system: alpha = rho / sigma, or a breakdown; then the number still running.
+// (A loop over the systems in one thread makes a dependent round trip to
+// memory per system: 16 us for 32 systems.)
 __device__ __forceinline__ void finish_alpha(const double *tot, int B, Ctl *ctl, SysState *st,
                                              int32_t *h_running) {
-    if (threadIdx.x == 0) {
-        int running = 0;
-        for (int b = 0; b < B; ++b) {
-            SysState &s = st[b];
-            if (s.status != kRunning) continue;
-            const double sigma = tot[b];
-            if (!(sigma > 0.0) || !isfinite(sigma)) {
-                s.status = SLA_BREAKDOWN;
-                s.iter += 1;
-            } else {
-                s.alpha = s.rho / sigma;
-                ++running;
-            }
+    int running = 0;
+    for (int b = threadIdx.x; b < B; b += kBlock) {
+        SysState &s = st[b];
+        if (s.status != kRunning) continue;
+        const double sigma = tot[b];
+        if (!(sigma > 0.0) || !isfinite(sigma)) {
+            s.status = SLA_BREAKDOWN;
+            s.iter += 1;
+        } else {
+            s.alpha = s.rho / sigma;
+            ++running;
         }
-        publish_running(ctl, h_running, running);
     }
+    running = block_count(running);
+    if (threadIdx.x == 0) publish_running(ctl, h_running, running);
 }
 
 template <typename T>

@@ -84,52 +84,54 @@ __global__ __launch_bounds__(kBlock) void k_init(int64_t n, int B, const T *__re
     if (threadIdx.x < B)
         store_partial(red.part + (int64_t)blockIdx.x * 2 * B + B + threadIdx.x, blk[threadIdx.x]);
     if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, 2 * B, tmp, tot)) {
-        if (threadIdx.x == 0) {
-            int running = 0;
-            for (int b = 0; b < B; ++b) {
-                SysState s;
-                s.bb = tot[b];
-                s.rho = tot[B + b];
-                s.alpha = 0.0;
-                s.beta = 0.0;
-                s.rr = s.bb;
-                s.iter = 0;
-                if (s.bb == 0.0) s.status = SLA_CONVERGED;
-                else if (ctl->maxit <= 0) s.status = SLA_MAXIT;
-                else s.status = kRunning;
-                running += s.status == kRunning;
-                st[b] = s;
-            }
-            publish_running(ctl, h_running, running);
+        // one thread per system
+        const int32_t maxit = ctl->maxit;
+        int running = 0;
+        for (int b = threadIdx.x; b < B; b += kBlock) {
+            SysState s;
+            s.bb = tot[b];
+            s.rho = tot[B + b];
+            s.alpha = 0.0;
+            s.beta = 0.0;
+            s.rr = s.bb;
+            s.iter = 0;
+            if (s.bb == 0.0) s.status = SLA_CONVERGED;
+            else if (maxit <= 0) s.status = SLA_MAXIT;
+            else s.status = kRunning;
+            running += s.status == kRunning;
+            st[b] = s;
         }
+        running = block_count(running);
+        if (threadIdx.x == 0) publish_running(ctl, h_running, running);
     }
 }
 
-// Last block of an update: r.z and r.r per system in tot[0..2B); applies the
-// stopping test, the iteration budget and beta.
+// Last block of an update (every thread of it calls this, one thread per
+// system): r.z and r.r per system in tot[0..2B); applies the stopping test,
+// the iteration budget and beta, then publishes the number still running.
 __device__ __forceinline__ void finish_update(const double *tot, int B, Ctl *ctl, SysState *st,
                                               int32_t *h_running) {
-    if (threadIdx.x == 0) {
-        int running = 0;
-        const double tol = ctl->tol;
-        for (int b = 0; b < B; ++b) {
-            SysState &s = st[b];
-            if (s.status != kRunning) continue;
-            const double rz = tot[b], rr = tot[B + b];
-            s.rr = rr;
-            s.iter += 1;
-            if (sqrt(rr) <= tol * sqrt(s.bb)) {
-                s.status = SLA_CONVERGED;
-            } else if (s.iter >= ctl->maxit) {
-                s.status = SLA_MAXIT;
-            } else {
-                s.beta = rz / s.rho;
-                s.rho = rz;
-                ++running;
-            }
+    const double tol = ctl->tol;
+    const int32_t maxit = ctl->maxit;
+    int running = 0;
+    for (int b = threadIdx.x; b < B; b += kBlock) {
+        SysState &s = st[b];
+        if (s.status != kRunning) continue;
+        const double rz = tot[b], rr = tot[B + b];
+        s.rr = rr;
+        s.iter += 1;
+        if (sqrt(rr) <= tol * sqrt(s.bb)) {
+            s.status = SLA_CONVERGED;
+        } else if (s.iter >= maxit) {
+            s.status = SLA_MAXIT;
+        } else {
+            s.beta = rz / s.rho;
+            s.rho = rz;
+            ++running;
         }
-        publish_running(ctl, h_running, running);
     }
+    running = block_count(running);
+    if (threadIdx.x == 0) publish_running(ctl, h_running, running);
 }
 
 // x += alpha p, r -= alpha q; partials of r.z and r.r with z = dinv r; the

@@ -210,29 +210,76 @@ void to_outer(Handle &h, const void *in, void *out, hipStream_t s) {
 
 }  // namespace
 
-// A handle for a matrix with the same entries as h in another arrangement:
-// CSR (rp, col) on the host, and map[k] = position in h's CSR of entry k
-// (device array, kept by the caller). Values are gathered from h's.
-Handle *make_child(Handle &h, const std::vector<int64_t> &rp, const std::vector<int32_t> &col,
-                   const int64_t *map, uint32_t flags, hipStream_t s) {
-    const int64_t n = (int64_t)rp.size() - 1, nnz = (int64_t)col.size();
-    const bool rp64 = nnz >= ((int64_t)1 << 31);
-    void *d_rp = nullptr, *d_col = nullptr, *d_vals = nullptr;
-    SLA_HIP(hipMalloc(&d_rp, (size_t)(n + 1) * (rp64 ? 8 : 4)));
-    SLA_HIP(hipMalloc(&d_col, 4 * (size_t)(nnz + 1)));
+// Handles for a matrix with the same entries as h in another arrangement
+// (P A P^T, A^T): a CSR pattern and map[k] = position in h's CSR of entry k
+// (device array, kept by the caller); values are gathered from h's.
+namespace {
+
+// keys[k] = col[k] (the sort key), pos[k] = k (what the sort carries)
+__global__ __launch_bounds__(kBlock) void k_keys_by_column(const int32_t *__restrict__ col,
+                                                           int64_t nnz, uint64_t *__restrict__ keys,
+                                                           int64_t *__restrict__ pos) {
+    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < nnz;
+         k += (int64_t)gridDim.x * kBlock) {
+        keys[k] = (uint64_t)(uint32_t)col[k];
+        pos[k] = k;
+    }
+}
+
+// row of each stored entry: the last row whose first entry is at or before
+// it (binary search in row_ptr, so long rows cost nothing extra)
+template <typename RP>
+__global__ __launch_bounds__(kBlock) void k_row_of_entry(const RP *__restrict__ row_ptr, int64_t n,
+                                                         int64_t nnz, int32_t *__restrict__ rowof) {
+    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < nnz;
+         k += (int64_t)gridDim.x * kBlock) {
+        int64_t lo = 0, hi = n - 1;   // row_ptr[lo] <= k < row_ptr[hi + 1]
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) >> 1;
+            if ((int64_t)row_ptr[mid] <= k) lo = mid;
+            else hi = mid - 1;
+        }
+        rowof[k] = (int32_t)lo;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_gather_i32(const int32_t *__restrict__ src,
+                                                       const int64_t *__restrict__ idx, int64_t m,
+                                                       int32_t *__restrict__ out) {
+    for (int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x; j < m;
+         j += (int64_t)gridDim.x * kBlock)
+        out[j] = src[idx[j]];
+}
+
+// trp[c] = first position whose key is >= c, c = 0..n (keys sorted)
+template <typename RP>
+__global__ __launch_bounds__(kBlock) void k_column_starts(const uint64_t *__restrict__ keys,
+                                                          int64_t nnz, int64_t n,
+                                                          RP *__restrict__ trp) {
+    for (int64_t c = (int64_t)blockIdx.x * kBlock + threadIdx.x; c <= n;
+         c += (int64_t)gridDim.x * kBlock) {
+        int64_t lo = 0, hi = nnz;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (keys[mid] < (uint64_t)c) lo = mid + 1;
+            else hi = mid;
+        }
+        trp[c] = (RP)lo;
+    }
+}
+
+}  // namespace
+
+// A handle of the matrix whose CSR pattern is (d_rp, d_col) (device arrays,
+// d_rp int64 when rp64 else int32, [n+1]; d_col int32 [nnz]) and whose entry
+// j takes h's value at CSR position map[j] (device, kept by the caller).
+Handle *make_child_dev(Handle &h, int64_t n, int64_t nnz, const void *d_rp, bool rp64,
+                       const int32_t *d_col, const int64_t *map, uint32_t flags, hipStream_t s) {
+    void *d_vals = nullptr;
     SLA_HIP(hipMalloc(&d_vals, (size_t)(nnz + 1) * h.B * h.vbytes));
     Handle *in = nullptr;
     try {
-        if (rp64) {
-            SLA_HIP(hipMemcpyAsync(d_rp, rp.data(), 8 * (size_t)(n + 1), hipMemcpyHostToDevice, s));
-        } else {
-            std::vector<int32_t> r32((size_t)n + 1);
-            for (int64_t i = 0; i <= n; ++i) r32[(size_t)i] = (int32_t)rp[(size_t)i];
-            SLA_HIP(hipMemcpyAsync(d_rp, r32.data(), 4 * (size_t)(n + 1), hipMemcpyHostToDevice, s));
-            SLA_HIP(hipStreamSynchronize(s));
-        }
         if (nnz > 0) {
-            SLA_HIP(hipMemcpyAsync(d_col, col.data(), 4 * (size_t)nnz, hipMemcpyHostToDevice, s));
             if (h.vt == SLA_F64)
                 hipLaunchKernelGGL(k_vals_to_inner_bm<double>, dim3(grid_of(nnz * h.B)), dim3(kBlock),
                                    0, s, (const double *)h.vals, (double *)d_vals, map, nnz, h.B);
@@ -258,15 +305,42 @@ Handle *make_child(Handle &h, const std::vector<int64_t> &rp, const std::vector<
         if (want_reorder(*in)) build_reordered(*in, s);
         SLA_HIP(hipStreamSynchronize(s));
     } catch (...) {
-        (void)hipFree(d_rp);
-        (void)hipFree(d_col);
         (void)hipFree(d_vals);
         if (in) destroy_handle(in);
         throw;
     }
+    SLA_HIP(hipFree(d_vals));
+    return in;
+}
+
+// the same from host pattern arrays
+Handle *make_child(Handle &h, const std::vector<int64_t> &rp, const std::vector<int32_t> &col,
+                   const int64_t *map, uint32_t flags, hipStream_t s) {
+    const int64_t n = (int64_t)rp.size() - 1, nnz = (int64_t)col.size();
+    const bool rp64 = nnz >= ((int64_t)1 << 31);
+    void *d_rp = nullptr, *d_col = nullptr;
+    SLA_HIP(hipMalloc(&d_rp, (size_t)(n + 1) * (rp64 ? 8 : 4)));
+    SLA_HIP(hipMalloc(&d_col, 4 * (size_t)(nnz + 1)));
+    Handle *in = nullptr;
+    try {
+        if (rp64) {
+            SLA_HIP(hipMemcpyAsync(d_rp, rp.data(), 8 * (size_t)(n + 1), hipMemcpyHostToDevice, s));
+        } else {
+            std::vector<int32_t> r32((size_t)n + 1);
+            for (int64_t i = 0; i <= n; ++i) r32[(size_t)i] = (int32_t)rp[(size_t)i];
+            SLA_HIP(hipMemcpyAsync(d_rp, r32.data(), 4 * (size_t)(n + 1), hipMemcpyHostToDevice, s));
+            SLA_HIP(hipStreamSynchronize(s));
+        }
+        if (nnz > 0)
+            SLA_HIP(hipMemcpyAsync(d_col, col.data(), 4 * (size_t)nnz, hipMemcpyHostToDevice, s));
+        in = make_child_dev(h, n, nnz, d_rp, rp64, (const int32_t *)d_col, map, flags, s);
+    } catch (...) {
+        (void)hipFree(d_rp);
+        (void)hipFree(d_col);
+        throw;
+    }
     SLA_HIP(hipFree(d_rp));
     SLA_HIP(hipFree(d_col));
-    SLA_HIP(hipFree(d_vals));
     return in;
 }
 
@@ -434,10 +508,9 @@ void reordered_adjoint(Handle &h, const void *x, const void *g, void *grad_b, vo
 // ------------------------------------------------------------------ A^T for the matvec backward
 // The backward of y = A x needs A^T g. A handle checked for bitwise symmetry
 // uses itself (row i of A^T holds the same values in the same column order as
-// row i of A). Otherwise the first backward builds a child handle of A^T:
-// the pattern by a counting sort of the columns on the host (rows of A^T list
-// their entries in increasing row of A), values gathered from A's through a
-// position map, refreshed after set_values.
+// row i of A). Otherwise the first backward builds a child handle of A^T on
+// the device (rows of A^T list their entries in increasing row of A), values
+// gathered from A's through a position map, refreshed after set_values.
 Handle *transpose_for_backward(Handle &h, hipStream_t s) {
     if (h.flags & SLA_FLAG_CHECK_SYMMETRIC) return &h;
     if (h.tr) {
@@ -447,36 +520,60 @@ Handle *transpose_for_backward(Handle &h, hipStream_t s) {
         }
         return h.tr;
     }
+    // A^T's pattern on the device: a stable sort of the CSR positions by
+    // column (rows stay ascending inside each column, since positions are in
+    // row order) gives A^T's entries in its CSR order; the sorted positions
+    // are the value map, the rows of those positions A^T's columns, and the
+    // first sorted position of each column A^T's row pointer.
     const int64_t n = h.n, nnz = h.nnz;
-    std::vector<int64_t> rp((size_t)n + 1);
-    std::vector<int32_t> col((size_t)nnz);
-    if (h.rp64) {
-        SLA_HIP(hipMemcpyAsync(rp.data(), h.row_ptr, 8 * (size_t)(n + 1), hipMemcpyDeviceToHost, s));
-    } else {
-        std::vector<int32_t> r32((size_t)n + 1);
-        SLA_HIP(hipMemcpyAsync(r32.data(), h.row_ptr, 4 * (size_t)(n + 1), hipMemcpyDeviceToHost, s));
-        SLA_HIP(hipStreamSynchronize(s));
-        for (int64_t i = 0; i <= n; ++i) rp[(size_t)i] = r32[(size_t)i];
-    }
-    if (nnz > 0)
-        SLA_HIP(hipMemcpyAsync(col.data(), h.col, 4 * (size_t)nnz, hipMemcpyDeviceToHost, s));
-    SLA_HIP(hipStreamSynchronize(s));
-    std::vector<int64_t> trp((size_t)n + 1, 0);
-    for (int64_t k = 0; k < nnz; ++k) ++trp[(size_t)col[(size_t)k] + 1];
-    for (int64_t j = 0; j < n; ++j) trp[(size_t)j + 1] += trp[(size_t)j];
-    std::vector<int64_t> fill(trp.begin(), trp.end() - 1);
-    std::vector<int32_t> tcol((size_t)nnz);
-    std::vector<int64_t> tmap((size_t)nnz);
-    for (int64_t i = 0; i < n; ++i)
-        for (int64_t k = rp[(size_t)i]; k < rp[(size_t)i + 1]; ++k) {
-            const int64_t pos = fill[(size_t)col[(size_t)k]]++;
-            tcol[(size_t)pos] = (int32_t)i;
-            tmap[(size_t)pos] = k;
-        }
+    const bool rp64 = nnz >= ((int64_t)1 << 31);
     h.tr_map = (int64_t *)dalloc(h, sizeof(int64_t) * (size_t)(nnz + 1));
-    if (nnz > 0)
-        SLA_HIP(hipMemcpyAsync(h.tr_map, tmap.data(), 8 * (size_t)nnz, hipMemcpyHostToDevice, s));
-    h.tr = make_child(h, trp, tcol, h.tr_map, 0, s);
+    uint64_t *keys = nullptr;
+    int32_t *rowof = nullptr, *tcol = nullptr;
+    void *trp = nullptr;
+    SLA_HIP(hipMallocAsync((void **)&keys, sizeof(uint64_t) * (size_t)(nnz + 1), s));
+    SLA_HIP(hipMallocAsync((void **)&rowof, sizeof(int32_t) * (size_t)(nnz + 1), s));
+    SLA_HIP(hipMallocAsync((void **)&tcol, sizeof(int32_t) * (size_t)(nnz + 1), s));
+    SLA_HIP(hipMallocAsync(&trp, (size_t)(n + 1) * (rp64 ? 8 : 4), s));
+    Handle *tr = nullptr;
+    try {
+        int bits = 0;
+        while (bits < 63 && ((int64_t)1 << bits) < n) ++bits;
+        if (nnz > 0) {
+            hipLaunchKernelGGL(k_keys_by_column, dim3(grid_of(nnz)), dim3(kBlock), 0, s,
+                               (const int32_t *)h.col, nnz, keys, h.tr_map);
+            if (h.rp64)
+                hipLaunchKernelGGL(k_row_of_entry<int64_t>, dim3(grid_of(nnz)), dim3(kBlock), 0, s,
+                                   (const int64_t *)h.row_ptr, n, nnz, rowof);
+            else
+                hipLaunchKernelGGL(k_row_of_entry<int32_t>, dim3(grid_of(nnz)), dim3(kBlock), 0, s,
+                                   (const int32_t *)h.row_ptr, n, nnz, rowof);
+            SLA_HIP(hipGetLastError());
+            radix_sort_pairs(keys, h.tr_map, nnz, bits, s);
+            hipLaunchKernelGGL(k_gather_i32, dim3(grid_of(nnz)), dim3(kBlock), 0, s,
+                               (const int32_t *)rowof, (const int64_t *)h.tr_map, nnz, tcol);
+            SLA_HIP(hipGetLastError());
+        }
+        if (rp64)
+            hipLaunchKernelGGL(k_column_starts<int64_t>, dim3(grid_of(n + 1)), dim3(kBlock), 0, s,
+                               (const uint64_t *)keys, nnz, n, (int64_t *)trp);
+        else
+            hipLaunchKernelGGL(k_column_starts<int32_t>, dim3(grid_of(n + 1)), dim3(kBlock), 0, s,
+                               (const uint64_t *)keys, nnz, n, (int32_t *)trp);
+        SLA_HIP(hipGetLastError());
+        tr = make_child_dev(h, n, nnz, trp, rp64, tcol, h.tr_map, 0, s);
+    } catch (...) {
+        (void)hipFreeAsync(keys, s);
+        (void)hipFreeAsync(rowof, s);
+        (void)hipFreeAsync(tcol, s);
+        (void)hipFreeAsync(trp, s);
+        throw;
+    }
+    SLA_HIP(hipFreeAsync(keys, s));
+    SLA_HIP(hipFreeAsync(rowof, s));
+    SLA_HIP(hipFreeAsync(tcol, s));
+    SLA_HIP(hipFreeAsync(trp, s));
+    h.tr = tr;
     h.tr_stale = false;
     return h.tr;
 }

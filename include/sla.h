@@ -257,8 +257,9 @@ sla_status sla_spmv(sla_csr h, const void *x, void *y, void *stream);
  * x, grad_y: [batch][n]. grad_x must not alias x or grad_y. fp32 handles form
  * products and sums in fp64. Asynchronous. A handle created with
  * SLA_FLAG_CHECK_SYMMETRIC uses A itself for A^T; otherwise the first call
- * builds A^T's pattern (host counting sort of the columns; allocates, once per
- * handle) and later calls only refresh its values after sla_csr_set_values.
+ * builds a handle of A^T on the device (a stable radix sort of the entries by
+ * column; allocates, once per handle) and later calls only refresh its values
+ * after sla_csr_set_values.
  * grad_vals reaches input order through sla_csr_gather_to_input. */
 sla_status sla_spmv_backward(sla_csr h, const void *x, const void *grad_y, void *grad_x,
                              void *grad_vals, void *stream);
@@ -354,9 +355,8 @@ sla_status sla_bicgstab_solve(sla_csr h, const void *b, void *x, double tol, int
  *   grad_b = lambda                              ([n], or NULL)
  *   grad_vals[k] = -lambda[row(k)] * x[col(k)]    ([nnz] in CSR order, or NULL)
  * A^T is the handle itself when it was created with SLA_FLAG_CHECK_SYMMETRIC;
- * otherwise the first call builds a handle of A^T (pattern sorted on the
- * host, values gathered on the device and refreshed after set_values), as
- * sla_spmv_backward does. x is the forward solution [n]; grad_b must not
+ * otherwise the first call builds a handle of A^T on the device (values
+ * gathered, and refreshed after set_values), as sla_spmv_backward does. x is the forward solution [n]; grad_b must not
  * alias x or grad_x. info (host [1]) reports the adjoint solve. Same
  * restrictions and errors as sla_bicgstab_solve. Blocks the host until done.
  */
