@@ -426,7 +426,8 @@ def measure(args, name: str, steps: int, warmup: int, cpu_budget: float,
         # iterations: one direction-kernel launch each (two SpMVs in BiCGStab)
         n_it = max(prof["direction"][0] if method == "bicgstab" else prof["spmv_dot"][0], 1)
         per_iter_ms = sum(prof[k][1] for k in ("spmv_dot", "update", "direction")) / n_it
-        kernel = "k_spmv_tile (q = A p; 50 back-to-back sla_spmv launches, median of 3 batches)"
+        kernel = (("k_spmv_tile_ring" if layout.get("ring_tiles") else "k_spmv_tile")
+                  + " (q = A p; 50 back-to-back sla_spmv launches, median of 3 batches)")
     else:
         # batched, or reordered: sla_spmv also transposes or permutes x and y,
         # so the fused SpMV of the solve is timed per launch (events around

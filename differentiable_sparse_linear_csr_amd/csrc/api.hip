@@ -320,6 +320,16 @@ void record_path(Handle &caller, const Handle &ran) {
     caller.last_fallback = r.last_fallback;
 }
 
+// the captured iteration graphs hold the kernels of the options they were
+// captured under
+void drop_graphs(Handle &h) {
+    if (h.graph) (void)hipGraphExecDestroy(h.graph);
+    if (h.bi_graph) (void)hipGraphExecDestroy(h.bi_graph);
+    h.graph = nullptr;
+    h.bi_graph = nullptr;
+    h.graph_k = h.bi_graph_k = 0;
+}
+
 void set_option(Handle *h, int32_t key, int64_t value) {
     switch (key) {
         case SLA_OPT_CHECK_INTERVAL:
@@ -344,15 +354,12 @@ void set_option(Handle *h, int32_t key, int64_t value) {
                 fail(SLA_ERR_INVALID_ARG, "spin limit in [0, 2^32)");
             h->spin_limit = (uint32_t)value;
             break;
+        case SLA_OPT_SPMV_RING:
+            if (h->spmv_ring != (value != 0)) drop_graphs(*h);
+            h->spmv_ring = value != 0;
+            break;
         case SLA_OPT_FUSED_UPDATE:
-            if (h->fuse_update != (value != 0)) {
-                // the captured iteration graphs hold the other kernel sequence
-                if (h->graph) (void)hipGraphExecDestroy(h->graph);
-                if (h->bi_graph) (void)hipGraphExecDestroy(h->bi_graph);
-                h->graph = nullptr;
-                h->bi_graph = nullptr;
-                h->graph_k = h->bi_graph_k = 0;
-            }
+            if (h->fuse_update != (value != 0)) drop_graphs(*h);
             h->fuse_update = value != 0;
             break;
         default:
@@ -549,7 +556,7 @@ sla_status sla_csr_get_layout(sla_csr hd, int32_t *reordered, int32_t *narrow_co
         const Handle *h = reinterpret_cast<const Handle *>(hd);
         if (reordered) *reordered = h->inner ? 1 : 0;
         const Handle *sv = h->inner ? h->inner : h;
-        if (narrow_columns) *narrow_columns = sv->all_narrow ? 1 : 0;
+        if (narrow_columns) *narrow_columns = sv->all_narrow ? (sv->ring_tiles ? 2 : 1) : 0;
         if (tiles) *tiles = sv->ntiles;
         if (long_rows) *long_rows = sv->nlong;
     });

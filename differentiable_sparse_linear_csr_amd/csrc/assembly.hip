@@ -8,6 +8,9 @@
 // value type, so the result is bit-identical for any launch configuration.
 #include <type_traits>
 
+#include <algorithm>
+#include <cmath>
+
 #include "common.h"
 
 namespace sla {
@@ -145,6 +148,7 @@ __global__ __launch_bounds__(kBlock) void k_csr_check(const RI *__restrict__ row
 
 template <typename RP>
 __global__ __launch_bounds__(kBlock) void k_tile_flags(const RP *__restrict__ row_ptr, int64_t n,
+                                                       int64_t band_n, int64_t band_l,
                                                        int64_t *__restrict__ flag) {
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * kBlock) {
@@ -154,11 +158,36 @@ __global__ __launch_bounds__(kBlock) void k_tile_flags(const RP *__restrict__ ro
         if (i > 0) {
             const int64_t pa = row_ptr[i - 1];
             const bool long_prev = (a - pa) > kLongRow;
-            const int64_t u_prev = pa + (i - 1), u_cur = a + i;
-            f = (long_i || long_prev || (u_prev / kTileUnits) != (u_cur / kTileUnits)) ? 1 : 0;
+            // banded: tile j holds the rows i with floor(i L / N) = j, so tile
+            // j + L is tile j moved down by N rows; else runs of kTileUnits
+            // rows + entries
+            const bool cut = band_l > 0 ? (i * band_l) / band_n != ((i - 1) * band_l) / band_n
+                                        : (pa + (i - 1)) / kTileUnits != (a + i) / kTileUnits;
+            f = (long_i || long_prev || cut) ? 1 : 0;
         }
         flag[i] = f;
     }
+}
+
+// Band test of a pattern: the farthest column to the right of row i is
+// i + band for at least 9 rows in 10 (a stencil on a grid: band = the grid's
+// largest stride). Counts the rows that match `band` and the longest row.
+template <typename RP>
+__global__ __launch_bounds__(kBlock) void k_band_count(const RP *__restrict__ row_ptr,
+                                                       const int32_t *__restrict__ col, int64_t n,
+                                                       int64_t band,
+                                                       unsigned long long *__restrict__ match,
+                                                       int *__restrict__ maxlen) {
+    unsigned long long m = 0;
+    int ml = 0;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * kBlock) {
+        const int64_t a = row_ptr[i], b = row_ptr[i + 1];
+        if (b > a && (int64_t)col[b - 1] - i == band) ++m;
+        ml = max(ml, (int)min(b - a, (int64_t)1 << 30));
+    }
+    if (m) atomicAdd(match, m);
+    if (ml) atomicMax(maxlen, ml);
 }
 
 __global__ __launch_bounds__(kBlock) void k_tile_fill(const int64_t *__restrict__ flag,
@@ -533,17 +562,104 @@ __global__ __launch_bounds__(kBlock) void k_gather_rp(const RP *__restrict__ row
     if (j < m) out[j] = (int64_t)row_ptr[rows[j]];
 }
 
+// Band-aligned tiles for a large single stencil-like matrix: with band N
+// (the farthest column right of most rows is row + N) and L tiles per N rows,
+// tile j + L holds the rows of tile j moved by N, so the p values tile j
+// gathers from rows near +N are the ones tile j + L owns and tile j + 2L
+// gathers near -N. The SpMV walks tiles j, j + L, j + 2L, ... in one
+// wavefront, one step apart, so those p lines are reused from the L2 whatever
+// the pace of the other wavefronts (with the usual tiles the three uses fall
+// to different wavefronts, which drift apart: at 133M rows each p line was
+// fetched about three times). L = the SpMV's wavefronts per XCD divided by a
+// panel count P, picked so that a tile has 36 to 64 rows (at most 63 rows and
+// 253 entries for the ring form of the SpMV), nearest 45. On the 133M-row
+// Poisson matrix: one-tile-ahead SpMV (768 wavefronts per XCD), 3 panels of
+// 256 columns and 45-row tiles took it from 2.28 to 2.14 ms (HBM fetches
+// 10.2 -> 8.4 GB), 30-row tiles were slower than the usual ones (2.69 ms),
+// 60-row ones 2.22 ms; ring SpMV (512 wavefronts), 2 panels of 256 columns
+// and 45-row tiles 2.05 ms against 2.40 with the usual tiles. Bands under
+// 4096 rows keep the usual tiles: their p lines are reused by neighbouring
+// wavefronts anyway.
+void choose_band(Handle &h, hipStream_t s) {
+    h.band_n = h.band_l = 0;
+    h.band_p = 0;
+    const int64_t n = h.n;
+    if (h.B != 1 || n < ((int64_t)1 << 20) || h.nnz == 0) return;
+    Scratch sc(s);
+    unsigned long long *match = sc.get<unsigned long long>(1);
+    int *maxlen = sc.get<int>(1);
+    SLA_HIP(hipMemsetAsync(match, 0, sizeof(unsigned long long), s));
+    SLA_HIP(hipMemsetAsync(maxlen, 0, sizeof(int), s));
+    // the candidate: the middle row's farthest offset
+    int64_t mid[2] = {0, 0};
+    int32_t last = 0;
+    if (h.rp64) {
+        SLA_HIP(hipMemcpyAsync(mid, (const int64_t *)h.row_ptr + n / 2, 16, hipMemcpyDeviceToHost, s));
+    } else {
+        int32_t m32[2];
+        SLA_HIP(hipMemcpyAsync(m32, (const int32_t *)h.row_ptr + n / 2, 8, hipMemcpyDeviceToHost, s));
+        SLA_HIP(hipStreamSynchronize(s));
+        mid[0] = m32[0];
+        mid[1] = m32[1];
+    }
+    SLA_HIP(hipStreamSynchronize(s));
+    if (mid[1] <= mid[0]) return;
+    SLA_HIP(hipMemcpyAsync(&last, h.col + mid[1] - 1, 4, hipMemcpyDeviceToHost, s));
+    SLA_HIP(hipStreamSynchronize(s));
+    const int64_t band = (int64_t)last - n / 2;
+    if (band < 2) return;
+    if (h.rp64)
+        hipLaunchKernelGGL(k_band_count<int64_t>, dim3(grid_for(n)), dim3(kBlock), 0, s,
+                           (const int64_t *)h.row_ptr, (const int32_t *)h.col, n, band, match, maxlen);
+    else
+        hipLaunchKernelGGL(k_band_count<int32_t>, dim3(grid_for(n)), dim3(kBlock), 0, s,
+                           (const int32_t *)h.row_ptr, (const int32_t *)h.col, n, band, match, maxlen);
+    SLA_HIP(hipGetLastError());
+    unsigned long long hm = 0;
+    int hl = 0;
+    SLA_HIP(hipMemcpyAsync(&hm, match, sizeof(hm), hipMemcpyDeviceToHost, s));
+    SLA_HIP(hipMemcpyAsync(&hl, maxlen, sizeof(hl), hipMemcpyDeviceToHost, s));
+    SLA_HIP(hipStreamSynchronize(s));
+    if ((double)hm < 0.9 * (double)n || hl < 1 || hl > kLongRow || band < 4096 || n < 8 * band)
+        return;
+    // wavefronts per XCD of the SpMV (its grid is the resident count when the
+    // tiles outnumber it, as they do here)
+    const int64_t W = tile_spmv_waves_per_xcd(h, h.spmv_ring);
+    // tiles the ring form of the SpMV takes: at most 63 rows and 253 entries
+    const int64_t max_rows = h.spmv_ring ? std::min<int64_t>(63, 253 / hl)
+                                         : std::min<int64_t>(64, kTileCap / hl);
+    int64_t best_p = 0;
+    double best_err = 1e300;
+    for (int64_t P = 1; P <= 16; ++P) {
+        if (W % P) continue;
+        const int64_t L = W / P;
+        const double rows = (double)band / (double)L;
+        if (rows < 36.0 || std::ceil(rows) > (double)max_rows) continue;
+        const double err = std::fabs(rows - 45.0);
+        if (err < best_err) {
+            best_err = err;
+            best_p = P;
+        }
+    }
+    if (best_p == 0) return;
+    h.band_n = band;
+    h.band_p = (int32_t)best_p;
+    h.band_l = W / best_p;
+}
+
 void build_tiles(Handle &h, hipStream_t s, const int64_t *seg_rows, int32_t nseg) {
     const int64_t n = h.n;
+    if (nseg == 0) choose_band(h, s);
+    else h.band_n = h.band_l = h.band_p = 0;
     Scratch sc(s);
     int64_t *flag = sc.get<int64_t>(n);
     int64_t *excl = sc.get<int64_t>(n);
     if (h.rp64)
         hipLaunchKernelGGL(k_tile_flags<int64_t>, dim3(grid_for(n)), dim3(kBlock), 0, s,
-                           (const int64_t *)h.row_ptr, n, flag);
+                           (const int64_t *)h.row_ptr, n, h.band_n, h.band_l, flag);
     else
         hipLaunchKernelGGL(k_tile_flags<int32_t>, dim3(grid_for(n)), dim3(kBlock), 0, s,
-                           (const int32_t *)h.row_ptr, n, flag);
+                           (const int32_t *)h.row_ptr, n, h.band_n, h.band_l, flag);
     SLA_HIP(hipGetLastError());
     exclusive_scan_i64(flag, excl, n, s);
     const int64_t nt = read_i64(excl + (n - 1), s) + read_i64(flag + (n - 1), s);
@@ -667,6 +783,14 @@ void build_tiles(Handle &h, hipStream_t s, const int64_t *seg_rows, int32_t nseg
         h.wide_tiles = read_flag(wide, s);
         h.all_narrow = h.wide_tiles == 0;
     }
+    // the ring form of the SpMV: every tile's entries from k0 rounded down to
+    // a multiple of 4 fit one 4-entry group per lane, its row offsets one per lane
+    h.ring_tiles = h.all_narrow;
+    for (const TileDesc &d : shorts)
+        if (d.k1 - (d.k0 & ~(int64_t)3) > 4 * 64 || d.re - d.rs > 63) {
+            h.ring_tiles = false;
+            break;
+        }
     SLA_HIP(hipStreamSynchronize(s));
 }
 

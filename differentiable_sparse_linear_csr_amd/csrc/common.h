@@ -149,6 +149,12 @@ struct Handle {
     uint16_t *col16 = nullptr;   // [nnz + pad] tile-relative columns of narrow tiles
     uint16_t *roff16 = nullptr;  // per tile: row offsets relative to the tile's k0
     bool all_narrow = false;     // every tile narrow: the SpMV reads col16 only
+    bool ring_tiles = false;     // every tile narrow, <= 256 entry slots and <= 63 rows
+    bool spmv_ring = true;       // SpMV on ring_tiles handles: the ring form
+    // band-aligned tiles (see choose_band): band N rows, L tiles per N rows,
+    // P panels of L wavefronts per XCD; 0 when the tiles are the usual runs
+    int64_t band_n = 0, band_l = 0;
+    int32_t band_p = 0;
     int32_t *long_rows = nullptr; // rows longer than kLongRow, in row order
     int64_t nlong = 0;
     double *long_dot = nullptr;   // [nlong] p_i q_i of the long rows (fused SpMV)
@@ -182,6 +188,7 @@ struct Handle {
     // resident workgroups of the persistent SpMV on this device (CUs x occupancy,
     // a multiple of the XCD count): larger grids would run in two rounds
     int64_t spmv_resident = kMaxGrid;
+    int64_t ring_resident = kMaxGrid;
     // the same for the batched 16-byte-lane kernels: SpMV (plain, fused),
     // update, direction
     int64_t bvec_resident[2] = {kMaxGrid, kMaxGrid};
@@ -318,7 +325,8 @@ Handle *transpose_for_backward(Handle &h, hipStream_t s);
 void build_segments(Handle &h, const int64_t *seg_rows, int32_t nseg, hipStream_t s);
 void launch_spmv_plain(Handle &h, const void *x, void *y, hipStream_t s);
 inline int32_t num_systems(const Handle &h) { return h.nseg > 0 ? h.nseg : h.B; }
-int64_t resident_workgroups(const void *kernel, int device);
+int64_t resident_workgroups(const void *kernel, int device, size_t dyn_lds = 0);
+int64_t tile_spmv_waves_per_xcd(const Handle &h, bool ring);
 void pcg(Handle &h, const void *b_user, void *x_user, double tol, int32_t maxit, sla_info *info,
          hipStream_t s, bool keep_internal_solution);
 // grad[b][k] = sign * a[row k][b] * x[b][col k]: a in the internal layout

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
     const T *__restrict__ x, T *__restrict__ y, const T *__restrict__ w,
     const double *__restrict__ long_dot, int64_t nlong, double *__restrict__ spart,
     const int32_t *__restrict__ status, const uint8_t *__restrict__ live,
-    double *__restrict__ tile_dot) {
+    double *__restrict__ tile_dot, int64_t band_l, int32_t band_p) {
     constexpr bool FUSED = DOT > 0;
     constexpr bool PERTILE = DOT == 3;
     __shared__ __align__(16) double prod_all[kWaves][kProdSlots];
@@ -113,10 +113,22 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
     int32_t *roff = roff_all[wv];
     double *pown = pown_all[FUSED ? wv : 0];  // w of the tile's own rows (fused forms)
     const int xcd = blockIdx.x % kXcds;
-    const int64_t waves_per_xcd = (int64_t)(gridDim.x / kXcds) * kWaves;
+    int64_t waves_per_xcd = (int64_t)(gridDim.x / kXcds) * kWaves;
     const int64_t wid = (int64_t)(blockIdx.x / kXcds) * kWaves + wv;  // rank within its XCD
     int64_t t = ntiles * xcd / kXcds + wid;
-    const int64_t t_end = ntiles * (xcd + 1) / kXcds;
+    int64_t t_end = ntiles * (xcd + 1) / kXcds;
+    if (!PERTILE && band_l > 0 && band_l * band_p == waves_per_xcd) {
+        // band-aligned tiles: the XCD's range splits into band_p panels of
+        // band_l columns; wavefront `col` of a panel walks tiles col, col + L,
+        // col + 2L, ... of it, so the p lines that tile j gathers near +N are
+        // gathered again, as its own rows, one step later by the same
+        // wavefront (tile j + L), and near -N one step after that
+        const int64_t T0 = t - wid, T1 = t_end;
+        const int64_t panel = wid / band_l, col = wid - panel * band_l;
+        t = T0 + (T1 - T0) * panel / band_p + col;
+        t_end = T0 + (T1 - T0) * (panel + 1) / band_p;
+        waves_per_xcd = band_l;   // the stride of the walk
+    }
     double dot = 0.0, dot2 = 0.0;
 
     TileDesc d{0, 0, 0, 0, 0, 0, 0};
@@ -278,6 +290,215 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
         // this workgroup's partials; the next kernel sums them (every
         // workgroup there, in block order) and forms its step, so this
         // kernel ends without a grid-wide arrival
+        for (int64_t l = blockIdx.x + (int64_t)threadIdx.x * gridDim.x; l < nlong;
+             l += (int64_t)kBlock * gridDim.x) {
+            dot += long_dot[l];
+            if (DOT == 2) dot2 += long_dot[nlong + l];
+        }
+        dot = block_sum(dot, lds4);
+        if (DOT == 2) dot2 = block_sum(dot2, lds4);
+        if (threadIdx.x == 0) {
+            spart[(int64_t)DOT * blockIdx.x] = dot;
+            if (DOT == 2) spart[2 * (int64_t)blockIdx.x + 1] = dot2;
+        }
+    }
+}
+
+// The same product for tiles that each fit one 4-entry group per lane and one
+// row offset per lane (entries from k0 rounded down to a multiple of 4 up to
+// k1 at most 256, at most 63 rows) with 16-bit columns: a ring of kRing tiles
+// per wavefront. Memory operations complete in issue order, so a wavefront
+// that waits for a tile's gathers also waits for everything issued before
+// them; here a tile's entries (packed columns, values, row offsets and w of
+// its rows) are issued kRing tiles, and its gathers two tiles, before the
+// tile is summed, and each wait leaves the later tiles' loads in flight
+// (in k_spmv_tile a tile's gathers are waited for with nothing else of the
+// wavefront's in flight). Descriptors come one tile ahead of the entries.
+// Same tiles, walk, sums and results as k_spmv_tile.
+constexpr int kRing = 4;
+// Unused LDS requested at launch so that every form (fp64 or fp32, 0 to 3
+// fused dots; static LDS 9 to 11 KB) holds four workgroups per CU (160 KB
+// each), whatever its register count: the grid is the resident count of one
+// form, and the band-aligned walk needs the wavefronts per XCD it was built
+// for. Four rather than five (the most registers allow): 512 wavefronts per
+// XCD make 45-row tiles of the 11548-row band (640: 36 rows), and on the
+// 133M-row Poisson matrix the SpMV took 2.05 ms against 2.14 (kernel trace;
+// 23-row tiles 2.52 ms, 30-row 2.20 ms, the usual tiles 2.40 ms).
+constexpr size_t kRingLdsPad = 24 * 1024;
+
+template <typename T, typename RP, int DOT>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_spmv_tile_ring(
+    const TileDesc *__restrict__ tiles, int64_t ntiles, const uint16_t *__restrict__ roff16,
+    const uint16_t *__restrict__ col16, const T *__restrict__ val, const T *__restrict__ x,
+    T *__restrict__ y, const T *__restrict__ w, const double *__restrict__ long_dot, int64_t nlong,
+    double *__restrict__ spart, const int32_t *__restrict__ status, const uint8_t *__restrict__ live,
+    double *__restrict__ tile_dot, int64_t band_l, int32_t band_p) {
+    constexpr bool FUSED = DOT > 0;
+    constexpr bool PERTILE = DOT == 3;
+    __shared__ __align__(16) double prod_all[kWaves][4 * 64];
+    __shared__ int32_t roff_all[kWaves][64];
+    __shared__ double pown_all[FUSED ? kWaves : 1][FUSED ? 64 : 1];
+    __shared__ double lds4[kWaves];
+    if (FUSED && !PERTILE && *status != kRunning) return;
+
+    const int lane = threadIdx.x & 63;
+    // wave-uniform, so that tile indices and descriptors live in scalar registers
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    double *prod = prod_all[wv];
+    int32_t *roff = roff_all[wv];
+    double *pown = pown_all[FUSED ? wv : 0];
+    const int xcd = blockIdx.x % kXcds;
+    int64_t stride = (int64_t)(gridDim.x / kXcds) * kWaves;
+    const int64_t wid = (int64_t)(blockIdx.x / kXcds) * kWaves + wv;
+    int64_t t_next = ntiles * xcd / kXcds + wid;
+    int64_t t_end = ntiles * (xcd + 1) / kXcds;
+    if (!PERTILE && band_l > 0 && band_l * band_p == stride) {
+        const int64_t T0 = t_next - wid, T1 = t_end;
+        const int64_t panel = wid / band_l, colw = wid - panel * band_l;
+        t_next = T0 + (T1 - T0) * panel / band_p + colw;
+        t_end = T0 + (T1 - T0) * (panel + 1) / band_p;
+        stride = band_l;
+    }
+    auto next_live = [&](int64_t u) {
+        if (PERTILE)
+            while (u < t_end && !live[u]) u += stride;
+        return u;
+    };
+    double dot = 0.0, dot2 = 0.0;
+
+    // slot u: tile, descriptor fields, the lane's packed 16-bit columns,
+    // values, row offset and w; gather buffer h: x at the slot's columns
+    int64_t s_t[kRing];
+    int32_t s_rs[kRing], s_nr[kRing], s_nk[kRing], s_shift[kRing], s_cb[kRing];
+    uint2 s_c[kRing];
+    T s_v[kRing][4];
+    int32_t s_ro[kRing];
+    T s_w[kRing];
+    double xv[2][4];
+    t_next = next_live(t_next);
+    TileDesc dn{0, 0, 0, 0, 0, 0, 0};
+    if (t_next < t_end) dn = tiles[t_next];
+    // Slot u takes tile t_next (descriptor dn; past the end, an empty tile
+    // whose loads read entry 0, row 0 and offset 0). Every load is issued by
+    // every lane, at a clamped offset where the lane has nothing to load:
+    // loads that are always issued let the compiler wait for a tile's loads
+    // while the later ones stay in flight. What clamped lanes load is never
+    // used: their products go to slots the sums do not read, their gathers
+    // read x[0], their offsets and w are not stored.
+    auto fetch = [&](int u) {
+        s_t[u] = t_next;
+        TileDesc e{0, 0, 0, 0, 0, 0, 0};
+        if (t_next < t_end) e = dn;
+        s_rs[u] = e.rs;
+        s_nr[u] = e.re - e.rs;
+        s_nk[u] = (int)(e.k1 - e.k0);
+        s_shift[u] = (int)(e.k0 & 3);
+        s_cb[u] = e.cbase;
+        const int64_t base = e.k0 & ~(int64_t)3;
+        const int span = (int)(e.k1 - base);
+        const int g = 4 * lane < span ? 4 * lane : 0;
+        s_c[u] = *reinterpret_cast<const uint2 *>(col16 + base + g);
+        load4(val + base + g, s_v[u]);
+        const int nr = s_nr[u];
+        s_ro[u] = (int32_t)roff16[e.rpos + (lane <= nr ? lane : nr)];
+        if (FUSED) s_w[u] = w[e.rs + (lane < nr ? lane : 0)];
+        if (t_next < t_end) t_next = next_live(t_next + stride);
+    };
+    // the descriptor of the tile the next fetch takes (scalar loads; issued
+    // after a tile's sums, it is back by the next fetch)
+    auto load_desc = [&]() {
+        if (t_next < t_end) dn = tiles[t_next];
+    };
+    auto gather = [&](int u, int hb) {
+        const int shift = s_shift[u], nk = s_nk[u], cb = s_cb[u];
+        const uint32_t raw[2] = {s_c[u].x, s_c[u].y};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int j = 4 * lane + k - shift;
+            const int32_t c = cb + (int32_t)((raw[k >> 1] >> (16 * (k & 1))) & 0xffffu);
+            xv[hb][k] = (double)x[(j >= 0 && j < nk) ? c : 0];
+        }
+    };
+    // the tile of slot u (gathers in xv[hb]): products, row offsets and w to
+    // LDS; slot u refilled with the next tile; the gathers of the tile two
+    // on issued; the row sums; the next descriptor requested
+    auto step = [&](int u, int hb) {
+        const int nrows = s_nr[u], shift = s_shift[u], nk = s_nk[u], rs = s_rs[u];
+        const int64_t ti = s_t[u];
+        {
+            const int g = 4 * lane;
+            if (g < nk + shift) {
+                double2 *pd = reinterpret_cast<double2 *>(prod + g);
+                pd[0] = make_double2((double)s_v[u][0] * xv[hb][0], (double)s_v[u][1] * xv[hb][1]);
+                pd[1] = make_double2((double)s_v[u][2] * xv[hb][2], (double)s_v[u][3] * xv[hb][3]);
+            }
+            if (lane <= nrows) roff[lane] = s_ro[u];
+            if (FUSED && lane < nrows) pown[lane] = (double)s_w[u];
+        }
+        fetch(u);
+        gather((u + 2) % kRing, hb);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // groups of G lanes, G the largest power of two with 2 G nrows <= 64
+        // (64 for nrows <= 1): 64 / G >= nrows groups, one row each
+        int G = 1;
+        while (G < 64 && G * 2 * nrows <= 64) G *= 2;
+        const int lg = lane & (G - 1);
+        const int i = lane / G;
+        if (i < nrows) {
+            const int a = roff[i] + shift, b = roff[i + 1] + shift;
+            constexpr int kSB = kSumBatch;
+            double pv[kSB];
+#pragma unroll
+            for (int q = 0; q < kSB; ++q) {
+                const int j = a + lg + q * G;
+                pv[q] = prod[j < 4 * 64 - 1 ? j : 4 * 64 - 1];   // clamped; unused past b
+            }
+            double sm = 0.0;
+#pragma unroll
+            for (int q = 0; q < kSB; ++q)
+                if (a + lg + q * G < b) sm += pv[q];
+            for (int j = a + lg + kSB * G; j < b; j += G) sm += prod[j];
+            for (int off = G >> 1; off > 0; off >>= 1) sm += __shfl_xor(sm, off, 64);
+            if (lg == 0) {
+                const T q = (T)sm;
+                y[rs + i] = q;
+                if (FUSED) dot += pown[i] * (double)q;
+                if (DOT == 2) dot2 += (double)q * (double)q;
+            }
+        }
+        if (PERTILE) {
+            const double td = wave_sum(dot);
+            if (lane == 0 && ti < t_end) tile_dot[ti] = td;
+            dot = 0.0;
+        }
+        load_desc();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    // (a wavefront without tiles loads nothing: x and w may be empty)
+    if (t_next < t_end) {
+#pragma unroll
+        for (int u = 0; u < kRing; ++u) {
+            fetch(u);
+            load_desc();
+        }
+        gather(0, 0);
+        gather(1, 1);
+        while (s_t[0] < t_end) {
+            step(0, 0);
+            if (s_t[1] >= t_end) break;
+            step(1, 1);
+            if (s_t[2] >= t_end) break;
+            step(2, 0);
+            if (s_t[3] >= t_end) break;
+            step(3, 1);
+        }
+    }
+    if (FUSED && !PERTILE) {
         for (int64_t l = blockIdx.x + (int64_t)threadIdx.x * gridDim.x; l < nlong;
              l += (int64_t)kBlock * gridDim.x) {
             dot += long_dot[l];
@@ -496,6 +717,16 @@ int64_t batched_grid_t(const Handle &h) {
     return (h.n + rows_block - 1) / rows_block;
 }
 
+bool use_ring(const Handle &h) { return h.all_narrow && h.ring_tiles && h.spmv_ring; }
+
+const void *ring_kernel(const Handle &h) {
+    if (h.vt == SLA_F64)
+        return h.rp64 ? (const void *)&k_spmv_tile_ring<double, int64_t, 1>
+                      : (const void *)&k_spmv_tile_ring<double, int32_t, 1>;
+    return h.rp64 ? (const void *)&k_spmv_tile_ring<float, int64_t, 1>
+                  : (const void *)&k_spmv_tile_ring<float, int32_t, 1>;
+}
+
 // Single system: the long-row kernel (if any) and the tile kernel, with DOT
 // fused inner products against w (see k_spmv_tile).
 template <typename T, typename RP, int DOT>
@@ -507,12 +738,21 @@ void launch_tiles(Handle &h, const void *x, void *y, const void *w, double *spar
                            (const int32_t *)h.col, (const T *)h.vals, (const T *)x, (T *)y,
                            (const T *)w, h.long_dot, status);
     const int64_t grid = spmv_grid(h);
+    if (use_ring(h)) {
+        hipLaunchKernelGGL((k_spmv_tile_ring<T, RP, DOT>), dim3((unsigned)grid), dim3(kBlock),
+                           kRingLdsPad, s,
+                           (const TileDesc *)h.tiles, h.ntiles, (const uint16_t *)h.roff16,
+                           (const uint16_t *)h.col16, (const T *)h.vals, (const T *)x, (T *)y,
+                           (const T *)w, (const double *)h.long_dot, h.nlong, spart, status,
+                           (const uint8_t *)h.tile_live, h.tile_dot, h.band_l, h.band_p);
+        return;
+    }
     auto kern = h.all_narrow ? k_spmv_tile<T, RP, DOT, true> : k_spmv_tile<T, RP, DOT, false>;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBlock), 0, s, (const TileDesc *)h.tiles,
                        h.ntiles, (const uint16_t *)h.roff16, (const int32_t *)h.col,
                        (const uint16_t *)h.col16, (const T *)h.vals, (const T *)x, (T *)y,
                        (const T *)w, (const double *)h.long_dot, h.nlong, spart, status,
-                       (const uint8_t *)h.tile_live, h.tile_dot);
+                       (const uint8_t *)h.tile_live, h.tile_dot, h.band_l, h.band_p);
 }
 
 template <typename T, typename RP, bool FUSED>
@@ -541,7 +781,8 @@ int64_t spmv_grid(const Handle &h) {
         const int64_t blocks = (h.ntiles + kWaves - 1) / kWaves;   // one tile per wavefront
         int64_t g = (blocks + kXcds - 1) / kXcds * kXcds;         // multiple of the XCD count
         if (g < kXcds) g = kXcds;
-        return g < h.spmv_resident ? g : h.spmv_resident;
+        const int64_t res = use_ring(h) ? h.ring_resident : h.spmv_resident;
+        return g < res ? g : res;
     }
     return h.vt == SLA_F64 ? batched_grid_t<double>(h) : batched_grid_t<float>(h);
 }
@@ -549,15 +790,27 @@ int64_t spmv_grid(const Handle &h) {
 // Resident capacity of the persistent tile kernel: every workgroup of the
 // grid must be on a CU at once, or the later ones start only when earlier
 // ones finish and the kernel runs in two rounds.
-int64_t resident_workgroups(const void *kernel, int device) {
+int64_t resident_workgroups(const void *kernel, int device, size_t dyn_lds) {
     int cus = 0, per_cu = 0;
     SLA_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device));
-    SLA_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0));
+    SLA_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, dyn_lds));
     int64_t g = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
     g = g / kXcds * kXcds;
     if (g < kXcds) g = kXcds;
     if (g > kMaxGrid) g = kMaxGrid;
     return g;
+}
+
+// Wavefronts per XCD of the tile SpMV when its grid is the resident count (the
+// narrow and wide forms have the same occupancy; ring: the ring form's)
+int64_t tile_spmv_waves_per_xcd(const Handle &h, bool ring) {
+    if (ring) return resident_workgroups(ring_kernel(h), h.device, kRingLdsPad) / kXcds * kWaves;
+    const void *fn = h.vt == SLA_F64
+                         ? (h.rp64 ? (const void *)&k_spmv_tile<double, int64_t, 1, true>
+                                   : (const void *)&k_spmv_tile<double, int32_t, 1, true>)
+                         : (h.rp64 ? (const void *)&k_spmv_tile<float, int64_t, 1, true>
+                                   : (const void *)&k_spmv_tile<float, int32_t, 1, true>);
+    return resident_workgroups(fn, h.device) / kXcds * kWaves;
 }
 
 void init_launch_limits(Handle &h) {
@@ -578,6 +831,7 @@ void init_launch_limits(Handle &h) {
                         : (const void *)&k_spmv_tile<float, int32_t, 1, false>;
     }
     h.spmv_resident = resident_workgroups(fn, h.device);
+    h.ring_resident = resident_workgroups(ring_kernel(h), h.device, kRingLdsPad);
     if (h.B > 1) {
         auto pick = [&](auto ttag, auto rtag) {
             using T = decltype(ttag);

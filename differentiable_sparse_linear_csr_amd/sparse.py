@@ -194,13 +194,14 @@ class SparseCSR:
 
     def layout(self) -> dict:
         """How the solver holds the matrix: reordered (P A P^T), 16-bit column
-        offsets in every SpMV tile, tile and long-row counts."""
+        offsets in every SpMV tile, every tile small enough for the four-tile
+        pipelined SpMV, tile and long-row counts."""
         r, nc = ctypes.c_int32(), ctypes.c_int32()
         t, lr = ctypes.c_int64(), ctypes.c_int64()
         check(_lib.load().sla_csr_get_layout(self._h, ctypes.byref(r), ctypes.byref(nc),
                                              ctypes.byref(t), ctypes.byref(lr)))
-        return {"reordered": bool(r.value), "narrow_columns": bool(nc.value), "tiles": t.value,
-                "long_rows": lr.value}
+        return {"reordered": bool(r.value), "narrow_columns": bool(nc.value),
+                "ring_tiles": nc.value == 2, "tiles": t.value, "long_rows": lr.value}
 
     def profile_reset(self) -> None:
         check(_lib.load().sla_profile_reset(self._h))

@@ -119,13 +119,19 @@ enum {
                                    work) makes the others' bounded waits expire: the solve
                                    then runs again on the per-step kernels (same result;
                                    reported by sla_csr_get_last_path), never hangs. */
-    SLA_OPT_SPIN_LIMIT = 7      /* polls a bounded grid-wide wait (single-kernel solve,
+    SLA_OPT_SPIN_LIMIT = 7,     /* polls a bounded grid-wide wait (single-kernel solve,
                                    fused update) makes before it gives up; default 2^22
                                    (about a second), 0 .. 2^32 - 1. A wait that gives up
                                    never changes a result: the solve is run again from the
                                    start on kernels without such waits. 0 makes every wait
                                    that is not already satisfied give up at once, which
                                    exercises that path. */
+    SLA_OPT_SPMV_RING = 8       /* 1 (default): the per-step SpMV of a single system whose
+                                   row tiles are all small (at most 63 rows and 253 entries,
+                                   columns within 65535 of the tile's smallest) keeps four
+                                   tiles' entries and two tiles' gathers in flight per
+                                   wavefront; 0: one tile ahead. Same tiles, same sums, bitwise
+                                   equal results. */
 };
 
 /* How the last sla_pcg_solve / sla_adjoint_backward / BiCGStab call on a
@@ -366,8 +372,9 @@ sla_status sla_bicgstab_adjoint(sla_csr h, const void *x, const void *grad_x, vo
 
 /* How the solver holds the matrix (host outputs; any may be NULL): reordered
  * = 1 when it runs on P A P^T; narrow_columns = 1 when every SpMV tile reads
- * 16-bit column offsets; tiles and long_rows count the SpMV's short-row tiles
- * and its rows longer than 128 entries. */
+ * 16-bit column offsets, 2 when in addition every tile is small enough for
+ * the four-tile pipeline of SLA_OPT_SPMV_RING; tiles and long_rows count the
+ * SpMV's short-row tiles and its rows longer than 128 entries. */
 sla_status sla_csr_get_layout(sla_csr h, int32_t *reordered, int32_t *narrow_columns,
                               int64_t *tiles, int64_t *long_rows);
 

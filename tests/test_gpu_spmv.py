@@ -116,3 +116,109 @@ def test_deterministic_bitwise():
     y1 = host(A.matvec(x))
     y2 = host(A.matvec(x))
     assert y1.tobytes() == y2.tobytes()
+
+
+@pytest.mark.parametrize("name,size", [("poisson2d_11548", 4100), ("diffusion3d_128", 110),
+                                       ("convdiff2d_1448", 1030)])
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_band_aligned_tiles(name, size, dtype):
+    """Stencil matrices of over 2^20 rows whose grid stride is 4096 rows or
+    more (the 2D and 3D ones here) get band-aligned tiles (tile j + L is tile
+    j moved by the stride) walked by columns; the smaller stride keeps the
+    usual tiles. The product, and 30 PCG steps or 12 BiCGStab steps on the
+    per-step kernels (tol 0), against the oracle."""
+    w = make_workload(name, size=size)
+    assert w.n >= 1 << 20
+    if w.fmt == "csr":
+        rows = np.repeat(np.arange(w.n), np.diff(w.row_ptr))
+        r, c = rows, w.cols
+    else:
+        r, c = w.rows, w.cols
+    v = w.vals.astype(dtype)
+    print(f"band-aligned tiles: {name} n={w.n} {np.dtype(dtype).name}", flush=True)
+    A = coo_handle(w.n, r, c, v)
+    x = np.random.default_rng(5).standard_normal(w.n).astype(dtype)
+    check(A, r, c, v, w.n, x, 1e-12 if dtype == np.float64 else 1e-5)
+    ref = oracle.coo_to_csr(w.n, r, c, v)
+    b = w.b.astype(dtype)
+    from differentiable_sparse_linear_csr_amd import _lib
+    A.set_option(_lib.SLA_OPT_RESIDENT, 0)
+    if w.extra.get("method") == "bicgstab":
+        xg, info = A.solve_raw(dev(b), 0.0, 12, method="bicgstab")
+        xo, *_ = oracle.bicgstab(ref["row_ptr"], ref["col"], ref["vals"], b, 0.0, 12)
+        tol = 1e-9 if dtype == np.float64 else 1e-4
+    else:
+        xg, info = A.solve_raw(dev(b), 0.0, 30)
+        xo, *_ = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, 0.0, 30)
+        tol = 1e-12 if dtype == np.float64 else 1e-5
+    assert rel(host(xg), xo) <= tol, rel(host(xg), xo)
+
+
+def banded_irregular(n, seed):
+    """Rows of 3 to 7 entries (one row in 50 empty) at columns within 2000 of
+    the diagonal: every SpMV tile small and narrow, row lengths ragged."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(3, 8, n)
+    lens[rng.random(n) < 0.02] = 0
+    rows = np.repeat(np.arange(n), lens)
+    off = rng.integers(-2000, 2001, rows.size)
+    cols = np.clip(rows + off, 0, n - 1)
+    key = np.unique(rows * n + cols)
+    rows, cols = key // n, key % n
+    vals = rng.standard_normal(rows.size)
+    return rows, cols, vals
+
+
+@pytest.mark.parametrize("case", ["poisson2d_1100", "diffusion3d_40", "banded_irregular", "tiny"])
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_ring_pipeline_matches_one_tile_ahead(case, dtype):
+    """SLA_OPT_SPMV_RING: the SpMV that keeps four tiles of entries and two
+    of gathers in flight per wavefront (the default where every tile is
+    small) against the one-tile-ahead kernel on the same handle: the same
+    tiles and sums, so bitwise equal products; both against the oracle; and
+    PCG (fused w.q) and BiCGStab (two fused dots) steps on the per-step
+    kernels against the oracle's."""
+    from differentiable_sparse_linear_csr_amd import _lib
+    spd = True
+    if case in ("poisson2d_1100", "diffusion3d_40"):
+        w = (make_workload("poisson2d_11548", size=1100) if case == "poisson2d_1100"
+             else make_workload("diffusion3d_128", size=40))
+        n, c, v = w.n, w.cols, w.vals
+        r = np.repeat(np.arange(n), np.diff(w.row_ptr)) if w.fmt == "csr" else w.rows
+    elif case == "banded_irregular":
+        n = 300000
+        r, c, v = banded_irregular(n, 7)
+        spd = False
+    else:
+        # fewer tiles than the ring holds: three wavefronts' rings never fill
+        n = 10
+        i = np.arange(n)
+        r = np.concatenate([i, i[1:], i[:-1]])
+        c = np.concatenate([i, i[:-1], i[1:]])
+        v = np.concatenate([np.full(n, 2.0), np.full(n - 1, -1.0), np.full(n - 1, -1.0)])
+    v = v.astype(dtype)
+    print(f"ring SpMV: {case} n={n} nnz={v.size} {np.dtype(dtype).name}", flush=True)
+    A = coo_handle(n, r, c, v)
+    lay = A.layout()
+    assert lay["narrow_columns"] and lay["ring_tiles"], lay
+    x = np.random.default_rng(11).standard_normal(n).astype(dtype)
+    y_ring = host(A.matvec(dev(x)))
+    A.set_option(_lib.SLA_OPT_SPMV_RING, 0)
+    y_one = host(A.matvec(dev(x)))
+    assert y_ring.tobytes() == y_one.tobytes()
+    A.set_option(_lib.SLA_OPT_SPMV_RING, 1)
+    check(A, r, c, v, n, x, 1e-12 if dtype == np.float64 else 1e-5)
+    if not spd:
+        return
+    ref = oracle.coo_to_csr(n, r, c, v)
+    b = np.random.default_rng(12).standard_normal(n).astype(dtype)
+    A.set_option(_lib.SLA_OPT_RESIDENT, 0)
+    steps, bsteps = (25, 8) if n > 1000 else (4, 3)   # short of exact convergence
+    xg, _ = A.solve_raw(dev(b), 0.0, steps)
+    xo, *_ = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, 0.0, steps)
+    tol = 1e-11 if dtype == np.float64 else 1e-4
+    assert rel(host(xg), xo) <= tol, rel(host(xg), xo)
+    xg, _ = A.solve_raw(dev(b), 0.0, bsteps, method="bicgstab")
+    xo, *_ = oracle.bicgstab(ref["row_ptr"], ref["col"], ref["vals"], b, 0.0, bsteps)
+    tol = 1e-9 if dtype == np.float64 else 1e-4
+    assert rel(host(xg), xo) <= tol, rel(host(xg), xo)
