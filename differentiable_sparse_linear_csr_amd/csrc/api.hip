@@ -358,6 +358,10 @@ void set_option(Handle *h, int32_t key, int64_t value) {
             if (h->spmv_ring != (value != 0)) drop_graphs(*h);
             h->spmv_ring = value != 0;
             break;
+        case SLA_OPT_FOLD_DIRECTION:
+            if (h->fold_direction != (value != 0)) drop_graphs(*h);
+            h->fold_direction = value != 0;
+            break;
         case SLA_OPT_FUSED_UPDATE:
             if (h->fuse_update != (value != 0)) drop_graphs(*h);
             h->fuse_update = value != 0;

@@ -743,7 +743,8 @@ void build_tiles(Handle &h, hipStream_t s, const int64_t *seg_rows, int32_t nseg
         }
         h.seg_tile0 = (int64_t *)dalloc(h, 8 * ((size_t)nseg + 1));
         h.seg_long0 = (int64_t *)dalloc(h, 8 * ((size_t)nseg + 1));
-        h.tile_live = (uint8_t *)dalloc(h, shorts.size() + 1);
+        // (+4: the SpMV reads the flags as 32-bit words)
+        h.tile_live = (uint8_t *)dalloc(h, shorts.size() + 4);
         h.tile_dot = (double *)dalloc(h, sizeof(double) * (shorts.size() + 1));
         SLA_HIP(hipMemcpyAsync(h.seg_tile0, t0.data(), 8 * ((size_t)nseg + 1), hipMemcpyHostToDevice,
                                s));

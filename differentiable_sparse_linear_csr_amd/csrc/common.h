@@ -98,6 +98,19 @@ struct Bcast {
     int32_t pad;
 };
 
+// The direction update folded into the SpMV of a single system (per-step
+// solve): p_new = z + beta p_old is formed where the SpMV reads it, at every
+// gathered column and at the tile's own rows, and x += alpha p_old (the step
+// of the update before) is applied to the own rows. p_old = p[iter & 1],
+// p_new = p[(iter + 1) & 1], so that a captured block of iterations reads
+// the buffers from the iteration count, not from its arguments.
+struct FoldArgs {
+    const void *z;        // z = dinv r of the last update
+    void *p[2];           // the two direction buffers
+    void *x;              // the iterate
+    const SysState *st;   // beta, alpha (0: no pending step) and iter
+};
+
 // Arrival counters of the grid reductions: per kernel kind, kGroups group
 // counters and one top counter, each on its own 256-byte line so that
 // arrivals at different counters do not serialize.
@@ -151,6 +164,10 @@ struct Handle {
     bool all_narrow = false;     // every tile narrow: the SpMV reads col16 only
     bool ring_tiles = false;     // every tile narrow, <= 256 entry slots and <= 63 rows
     bool spmv_ring = true;       // SpMV on ring_tiles handles: the ring form
+    bool fold_direction = true;  // per-step single-system solve: direction folded into the SpMV
+    bool fold_active = false;    // the solve being run folds it (set per attempt)
+    void *fold_z = nullptr;      // z = dinv r (folded solves)
+    void *fold_p2 = nullptr;     // second direction buffer (folded solves)
     // band-aligned tiles (see choose_band): band N rows, L tiles per N rows,
     // P panels of L wavefronts per XCD; 0 when the tiles are the usual runs
     int64_t band_n = 0, band_l = 0;
@@ -628,6 +645,8 @@ void launch_update_raw(int64_t n, double *x, double *r, const double *p, const d
 void launch_direction_raw(int64_t n, const double *r, double *p, const double *dinv,
                           const Ctl *ctl, const SysState *st, hipStream_t s);
 int64_t raw_vec_grid(int64_t n);
+bool fold_possible(const Handle &h);
+void launch_spmv_fold(Handle &h, hipStream_t s);
 void launch_spmv_csr_dot_raw(int64_t n, const int32_t *row_ptr, const int32_t *col,
                              const double *val, const double *p, double *q, Red red, Ctl *ctl,
                              SysState *st, int32_t *running, hipStream_t s);

@@ -37,14 +37,14 @@ int64_t vec_grid(int64_t n, int B) {
     return g;
 }
 
-// r = b, x = 0, p = z = dinv r; partials of b.b and r.z; last block sets up
-// the per-system scalars and status.
+// r = b, x = 0, p = z = dinv r (and z into z_out unless null); partials of
+// b.b and r.z; last block sets up the per-system scalars and status.
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_init(int64_t n, int B, const T *__restrict__ b_in,
                                                  T *__restrict__ x, T *__restrict__ r,
                                                  T *__restrict__ p, const T *__restrict__ dinv,
-                                                 Red red, Ctl *__restrict__ ctl,
-                                                 SysState *__restrict__ st,
+                                                 T *__restrict__ z_out, Red red,
+                                                 Ctl *__restrict__ ctl, SysState *__restrict__ st,
                                                  int32_t *__restrict__ h_running) {
     __shared__ double tmp[kBlock];
     __shared__ double blk[kMaxBatch];
@@ -71,6 +71,7 @@ __global__ __launch_bounds__(kBlock) void k_init(int64_t n, int B, const T *__re
                 x[f] = (T)0;
                 r[f] = bv[u];
                 p[f] = (T)z;
+                if (z_out) z_out[f] = (T)z;
                 sbb += (double)bv[u] * (double)bv[u];
                 srz += (double)bv[u] * z;
             }
@@ -515,7 +516,12 @@ int64_t bv_grid(int64_t nc, int64_t resident) {
 // each memory instruction moves twice (fp64) or four times (fp32) the data of
 // the per-row forms; rows past the last full group are done by block 0.
 
-template <typename T, bool NT>
+//
+// FOLD (direction folded into the SpMV, see FoldArgs): x and p are not
+// touched here; z = dinv r is stored into x's place (the z buffer), and the
+// step alpha is kept in the system state for the next SpMV (or the final
+// x update) to apply to x.
+template <typename T, bool NT, bool FOLD = false>
 __global__ __launch_bounds__(kBlock) void k_update1(int64_t n, T *__restrict__ x,
                                                     T *__restrict__ r, const T *__restrict__ p,
                                                     const T *__restrict__ q,
@@ -545,10 +551,12 @@ __global__ __launch_bounds__(kBlock) void k_update1(int64_t n, T *__restrict__ x
     const bool breakdown = !(sigma > 0.0) || !isfinite(sigma);
     const double alpha = breakdown ? 0.0 : st[0].rho / sigma;
     double srz = 0.0, srr = 0.0;
+    // FOLD: xv carries z out instead of x
     auto row = [&](T &xv, T &rv, T pv, T qv, T dv) {
-        xv = (T)((double)xv + alpha * (double)pv);
+        if (!FOLD) xv = (T)((double)xv + alpha * (double)pv);
         rv = (T)((double)rv - alpha * (double)qv);
         const double z = (double)dv * (double)rv;
+        if (FOLD) xv = (T)z;
         srz += (double)rv * z;
         srr += (double)rv * (double)rv;
     };
@@ -561,8 +569,10 @@ __global__ __launch_bounds__(kBlock) void k_update1(int64_t n, T *__restrict__ x
         for (int u = 0; u < kVecGroups; ++u) {
             const int64_t g = g0 + u * kBlock + tid;
             if (g < ng) {
-                vload_h<NT>(x + g * W, xv[u]);
-                vload_h<NT>(p + g * W, pv[u]);
+                if (!FOLD) {
+                    vload_h<NT>(x + g * W, xv[u]);
+                    vload_h<NT>(p + g * W, pv[u]);
+                }
                 vload_h<NT>(r + g * W, rv[u]);
                 vload_h<NT>(q + g * W, qv[u]);
                 vload_h<NT>(dinv + g * W, dv[u]);
@@ -581,8 +591,8 @@ __global__ __launch_bounds__(kBlock) void k_update1(int64_t n, T *__restrict__ x
     }
     if (!breakdown && blockIdx.x == 0 && tid < n - ng * W) {
         const int64_t i = ng * W + tid;
-        T xi = x[i], ri = r[i];
-        row(xi, ri, p[i], q[i], dinv[i]);
+        T xi = FOLD ? (T)0 : x[i], ri = r[i];
+        row(xi, ri, FOLD ? (T)0 : p[i], q[i], dinv[i]);
         x[i] = xi;
         r[i] = ri;
     }
@@ -598,6 +608,7 @@ __global__ __launch_bounds__(kBlock) void k_update1(int64_t n, T *__restrict__ x
             const double rz = tot[0], rr = tot[1];
             int running = 0;
             sy.iter += 1;
+            if (FOLD) sy.alpha = alpha;   // x += alpha p is applied later (0 at breakdown)
             if (breakdown) {
                 sy.status = SLA_BREAKDOWN;  // x, r untouched; rr keeps the last residual
             } else {
@@ -818,6 +829,46 @@ __global__ __launch_bounds__(kBlock) void k_direction1(int64_t n, const T *__res
     }
 }
 
+// End of a folded solve: the last update's step x += alpha p (p = the
+// direction the last SpMV formed, p[iter & 1]), which no later SpMV applied.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_fold_finish(int64_t n, T *__restrict__ x,
+                                                        const T *__restrict__ p0,
+                                                        const T *__restrict__ p1,
+                                                        const SysState *__restrict__ st) {
+    constexpr int W = VecW<T>::W;
+    const double alpha = st[0].alpha;
+    if (alpha == 0.0) return;
+    const T *p = (st[0].iter & 1) ? p1 : p0;
+    const int tid = threadIdx.x;
+    const int64_t ng = n / W;
+    const int64_t per_pass = (int64_t)kBlock * kVecGroups;
+    for (int64_t g0 = (int64_t)blockIdx.x * per_pass; g0 < ng; g0 += (int64_t)gridDim.x * per_pass) {
+        T xv[kVecGroups][W], pv[kVecGroups][W];
+#pragma unroll
+        for (int u = 0; u < kVecGroups; ++u) {
+            const int64_t g = g0 + u * kBlock + tid;
+            if (g < ng) {
+                vload(x + g * W, xv[u]);
+                vload(p + g * W, pv[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kVecGroups; ++u) {
+            const int64_t g = g0 + u * kBlock + tid;
+            if (g < ng) {
+#pragma unroll
+                for (int k = 0; k < W; ++k) xv[u][k] = (T)((double)xv[u][k] + alpha * (double)pv[u][k]);
+                vstore(x + g * W, xv[u]);
+            }
+        }
+    }
+    if (blockIdx.x == 0 && tid < n - ng * W) {
+        const int64_t i = ng * W + tid;
+        x[i] = (T)((double)x[i] + alpha * (double)p[i]);
+    }
+}
+
 // grid of the fused update + direction: one pass per workgroup, all of them
 // resident at once; 0 when the system does not fit (or B > 1)
 int64_t fused_grid(const Handle &h, int W) {
@@ -837,6 +888,14 @@ int64_t fused_bv_grid(const Handle &h, int W) {
     int64_t g = (nc + per - 1) / per;
     if (g < 1) g = 1;
     return g <= h.upd_dir_bv_resident ? g : 0;
+}
+
+// the per-step solve folds the direction into the SpMV: a single system on
+// ring-form tiles without long rows, where the fused update + direction
+// kernel does not apply (too large for one resident pass, or switched off)
+bool want_fold(const Handle &h) {
+    if (!h.fold_direction || !fold_possible(h)) return false;
+    return fused_grid(h, h.vt == SLA_F64 ? VecW<double>::W : VecW<float>::W) == 0;
 }
 
 int64_t vec1_grid(int64_t n, int W) {
@@ -949,6 +1008,23 @@ template <typename T>
 void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
     const int64_t g = vec_grid(h.n, h.B);
     hipEvent_t a = nullptr;
+    if (h.fold_active) {
+        // direction folded into the SpMV; the update stores z, not x
+        if (lp) lp->begin(SLA_KERNEL_SPMV_DOT, &a);
+        launch_spmv_fold(h, s);
+        if (lp) lp->end(SLA_KERNEL_SPMV_DOT, a);
+        if (lp) lp->begin(SLA_KERNEL_UPDATE, &a);
+        const Red red{h.part, h.gpart, h.sync + kCntUpdate * kCountersPerKind};
+        const int64_t g1 = vec1_grid(h.n, VecW<T>::W);
+        const bool nt = h.n * (int64_t)sizeof(T) >= kNtVectorBytes;
+        hipLaunchKernelGGL((nt ? k_update1<T, true, true> : k_update1<T, false, true>),
+                           dim3((unsigned)g1), dim3(kBlock), 0, s, h.n, (T *)h.fold_z, (T *)h.r,
+                           (const T *)nullptr, (const T *)h.q, (const T *)h.dinv,
+                           (const double *)h.spart, spmv_grid(h), red, h.ctl, h.st, h.d_running);
+        SLA_HIP(hipGetLastError());
+        if (lp) lp->end(SLA_KERNEL_UPDATE, a);
+        return;
+    }
     if (lp) lp->begin(SLA_KERNEL_SPMV_DOT, &a);
     launch_spmv_dot(h, s);
     if (lp) lp->end(SLA_KERNEL_SPMV_DOT, a);
@@ -1057,8 +1133,8 @@ void init_t(Handle &h, const void *b_int, hipStream_t s, Launcher *lp) {
     if (lp) lp->begin(SLA_KERNEL_INIT, &a);
     const Red red{h.part, h.gpart, h.sync + kCntInit * kCountersPerKind};
     hipLaunchKernelGGL(k_init<T>, dim3((unsigned)g), dim3(kBlock), 0, s, h.n, h.B, (const T *)b_int,
-                       (T *)h.x, (T *)h.r, (T *)h.p, (const T *)h.dinv, red, h.ctl, h.st,
-                       h.d_running);
+                       (T *)h.x, (T *)h.r, (T *)h.p, (const T *)h.dinv,
+                       (T *)(h.fold_active ? h.fold_z : nullptr), red, h.ctl, h.st, h.d_running);
     SLA_HIP(hipGetLastError());
     if (lp) lp->end(SLA_KERNEL_INIT, a);
 }
@@ -1095,7 +1171,7 @@ void launch_init_raw(int64_t n, const double *b, double *x, double *r, double *p
                      const double *dinv, Red red, Ctl *ctl, SysState *st, int32_t *running,
                      hipStream_t s) {
     hipLaunchKernelGGL(k_init<double>, dim3((unsigned)vec_grid(n, 1)), dim3(kBlock), 0, s, n, 1, b,
-                       x, r, p, dinv, red, ctl, st, running);
+                       x, r, p, dinv, (double *)nullptr, red, ctl, st, running);
     SLA_HIP(hipGetLastError());
 }
 
@@ -1210,6 +1286,11 @@ bool pcg_attempt(Handle &h, const void *b_user, void *x_user, double tol, int32_
         transpose(b_user, h.q, h.B, h.n, h.vbytes, s);  // q is free until the first SpMV
         b_int = h.q;
     }
+    h.fold_active = want_fold(h);
+    if (h.fold_active && !h.fold_z) {
+        h.fold_z = dalloc(h, (size_t)h.n * h.vbytes);
+        h.fold_p2 = dalloc(h, (size_t)h.n * h.vbytes);
+    }
     if (h.nseg > 0) seg_init(h, b_int, s, lp);
     else if (h.vt == SLA_F64) init_t<double>(h, b_int, s, lp);
     else init_t<float>(h, b_int, s, lp);
@@ -1230,6 +1311,19 @@ bool pcg_attempt(Handle &h, const void *b_user, void *x_user, double tol, int32_
             SLA_HIP(hipEventSynchronize(h.ev[(ch - 1) & 1]));
             if (__atomic_load_n(h.h_running, __ATOMIC_ACQUIRE) == 0) break;
         }
+    }
+    if (h.fold_active) {
+        const int W = h.vt == SLA_F64 ? VecW<double>::W : VecW<float>::W;
+        const unsigned gf = (unsigned)vec1_grid(h.n, W);
+        if (h.vt == SLA_F64)
+            hipLaunchKernelGGL(k_fold_finish<double>, dim3(gf), dim3(kBlock), 0, s, h.n,
+                               (double *)h.x, (const double *)h.p, (const double *)h.fold_p2,
+                               (const SysState *)h.st);
+        else
+            hipLaunchKernelGGL(k_fold_finish<float>, dim3(gf), dim3(kBlock), 0, s, h.n,
+                               (float *)h.x, (const float *)h.p, (const float *)h.fold_p2,
+                               (const SysState *)h.st);
+        SLA_HIP(hipGetLastError());
     }
     if (!keep_internal_solution) {
         // (if a wait gave up, the re-run overwrites what is copied here)

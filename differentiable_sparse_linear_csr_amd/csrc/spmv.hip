@@ -304,6 +304,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
     }
 }
 
+// The folded direction p = z + beta p_old of one row, rounded to T: the same
+// fused multiply-add wherever it is formed (a tile's own rows and every
+// gathered column), so each row's p_new is one value.
+template <typename T>
+__device__ __forceinline__ T fold_p(double z, double pold, double beta) {
+    return (T)__builtin_fma(beta, pold, z);
+}
+
 // The same product for tiles that each fit one 4-entry group per lane and one
 // row offset per lane (entries from k0 rounded down to a multiple of 4 up to
 // k1 at most 256, at most 63 rows) with 16-bit columns: a ring of kRing tiles
@@ -332,9 +340,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     const uint16_t *__restrict__ col16, const T *__restrict__ val, const T *__restrict__ x,
     T *__restrict__ y, const T *__restrict__ w, const double *__restrict__ long_dot, int64_t nlong,
     double *__restrict__ spart, const int32_t *__restrict__ status, const uint8_t *__restrict__ live,
-    double *__restrict__ tile_dot, int64_t band_l, int32_t band_p) {
+    double *__restrict__ tile_dot, int64_t band_l, int32_t band_p, FoldArgs fa) {
     constexpr bool FUSED = DOT > 0;
     constexpr bool PERTILE = DOT == 3;
+    constexpr bool FOLD = DOT == 4;   // direction folded in (see FoldArgs); w.q with w = p_new
     __shared__ __align__(16) double prod_all[kWaves][4 * 64];
     __shared__ int32_t roff_all[kWaves][64];
     __shared__ double pown_all[FUSED ? kWaves : 1][FUSED ? 64 : 1];
@@ -359,12 +368,29 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         t_end = T0 + (T1 - T0) * (panel + 1) / band_p;
         stride = band_l;
     }
+    // the live flags read as 32-bit words from wave-uniform addresses
+    // (scalar loads, which the in-order vector counter does not wait for)
+    const uint32_t *live32 = reinterpret_cast<const uint32_t *>(live);
     auto next_live = [&](int64_t u) {
         if (PERTILE)
-            while (u < t_end && !live[u]) u += stride;
+            while (u < t_end && ((live32[u >> 2] >> (8 * (u & 3))) & 0xffu) == 0) u += stride;
         return u;
     };
     double dot = 0.0, dot2 = 0.0;
+    // folded form: the gathers read z and p_old; x is updated in place
+    double beta = 0.0, ax = 0.0;
+    const T *zz = nullptr, *pold = nullptr;
+    T *pnew = nullptr, *xx = nullptr;
+    if (FOLD) {
+        const SysState s0 = *fa.st;
+        beta = s0.beta;
+        ax = s0.alpha;
+        const int par = s0.iter & 1;
+        zz = (const T *)fa.z;
+        pold = (const T *)fa.p[par];
+        pnew = (T *)fa.p[par ^ 1];
+        xx = (T *)fa.x;
+    }
 
     // slot u: tile, descriptor fields, the lane's packed 16-bit columns,
     // values, row offset and w; gather buffer h: x at the slot's columns
@@ -375,6 +401,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     int32_t s_ro[kRing];
     T s_w[kRing];
     double xv[2][4];
+    // folded form: p_old at the columns, z and p_old of the lane's own row
+    // (gathered with the columns) and x of it (fetched with the entries: it
+    // is read nowhere else, so it comes from HBM)
+    double pg[FOLD ? 2 : 1][4];
+    T oz[FOLD ? 2 : 1], op[FOLD ? 2 : 1], s_x[FOLD ? kRing : 1];
     t_next = next_live(t_next);
     TileDesc dn{0, 0, 0, 0, 0, 0, 0};
     if (t_next < t_end) dn = tiles[t_next];
@@ -401,7 +432,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         load4(val + base + g, s_v[u]);
         const int nr = s_nr[u];
         s_ro[u] = (int32_t)roff16[e.rpos + (lane <= nr ? lane : nr)];
-        if (FUSED) s_w[u] = w[e.rs + (lane < nr ? lane : 0)];
+        if (FUSED && !FOLD) s_w[u] = w[e.rs + (lane < nr ? lane : 0)];
+        if (FOLD) s_x[FOLD ? u : 0] = xx[e.rs + (lane < nr ? lane : 0)];
         if (t_next < t_end) t_next = next_live(t_next + stride);
     };
     // the descriptor of the tile the next fetch takes (scalar loads; issued
@@ -416,7 +448,18 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         for (int k = 0; k < 4; ++k) {
             const int j = 4 * lane + k - shift;
             const int32_t c = cb + (int32_t)((raw[k >> 1] >> (16 * (k & 1))) & 0xffffu);
-            xv[hb][k] = (double)x[(j >= 0 && j < nk) ? c : 0];
+            const int32_t cc = (j >= 0 && j < nk) ? c : 0;
+            if (FOLD) {
+                xv[hb][k] = (double)zz[cc];
+                pg[FOLD ? hb : 0][k] = (double)pold[cc];
+            } else {
+                xv[hb][k] = (double)x[cc];
+            }
+        }
+        if (FOLD) {
+            const int64_t i = s_rs[u] + (lane < s_nr[u] ? lane : 0);
+            oz[FOLD ? hb : 0] = zz[i];
+            op[FOLD ? hb : 0] = pold[i];
         }
     };
     // the tile of slot u (gathers in xv[hb]): products, row offsets and w to
@@ -427,13 +470,28 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         const int64_t ti = s_t[u];
         {
             const int g = 4 * lane;
+            if (FOLD) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    xv[hb][q] = (double)fold_p<T>(xv[hb][q], pg[FOLD ? hb : 0][q], beta);
+            }
             if (g < nk + shift) {
                 double2 *pd = reinterpret_cast<double2 *>(prod + g);
                 pd[0] = make_double2((double)s_v[u][0] * xv[hb][0], (double)s_v[u][1] * xv[hb][1]);
                 pd[1] = make_double2((double)s_v[u][2] * xv[hb][2], (double)s_v[u][3] * xv[hb][3]);
             }
             if (lane <= nrows) roff[lane] = s_ro[u];
-            if (FUSED && lane < nrows) pown[lane] = (double)s_w[u];
+            if (FOLD) {
+                if (lane < nrows) {
+                    const int hf = FOLD ? hb : 0;
+                    const T pn = fold_p<T>((double)oz[hf], (double)op[hf], beta);
+                    pnew[rs + lane] = pn;
+                    xx[rs + lane] = (T)((double)s_x[FOLD ? u : 0] + ax * (double)op[hf]);
+                    pown[lane] = (double)pn;
+                }
+            } else if (FUSED && lane < nrows) {
+                pown[lane] = (double)s_w[u];
+            }
         }
         fetch(u);
         gather((u + 2) % kRing, hb);
@@ -488,13 +546,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         }
         gather(0, 0);
         gather(1, 1);
+        // four steps per pass, with no exit between them (a single path
+        // through the loop body keeps the compiler's waits for the in-order
+        // counter tight); the slots hold consecutive tiles of the walk, so a
+        // pass that starts with a tile in slot 0 runs the at most three
+        // others still in range, and steps on slots past the end are empty
         while (s_t[0] < t_end) {
             step(0, 0);
-            if (s_t[1] >= t_end) break;
             step(1, 1);
-            if (s_t[2] >= t_end) break;
             step(2, 0);
-            if (s_t[3] >= t_end) break;
             step(3, 1);
         }
     }
@@ -507,7 +567,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         dot = block_sum(dot, lds4);
         if (DOT == 2) dot2 = block_sum(dot2, lds4);
         if (threadIdx.x == 0) {
-            spart[(int64_t)DOT * blockIdx.x] = dot;
+            spart[(int64_t)(FOLD ? 1 : DOT) * blockIdx.x] = dot;
             if (DOT == 2) spart[2 * (int64_t)blockIdx.x + 1] = dot2;
         }
     }
@@ -744,7 +804,8 @@ void launch_tiles(Handle &h, const void *x, void *y, const void *w, double *spar
                            (const TileDesc *)h.tiles, h.ntiles, (const uint16_t *)h.roff16,
                            (const uint16_t *)h.col16, (const T *)h.vals, (const T *)x, (T *)y,
                            (const T *)w, (const double *)h.long_dot, h.nlong, spart, status,
-                           (const uint8_t *)h.tile_live, h.tile_dot, h.band_l, h.band_p);
+                           (const uint8_t *)h.tile_live, h.tile_dot, h.band_l, h.band_p,
+                           FoldArgs{});
         return;
     }
     auto kern = h.all_narrow ? k_spmv_tile<T, RP, DOT, true> : k_spmv_tile<T, RP, DOT, false>;
@@ -861,6 +922,36 @@ void launch_spmv_csr_dot_raw(int64_t n, const int32_t *row_ptr, const int32_t *c
     const int64_t grid = (n + (int64_t)kBlock * rpl - 1) / ((int64_t)kBlock * rpl);
     hipLaunchKernelGGL((k_spmv_batched<double, int32_t, true>), dim3((unsigned)grid), dim3(kBlock),
                        0, s, n, 1, rpl, row_ptr, col, val, p, q, red, ctl, st, running);
+    SLA_HIP(hipGetLastError());
+}
+
+// The folded-direction SpMV of a per-step single-system solve (see
+// FoldArgs): p_new = z + beta p_old, x += alpha p_old on the own rows,
+// q = A p_new and the p_new.q partials. Needs use_ring(h) and no long rows.
+bool fold_possible(const Handle &h) {
+    return h.B == 1 && h.nseg == 0 && h.nlong == 0 && use_ring(h);
+}
+
+void launch_spmv_fold(Handle &h, hipStream_t s) {
+    const FoldArgs fa{h.fold_z, {h.p, h.fold_p2}, h.x, h.st};
+    const int64_t grid = spmv_grid(h);
+    auto go = [&](auto ttag, auto rtag) {
+        using T = decltype(ttag);
+        using RP = decltype(rtag);
+        hipLaunchKernelGGL((k_spmv_tile_ring<T, RP, 4>), dim3((unsigned)grid), dim3(kBlock),
+                           kRingLdsPad, s, (const TileDesc *)h.tiles, h.ntiles,
+                           (const uint16_t *)h.roff16, (const uint16_t *)h.col16,
+                           (const T *)h.vals, (const T *)nullptr, (T *)h.q, (const T *)nullptr,
+                           (const double *)h.long_dot, h.nlong, h.spart, &h.st[0].status,
+                           (const uint8_t *)nullptr, (double *)nullptr, h.band_l, h.band_p, fa);
+    };
+    if (h.vt == SLA_F64) {
+        if (h.rp64) go(double(), int64_t());
+        else go(double(), int32_t());
+    } else {
+        if (h.rp64) go(float(), int64_t());
+        else go(float(), int32_t());
+    }
     SLA_HIP(hipGetLastError());
 }
 

@@ -126,12 +126,21 @@ enum {
                                    start on kernels without such waits. 0 makes every wait
                                    that is not already satisfied give up at once, which
                                    exercises that path. */
-    SLA_OPT_SPMV_RING = 8       /* 1 (default): the per-step SpMV of a single system whose
+    SLA_OPT_SPMV_RING = 8,      /* 1 (default): the per-step SpMV of a single system whose
                                    row tiles are all small (at most 63 rows and 253 entries,
                                    columns within 65535 of the tile's smallest) keeps four
                                    tiles' entries and two tiles' gathers in flight per
                                    wavefront; 0: one tile ahead. Same tiles, same sums, bitwise
                                    equal results. */
+    SLA_OPT_FOLD_DIRECTION = 9  /* 1 (default): a per-step PCG solve of a single system on
+                                   such tiles (no row longer than 128 entries) that is too
+                                   large for the fused update (SLA_OPT_FUSED_UPDATE) forms
+                                   p = z + beta p inside the SpMV, where it reads p, and
+                                   applies x += alpha p there one iteration later; the
+                                   update then reads r, q, dinv and writes r and z. Two
+                                   kernels and about two vector passes fewer per
+                                   iteration; the same recurrence, rounded the same way up
+                                   to the order of two operations. 0: three kernels. */
 };
 
 /* How the last sla_pcg_solve / sla_adjoint_backward / BiCGStab call on a

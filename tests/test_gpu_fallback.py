@@ -86,6 +86,7 @@ def test_fused_update_wait_gives_up(dtype):
     R = reference(w, v, b, tol)
     A = coo_handle(w.n, w.rows, w.cols, v)
     A.set_option(_lib.SLA_OPT_RESIDENT, 0)
+    A.set_option(_lib.SLA_OPT_FOLD_DIRECTION, 0)   # unfused: update, then direction
 
     def solve_profiled():
         A.profile_reset()

@@ -86,6 +86,7 @@ def test_fused_update_direction_matches_two_kernels(name, size, dtype):
     xo, ito, _, _ = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, tol, w.maxit)
     A = coo_handle(w.n, w.rows, w.cols, v)
     A.set_option(_lib.SLA_OPT_RESIDENT, 0)
+    A.set_option(_lib.SLA_OPT_FOLD_DIRECTION, 0)   # unfused: update, then direction
     out = []
     for fused in (1, 0):
         A.set_option(_lib.SLA_OPT_FUSED_UPDATE, fused)
@@ -508,3 +509,80 @@ def test_batched_single_kernel_largest_register_shape(dtype):
         assert ainfo.status[s] == oca[s] == oracle.CONVERGED, s
         assert abs(ainfo.iterations[s] - ita[s]) <= 2, s
         assert rel(GB[s], lam[s]) <= gtol and rel(GV[s], gvo[s]) <= gtol, s
+
+
+@pytest.mark.parametrize("name,size", [("diffusion3d_128", 64), ("poisson2d_11548", 700)])
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_folded_direction_matches_oracle_and_three_kernels(name, size, dtype):
+    """SLA_OPT_FOLD_DIRECTION on the per-step path (single kernel and fused
+    update off, so that it applies at these sizes): p = z + beta p formed in
+    the SpMV and x += alpha p applied one iteration later, two kernels per
+    iteration. Against the oracle (converged solve, tol-0 step counts with an
+    odd check interval so that captured blocks start on either direction
+    buffer, eager launches, the iteration budget, b = 0, the adjoint) and
+    against the three-kernel form."""
+    w = make_workload(name, size=size)
+    n = w.n
+    rows = np.repeat(np.arange(n), np.diff(w.row_ptr)) if w.fmt == "csr" else w.rows
+    v, b = w.vals.astype(dtype), w.b.astype(dtype)
+    f64 = dtype == np.float64
+    tol = 1e-10 if f64 else 1e-5
+    xtol = 1e-8 if f64 else 1e-4
+    print(f"folded direction: {name} n={n} {np.dtype(dtype).name}", flush=True)
+    ref = oracle.coo_to_csr(n, rows, w.cols, v)
+    rp, cc, vv = ref["row_ptr"], ref["col"], ref["vals"]
+    xo, ito, _, oco = oracle.pcg(rp, cc, vv, b, tol, 20000)
+    A = coo_handle(n, rows, w.cols, v)
+    lay = A.layout()
+    assert lay["ring_tiles"] and lay["long_rows"] == 0, lay
+    A.set_option(_lib.SLA_OPT_RESIDENT, 0)
+    A.set_option(_lib.SLA_OPT_FUSED_UPDATE, 0)
+
+    def solve(bb, t, maxit, prof=False):
+        if prof:
+            A.profile_reset()
+            A.set_option(_lib.SLA_OPT_PROFILE, 1)
+        x, info = A.solve_raw(dev(bb), t, maxit)
+        p = A.profile() if prof else None
+        A.set_option(_lib.SLA_OPT_PROFILE, 0)
+        return host(x), info, p
+
+    out = {}
+    for fold in (1, 0):
+        A.set_option(_lib.SLA_OPT_FOLD_DIRECTION, fold)
+        x, info, p = solve(b, tol, 20000, prof=True)
+        # folded: no direction kernel; one update per SpMV either way
+        assert (p["direction"][0] == 0) == bool(fold), p
+        assert p["update"][0] == p["spmv_dot"][0] > 0, p
+        assert info.status[0] == oco == oracle.CONVERGED
+        assert abs(info.iterations[0] - ito) <= 2, (info.iterations[0], ito)
+        assert rel(x, xo) <= xtol, rel(x, xo)
+        if f64:
+            # the true residual of the returned x (the last step applied)
+            r_true = b - oracle.spmv(rp, cc, vv, x)
+            assert np.linalg.norm(r_true) <= 10 * tol * np.linalg.norm(b)
+        out[fold] = x
+    assert rel(out[1], out[0]) <= xtol
+    A.set_option(_lib.SLA_OPT_FOLD_DIRECTION, 1)
+    # fixed step counts (tol 0): both buffer parities, graphs and eager
+    stol = 1e-11 if f64 else 1e-4
+    for k, interval, graph in ((7, 3, 1), (8, 3, 1), (5, 16, 0), (1, 16, 1)):
+        A.set_option(_lib.SLA_OPT_CHECK_INTERVAL, interval)
+        A.set_option(_lib.SLA_OPT_USE_GRAPH, graph)
+        x, info, _ = solve(b, 0.0, k)
+        xk, itk, _, ock = oracle.pcg(rp, cc, vv, b, 0.0, k)
+        assert info.iterations[0] == itk == k and info.status[0] == ock == oracle.MAXIT
+        assert rel(x, xk) <= stol, (k, interval, graph, rel(x, xk))
+    A.set_option(_lib.SLA_OPT_CHECK_INTERVAL, 16)
+    A.set_option(_lib.SLA_OPT_USE_GRAPH, 1)
+    # b = 0: converged at once, x = 0
+    x, info, _ = solve(np.zeros_like(b), tol, 100)
+    assert info.status[0] == oracle.CONVERGED and info.iterations[0] == 0 and not x.any()
+    # the adjoint (the same folded solve on A^T = A)
+    g = np.random.default_rng(21).standard_normal(n).astype(dtype)
+    lam_o, gv_o, it_o, _, _ = oracle.adjoint(rp, cc, vv, xo, g, tol, 20000)
+    xg = A.solve_raw(dev(b), tol, 20000)[0]
+    gb, gv, ainfo = A.adjoint_raw(xg, dev(g), tol, 20000)
+    assert abs(ainfo.iterations[0] - it_o) <= 2
+    assert rel(host(gb), lam_o) <= 10 * xtol
+    assert rel(host(gv), gv_o) <= 10 * xtol
