@@ -546,16 +546,22 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         }
         gather(0, 0);
         gather(1, 1);
-        // four steps per pass, with no exit between them (a single path
-        // through the loop body keeps the compiler's waits for the in-order
-        // counter tight); the slots hold consecutive tiles of the walk, so a
-        // pass that starts with a tile in slot 0 runs the at most three
-        // others still in range, and steps on slots past the end are empty
-        while (s_t[0] < t_end) {
+        // The slots hold consecutive tiles of the walk. Four steps per pass
+        // while all four slots hold a tile, with no exit between them (a
+        // single path through the loop body keeps the compiler's waits for
+        // the in-order counter tight); then the at most three tiles left.
+        while (s_t[3] < t_end) {
             step(0, 0);
             step(1, 1);
             step(2, 0);
             step(3, 1);
+        }
+        if (s_t[0] < t_end) {
+            step(0, 0);
+            if (s_t[1] < t_end) {
+                step(1, 1);
+                if (s_t[2] < t_end) step(2, 0);
+            }
         }
     }
     if (FUSED && !PERTILE) {
