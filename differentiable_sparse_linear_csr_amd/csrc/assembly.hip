@@ -575,7 +575,7 @@ __global__ __launch_bounds__(kBlock) void k_gather_rp(const RP *__restrict__ row
 // 253 entries for the ring form of the SpMV), nearest 45. On the 133M-row
 // Poisson matrix: one-tile-ahead SpMV (768 wavefronts per XCD), 3 panels of
 // 256 columns and 45-row tiles took it from 2.28 to 2.14 ms (HBM fetches
-// 10.2 -> 8.4 GB), 30-row tiles were slower than the usual ones (2.69 ms),
+// 10.7 -> 8.4 GB), 30-row tiles were slower than the usual ones (2.69 ms),
 // 60-row ones 2.22 ms; ring SpMV (512 wavefronts), 2 panels of 256 columns
 // and 45-row tiles 2.05 ms against 2.40 with the usual tiles. Bands under
 // 4096 rows keep the usual tiles: their p lines are reused by neighbouring
