@@ -79,7 +79,7 @@ struct Ctl {
     uint32_t epoch;   // solve counter: with the iteration count it names a broadcast
     int32_t error;    // set by a kernel whose bounded wait timed out (sticky for the solve)
     uint32_t spin_limit;  // polls a bounded grid-wide wait makes before it gives up
-    int32_t pad;
+    int32_t fold_iter;    // folded batched solve: updates completed (picks the direction buffer)
 };
 
 // polls of a bounded grid-wide wait before it gives up (about a second)
@@ -195,6 +195,7 @@ struct Handle {
     uint32_t last_fallback = 0;
     int64_t upd_dir_resident = 0;  // resident workgroups of the fused update + direction
     int64_t upd_dir_bv_resident = 0;  // the same for batches
+    int64_t bvec_fold_resident = 0;   // resident workgroups of the folded batched SpMV
     double *bcast_bv = nullptr;    // [2][kMaxBatch] beta and running flag per system
     bool fuse_update = true;       // single system: update and direction in one kernel
     int32_t *h_running = nullptr; // pinned, mapped
@@ -687,6 +688,7 @@ __device__ __forceinline__ void finish_alpha(const double *tot, int B, Ctl *ctl,
         if (!(sigma > 0.0) || !isfinite(sigma)) {
             s.status = SLA_BREAKDOWN;
             s.iter += 1;
+            s.alpha = 0.0;   // no step (a folded solve applies alpha to x later)
         } else {
             s.alpha = s.rho / sigma;
             ++running;

@@ -79,7 +79,7 @@ __global__ void k_set_ctl(Ctl *ctl, double tol, int32_t maxit, uint32_t spin_lim
     c.epoch = 0;
     c.error = 0;
     c.spin_limit = spin_limit;
-    c.pad = 0;
+    c.fold_iter = 0;
     *ctl = c;
 }
 

@@ -208,7 +208,10 @@ __global__ __launch_bounds__(kBlock) void k_update(int64_t n, int B, T *__restri
 // the chunk stride of every lane is a multiple of kBlock, lane t always holds
 // systems (t % Q) * W + w. Systems that are not running keep their values
 // (the stored chunk carries the old bits for them).
-template <typename T>
+// FOLD (folded batched solve): x and p are not touched; z = dinv r is stored
+// in x's place (the z buffer), and the last block counts the update in
+// ctl->fold_iter.
+template <typename T, bool FOLD = false>
 __global__ __launch_bounds__(kBlock) void k_update_bv(int64_t nc, int B, T *__restrict__ x,
                                                       T *__restrict__ r, const T *__restrict__ p,
                                                       const T *__restrict__ q,
@@ -245,8 +248,9 @@ __global__ __launch_bounds__(kBlock) void k_update_bv(int64_t nc, int B, T *__re
             for (int u = 0; u < kVecGroups; ++u) {
                 const int64_t c = c0 + u * kBlock + t;
                 if (c < nc) {
+                    // FOLD: xv carries z (x's own bits for stopped systems)
                     vload(x + c * W, xv[u]);
-                    vload(p + c * W, pv[u]);
+                    if (!FOLD) vload(p + c * W, pv[u]);
                     vload(r + c * W, rv[u]);
                     vload(q + c * W, qv[u]);
                     vload(dinv + c * W, dv[u]);
@@ -259,9 +263,10 @@ __global__ __launch_bounds__(kBlock) void k_update_bv(int64_t nc, int B, T *__re
 #pragma unroll
                 for (int w = 0; w < W; ++w) {
                     if (!act[w]) continue;
-                    xv[u][w] = (T)((double)xv[u][w] + alpha[w] * (double)pv[u][w]);
+                    if (!FOLD) xv[u][w] = (T)((double)xv[u][w] + alpha[w] * (double)pv[u][w]);
                     rv[u][w] = (T)((double)rv[u][w] - alpha[w] * (double)qv[u][w]);
                     const double z = (double)dv[u][w] * (double)rv[u][w];
+                    if (FOLD) xv[u][w] = (T)z;
                     srz[w] += (double)rv[u][w] * z;
                     srr[w] += (double)rv[u][w] * (double)rv[u][w];
                 }
@@ -276,8 +281,10 @@ __global__ __launch_bounds__(kBlock) void k_update_bv(int64_t nc, int B, T *__re
     block_sum_systems<W>(srr, Q, tmp, blk);
     for (int s = t; s < B; s += kBlock)
         store_partial(red.part + (int64_t)blockIdx.x * 2 * B + B + s, blk[s]);
-    if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, 2 * B, tmp, tot))
+    if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, 2 * B, tmp, tot)) {
         finish_update(tot, B, ctl, st, h_running);
+        if (FOLD && t == 0) ctl->fold_iter += 1;
+    }
 }
 
 template <typename T>
@@ -869,6 +876,39 @@ __global__ __launch_bounds__(kBlock) void k_fold_finish(int64_t n, T *__restrict
     }
 }
 
+// The same for a folded batch ([n][B], 16-byte groups of W systems): each
+// system's last step x += alpha_b p, p = the newest direction buffer
+// (p[fold_iter & 1]; stopped systems carried their last direction into it).
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_fold_finish_bv(int64_t nc, int B, T *__restrict__ x,
+                                                           const T *__restrict__ p0,
+                                                           const T *__restrict__ p1,
+                                                           const Ctl *__restrict__ ctl,
+                                                           const SysState *__restrict__ st) {
+    constexpr int W = VecW<T>::W;
+    const int Q = B / W;
+    const int t = threadIdx.x;
+    const int s0 = (t & (Q - 1)) * W;
+    double alpha[W];
+    bool any = false;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        alpha[w] = st[s0 + w].alpha;
+        any |= alpha[w] != 0.0;
+    }
+    if (!any) return;
+    const T *p = (ctl->fold_iter & 1) ? p1 : p0;
+    for (int64_t c = (int64_t)blockIdx.x * kBlock + t; c < nc; c += (int64_t)gridDim.x * kBlock) {
+        T xv[W], pv[W];
+        vload(x + c * W, xv);
+        vload(p + c * W, pv);
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+            if (alpha[w] != 0.0) xv[w] = (T)((double)xv[w] + alpha[w] * (double)pv[w]);
+        vstore(x + c * W, xv);
+    }
+}
+
 // grid of the fused update + direction: one pass per workgroup, all of them
 // resident at once; 0 when the system does not fit (or B > 1)
 int64_t fused_grid(const Handle &h, int W) {
@@ -890,12 +930,16 @@ int64_t fused_bv_grid(const Handle &h, int W) {
     return g <= h.upd_dir_bv_resident ? g : 0;
 }
 
-// the per-step solve folds the direction into the SpMV: a single system on
-// ring-form tiles without long rows, where the fused update + direction
-// kernel does not apply (too large for one resident pass, or switched off)
+// the per-step solve folds the direction into the SpMV: fp64 storage (z is
+// stored, and in fp64 z = dinv r rounds once where the direction formed it
+// anyway; in fp32 storage it would add an fp32 rounding per step), a single
+// system on ring-form tiles without long rows or a batch of 16-byte lanes,
+// where the fused update + direction kernel does not apply (too large for
+// one resident pass, or switched off)
 bool want_fold(const Handle &h) {
-    if (!h.fold_direction || !fold_possible(h)) return false;
-    return fused_grid(h, h.vt == SLA_F64 ? VecW<double>::W : VecW<float>::W) == 0;
+    if (!h.fold_direction || h.vt != SLA_F64 || !fold_possible(h)) return false;
+    const int W = h.vt == SLA_F64 ? VecW<double>::W : VecW<float>::W;
+    return h.B > 1 ? fused_bv_grid(h, W) == 0 : fused_grid(h, W) == 0;
 }
 
 int64_t vec1_grid(int64_t n, int W) {
@@ -1015,6 +1059,16 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
         if (lp) lp->end(SLA_KERNEL_SPMV_DOT, a);
         if (lp) lp->begin(SLA_KERNEL_UPDATE, &a);
         const Red red{h.part, h.gpart, h.sync + kCntUpdate * kCountersPerKind};
+        if (h.B > 1) {
+            const int64_t nc = h.n * h.B / VecW<T>::W;
+            hipLaunchKernelGGL((k_update_bv<T, true>), dim3((unsigned)bv_grid(nc, h.bv_update_resident)),
+                               dim3(kBlock), 0, s, nc, h.B, (T *)h.fold_z, (T *)h.r,
+                               (const T *)nullptr, (const T *)h.q, (const T *)h.dinv, red, h.ctl,
+                               h.st, h.d_running);
+            SLA_HIP(hipGetLastError());
+            if (lp) lp->end(SLA_KERNEL_UPDATE, a);
+            return;
+        }
         const int64_t g1 = vec1_grid(h.n, VecW<T>::W);
         const bool nt = h.n * (int64_t)sizeof(T) >= kNtVectorBytes;
         hipLaunchKernelGGL((nt ? k_update1<T, true, true> : k_update1<T, false, true>),
@@ -1242,6 +1296,7 @@ bool pcg_attempt(Handle &h, const void *b_user, void *x_user, double tol, int32_
     h.h_ctl->epoch = ++h.epoch;
     h.h_ctl->error = 0;
     h.h_ctl->spin_limit = h.spin_limit;
+    h.h_ctl->fold_iter = 0;
     SLA_HIP(hipMemcpyAsync(h.ctl, h.h_ctl, sizeof(Ctl), hipMemcpyHostToDevice, s));
     // the whole solve in one cooperative kernel (same recurrence; a batch
     // leaves x as [B][n] in q), unless the cooperative launch is refused
@@ -1288,8 +1343,8 @@ bool pcg_attempt(Handle &h, const void *b_user, void *x_user, double tol, int32_
     }
     h.fold_active = want_fold(h);
     if (h.fold_active && !h.fold_z) {
-        h.fold_z = dalloc(h, (size_t)h.n * h.vbytes);
-        h.fold_p2 = dalloc(h, (size_t)h.n * h.vbytes);
+        h.fold_z = dalloc(h, (size_t)h.n * h.B * h.vbytes);
+        h.fold_p2 = dalloc(h, (size_t)h.n * h.B * h.vbytes);
     }
     if (h.nseg > 0) seg_init(h, b_int, s, lp);
     else if (h.vt == SLA_F64) init_t<double>(h, b_int, s, lp);
@@ -1312,7 +1367,21 @@ bool pcg_attempt(Handle &h, const void *b_user, void *x_user, double tol, int32_
             if (__atomic_load_n(h.h_running, __ATOMIC_ACQUIRE) == 0) break;
         }
     }
-    if (h.fold_active) {
+    if (h.fold_active && h.B > 1) {
+        const int W = h.vt == SLA_F64 ? VecW<double>::W : VecW<float>::W;
+        const int64_t nc = h.n * h.B / W;
+        int64_t gb = (nc + kBlock - 1) / kBlock;
+        if (gb > kMaxGrid) gb = kMaxGrid;
+        if (h.vt == SLA_F64)
+            hipLaunchKernelGGL(k_fold_finish_bv<double>, dim3((unsigned)gb), dim3(kBlock), 0, s, nc,
+                               h.B, (double *)h.x, (const double *)h.p, (const double *)h.fold_p2,
+                               (const Ctl *)h.ctl, (const SysState *)h.st);
+        else
+            hipLaunchKernelGGL(k_fold_finish_bv<float>, dim3((unsigned)gb), dim3(kBlock), 0, s, nc,
+                               h.B, (float *)h.x, (const float *)h.p, (const float *)h.fold_p2,
+                               (const Ctl *)h.ctl, (const SysState *)h.st);
+        SLA_HIP(hipGetLastError());
+    } else if (h.fold_active) {
         const int W = h.vt == SLA_F64 ? VecW<double>::W : VecW<float>::W;
         const unsigned gf = (unsigned)vec1_grid(h.n, W);
         if (h.vt == SLA_F64)

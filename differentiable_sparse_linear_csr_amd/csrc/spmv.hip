@@ -749,6 +749,125 @@ __global__ __launch_bounds__(kBlock) void k_spmv_bvec(
     }
 }
 
+// The folded-direction form of k_spmv_bvec for a per-step batched solve
+// (see FoldArgs): one row per lane and pass; the gathers read z and p_old,
+// p_new = z + beta_b p_old is formed per system (one fused multiply-add) at
+// every gathered column and at the lane's own row, x += alpha_b p_old is
+// applied to the own row, and q = A p_new with its p_new.q partials. The
+// direction buffers are picked by ctl->fold_iter (updates completed in this
+// solve, the same for all systems). A system that has stopped keeps x and
+// copies p_old into p_new, so that the newest buffer holds its last
+// direction for the final x update.
+template <typename T, typename RP>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_spmv_bvec_fold(
+    int64_t n, int B, int64_t rows_block, const RP *__restrict__ row_ptr,
+    const int32_t *__restrict__ col, const T *__restrict__ val, T *__restrict__ y, Red red,
+    Ctl *__restrict__ ctl, SysState *__restrict__ st, int32_t *__restrict__ h_running,
+    FoldArgs fa) {
+    constexpr int W = VecW<T>::W;
+    constexpr int E = kBvEntries;
+    __shared__ double tmp[4 * kMaxBatch];
+    __shared__ double tot[kMaxBatch];
+    __shared__ double blk[kMaxBatch];
+    // beta and alpha of every system in LDS (read where used: registers are
+    // what limits how many wavefronts a CU holds here)
+    __shared__ double s_beta[kMaxBatch], s_ax[kMaxBatch];
+    if (ctl->n_running == 0) return;
+    const int Q = B / W;
+    const int t = threadIdx.x;
+    const int s0 = (t & (Q - 1)) * W;
+    const int J = kBlock / Q;
+    const int jr = t / Q;
+    for (int b = t; b < B; b += kBlock) {
+        s_beta[b] = st[b].beta;
+        s_ax[b] = st[b].alpha;
+    }
+    uint32_t run = 0;   // bit w: system s0 + w still runs
+#pragma unroll
+    for (int w = 0; w < W; ++w) run |= (st[s0 + w].status == kRunning ? 1u : 0u) << w;
+    const bool any = run != 0;
+    __syncthreads();
+    const int par = ctl->fold_iter & 1;
+    const T *zz = (const T *)fa.z;
+    const T *pold = (const T *)fa.p[par];
+    T *pnew = (T *)fa.p[par ^ 1];
+    T *xx = (T *)fa.x;
+    auto runs = [&](int w) { return ((run >> w) & 1u) != 0; };
+    auto pn = [&](int w, T z, T p) {
+        return runs(w) ? fold_p<T>((double)z, (double)p, s_beta[s0 + w]) : p;
+    };
+    const int64_t G = gridDim.x;  // a multiple of kXcds
+    const int64_t lb = (int64_t)(blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
+    const int64_t r_begin = lb * rows_block;
+    const int64_t r_end = r_begin + rows_block < n ? r_begin + rows_block : n;
+    double dot[W];
+#pragma unroll
+    for (int k = 0; k < W; ++k) dot[k] = 0.0;
+    if (any) {
+        for (int64_t ri = r_begin + jr; ri < r_end; ri += J) {
+            const int64_t ka = (int64_t)row_ptr[ri], kb = (int64_t)row_ptr[ri + 1];
+            int32_t c[E];
+            T v[E][W], gz[E][W], gp[E][W], oz[W], op[W], ox[W];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int64_t k = ka + e;
+                c[e] = k < kb ? col[k] : 0;
+                vload(val + (k < kb ? k : 0) * B + s0, v[e]);
+            }
+            vload(zz + ri * B + s0, oz);
+            vload(pold + ri * B + s0, op);
+            vload(xx + ri * B + s0, ox);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                vload(zz + (int64_t)c[e] * B + s0, gz[e]);
+                vload(pold + (int64_t)c[e] * B + s0, gp[e]);
+            }
+            double sum[W];
+#pragma unroll
+            for (int w = 0; w < W; ++w) sum[w] = 0.0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const bool in = ka + e < kb;
+#pragma unroll
+                for (int w = 0; w < W; ++w)
+                    if (in) sum[w] += (double)v[e][w] * (double)pn(w, gz[e][w], gp[e][w]);
+            }
+            for (int64_t k = ka + E; k < kb; ++k) {
+                T a[W], bz[W], bp[W];
+                const int64_t ck = col[k];
+                vload(val + k * B + s0, a);
+                vload(zz + ck * B + s0, bz);
+                vload(pold + ck * B + s0, bp);
+#pragma unroll
+                for (int w = 0; w < W; ++w) sum[w] += (double)a[w] * (double)pn(w, bz[w], bp[w]);
+            }
+            T qv[W], pw[W], xw[W];
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                qv[w] = (T)sum[w];
+                pw[w] = pn(w, oz[w], op[w]);
+                xw[w] = runs(w) ? (T)((double)ox[w] + s_ax[s0 + w] * (double)op[w]) : ox[w];
+                dot[w] += (double)pw[w] * (double)qv[w];
+            }
+            vstore(y + ri * B + s0, qv);
+            vstore(pnew + ri * B + s0, pw);
+            vstore(xx + ri * B + s0, xw);
+        }
+    } else {
+        // every system of this lane has stopped: carry its directions over
+        for (int64_t ri = r_begin + jr; ri < r_end; ri += J) {
+            T op[W];
+            vload(pold + ri * B + s0, op);
+            vstore(pnew + ri * B + s0, op);
+        }
+    }
+    block_sum_systems<W>(dot, Q, tmp, blk);
+    for (int s = t; s < B; s += kBlock)
+        store_partial(red.part + (int64_t)blockIdx.x * B + s, blk[s]);
+    if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, B, tmp, tot))
+        finish_alpha(tot, B, ctl, st, h_running);
+}
+
 template <typename T>
 bool bvec_ok(const Handle &h) {
     constexpr int W = VecW<T>::W;
@@ -905,6 +1024,7 @@ void init_launch_limits(Handle &h) {
             using RP = decltype(rtag);
             h.bvec_resident[0] = resident_workgroups((const void *)&k_spmv_bvec<T, RP, false>, h.device);
             h.bvec_resident[1] = resident_workgroups((const void *)&k_spmv_bvec<T, RP, true>, h.device);
+            h.bvec_fold_resident = resident_workgroups((const void *)&k_spmv_bvec_fold<T, RP>, h.device);
         };
         if (h.vt == SLA_F64) {
             if (h.rp64) pick(double(), int64_t());
@@ -935,11 +1055,40 @@ void launch_spmv_csr_dot_raw(int64_t n, const int32_t *row_ptr, const int32_t *c
 // FoldArgs): p_new = z + beta p_old, x += alpha p_old on the own rows,
 // q = A p_new and the p_new.q partials. Needs use_ring(h) and no long rows.
 bool fold_possible(const Handle &h) {
-    return h.B == 1 && h.nseg == 0 && h.nlong == 0 && use_ring(h);
+    if (h.nseg > 0) return false;
+    if (h.B > 1) return h.vt == SLA_F64 ? bvec_ok<double>(h) : bvec_ok<float>(h);
+    return h.nlong == 0 && use_ring(h);
 }
 
 void launch_spmv_fold(Handle &h, hipStream_t s) {
     const FoldArgs fa{h.fold_z, {h.p, h.fold_p2}, h.x, h.st};
+    if (h.B > 1) {
+        // one row per lane and pass; the grid fills the resident workgroups
+        const int W = h.vt == SLA_F64 ? VecW<double>::W : VecW<float>::W;
+        const int64_t J = kBlock / (h.B / W);
+        const int64_t slots = (h.n + J - 1) / J;
+        const int64_t R = h.bvec_fold_resident > 0 ? h.bvec_fold_resident : kXcds;
+        const int64_t rows_block = J * ((slots + R - 1) / R);
+        int64_t grid = (h.n + rows_block - 1) / rows_block;
+        grid = (grid + kXcds - 1) / kXcds * kXcds;
+        const Red red{h.part, h.gpart, h.sync + kCntSpmv * kCountersPerKind};
+        auto go = [&](auto ttag, auto rtag) {
+            using T = decltype(ttag);
+            using RP = decltype(rtag);
+            hipLaunchKernelGGL((k_spmv_bvec_fold<T, RP>), dim3((unsigned)grid), dim3(kBlock), 0, s,
+                               h.n, h.B, rows_block, (const RP *)h.row_ptr, (const int32_t *)h.col,
+                               (const T *)h.vals, (T *)h.q, red, h.ctl, h.st, h.d_running, fa);
+        };
+        if (h.vt == SLA_F64) {
+            if (h.rp64) go(double(), int64_t());
+            else go(double(), int32_t());
+        } else {
+            if (h.rp64) go(float(), int64_t());
+            else go(float(), int32_t());
+        }
+        SLA_HIP(hipGetLastError());
+        return;
+    }
     const int64_t grid = spmv_grid(h);
     auto go = [&](auto ttag, auto rtag) {
         using T = decltype(ttag);

@@ -132,15 +132,17 @@ enum {
                                    tiles' entries and two tiles' gathers in flight per
                                    wavefront; 0: one tile ahead. Same tiles, same sums, bitwise
                                    equal results. */
-    SLA_OPT_FOLD_DIRECTION = 9  /* 1 (default): a per-step PCG solve of a single system on
-                                   such tiles (no row longer than 128 entries) that is too
-                                   large for the fused update (SLA_OPT_FUSED_UPDATE) forms
-                                   p = z + beta p inside the SpMV, where it reads p, and
-                                   applies x += alpha p there one iteration later; the
-                                   update then reads r, q, dinv and writes r and z. Two
-                                   kernels and about two vector passes fewer per
-                                   iteration; the same recurrence, rounded the same way up
-                                   to the order of two operations. 0: three kernels. */
+    SLA_OPT_FOLD_DIRECTION = 9  /* 1 (default): a per-step PCG solve with fp64 values, of a
+                                   single system on such tiles (no row longer than 128
+                                   entries) or of a batch whose B / (16 / value bytes) is a
+                                   power of two, that is too large for the fused update
+                                   (SLA_OPT_FUSED_UPDATE), forms p = z + beta p inside the
+                                   SpMV, where it reads p, and applies x += alpha p there one
+                                   iteration later; the update then reads r, q, dinv and
+                                   writes r and z = dinv r. Two kernels and two vector
+                                   passes fewer per iteration; the same recurrence, z
+                                   rounded once more in fp64. 0: three kernels. fp32
+                                   values never fold (z would add an fp32 rounding). */
 };
 
 /* How the last sla_pcg_solve / sla_adjoint_backward / BiCGStab call on a

@@ -117,6 +117,7 @@ def test_batched_fused_update_direction(B, dtype):
     xo, ito, _, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, tol, 5000)
     A = coo_handle(w.n, w.rows, w.cols, v)
     A.set_option(_lib.SLA_OPT_RESIDENT, 0)   # the per-step kernels
+    A.set_option(_lib.SLA_OPT_FOLD_DIRECTION, 0)   # unfused: update, then direction
     out = []
     for fused in (1, 0, 1):
         A.set_option(_lib.SLA_OPT_FUSED_UPDATE, fused)
@@ -517,7 +518,7 @@ def test_folded_direction_matches_oracle_and_three_kernels(name, size, dtype):
     """SLA_OPT_FOLD_DIRECTION on the per-step path (single kernel and fused
     update off, so that it applies at these sizes): p = z + beta p formed in
     the SpMV and x += alpha p applied one iteration later, two kernels per
-    iteration. Against the oracle (converged solve, tol-0 step counts with an
+    iteration; fp64 values only (fp32 ones keep three kernels). Against the oracle (converged solve, tol-0 step counts with an
     odd check interval so that captured blocks start on either direction
     buffer, eager launches, the iteration budget, b = 0, the adjoint) and
     against the three-kernel form."""
@@ -551,8 +552,9 @@ def test_folded_direction_matches_oracle_and_three_kernels(name, size, dtype):
     for fold in (1, 0):
         A.set_option(_lib.SLA_OPT_FOLD_DIRECTION, fold)
         x, info, p = solve(b, tol, 20000, prof=True)
-        # folded: no direction kernel; one update per SpMV either way
-        assert (p["direction"][0] == 0) == bool(fold), p
+        # folded (fp64 values only): no direction kernel; one update per
+        # SpMV either way
+        assert (p["direction"][0] == 0) == (bool(fold) and f64), p
         assert p["update"][0] == p["spmv_dot"][0] > 0, p
         assert info.status[0] == oco == oracle.CONVERGED
         assert abs(info.iterations[0] - ito) <= 2, (info.iterations[0], ito)
@@ -586,3 +588,97 @@ def test_folded_direction_matches_oracle_and_three_kernels(name, size, dtype):
     assert abs(ainfo.iterations[0] - it_o) <= 2
     assert rel(host(gb), lam_o) <= 10 * xtol
     assert rel(host(gv), gv_o) <= 10 * xtol
+
+
+@pytest.mark.parametrize("dtype,B", [(np.float32, 8), (np.float64, 8), (np.float32, 32),
+                                     (np.float64, 4)])
+def test_batched_folded_direction_mixed_outcomes(dtype, B):
+    """The folded direction on a batch (per-step path, fused update off so
+    that it applies): systems that converge at once, break down at the first
+    step and stop at different iterations, in the same 16-byte lanes. A
+    stopped system keeps x and carries its direction into the newer buffer,
+    and its last step is applied once at the end. Against the oracle, with
+    graphs at poll interval 3 (captured blocks start on either buffer) and
+    eager launches."""
+    N = 24
+    r, c, V, b = shifted_batch(N, B, dtype, broken=3 if B > 3 else None)
+    b[2] = 0.0
+    if B > 3:
+        b[3] = 1.0   # z = D^-1 1 makes p.Ap < 0 at the first step
+    A = coo_handle(N * N, r, c, V)
+    A.set_option(_lib.SLA_OPT_RESIDENT, 0)
+    A.set_option(_lib.SLA_OPT_FUSED_UPDATE, 0)
+    ref = oracle.coo_to_csr(N * N, r, c, V)
+    tol = 1e-6 if dtype == np.float32 else 1e-10
+    xtol = 1e-4 if dtype == np.float32 else 1e-8
+    xo, ito, rlo, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, tol, 300)
+    print(f"batched folded direction: B={B} {np.dtype(dtype).name}", flush=True)
+    for interval, graph in ((3, 1), (16, 0)):
+        A.set_option(_lib.SLA_OPT_CHECK_INTERVAL, interval)
+        A.set_option(_lib.SLA_OPT_USE_GRAPH, graph)
+        A.profile_reset()
+        A.set_option(_lib.SLA_OPT_PROFILE, 1)
+        x, info = A.solve_raw(dev(b), tol, 300)
+        prof = A.profile()
+        A.set_option(_lib.SLA_OPT_PROFILE, 0)
+        # fp64 folds; fp32 keeps the direction kernel (z would add a rounding)
+        assert (prof["direction"][0] == 0) == (dtype == np.float64), prof
+        assert prof["update"][0] > 0, prof
+        X = host(x)
+        assert info.status[2] == _lib.SLA_CONVERGED and info.iterations[2] == 0
+        assert not X[2].any()
+        if B > 3:
+            assert info.status[3] == _lib.SLA_BREAKDOWN and info.iterations[3] == 1
+            assert not X[3].any()
+        for s in range(B):
+            assert info.status[s] == oco[s], s
+            assert abs(info.iterations[s] - ito[s]) <= 2, (s, info.iterations[s], ito[s])
+            assert rel(X[s], xo[s]) <= xtol, (s, rel(X[s], xo[s]))
+    A.set_option(_lib.SLA_OPT_CHECK_INTERVAL, 16)
+    A.set_option(_lib.SLA_OPT_USE_GRAPH, 1)
+    # fixed step counts, odd and even, against the oracle's
+    for k in (5, 6):
+        x, info = A.solve_raw(dev(b), 0.0, k)
+        xk, itk, _, ock = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, 0.0, k)
+        X = host(x)
+        for s in range(B):
+            assert info.iterations[s] == itk[s] and info.status[s] == ock[s], s
+            assert rel(X[s], xk[s]) <= (1e-11 if dtype == np.float64 else 1e-4), (k, s)
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_batched_folded_direction_matches_three_kernels(dtype):
+    """The 512x512 x 32 workload's family at 40x40 x 8: folded and three-kernel
+    forms against the oracle, and the adjoint on the folded form."""
+    B = 8
+    w = make_workload("batched_diffusion2d_512x32", size=40, batch=B)
+    v, b = w.vals.astype(dtype), w.b.astype(dtype)
+    tol = 1e-10 if dtype == np.float64 else 1e-5
+    xtol = 1e-8 if dtype == np.float64 else 1e-4
+    ref = oracle.coo_to_csr(w.n, w.rows, w.cols, v)
+    xo, ito, _, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, tol, 5000)
+    A = coo_handle(w.n, w.rows, w.cols, v)
+    A.set_option(_lib.SLA_OPT_RESIDENT, 0)
+    A.set_option(_lib.SLA_OPT_FUSED_UPDATE, 0)
+    out = {}
+    for fold in (1, 0):
+        A.set_option(_lib.SLA_OPT_FOLD_DIRECTION, fold)
+        x, info = A.solve_raw(dev(b), tol, 5000)
+        X = host(x)
+        for s in range(B):
+            assert info.status[s] == oco[s] and abs(info.iterations[s] - ito[s]) <= 2, s
+            assert rel(X[s], xo[s]) <= xtol, (fold, s, rel(X[s], xo[s]))
+        out[fold] = X
+    for s in range(B):
+        assert rel(out[1][s], out[0][s]) <= xtol
+    A.set_option(_lib.SLA_OPT_FOLD_DIRECTION, 1)
+    g = w.g.astype(dtype)
+    lam_o, gv_o, it_o, _, _ = oracle.adjoint(ref["row_ptr"], ref["col"], ref["vals"], xo, g, tol,
+                                            5000)
+    x, _ = A.solve_raw(dev(b), tol, 5000)
+    gb, gv, ainfo = A.adjoint_raw(x, dev(g), tol, 5000)
+    GB, GV = host(gb), host(gv)
+    gtol = 1e-8 if dtype == np.float64 else 1e-3
+    for s in range(B):
+        assert abs(ainfo.iterations[s] - it_o[s]) <= 2
+        assert rel(GB[s], lam_o[s]) <= gtol and rel(GV[s], gv_o[s]) <= gtol, s
