@@ -97,6 +97,7 @@ void alloc_workspace(Handle &h, hipStream_t s) {
     h.part = (double *)dalloc(h, (size_t)plen * sizeof(double));
     h.gpart = (double *)dalloc(h, (size_t)kGroups * 2 * kMaxBatch * sizeof(double));
     h.spart = (double *)dalloc(h, (size_t)kMaxGrid * sizeof(double));
+    h.gpart_spmv = (double *)dalloc(h, (size_t)kGroups * kMaxBatch * sizeof(double));
     h.sync = (uint32_t *)dalloc(h, (size_t)kCntKinds * kCountersPerKind * sizeof(uint32_t));
     SLA_HIP(hipMemsetAsync(h.sync, 0, (size_t)kCntKinds * kCountersPerKind * sizeof(uint32_t), s));
     h.st = (SysState *)dalloc(h, sizeof(SysState) * num_systems(h));

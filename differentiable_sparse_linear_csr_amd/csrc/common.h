@@ -183,7 +183,8 @@ struct Handle {
     void *x = nullptr, *r = nullptr, *p = nullptr, *q = nullptr; // [n][B]
     double *part = nullptr;
     int64_t part_len = 0;
-    double *gpart = nullptr;      // [kGroups][C] group sums of the grid reductions
+    double *gpart = nullptr;       // [kGroups][C] group sums of the grid reductions
+    double *gpart_spmv = nullptr;  // [kGroups][B] group sums a batched SpMV leaves for the update
     double *spart = nullptr;      // [spmv grid] p.q partials of the single-system SpMV
     uint32_t *sync = nullptr;     // [kCntKinds][kCountersPerKind] arrival counters
     SysState *st = nullptr;
@@ -530,6 +531,30 @@ __device__ __forceinline__ bool last_block_sums(double *part, double *gpart, uin
     return true;
 }
 
+// The group level of last_block_sums alone: the last block of each group
+// sums the group's rows (block order) into gpart[g][C]. The next kernel
+// finishes the sum with group_total(), in every block, with the tree
+// last_block_sums uses, so that the grid-wide serial tail (a second arrival
+// and the final sum) leaves the producing kernel.
+__device__ __forceinline__ void last_group_sums(double *part, double *gpart, uint32_t *counters,
+                                                int64_t nblk, int C, double *tmp, double *tot) {
+    const int64_t gb = (nblk + kGroups - 1) / kGroups;
+    const int64_t g = blockIdx.x / gb;
+    const int64_t j0 = g * gb;
+    const int64_t j1 = (j0 + gb < nblk) ? j0 + gb : nblk;
+    if (!arrive(counters + g * kCounterStride, (uint32_t)(j1 - j0))) return;
+    sum_rows(part, j0, j1, C, tmp, tot);
+    for (int c = threadIdx.x; c < C; c += kBlock) store_partial(gpart + g * C + c, tot[c]);
+}
+// tot[0..C) = the sum of the group rows that last_group_sums left for a
+// launch of nblk blocks (group order)
+__device__ __forceinline__ void group_total(const double *gpart, int64_t nblk, int C, double *tmp,
+                                            double *tot) {
+    const int64_t gb = (nblk + kGroups - 1) / kGroups;
+    const int64_t ngroups = (nblk + gb - 1) / gb;
+    sum_rows(gpart, 0, ngroups, C, tmp, tot);
+}
+
 // Last-block epilogue of a fused SpMV: sigma = p.q per system in tot[0..B);
 // alpha = rho / sigma, or a breakdown when sigma is not > 0 or not finite.
 __device__ __forceinline__ void finish_alpha(const double *tot, int B, Ctl *ctl, SysState *st,
@@ -647,6 +672,8 @@ void launch_direction_raw(int64_t n, const double *r, double *p, const double *d
                           const Ctl *ctl, const SysState *st, hipStream_t s);
 int64_t raw_vec_grid(int64_t n);
 bool fold_possible(const Handle &h);
+int64_t bvec_fold_grid(const Handle &h, int64_t *rows_block_out);
+int64_t bvec_spmv_blocks(const Handle &h);
 void launch_spmv_fold(Handle &h, hipStream_t s);
 void launch_spmv_csr_dot_raw(int64_t n, const int32_t *row_ptr, const int32_t *col,
                              const double *val, const double *p, double *q, Red red, Ctl *ctl,

@@ -135,6 +135,42 @@ __device__ __forceinline__ void finish_update(const double *tot, int B, Ctl *ctl
     if (threadIdx.x == 0) publish_running(ctl, h_running, running);
 }
 
+// The same for the batched kernels whose SpMV left only group sums of p.q
+// (sigma[b], summed by every block of the update): the breakdown test on
+// sigma, alpha kept in the state (the folded solve applies it to x later),
+// then the stopping test, budget and beta of every system that stepped.
+__device__ __forceinline__ void finish_update_sigma(const double *tot, const double *sigma, int B,
+                                                    Ctl *ctl, SysState *st, int32_t *h_running) {
+    const double tol = ctl->tol;
+    const int32_t maxit = ctl->maxit;
+    int running = 0;
+    for (int b = threadIdx.x; b < B; b += kBlock) {
+        SysState &s = st[b];
+        if (s.status != kRunning) continue;
+        s.iter += 1;
+        const double sg = sigma[b];
+        if (!(sg > 0.0) || !isfinite(sg)) {
+            s.status = SLA_BREAKDOWN;   // x, r untouched; rr keeps the last residual
+            s.alpha = 0.0;
+            continue;
+        }
+        s.alpha = s.rho / sg;
+        const double rz = tot[b], rr = tot[B + b];
+        s.rr = rr;
+        if (sqrt(rr) <= tol * sqrt(s.bb)) {
+            s.status = SLA_CONVERGED;
+        } else if (s.iter >= maxit) {
+            s.status = SLA_MAXIT;
+        } else {
+            s.beta = rz / s.rho;
+            s.rho = rz;
+            ++running;
+        }
+    }
+    running = block_count(running);
+    if (threadIdx.x == 0) publish_running(ctl, h_running, running);
+}
+
 // x += alpha p, r -= alpha q; partials of r.z and r.r with z = dinv r; the
 // last block applies the stopping test, the iteration budget and beta.
 template <typename T>
@@ -211,11 +247,17 @@ __global__ __launch_bounds__(kBlock) void k_update(int64_t n, int B, T *__restri
 // FOLD (folded batched solve): x and p are not touched; z = dinv r is stored
 // in x's place (the z buffer), and the last block counts the update in
 // ctl->fold_iter.
+//
+// The SpMV before it left group sums of p.q (sg, for an SpMV of sg_blocks
+// blocks): every block finishes that sum (group order) and forms alpha per
+// system; a system whose p.q is not > 0 or not finite breaks down here.
 template <typename T, bool FOLD = false>
 __global__ __launch_bounds__(kBlock) void k_update_bv(int64_t nc, int B, T *__restrict__ x,
                                                       T *__restrict__ r, const T *__restrict__ p,
                                                       const T *__restrict__ q,
-                                                      const T *__restrict__ dinv, Red red,
+                                                      const T *__restrict__ dinv,
+                                                      const double *__restrict__ sg,
+                                                      int64_t sg_blocks, Red red,
                                                       Ctl *__restrict__ ctl,
                                                       SysState *__restrict__ st,
                                                       int32_t *__restrict__ h_running) {
@@ -223,56 +265,73 @@ __global__ __launch_bounds__(kBlock) void k_update_bv(int64_t nc, int B, T *__re
     __shared__ double tmp[4 * kMaxBatch];
     __shared__ double blk[kMaxBatch];
     __shared__ double tot[2 * kMaxBatch];
+    __shared__ double sigma[kMaxBatch];
     if (ctl->n_running == 0) return;
     const int Q = B / W;
     const int t = threadIdx.x;
     const int s0 = (t & (Q - 1)) * W;
+    // the first pass's rows are requested before the sum of the SpMV's group
+    // rows, so that their latency overlaps it
+    bool any_run = false;
+#pragma unroll
+    for (int w = 0; w < W; ++w) any_run |= st[s0 + w].status == kRunning;
+    const int64_t per_pass = (int64_t)kBlock * kVecGroups;
+    T xv[kVecGroups][W], pv[kVecGroups][W], rv[kVecGroups][W], qv[kVecGroups][W],
+        dv[kVecGroups][W];
+    auto load_pass = [&](int64_t c0) {
+#pragma unroll
+        for (int u = 0; u < kVecGroups; ++u) {
+            const int64_t c = c0 + u * kBlock + t;
+            if (c < nc) {
+                // FOLD: xv carries z (x's own bits for stopped systems)
+                vload(x + c * W, xv[u]);
+                if (!FOLD) vload(p + c * W, pv[u]);
+                vload(r + c * W, rv[u]);
+                vload(q + c * W, qv[u]);
+                vload(dinv + c * W, dv[u]);
+            }
+        }
+    };
+    int64_t c0 = (int64_t)blockIdx.x * per_pass;
+    if (any_run && c0 < nc) load_pass(c0);
+    group_total(sg, sg_blocks, B, tmp, sigma);
     bool act[W];
     double alpha[W];
     bool any = false;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
-        act[w] = st[s0 + w].status == kRunning;
-        alpha[w] = act[w] ? st[s0 + w].alpha : 0.0;
+        const double sw = sigma[s0 + w];
+        act[w] = st[s0 + w].status == kRunning && sw > 0.0 && isfinite(sw);
+        alpha[w] = act[w] ? st[s0 + w].rho / sw : 0.0;
         any |= act[w];
     }
     double srz[W], srr[W];
 #pragma unroll
     for (int w = 0; w < W; ++w) srz[w] = srr[w] = 0.0;
+    auto process_pass = [&](int64_t c0) {
+#pragma unroll
+        for (int u = 0; u < kVecGroups; ++u) {
+            const int64_t c = c0 + u * kBlock + t;
+            if (c >= nc) continue;
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                if (!act[w]) continue;
+                if (!FOLD) xv[u][w] = (T)((double)xv[u][w] + alpha[w] * (double)pv[u][w]);
+                rv[u][w] = (T)((double)rv[u][w] - alpha[w] * (double)qv[u][w]);
+                const double z = (double)dv[u][w] * (double)rv[u][w];
+                if (FOLD) xv[u][w] = (T)z;
+                srz[w] += (double)rv[u][w] * z;
+                srr[w] += (double)rv[u][w] * (double)rv[u][w];
+            }
+            vstore(x + c * W, xv[u]);
+            vstore(r + c * W, rv[u]);
+        }
+    };
     if (any) {
-        const int64_t per_pass = (int64_t)kBlock * kVecGroups;
-        for (int64_t c0 = (int64_t)blockIdx.x * per_pass; c0 < nc; c0 += (int64_t)gridDim.x * per_pass) {
-            T xv[kVecGroups][W], pv[kVecGroups][W], rv[kVecGroups][W], qv[kVecGroups][W],
-                dv[kVecGroups][W];
-#pragma unroll
-            for (int u = 0; u < kVecGroups; ++u) {
-                const int64_t c = c0 + u * kBlock + t;
-                if (c < nc) {
-                    // FOLD: xv carries z (x's own bits for stopped systems)
-                    vload(x + c * W, xv[u]);
-                    if (!FOLD) vload(p + c * W, pv[u]);
-                    vload(r + c * W, rv[u]);
-                    vload(q + c * W, qv[u]);
-                    vload(dinv + c * W, dv[u]);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < kVecGroups; ++u) {
-                const int64_t c = c0 + u * kBlock + t;
-                if (c >= nc) continue;
-#pragma unroll
-                for (int w = 0; w < W; ++w) {
-                    if (!act[w]) continue;
-                    if (!FOLD) xv[u][w] = (T)((double)xv[u][w] + alpha[w] * (double)pv[u][w]);
-                    rv[u][w] = (T)((double)rv[u][w] - alpha[w] * (double)qv[u][w]);
-                    const double z = (double)dv[u][w] * (double)rv[u][w];
-                    if (FOLD) xv[u][w] = (T)z;
-                    srz[w] += (double)rv[u][w] * z;
-                    srr[w] += (double)rv[u][w] * (double)rv[u][w];
-                }
-                vstore(x + c * W, xv[u]);
-                vstore(r + c * W, rv[u]);
-            }
+        if (c0 < nc) process_pass(c0);
+        for (c0 += (int64_t)gridDim.x * per_pass; c0 < nc; c0 += (int64_t)gridDim.x * per_pass) {
+            load_pass(c0);
+            process_pass(c0);
         }
     }
     block_sum_systems<W>(srz, Q, tmp, blk);
@@ -282,7 +341,7 @@ __global__ __launch_bounds__(kBlock) void k_update_bv(int64_t nc, int B, T *__re
     for (int s = t; s < B; s += kBlock)
         store_partial(red.part + (int64_t)blockIdx.x * 2 * B + B + s, blk[s]);
     if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, 2 * B, tmp, tot)) {
-        finish_update(tot, B, ctl, st, h_running);
+        finish_update_sigma(tot, sigma, B, ctl, st, h_running);
         if (FOLD && t == 0) ctl->fold_iter += 1;
     }
 }
@@ -361,7 +420,9 @@ template <typename T>
 __global__ __launch_bounds__(kBlock) void k_update_dir_bv(int64_t nc, int B, T *__restrict__ x,
                                                           T *__restrict__ r, T *__restrict__ p,
                                                           const T *__restrict__ q,
-                                                          const T *__restrict__ dinv, Red red,
+                                                          const T *__restrict__ dinv,
+                                                          const double *__restrict__ sg,
+                                                          int64_t sg_blocks, Red red,
                                                           Ctl *__restrict__ ctl,
                                                           SysState *__restrict__ st,
                                                           int32_t *__restrict__ h_running,
@@ -372,6 +433,7 @@ __global__ __launch_bounds__(kBlock) void k_update_dir_bv(int64_t nc, int B, T *
     __shared__ double tmp[4 * kMaxBatch];
     __shared__ double blk[kMaxBatch];
     __shared__ double tot[2 * kMaxBatch];
+    __shared__ double sigma[kMaxBatch];
     __shared__ int s_ok;
     if (fused_step_idle(ctl, h_running)) return;
     const uint64_t gen =
@@ -379,16 +441,8 @@ __global__ __launch_bounds__(kBlock) void k_update_dir_bv(int64_t nc, int B, T *
     const int Q = B / W;
     const int t = threadIdx.x;
     const int s0 = (t & (Q - 1)) * W;
-    bool act[W];
-    double alpha[W];
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-        act[w] = st[s0 + w].status == kRunning;
-        alpha[w] = act[w] ? st[s0 + w].alpha : 0.0;
-    }
-    double srz[W], srr[W];
-#pragma unroll
-    for (int w = 0; w < W; ++w) srz[w] = srr[w] = 0.0;
+    // this workgroup's rows first, so that their latency overlaps the sum of
+    // the SpMV's group rows (sigma = p.q per system, group order)
     const int64_t c0 = (int64_t)blockIdx.x * kBlock * U;
     T xv[U][W], pv[U][W], rv[U][W], qv[U][W], dv[U][W];
 #pragma unroll
@@ -402,6 +456,18 @@ __global__ __launch_bounds__(kBlock) void k_update_dir_bv(int64_t nc, int B, T *
             vload(dinv + c * W, dv[u]);
         }
     }
+    group_total(sg, sg_blocks, B, tmp, sigma);
+    bool act[W];
+    double alpha[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        const double sw = sigma[s0 + w];
+        act[w] = st[s0 + w].status == kRunning && sw > 0.0 && isfinite(sw);
+        alpha[w] = act[w] ? st[s0 + w].rho / sw : 0.0;
+    }
+    double srz[W], srr[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) srz[w] = srr[w] = 0.0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t c = c0 + u * kBlock + t;
@@ -432,8 +498,14 @@ __global__ __launch_bounds__(kBlock) void k_update_dir_bv(int64_t nc, int B, T *
         for (int b = t; b < B; b += kBlock) {
             SysState &sy = st[b];
             int run = 0;
-            if (sy.status == kRunning) {
+            const double sgb = sigma[b];
+            if (sy.status == kRunning && !(sgb > 0.0 && isfinite(sgb))) {
+                sy.iter += 1;
+                sy.status = SLA_BREAKDOWN;   // x, r untouched; rr keeps the last residual
+                sy.alpha = 0.0;
+            } else if (sy.status == kRunning) {
                 const double rz = tot[b], rr = tot[B + b];
+                sy.alpha = sy.rho / sgb;
                 sy.rr = rr;
                 sy.iter += 1;
                 if (sqrt(rr) <= tol * sqrt(sy.bb)) {
@@ -1063,7 +1135,8 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
             const int64_t nc = h.n * h.B / VecW<T>::W;
             hipLaunchKernelGGL((k_update_bv<T, true>), dim3((unsigned)bv_grid(nc, h.bv_update_resident)),
                                dim3(kBlock), 0, s, nc, h.B, (T *)h.fold_z, (T *)h.r,
-                               (const T *)nullptr, (const T *)h.q, (const T *)h.dinv, red, h.ctl,
+                               (const T *)nullptr, (const T *)h.q, (const T *)h.dinv,
+                               (const double *)h.gpart_spmv, bvec_spmv_blocks(h), red, h.ctl,
                                h.st, h.d_running);
             SLA_HIP(hipGetLastError());
             if (lp) lp->end(SLA_KERNEL_UPDATE, a);
@@ -1105,8 +1178,9 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
         const int64_t nc = h.n * h.B / VecW<T>::W;
         hipLaunchKernelGGL(k_update_dir_bv<T>, dim3((unsigned)fused_bv_grid(h, VecW<T>::W)),
                            dim3(kBlock), 0, s, nc, h.B, (T *)h.x, (T *)h.r, (T *)h.p,
-                           (const T *)h.q, (const T *)h.dinv, red, h.ctl, h.st, h.d_running,
-                           h.bcast, h.bcast_bv);
+                           (const T *)h.q, (const T *)h.dinv, (const double *)h.gpart_spmv,
+                           bvec_spmv_blocks(h), red, h.ctl, h.st, h.d_running, h.bcast,
+                           h.bcast_bv);
         SLA_HIP(hipGetLastError());
         if (lp) lp->end(SLA_KERNEL_UPDATE, a);
         return;
@@ -1115,7 +1189,8 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
         hipLaunchKernelGGL(k_update_bv<T>, dim3((unsigned)bv_grid(nc, h.bv_update_resident)),
                            dim3(kBlock), 0, s, nc,
                            h.B, (T *)h.x, (T *)h.r, (const T *)h.p, (const T *)h.q,
-                           (const T *)h.dinv, red, h.ctl, h.st, h.d_running);
+                           (const T *)h.dinv, (const double *)h.gpart_spmv, bvec_spmv_blocks(h),
+                           red, h.ctl, h.st, h.d_running);
     } else {
         hipLaunchKernelGGL(k_update<T>, dim3((unsigned)g), dim3(kBlock), 0, s, h.n, h.B, (T *)h.x,
                            (T *)h.r, (const T *)h.p, (const T *)h.q, (const T *)h.dinv, red, h.ctl,

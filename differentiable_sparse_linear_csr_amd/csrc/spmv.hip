@@ -741,11 +741,13 @@ __global__ __launch_bounds__(kBlock) void k_spmv_bvec(
         }
     }
     if (FUSED) {
+        // group sums only: the update finishes the sum (group_total), forms
+        // alpha and takes the breakdown test, so this kernel ends without
+        // the grid-wide tail
         block_sum_systems<W>(dot, Q, tmp, blk);
         for (int s = t; s < B; s += kBlock)
             store_partial(red.part + (int64_t)blockIdx.x * B + s, blk[s]);
-        if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, B, tmp, tot))
-            finish_alpha(tot, B, ctl, st, h_running);
+        last_group_sums(red.part, red.gpart, red.sync, gridDim.x, B, tmp, tot);
     }
 }
 
@@ -864,8 +866,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     block_sum_systems<W>(dot, Q, tmp, blk);
     for (int s = t; s < B; s += kBlock)
         store_partial(red.part + (int64_t)blockIdx.x * B + s, blk[s]);
-    if (last_block_sums(red.part, red.gpart, red.sync, gridDim.x, B, tmp, tot))
-        finish_alpha(tot, B, ctl, st, h_running);
+    last_group_sums(red.part, red.gpart, red.sync, gridDim.x, B, tmp, tot);   // as k_spmv_bvec
 }
 
 template <typename T>
@@ -947,10 +948,11 @@ void launch_spmv_t(Handle &h, const void *x, void *y, hipStream_t s) {
     if (h.B == 1) {
         launch_tiles<T, RP, FUSED ? 1 : 0>(h, x, y, x, h.spart, &h.st[0].status, s);
     } else if (bvec_ok<T>(h)) {
+        const Red red_g{h.part, h.gpart_spmv, h.sync + kCntSpmv * kCountersPerKind};
         hipLaunchKernelGGL((k_spmv_bvec<T, RP, FUSED>), dim3((unsigned)bvec_grid<T, FUSED>(h)),
                            dim3(kBlock), 0, s, h.n, h.B, bvec_rows_block<T, FUSED>(h),
                            (const RP *)h.row_ptr, (const int32_t *)h.col, (const T *)h.vals,
-                           (const T *)x, (T *)y, red, h.ctl, h.st, h.d_running);
+                           (const T *)x, (T *)y, red_g, h.ctl, h.st, h.d_running);
     } else {
         hipLaunchKernelGGL((k_spmv_batched<T, RP, FUSED>), dim3((unsigned)batched_grid_t<T>(h)),
                            dim3(kBlock), 0, s, h.n, h.B, batched_rows_per_lane(h),
@@ -1054,6 +1056,26 @@ void launch_spmv_csr_dot_raw(int64_t n, const int32_t *row_ptr, const int32_t *c
 // The folded-direction SpMV of a per-step single-system solve (see
 // FoldArgs): p_new = z + beta p_old, x += alpha p_old on the own rows,
 // q = A p_new and the p_new.q partials. Needs use_ring(h) and no long rows.
+// grid (and rows per workgroup) of the folded batched SpMV: one row per
+// lane and pass, the grid filling the resident workgroups
+int64_t bvec_fold_grid(const Handle &h, int64_t *rows_block_out) {
+    const int W = h.vt == SLA_F64 ? VecW<double>::W : VecW<float>::W;
+    const int64_t J = kBlock / (h.B / W);
+    const int64_t slots = (h.n + J - 1) / J;
+    const int64_t R = h.bvec_fold_resident > 0 ? h.bvec_fold_resident : kXcds;
+    const int64_t rows_block = J * ((slots + R - 1) / R);
+    int64_t grid = (h.n + rows_block - 1) / rows_block;
+    grid = (grid + kXcds - 1) / kXcds * kXcds;
+    if (rows_block_out) *rows_block_out = rows_block;
+    return grid;
+}
+
+// blocks of the batched SpMV the update consumes the group sums of
+int64_t bvec_spmv_blocks(const Handle &h) {
+    if (h.fold_active) return bvec_fold_grid(h, nullptr);
+    return h.vt == SLA_F64 ? bvec_grid<double, true>(h) : bvec_grid<float, true>(h);
+}
+
 bool fold_possible(const Handle &h) {
     if (h.nseg > 0) return false;
     if (h.B > 1) return h.vt == SLA_F64 ? bvec_ok<double>(h) : bvec_ok<float>(h);
@@ -1063,15 +1085,9 @@ bool fold_possible(const Handle &h) {
 void launch_spmv_fold(Handle &h, hipStream_t s) {
     const FoldArgs fa{h.fold_z, {h.p, h.fold_p2}, h.x, h.st};
     if (h.B > 1) {
-        // one row per lane and pass; the grid fills the resident workgroups
-        const int W = h.vt == SLA_F64 ? VecW<double>::W : VecW<float>::W;
-        const int64_t J = kBlock / (h.B / W);
-        const int64_t slots = (h.n + J - 1) / J;
-        const int64_t R = h.bvec_fold_resident > 0 ? h.bvec_fold_resident : kXcds;
-        const int64_t rows_block = J * ((slots + R - 1) / R);
-        int64_t grid = (h.n + rows_block - 1) / rows_block;
-        grid = (grid + kXcds - 1) / kXcds * kXcds;
-        const Red red{h.part, h.gpart, h.sync + kCntSpmv * kCountersPerKind};
+        int64_t rows_block = 0;
+        const int64_t grid = bvec_fold_grid(h, &rows_block);
+        const Red red{h.part, h.gpart_spmv, h.sync + kCntSpmv * kCountersPerKind};
         auto go = [&](auto ttag, auto rtag) {
             using T = decltype(ttag);
             using RP = decltype(rtag);
