@@ -324,18 +324,34 @@ def measure(args, name: str, steps: int, warmup: int, cpu_budget: float,
 
     method = w.extra.get("method", "cg")
 
+    # how each solve ran (single kernel or per-step, and whether it fell
+    # back), counted over the timed steps
+    path_counts = {}
+    counting = [False]
+
+    def note_path():
+        if not counting[0] or not hasattr(A, "last_path"):
+            return
+        lp = A.last_path()
+        key = lp["path"] + ("+cooperative_refused" if lp["cooperative_refused"] else "") + \
+            ("+wait_timed_out" if lp["wait_timed_out"] else "")
+        path_counts[key] = path_counts.get(key, 0) + 1
+
     def step():
         A.set_values(vals)
         _, info = A.solve_raw(b, w.tol, w.maxit, out=x, method=method)
+        note_path()
         its = list(info.iterations)
         if w.adjoint:
             _, _, ainfo = A.adjoint_raw(x, g, w.tol, w.maxit, method=method)
+            note_path()
             its = [i + j for i, j in zip(its, ainfo.iterations)]
         return its, info
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    counting[0] = True
     t0 = time.perf_counter()
     total_its = 0
     for _ in range(steps):
@@ -343,6 +359,7 @@ def measure(args, name: str, steps: int, warmup: int, cpu_budget: float,
         total_its += sum(its)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    counting[0] = False
     value = total_its / elapsed
     ms_per_step = elapsed / steps * 1e3
     fwd_its = info.iterations
@@ -500,6 +517,8 @@ def measure(args, name: str, steps: int, warmup: int, cpu_budget: float,
             # a few microseconds of event overhead per launch)
             "iteration_kernels_ms": round(per_iter_ms, 5),
             "path": "single cooperative kernel" if res_launches > 0 else "per-step kernels",
+            # solves (forward and adjoint) of the timed steps by the path they took
+            "solve_paths": path_counts or None,
             "spmv_ms": round(b2b_ms, 5),
             "spmv_gflops": round(2 * w.nnz * w.batch / (b2b_ms * 1e-3) / 1e9, 1),
             "spmv_gbps": round(ab["spmv"] / (b2b_ms * 1e-3) / 1e9, 1),
@@ -582,7 +601,7 @@ def main() -> int:
             "steps": big["steps"], "warmup": big["warmup"], "ms_per_step": big["ms_per_step"],
             "step": big["config"]["step"], "tol": big["config"]["tol"],
             "maxit": big["config"]["maxit"], "roofline": big["roofline"],
-            **{k: big["extra"][k] for k in ("path", "iteration_ms", "iteration_gbps_3k",
+            **{k: big["extra"][k] for k in ("path", "solve_paths", "iteration_ms", "iteration_gbps_3k",
                                             "iteration_frac_3k", "iteration_kernels_ms",
                                             "spmv_ms", "spmv_gbps", "kernel_avg_ms")},
             "cpu_baseline": big["cpu_baseline"]}
