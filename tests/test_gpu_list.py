@@ -120,3 +120,33 @@ def test_entry_outside_its_block_is_rejected():
     with pytest.raises(SlaError) as e:
         SparseTensorList.from_coo_list(r, c, v, [2, 2])
     assert e.value.status == _lib.SLA_ERR_INDEX_RANGE
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_list_ring_spmv_matches_one_tile_ahead(dtype):
+    """A list of stencil members (every tile small and narrow, so the list's
+    SpMV takes the ring form, reading the per-tile live flags as words and
+    skipping finished members' tiles): the solve bitwise equal with the ring
+    on and off (same tiles, same per-tile dots), and every member against
+    its own oracle solve."""
+    ms = [m for m in members() if m[0] in ("poisson30", "diffusion12", "poisson70", "one",
+                                           "zero_rhs")]
+    A = build(ms, dtype)
+    lay = A.layout()
+    assert lay["ring_tiles"], lay
+    bs = rhs(ms, dtype, 300)
+    tol = 1e-10 if dtype == np.float64 else 1e-5
+    xs = []
+    for ring in (1, 0):
+        A.set_option(_lib.SLA_OPT_SPMV_RING, ring)
+        x, info = A.solve_raw(dev(np.concatenate(bs)), tol, 3000)
+        xs.append((host(x), list(info.iterations)))
+    assert xs[0][0].tobytes() == xs[1][0].tobytes() and xs[0][1] == xs[1][1]
+    X = xs[0][0]
+    o = 0
+    for q, (name, n, r, c, v) in enumerate(ms):
+        ref = oracle.coo_to_csr(n, r, c, v.astype(dtype))
+        xo, ito, _, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], bs[q], tol, 3000)
+        assert abs(xs[0][1][q] - ito) <= 2, (name, xs[0][1][q], ito)
+        assert rel(X[o:o + n], xo) <= (1e-8 if dtype == np.float64 else 1e-4), name
+        o += n

@@ -682,3 +682,42 @@ def test_batched_folded_direction_matches_three_kernels(dtype):
     for s in range(B):
         assert abs(ainfo.iterations[s] - it_o[s]) <= 2
         assert rel(GB[s], lam_o[s]) <= gtol and rel(GV[s], gv_o[s]) <= gtol, s
+
+
+def test_folded_direction_on_reordered_handle():
+    """The folded solve runs on the reordered handle's P A P^T (options reach
+    it through the caller's handle); x in the caller's order against the
+    oracle on A, folded and not, and the adjoint's value gradient in the
+    caller's CSR order."""
+    from differentiable_sparse_linear_csr_amd import SparseCSR
+    N = 300
+    r, c, v = poisson2d_coo(N)
+    n = N * N
+    b = np.random.default_rng(31).standard_normal(n)
+    A = SparseCSR.from_coo(dev(r), dev(c), dev(v), n, reorder=True)
+    assert A.layout()["reordered"]
+    A.set_option(_lib.SLA_OPT_RESIDENT, 0)
+    A.set_option(_lib.SLA_OPT_FUSED_UPDATE, 0)
+    ref = oracle.coo_to_csr(n, r, c, v)
+    tol = 1e-10
+    xo, ito, _, _ = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, tol, 20000)
+    out = {}
+    for fold in (1, 0):
+        A.set_option(_lib.SLA_OPT_FOLD_DIRECTION, fold)
+        A.profile_reset()
+        A.set_option(_lib.SLA_OPT_PROFILE, 1)
+        x, info = A.solve_raw(dev(b), tol, 20000)
+        prof = A.profile()
+        A.set_option(_lib.SLA_OPT_PROFILE, 0)
+        assert (prof["direction"][0] == 0) == bool(fold), prof
+        assert abs(info.iterations[0] - ito) <= 2
+        assert rel(host(x), xo) <= 1e-8
+        out[fold] = host(x)
+    assert rel(out[1], out[0]) <= 1e-8
+    A.set_option(_lib.SLA_OPT_FOLD_DIRECTION, 1)
+    g = np.random.default_rng(32).standard_normal(n)
+    lam, gvo, ita, _, _ = oracle.adjoint(ref["row_ptr"], ref["col"], ref["vals"], xo, g, tol, 20000)
+    x, _ = A.solve_raw(dev(b), tol, 20000)
+    gb, gv, ainfo = A.adjoint_raw(x, dev(g), tol, 20000)
+    assert abs(ainfo.iterations[0] - ita) <= 2
+    assert rel(host(gb), lam) <= 1e-8 and rel(host(gv), gvo) <= 1e-8
