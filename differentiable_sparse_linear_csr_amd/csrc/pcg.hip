@@ -16,6 +16,8 @@
 // and the direction update. Each system's status lives on the device; kernels
 // leave finished systems untouched, so the host can poll every k iterations
 // without changing the iterate or the count.
+#include <atomic>
+
 #include "common.h"
 
 namespace sla {
@@ -1102,6 +1104,184 @@ __global__ __launch_bounds__(kBlock) void k_grad_tile(const TileDesc *__restrict
     }
 }
 
+// The same gradient, single system, over tiles in the ring form of the tile
+// SpMV (every tile narrow; entries from k0 rounded down to a multiple of 4 up
+// to k1 at most 256; at most 63 rows): lane l owns the 4-entry group 4 l, and
+// each entry's lambda comes from a per-wavefront LDS table that the lanes of
+// the tile's rows fill over their entry ranges. A tile's packed columns, row
+// offsets and lambda of its rows are issued kGradRing tiles ahead and its x
+// gathers two tiles ahead, so that each wait leaves the later tiles' loads
+// in flight (memory operations complete in issue order); the stores of a
+// tile go out before the loads it refills. Lanes whose group lies inside the
+// tile store it whole, past the caches. On the 133M-row Poisson matrix (5.3 GB
+// of gradient) it took 2.21 ms against 3.13 for k_grad_tile (one run);
+// streaming the whole-group stores took it from 2.80 to 2.48 ms (another
+// run), while six or eight slots with gathers three or four tiles ahead, or
+// eight workgroups per CU, were no faster. The walk over the tiles (a contiguous share per XCD,
+// band-aligned when the band fits the grid) is the ring SpMV's. Same values
+// as k_grad_tile, bit for bit.
+constexpr int kGradRing = 4;
+// four values as streaming (non-temporal) stores: the gradient is written
+// once and not read back by the kernel, so its lines need not displace the
+// gathered x and lambda in the caches
+typedef double sla_d2 __attribute__((ext_vector_type(2)));
+typedef float sla_f4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store4_stream(double *p, const double (&v)[4]) {
+    const sla_d2 a = {v[0], v[1]}, b = {v[2], v[3]};
+    __builtin_nontemporal_store(a, reinterpret_cast<sla_d2 *>(p));
+    __builtin_nontemporal_store(b, reinterpret_cast<sla_d2 *>(p) + 1);
+}
+__device__ __forceinline__ void store4_stream(float *p, const float (&v)[4]) {
+    const sla_f4 a = {v[0], v[1], v[2], v[3]};
+    __builtin_nontemporal_store(a, reinterpret_cast<sla_f4 *>(p));
+}
+// unused LDS at launch so that the fp64 and fp32 forms both hold four
+// workgroups per CU (static LDS 8 or 4 KB), the grid the band walk is cut for
+constexpr size_t kGradLdsPad = 30 * 1024;
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_grad_ring(
+    const TileDesc *__restrict__ tiles, int64_t ntiles, const uint16_t *__restrict__ roff16,
+    const uint16_t *__restrict__ col16, const T *__restrict__ lam, const T *__restrict__ x,
+    T *__restrict__ grad, double sign, int vec_store, int64_t band_l, int32_t band_p) {
+    __shared__ __align__(16) T lt_all[kWaves][4 * 64];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    T *lt = lt_all[wv];
+    const int xcd = blockIdx.x % kXcds;
+    int64_t stride = (int64_t)(gridDim.x / kXcds) * kWaves;
+    const int64_t wid = (int64_t)(blockIdx.x / kXcds) * kWaves + wv;
+    int64_t t_next = ntiles * xcd / kXcds + wid;
+    int64_t t_end = ntiles * (xcd + 1) / kXcds;
+    if (band_l > 0 && band_l * band_p == stride) {
+        const int64_t T0 = t_next - wid, T1 = t_end;
+        const int64_t panel = wid / band_l, colw = wid - panel * band_l;
+        t_next = T0 + (T1 - T0) * panel / band_p + colw;
+        t_end = T0 + (T1 - T0) * (panel + 1) / band_p;
+        stride = band_l;
+    }
+    // slot u: tile, descriptor fields, the lane's packed 16-bit columns, row
+    // offset and lambda; gather buffer h: x at the slot's columns
+    int64_t s_t[kGradRing], s_base[kGradRing];
+    int32_t s_nr[kGradRing], s_nk[kGradRing], s_shift[kGradRing], s_cb[kGradRing];
+    uint2 s_c[kGradRing];
+    int32_t s_ro[kGradRing];
+    T s_l[kGradRing];
+    double xv[2][4];
+    TileDesc dn{0, 0, 0, 0, 0, 0, 0};
+    if (t_next < t_end) dn = tiles[t_next];
+    // Every load is issued by every lane, at a clamped offset where the lane
+    // has nothing to load (past the end: an empty tile reading entry 0, row 0
+    // and offset 0; the entry arrays are padded past nnz). What clamped lanes
+    // load is never stored.
+    auto fetch = [&](int u) {
+        s_t[u] = t_next;
+        TileDesc e{0, 0, 0, 0, 0, 0, 0};
+        if (t_next < t_end) e = dn;
+        const int nr = e.re - e.rs;
+        s_nr[u] = nr;
+        s_nk[u] = (int)(e.k1 - e.k0);
+        s_shift[u] = (int)(e.k0 & 3);
+        s_cb[u] = e.cbase;
+        const int64_t base = e.k0 & ~(int64_t)3;
+        s_base[u] = base;
+        const int span = (int)(e.k1 - base);
+        const int g = 4 * lane < span ? 4 * lane : 0;
+        s_c[u] = *reinterpret_cast<const uint2 *>(col16 + base + g);
+        s_ro[u] = (int32_t)roff16[e.rpos + (lane <= nr ? lane : nr)];
+        s_l[u] = lam[e.rs + (lane < nr ? lane : 0)];
+        if (t_next < t_end) t_next += stride;
+    };
+    auto load_desc = [&]() {
+        if (t_next < t_end) dn = tiles[t_next];
+    };
+    auto gather = [&](int u, int hb) {
+        const int shift = s_shift[u], nk = s_nk[u], cb = s_cb[u];
+        const uint32_t raw[2] = {s_c[u].x, s_c[u].y};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int j = 4 * lane + k - shift;
+            const int32_t c = cb + (int32_t)((raw[k >> 1] >> (16 * (k & 1))) & 0xffffu);
+            xv[hb][k] = (double)x[(j >= 0 && j < nk) ? c : 0];
+        }
+    };
+    auto step = [&](int u, int hb) {
+        const int nrows = s_nr[u], shift = s_shift[u], nk = s_nk[u];
+        // row r's entry slots are [roff[r], roff[r + 1]) + shift; lane r + 1
+        // holds roff[r + 1] (lane nrows the end)
+        const int a = s_ro[u] + shift;
+        const int b = __shfl_down(s_ro[u], 1, 64) + shift;
+        if (lane < nrows)
+            for (int j = a; j < b; ++j) lt[j] = s_l[u];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        T l4[4];
+        load4(lt + 4 * lane, l4);
+        T gv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) gv[k] = (T)(sign * ((double)l4[k] * xv[hb][k]));
+        const int j0 = 4 * lane - shift;
+        T *gp = grad + s_base[u] + 4 * lane;
+        if (vec_store && j0 >= 0 && j0 + 3 < nk) {
+            store4_stream(gp, gv);
+        } else {
+            // the group shared with a neighbouring tile: cached stores, so
+            // that its line is merged in L2 rather than written twice
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (j0 + k >= 0 && j0 + k < nk) gp[k] = gv[k];
+        }
+        fetch(u);
+        gather((u + 2) % kGradRing, hb);
+        load_desc();
+        // the next tile's table is written after these reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    if (t_next < t_end) {
+#pragma unroll
+        for (int u = 0; u < kGradRing; ++u) {
+            fetch(u);
+            load_desc();
+        }
+        gather(0, 0);
+        gather(1, 1);
+        // four steps per pass while all four slots hold a tile (one path
+        // through the loop body keeps the waits for the in-order counter
+        // tight), then the at most three tiles left
+        while (s_t[3] < t_end) {
+            step(0, 0);
+            step(1, 1);
+            step(2, 0);
+            step(3, 1);
+        }
+        if (s_t[0] < t_end) {
+            step(0, 0);
+            if (s_t[1] < t_end) {
+                step(1, 1);
+                if (s_t[2] < t_end) step(2, 0);
+            }
+        }
+    }
+}
+
+// resident workgroups of k_grad_ring<T> on a device (computed once per device)
+template <typename T>
+int64_t grad_ring_resident(int device) {
+    constexpr int kDevs = 64;
+    static std::atomic<int64_t> cache[kDevs];
+    if (device < 0 || device >= kDevs)
+        return resident_workgroups((const void *)&k_grad_ring<T>, device, kGradLdsPad);
+    int64_t r = cache[device].load(std::memory_order_relaxed);
+    if (r == 0) {
+        r = resident_workgroups((const void *)&k_grad_ring<T>, device, kGradLdsPad);
+        cache[device].store(r, std::memory_order_relaxed);
+    }
+    return r;
+}
+
 // the same for rows longer than kLongRow, one workgroup per row
 template <typename T, typename RP>
 __global__ __launch_bounds__(kBlock) void k_grad_long(const int32_t *__restrict__ long_rows,
@@ -1540,7 +1720,17 @@ void grad_vals(Handle &h, const void *lam_internal, const void *x_user, void *gr
     auto go = [&](auto ttag, auto rtag) {
         using T = decltype(ttag);
         using RP = decltype(rtag);
-        if (h.ntiles > 0) {
+        if (h.ntiles > 0 && h.B == 1 && h.all_narrow && h.ring_tiles && h.spmv_ring) {
+            int64_t g = (h.ntiles + kWaves - 1) / kWaves;
+            g = (g + kXcds - 1) / kXcds * kXcds;
+            const int64_t res = grad_ring_resident<T>(h.device);
+            if (g > res) g = res;
+            const int vec = ((uintptr_t)grad % 16) == 0;
+            hipLaunchKernelGGL(k_grad_ring<T>, dim3((unsigned)g), dim3(kBlock), kGradLdsPad, s,
+                               (const TileDesc *)h.tiles, h.ntiles, (const uint16_t *)h.roff16,
+                               (const uint16_t *)h.col16, (const T *)lam_internal,
+                               (const T *)x_int, (T *)grad, sign, vec, h.band_l, h.band_p);
+        } else if (h.ntiles > 0) {
             int64_t g = (h.ntiles + kWaves - 1) / kWaves;
             if (g > 4 * kMaxGrid) g = 4 * kMaxGrid;
             hipLaunchKernelGGL(k_grad_tile<T>, dim3((unsigned)g), dim3(kBlock), 0, s,

@@ -131,7 +131,10 @@ enum {
                                    columns within 65535 of the tile's smallest) keeps four
                                    tiles' entries and two tiles' gathers in flight per
                                    wavefront; 0: one tile ahead. Same tiles, same sums, bitwise
-                                   equal results. */
+                                   equal results. The value gradient of such a handle
+                                   (sla_spmv_backward, the adjoints) follows the same
+                                   setting: four tiles ahead, or one tile per wavefront;
+                                   bitwise equal too. */
     SLA_OPT_FOLD_DIRECTION = 9  /* 1 (default): a per-step PCG solve with fp64 values, of a
                                    single system on such tiles (no row longer than 128
                                    entries) or of a batch whose B / (16 / value bytes) is a

@@ -96,3 +96,57 @@ def test_autograd_through_mv_with_duplicates():
     assert rel(host(gx), gx_o) <= 1e-12
     # every input entry receives the gradient of the CSR entry it merged into
     assert np.array_equal(host(gvals), gv_o[ref["slot"]])
+
+
+@pytest.mark.parametrize("case", ["poisson2d_1100", "diffusion3d_40", "banded_irregular", "tiny"])
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_ring_gradient_matches_tile_kernel(case, dtype):
+    """The value gradient in the ring form (single system, every tile small
+    and narrow: four tiles of entries and two of gathers in flight per
+    wavefront, whole 4-entry groups stored at once) against the
+    one-tile-per-wavefront kernel (SLA_OPT_SPMV_RING off) on the same
+    handle, bit for bit, and against the oracle; also into an output that
+    starts 8 bytes past a 16-byte boundary (every group stored entry by
+    entry)."""
+    from differentiable_sparse_linear_csr_amd import _lib
+    from differentiable_sparse_linear_csr_amd.sparse import _ptr, _stream
+    from test_gpu_spmv import banded_irregular
+    if case in ("poisson2d_1100", "diffusion3d_40"):
+        w = (make_workload("poisson2d_11548", size=1100) if case == "poisson2d_1100"
+             else make_workload("diffusion3d_128", size=40))
+        n, c, v = w.n, w.cols, w.vals
+        r = np.repeat(np.arange(n), np.diff(w.row_ptr)) if w.fmt == "csr" else w.rows
+    elif case == "banded_irregular":
+        n = 300000
+        r, c, v = banded_irregular(n, 7)
+    else:
+        n = 10
+        i = np.arange(n)
+        r = np.concatenate([i, i[1:], i[:-1]])
+        c = np.concatenate([i, i[:-1], i[1:]])
+        v = np.concatenate([np.full(n, 2.0), np.full(n - 1, -1.0), np.full(n - 1, -1.0)])
+    v = v.astype(dtype)
+    print(f"ring gradient: {case} n={n} nnz={v.size} {np.dtype(dtype).name}", flush=True)
+    A = handle(n, r, c, v)
+    lay = A.layout()
+    assert lay["narrow_columns"] and lay["ring_tiles"], lay
+    x = np.random.default_rng(31).standard_normal(n).astype(dtype)
+    g = np.random.default_rng(32).standard_normal(n).astype(dtype)
+    _, gv_ring = A.matvec_backward_raw(dev(x), dev(g), want_x=False)
+    # the same gradient into an output 8 bytes off a 16-byte boundary
+    buf = torch.zeros(A.nnz + 2, dtype=gv_ring.dtype, device=gv_ring.device)
+    off = 1 if dtype == np.float64 else 2
+    gv_off = buf[off:off + A.nnz]
+    assert gv_off.data_ptr() % 16 == 8
+    xd, gd = dev(x), dev(g)
+    _lib.check(_lib.load().sla_spmv_backward(A._h, _ptr(xd), _ptr(gd), None, _ptr(gv_off),
+                                             _stream(xd.device)))
+    A.set_option(_lib.SLA_OPT_SPMV_RING, 0)
+    _, gv_tile = A.matvec_backward_raw(dev(x), dev(g), want_x=False)
+    A.set_option(_lib.SLA_OPT_SPMV_RING, 1)
+    assert host(gv_ring).tobytes() == host(gv_tile).tobytes()
+    assert host(gv_off).tobytes() == host(gv_tile).tobytes()
+    # nothing written outside the output
+    assert host(buf[:off]).tobytes() == bytes(off * buf.element_size())
+    assert host(buf[off + A.nnz:]).tobytes() == bytes((2 - off) * buf.element_size())
+    check(A, r, c, v, n, x, g, dtype)
