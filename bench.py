@@ -114,11 +114,18 @@ def cpu_baseline(w, budget_s: float, budget_1t_s: float = 0.0):
     solve (Jacobi-PCG, or Jacobi-BiCGStab for a non-symmetric workload) on the
     same matrix and right-hand side, over a bounded number of iterations (the
     first ones of the same solve), with all threads and (budget_1t_s > 0)
-    with one thread."""
+    with one thread. For a workload whose step also runs the adjoint, the
+    oracle's adjoint (the transposed solve, tol 0, for a bounded number of
+    iterations, then the value gradient) is timed the same way after the
+    forward sample, and value is forward + adjoint iterations over their
+    summed time, as the GPU's value counts them."""
     import numpy as np
     import oracle
 
     threads = oracle.num_threads()
+    bicg = w.extra.get("method") == "bicgstab"
+    solve = oracle.bicgstab if bicg else oracle.pcg
+    adjoint = oracle.bicgstab_adjoint if bicg else oracle.adjoint
     if "seg_rows" in w.extra:
         # every member is its own system: the oracle solves them one by one,
         # each for the same bounded number of iterations
@@ -128,15 +135,9 @@ def cpu_baseline(w, budget_s: float, budget_1t_s: float = 0.0):
             sel = (w.rows >= seg[q]) & (w.rows < seg[q + 1])
             ref = oracle.coo_to_csr(seg[q + 1] - seg[q], w.rows[sel] - seg[q], w.cols[sel] - seg[q],
                                     w.vals[sel])
-            members.append((ref, w.b[seg[q]:seg[q + 1]]))
-
-        def run(iters):
-            total = 0
-            for ref, bq in members:
-                _, it, _, _ = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], bq, 0.0, iters)
-                total += int(it)
-            return total
-        what = f"Jacobi-PCG iterations (tol 0) of each of the {len(members)} members of {w.name}, " \
+            members.append((ref, ref["vals"], w.b[seg[q]:seg[q + 1]],
+                            w.g[seg[q]:seg[q + 1]] if w.g is not None else None))
+        what = f"iterations (tol 0) of each of the {len(members)} members of {w.name}, " \
                f"solved one by one"
         probe_iters = 2
     else:
@@ -146,38 +147,59 @@ def cpu_baseline(w, budget_s: float, budget_1t_s: float = 0.0):
         else:
             ref = oracle.coo_to_csr(w.n, w.rows, w.cols, w.vals)
             vals = ref["vals"]
-        bicg = w.extra.get("method") == "bicgstab"
-        solve = oracle.bicgstab if bicg else oracle.pcg
-
-        def run(iters):
-            _, it, _, _ = solve(ref["row_ptr"], ref["col"], vals, w.b, 0.0, iters)
-            return int(np.sum(it))
-        name = "Jacobi-BiCGStab" if bicg else "Jacobi-PCG"
-        what = f"{name} iterations (tol 0) of the forward solve of {w.name} ({w.batch} " \
-               f"system(s)), oracle CSR built from the same input"
+        members = [(ref, vals, w.b, w.g)]
+        what = f"iterations (tol 0) of {w.name} ({w.batch} system(s)), oracle CSR built from " \
+               f"the same input"
         probe_iters = 5 if w.n * w.batch < (1 << 24) else 1
+    xs = [None] * len(members)
 
-    def timed(budget, probe):
+    def run(iters):
+        total = 0
+        for q, (ref, vals, bq, _) in enumerate(members):
+            xs[q], it, _, _ = solve(ref["row_ptr"], ref["col"], vals, bq, 0.0, iters)
+            total += int(np.sum(it))
+        return total
+
+    def run_adj(iters):
+        total = 0
+        for q, (ref, vals, _, gq) in enumerate(members):
+            _, _, it, _, _ = adjoint(ref["row_ptr"], ref["col"], vals, xs[q], gq, 0.0, iters)
+            total += int(np.sum(it))
+        return total
+
+    def timed(fn, budget, probe):
         t0 = time.perf_counter()
-        run(probe)
+        fn(probe)
         per = (time.perf_counter() - t0) / probe
         iters = int(max(1, min(w.maxit, budget / max(per, 1e-9))))
         t0 = time.perf_counter()
-        it = run(iters)
+        it = fn(iters)
         dt = time.perf_counter() - t0
-        return it / dt, iters, dt
+        return it, iters, dt
 
-    rate, iters, dt = timed(budget_s, probe_iters)
-    out = {"value": round(rate, 3), "unit": "iterations/s", "cores": threads, "kind": "oracle",
-           "sample": f"first {iters} {what}; {dt:.1f} s on {threads} threads"}
+    name = "Jacobi-BiCGStab" if bicg else "Jacobi-PCG"
+    with_adj = bool(w.adjoint) and w.g is not None
+    it_f, iters_f, dt_f = timed(run, budget_s / 2 if with_adj else budget_s, probe_iters)
+    out = {"value": round(it_f / dt_f, 3), "unit": "iterations/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"first {iters_f} {name} {what}; {dt_f:.1f} s on {threads} threads"}
+    if with_adj:
+        it_a, iters_a, dt_a = timed(run_adj, budget_s / 2, probe_iters)
+        out["forward_value"] = out["value"]
+        out["adjoint_value"] = round(it_a / dt_a, 3)
+        out["value"] = round((it_f + it_a) / (dt_f + dt_a), 3)
+        out["sample"] = (f"first {iters_f} forward {name} {what} ({dt_f:.1f} s), then the "
+                         f"adjoint from the forward iterate: first {iters_a} transposed "
+                         f"iterations and the value gradient ({dt_a:.1f} s); value = forward + "
+                         f"adjoint iterations over both times, on {threads} threads")
     if budget_1t_s > 0:
         oracle.set_num_threads(1)
         try:
-            rate1, iters1, dt1 = timed(budget_1t_s, 1)
+            it1, iters1, dt1 = timed(run, budget_1t_s, 1)
         finally:
             oracle.set_num_threads(threads)
-        out["value_1_thread"] = round(rate1, 3)
-        out["sample_1_thread"] = f"first {iters1} iterations of the same solve; {dt1:.1f} s"
+        out["value_1_thread"] = round(it1 / dt1, 3)
+        out["sample_1_thread"] = f"first {iters1} iterations of the same forward solve; {dt1:.1f} s"
     out.update(host_info())
     return out
 
@@ -273,6 +295,10 @@ def run_inverse(args, N: int = 128, S: int = 4) -> int:
         w.vals = np.ascontiguousarray(
             g.values(rec.kappa_true).expand(S, -1).detach().cpu().numpy())
         w.b = rec.F.cpu().numpy()
+        # the step's adjoint too: tol-0 iterations cost the same whatever the
+        # upstream gradient, so a seeded normal one stands in for the misfit's
+        w.adjoint = True
+        w.g = np.random.default_rng(7).standard_normal(w.b.shape).astype(w.b.dtype)
         print("[bench] timing the CPU oracle ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     else:
