@@ -629,7 +629,9 @@ def main() -> int:
             "maxit": big["config"]["maxit"], "roofline": big["roofline"],
             **{k: big["extra"][k] for k in ("path", "solve_paths", "iteration_ms", "iteration_gbps_3k",
                                             "iteration_frac_3k", "iteration_kernels_ms",
-                                            "spmv_ms", "spmv_gbps", "kernel_avg_ms")},
+                                            "spmv_ms", "spmv_gbps", "spmv_backward_first_call_ms",
+                                            "spmv_backward_ms", "spmv_backward_gbps",
+                                            "kernel_avg_ms")},
             "cpu_baseline": big["cpu_baseline"]}
     print(json.dumps(out), flush=True)
     if args.calibrate_copy_mib > 0:

@@ -397,16 +397,22 @@ sla_status sla_spmv_backward(sla_csr hd, const void *x, const void *grad_y, void
         if (grad_x && (grad_x == grad_y || grad_x == x))
             fail(SLA_ERR_INVALID_ARG, "grad_x must not alias x or grad_y");
         hipStream_t s = (hipStream_t)stream;
-        if (grad_x) any_spmv(*transpose_for_backward(*h, s), grad_y, grad_x, s);
-        if (grad_vals_out && h->nnz > 0) {
-            // grad_y in the internal layout [n][B] (the workspace q holds it)
-            const void *g_int = grad_y;
-            if (h->B > 1) {
-                transpose(grad_y, h->q, h->B, h->n, h->vbytes, s);
-                g_int = h->q;
-            }
-            grad_vals(*h, g_int, x, grad_vals_out, s, 1.0);
+        Handle *t = grad_x ? transpose_for_backward(*h, s) : nullptr;
+        const bool want_vals = grad_vals_out && h->nnz > 0;
+        // a batch's grad_y in the internal layout [n][B] (the workspace q
+        // holds it), made once for A^T g (when neither handle is reordered)
+        // and the value gradient
+        const bool shared = h->B > 1 && t && !t->inner && want_vals;
+        const void *g_int = grad_y;
+        if (h->B > 1 && (shared || want_vals)) {
+            transpose(grad_y, h->q, h->B, h->n, h->vbytes, s);
+            g_int = h->q;
         }
+        if (t) {
+            if (shared) spmv_from_internal(*t, g_int, grad_x, s);
+            else any_spmv(*t, grad_y, grad_x, s);
+        }
+        if (want_vals) grad_vals(*h, g_int, x, grad_vals_out, s, 1.0);
         if (h->profile) {
             SLA_HIP(hipStreamSynchronize(s));
             flush_profile(*h);

@@ -314,6 +314,7 @@ void iota_i64(int64_t *out, int64_t m, hipStream_t s);
 
 // ------------------------------------------------------------------ SpMV / solve
 void spmv(Handle &h, const void *x, void *y, hipStream_t s);
+void spmv_from_internal(Handle &h, const void *x_int, void *y, hipStream_t s);
 void init_launch_limits(Handle &h);
 void init_vector_limits(Handle &h);
 void alloc_workspace(Handle &h, hipStream_t s);

@@ -1282,6 +1282,99 @@ int64_t grad_ring_resident(int device) {
     return r;
 }
 
+// 16 bytes of a row of an internal [n][B] vector (16-byte aligned)
+__device__ __forceinline__ void load16(const float *p, float (&o)[4]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+}
+__device__ __forceinline__ void load16(const double *p, double (&o)[2]) {
+    const double2 a = *reinterpret_cast<const double2 *>(p);
+    o[0] = a.x; o[1] = a.y;
+}
+
+// The same gradient for a batch whose systems fill 16-byte blocks (B a
+// multiple of W = 16 / sizeof(T); lambda and x in the internal [n][B]
+// layout): lanes are (entry e of a run of EL consecutive entries, block q of
+// W systems), so one 16-byte load brings W systems of x at the entry's
+// column (and of lambda at its row), a load instruction touches at most EL
+// cache lines (against 64 when each lane gathers one system of its own
+// entry), and the EL lanes of a block write EL consecutive entries of each
+// of its W gradient planes. A wavefront takes one (tile, pass) pair, pass h
+// covering blocks h QL .. h QL + QL - 1, so that a batch gives NQ / QL times
+// as many wavefronts as tiles; entries go four runs at a time (loads first).
+// Same values as k_grad_tile, bit for bit.
+template <typename T, int QLOG>
+__global__ __launch_bounds__(kBlock) void k_grad_tile_bq(const TileDesc *__restrict__ tiles,
+                                                         int64_t ntiles,
+                                                         const uint16_t *__restrict__ roff16,
+                                                         const int32_t *__restrict__ col,
+                                                         const uint16_t *__restrict__ col16,
+                                                         int64_t nnz, int B, const T *__restrict__ lam,
+                                                         const T *__restrict__ x,
+                                                         T *__restrict__ grad, double sign) {
+    constexpr int W = 16 / sizeof(T);
+    constexpr int QL = 1 << QLOG;
+    constexpr int EL = 64 / QL;
+    constexpr int U = 4;
+    __shared__ uint16_t rowid_all[kWaves][kTileCap];
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    uint16_t *rowid = rowid_all[wv];
+    const int e = lane & (EL - 1);
+    const int qq = lane / EL;
+    const int NQ = B / W;
+    const int NP = (NQ + QL - 1) / QL;
+    const int64_t nv = ntiles * NP;
+    const int64_t stride = (int64_t)gridDim.x * kWaves;
+    for (int64_t v = (int64_t)blockIdx.x * kWaves + wv; v < nv; v += stride) {
+        const int64_t t = v / NP;
+        const int q = (int)(v - t * NP) * QL + qq;
+        const TileDesc d = tiles[t];
+        const int nrows = d.re - d.rs;
+        const int nk = (int)(d.k1 - d.k0);
+        const uint16_t *rp = roff16 + d.rpos;
+        for (int j = lane; j < nrows; j += 64) {
+            const int a = rp[j], b = rp[j + 1];
+            for (int k = a; k < b; ++k) rowid[k] = (uint16_t)j;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (q < NQ) {
+            const T *xq = x + q * W;
+            const T *lq = lam + q * W;
+            T *gq = grad + (int64_t)q * W * nnz + d.k0;
+            for (int kb = 0; kb < nk; kb += U * EL) {
+                T xv[U][W], lv[U][W];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    // past the tile's end: entry 0's row and column (not stored)
+                    const int kk = kb + u * EL + e < nk ? kb + u * EL + e : 0;
+                    const int64_t k = d.k0 + kk;
+                    const int64_t c = d.narrow ? (int64_t)d.cbase + col16[k] : (int64_t)col[k];
+                    const int64_t i = d.rs + rowid[kk];
+                    load16(xq + c * B, xv[u]);
+                    load16(lq + i * B, lv[u]);
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int kk = kb + u * EL + e;
+                    if (kk < nk) {
+#pragma unroll
+                        for (int j = 0; j < W; ++j)
+                            gq[(int64_t)j * nnz + kk] =
+                                (T)(sign * ((double)lv[u][j] * (double)xv[u][j]));
+                    }
+                }
+            }
+        }
+        // the next pair's table is written after these reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
 // the same for rows longer than kLongRow, one workgroup per row
 template <typename T, typename RP>
 __global__ __launch_bounds__(kBlock) void k_grad_long(const int32_t *__restrict__ long_rows,
@@ -1535,6 +1628,17 @@ void spmv(Handle &h, const void *x, void *y, hipStream_t s) {
     }
 }
 
+// y = A x for a batch whose x is already in the internal [n][B] layout (not
+// h.p, which takes the product) and y in the caller's [B][n]
+void spmv_from_internal(Handle &h, const void *x_int, void *y, hipStream_t s) {
+    Launcher L{h, s, h.profile};
+    hipEvent_t a = nullptr;
+    L.begin(SLA_KERNEL_SPMV, &a);
+    launch_spmv_plain(h, x_int, h.p, s);
+    L.end(SLA_KERNEL_SPMV, a);
+    transpose(h.p, y, h.n, h.B, h.vbytes, s);
+}
+
 namespace {
 
 // One attempt at a solve (see pcg). Returns false, having done nothing the
@@ -1730,6 +1834,18 @@ void grad_vals(Handle &h, const void *lam_internal, const void *x_user, void *gr
                                (const TileDesc *)h.tiles, h.ntiles, (const uint16_t *)h.roff16,
                                (const uint16_t *)h.col16, (const T *)lam_internal,
                                (const T *)x_int, (T *)grad, sign, vec, h.band_l, h.band_p);
+        } else if (h.ntiles > 0 && h.B > 1 && h.B % (16 / (int)sizeof(T)) == 0) {
+            const int nq = h.B / (16 / (int)sizeof(T));
+            const int qlog = nq >= 4 ? 2 : nq >= 2 ? 1 : 0;
+            const int np = (nq + (1 << qlog) - 1) >> qlog;
+            int64_t g = (h.ntiles * np + kWaves - 1) / kWaves;
+            if (g > 4 * kMaxGrid) g = 4 * kMaxGrid;
+            auto kern = qlog == 2 ? k_grad_tile_bq<T, 2>
+                                  : qlog == 1 ? k_grad_tile_bq<T, 1> : k_grad_tile_bq<T, 0>;
+            hipLaunchKernelGGL(kern, dim3((unsigned)g), dim3(kBlock), 0, s,
+                               (const TileDesc *)h.tiles, h.ntiles, (const uint16_t *)h.roff16,
+                               (const int32_t *)h.col, (const uint16_t *)h.col16, h.nnz, h.B,
+                               (const T *)lam_internal, (const T *)x_int, (T *)grad, sign);
         } else if (h.ntiles > 0) {
             int64_t g = (h.ntiles + kWaves - 1) / kWaves;
             if (g > 4 * kMaxGrid) g = 4 * kMaxGrid;

@@ -2,7 +2,8 @@
 spmv_backward: A^T g normwise within 1e-12 (fp64) / 1e-5 (fp32) like the
 forward SpMV, grad_vals[k] = g[row k] x[col k] bit-exact in fp64 (one rounded
 product, the same on both sides) and within one fp32 rounding otherwise.
-Covers unsymmetric irregular patterns with empty and long rows, batches, the
+Covers unsymmetric irregular patterns with empty and long rows, batches (B a
+multiple of the 16-byte system block or not; 1, 2, 3 and 8 blocks), the
 reordered solver, the symmetric-flag shortcut, new values after the first
 backward, and autograd through SparseCSR.mv with duplicated COO input."""
 import numpy as np
@@ -38,7 +39,8 @@ def check(A, r, c, V, n, X, G, dtype):
 
 
 @pytest.mark.parametrize("dtype,B", [(np.float64, 1), (np.float32, 1), (np.float64, 3),
-                                     (np.float32, 8)])
+                                     (np.float32, 8), (np.float64, 4), (np.float64, 6),
+                                     (np.float32, 12), (np.float32, 32)])
 def test_unsymmetric_irregular(dtype, B):
     n = 40009
     lengths = np.random.default_rng(5).integers(0, 12, n)
@@ -65,6 +67,17 @@ def test_workload_matrices_and_symmetric_shortcut():
         for sym in (False, True):
             A = handle(w.n, w.rows, w.cols, w.vals, check_symmetric=sym)
             check(A, w.rows, w.cols, w.vals, w.n, x, g, np.float64)
+    # a batch: grad_y goes to the internal layout once for A^T g and the value
+    # gradient, also when A^T is the handle itself
+    w = make_workload("batched_diffusion2d_512x32", size=40, batch=8)
+    X = np.random.default_rng(12).standard_normal((8, w.n)).astype(np.float32)
+    G = np.random.default_rng(13).standard_normal((8, w.n)).astype(np.float32)
+    for sym in (False, True):
+        A = handle(w.n, w.rows, w.cols, w.vals, check_symmetric=sym)
+        check(A, w.rows, w.cols, w.vals, w.n, X, G, np.float32)
+        gx, _ = A.matvec_backward_raw(dev(X), dev(G), want_vals=False)
+        gx2, _ = A.matvec_backward_raw(dev(X), dev(G))
+        assert host(gx).tobytes() == host(gx2).tobytes()
 
 
 def test_new_values_reach_the_transpose():
