@@ -397,6 +397,14 @@ sla_status sla_spmv_backward(sla_csr hd, const void *x, const void *grad_y, void
         if (grad_x && (grad_x == grad_y || grad_x == x))
             fail(SLA_ERR_INVALID_ARG, "grad_x must not alias x or grad_y");
         hipStream_t s = (hipStream_t)stream;
+        if (h->inner) {
+            reordered_spmv_backward(*h, x, grad_y, grad_x, grad_vals_out, s);
+            if (h->profile) {
+                SLA_HIP(hipStreamSynchronize(s));
+                flush_profile(*h->inner);
+            }
+            return;
+        }
         Handle *t = grad_x ? transpose_for_backward(*h, s) : nullptr;
         const bool want_vals = grad_vals_out && h->nnz > 0;
         // a batch's grad_y in the internal layout [n][B] (the workspace q
@@ -510,6 +518,14 @@ sla_status sla_bicgstab_adjoint(sla_csr hd, const void *x, const void *grad_x, v
         if (grad_b && (grad_b == x || grad_b == grad_x))
             fail(SLA_ERR_INVALID_ARG, "grad_b must not alias x or grad_x");
         hipStream_t s = (hipStream_t)stream;
+        if (h->inner) {
+            Handle &t = reordered_bicgstab_adjoint(*h, x, grad_x, grad_b, grad_vals_out, tol, maxit,
+                                                   info, s);
+            record_path(*h, t);
+            SLA_HIP(hipStreamSynchronize(s));
+            if (h->inner->profile) flush_profile(*h->inner);
+            return;
+        }
         // A^T lambda = grad_x by BiCGStab on A^T (the handle itself when it was
         // checked symmetric)
         Handle &at = *transpose_for_backward(*h, s);
@@ -554,7 +570,8 @@ sla_status sla_csr_memory(sla_csr hd, int64_t *bytes) {
         const Handle *h = reinterpret_cast<const Handle *>(hd);
         int64_t b = 0;
         for (const Handle *c : {h, (const Handle *)h->inner, (const Handle *)h->tr,
-                                h->tr ? (const Handle *)h->tr->inner : nullptr})
+                                h->tr ? (const Handle *)h->tr->inner : nullptr,
+                                h->inner ? (const Handle *)h->inner->tr : nullptr})
             if (c) b += c->bytes;
         *bytes = b;
     });

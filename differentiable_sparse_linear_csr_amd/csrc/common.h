@@ -330,6 +330,11 @@ void reordered_adjoint(Handle &h, const void *x, const void *g, void *grad_b, vo
                        double tol, int32_t maxit, sla_info *info, hipStream_t s);
 void reordered_bicgstab(Handle &h, const void *b, void *x, double tol, int32_t maxit,
                         sla_info *info, hipStream_t s);
+void reordered_spmv_backward(Handle &h, const void *x, const void *g, void *grad_x,
+                             void *grad_vals_out, hipStream_t s);
+Handle &reordered_bicgstab_adjoint(Handle &h, const void *x, const void *g, void *grad_b,
+                                   void *grad_vals_out, double tol, int32_t maxit,
+                                   sla_info *info, hipStream_t s);
 // BiCGStab on one system (bicgstab.hip); b, x device vectors of n elements
 void bicgstab(Handle &h, const void *b, void *x, double tol, int32_t maxit, sla_info *info,
               hipStream_t s, bool keep_internal);

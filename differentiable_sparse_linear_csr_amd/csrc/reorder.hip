@@ -208,6 +208,20 @@ void to_outer(Handle &h, const void *in, void *out, hipStream_t s) {
     SLA_HIP(hipGetLastError());
 }
 
+// the value gradient in the inner CSR order (h.rtmp_grad) to this handle's
+void grad_to_outer(Handle &h, void *grad_vals_out, hipStream_t s) {
+    if (h.nnz == 0) return;
+    if (h.vt == SLA_F64)
+        hipLaunchKernelGGL(k_grad_to_outer<double>, dim3(grid_of(h.nnz * h.B)), dim3(kBlock), 0, s,
+                           (const double *)h.rtmp_grad, (double *)grad_vals_out,
+                           (const int64_t *)h.map_out, h.nnz, h.B);
+    else
+        hipLaunchKernelGGL(k_grad_to_outer<float>, dim3(grid_of(h.nnz * h.B)), dim3(kBlock), 0, s,
+                           (const float *)h.rtmp_grad, (float *)grad_vals_out,
+                           (const int64_t *)h.map_out, h.nnz, h.B);
+    SLA_HIP(hipGetLastError());
+}
+
 }  // namespace
 
 // Handles for a matrix with the same entries as h in another arrangement
@@ -443,7 +457,10 @@ void build_reordered(Handle &h, hipStream_t s) {
 }
 
 // after this handle's values changed: the inner values and Jacobi diagonal
-void reordered_set_values(Handle &h, hipStream_t s) { child_values(h, *h.inner, h.map_in, s); }
+void reordered_set_values(Handle &h, hipStream_t s) {
+    child_values(h, *h.inner, h.map_in, s);
+    h.inner->tr_stale = h.inner->tr != nullptr;
+}
 
 void reordered_spmv(Handle &h, const void *x, void *y, hipStream_t s) {
     to_inner(h, x, h.rtmp[0], s);
@@ -489,20 +506,58 @@ void reordered_adjoint(Handle &h, const void *x, const void *g, void *grad_b, vo
     if (grad_vals_out) {
         to_inner(h, x, h.rtmp[1], s);
         grad_vals(in, in.x, h.rtmp[1], h.rtmp_grad, s);
-        if (h.nnz > 0) {
-            if (h.vt == SLA_F64)
-                hipLaunchKernelGGL(k_grad_to_outer<double>, dim3(grid_of(h.nnz * h.B)),
-                                   dim3(kBlock), 0, s, (const double *)h.rtmp_grad,
-                                   (double *)grad_vals_out, (const int64_t *)h.map_out, h.nnz, h.B);
-            else
-                hipLaunchKernelGGL(k_grad_to_outer<float>, dim3(grid_of(h.nnz * h.B)),
-                                   dim3(kBlock), 0, s, (const float *)h.rtmp_grad,
-                                   (float *)grad_vals_out, (const int64_t *)h.map_out, h.nnz, h.B);
-            SLA_HIP(hipGetLastError());
-        }
+        grad_to_outer(h, grad_vals_out, s);
     }
     SLA_HIP(hipStreamSynchronize(s));
     if (in.profile) flush_profile(in);
+}
+
+// A^T for a backward on a reordered handle, in the inner order: (P A P^T)^T
+// (the inner handle itself when A was checked symmetric)
+Handle &inner_transpose(Handle &h, hipStream_t s) {
+    Handle &in = *h.inner;
+    return (h.flags & SLA_FLAG_CHECK_SYMMETRIC) ? in : *transpose_for_backward(in, s);
+}
+
+// The backward of y = A x on a reordered handle, through P A P^T: A^T g =
+// P^T (P A P^T)^T P g, and g_i x_j formed on the inner pattern (banded, so
+// its gathers stay local) and moved to this handle's CSR order.
+void reordered_spmv_backward(Handle &h, const void *x, const void *g, void *grad_x,
+                             void *grad_vals_out, hipStream_t s) {
+    Handle &in = *h.inner;
+    to_inner(h, g, h.rtmp[0], s);
+    if (grad_x) {
+        spmv(inner_transpose(h, s), h.rtmp[0], h.rtmp[1], s);
+        to_outer(h, h.rtmp[1], grad_x, s);
+    }
+    if (grad_vals_out && h.nnz > 0) {
+        to_inner(h, x, h.rtmp[1], s);
+        const void *g_int = h.rtmp[0];
+        if (in.B > 1) {
+            transpose(h.rtmp[0], in.q, in.B, in.n, in.vbytes, s);
+            g_int = in.q;
+        }
+        grad_vals(in, g_int, h.rtmp[1], h.rtmp_grad, s, 1.0);
+        grad_to_outer(h, grad_vals_out, s);
+    }
+}
+
+// The BiCGStab adjoint on a reordered handle: (P A P^T)^T (P lambda) = P g,
+// then the value gradient as above. Returns the handle that solved.
+Handle &reordered_bicgstab_adjoint(Handle &h, const void *x, const void *g, void *grad_b,
+                                   void *grad_vals_out, double tol, int32_t maxit,
+                                   sla_info *info, hipStream_t s) {
+    Handle &in = *h.inner;
+    Handle &t = inner_transpose(h, s);
+    to_inner(h, g, h.rtmp[0], s);
+    bicgstab(t, h.rtmp[0], h.rtmp[1], tol, maxit, info, s, false);   // P lambda
+    if (grad_b) to_outer(h, h.rtmp[1], grad_b, s);
+    if (grad_vals_out && h.nnz > 0) {
+        to_inner(h, x, h.rtmp[0], s);
+        grad_vals(in, h.rtmp[1], h.rtmp[0], h.rtmp_grad, s);
+        grad_to_outer(h, grad_vals_out, s);
+    }
+    return t;
 }
 
 // ------------------------------------------------------------------ A^T for the matvec backward
@@ -561,7 +616,9 @@ Handle *transpose_for_backward(Handle &h, hipStream_t s) {
             hipLaunchKernelGGL(k_column_starts<int32_t>, dim3(grid_of(n + 1)), dim3(kBlock), 0, s,
                                (const uint64_t *)keys, nnz, n, (int32_t *)trp);
         SLA_HIP(hipGetLastError());
-        tr = make_child_dev(h, n, nnz, trp, rp64, tcol, h.tr_map, 0, s);
+        // (a reordered handle's backward goes through its inner handle, so
+        // A^T itself is never reordered)
+        tr = make_child_dev(h, n, nnz, trp, rp64, tcol, h.tr_map, SLA_FLAG_NO_REORDER, s);
     } catch (...) {
         (void)hipFreeAsync(keys, s);
         (void)hipFreeAsync(rowof, s);

@@ -39,8 +39,9 @@ def check(A, r, c, V, n, X, G, dtype):
 
 
 @pytest.mark.parametrize("dtype,B", [(np.float64, 1), (np.float32, 1), (np.float64, 3),
-                                     (np.float32, 8), (np.float64, 4), (np.float64, 6),
-                                     (np.float32, 12), (np.float32, 32)])
+                                     (np.float32, 8), (np.float64, 2), (np.float32, 4),
+                                     (np.float64, 4), (np.float64, 6), (np.float32, 12),
+                                     (np.float32, 32)])
 def test_unsymmetric_irregular(dtype, B):
     n = 40009
     lengths = np.random.default_rng(5).integers(0, 12, n)
@@ -80,11 +81,14 @@ def test_workload_matrices_and_symmetric_shortcut():
         assert host(gx).tobytes() == host(gx2).tobytes()
 
 
-def test_new_values_reach_the_transpose():
+@pytest.mark.parametrize("reorder", [False, True])
+def test_new_values_reach_the_transpose(reorder):
+    # reordered: the backward runs on the inner handle's transpose
     n = 30000
     lengths = np.random.default_rng(12).integers(1, 9, n)
     r, c, v = adversarial.rows_of_lengths(lengths, n, seed=13)
-    A = handle(n, r, c, v)
+    A = handle(n, r, c, v, reorder=reorder)
+    assert A.layout()["reordered"] == reorder
     x = np.random.default_rng(14).standard_normal(n)
     g = np.random.default_rng(15).standard_normal(n)
     check(A, r, c, v, n, x, g, np.float64)            # builds A^T
