@@ -167,3 +167,43 @@ def test_ring_gradient_matches_tile_kernel(case, dtype):
     assert host(buf[:off]).tobytes() == bytes(off * buf.element_size())
     assert host(buf[off + A.nnz:]).tobytes() == bytes((2 - off) * buf.element_size())
     check(A, r, c, v, n, x, g, dtype)
+
+
+@pytest.mark.parametrize("dtype,B", [(np.float64, 1), (np.float32, 1), (np.float64, 2),
+                                     (np.float32, 4)])
+def test_degenerate_patterns(dtype, B):
+    """One entry (n = 1), an empty matrix (nnz = 0: A^T g = 0 and no value
+    gradient), and a 900-row matrix whose only entries are in rows 2, 4 and
+    a 700-entry row 6 (one long row beside short tiles, most rows empty),
+    single and batched (one 16-byte block of systems)."""
+    rng = np.random.default_rng(40)
+    z = np.zeros(0, np.int64)
+    lengths = np.array([0, 0, 3, 0, 1, 0, 700, 0, 0])
+    r9, c9, v9 = adversarial.rows_of_lengths(lengths, 900, seed=3)
+    cases = [(1, np.array([0]), np.array([0]), np.array([2.0])), (5, z, z, np.zeros(0)),
+             (900, r9, c9, v9)]
+    for n, r, c, v in cases:
+        print(f"degenerate backward n={n} nnz={v.size} B={B} {np.dtype(dtype).name}", flush=True)
+        V = np.stack([v * (1.0 + s) for s in range(B)]).astype(dtype) if B > 1 else v.astype(dtype)
+        X = rng.standard_normal((B, n)).astype(dtype)
+        G = rng.standard_normal((B, n)).astype(dtype)
+        if B == 1:
+            X, G = X[0], G[0]
+        A = handle(n, r, c, V)
+        ref = oracle.coo_to_csr(n, r, c, V)
+        gx_o, gv_o = oracle.spmv_backward(ref["row_ptr"], ref["col"], ref["vals"], X, G)
+        gx, gv = A.matvec_backward_raw(dev(X), dev(G))
+        gx, gv = host(gx), host(gv)
+        assert gv.shape == gv_o.shape
+        if v.size == 0:
+            assert not np.any(gx)
+            continue
+        tol = 1e-12 if dtype == np.float64 else 1e-5
+        for s in range(B):
+            a, o = np.atleast_2d(gx)[s], np.atleast_2d(gx_o)[s]
+            assert np.linalg.norm(a - o) <= tol * np.linalg.norm(o), s
+            ga, go = np.atleast_2d(gv)[s], np.atleast_2d(gv_o)[s]
+            if dtype == np.float64:
+                assert np.array_equal(ga, go)
+            else:
+                assert np.all(np.abs(ga - go) <= 2 ** -23 * np.abs(go))
