@@ -371,6 +371,9 @@ void set_option(Handle *h, int32_t key, int64_t value) {
             fail(SLA_ERR_INVALID_ARG, "unknown option");
     }
     if (h->inner) set_option(h->inner, key, value);
+    // A^T (the matvec backward, the BiCGStab adjoint) runs under A's options;
+    // its launches are not profiled, so A's per-kernel figures stay A's
+    if (h->tr && key != SLA_OPT_PROFILE) set_option(h->tr, key, value);
 }
 }  // namespace
 }  // namespace sla

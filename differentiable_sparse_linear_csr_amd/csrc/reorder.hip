@@ -630,6 +630,16 @@ Handle *transpose_for_backward(Handle &h, hipStream_t s) {
     SLA_HIP(hipFreeAsync(rowof, s));
     SLA_HIP(hipFreeAsync(tcol, s));
     SLA_HIP(hipFreeAsync(trp, s));
+    // A^T runs under the options set on A (set_option reaches it from now
+    // on), profiling aside
+    tr->check_k = h.check_k;
+    tr->use_graph = h.use_graph;
+    tr->res_mode = h.res_mode;
+    tr->res_coop = h.res_coop;
+    tr->spin_limit = h.spin_limit;
+    tr->spmv_ring = h.spmv_ring;
+    tr->fold_direction = h.fold_direction;
+    tr->fuse_update = h.fuse_update;
     h.tr = tr;
     h.tr_stale = false;
     return h.tr;

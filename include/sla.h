@@ -262,6 +262,11 @@ sla_status sla_csr_get_values(sla_csr h, void *values_out, void *stream);
 sla_status sla_csr_gather_to_input(sla_csr h, const void *csr_order, void *input_order,
                                    void *stream);
 
+/* Set one option (SLA_OPT_*) on the handle. It also applies to the kernels
+ * the handle runs on its behalf: the reordered solver handle and the A^T
+ * built for sla_spmv_backward / sla_bicgstab_adjoint (profiling aside: A^T's
+ * launches are not profiled). Unknown keys and out-of-range values return
+ * SLA_ERR_INVALID_ARG. */
 sla_status sla_csr_set_option(sla_csr h, int32_t key, int64_t value);
 
 /* Sparse matrix-vector product y = A x for every batch member (.matvec).

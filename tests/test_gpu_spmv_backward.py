@@ -207,3 +207,31 @@ def test_degenerate_patterns(dtype, B):
                 assert np.array_equal(ga, go)
             else:
                 assert np.all(np.abs(ga - go) <= 2 ** -23 * np.abs(go))
+
+
+def test_options_with_the_transpose():
+    """Options set on A after A^T is built (they are passed on to it) and
+    before (A^T starts with them): A^T g stays bitwise what the ring form
+    gives (the one-tile-ahead form has the same tiles and sums) and matches
+    the oracle."""
+    from differentiable_sparse_linear_csr_amd import _lib
+    w = make_workload("poisson2d_11548", size=300)
+    n = w.n
+    r = np.repeat(np.arange(n), np.diff(w.row_ptr))
+    rng = np.random.default_rng(50)
+    v = w.vals * (1.0 + 0.1 * rng.random(w.vals.size))     # unsymmetric values
+    A = handle(n, r, w.cols, v)
+    x, g = dev(rng.standard_normal(n)), dev(rng.standard_normal(n))
+    gx_ring, _ = A.matvec_backward_raw(x, g, want_vals=False)     # builds A^T
+    A.set_option(_lib.SLA_OPT_SPMV_RING, 0)
+    gx_one, _ = A.matvec_backward_raw(x, g, want_vals=False)
+    A.set_option(_lib.SLA_OPT_SPMV_RING, 1)
+    assert host(gx_one).tobytes() == host(gx_ring).tobytes()
+    B = handle(n, r, w.cols, v)
+    B.set_option(_lib.SLA_OPT_SPMV_RING, 0)                       # before A^T exists
+    B.set_option(_lib.SLA_OPT_CHECK_INTERVAL, 3)
+    gx_b, _ = B.matvec_backward_raw(x, g, want_vals=False)
+    assert host(gx_b).tobytes() == host(gx_ring).tobytes()
+    ref = oracle.coo_to_csr(n, r, w.cols, v)
+    gx_o, _ = oracle.spmv_backward(ref["row_ptr"], ref["col"], ref["vals"], host(x), host(g))
+    assert rel(host(gx_ring), gx_o) <= 1e-12
