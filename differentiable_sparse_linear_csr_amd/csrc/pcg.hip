@@ -1113,13 +1113,15 @@ __global__ __launch_bounds__(kBlock) void k_grad_tile(const TileDesc *__restrict
 // gathers two tiles ahead, so that each wait leaves the later tiles' loads
 // in flight (memory operations complete in issue order); the stores of a
 // tile go out before the loads it refills. Lanes whose group lies inside the
-// tile store it whole, past the caches. On the 133M-row Poisson matrix (5.3 GB
-// of gradient) it took 2.21 ms against 3.13 for k_grad_tile (one run);
-// streaming the whole-group stores took it from 2.80 to 2.48 ms (another
-// run), while six or eight slots with gathers three or four tiles ahead, or
-// eight workgroups per CU, were no faster. The walk over the tiles (a contiguous share per XCD,
-// band-aligned when the band fits the grid) is the ring SpMV's. Same values
-// as k_grad_tile, bit for bit.
+// tile store it whole, past the caches; the group a tile shares with its
+// neighbour is stored through them, so that L2 merges its line. The walk
+// over the tiles (a contiguous share per XCD, band-aligned when the band
+// fits the grid) is the ring SpMV's. Same values as k_grad_tile, bit for
+// bit. On the 133M-row Poisson matrix (5.3 GB of gradient) it took 2.21 ms
+// against 3.13 for k_grad_tile (one run); streaming the whole-group stores
+// took it from 2.80 to 2.48 ms (another run), while six or eight slots with
+// gathers three or four tiles ahead, or eight workgroups per CU, were no
+// faster.
 constexpr int kGradRing = 4;
 // four values as streaming (non-temporal) stores: the gradient is written
 // once and not read back by the kernel, so its lines need not displace the
