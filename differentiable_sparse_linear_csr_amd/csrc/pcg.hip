@@ -1284,20 +1284,25 @@ int64_t grad_ring_resident(int device) {
     return r;
 }
 
-// 16 bytes of a row of an internal [n][B] vector (16-byte aligned)
-__device__ __forceinline__ void load16(const float *p, float (&o)[4]) {
+// W consecutive values of a row of an internal [n][B] vector: 16 bytes
+// (16-byte aligned) or one value
+__device__ __forceinline__ void loadw(const float *p, float (&o)[4]) {
     const float4 a = *reinterpret_cast<const float4 *>(p);
     o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
 }
-__device__ __forceinline__ void load16(const double *p, double (&o)[2]) {
+__device__ __forceinline__ void loadw(const double *p, double (&o)[2]) {
     const double2 a = *reinterpret_cast<const double2 *>(p);
     o[0] = a.x; o[1] = a.y;
 }
+template <typename T>
+__device__ __forceinline__ void loadw(const T *p, T (&o)[1]) {
+    o[0] = *p;
+}
 
-// The same gradient for a batch whose systems fill 16-byte blocks (B a
-// multiple of W = 16 / sizeof(T); lambda and x in the internal [n][B]
-// layout): lanes are (entry e of a run of EL consecutive entries, block q of
-// W systems), so one 16-byte load brings W systems of x at the entry's
+// The same gradient for a batch (lambda and x in the internal [n][B]
+// layout), in blocks of W systems: W = 16 / sizeof(T) when B is a multiple
+// of it, else 1. Lanes are (entry e of a run of EL consecutive entries,
+// block q of W systems), so one load brings W systems of x at the entry's
 // column (and of lambda at its row), a load instruction touches at most EL
 // cache lines (against 64 when each lane gathers one system of its own
 // entry), and the EL lanes of a block write EL consecutive entries of each
@@ -1305,7 +1310,7 @@ __device__ __forceinline__ void load16(const double *p, double (&o)[2]) {
 // covering blocks h QL .. h QL + QL - 1, so that a batch gives NQ / QL times
 // as many wavefronts as tiles; entries go four runs at a time (loads first).
 // Same values as k_grad_tile, bit for bit.
-template <typename T, int QLOG>
+template <typename T, int QLOG, int W>
 __global__ __launch_bounds__(kBlock) void k_grad_tile_bq(const TileDesc *__restrict__ tiles,
                                                          int64_t ntiles,
                                                          const uint16_t *__restrict__ roff16,
@@ -1314,7 +1319,6 @@ __global__ __launch_bounds__(kBlock) void k_grad_tile_bq(const TileDesc *__restr
                                                          int64_t nnz, int B, const T *__restrict__ lam,
                                                          const T *__restrict__ x,
                                                          T *__restrict__ grad, double sign) {
-    constexpr int W = 16 / sizeof(T);
     constexpr int QL = 1 << QLOG;
     constexpr int EL = 64 / QL;
     constexpr int U = 4;
@@ -1355,8 +1359,8 @@ __global__ __launch_bounds__(kBlock) void k_grad_tile_bq(const TileDesc *__restr
                     const int64_t k = d.k0 + kk;
                     const int64_t c = d.narrow ? (int64_t)d.cbase + col16[k] : (int64_t)col[k];
                     const int64_t i = d.rs + rowid[kk];
-                    load16(xq + c * B, xv[u]);
-                    load16(lq + i * B, lv[u]);
+                    loadw(xq + c * B, xv[u]);
+                    loadw(lq + i * B, lv[u]);
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
@@ -1836,14 +1840,18 @@ void grad_vals(Handle &h, const void *lam_internal, const void *x_user, void *gr
                                (const TileDesc *)h.tiles, h.ntiles, (const uint16_t *)h.roff16,
                                (const uint16_t *)h.col16, (const T *)lam_internal,
                                (const T *)x_int, (T *)grad, sign, vec, h.band_l, h.band_p);
-        } else if (h.ntiles > 0 && h.B > 1 && h.B % (16 / (int)sizeof(T)) == 0) {
-            const int nq = h.B / (16 / (int)sizeof(T));
+        } else if (h.ntiles > 0 && h.B > 1) {
+            constexpr int W16 = 16 / (int)sizeof(T);
+            const bool wide = h.B % W16 == 0;
+            const int nq = wide ? h.B / W16 : h.B;
             const int qlog = nq >= 4 ? 2 : nq >= 2 ? 1 : 0;
             const int np = (nq + (1 << qlog) - 1) >> qlog;
             int64_t g = (h.ntiles * np + kWaves - 1) / kWaves;
             if (g > 4 * kMaxGrid) g = 4 * kMaxGrid;
-            auto kern = qlog == 2 ? k_grad_tile_bq<T, 2>
-                                  : qlog == 1 ? k_grad_tile_bq<T, 1> : k_grad_tile_bq<T, 0>;
+            auto kern = wide ? (qlog == 2   ? k_grad_tile_bq<T, 2, W16>
+                                : qlog == 1 ? k_grad_tile_bq<T, 1, W16>
+                                            : k_grad_tile_bq<T, 0, W16>)
+                             : (qlog == 2 ? k_grad_tile_bq<T, 2, 1> : k_grad_tile_bq<T, 1, 1>);
             hipLaunchKernelGGL(kern, dim3((unsigned)g), dim3(kBlock), 0, s,
                                (const TileDesc *)h.tiles, h.ntiles, (const uint16_t *)h.roff16,
                                (const int32_t *)h.col, (const uint16_t *)h.col16, h.nnz, h.B,

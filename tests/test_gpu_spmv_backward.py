@@ -3,7 +3,8 @@ spmv_backward: A^T g normwise within 1e-12 (fp64) / 1e-5 (fp32) like the
 forward SpMV, grad_vals[k] = g[row k] x[col k] bit-exact in fp64 (one rounded
 product, the same on both sides) and within one fp32 rounding otherwise.
 Covers unsymmetric irregular patterns with empty and long rows, batches (B a
-multiple of the 16-byte system block or not; 1, 2, 3 and 8 blocks), the
+multiple of the 16-byte system block, 1, 2, 3 and 8 blocks, or not: blocks of
+one system), the
 reordered solver, the symmetric-flag shortcut, new values after the first
 backward, and autograd through SparseCSR.mv with duplicated COO input."""
 import numpy as np
@@ -41,7 +42,7 @@ def check(A, r, c, V, n, X, G, dtype):
 @pytest.mark.parametrize("dtype,B", [(np.float64, 1), (np.float32, 1), (np.float64, 3),
                                      (np.float32, 8), (np.float64, 2), (np.float32, 4),
                                      (np.float64, 4), (np.float64, 6), (np.float32, 12),
-                                     (np.float32, 32)])
+                                     (np.float32, 32), (np.float32, 3), (np.float64, 5)])
 def test_unsymmetric_irregular(dtype, B):
     n = 40009
     lengths = np.random.default_rng(5).integers(0, 12, n)
