@@ -36,6 +36,7 @@ SLA_OPT_COOPERATIVE = 6
 SLA_OPT_SPIN_LIMIT = 7
 SLA_OPT_SPMV_RING = 8
 SLA_OPT_FOLD_DIRECTION = 9
+SLA_OPT_RESIDENT_WALK = 10
 SLA_PATH_NONE, SLA_PATH_SINGLE_KERNEL, SLA_PATH_PER_STEP = 0, 1, 2
 SLA_FALLBACK_COOPERATIVE_REFUSED, SLA_FALLBACK_WAIT_TIMED_OUT = 1, 2
 KERNELS = {"spmv_dot": 0, "update": 1, "direction": 2, "init": 3, "spmv": 4, "grad": 5,

@@ -367,6 +367,10 @@ void set_option(Handle *h, int32_t key, int64_t value) {
             if (h->fuse_update != (value != 0)) drop_graphs(*h);
             h->fuse_update = value != 0;
             break;
+        case SLA_OPT_RESIDENT_WALK:
+            if (value < 0 || value > 2) fail(SLA_ERR_INVALID_ARG, "resident walk in [0, 2]");
+            h->res_walk = (int)value;
+            break;
         default:
             fail(SLA_ERR_INVALID_ARG, "unknown option");
     }

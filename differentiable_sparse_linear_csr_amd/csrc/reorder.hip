@@ -636,6 +636,7 @@ Handle *transpose_for_backward(Handle &h, hipStream_t s) {
     tr->use_graph = h.use_graph;
     tr->res_mode = h.res_mode;
     tr->res_coop = h.res_coop;
+    tr->res_walk = h.res_walk;
     tr->spin_limit = h.spin_limit;
     tr->spmv_ring = h.spmv_ring;
     tr->fold_direction = h.fold_direction;

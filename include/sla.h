@@ -135,7 +135,7 @@ enum {
                                    (sla_spmv_backward, the adjoints) follows the same
                                    setting: four tiles ahead, or one tile per wavefront;
                                    bitwise equal too. */
-    SLA_OPT_FOLD_DIRECTION = 9  /* 1 (default): a per-step PCG solve with fp64 values, of a
+    SLA_OPT_FOLD_DIRECTION = 9, /* 1 (default): a per-step PCG solve with fp64 values, of a
                                    single system on such tiles (no row longer than 128
                                    entries) or of a batch whose B / (16 / value bytes) is a
                                    power of two, that is too large for the fused update
@@ -146,6 +146,15 @@ enum {
                                    passes fewer per iteration; the same recurrence, z
                                    rounded once more in fp64. 0: three kernels. fp32
                                    values never fold (z would add an fp32 rounding). */
+    SLA_OPT_RESIDENT_WALK = 10  /* the single-kernel solve's SpMV phase: 2 (default) picks by
+                                   matrix size, 0 and 1 force a form. 0: each wavefront sums
+                                   a contiguous run of its workgroup's tiles; 1: the
+                                   workgroup's tiles interleaved over its wavefronts (w, w + 8,
+                                   ...), so that a CU reads one stretch of the matrix at a
+                                   time. Automatic: interleaved when the values and column
+                                   indices exceed the 256 MB Infinity Cache (the matrix then
+                                   streams from HBM), else contiguous. Same tiles, same sums,
+                                   bitwise equal results. */
 };
 
 /* How the last sla_pcg_solve / sla_adjoint_backward / BiCGStab call on a

@@ -721,3 +721,43 @@ def test_folded_direction_on_reordered_handle():
     gb, gv, ainfo = A.adjoint_raw(x, dev(g), tol, 20000)
     assert abs(ainfo.iterations[0] - ita) <= 2
     assert rel(host(gb), lam) <= 1e-8 and rel(host(gv), gvo) <= 1e-8
+
+
+@pytest.mark.parametrize("case", ["diffusion3d_64", "knn_300k", "batched_fp32_b4"])
+def test_single_kernel_walks_bitwise_equal(case):
+    """SLA_OPT_RESIDENT_WALK: the single-kernel solve's SpMV phase with each
+    wavefront on a contiguous run of its workgroup's tiles (0) and with the
+    tiles interleaved over the wavefronts (1): the same tiles and sums, so
+    bitwise equal solutions, iteration counts and adjoint gradients; and the
+    solution against the oracle."""
+    if case == "diffusion3d_64":
+        w = make_workload("diffusion3d_128", size=64)
+        r, c, v, b, g = w.rows, w.cols, w.vals, w.b, w.g
+    elif case == "knn_300k":
+        w = make_workload("knn_laplacian_2m", size=300000)
+        r, c, v, b, g = w.rows, w.cols, w.vals, w.b, w.g
+    else:
+        w = make_workload("batched_diffusion2d_512x32", size=128, batch=4)
+        r, c, v, b, g = w.rows, w.cols, w.vals, w.b, w.g
+    print(f"resident walks: {case} n={w.n} nnz={w.nnz} batch={w.batch}", flush=True)
+    A = coo_handle(w.n, r, c, v)
+    out = {}
+    for walk in (0, 1):
+        A.set_option(_lib.SLA_OPT_RESIDENT_WALK, walk)
+        x, info = A.solve_raw(dev(b), w.tol, w.maxit)
+        assert A.last_path()["path"] == "single_kernel"
+        gb, gv, ainfo = A.adjoint_raw(x, dev(g), w.tol, w.maxit)
+        out[walk] = (host(x), list(info.iterations), host(gb), host(gv), list(ainfo.iterations))
+    x0, it0, gb0, gv0, ait0 = out[0]
+    x1, it1, gb1, gv1, ait1 = out[1]
+    assert it0 == it1 and ait0 == ait1
+    assert x0.tobytes() == x1.tobytes()
+    assert gb0.tobytes() == gb1.tobytes() and gv0.tobytes() == gv1.tobytes()
+    ref = oracle.coo_to_csr(w.n, r, c, v)
+    xo, *_ = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, w.tol, w.maxit)
+    tol = 1e-8 if w.dtype == "f64" else 1e-3
+    for s in range(w.batch):
+        assert rel(np.atleast_2d(x1)[s], np.atleast_2d(xo)[s]) <= tol
+    A.set_option(_lib.SLA_OPT_RESIDENT_WALK, 2)
+    with pytest.raises(SlaError):
+        A.set_option(_lib.SLA_OPT_RESIDENT_WALK, 3)
