@@ -631,10 +631,12 @@ static int batched_rows_per_lane(const Handle &h) {
 // as one contiguous run (index and values of an entry are read once for the
 // whole batch). A pass takes kBvRows rows per lane; the loads of a row's
 // first kBvEntries entries are issued together (row pointers, then indices
-// and values, then the gathers), longer rows finish in a loop. Workgroups
-// take contiguous row ranges, XCD-contiguous (workgroup b runs on XCD
-// b % 8; consecutive ranges go to the same XCD so stencil neighbours share
-// its L2).
+// and values, then the gathers), longer rows finish in a loop. Each XCD
+// takes a contiguous share of the rows (workgroup b runs on XCD b % 8), so
+// stencil neighbours share its L2, and its X workgroups take that share's
+// passes interleaved (workgroup j: passes j, j + X, ...), so the XCD reads
+// one stretch of the values at a time rather than X of them (on the 512^2 x
+// 32 fp32 batch 47.1 -> 46.4 us, the iteration 0.1217 -> 0.1203 ms).
 constexpr int kBvRows = 2;
 constexpr int kBvEntries = 5;
 
@@ -659,15 +661,18 @@ __global__ __launch_bounds__(kBlock) void k_spmv_bvec(
 #pragma unroll
         for (int k = 0; k < W; ++k) any |= st[s0 + k].status == kRunning;
     }
+    // the XCD's share: X workgroups' rows_block rows (whole passes, so the
+    // shares cover the rows), its passes dealt out in turn
     const int64_t G = gridDim.x;  // a multiple of kXcds
-    const int64_t lb = (int64_t)(blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
-    const int64_t r_begin = lb * rows_block;
-    const int64_t r_end = r_begin + rows_block < n ? r_begin + rows_block : n;
+    const int64_t X = G / kXcds, xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
+    const int64_t pass = (int64_t)J * kBvRows;
+    const int64_t xs = xcd * X * rows_block;
+    const int64_t r_end = xs + X * rows_block < n ? xs + X * rows_block : n;
     double dot[W];
 #pragma unroll
     for (int k = 0; k < W; ++k) dot[k] = 0.0;
     if (any) {
-        for (int64_t r0 = r_begin; r0 < r_end; r0 += (int64_t)J * kBvRows) {
+        for (int64_t r0 = xs + jx * pass; r0 < r_end; r0 += X * pass) {
             int64_t ri[kBvRows], ka[kBvRows], kb[kBvRows];
 #pragma unroll
             for (int u = 0; u < kBvRows; ++u) {
