@@ -19,7 +19,8 @@ minutes for. There its first 25 iterations are compared whole at 1e-12
 against the oracle's first 25, and the 500-iteration solve against the
 oracle's stored statistics (tests/golden/poisson2d_11548.json, written by
 tests/golden/make_golden.py): norm, seeded samples and projections, which are
-necessary conditions of a normwise bound.
+necessary conditions of a normwise bound. Its matvec backward is compared
+whole (the value gradient bit for bit).
 """
 import json
 import os
@@ -202,6 +203,33 @@ def test_full_size_133m_500_iterations():
     # only through the order of the row sums and reductions
     assert abs(info.rel_residual[0] - fr["rel_residual"]) <= 1e-6 * fr["rel_residual"]
     check_vector_stats(host(x), fr, 1e-8)
+
+
+def test_full_size_133m_matvec_backward():
+    """The matvec backward at 133M rows (int64 row pointers, band-aligned ring
+    tiles, 5.3 GB of value gradient) against the oracle's on the same seeded
+    x and g: g_i x_j bit for bit (one rounded product on both sides), A^T g
+    (the transposed child built on the device) normwise within 1e-12."""
+    name = "poisson2d_11548"
+    _cache.clear()
+    w = make_workload(name)
+    rp, col, vals = oracle_csr(w)
+    A = handle(w)
+    assert A.layout()["ring_tiles"]
+    x = np.random.default_rng(71).standard_normal(w.n)
+    g = np.random.default_rng(72).standard_normal(w.n)
+    print(f"full-size {name}: GPU matvec backward, nnz={w.nnz}", flush=True)
+    gx, gv = A.matvec_backward_raw(dev(x), dev(g))
+    gx, gv = host(gx), host(gv)
+    del A
+    torch.cuda.empty_cache()
+    print(f"full-size {name}: oracle matvec backward ({oracle.num_threads()} threads)", flush=True)
+    gx_o, gv_o = oracle.spmv_backward(rp, col, vals, x, g)
+    compare("A^T g", gx, gx_o, 1e-12)
+    assert gv.shape == gv_o.shape
+    nbad = int(np.count_nonzero(gv != gv_o))
+    print(f"    grad_vals: {nbad} of {gv.size} entries differ from the oracle's bits", flush=True)
+    assert nbad == 0
 
 
 def test_full_size_list_against_oracle():
