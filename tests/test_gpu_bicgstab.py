@@ -147,13 +147,16 @@ def test_zero_rhs_zero_budget_and_errors():
 
 
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
-def test_adjoint_iterates_match_oracle(dtype):
+@pytest.mark.parametrize("reorder", [False, True])
+def test_adjoint_iterates_match_oracle(dtype, reorder):
+    # reordered: A^T lambda = g is solved on the inner handle's transpose
     n, r, c, v = (30001,) + irregular(30001, 60)
     v = v.astype(dtype)
     ref = oracle.coo_to_csr(n, r, c, v)
     b = np.random.default_rng(53).standard_normal(n).astype(dtype)
     g = np.random.default_rng(54).standard_normal(n).astype(dtype)
-    A = handle(n, r, c, v)
+    A = handle(n, r, c, v, reorder=reorder)
+    assert A.layout()["reordered"] == reorder
     x, _ = A.solve_raw(dev(b), 1e-6, 30, method="bicgstab")
     X = host(x)
     tol = 1e-9 if dtype == np.float64 else 1e-4
@@ -194,10 +197,13 @@ def test_autograd_converged_against_oracle_and_new_values():
         assert rel(host(gvals), gvo[ref["slot"]]) <= 1e-7, step
 
 
-def test_symmetric_handle_solves_its_own_adjoint():
+@pytest.mark.parametrize("reorder", [False, True])
+def test_symmetric_handle_solves_its_own_adjoint(reorder):
+    # reordered: the inner handle solves its own adjoint
     rp, cp, vp = poisson2d_coo(90)
     n = 8100
-    A = handle(n, rp, cp, vp, check_symmetric=True)
+    A = handle(n, rp, cp, vp, check_symmetric=True, reorder=reorder)
+    assert A.layout()["reordered"] == reorder
     ref = oracle.coo_to_csr(n, rp, cp, vp)
     b = np.random.default_rng(59).standard_normal(n)
     g = np.random.default_rng(60).standard_normal(n)
