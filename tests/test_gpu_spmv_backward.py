@@ -116,7 +116,8 @@ def test_autograd_through_mv_with_duplicates():
     assert np.array_equal(host(gvals), gv_o[ref["slot"]])
 
 
-@pytest.mark.parametrize("case", ["poisson2d_1100", "diffusion3d_40", "banded_irregular", "tiny"])
+@pytest.mark.parametrize("case", ["poisson2d_1100", "diffusion3d_40", "banded_irregular",
+                                  "banded_long_rows", "tiny"])
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
 def test_ring_gradient_matches_tile_kernel(case, dtype):
     """The value gradient in the ring form (single system, every tile small
@@ -137,6 +138,21 @@ def test_ring_gradient_matches_tile_kernel(case, dtype):
     elif case == "banded_irregular":
         n = 300000
         r, c, v = banded_irregular(n, 7)
+    elif case == "banded_long_rows":
+        # two rows past the tile limit (one workgroup each) among ring tiles
+        n = 200000
+        r, c, v = banded_irregular(n, 8)
+        rng = np.random.default_rng(9)
+        extra = []
+        for row, m in ((1234, 200), (150001, 129)):
+            cols = np.setdiff1d(np.unique(np.clip(row + rng.integers(-1500, 1501, 3 * m), 0,
+                                                  n - 1)), c[r == row])[:m]
+            extra.append((np.full(cols.size, row), cols, rng.standard_normal(cols.size)))
+        r = np.concatenate([r] + [e[0] for e in extra])
+        c = np.concatenate([c] + [e[1] for e in extra])
+        v = np.concatenate([v] + [e[2] for e in extra])
+        order = np.lexsort((c, r))
+        r, c, v = r[order], c[order], v[order]
     else:
         n = 10
         i = np.arange(n)
