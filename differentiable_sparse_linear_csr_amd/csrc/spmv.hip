@@ -975,7 +975,20 @@ int64_t spmv_grid(const Handle &h) {
         int64_t g = (blocks + kXcds - 1) / kXcds * kXcds;         // multiple of the XCD count
         if (g < kXcds) g = kXcds;
         const int64_t res = use_ring(h) ? h.ring_resident : h.spmv_resident;
-        return g < res ? g : res;
+        g = g < res ? g : res;
+        // Band-aligned tiles under the ring SpMV: one panel per XCD. The grid
+        // keeps band_l wavefronts per XCD, so the plain walk (wavefront w:
+        // tiles T0 + w, T0 + w + band_l, ...) is the band walk over the XCD's
+        // whole range, one band after the other: the p lines a tile gathers
+        // near +N are used again one and two steps later while only one band
+        // of rows per XCD streams in between (with band_p panels side by
+        // side, band_p bands' entries and gathers pass through the L2 in that
+        // time). On the 133M-row Poisson matrix, 2 panels -> 1: folded SpMV
+        // 2.82 -> 2.74 ms.
+        if (use_ring(h) && h.band_p > 1 && g % kXcds == 0 && (g / kXcds) % h.band_p == 0 &&
+            g / kXcds / h.band_p * kWaves == h.band_l)
+            g /= h.band_p;
+        return g;
     }
     return h.vt == SLA_F64 ? batched_grid_t<double>(h) : batched_grid_t<float>(h);
 }
