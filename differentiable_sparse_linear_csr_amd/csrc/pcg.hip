@@ -1835,6 +1835,11 @@ void grad_vals(Handle &h, const void *lam_internal, const void *x_user, void *gr
             g = (g + kXcds - 1) / kXcds * kXcds;
             const int64_t res = grad_ring_resident<T>(h.device);
             if (g > res) g = res;
+            // band-aligned tiles: band_l wavefronts per XCD walk its whole
+            // range band by band (one panel, as the ring SpMV does)
+            if (h.band_l > 0 && h.band_l % kWaves == 0 && g % kXcds == 0 &&
+                g / kXcds * kWaves > h.band_l)
+                g = h.band_l / kWaves * kXcds;
             const int vec = ((uintptr_t)grad % 16) == 0;
             hipLaunchKernelGGL(k_grad_ring<T>, dim3((unsigned)g), dim3(kBlock), kGradLdsPad, s,
                                (const TileDesc *)h.tiles, h.ntiles, (const uint16_t *)h.roff16,
