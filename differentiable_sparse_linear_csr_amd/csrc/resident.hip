@@ -10,7 +10,8 @@
 // its LDS slice for the whole solve (lane l holds rows R0 + l + 64 j). Per
 // iteration:
 //   A   q = A p over the workgroup's tiles (each wavefront a run of them,
-//       weighted by the SIMD slot it holds), gathering p from a global copy,
+//       weighted by the SIMD slot it holds, walked backwards on every other
+//       iteration), gathering p from a global copy,
 //       with kRD tiles in flight (the entries of the next tiles and the
 //       gathers of the tile two on are loading while a tile is summed); q
 //       goes to the LDS slot of its rows' owner; p.q from registers and LDS
@@ -488,6 +489,18 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
+        }
+        // The tiles are walked forwards and backwards on alternate
+        // iterations, so that each SpMV phase starts on the lines the last
+        // one read most recently, which the Infinity Cache may still hold
+        // where the whole matrix does not fit it (on the 2M-point kNN
+        // matrix, 378 MB as held here: 110 -> 95 us per iteration; at 2.1M
+        // rows of 3D diffusion, which fits, 0.3-1 us less of ~40). Each
+        // tile's sums do not depend on the order: the results are the same
+        // bits.
+        if (nt > 0) {
+            t0 += (nt - 1) * ts;
+            ts = -ts;
         }
         fetch_head();
         // q rows summed by other wavefronts
