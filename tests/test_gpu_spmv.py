@@ -154,6 +154,23 @@ def test_band_aligned_tiles(name, size, dtype):
     assert rel(host(xg), xo) <= tol, rel(host(xg), xo)
 
 
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_band_aligned_tiles_bicgstab(dtype):
+    """BiCGStab's two fused SpMVs on band-aligned tiles (the 4100^2 Poisson
+    matrix, one panel per XCD): 12 steps (tol 0) against the oracle's."""
+    w = make_workload("poisson2d_11548", size=4100)
+    rows = np.repeat(np.arange(w.n), np.diff(w.row_ptr))
+    v = w.vals.astype(dtype)
+    b = w.b.astype(dtype)
+    print(f"band-aligned bicgstab n={w.n} {np.dtype(dtype).name}", flush=True)
+    A = coo_handle(w.n, rows, w.cols, v)
+    ref = oracle.coo_to_csr(w.n, rows, w.cols, v)
+    xg, info = A.solve_raw(dev(b), 0.0, 12, method="bicgstab")
+    xo, *_ = oracle.bicgstab(ref["row_ptr"], ref["col"], ref["vals"], b, 0.0, 12)
+    tol = 1e-9 if dtype == np.float64 else 1e-4
+    assert rel(host(xg), xo) <= tol, rel(host(xg), xo)
+
+
 def banded_irregular(n, seed):
     """Rows of 3 to 7 entries (one row in 50 empty) at columns within 2000 of
     the diagonal: every SpMV tile small and narrow, row lengths ragged."""
