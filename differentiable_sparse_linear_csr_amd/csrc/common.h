@@ -44,6 +44,7 @@ struct SysState {
     double alpha;   // step of the current iteration
     double beta;    // direction update factor
     double rr;      // ||r||^2 of the last updated residual
+    double alpha2;  // folded single-system solve: the step before alpha (0 when none)
     int32_t iter;   // completed iterations
     int32_t status; // kRunning or sla_outcome
 };

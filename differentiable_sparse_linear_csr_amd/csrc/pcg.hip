@@ -95,6 +95,7 @@ __global__ __launch_bounds__(kBlock) void k_init(int64_t n, int B, const T *__re
             s.bb = tot[b];
             s.rho = tot[B + b];
             s.alpha = 0.0;
+            s.alpha2 = 0.0;
             s.beta = 0.0;
             s.rr = s.bb;
             s.iter = 0;
@@ -689,7 +690,12 @@ __global__ __launch_bounds__(kBlock) void k_update1(int64_t n, T *__restrict__ x
             const double rz = tot[0], rr = tot[1];
             int running = 0;
             sy.iter += 1;
-            if (FOLD) sy.alpha = alpha;   // x += alpha p is applied later (0 at breakdown)
+            if (FOLD) {
+                // x += alpha p is applied later (0 at breakdown), together
+                // with the step before where that one is still pending
+                sy.alpha2 = sy.alpha;
+                sy.alpha = alpha;
+            }
             if (breakdown) {
                 sy.status = SLA_BREAKDOWN;  // x, r untouched; rr keeps the last residual
             } else {
@@ -910,28 +916,45 @@ __global__ __launch_bounds__(kBlock) void k_direction1(int64_t n, const T *__res
     }
 }
 
-// End of a folded solve: the last update's step x += alpha p (p = the
-// direction the last SpMV formed, p[iter & 1]), which no later SpMV applied.
+// End of a single-system folded solve: the steps no SpMV applied to x, in
+// their order: for an odd count K of updates (the last SpMV skipped x),
+// alpha2 p_(K-1) (in p[(K - 1) & 1]), then the last update's alpha p_K (the
+// direction the last SpMV formed, p[K & 1]).
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_fold_finish(int64_t n, T *__restrict__ x,
                                                         const T *__restrict__ p0,
                                                         const T *__restrict__ p1,
                                                         const SysState *__restrict__ st) {
     constexpr int W = VecW<T>::W;
-    const double alpha = st[0].alpha;
-    if (alpha == 0.0) return;
-    const T *p = (st[0].iter & 1) ? p1 : p0;
+    // pending: alpha p_K (K = st.iter, its direction in p[K & 1]) and, for
+    // an odd K (the last SpMV did not update x), alpha2 p_(K-1) before it
+    const int32_t K = st[0].iter;
+    const double alpha = st[0].alpha, alpha2 = (K & 1) ? st[0].alpha2 : 0.0;
+    if (alpha == 0.0 && alpha2 == 0.0) return;
+    const T *p = (K & 1) ? p1 : p0;
+    const T *pp = (K & 1) ? p0 : p1;
+    auto upd = [&](T xv, T pv, T ppv) {
+        if (alpha2 != 0.0) xv = (T)((double)xv + alpha2 * (double)ppv);
+        if (alpha != 0.0) xv = (T)((double)xv + alpha * (double)pv);
+        return xv;
+    };
     const int tid = threadIdx.x;
     const int64_t ng = n / W;
     const int64_t per_pass = (int64_t)kBlock * kVecGroups;
     for (int64_t g0 = (int64_t)blockIdx.x * per_pass; g0 < ng; g0 += (int64_t)gridDim.x * per_pass) {
-        T xv[kVecGroups][W], pv[kVecGroups][W];
+        T xv[kVecGroups][W], pv[kVecGroups][W], ppv[kVecGroups][W];
 #pragma unroll
         for (int u = 0; u < kVecGroups; ++u) {
             const int64_t g = g0 + u * kBlock + tid;
             if (g < ng) {
                 vload(x + g * W, xv[u]);
                 vload(p + g * W, pv[u]);
+                if (alpha2 != 0.0) {
+                    vload(pp + g * W, ppv[u]);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < W; ++k) ppv[u][k] = (T)0;
+                }
             }
         }
 #pragma unroll
@@ -939,14 +962,14 @@ __global__ __launch_bounds__(kBlock) void k_fold_finish(int64_t n, T *__restrict
             const int64_t g = g0 + u * kBlock + tid;
             if (g < ng) {
 #pragma unroll
-                for (int k = 0; k < W; ++k) xv[u][k] = (T)((double)xv[u][k] + alpha * (double)pv[u][k]);
+                for (int k = 0; k < W; ++k) xv[u][k] = upd(xv[u][k], pv[u][k], ppv[u][k]);
                 vstore(x + g * W, xv[u]);
             }
         }
     }
     if (blockIdx.x == 0 && tid < n - ng * W) {
         const int64_t i = ng * W + tid;
-        x[i] = (T)((double)x[i] + alpha * (double)p[i]);
+        x[i] = upd(x[i], p[i], alpha2 != 0.0 ? pp[i] : (T)0);
     }
 }
 

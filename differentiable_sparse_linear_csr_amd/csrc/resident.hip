@@ -579,6 +579,7 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
         s.bb = bb;
         s.rho = rho;
         s.alpha = alpha;
+        s.alpha2 = 0.0;
         s.beta = beta;
         s.rr = rrv;
         s.iter = iter;

@@ -141,6 +141,7 @@ __global__ __launch_bounds__(kBlock) void k_seg_init(Seg g, const T *__restrict_
         s.bb = tot[0];
         s.rho = tot[1];
         s.alpha = 0.0;
+        s.alpha2 = 0.0;
         s.beta = 0.0;
         s.rr = s.bb;
         s.iter = 0;

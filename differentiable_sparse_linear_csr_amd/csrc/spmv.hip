@@ -377,14 +377,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         return u;
     };
     double dot = 0.0, dot2 = 0.0;
-    // folded form: the gathers read z and p_old; x is updated in place
-    double beta = 0.0, ax = 0.0;
+    // folded form: the gathers read z and p_old; x is updated in place on
+    // every other launch (xstep: an odd count of completed updates), with
+    // the two steps pending since the last such launch, in their order:
+    // alpha2 p_old2 (the step before, its direction still in the buffer
+    // p_new is about to take) and alpha p_old. Each step rounds x as it
+    // would on its own, so x takes the same values as when updated on every
+    // launch, and the x stream (read and write, 16 bytes a row) is replaced
+    // by 12 bytes a row on average.
+    double beta = 0.0, ax = 0.0, ax2 = 0.0;
+    bool xstep = false;
     const T *zz = nullptr, *pold = nullptr;
     T *pnew = nullptr, *xx = nullptr;
     if (FOLD) {
         const SysState s0 = *fa.st;
         beta = s0.beta;
         ax = s0.alpha;
+        ax2 = s0.alpha2;
+        xstep = (s0.iter & 1) != 0;
         const int par = s0.iter & 1;
         zz = (const T *)fa.z;
         pold = (const T *)fa.p[par];
@@ -405,7 +415,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     // (gathered with the columns) and x of it (fetched with the entries: it
     // is read nowhere else, so it comes from HBM)
     double pg[FOLD ? 2 : 1][4];
-    T oz[FOLD ? 2 : 1], op[FOLD ? 2 : 1], s_x[FOLD ? kRing : 1];
+    T oz[FOLD ? 2 : 1], op[FOLD ? 2 : 1], op2[FOLD ? 2 : 1], s_x[FOLD ? kRing : 1];
     t_next = next_live(t_next);
     TileDesc dn{0, 0, 0, 0, 0, 0, 0};
     if (t_next < t_end) dn = tiles[t_next];
@@ -433,7 +443,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         const int nr = s_nr[u];
         s_ro[u] = (int32_t)roff16[e.rpos + (lane <= nr ? lane : nr)];
         if (FUSED && !FOLD) s_w[u] = w[e.rs + (lane < nr ? lane : 0)];
-        if (FOLD) s_x[FOLD ? u : 0] = xx[e.rs + (lane < nr ? lane : 0)];
+        // (x only where this launch updates it; else every lane reads x[0],
+        // one cached line, so that the load is still always issued)
+        if (FOLD) s_x[FOLD ? u : 0] = xx[xstep ? e.rs + (lane < nr ? lane : 0) : 0];
         if (t_next < t_end) t_next = next_live(t_next + stride);
     };
     // the descriptor of the tile the next fetch takes (scalar loads; issued
@@ -460,6 +472,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
             const int64_t i = s_rs[u] + (lane < s_nr[u] ? lane : 0);
             oz[FOLD ? hb : 0] = zz[i];
             op[FOLD ? hb : 0] = pold[i];
+            op2[FOLD ? hb : 0] = pnew[xstep ? i : 0];   // read before this lane writes it
         }
     };
     // the tile of slot u (gathers in xv[hb]): products, row offsets and w to
@@ -485,8 +498,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
                 if (lane < nrows) {
                     const int hf = FOLD ? hb : 0;
                     const T pn = fold_p<T>((double)oz[hf], (double)op[hf], beta);
+                    if (xstep) {
+                        T xn = s_x[FOLD ? u : 0];
+                        if (ax2 != 0.0) xn = (T)((double)xn + ax2 * (double)op2[hf]);
+                        if (ax != 0.0) xn = (T)((double)xn + ax * (double)op[hf]);
+                        xx[rs + lane] = xn;
+                    }
                     pnew[rs + lane] = pn;
-                    xx[rs + lane] = (T)((double)s_x[FOLD ? u : 0] + ax * (double)op[hf]);
                     pown[lane] = (double)pn;
                 }
             } else if (FUSED && lane < nrows) {
@@ -1134,13 +1152,10 @@ void launch_spmv_fold(Handle &h, hipStream_t s) {
                            (const double *)h.long_dot, h.nlong, h.spart, &h.st[0].status,
                            (const uint8_t *)nullptr, (double *)nullptr, h.band_l, h.band_p, fa);
     };
-    if (h.vt == SLA_F64) {
-        if (h.rp64) go(double(), int64_t());
-        else go(double(), int32_t());
-    } else {
-        if (h.rp64) go(float(), int64_t());
-        else go(float(), int32_t());
-    }
+    // fp32 values never fold (a stored z would add an fp32 rounding)
+    if (h.vt != SLA_F64) fail(SLA_ERR_HIP, "internal: folded direction with fp32 values");
+    if (h.rp64) go(double(), int64_t());
+    else go(double(), int32_t());
     SLA_HIP(hipGetLastError());
 }
 

@@ -590,6 +590,37 @@ def test_folded_direction_matches_oracle_and_three_kernels(name, size, dtype):
     assert rel(host(gv), gv_o) <= 10 * xtol
 
 
+@pytest.mark.parametrize("shift,at", [(0.3, 6), (0.5, 5), (0.7, 4), (1.2, 3), (2.5, 2)])
+def test_folded_direction_breakdown(shift, at):
+    """The folded single-system solve applies x += alpha p on every other
+    SpMV (two pending steps at once) and the rest at the end: a Poisson
+    matrix shifted to be indefinite breaks down at iteration `at` (odd and
+    even counts), where x must hold exactly the steps before the breakdown,
+    as in the oracle."""
+    r, c, v = poisson2d_coo(30)
+    v = v.astype(np.float64).copy()
+    v[r == c] -= shift
+    b = np.random.default_rng(0).standard_normal(900)
+    ref = oracle.coo_to_csr(900, r, c, v)
+    xo, ito, _, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, 1e-10, 400)
+    assert oco == oracle.BREAKDOWN and ito == at
+    A = coo_handle(900, r, c, v)
+    assert A.layout()["ring_tiles"]
+    A.set_option(_lib.SLA_OPT_RESIDENT, 0)
+    A.set_option(_lib.SLA_OPT_FUSED_UPDATE, 0)
+    for graph, interval in ((1, 16), (0, 1), (1, 3)):
+        A.set_option(_lib.SLA_OPT_USE_GRAPH, graph)
+        A.set_option(_lib.SLA_OPT_CHECK_INTERVAL, interval)
+        A.profile_reset()
+        A.set_option(_lib.SLA_OPT_PROFILE, 1)
+        x, info = A.solve_raw(dev(b), 1e-10, 400)
+        prof = A.profile()
+        A.set_option(_lib.SLA_OPT_PROFILE, 0)
+        assert prof["direction"][0] == 0, prof      # folded
+        assert info.status[0] == oracle.BREAKDOWN and info.iterations[0] == at
+        assert rel(host(x), xo) <= 1e-12, (graph, interval, rel(host(x), xo))
+
+
 @pytest.mark.parametrize("dtype,B", [(np.float32, 8), (np.float64, 8), (np.float32, 32),
                                      (np.float64, 4)])
 def test_batched_folded_direction_mixed_outcomes(dtype, B):
