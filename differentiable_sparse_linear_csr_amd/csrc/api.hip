@@ -371,6 +371,9 @@ void set_option(Handle *h, int32_t key, int64_t value) {
             if (value < 0 || value > 2) fail(SLA_ERR_INVALID_ARG, "resident walk in [0, 2]");
             h->res_walk = (int)value;
             break;
+        case SLA_OPT_RESIDENT_DIA:
+            h->res_dia_on = value != 0;
+            break;
         default:
             fail(SLA_ERR_INVALID_ARG, "unknown option");
     }
@@ -603,6 +606,14 @@ sla_status sla_csr_get_last_path(sla_csr hd, int32_t *path, uint32_t *fallbacks)
         const Handle *h = reinterpret_cast<const Handle *>(hd);
         if (path) *path = h->last_path;
         if (fallbacks) *fallbacks = h->last_fallback;
+    });
+}
+
+sla_status sla_csr_get_diagonals(sla_csr hd, int32_t *ndiag) {
+    return guard([&] {
+        const Handle *h = checked(hd);
+        if (h->inner) h = h->inner;
+        if (ndiag) *ndiag = (h->res_state > 0 && h->res_dia_on && h->B == 1) ? h->res_dia_m : 0;
     });
 }
 

@@ -30,6 +30,7 @@ constexpr int kTileCap = kTileUnits + kLongRow;    // max entries of a short til
 constexpr int kMaxGrid = 2048;                     // grid cap of the persistent / grid-stride kernels
 constexpr int kXcds = 8;                           // workgroups go round-robin over 8 XCDs
 constexpr int kMaxBatch = 256;
+constexpr int kDiaMax = 8;   // diagonals of a matrix the single-kernel solve holds by diagonals
 // col and values carry this many spare entries past nnz: the SpMV reads
 // entries in 16-byte groups from a 4-aligned base and may touch (never use)
 // up to 3 entries beyond a tile's end.
@@ -231,6 +232,14 @@ struct Handle {
     bool res_narrow = false;       // every tile's columns span less than 2^16
     bool res_coop = true;          // cooperative launch (else an ordinary one)
     int res_walk = 2;              // SpMV phase: 0 contiguous runs, 1 interleaved, 2 by size
+    // the single system held by diagonals (a pattern with at most kDiaMax
+    // distinct column offsets j - i, little padding): the SpMV phase reads
+    // dia_val[d][row] and p[row + dia_off[d]], no column indices
+    int32_t res_dia_m = 0;         // diagonals (0: tiles)
+    int32_t *res_dia_off = nullptr;  // [m] offsets, ascending (column order)
+    int32_t *res_dia_map = nullptr;  // [nnz] CSR entry -> d * n + row
+    void *res_dia_val = nullptr;     // [m][n], zero where a row has no entry
+    bool res_dia_on = true;        // SLA_OPT_RESIDENT_DIA
 
     // symmetric reordering for locality (reverse Cuthill-McKee): the solver
     // runs on `inner`, a handle of P A P^T; this handle keeps the caller's CSR

@@ -247,7 +247,7 @@ __device__ __forceinline__ void store_shared(T *p, T v) {
 // System sys = blockIdx.x / G of B: values val + sys * vstride (batch-major),
 // dinv[row * B + sys] (the internal interleaved layout), b, x_out and the
 // global p copy pg at sys * n, stamps at sys * 2 * G * 2 * kMaxC, st[sys].
-template <typename T, bool NARROW>
+template <typename T, bool NARROW, int DIA>
 __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
     const ResTile *__restrict__ tiles, const int32_t *__restrict__ wave_row0,
     const int32_t *__restrict__ wave_tile0, const uint8_t *__restrict__ roff8,
@@ -255,7 +255,8 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
     const T *__restrict__ val_all, int64_t vstride,
     const T *__restrict__ dinv_all, const T *__restrict__ b_all, T *__restrict__ x_all,
     T *pg_all, GridSync gs, int B, int64_t n, double tol, int32_t maxit,
-    SysState *__restrict__ st_all) {
+    SysState *__restrict__ st_all, const int32_t *__restrict__ dia_off, int dia_m,
+    const T *__restrict__ dia_val) {
     __shared__ __align__(16) double prod_all[kRW][4 * 64];
     __shared__ __align__(16) int32_t roff_all[kRW][256];
     __shared__ T qbuf_all[kRW][64 * kRJ];
@@ -411,7 +412,15 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
         for (int u = 0; u < kRD; ++u)
             if (u < nt) fetch(u, tiles[t0 + u * ts]);
     };
-    fetch_head();
+    // DIA (the number of diagonals, or 0): their offsets (wave-uniform) and
+    // the walk direction
+    constexpr int ND = DIA > 0 ? DIA : 1;
+    int doff[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) doff[d] = DIA > 0 ? dia_off[d] : 0;
+    const int n32 = (int)n;   // m n < 2^31 for a matrix held by diagonals
+    bool back = false;
+    if (!DIA) fetch_head();
     while (ok && status == kRunning) {
         // p written by other workgroups (other XCDs) since these caches last
         // held it: drop stale lines before gathering. The CU's L1 and the
@@ -423,6 +432,45 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
             __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
         __syncthreads();
+        if constexpr (DIA > 0) {
+        // ---- A by diagonals: lane l sums its rows R0 + l + 64 j over the
+        // diagonals in column order, q_i = sum_d val[d][i] p[i + off_d],
+        // into its own LDS slots; two row groups' loads (values and
+        // gathers, all coalesced) in flight at a time, the groups walked
+        // backwards on every other iteration. A row without an entry on a
+        // diagonal holds 0 there (its column clamped into the matrix).
+#pragma unroll 1
+        for (int jj = 0; jj < kRJ; jj += 2) {
+            const int jb = back ? kRJ - 2 - jj : jj;
+            if (64 * jb >= R1 - R0) {   // wave-uniform: no rows of this wavefront there
+                if (back) continue;
+                break;
+            }
+            double dv2[2][ND], dg2[2][ND];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int j = jb + h2;
+                const bool in = 64 * j < nl;
+                const int i = R0 + lane + 64 * j;
+#pragma unroll
+                for (int d = 0; d < ND; ++d) {
+                    int c = i + doff[d];
+                    c = c < 0 ? 0 : (c >= n32 ? n32 - 1 : c);
+                    dv2[h2][d] = in ? (double)dia_val[d * n32 + i] : 0.0;
+                    dg2[h2][d] = (double)pg[in ? c : 0];
+                }
+            }
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int j = jb + h2;
+                double acc = 0.0;
+#pragma unroll
+                for (int d = 0; d < ND; ++d) acc = __builtin_fma(dv2[h2][d], dg2[h2][d], acc);
+                if (64 * j < nl) ql[64 * j] = (T)acc;
+            }
+        }
+        back = !back;
+        } else {
         // ---- A: q = A p on this wavefront's tiles, into its LDS slice (the
         // entries of its first kRD tiles are already in the ring)
         if (nt > 0) gather(0, 0);
@@ -503,6 +551,7 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
             ts = -ts;
         }
         fetch_head();
+        }
         // q rows summed by other wavefronts
         __syncthreads();
         // ---- sigma = p.q
@@ -601,12 +650,82 @@ __global__ __launch_bounds__(kBlock) void k_vals_bm(const T *__restrict__ vals, 
     }
 }
 
+bool use_dia(const Handle &h) { return h.res_dia_m > 0 && h.res_dia_on && h.B == 1; }
+
+// the form by diagonals for m diagonals (the 2D and 3D stencils' counts)
+template <typename T>
+const void *dia_kernel(int m) {
+    return m == 5 ? (const void *)&k_cg_resident<T, false, 5>
+                  : (const void *)&k_cg_resident<T, false, 7>;
+}
+
 const void *kernel_for(const Handle &h) {
-    if (h.vt == SLA_F64)
-        return h.res_narrow ? (const void *)&k_cg_resident<double, true>
-                            : (const void *)&k_cg_resident<double, false>;
-    return h.res_narrow ? (const void *)&k_cg_resident<float, true>
-                        : (const void *)&k_cg_resident<float, false>;
+    if (h.vt == SLA_F64) {
+        if (use_dia(h)) return dia_kernel<double>(h.res_dia_m);
+        return h.res_narrow ? (const void *)&k_cg_resident<double, true, 0>
+                            : (const void *)&k_cg_resident<double, false, 0>;
+    }
+    if (use_dia(h)) return dia_kernel<float>(h.res_dia_m);
+    return h.res_narrow ? (const void *)&k_cg_resident<float, true, 0>
+                        : (const void *)&k_cg_resident<float, false, 0>;
+}
+
+// out[map[k]] = vals[k]: CSR values to the diagonals (the slots no entry
+// maps to stay zero)
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_dia_scatter(const T *__restrict__ vals,
+                                                        const int32_t *__restrict__ map,
+                                                        int64_t nnz, T *__restrict__ out) {
+    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < nnz;
+         k += (int64_t)gridDim.x * kBlock)
+        out[map[k]] = vals[k];
+}
+
+// A single system whose entries lie on at most kDiaMax offsets j - i, with
+// at most a quarter more diagonal slots than entries, is held by diagonals
+// for the single-kernel solve (offsets ascending, so a row's sum runs in
+// column order as in CSR): the map from CSR entries to slots is built here,
+// the values are scattered at every solve.
+template <typename RP>
+void build_dia(Handle &h, const std::vector<RP> &rp, const std::vector<int32_t> &col,
+               hipStream_t s) {
+    h.res_dia_m = 0;
+    const int64_t n = h.n;
+    if (h.B != 1 || n < 1 || h.nnz < 1) return;
+    int64_t offs[kDiaMax];
+    int m = 0;
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t k = (int64_t)rp[(size_t)i]; k < (int64_t)rp[(size_t)i + 1]; ++k) {
+            const int64_t o = (int64_t)col[(size_t)k] - i;
+            int d = 0;
+            while (d < m && offs[d] != o) ++d;
+            if (d == m) {
+                if (m == kDiaMax) return;
+                offs[m++] = o;
+            }
+        }
+    if (m != 5 && m != 7) return;   // the kernel is built for these counts
+    if ((double)m * (double)n > 1.25 * (double)h.nnz || (int64_t)m * n >= (int64_t)INT32_MAX) return;
+    std::sort(offs, offs + m);
+    std::vector<int32_t> off32((size_t)m), map((size_t)h.nnz);
+    for (int d = 0; d < m; ++d) off32[(size_t)d] = (int32_t)offs[d];
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t k = (int64_t)rp[(size_t)i]; k < (int64_t)rp[(size_t)i + 1]; ++k) {
+            const int64_t o = (int64_t)col[(size_t)k] - i;
+            int d = 0;
+            while (offs[d] != o) ++d;
+            map[(size_t)k] = (int32_t)(d * n + i);
+        }
+    h.res_dia_off = (int32_t *)dalloc(h, sizeof(int32_t) * (size_t)m);
+    h.res_dia_map = (int32_t *)dalloc(h, sizeof(int32_t) * (size_t)h.nnz);
+    h.res_dia_val = dalloc(h, (size_t)m * (size_t)n * h.vbytes);
+    SLA_HIP(hipMemsetAsync(h.res_dia_val, 0, (size_t)m * (size_t)n * h.vbytes, s));
+    SLA_HIP(hipMemcpyAsync(h.res_dia_off, off32.data(), sizeof(int32_t) * (size_t)m,
+                           hipMemcpyHostToDevice, s));
+    SLA_HIP(hipMemcpyAsync(h.res_dia_map, map.data(), sizeof(int32_t) * (size_t)h.nnz,
+                           hipMemcpyHostToDevice, s));
+    SLA_HIP(hipStreamSynchronize(s));
+    h.res_dia_m = m;
 }
 
 template <typename RP>
@@ -743,6 +862,7 @@ void build_plan(Handle &h, int64_t G, int64_t rpw, hipStream_t s) {
     SLA_HIP(hipMemcpyAsync(h.res_wave, wave.data(), sizeof(int32_t) * wave.size(),
                            hipMemcpyHostToDevice, s));
     SLA_HIP(hipStreamSynchronize(s));
+    build_dia<RP>(h, rp, col, s);
 }
 
 // false when the cooperative launch is refused: not all workgroups can run
@@ -775,6 +895,18 @@ bool launch(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStr
     const T *bp = (const T *)b;
     T *xo = (T *)x;
     T *pg = (T *)h.p;
+    const bool dia = use_dia(h);
+    const int32_t *doff = dia ? h.res_dia_off : nullptr;
+    int dm = dia ? h.res_dia_m : 0;
+    const T *dval = dia ? (const T *)h.res_dia_val : nullptr;
+    if (dia) {
+        int64_t g = (h.nnz + kBlock - 1) / kBlock;
+        if (g > 4 * kMaxGrid) g = 4 * kMaxGrid;
+        hipLaunchKernelGGL(k_dia_scatter<T>, dim3((unsigned)g), dim3(kBlock), 0, s,
+                           (const T *)h.vals, (const int32_t *)h.res_dia_map, h.nnz,
+                           (T *)h.res_dia_val);
+        SLA_HIP(hipGetLastError());
+    }
     // interleaved walk: forced, or where the matrix (values and columns of
     // every system) exceeds the 256 MB Infinity Cache
     const double mat_bytes = (double)h.nnz * (h.vbytes * h.B + (h.res_narrow ? 2 : 4));
@@ -787,7 +919,7 @@ bool launch(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStr
     void *args[] = {(void *)&tiles, (void *)&wrow, (void *)&wtile, (void *)&roff8, (void *)&col,
                     (void *)&col16, (void *)&val, (void *)&vstride, (void *)&dinv, (void *)&bp, (void *)&xo,
                     (void *)&pg, (void *)&gs, (void *)&B, (void *)&n, (void *)&tol,
-                    (void *)&maxit, (void *)&st};
+                    (void *)&maxit, (void *)&st, (void *)&doff, (void *)&dm, (void *)&dval};
     if (h.res_coop) {
         const hipError_t e = hipLaunchCooperativeKernel(
             kernel_for(h), dim3((unsigned)(h.res_grid * h.B)), dim3(kRT), args, 0, s);
@@ -841,6 +973,15 @@ bool resident_ready(Handle &h, hipStream_t s) {
     h.res_rows_per_wave = rpw;
     if (h.rp64) build_plan<int64_t>(h, G, rpw, s);
     else build_plan<int32_t>(h, G, rpw, s);
+    if (h.res_dia_m > 0) {
+        // the form by diagonals must fit one workgroup per CU as well
+        int dia_cu = 0;
+        SLA_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &dia_cu,
+            h.vt == SLA_F64 ? dia_kernel<double>(h.res_dia_m) : dia_kernel<float>(h.res_dia_m),
+            kRT, 0));
+        if (dia_cu < 1) h.res_dia_m = 0;
+    }
     h.res_state = 1;
     return true;
 }

@@ -203,6 +203,13 @@ class SparseCSR:
         return {"reordered": bool(r.value), "narrow_columns": bool(nc.value),
                 "ring_tiles": nc.value == 2, "tiles": t.value, "long_rows": lr.value}
 
+    def diagonals(self) -> int:
+        """Diagonals the single-kernel solve holds the matrix by (0: row
+        tiles, or no single-kernel solve yet)."""
+        m = ctypes.c_int32()
+        check(_lib.load().sla_csr_get_diagonals(self._h, ctypes.byref(m)))
+        return m.value
+
     def profile_reset(self) -> None:
         check(_lib.load().sla_profile_reset(self._h))
 

@@ -146,6 +146,14 @@ enum {
                                    passes fewer per iteration; the same recurrence, z
                                    rounded once more in fp64. 0: three kernels. fp32
                                    values never fold (z would add an fp32 rounding). */
+    SLA_OPT_RESIDENT_DIA = 11,  /* 1 (default): the single-kernel solve of one system whose
+                                   entries lie on 5 or 7 diagonals (offsets j - i), with
+                                   at most a quarter more diagonal slots than entries (the
+                                   2D and 3D stencils), holds the matrix by diagonals: the
+                                   SpMV phase reads values[d][i] and p[i + offset_d], no
+                                   column indices, each row summed over its diagonals in
+                                   column order; 0: the row tiles. The values are copied to
+                                   the diagonals at every solve. */
     SLA_OPT_RESIDENT_WALK = 10  /* the single-kernel solve's SpMV phase: 2 (default) picks by
                                    matrix size, 0 and 1 force a form. 0: each wavefront sums
                                    a contiguous run of its workgroup's tiles; 1: the
@@ -410,6 +418,12 @@ sla_status sla_csr_get_layout(sla_csr h, int32_t *reordered, int32_t *narrow_col
  * *path an SLA_PATH_* value, *fallbacks a mask of SLA_FALLBACK_* bits (0
  * when the preferred path ran). Results do not depend on the path. */
 sla_status sla_csr_get_last_path(sla_csr h, int32_t *path, uint32_t *fallbacks);
+
+/* Diagonals the single-kernel solve holds the matrix by (host output):
+ * *ndiag = their number once a solve has built that solve's plan and
+ * SLA_OPT_RESIDENT_DIA applies (for a reordered handle, of P A P^T), else 0
+ * (row tiles, or no single-kernel solve yet). */
+sla_status sla_csr_get_diagonals(sla_csr h, int32_t *ndiag);
 
 /* Accumulated kernel timings of calls made while SLA_OPT_PROFILE was on
  * (host outputs): number of launches and total milliseconds per kind. */

@@ -345,7 +345,10 @@ def resident_cases():
 @pytest.mark.parametrize("name", ["poisson2d_64", "diffusion3d_128_s40", "knn_laplacian_2m_s60000",
                                   "random_spd_30011", "diffusion3d_128_s70", "block_chains_65536"])
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
-def test_single_kernel_solve_matches_oracle_and_multi_kernel_path(name, dtype):
+@pytest.mark.parametrize("dia", [1, 0])
+def test_single_kernel_solve_matches_oracle_and_multi_kernel_path(name, dtype, dia):
+    """dia 1: the stencils (Poisson, 3D diffusion) are held by diagonals;
+    dia 0: every matrix by row tiles."""
     case = resident_cases()[name]
     if isinstance(case, tuple):
         n, r, c, v = case
@@ -360,6 +363,7 @@ def test_single_kernel_solve_matches_oracle_and_multi_kernel_path(name, dtype):
     ref = oracle.coo_to_csr(n, r, c, v)
     xo, ito, rlo, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, tol, maxit)
     A = coo_handle(n, r, c, v)      # the automatic choice: the single-kernel solve
+    A.set_option(_lib.SLA_OPT_RESIDENT_DIA, dia)
     A.profile_reset()
     A.set_option(_lib.SLA_OPT_PROFILE, 1)
     x1, i1 = A.solve_raw(dev(b), tol, maxit)
@@ -772,6 +776,7 @@ def test_single_kernel_walks_bitwise_equal(case):
         r, c, v, b, g = w.rows, w.cols, w.vals, w.b, w.g
     print(f"resident walks: {case} n={w.n} nnz={w.nnz} batch={w.batch}", flush=True)
     A = coo_handle(w.n, r, c, v)
+    A.set_option(_lib.SLA_OPT_RESIDENT_DIA, 0)   # the walks of the row tiles
     out = {}
     for walk in (0, 1):
         A.set_option(_lib.SLA_OPT_RESIDENT_WALK, walk)
@@ -792,3 +797,112 @@ def test_single_kernel_walks_bitwise_equal(case):
     A.set_option(_lib.SLA_OPT_RESIDENT_WALK, 2)
     with pytest.raises(SlaError):
         A.set_option(_lib.SLA_OPT_RESIDENT_WALK, 3)
+
+
+def nine_point(N):
+    """2D 9-point Laplacian (8 on the diagonal, -1 to the 8 neighbours): 9
+    diagonals, one more than a matrix held by diagonals may have."""
+    i, j = np.meshgrid(np.arange(N), np.arange(N), indexing="ij")
+    idx = (i * N + j).ravel()
+    rows, cols, vals = [idx], [idx], [np.full(N * N, 8.0)]
+    for di in (-1, 0, 1):
+        for dj in (-1, 0, 1):
+            if di == 0 and dj == 0:
+                continue
+            ok = ((i + di >= 0) & (i + di < N) & (j + dj >= 0) & (j + dj < N)).ravel()
+            rows.append(idx[ok])
+            cols.append(((i + di) * N + (j + dj)).ravel()[ok])
+            vals.append(np.full(int(ok.sum()), -1.0))
+    return np.concatenate(rows), np.concatenate(cols), np.concatenate(vals)
+
+
+@pytest.mark.parametrize("name,size,ndiag", [("poisson2d_64", None, 5), ("diffusion3d_128", 40, 7),
+                                             ("diffusion3d_128", 64, 7),
+                                             ("poisson2d_11548", 30, 5)])
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_single_kernel_by_diagonals(name, size, ndiag, dtype):
+    """Stencil matrices (5 and 7 diagonals; 900 rows, not a multiple of a
+    wavefront's 64) in the single-kernel solve held by diagonals: converged
+    solve, fixed step counts and the adjoint against the oracle, and the
+    row-tile form (SLA_OPT_RESIDENT_DIA 0) against the oracle too."""
+    w = make_workload(name, size=size)
+    n = w.n
+    rows = np.repeat(np.arange(n), np.diff(w.row_ptr)) if w.fmt == "csr" else w.rows
+    v, b = w.vals.astype(dtype), w.b.astype(dtype)
+    f64 = dtype == np.float64
+    tol = 1e-10 if f64 else 1e-5
+    xtol = 1e-8 if f64 else 1e-4
+    print(f"by diagonals: {name} n={n} {np.dtype(dtype).name}", flush=True)
+    ref = oracle.coo_to_csr(n, rows, w.cols, v)
+    rp, cc, vv = ref["row_ptr"], ref["col"], ref["vals"]
+    xo, ito, _, oco = oracle.pcg(rp, cc, vv, b, tol, 20000)
+    g = np.random.default_rng(22).standard_normal(n).astype(dtype)
+    lam_o, gv_o, it_o, _, _ = oracle.adjoint(rp, cc, vv, xo, g, tol, 20000)
+    A = coo_handle(n, rows, w.cols, v)
+    for dia in (1, 0):
+        A.set_option(_lib.SLA_OPT_RESIDENT_DIA, dia)
+        x, info = A.solve_raw(dev(b), tol, 20000)
+        assert A.last_path()["path"] == "single_kernel"
+        assert A.diagonals() == (ndiag if dia else 0)
+        assert info.status[0] == oco == oracle.CONVERGED
+        assert abs(info.iterations[0] - ito) <= 2, (dia, info.iterations[0], ito)
+        assert rel(host(x), xo) <= xtol, (dia, rel(host(x), xo))
+        for k in (1, 2, 7):
+            xk, info = A.solve_raw(dev(b), 0.0, k)
+            xko, itk, _, _ = oracle.pcg(rp, cc, vv, b, 0.0, k)
+            assert info.iterations[0] == k == itk
+            assert rel(host(xk), xko) <= (1e-12 if f64 else 1e-5), (dia, k, rel(host(xk), xko))
+        gb, gv, ainfo = A.adjoint_raw(x, dev(g), tol, 20000)
+        assert abs(ainfo.iterations[0] - it_o) <= 2
+        assert rel(host(gb), lam_o) <= 10 * xtol and rel(host(gv), gv_o) <= 10 * xtol, dia
+
+
+@pytest.mark.parametrize("shift,at", [(0.3, 6), (0.5, 5), (2.5, 2)])
+def test_single_kernel_by_diagonals_breakdown(shift, at):
+    """A Poisson matrix shifted to be indefinite, held by diagonals in the
+    single-kernel solve: breakdown at the oracle's iteration, x as the
+    oracle's."""
+    r, c, v = poisson2d_coo(30)
+    v = v.astype(np.float64).copy()
+    v[r == c] -= shift
+    b = np.random.default_rng(0).standard_normal(900)
+    ref = oracle.coo_to_csr(900, r, c, v)
+    xo, ito, _, oco = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, 1e-10, 400)
+    A = coo_handle(900, r, c, v)
+    x, info = A.solve_raw(dev(b), 1e-10, 400)
+    assert A.last_path()["path"] == "single_kernel" and A.diagonals() == 5
+    assert info.status[0] == oco == oracle.BREAKDOWN and info.iterations[0] == ito == at
+    assert rel(host(x), xo) <= 1e-12
+
+
+def test_single_kernel_row_tiles_where_diagonals_do_not_fit():
+    """Nine diagonals, a pattern whose diagonals would be mostly empty (a
+    tridiagonal matrix with one far symmetric pair), and a batch keep the
+    row tiles; each against the oracle."""
+    r, c, v = nine_point(40)
+    n = 1600
+    b = np.random.default_rng(3).standard_normal(n)
+    ref = oracle.coo_to_csr(n, r, c, v)
+    xo, ito, _, _ = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, 1e-10, 2000)
+    A = coo_handle(n, r, c, v)
+    x, info = A.solve_raw(dev(b), 1e-10, 2000)
+    assert A.last_path()["path"] == "single_kernel" and A.diagonals() == 0
+    assert abs(info.iterations[0] - ito) <= 2 and rel(host(x), xo) <= 1e-8
+    # tridiagonal + one far pair: 5 offsets but 5 n slots for ~3 n entries
+    n = 5000
+    i = np.arange(n)
+    r = np.concatenate([i, i[1:], i[:-1], [0, n - 1]])
+    c = np.concatenate([i, i[:-1], i[1:], [n - 1, 0]])
+    v = np.concatenate([np.full(n, 4.0), np.full(2 * (n - 1), -1.0), [0.5, 0.5]])
+    b = np.random.default_rng(4).standard_normal(n)
+    ref = oracle.coo_to_csr(n, r, c, v)
+    xo, ito, _, _ = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, 1e-10, 2000)
+    A = coo_handle(n, r, c, v)
+    x, info = A.solve_raw(dev(b), 1e-10, 2000)
+    assert A.last_path()["path"] == "single_kernel" and A.diagonals() == 0
+    assert abs(info.iterations[0] - ito) <= 2 and rel(host(x), xo) <= 1e-8
+    # a batch of stencil systems
+    w = make_workload("batched_diffusion2d_512x32", size=40, batch=4)
+    A = coo_handle(w.n, w.rows, w.cols, w.vals.astype(np.float64))
+    A.solve_raw(dev(w.b.astype(np.float64)), 1e-8, 2000)
+    assert A.last_path()["path"] == "single_kernel" and A.diagonals() == 0
