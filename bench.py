@@ -452,6 +452,11 @@ def measure(args, name: str, steps: int, warmup: int, cpu_budget: float,
         # for all B systems
         job_bps = {k: ab[k] / w.batch * value for k in ("iter_3k", "iter_min")}
     res_launches, res_ms = prof["cg_resident"]
+    ndiag = A.diagonals()
+    layout["diagonals"] = ndiag
+    # what the single-kernel solve reads per iteration: the matrix as held
+    # (by diagonals: their values, no column indices) and p gathered and stored
+    moved_iter = (ndiag * w.n * V + 2 * V * w.n) if ndiag > 0 else ab["spmv"] / w.batch
     if res_launches > 0:
         # whole solves in one cooperative kernel: per iteration the matrix, the
         # p gathers and the p store (x, r, p, dinv stay on chip); plus b and
@@ -459,6 +464,7 @@ def measure(args, name: str, steps: int, warmup: int, cpu_budget: float,
         launches, total_ms = res_launches, res_ms
         avg_ms = total_ms / launches
         bytes_launch = prof_its / launches * ab["spmv"] + 3 * V * w.n * w.batch
+        moved_launch = prof_its / launches * moved_iter * w.batch + 3 * V * w.n * w.batch
         per_iter_ms = total_ms / max(prof_its, 1)
         kernel = "k_cg_resident (whole solve per launch: SpMV, p.q, update, r.z/r.r, direction)"
     elif w.batch == 1 and not layout["reordered"]:
@@ -528,16 +534,19 @@ def measure(args, name: str, steps: int, warmup: int, cpu_budget: float,
             "iteration_ms": round(1e3 / value, 5),
             "iteration_model": ("BiCGStab: 2 matrix reads + 25 vector passes per iteration"
                                 if method == "bicgstab" else
-                                "PCG in one kernel: the matrix, p gathered and p stored per "
-                                "iteration (x, r, p, dinv stay on chip) = 'moved'; 3k/min: what "
-                                "the per-step kernels would move for the same iterations"
+                                ("PCG in one kernel: the matrix"
+                                 + (f" (held by {ndiag} diagonals: their values, no column "
+                                    f"indices)" if ndiag > 0 else "")
+                                 + ", p gathered and p stored per iteration (x, r, p, dinv stay "
+                                 "on chip) = 'moved'; 3k/min: what the per-step kernels would "
+                                 "move for the same iterations")
                                 if res_launches > 0 else
                                 "PCG: matrix + 13 vector passes (3k) / + 7 (min) per iteration"),
             "iteration_gbps_3k": round(job_bps["iter_3k"] / 1e9, 1),
             "iteration_frac_3k": round(job_bps["iter_3k"] / 1e9 / HBM_PEAK_GBS, 4),
             "iteration_gbps_min": round(job_bps["iter_min"] / 1e9, 1),
-            **({"iteration_gbps_moved": round(ab["spmv"] / w.batch * value / 1e9, 1),
-                "iteration_frac_moved": round(ab["spmv"] / w.batch * value / 1e9 / HBM_PEAK_GBS, 4)}
+            **({"iteration_gbps_moved": round(moved_iter * value / 1e9, 1),
+                "iteration_frac_moved": round(moved_iter * value / 1e9 / HBM_PEAK_GBS, 4)}
                if res_launches > 0 else {}),
             # the kernels of one iteration alone (per-launch events, which add
             # a few microseconds of event overhead per launch)
@@ -558,6 +567,15 @@ def measure(args, name: str, steps: int, warmup: int, cpu_budget: float,
             "layout": layout,
         },
     }
+    if res_launches > 0 and ndiag > 0:
+        out["roofline"]["bytes_moved_per_launch"] = round(moved_launch)
+        out["roofline"]["frac_on_moved"] = round(
+            moved_launch / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        out["roofline"]["held_by_diagonals"] = (
+            f"the kernel holds the matrix by {ndiag} diagonals and reads no column indices: "
+            f"'achieved' counts the CSR algorithmic bytes (values, column indices, row "
+            f"pointers, p in and q out per iteration), bytes_moved_per_launch what it reads "
+            f"and writes")
     matrix_mb = (ab["spmv"] - 2 * V * w.n * w.batch) / 1e6
     if matrix_mb < 256.0:
         out["roofline"]["note"] = (
