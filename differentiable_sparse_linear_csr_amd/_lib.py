@@ -38,6 +38,7 @@ SLA_OPT_SPMV_RING = 8
 SLA_OPT_FOLD_DIRECTION = 9
 SLA_OPT_RESIDENT_WALK = 10
 SLA_OPT_RESIDENT_DIA = 11
+SLA_OPT_SPMV_DIA = 12
 SLA_PATH_NONE, SLA_PATH_SINGLE_KERNEL, SLA_PATH_PER_STEP = 0, 1, 2
 SLA_FALLBACK_COOPERATIVE_REFUSED, SLA_FALLBACK_WAIT_TIMED_OUT = 1, 2
 KERNELS = {"spmv_dot": 0, "update": 1, "direction": 2, "init": 3, "spmv": 4, "grad": 5,
@@ -101,7 +102,7 @@ def load() -> ctypes.CDLL:
     L.sla_csr_memory.argtypes = [P, pi64]
     L.sla_csr_get_layout.argtypes = [P, pi32, pi32, pi64, pi64]
     L.sla_csr_get_last_path.argtypes = [P, pi32, ctypes.POINTER(ctypes.c_uint32)]
-    L.sla_csr_get_diagonals.argtypes = [P, pi32]
+    L.sla_csr_get_diagonals.argtypes = [P, pi32, pi32]
     L.sla_pcg_solve_noalloc.argtypes = [i64, i64, P, P, P, P, P, f64, i32, ctypes.POINTER(Info), P]
     L.sla_csr_destroy.argtypes = [P]
     L.sla_csr_destroy.restype = None

@@ -6,6 +6,8 @@
 
 #include "common.h"
 
+#include <algorithm>
+
 namespace sla {
 
 namespace {
@@ -96,7 +98,7 @@ void alloc_workspace(Handle &h, hipStream_t s) {
     h.part_len = plen;
     h.part = (double *)dalloc(h, (size_t)plen * sizeof(double));
     h.gpart = (double *)dalloc(h, (size_t)kGroups * 2 * kMaxBatch * sizeof(double));
-    h.spart = (double *)dalloc(h, (size_t)kMaxGrid * sizeof(double));
+    h.spart = (double *)dalloc(h, (size_t)std::max(kMaxGrid, kDiaGridMax) * sizeof(double));
     h.gpart_spmv = (double *)dalloc(h, (size_t)kGroups * kMaxBatch * sizeof(double));
     h.sync = (uint32_t *)dalloc(h, (size_t)kCntKinds * kCountersPerKind * sizeof(uint32_t));
     SLA_HIP(hipMemsetAsync(h.sync, 0, (size_t)kCntKinds * kCountersPerKind * sizeof(uint32_t), s));
@@ -374,6 +376,10 @@ void set_option(Handle *h, int32_t key, int64_t value) {
         case SLA_OPT_RESIDENT_DIA:
             h->res_dia_on = value != 0;
             break;
+        case SLA_OPT_SPMV_DIA:
+            if (h->spmv_dia != (value != 0)) drop_graphs(*h);
+            h->spmv_dia = value != 0;
+            break;
         default:
             fail(SLA_ERR_INVALID_ARG, "unknown option");
     }
@@ -609,11 +615,12 @@ sla_status sla_csr_get_last_path(sla_csr hd, int32_t *path, uint32_t *fallbacks)
     });
 }
 
-sla_status sla_csr_get_diagonals(sla_csr hd, int32_t *ndiag) {
+sla_status sla_csr_get_diagonals(sla_csr hd, int32_t *ndiag, int32_t *per_step) {
     return guard([&] {
         const Handle *h = checked(hd);
         if (h->inner) h = h->inner;
-        if (ndiag) *ndiag = (h->res_state > 0 && h->res_dia_on && h->B == 1) ? h->res_dia_m : 0;
+        if (ndiag) *ndiag = (h->res_state > 0 && h->res_dia_on && h->res_dia_fits) ? h->dia_m : 0;
+        if (per_step) *per_step = (h->spmv_dia && h->B == 1 && h->nseg == 0) ? h->dia_m : 0;
     });
 }
 

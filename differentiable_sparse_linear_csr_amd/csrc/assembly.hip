@@ -490,7 +490,7 @@ void build_from_csr(Handle &h, sla_itype rit, const void *row_ptr, sla_itype cit
 }
 
 // values [B][nnz_in] (input order) -> internal [nnz][B]
-void load_values(Handle &h, const void *values, hipStream_t s) {
+static void load_values_csr(Handle &h, const void *values, hipStream_t s) {
     if (h.nnz_in == 0) return;
     if (!h.perm) {
         if (h.B == 1)
@@ -510,6 +510,11 @@ void load_values(Handle &h, const void *values, hipStream_t s) {
                            (const int64_t *)h.perm, (const int64_t *)h.run, h.nnz, h.nnz_in, h.B,
                            (float *)h.vals);
     SLA_HIP(hipGetLastError());
+}
+
+void load_values(Handle &h, const void *values, hipStream_t s) {
+    load_values_csr(h, values, s);
+    dia_scatter(h, s);
 }
 
 // ------------------------------------------------------------------ tiles
@@ -793,6 +798,7 @@ void build_tiles(Handle &h, hipStream_t s, const int64_t *seg_rows, int32_t nseg
             break;
         }
     SLA_HIP(hipStreamSynchronize(s));
+    if (nseg == 0) build_dia(h, s);
 }
 
 // ------------------------------------------------------------------ Jacobi
@@ -819,6 +825,154 @@ void compute_dinv(Handle &h, hipStream_t s) {
     const int flags = read_flag(bad, s);
     h.diag_ok = flags == 0;
     h.diag_nonzero = (flags & kDiagUnusable) == 0;
+}
+
+// ---- a single system held by diagonals
+struct DiaOffs {
+    int32_t o[kDiaMax];
+    int32_t m;
+};
+
+// flag = 1 if an entry's offset j - i is not one of the m candidates
+template <typename RP>
+__global__ __launch_bounds__(kBlock) void k_dia_check(const RP *__restrict__ row_ptr,
+                                                      const int32_t *__restrict__ col, int64_t n,
+                                                      DiaOffs d, int *__restrict__ flag) {
+    int bad = 0;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * kBlock)
+        for (int64_t k = row_ptr[i]; k < (int64_t)row_ptr[i + 1]; ++k) {
+            const int64_t o = (int64_t)col[k] - i;
+            bool hit = false;
+            for (int q = 0; q < d.m; ++q) hit |= o == (int64_t)d.o[q];
+            bad |= hit ? 0 : 1;
+        }
+    if (bad) atomicOr(flag, 1);
+}
+
+// map[k] = q n + i for entry k = (i, i + o_q)
+template <typename RP>
+__global__ __launch_bounds__(kBlock) void k_dia_map(const RP *__restrict__ row_ptr,
+                                                    const int32_t *__restrict__ col, int64_t n,
+                                                    DiaOffs d, int32_t *__restrict__ map) {
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * kBlock)
+        for (int64_t k = row_ptr[i]; k < (int64_t)row_ptr[i + 1]; ++k) {
+            const int64_t o = (int64_t)col[k] - i;
+            int q = 0;
+            while (q < d.m - 1 && (int64_t)d.o[q] != o) ++q;
+            map[k] = (int32_t)(q * n + i);
+        }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_dia_scatter(const T *__restrict__ vals,
+                                                        const int32_t *__restrict__ map,
+                                                        int64_t nnz, T *__restrict__ out) {
+    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < nnz;
+         k += (int64_t)gridDim.x * kBlock)
+        out[map[k]] = vals[k];
+}
+
+// key = length << 40 | (2^40 - 1 - row), maximised: the first longest row
+template <typename RP>
+__global__ __launch_bounds__(kBlock) void k_longest_row(const RP *__restrict__ row_ptr, int64_t n,
+                                                        unsigned long long *__restrict__ key) {
+    unsigned long long best = 0;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * kBlock) {
+        const unsigned long long len = (unsigned long long)(row_ptr[i + 1] - row_ptr[i]);
+        const unsigned long long k = (len << 40) | ((1ull << 40) - 1 - (unsigned long long)i);
+        best = k > best ? k : best;
+    }
+    if (best) atomicMax(key, best);
+}
+
+// A single system whose entries lie on 5 or 7 distinct offsets j - i (the
+// 2D and 3D stencils), with m n at most a quarter above nnz, is also held by
+// diagonals: the candidates are the offsets of a longest row, checked
+// against every entry on the device; offsets ascending, so a row's
+// diagonals run in its column order.
+void build_dia(Handle &h, hipStream_t s) {
+    h.dia_m = 0;
+    const int64_t n = h.n;
+    if (h.B != 1 || h.nseg > 0 || n < 2 || h.nnz < 1) return;
+    // the candidate row: the first of the longest rows (found on the device)
+    Scratch sc0(s);
+    unsigned long long *key = sc0.get<unsigned long long>(1);
+    SLA_HIP(hipMemsetAsync(key, 0, sizeof(unsigned long long), s));
+    if (h.rp64)
+        hipLaunchKernelGGL(k_longest_row<int64_t>, dim3(grid_for(n)), dim3(kBlock), 0, s,
+                           (const int64_t *)h.row_ptr, n, key);
+    else
+        hipLaunchKernelGGL(k_longest_row<int32_t>, dim3(grid_for(n)), dim3(kBlock), 0, s,
+                           (const int32_t *)h.row_ptr, n, key);
+    SLA_HIP(hipGetLastError());
+    unsigned long long hkey = 0;
+    SLA_HIP(hipMemcpyAsync(&hkey, key, sizeof(hkey), hipMemcpyDeviceToHost, s));
+    SLA_HIP(hipStreamSynchronize(s));
+    const int64_t crow = (int64_t)((1ull << 40) - 1 - (hkey & ((1ull << 40) - 1)));
+    int64_t mid[2] = {0, 0};
+    if (h.rp64) {
+        SLA_HIP(hipMemcpyAsync(mid, (const int64_t *)h.row_ptr + crow, 16, hipMemcpyDeviceToHost, s));
+    } else {
+        int32_t m32[2] = {0, 0};
+        SLA_HIP(hipMemcpyAsync(m32, (const int32_t *)h.row_ptr + crow, 8, hipMemcpyDeviceToHost, s));
+        SLA_HIP(hipStreamSynchronize(s));
+        mid[0] = m32[0];
+        mid[1] = m32[1];
+    }
+    SLA_HIP(hipStreamSynchronize(s));
+    const int64_t m = mid[1] - mid[0];
+    if (m != 5 && m != 7) return;
+    if ((double)m * (double)n > 1.25 * (double)h.nnz || m * n >= (int64_t)INT32_MAX) return;
+    int32_t cols[kDiaMax];
+    SLA_HIP(hipMemcpyAsync(cols, h.col + mid[0], sizeof(int32_t) * (size_t)m, hipMemcpyDeviceToHost, s));
+    SLA_HIP(hipStreamSynchronize(s));
+    DiaOffs d{};
+    d.m = (int32_t)m;
+    for (int q = 0; q < m; ++q) d.o[q] = (int32_t)(cols[q] - crow);   // ascending (sorted row)
+    Scratch sc(s);
+    int *flag = sc.get<int>(1);
+    SLA_HIP(hipMemsetAsync(flag, 0, sizeof(int), s));
+    const unsigned g = grid_for(n);
+    if (h.rp64)
+        hipLaunchKernelGGL(k_dia_check<int64_t>, dim3(g), dim3(kBlock), 0, s,
+                           (const int64_t *)h.row_ptr, (const int32_t *)h.col, n, d, flag);
+    else
+        hipLaunchKernelGGL(k_dia_check<int32_t>, dim3(g), dim3(kBlock), 0, s,
+                           (const int32_t *)h.row_ptr, (const int32_t *)h.col, n, d, flag);
+    SLA_HIP(hipGetLastError());
+    if (read_flag(flag, s) != 0) return;
+    h.dia_off = (int32_t *)dalloc(h, sizeof(int32_t) * kDiaMax);
+    h.dia_map = (int32_t *)dalloc(h, sizeof(int32_t) * (size_t)h.nnz);
+    h.dia_val = dalloc(h, (size_t)(m * n) * h.vbytes);
+    SLA_HIP(hipMemcpyAsync(h.dia_off, d.o, sizeof(int32_t) * kDiaMax, hipMemcpyHostToDevice, s));
+    SLA_HIP(hipMemsetAsync(h.dia_val, 0, (size_t)(m * n) * h.vbytes, s));
+    if (h.rp64)
+        hipLaunchKernelGGL(k_dia_map<int64_t>, dim3(g), dim3(kBlock), 0, s,
+                           (const int64_t *)h.row_ptr, (const int32_t *)h.col, n, d, h.dia_map);
+    else
+        hipLaunchKernelGGL(k_dia_map<int32_t>, dim3(g), dim3(kBlock), 0, s,
+                           (const int32_t *)h.row_ptr, (const int32_t *)h.col, n, d, h.dia_map);
+    SLA_HIP(hipGetLastError());
+    h.dia_m = (int32_t)m;
+    dia_scatter(h, s);
+    SLA_HIP(hipStreamSynchronize(s));
+}
+
+void dia_scatter(Handle &h, hipStream_t s) {
+    if (h.dia_m == 0 || h.nnz == 0) return;
+    const unsigned g = grid_for(h.nnz);
+    if (h.vt == SLA_F64)
+        hipLaunchKernelGGL(k_dia_scatter<double>, dim3(g), dim3(kBlock), 0, s,
+                           (const double *)h.vals, (const int32_t *)h.dia_map, h.nnz,
+                           (double *)h.dia_val);
+    else
+        hipLaunchKernelGGL(k_dia_scatter<float>, dim3(g), dim3(kBlock), 0, s,
+                           (const float *)h.vals, (const int32_t *)h.dia_map, h.nnz,
+                           (float *)h.dia_val);
+    SLA_HIP(hipGetLastError());
 }
 
 bool check_symmetric(Handle &h, hipStream_t s) {

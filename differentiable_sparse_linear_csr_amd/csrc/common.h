@@ -31,6 +31,7 @@ constexpr int kMaxGrid = 2048;                     // grid cap of the persistent
 constexpr int kXcds = 8;                           // workgroups go round-robin over 8 XCDs
 constexpr int kMaxBatch = 256;
 constexpr int kDiaMax = 8;   // diagonals of a matrix the single-kernel solve holds by diagonals
+constexpr int kDiaGridMax = 8192;   // grid cap of the per-step SpMV by diagonals (spart entries)
 // col and values carry this many spare entries past nnz: the SpMV reads
 // entries in 16-byte groups from a 4-aligned base and may touch (never use)
 // up to 3 entries beyond a tile's end.
@@ -156,6 +157,15 @@ struct Handle {
     void *row_ptr = nullptr;
     int32_t *col = nullptr;
     void *vals = nullptr;    // [nnz][B]
+    // a single system held by diagonals as well (its entries on 5 or 7
+    // distinct offsets j - i, at most a quarter more slots than entries):
+    // dia_val[d][row] = the entry (row, row + dia_off[d]), 0 where absent;
+    // kept in step with vals (load_values, child_values)
+    int32_t dia_m = 0;              // diagonals (0: not held by diagonals)
+    int32_t *dia_off = nullptr;     // [m] offsets, ascending (column order)
+    int32_t *dia_map = nullptr;     // [nnz] CSR entry -> d * n + row
+    void *dia_val = nullptr;        // [m][n]
+    bool spmv_dia = true;           // SLA_OPT_SPMV_DIA: the per-step SpMV by diagonals
     int64_t *slot = nullptr; // input entry -> CSR position (null: identity)
     int64_t *perm = nullptr; // sorted position -> input entry (null: identity)
     int64_t *run = nullptr;  // [nnz+1] first sorted position of each CSR entry
@@ -232,14 +242,8 @@ struct Handle {
     bool res_narrow = false;       // every tile's columns span less than 2^16
     bool res_coop = true;          // cooperative launch (else an ordinary one)
     int res_walk = 2;              // SpMV phase: 0 contiguous runs, 1 interleaved, 2 by size
-    // the single system held by diagonals (a pattern with at most kDiaMax
-    // distinct column offsets j - i, little padding): the SpMV phase reads
-    // dia_val[d][row] and p[row + dia_off[d]], no column indices
-    int32_t res_dia_m = 0;         // diagonals (0: tiles)
-    int32_t *res_dia_off = nullptr;  // [m] offsets, ascending (column order)
-    int32_t *res_dia_map = nullptr;  // [nnz] CSR entry -> d * n + row
-    void *res_dia_val = nullptr;     // [m][n], zero where a row has no entry
     bool res_dia_on = true;        // SLA_OPT_RESIDENT_DIA
+    bool res_dia_fits = true;      // the single-kernel form by diagonals fits a CU
 
     // symmetric reordering for locality (reverse Cuthill-McKee): the solver
     // runs on `inner`, a handle of P A P^T; this handle keeps the caller's CSR
@@ -313,7 +317,12 @@ void load_values(Handle &h, const void *values, hipStream_t s);
 // seg_rows (host, [nseg+1]) splits tiles at member boundaries (nseg = 0: none)
 void build_tiles(Handle &h, hipStream_t s, const int64_t *seg_rows = nullptr, int32_t nseg = 0);
 void compute_dinv(Handle &h, hipStream_t s);       // sets h.diag_ok (synchronizes)
-bool check_symmetric(Handle &h, hipStream_t s);    // synchronizes
+bool check_symmetric(Handle &h, hipStream_t s);
+// per-workgroup partials the PCG SpMV leaves in spart (the tile grid, or
+// the grid of the SpMV by diagonals)
+int64_t spmv_blocks(const Handle &h);
+void build_dia(Handle &h, hipStream_t s);    // synchronizes
+void dia_scatter(Handle &h, hipStream_t s);  // vals -> dia_val    // synchronizes
 void gather_to_input(Handle &h, const void *in, void *out, hipStream_t s);
 void values_to_batch_major(Handle &h, void *out, hipStream_t s);
 

@@ -1449,7 +1449,7 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
         hipLaunchKernelGGL((nt ? k_update1<T, true, true> : k_update1<T, false, true>),
                            dim3((unsigned)g1), dim3(kBlock), 0, s, h.n, (T *)h.fold_z, (T *)h.r,
                            (const T *)nullptr, (const T *)h.q, (const T *)h.dinv,
-                           (const double *)h.spart, spmv_grid(h), red, h.ctl, h.st, h.d_running);
+                           (const double *)h.spart, spmv_blocks(h), red, h.ctl, h.st, h.d_running);
         SLA_HIP(hipGetLastError());
         if (lp) lp->end(SLA_KERNEL_UPDATE, a);
         return;
@@ -1463,7 +1463,7 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
     if (gf > 0) {
         hipLaunchKernelGGL(k_update_dir1<T>, dim3((unsigned)gf), dim3(kBlock), 0, s, h.n, (T *)h.x,
                            (T *)h.r, (T *)h.p, (const T *)h.q, (const T *)h.dinv,
-                           (const double *)h.spart, spmv_grid(h), red, h.ctl, h.st, h.d_running,
+                           (const double *)h.spart, spmv_blocks(h), red, h.ctl, h.st, h.d_running,
                            h.bcast);
         SLA_HIP(hipGetLastError());
         if (lp) lp->end(SLA_KERNEL_UPDATE, a);
@@ -1475,7 +1475,7 @@ void iter_kernels_t(Handle &h, hipStream_t s, Launcher *lp) {
         hipLaunchKernelGGL((nt ? k_update1<T, true> : k_update1<T, false>), dim3((unsigned)g1),
                            dim3(kBlock), 0, s, h.n, (T *)h.x,
                            (T *)h.r, (const T *)h.p, (const T *)h.q, (const T *)h.dinv,
-                           (const double *)h.spart, spmv_grid(h), red, h.ctl, h.st, h.d_running);
+                           (const double *)h.spart, spmv_blocks(h), red, h.ctl, h.st, h.d_running);
     } else if (bv_ok<T>(h) && fused_bv_grid(h, VecW<T>::W) > 0) {
         const int64_t nc = h.n * h.B / VecW<T>::W;
         hipLaunchKernelGGL(k_update_dir_bv<T>, dim3((unsigned)fused_bv_grid(h, VecW<T>::W)),

@@ -369,6 +369,7 @@ void child_values(Handle &h, Handle &child, const int64_t *map, hipStream_t s) {
                                s, (const float *)h.vals, (float *)child.vals, map, h.nnz, h.B);
         SLA_HIP(hipGetLastError());
     }
+    dia_scatter(child, s);
     compute_dinv(child, s);
     if (child.inner) reordered_set_values(child, s);
 }

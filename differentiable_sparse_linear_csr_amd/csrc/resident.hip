@@ -650,7 +650,9 @@ __global__ __launch_bounds__(kBlock) void k_vals_bm(const T *__restrict__ vals, 
     }
 }
 
-bool use_dia(const Handle &h) { return h.res_dia_m > 0 && h.res_dia_on && h.B == 1; }
+bool use_dia(const Handle &h) {
+    return h.dia_m > 0 && h.res_dia_on && h.res_dia_fits && h.B == 1;
+}
 
 // the form by diagonals for m diagonals (the 2D and 3D stencils' counts)
 template <typename T>
@@ -661,71 +663,13 @@ const void *dia_kernel(int m) {
 
 const void *kernel_for(const Handle &h) {
     if (h.vt == SLA_F64) {
-        if (use_dia(h)) return dia_kernel<double>(h.res_dia_m);
+        if (use_dia(h)) return dia_kernel<double>(h.dia_m);
         return h.res_narrow ? (const void *)&k_cg_resident<double, true, 0>
                             : (const void *)&k_cg_resident<double, false, 0>;
     }
-    if (use_dia(h)) return dia_kernel<float>(h.res_dia_m);
+    if (use_dia(h)) return dia_kernel<float>(h.dia_m);
     return h.res_narrow ? (const void *)&k_cg_resident<float, true, 0>
                         : (const void *)&k_cg_resident<float, false, 0>;
-}
-
-// out[map[k]] = vals[k]: CSR values to the diagonals (the slots no entry
-// maps to stay zero)
-template <typename T>
-__global__ __launch_bounds__(kBlock) void k_dia_scatter(const T *__restrict__ vals,
-                                                        const int32_t *__restrict__ map,
-                                                        int64_t nnz, T *__restrict__ out) {
-    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < nnz;
-         k += (int64_t)gridDim.x * kBlock)
-        out[map[k]] = vals[k];
-}
-
-// A single system whose entries lie on at most kDiaMax offsets j - i, with
-// at most a quarter more diagonal slots than entries, is held by diagonals
-// for the single-kernel solve (offsets ascending, so a row's sum runs in
-// column order as in CSR): the map from CSR entries to slots is built here,
-// the values are scattered at every solve.
-template <typename RP>
-void build_dia(Handle &h, const std::vector<RP> &rp, const std::vector<int32_t> &col,
-               hipStream_t s) {
-    h.res_dia_m = 0;
-    const int64_t n = h.n;
-    if (h.B != 1 || n < 1 || h.nnz < 1) return;
-    int64_t offs[kDiaMax];
-    int m = 0;
-    for (int64_t i = 0; i < n; ++i)
-        for (int64_t k = (int64_t)rp[(size_t)i]; k < (int64_t)rp[(size_t)i + 1]; ++k) {
-            const int64_t o = (int64_t)col[(size_t)k] - i;
-            int d = 0;
-            while (d < m && offs[d] != o) ++d;
-            if (d == m) {
-                if (m == kDiaMax) return;
-                offs[m++] = o;
-            }
-        }
-    if (m != 5 && m != 7) return;   // the kernel is built for these counts
-    if ((double)m * (double)n > 1.25 * (double)h.nnz || (int64_t)m * n >= (int64_t)INT32_MAX) return;
-    std::sort(offs, offs + m);
-    std::vector<int32_t> off32((size_t)m), map((size_t)h.nnz);
-    for (int d = 0; d < m; ++d) off32[(size_t)d] = (int32_t)offs[d];
-    for (int64_t i = 0; i < n; ++i)
-        for (int64_t k = (int64_t)rp[(size_t)i]; k < (int64_t)rp[(size_t)i + 1]; ++k) {
-            const int64_t o = (int64_t)col[(size_t)k] - i;
-            int d = 0;
-            while (offs[d] != o) ++d;
-            map[(size_t)k] = (int32_t)(d * n + i);
-        }
-    h.res_dia_off = (int32_t *)dalloc(h, sizeof(int32_t) * (size_t)m);
-    h.res_dia_map = (int32_t *)dalloc(h, sizeof(int32_t) * (size_t)h.nnz);
-    h.res_dia_val = dalloc(h, (size_t)m * (size_t)n * h.vbytes);
-    SLA_HIP(hipMemsetAsync(h.res_dia_val, 0, (size_t)m * (size_t)n * h.vbytes, s));
-    SLA_HIP(hipMemcpyAsync(h.res_dia_off, off32.data(), sizeof(int32_t) * (size_t)m,
-                           hipMemcpyHostToDevice, s));
-    SLA_HIP(hipMemcpyAsync(h.res_dia_map, map.data(), sizeof(int32_t) * (size_t)h.nnz,
-                           hipMemcpyHostToDevice, s));
-    SLA_HIP(hipStreamSynchronize(s));
-    h.res_dia_m = m;
 }
 
 template <typename RP>
@@ -862,7 +806,6 @@ void build_plan(Handle &h, int64_t G, int64_t rpw, hipStream_t s) {
     SLA_HIP(hipMemcpyAsync(h.res_wave, wave.data(), sizeof(int32_t) * wave.size(),
                            hipMemcpyHostToDevice, s));
     SLA_HIP(hipStreamSynchronize(s));
-    build_dia<RP>(h, rp, col, s);
 }
 
 // false when the cooperative launch is refused: not all workgroups can run
@@ -896,17 +839,9 @@ bool launch(Handle &h, const void *b, void *x, double tol, int32_t maxit, hipStr
     T *xo = (T *)x;
     T *pg = (T *)h.p;
     const bool dia = use_dia(h);
-    const int32_t *doff = dia ? h.res_dia_off : nullptr;
-    int dm = dia ? h.res_dia_m : 0;
-    const T *dval = dia ? (const T *)h.res_dia_val : nullptr;
-    if (dia) {
-        int64_t g = (h.nnz + kBlock - 1) / kBlock;
-        if (g > 4 * kMaxGrid) g = 4 * kMaxGrid;
-        hipLaunchKernelGGL(k_dia_scatter<T>, dim3((unsigned)g), dim3(kBlock), 0, s,
-                           (const T *)h.vals, (const int32_t *)h.res_dia_map, h.nnz,
-                           (T *)h.res_dia_val);
-        SLA_HIP(hipGetLastError());
-    }
+    const int32_t *doff = dia ? h.dia_off : nullptr;
+    int dm = dia ? h.dia_m : 0;
+    const T *dval = dia ? (const T *)h.dia_val : nullptr;
     // interleaved walk: forced, or where the matrix (values and columns of
     // every system) exceeds the 256 MB Infinity Cache
     const double mat_bytes = (double)h.nnz * (h.vbytes * h.B + (h.res_narrow ? 2 : 4));
@@ -973,14 +908,14 @@ bool resident_ready(Handle &h, hipStream_t s) {
     h.res_rows_per_wave = rpw;
     if (h.rp64) build_plan<int64_t>(h, G, rpw, s);
     else build_plan<int32_t>(h, G, rpw, s);
-    if (h.res_dia_m > 0) {
+    if (h.dia_m > 0) {
         // the form by diagonals must fit one workgroup per CU as well
         int dia_cu = 0;
         SLA_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &dia_cu,
-            h.vt == SLA_F64 ? dia_kernel<double>(h.res_dia_m) : dia_kernel<float>(h.res_dia_m),
+            h.vt == SLA_F64 ? dia_kernel<double>(h.dia_m) : dia_kernel<float>(h.dia_m),
             kRT, 0));
-        if (dia_cu < 1) h.res_dia_m = 0;
+        h.res_dia_fits = dia_cu >= 1;
     }
     h.res_state = 1;
     return true;

@@ -597,6 +597,115 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     }
 }
 
+// Single system held by diagonals (Handle.dia_*, M of them): one row per
+// lane, kDiaRows rows per lane in flight; every load of a wavefront is 512
+// contiguous bytes (a diagonal's values, or the gathered vector at a fixed
+// offset from the rows). Each XCD takes a contiguous eighth of the rows
+// (workgroup b runs on XCD b % 8) and its workgroups take their row groups
+// interleaved, so the XCD streams one stretch of the diagonals and the
+// vector lines near +-offset are shared in its L2. A row's sum runs over
+// the diagonals in column order (one fused multiply-add each; an absent
+// entry is a 0 at a clamped column). DOT 0: y = A x; 1: and the w.y partial
+// of each workgroup in spart; 4: the folded direction as in the ring form
+// (p_new formed at every gathered column and at the own row, x updated on
+// every other launch, p_new.q partials).
+constexpr int kDiaRows = 4;
+
+template <typename T, int M, int DOT>
+__global__ __launch_bounds__(kBlock) void k_spmv_dia(
+    int64_t n, const int32_t *__restrict__ dia_off, const T *__restrict__ dval,
+    const T *__restrict__ x, T *__restrict__ y, const T *__restrict__ w,
+    double *__restrict__ spart, const int32_t *__restrict__ status, FoldArgs fa) {
+    constexpr bool FOLD = DOT == 4;
+    __shared__ double lds4[kWaves];
+    if (DOT > 0 && *status != kRunning) return;
+    int off[M];
+#pragma unroll
+    for (int d = 0; d < M; ++d) off[d] = dia_off[d];
+    double beta = 0.0, ax = 0.0, ax2 = 0.0;
+    bool xstep = false;
+    const T *zz = nullptr, *pold = nullptr;
+    T *pnew = nullptr, *xx = nullptr;
+    if (FOLD) {
+        const SysState s0 = *fa.st;
+        beta = s0.beta;
+        ax = s0.alpha;
+        ax2 = s0.alpha2;
+        xstep = (s0.iter & 1) != 0;
+        const int par = s0.iter & 1;
+        zz = (const T *)fa.z;
+        pold = (const T *)fa.p[par];
+        pnew = (T *)fa.p[par ^ 1];
+        xx = (T *)fa.x;
+    }
+    const int64_t G = gridDim.x;   // a multiple of kXcds
+    const int64_t X = G / kXcds, xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
+    const int64_t xs = n * xcd / kXcds, xe = n * (xcd + 1) / kXcds;
+    const int64_t step = X * kBlock * kDiaRows;
+    double dot = 0.0;
+    for (int64_t r0 = xs + jx * kBlock * kDiaRows; r0 < xe; r0 += step) {
+        double v[kDiaRows][M], g[kDiaRows][M], gp[FOLD ? kDiaRows : 1][FOLD ? M : 1];
+        T oz[kDiaRows], op[kDiaRows], op2[kDiaRows], ox[kDiaRows], ow[kDiaRows];
+#pragma unroll
+        for (int u = 0; u < kDiaRows; ++u) {
+            const int64_t i = r0 + u * kBlock + threadIdx.x;
+            const bool in = i < xe;
+            const int64_t ii = in ? i : 0;
+#pragma unroll
+            for (int d = 0; d < M; ++d) {
+                int64_t c = i + off[d];
+                c = c < 0 ? 0 : (c >= n ? n - 1 : c);
+                c = in ? c : 0;
+                v[u][d] = in ? (double)dval[d * n + i] : 0.0;
+                if (FOLD) {
+                    g[u][d] = (double)zz[c];
+                    gp[FOLD ? u : 0][FOLD ? d : 0] = (double)pold[c];
+                } else {
+                    g[u][d] = (double)x[c];
+                }
+            }
+            if (FOLD) {
+                oz[u] = zz[ii];
+                op[u] = pold[ii];
+                op2[u] = pnew[xstep ? ii : 0];   // read before this lane writes it
+                ox[u] = xx[xstep ? ii : 0];
+            }
+            if (DOT == 1) ow[u] = w[ii];
+        }
+#pragma unroll
+        for (int u = 0; u < kDiaRows; ++u) {
+            const int64_t i = r0 + u * kBlock + threadIdx.x;
+            double acc = 0.0;
+#pragma unroll
+            for (int d = 0; d < M; ++d) {
+                const double gv = FOLD ? (double)fold_p<T>(g[u][d], gp[FOLD ? u : 0][FOLD ? d : 0], beta)
+                                       : g[u][d];
+                acc = __builtin_fma(v[u][d], gv, acc);
+            }
+            if (i < xe) {
+                const T q = (T)acc;
+                y[i] = q;
+                if (DOT == 1) dot += (double)ow[u] * (double)q;
+                if (FOLD) {
+                    const T pn = fold_p<T>((double)oz[u], (double)op[u], beta);
+                    if (xstep) {
+                        T xn = ox[u];
+                        if (ax2 != 0.0) xn = (T)((double)xn + ax2 * (double)op2[u]);
+                        if (ax != 0.0) xn = (T)((double)xn + ax * (double)op[u]);
+                        xx[i] = xn;
+                    }
+                    pnew[i] = pn;
+                    dot += (double)pn * (double)q;
+                }
+            }
+        }
+    }
+    if (DOT > 0) {
+        dot = block_sum(dot, lds4);
+        if (threadIdx.x == 0) spart[blockIdx.x] = dot;
+    }
+}
+
 // Batch sharing one pattern (B > 1), general B: lane (row slot jr, system b)
 // walks its row; the B lanes of a row read one index and B consecutive
 // values, so col_idx / row_ptr are read once for all systems.
@@ -928,6 +1037,28 @@ int64_t batched_grid_t(const Handle &h) {
 
 bool use_ring(const Handle &h) { return h.all_narrow && h.ring_tiles && h.spmv_ring; }
 
+// the per-step SpMV of a single system held by diagonals
+bool use_dia_step(const Handle &h) { return h.dia_m > 0 && h.spmv_dia && h.B == 1 && h.nseg == 0; }
+
+int64_t dia_grid(const Handle &h) {
+    const int64_t per = (int64_t)kBlock * kDiaRows;
+    int64_t g = (h.n + per - 1) / per;
+    g = (g + kXcds - 1) / kXcds * kXcds;
+    return g < kDiaGridMax ? g : kDiaGridMax;
+}
+
+template <typename T, int DOT>
+void launch_dia(Handle &h, const void *x, void *y, const void *w, double *spart,
+                const int32_t *status, const FoldArgs &fa, hipStream_t s) {
+    const dim3 g((unsigned)dia_grid(h)), b(kBlock);
+    if (h.dia_m == 5)
+        hipLaunchKernelGGL((k_spmv_dia<T, 5, DOT>), g, b, 0, s, h.n, (const int32_t *)h.dia_off,
+                           (const T *)h.dia_val, (const T *)x, (T *)y, (const T *)w, spart, status, fa);
+    else
+        hipLaunchKernelGGL((k_spmv_dia<T, 7, DOT>), g, b, 0, s, h.n, (const int32_t *)h.dia_off,
+                           (const T *)h.dia_val, (const T *)x, (T *)y, (const T *)w, spart, status, fa);
+}
+
 const void *ring_kernel(const Handle &h) {
     if (h.vt == SLA_F64)
         return h.rp64 ? (const void *)&k_spmv_tile_ring<double, int64_t, 1>
@@ -968,7 +1099,9 @@ void launch_tiles(Handle &h, const void *x, void *y, const void *w, double *spar
 template <typename T, typename RP, bool FUSED>
 void launch_spmv_t(Handle &h, const void *x, void *y, hipStream_t s) {
     const Red red{h.part, h.gpart, h.sync + kCntSpmv * kCountersPerKind};
-    if (h.B == 1) {
+    if (h.B == 1 && use_dia_step(h)) {
+        launch_dia<T, FUSED ? 1 : 0>(h, x, y, x, h.spart, &h.st[0].status, FoldArgs{}, s);
+    } else if (h.B == 1) {
         launch_tiles<T, RP, FUSED ? 1 : 0>(h, x, y, x, h.spart, &h.st[0].status, s);
     } else if (bvec_ok<T>(h)) {
         const Red red_g{h.part, h.gpart_spmv, h.sync + kCntSpmv * kCountersPerKind};
@@ -1115,8 +1248,10 @@ int64_t bvec_spmv_blocks(const Handle &h) {
 bool fold_possible(const Handle &h) {
     if (h.nseg > 0) return false;
     if (h.B > 1) return h.vt == SLA_F64 ? bvec_ok<double>(h) : bvec_ok<float>(h);
-    return h.nlong == 0 && use_ring(h);
+    return use_dia_step(h) || (h.nlong == 0 && use_ring(h));
 }
+
+int64_t spmv_blocks(const Handle &h) { return use_dia_step(h) ? dia_grid(h) : spmv_grid(h); }
 
 void launch_spmv_fold(Handle &h, hipStream_t s) {
     const FoldArgs fa{h.fold_z, {h.p, h.fold_p2}, h.x, h.st};
@@ -1154,6 +1289,11 @@ void launch_spmv_fold(Handle &h, hipStream_t s) {
     };
     // fp32 values never fold (a stored z would add an fp32 rounding)
     if (h.vt != SLA_F64) fail(SLA_ERR_HIP, "internal: folded direction with fp32 values");
+    if (use_dia_step(h)) {
+        launch_dia<double, 4>(h, nullptr, h.q, nullptr, h.spart, &h.st[0].status, fa, s);
+        SLA_HIP(hipGetLastError());
+        return;
+    }
     if (h.rp64) go(double(), int64_t());
     else go(double(), int32_t());
     SLA_HIP(hipGetLastError());

@@ -207,7 +207,13 @@ class SparseCSR:
         """Diagonals the single-kernel solve holds the matrix by (0: row
         tiles, or no single-kernel solve yet)."""
         m = ctypes.c_int32()
-        check(_lib.load().sla_csr_get_diagonals(self._h, ctypes.byref(m)))
+        check(_lib.load().sla_csr_get_diagonals(self._h, ctypes.byref(m), None))
+        return m.value
+
+    def step_diagonals(self) -> int:
+        """Diagonals the per-step SpMV reads (0: row tiles)."""
+        m = ctypes.c_int32()
+        check(_lib.load().sla_csr_get_diagonals(self._h, None, ctypes.byref(m)))
         return m.value
 
     def profile_reset(self) -> None:

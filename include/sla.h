@@ -152,8 +152,15 @@ enum {
                                    2D and 3D stencils), holds the matrix by diagonals: the
                                    SpMV phase reads values[d][i] and p[i + offset_d], no
                                    column indices, each row summed over its diagonals in
-                                   column order; 0: the row tiles. The values are copied to
-                                   the diagonals at every solve. */
+                                   column order; 0: the row tiles. The diagonals are a second
+                                   copy of the values, made at create and at every
+                                   sla_csr_set_values. */
+    SLA_OPT_SPMV_DIA = 12,      /* 1 (default): the per-step SpMV of such a system (the one
+                                   sla_spmv, the per-step PCG solve and its folded form
+                                   run; not BiCGStab's) reads the diagonals too: one row
+                                   per lane, every load of a wavefront 512 contiguous
+                                   bytes, each row summed over its diagonals in column
+                                   order; 0: the row tiles. */
     SLA_OPT_RESIDENT_WALK = 10  /* the single-kernel solve's SpMV phase: 2 (default) picks by
                                    matrix size, 0 and 1 force a form. 0: each wavefront sums
                                    a contiguous run of its workgroup's tiles; 1: the
@@ -419,11 +426,13 @@ sla_status sla_csr_get_layout(sla_csr h, int32_t *reordered, int32_t *narrow_col
  * when the preferred path ran). Results do not depend on the path. */
 sla_status sla_csr_get_last_path(sla_csr h, int32_t *path, uint32_t *fallbacks);
 
-/* Diagonals the single-kernel solve holds the matrix by (host output):
- * *ndiag = their number once a solve has built that solve's plan and
- * SLA_OPT_RESIDENT_DIA applies (for a reordered handle, of P A P^T), else 0
- * (row tiles, or no single-kernel solve yet). */
-sla_status sla_csr_get_diagonals(sla_csr h, int32_t *ndiag);
+/* Diagonals the solver holds the matrix by (host outputs; either may be
+ * NULL; for a reordered handle, of P A P^T): *ndiag = their number for the
+ * single-kernel solve once a solve has built its plan and
+ * SLA_OPT_RESIDENT_DIA applies, else 0 (row tiles, or no single-kernel solve
+ * yet); *per_step = their number where the per-step SpMV reads them
+ * (SLA_OPT_SPMV_DIA), else 0. */
+sla_status sla_csr_get_diagonals(sla_csr h, int32_t *ndiag, int32_t *per_step);
 
 /* Accumulated kernel timings of calls made while SLA_OPT_PROFILE was on
  * (host outputs): number of launches and total milliseconds per kind. */

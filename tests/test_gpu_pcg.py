@@ -518,7 +518,8 @@ def test_batched_single_kernel_largest_register_shape(dtype):
 
 @pytest.mark.parametrize("name,size", [("diffusion3d_128", 64), ("poisson2d_11548", 700)])
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
-def test_folded_direction_matches_oracle_and_three_kernels(name, size, dtype):
+@pytest.mark.parametrize("dia", [1, 0])
+def test_folded_direction_matches_oracle_and_three_kernels(name, size, dtype, dia):
     """SLA_OPT_FOLD_DIRECTION on the per-step path (single kernel and fused
     update off, so that it applies at these sizes): p = z + beta p formed in
     the SpMV and x += alpha p applied one iteration later, two kernels per
@@ -542,6 +543,8 @@ def test_folded_direction_matches_oracle_and_three_kernels(name, size, dtype):
     assert lay["ring_tiles"] and lay["long_rows"] == 0, lay
     A.set_option(_lib.SLA_OPT_RESIDENT, 0)
     A.set_option(_lib.SLA_OPT_FUSED_UPDATE, 0)
+    A.set_option(_lib.SLA_OPT_SPMV_DIA, dia)   # the SpMV by diagonals (dia 1) or the ring
+    assert (A.step_diagonals() > 0) == bool(dia)
 
     def solve(bb, t, maxit, prof=False):
         if prof:
@@ -595,7 +598,8 @@ def test_folded_direction_matches_oracle_and_three_kernels(name, size, dtype):
 
 
 @pytest.mark.parametrize("shift,at", [(0.3, 6), (0.5, 5), (0.7, 4), (1.2, 3), (2.5, 2)])
-def test_folded_direction_breakdown(shift, at):
+@pytest.mark.parametrize("dia", [1, 0])
+def test_folded_direction_breakdown(shift, at, dia):
     """The folded single-system solve applies x += alpha p on every other
     SpMV (two pending steps at once) and the rest at the end: a Poisson
     matrix shifted to be indefinite breaks down at iteration `at` (odd and
@@ -612,6 +616,7 @@ def test_folded_direction_breakdown(shift, at):
     assert A.layout()["ring_tiles"]
     A.set_option(_lib.SLA_OPT_RESIDENT, 0)
     A.set_option(_lib.SLA_OPT_FUSED_UPDATE, 0)
+    A.set_option(_lib.SLA_OPT_SPMV_DIA, dia)
     for graph, interval in ((1, 16), (0, 1), (1, 3)):
         A.set_option(_lib.SLA_OPT_USE_GRAPH, graph)
         A.set_option(_lib.SLA_OPT_CHECK_INTERVAL, interval)

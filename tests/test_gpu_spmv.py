@@ -6,7 +6,8 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import adversarial, make_workload
+from differentiable_sparse_linear_csr_amd import _lib
+from workloads import adversarial, make_workload, poisson2d_coo
 
 from gpu_util import coo_handle, csr_handle, dev, host, rel
 
@@ -137,11 +138,11 @@ def test_band_aligned_tiles(name, size, dtype):
     v = w.vals.astype(dtype)
     print(f"band-aligned tiles: {name} n={w.n} {np.dtype(dtype).name}", flush=True)
     A = coo_handle(w.n, r, c, v)
+    A.set_option(_lib.SLA_OPT_SPMV_DIA, 0)   # the tiles (stencils are also held by diagonals)
     x = np.random.default_rng(5).standard_normal(w.n).astype(dtype)
     check(A, r, c, v, w.n, x, 1e-12 if dtype == np.float64 else 1e-5)
     ref = oracle.coo_to_csr(w.n, r, c, v)
     b = w.b.astype(dtype)
-    from differentiable_sparse_linear_csr_amd import _lib
     A.set_option(_lib.SLA_OPT_RESIDENT, 0)
     if w.extra.get("method") == "bicgstab":
         xg, info = A.solve_raw(dev(b), 0.0, 12, method="bicgstab")
@@ -195,7 +196,6 @@ def test_ring_pipeline_matches_one_tile_ahead(case, dtype):
     tiles and sums, so bitwise equal products; both against the oracle; and
     PCG (fused w.q) and BiCGStab (two fused dots) steps on the per-step
     kernels against the oracle's."""
-    from differentiable_sparse_linear_csr_amd import _lib
     spd = True
     if case in ("poisson2d_1100", "diffusion3d_40"):
         w = (make_workload("poisson2d_11548", size=1100) if case == "poisson2d_1100"
@@ -216,6 +216,7 @@ def test_ring_pipeline_matches_one_tile_ahead(case, dtype):
     v = v.astype(dtype)
     print(f"ring SpMV: {case} n={n} nnz={v.size} {np.dtype(dtype).name}", flush=True)
     A = coo_handle(n, r, c, v)
+    A.set_option(_lib.SLA_OPT_SPMV_DIA, 0)   # the tile kernels (stencils are also held by diagonals)
     lay = A.layout()
     assert lay["narrow_columns"] and lay["ring_tiles"], lay
     x = np.random.default_rng(11).standard_normal(n).astype(dtype)
@@ -239,3 +240,69 @@ def test_ring_pipeline_matches_one_tile_ahead(case, dtype):
     xo, *_ = oracle.bicgstab(ref["row_ptr"], ref["col"], ref["vals"], b, 0.0, bsteps)
     tol = 1e-9 if dtype == np.float64 else 1e-4
     assert rel(host(xg), xo) <= tol, rel(host(xg), xo)
+
+
+@pytest.mark.parametrize("name,size,m", [("poisson2d_64", None, 5), ("poisson2d_11548", 1101, 5),
+                                         ("diffusion3d_128", 45, 7), ("poisson2d_11548", 4100, 5)])
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_spmv_by_diagonals(name, size, m, dtype):
+    """Stencils (5 and 7 diagonals; 1101^2 and 45^3 rows, ragged against the
+    kernel's 1024-row groups; 4100^2 past 2^24 rows) also held by diagonals:
+    the per-step SpMV reads them (one row per lane) against the oracle and
+    the row tiles (SLA_OPT_SPMV_DIA 0), 30 per-step PCG steps against the
+    oracle, and new values after create reach the diagonals."""
+    w = make_workload(name, size=size)
+    n = w.n
+    r = np.repeat(np.arange(n), np.diff(w.row_ptr)) if w.fmt == "csr" else w.rows
+    v = w.vals.astype(dtype)
+    print(f"SpMV by diagonals: {name} n={n} {np.dtype(dtype).name}", flush=True)
+    A = coo_handle(n, r, w.cols, v)
+    assert A.step_diagonals() == m
+    x = np.random.default_rng(5).standard_normal(n).astype(dtype)
+    tol = 1e-12 if dtype == np.float64 else 1e-5
+    check(A, r, w.cols, v, n, x, tol)
+    y1 = host(A.matvec(dev(x)))
+    A.set_option(_lib.SLA_OPT_SPMV_DIA, 0)
+    assert A.step_diagonals() == 0
+    y0 = host(A.matvec(dev(x)))
+    assert rel(y1, y0) <= tol
+    A.set_option(_lib.SLA_OPT_SPMV_DIA, 1)
+    # new values (scaled rows keep the pattern): the diagonals follow
+    v2 = (v * (1.0 + 0.5 * (r % 7 == 3))).astype(dtype)
+    A.set_values(dev(v2))
+    check(A, r, w.cols, v2, n, x, tol)
+    ref = oracle.coo_to_csr(n, r, w.cols, v)
+    A.set_values(dev(v))
+    A.set_option(_lib.SLA_OPT_RESIDENT, 0)
+    b = w.b.astype(dtype)
+    xg, info = A.solve_raw(dev(b), 0.0, 30)
+    xo, *_ = oracle.pcg(ref["row_ptr"], ref["col"], ref["vals"], b, 0.0, 30)
+    assert rel(host(xg), xo) <= (1e-12 if dtype == np.float64 else 1e-5), rel(host(xg), xo)
+
+
+def test_diagonals_only_for_fitting_patterns():
+    """Patterns that are not held by diagonals: a nine-point stencil, a
+    tridiagonal matrix with one far pair (5 offsets, mostly empty
+    diagonals), an irregular pattern, a batch."""
+    N = 30
+    i, j = np.meshgrid(np.arange(N), np.arange(N), indexing="ij")
+    idx = (i * N + j).ravel()
+    rows, cols = [idx], [idx]
+    for di in (-1, 0, 1):
+        for dj in (-1, 0, 1):
+            if di or dj:
+                ok = ((i + di >= 0) & (i + di < N) & (j + dj >= 0) & (j + dj < N)).ravel()
+                rows.append(idx[ok])
+                cols.append(((i + di) * N + (j + dj)).ravel()[ok])
+    r9, c9 = np.concatenate(rows), np.concatenate(cols)
+    assert coo_handle(N * N, r9, c9, np.ones(r9.size)).step_diagonals() == 0
+    n = 5000
+    k = np.arange(n)
+    r = np.concatenate([k, k[1:], k[:-1], [0, n - 1]])
+    c = np.concatenate([k, k[:-1], k[1:], [n - 1, 0]])
+    assert coo_handle(n, r, c, np.ones(r.size)).step_diagonals() == 0
+    r, c, v = adversarial.random_spd_coo(3000, 6.0, seed=2)
+    assert coo_handle(3000, r, c, v).step_diagonals() == 0
+    rp, cp, vp = poisson2d_coo(20)
+    V = np.stack([vp, 2 * vp]).astype(np.float32)
+    assert coo_handle(400, rp, cp, V).step_diagonals() == 0
