@@ -453,7 +453,9 @@ def measure(args, name: str, steps: int, warmup: int, cpu_budget: float,
         job_bps = {k: ab[k] / w.batch * value for k in ("iter_3k", "iter_min")}
     res_launches, res_ms = prof["cg_resident"]
     ndiag = A.diagonals()
+    sdiag = A.step_diagonals()
     layout["diagonals"] = ndiag
+    layout["step_diagonals"] = sdiag
     # what the single-kernel solve reads per iteration: the matrix as held
     # (by diagonals: their values, no column indices) and p gathered and stored
     moved_iter = (ndiag * w.n * V + 2 * V * w.n) if ndiag > 0 else ab["spmv"] / w.batch
@@ -475,8 +477,11 @@ def measure(args, name: str, steps: int, warmup: int, cpu_budget: float,
         # iterations: one direction-kernel launch each (two SpMVs in BiCGStab)
         n_it = max(prof["direction"][0] if method == "bicgstab" else prof["spmv_dot"][0], 1)
         per_iter_ms = sum(prof[k][1] for k in ("spmv_dot", "update", "direction")) / n_it
-        kernel = (("k_spmv_tile_ring" if layout.get("ring_tiles") else "k_spmv_tile")
+        kernel = ((f"k_spmv_dia (the matrix held by {sdiag} diagonals)" if sdiag > 0 else
+                   "k_spmv_tile_ring" if layout.get("ring_tiles") else "k_spmv_tile")
                   + " (q = A p; 50 back-to-back sla_spmv launches, median of 3 batches)")
+        if sdiag > 0:
+            moved_launch = sdiag * w.n * V + 2 * V * w.n
     else:
         # batched, or reordered: sla_spmv also transposes or permutes x and y,
         # so the fused SpMV of the solve is timed per launch (events around
@@ -567,12 +572,14 @@ def measure(args, name: str, steps: int, warmup: int, cpu_budget: float,
             "layout": layout,
         },
     }
-    if res_launches > 0 and ndiag > 0:
+    if (res_launches > 0 and ndiag > 0) or (res_launches == 0 and sdiag > 0
+                                             and w.batch == 1 and not layout["reordered"]):
         out["roofline"]["bytes_moved_per_launch"] = round(moved_launch)
         out["roofline"]["frac_on_moved"] = round(
             moved_launch / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         out["roofline"]["held_by_diagonals"] = (
-            f"the kernel holds the matrix by {ndiag} diagonals and reads no column indices: "
+            f"the kernel holds the matrix by {max(ndiag, sdiag)} diagonals and reads no column "
+            f"indices: "
             f"'achieved' counts the CSR algorithmic bytes (values, column indices, row "
             f"pointers, p in and q out per iteration), bytes_moved_per_launch what it reads "
             f"and writes")

@@ -391,7 +391,7 @@ void ensure_workspace(Handle &h, hipStream_t s) {
     for (void *&v : h.bi_vec) v = dalloc(h, vec);
     h.bi_part = (double *)dalloc(h, sizeof(double) * 2 * kMaxGrid);
     h.bi_gpart = (double *)dalloc(h, sizeof(double) * 2 * kGroups);
-    h.bi_spart2 = (double *)dalloc(h, sizeof(double) * 2 * kMaxGrid);
+    h.bi_spart2 = (double *)dalloc(h, sizeof(double) * 2 * std::max(kMaxGrid, kDiaGridMax));
     h.bi_sync = (uint32_t *)dalloc(h, sizeof(uint32_t) * 3 * kCountersPerKind);
     SLA_HIP(hipMemsetAsync(h.bi_sync, 0, sizeof(uint32_t) * 3 * kCountersPerKind, s));
     h.bi_state = dalloc(h, sizeof(BiState));
@@ -407,7 +407,7 @@ void iter_t(Handle &h, hipStream_t s, Launcher *lp) {
     T *v = (T *)h.q;
     BiState *st = (BiState *)h.bi_state;
     const int32_t *status = &st->status;
-    const int64_t sg = spmv_grid(h);
+    const int64_t sg = spmv_blocks(h);
     hipEvent_t a = nullptr;
     if (lp) lp->begin(SLA_KERNEL_DIRECTION, &a);
     hipLaunchKernelGGL(k_bi_dir<T>, dim3(g), dim3(kBlock), 0, s, h.n, (const T *)h.r, (T *)h.p, ph,

@@ -608,7 +608,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 // entry is a 0 at a clamped column). DOT 0: y = A x; 1: and the w.y partial
 // of each workgroup in spart; 4: the folded direction as in the ring form
 // (p_new formed at every gathered column and at the own row, x updated on
-// every other launch, p_new.q partials).
+// every other launch, p_new.q partials); 2: w.y and y.y partials (BiCGStab),
+// spart[2 b] and spart[2 b + 1].
 constexpr int kDiaRows = 4;
 
 template <typename T, int M, int DOT>
@@ -642,7 +643,7 @@ __global__ __launch_bounds__(kBlock) void k_spmv_dia(
     const int64_t X = G / kXcds, xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
     const int64_t xs = n * xcd / kXcds, xe = n * (xcd + 1) / kXcds;
     const int64_t step = X * kBlock * kDiaRows;
-    double dot = 0.0;
+    double dot = 0.0, dot2 = 0.0;
     for (int64_t r0 = xs + jx * kBlock * kDiaRows; r0 < xe; r0 += step) {
         double v[kDiaRows][M], g[kDiaRows][M], gp[FOLD ? kDiaRows : 1][FOLD ? M : 1];
         T oz[kDiaRows], op[kDiaRows], op2[kDiaRows], ox[kDiaRows], ow[kDiaRows];
@@ -670,7 +671,7 @@ __global__ __launch_bounds__(kBlock) void k_spmv_dia(
                 op2[u] = pnew[xstep ? ii : 0];   // read before this lane writes it
                 ox[u] = xx[xstep ? ii : 0];
             }
-            if (DOT == 1) ow[u] = w[ii];
+            if (DOT == 1 || DOT == 2) ow[u] = w[ii];
         }
 #pragma unroll
         for (int u = 0; u < kDiaRows; ++u) {
@@ -685,7 +686,8 @@ __global__ __launch_bounds__(kBlock) void k_spmv_dia(
             if (i < xe) {
                 const T q = (T)acc;
                 y[i] = q;
-                if (DOT == 1) dot += (double)ow[u] * (double)q;
+                if (DOT == 1 || DOT == 2) dot += (double)ow[u] * (double)q;
+                if (DOT == 2) dot2 += (double)q * (double)q;
                 if (FOLD) {
                     const T pn = fold_p<T>((double)oz[u], (double)op[u], beta);
                     if (xstep) {
@@ -702,7 +704,11 @@ __global__ __launch_bounds__(kBlock) void k_spmv_dia(
     }
     if (DOT > 0) {
         dot = block_sum(dot, lds4);
-        if (threadIdx.x == 0) spart[blockIdx.x] = dot;
+        if (DOT == 2) dot2 = block_sum(dot2, lds4);
+        if (threadIdx.x == 0) {
+            spart[(DOT == 2 ? 2 : 1) * (int64_t)blockIdx.x] = dot;
+            if (DOT == 2) spart[2 * (int64_t)blockIdx.x + 1] = dot2;
+        }
     }
 }
 
@@ -1332,6 +1338,12 @@ void launch_spmv_dots(Handle &h, const void *x, void *y, const void *w, int ndot
     auto go = [&](auto ttag, auto rtag) {
         using T = decltype(ttag);
         using RP = decltype(rtag);
+        if (use_dia_step(h) && ndot <= 2) {
+            if (ndot == 0) launch_dia<T, 0>(h, x, y, w, spart, status, FoldArgs{}, s);
+            else if (ndot == 1) launch_dia<T, 1>(h, x, y, w, spart, status, FoldArgs{}, s);
+            else launch_dia<T, 2>(h, x, y, w, spart, status, FoldArgs{}, s);
+            return;
+        }
         if (ndot == 0) launch_tiles<T, RP, 0>(h, x, y, w, spart, status, s);
         else if (ndot == 1) launch_tiles<T, RP, 1>(h, x, y, w, spart, status, s);
         else if (ndot == 2) launch_tiles<T, RP, 2>(h, x, y, w, spart, status, s);

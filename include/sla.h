@@ -156,8 +156,8 @@ enum {
                                    copy of the values, made at create and at every
                                    sla_csr_set_values. */
     SLA_OPT_SPMV_DIA = 12,      /* 1 (default): the per-step SpMV of such a system (the one
-                                   sla_spmv, the per-step PCG solve and its folded form
-                                   run; not BiCGStab's) reads the diagonals too: one row
+                                   sla_spmv, the per-step PCG solve and its folded form and
+                                   BiCGStab run) reads the diagonals too: one row
                                    per lane, every load of a wavefront 512 contiguous
                                    bytes, each row summed over its diagonals in column
                                    order; 0: the row tiles. */
