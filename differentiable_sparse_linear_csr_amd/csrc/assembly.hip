@@ -861,7 +861,7 @@ __global__ __launch_bounds__(kBlock) void k_dia_map(const RP *__restrict__ row_p
             const int64_t o = (int64_t)col[k] - i;
             int q = 0;
             while (q < d.m - 1 && (int64_t)d.o[q] != o) ++q;
-            map[k] = (int32_t)(q * n + i);
+            map[k] = (int32_t)dia_slot(q, i, d.m);
         }
 }
 
@@ -925,7 +925,7 @@ void build_dia(Handle &h, hipStream_t s) {
     SLA_HIP(hipStreamSynchronize(s));
     const int64_t m = mid[1] - mid[0];
     if (m != 5 && m != 7) return;
-    if ((double)m * (double)n > 1.25 * (double)h.nnz || m * n >= (int64_t)INT32_MAX) return;
+    if ((double)m * (double)n > 1.25 * (double)h.nnz || dia_slots(n, (int)m) >= (int64_t)INT32_MAX) return;
     int32_t cols[kDiaMax];
     SLA_HIP(hipMemcpyAsync(cols, h.col + mid[0], sizeof(int32_t) * (size_t)m, hipMemcpyDeviceToHost, s));
     SLA_HIP(hipStreamSynchronize(s));
@@ -946,9 +946,9 @@ void build_dia(Handle &h, hipStream_t s) {
     if (read_flag(flag, s) != 0) return;
     h.dia_off = (int32_t *)dalloc(h, sizeof(int32_t) * kDiaMax);
     h.dia_map = (int32_t *)dalloc(h, sizeof(int32_t) * (size_t)h.nnz);
-    h.dia_val = dalloc(h, (size_t)(m * n) * h.vbytes);
+    h.dia_val = dalloc(h, (size_t)dia_slots(n, (int)m) * h.vbytes);
     SLA_HIP(hipMemcpyAsync(h.dia_off, d.o, sizeof(int32_t) * kDiaMax, hipMemcpyHostToDevice, s));
-    SLA_HIP(hipMemsetAsync(h.dia_val, 0, (size_t)(m * n) * h.vbytes, s));
+    SLA_HIP(hipMemsetAsync(h.dia_val, 0, (size_t)dia_slots(n, (int)m) * h.vbytes, s));
     if (h.rp64)
         hipLaunchKernelGGL(k_dia_map<int64_t>, dim3(g), dim3(kBlock), 0, s,
                            (const int64_t *)h.row_ptr, (const int32_t *)h.col, n, d, h.dia_map);

@@ -32,6 +32,14 @@ constexpr int kXcds = 8;                           // workgroups go round-robin 
 constexpr int kMaxBatch = 256;
 constexpr int kDiaMax = 8;   // diagonals of a matrix the single-kernel solve holds by diagonals
 constexpr int kDiaGridMax = 8192;   // grid cap of the per-step SpMV by diagonals (spart entries)
+// diagonal values by blocks of kDiaBlock rows: block c holds its rows' m
+// diagonals one after the other, so a lane's loads stay 512 contiguous
+// bytes per wavefront and the whole matrix is one stream
+constexpr int kDiaBlock = 1024;
+__host__ __device__ inline int64_t dia_slot(int d, int64_t i, int m) {
+    return (i / kDiaBlock) * ((int64_t)m * kDiaBlock) + (int64_t)d * kDiaBlock + (i % kDiaBlock);
+}
+inline int64_t dia_slots(int64_t n, int m) { return (n + kDiaBlock - 1) / kDiaBlock * m * kDiaBlock; }
 // col and values carry this many spare entries past nnz: the SpMV reads
 // entries in 16-byte groups from a 4-aligned base and may touch (never use)
 // up to 3 entries beyond a tile's end.

@@ -456,7 +456,7 @@ __global__ __launch_bounds__(kRT, 1) void k_cg_resident(
                 for (int d = 0; d < ND; ++d) {
                     int c = i + doff[d];
                     c = c < 0 ? 0 : (c >= n32 ? n32 - 1 : c);
-                    dv2[h2][d] = in ? (double)dia_val[d * n32 + i] : 0.0;
+                    dv2[h2][d] = in ? (double)dia_val[dia_slot(d, i, ND)] : 0.0;
                     dg2[h2][d] = (double)pg[in ? c : 0];
                 }
             }

@@ -657,7 +657,7 @@ __global__ __launch_bounds__(kBlock) void k_spmv_dia(
                 int64_t c = i + off[d];
                 c = c < 0 ? 0 : (c >= n ? n - 1 : c);
                 c = in ? c : 0;
-                v[u][d] = in ? (double)dval[d * n + i] : 0.0;
+                v[u][d] = in ? (double)dval[dia_slot(d, i, M)] : 0.0;
                 if (FOLD) {
                     g[u][d] = (double)zz[c];
                     gp[FOLD ? u : 0][FOLD ? d : 0] = (double)pold[c];
